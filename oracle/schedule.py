@@ -1,0 +1,148 @@
+"""The tile scheduling rules, written out as the bit-exact specification of the host
+scheduler.  Test infrastructure only (see the package docstring).
+
+What the pages fix:
+
+* Forward tiles cost in proportion to the key/value length of their sequence; the
+  host sorts them by decreasing cost and deals them out in a zigzag: even passes from
+  the first program to the last, odd passes back from the last to the first
+  (aixai.ru page, "Tile balancing and Cluster Launch Control"; yuxiaoba page, "load
+  balancing needs a static and a dynamic layer").
+* Backward tiles cost about the same but their number varies; the host enumerates
+  only the valid tiles and deals them round robin, ordered so that neighbouring tiles
+  reuse the same data in L2 (same sections).
+* Static pre-filtering removes empty tiles; a runtime counter then hands the next
+  tile to whichever processor is free (same sections).
+* min(#processors, #tiles) persistent programs; for fixed 64-token blocks each
+  program gets a balanced contiguous range computed in closed form with divmod
+  (bittide page, section 5).
+
+Readings (listed in the design doc):
+
+* Tiles are tuples (b, h, blk).  A forward tile is ``rows`` query rows of one (b, h);
+  a self-attention backward tile is ``rows`` key rows of one (b, h).
+* Cost key of a forward tile: L_kv(b) = L_b.  Ties are broken by (b, h, blk), so the
+  sort key (-L_b, b, h, blk) is a total order.  Pass 0 runs left to right.
+* Self-attention backward tiles cost in proportion to L_b as well (their loop runs
+  over every query row of the sequence), so they take the forward rule.  The pages'
+  round robin is applied where tiles really cost the same: the broadcast-Q backward,
+  whose every tile loops over the same Mq shared queries.
+* Broadcast-Q backward is head-pinned: the program count is rounded to a multiple of
+  H, programs form H groups of P_h = P / H, and the n-th tile of head h (in (b, blk)
+  order) goes to program h * P_h + (n mod P_h).  Every program then adds into one
+  head's dQ only.
+* Broadcast-Q forward keeps the tiles of empty sequences (they must still write
+  O = 0 and lse = -inf); self and block-diagonal modes have no tile for them.
+* Dynamic mode keeps the same global order; program p starts with tile p of its group
+  and then takes tiles from a per-group atomic counter.  Its output here is that
+  global order with one segment per counter group.
+
+Every function returns plain Python lists so that a reader can compare them by eye.
+"""
+
+MODE_SELF = 0
+MODE_BROADCAST_Q = 1
+MODE_BLOCK_DIAG = 2
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def zigzag_program(n, num_programs):
+    """Program that receives the tile at sorted position n under zigzag dealing."""
+    r, pos = divmod(n, num_programs)
+    return pos if r % 2 == 0 else num_programs - 1 - pos
+
+
+def sorted_cost_tiles(lengths, num_heads, rows, rows_of):
+    """All (b, h, blk) tiles with blk < ceil(rows_of(b) / rows), sorted by the key
+    (-L_b, b, h, blk)."""
+    tiles = [(b, h, i)
+             for b in range(len(lengths))
+             for h in range(num_heads)
+             for i in range(_cdiv(rows_of(b), rows))]
+    return sorted(tiles, key=lambda t: (-int(lengths[t[0]]), t[0], t[1], t[2]))
+
+
+def _deal_zigzag(order, num_programs):
+    n_tiles = len(order)
+    p_used = min(num_programs, n_tiles)
+    if p_used == 0:
+        return [], [0], 0
+    per_prog = [[] for _ in range(p_used)]
+    for n, t in enumerate(order):
+        per_prog[zigzag_program(n, p_used)].append(t)
+    tiles, ptr = [], [0]
+    for lst in per_prog:
+        tiles.extend(lst)
+        ptr.append(len(tiles))
+    return tiles, ptr, p_used
+
+
+def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=False):
+    """Forward schedule for MODE_SELF / MODE_BROADCAST_Q.
+
+    Returns (tiles, segment_ptr, programs).  Static: tiles in program-major order and
+    one segment per program.  Dynamic: the sorted global order and one segment."""
+    if mode == MODE_SELF:
+        order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(lengths[b]))
+    elif mode == MODE_BROADCAST_Q:
+        order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(num_q))
+    else:
+        raise ValueError("fwd_schedule covers the self and broadcast-Q modes")
+    if dynamic:
+        return order, [0, len(order)], min(num_programs, len(order))
+    return _deal_zigzag(order, num_programs)
+
+
+def bwd_schedule(lengths, num_heads, mode, rows, num_programs, dynamic=False):
+    """Backward schedule for MODE_SELF / MODE_BROADCAST_Q over key/value tiles of
+    ``rows`` keys.  Returns (tiles, segment_ptr, programs) as in fwd_schedule; the
+    broadcast-Q dynamic form has one segment per head."""
+    if mode == MODE_SELF:
+        order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(lengths[b]))
+        if dynamic:
+            return order, [0, len(order)], min(num_programs, len(order))
+        return _deal_zigzag(order, num_programs)
+    if mode != MODE_BROADCAST_Q:
+        raise ValueError("bwd_schedule covers the self and broadcast-Q modes")
+    per_head = [[(b, h, j) for b in range(len(lengths)) for j in range(_cdiv(int(lengths[b]), rows))]
+                for h in range(num_heads)]
+    n_head = len(per_head[0]) if num_heads else 0
+    if n_head == 0:
+        return [], [0], 0
+    p_h = max(1, min(num_programs // num_heads, n_head))
+    if dynamic:
+        tiles, ptr = [], [0]
+        for lst in per_head:
+            tiles.extend(lst)
+            ptr.append(len(tiles))
+        return tiles, ptr, p_h * num_heads
+    per_prog = [[] for _ in range(p_h * num_heads)]
+    for h, lst in enumerate(per_head):
+        for n, t in enumerate(lst):
+            per_prog[h * p_h + n % p_h].append(t)
+    tiles, ptr = [], [0]
+    for lst in per_prog:
+        tiles.extend(lst)
+        ptr.append(len(tiles))
+    return tiles, ptr, p_h * num_heads
+
+
+def blockdiag_schedule(lengths, num_heads, num_programs, block=64):
+    """Block-diagonal schedule: tiles (b, h, j) for every block j < ceil(L_b / block),
+    enumerated with the head fastest, so consecutive tiles cover one contiguous slab
+    of the packed buffer.  Program p receives the contiguous range
+    [p*q + min(p, r), (p+1)*q + min(p+1, r)) with (q, r) = divmod(N, P)."""
+    tiles = [(b, h, j)
+             for b in range(len(lengths))
+             for j in range(_cdiv(int(lengths[b]), block))
+             for h in range(num_heads)]
+    n_tiles = len(tiles)
+    p_used = min(num_programs, n_tiles)
+    if p_used == 0:
+        return [], [0], 0
+    q, r = divmod(n_tiles, p_used)
+    ptr = [p * q + min(p, r) for p in range(p_used + 1)]
+    return tiles, ptr, p_used

@@ -1,0 +1,31 @@
+"""Valid-token accounting pinned to the worked example on the explore.n1n.ai page
+(section on the performance defects of padded tensors) and to closed forms."""
+
+import json
+import os
+
+from variable_length_flash_jagged_amd import metrics as M
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_worked_example_pairs_and_padding_waste():
+    g = json.load(open(os.path.join(GOLDEN, "worked_offsets.json")))
+    lengths = g["lengths"]
+    assert M.valid_pairs(lengths, M.MODE_SELF) == 128**2 + 4096**2 + 512**2 + 2048**2 == 21_250_048
+    assert M.padded_pairs(lengths) == 4 * 4096**2 == 67_108_864
+    # token waste of padding: 1 - 6784 / 16384 ~ 58.6 %, the page's "up to 60 %"
+    assert abs((1 - g["total_tokens"] / g["padded_tokens"]) - 0.586) < 1e-3
+
+
+def test_block_diag_pairs_closed_form():
+    # full blocks give 64^2 each; a trailing block of r tokens gives r^2
+    assert M.valid_pairs([64 * 3, 70, 5], M.MODE_BLOCK_DIAG) == 4 * 64 * 64 + 36 + 25
+
+
+def test_flop_and_byte_counts():
+    assert M.fwd_flops([4, 2], M.MODE_SELF, 2, 8) == 4 * 2 * 8 * 20
+    assert M.bwd_flops([4, 2], M.MODE_SELF, 2, 8) == 10 * 2 * 8 * 20
+    assert M.valid_pairs([3, 5], M.MODE_BROADCAST_Q, num_q=7) == 56
+    assert M.fwd_bytes([4, 2], M.MODE_SELF, 2, 8) == 8 * 6 * 16 + 4 * 12
+    assert M.bwd_bytes([4, 2], M.MODE_SELF, 2, 8) == 16 * 6 * 16 + 4 * 12

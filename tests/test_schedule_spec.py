@@ -1,0 +1,121 @@
+"""Pins of the scheduler specification (oracle/schedule.py): hand-worked examples of
+the pages' rules (tests/golden) and invariants that hold for any input."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import schedule as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def test_zigzag_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "zigzag_example.json")))
+    order = S.sorted_cost_tiles(g["lengths"], g["num_heads"], g["rows"], lambda b: g["lengths"][b])
+    assert [list(t) for t in order] == g["sorted_order"]
+    tiles, ptr, p = S.fwd_schedule(g["lengths"], g["num_heads"], S.MODE_SELF, 0, g["rows"], g["num_programs"])
+    assert p == g["num_programs"]
+    got = [[list(t) for t in tiles[ptr[i]:ptr[i + 1]]] for i in range(p)]
+    assert got == g["program_tiles"]
+
+
+def test_zigzag_program_rule():
+    # even passes left to right, odd passes right to left
+    assert [S.zigzag_program(n, 3) for n in range(9)] == [0, 1, 2, 2, 1, 0, 0, 1, 2]
+
+
+def test_blockdiag_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "blockdiag_example.json")))
+    off = g["offsets"]
+    lengths = [off[i + 1] - off[i] for i in range(len(off) - 1)]
+    tiles, ptr, p = S.blockdiag_schedule(lengths, g["num_heads"], g["num_programs"], g["block"])
+    assert [list(t) for t in tiles] == g["tiles"]
+    assert ptr == g["program_ptr"]
+
+
+def _random_lengths(rng, n):
+    x = rng.integers(0, 300, size=n)
+    x[rng.random(n) < 0.1] = 0
+    x[rng.random(n) < 0.1] = 1
+    return x.tolist()
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("mode", [S.MODE_SELF, S.MODE_BROADCAST_Q])
+def test_fwd_covers_every_tile_once_and_balances(seed, mode):
+    rng = np.random.default_rng(seed)
+    lengths = _random_lengths(rng, 37)
+    h, rows, mq, nprog = 3, 64, 100, 13
+    tiles, ptr, p = S.fwd_schedule(lengths, h, mode, mq, rows, nprog)
+    lq = (lambda b: lengths[b]) if mode == S.MODE_SELF else (lambda b: mq)
+    expect = {(b, hh, i) for b in range(len(lengths)) for hh in range(h) for i in range(_cdiv(lq(b), rows))}
+    assert len(tiles) == len(expect) == h * sum(_cdiv(lq(b), rows) for b in range(len(lengths)))
+    assert set(tiles) == expect
+    assert p == min(nprog, len(expect)) and ptr[-1] == len(tiles)
+    # within a program, tiles keep sorted order; program loads differ by at most one tile cost
+    cost = {t: lengths[t[0]] for t in tiles}
+    loads = [sum(cost[t] for t in tiles[ptr[i]:ptr[i + 1]]) for i in range(p)]
+    assert max(loads) - min(loads) <= max(lengths)
+    # dynamic mode: the same tiles in global sorted order
+    dt, dptr, dp = S.fwd_schedule(lengths, h, mode, mq, rows, nprog, dynamic=True)
+    assert sorted(dt) == sorted(tiles) and dptr == [0, len(dt)] and dp == p
+    keys = [(-lengths[t[0]], t) for t in dt]
+    assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_bwd_broadcast_q_head_pinned_round_robin(seed):
+    rng = np.random.default_rng(100 + seed)
+    lengths = _random_lengths(rng, 23)
+    h, rows, nprog = 4, 128, 30
+    tiles, ptr, p = S.bwd_schedule(lengths, h, S.MODE_BROADCAST_Q, rows, nprog)
+    n_head = sum(_cdiv(n, rows) for n in lengths)
+    p_h = max(1, min(nprog // h, n_head))
+    assert p == p_h * h
+    for prog in range(p):
+        mine = tiles[ptr[prog]:ptr[prog + 1]]
+        assert all(t[1] == prog // p_h for t in mine)  # one head per program
+    # round robin within the head group, in (b, blk) order
+    for hh in range(h):
+        order = [(b, hh, j) for b in range(len(lengths)) for j in range(_cdiv(lengths[b], rows))]
+        for n, t in enumerate(order):
+            prog = hh * p_h + n % p_h
+            assert t in tiles[ptr[prog]:ptr[prog + 1]]
+    dt, dptr, dp = S.bwd_schedule(lengths, h, S.MODE_BROADCAST_Q, rows, nprog, dynamic=True)
+    assert dp == p and len(dptr) == h + 1 and sorted(dt) == sorted(tiles)
+
+
+def test_bwd_self_uses_sorted_zigzag():
+    lengths = [300, 5, 0, 129, 64]
+    tiles, ptr, p = S.bwd_schedule(lengths, 2, S.MODE_SELF, 64, 4)
+    ft, fptr, fp = S.fwd_schedule(lengths, 2, S.MODE_SELF, 0, 64, 4)
+    assert (tiles, ptr, p) == (ft, fptr, fp)
+
+
+@pytest.mark.parametrize("nprog", [1, 3, 7, 1000])
+def test_blockdiag_ranges_are_contiguous_and_balanced(nprog):
+    rng = np.random.default_rng(nprog)
+    lengths = (rng.integers(0, 5, size=20) * 64 + rng.integers(0, 2, size=20) * 7).tolist()
+    tiles, ptr, p = S.blockdiag_schedule(lengths, 3, nprog)
+    n = sum(_cdiv(x, 64) for x in lengths) * 3
+    assert len(tiles) == n and p == min(nprog, n)
+    sizes = [ptr[i + 1] - ptr[i] for i in range(p)]
+    assert max(sizes) - min(sizes) <= 1 and ptr[0] == 0 and ptr[-1] == n
+    # head fastest
+    assert [t[1] for t in tiles[:3]] == [0, 1, 2]
+
+
+def test_empty_batch():
+    assert S.fwd_schedule([0, 0], 2, S.MODE_SELF, 0, 64, 8) == ([], [0], 0)
+    assert S.bwd_schedule([0], 2, S.MODE_BROADCAST_Q, 64, 8) == ([], [0], 0)
+    assert S.blockdiag_schedule([], 2, 8) == ([], [0], 0)
+    # broadcast-Q forward keeps tiles of empty sequences (they write O = 0)
+    t, _, _ = S.fwd_schedule([0, 0], 1, S.MODE_BROADCAST_Q, 64, 64, 8)
+    assert sorted(t) == [(0, 0, 0), (1, 0, 0)]

@@ -1,0 +1,58 @@
+"""Work and traffic accounting over valid tokens only (no padding counted).
+
+Valid query-key pairs: self-attention sum_b L_b^2; broadcast-Q Mq * sum_b L_b;
+64-token block-diagonal sum over blocks of len^2.  Forward FLOPs = 4 * H * D * pairs
+(two products, 2 FLOPs per multiply-add); backward FLOPs = 2.5 x forward (five
+products).  Algorithmic bytes are each input read once and each output written once
+(bf16 tensors, fp32 lse).
+"""
+
+import numpy as np
+
+MODE_SELF = 0
+MODE_BROADCAST_Q = 1
+MODE_BLOCK_DIAG = 2
+
+
+def valid_pairs(lengths, mode, num_q=0, block=64):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if mode == MODE_SELF:
+        return int((lengths * lengths).sum())
+    if mode == MODE_BROADCAST_Q:
+        return int(num_q) * int(lengths.sum())
+    if mode == MODE_BLOCK_DIAG:
+        full = lengths // block
+        rem = lengths % block
+        return int((full * block * block + rem * rem).sum())
+    raise ValueError("unknown mode")
+
+
+def padded_pairs(lengths):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return int(len(lengths) * int(lengths.max(initial=0)) ** 2)
+
+
+def fwd_flops(lengths, mode, num_heads, head_dim, num_q=0):
+    return 4 * num_heads * head_dim * valid_pairs(lengths, mode, num_q)
+
+
+def bwd_flops(lengths, mode, num_heads, head_dim, num_q=0):
+    return 10 * num_heads * head_dim * valid_pairs(lengths, mode, num_q)
+
+
+def fwd_bytes(lengths, mode, num_heads, head_dim, num_q=0):
+    t = int(np.asarray(lengths, dtype=np.int64).sum())
+    h, d = num_heads, head_dim
+    if mode == MODE_BROADCAST_Q:
+        b = len(lengths)
+        return 2 * num_q * h * d + 4 * t * h * d + 2 * b * num_q * h * d + 4 * b * h * num_q
+    return 8 * t * h * d + 4 * t * h
+
+
+def bwd_bytes(lengths, mode, num_heads, head_dim, num_q=0):
+    t = int(np.asarray(lengths, dtype=np.int64).sum())
+    h, d = num_heads, head_dim
+    if mode == MODE_BROADCAST_Q:
+        b = len(lengths)
+        return 4 * num_q * h * d + 8 * t * h * d + 4 * b * num_q * h * d + 4 * b * h * num_q
+    return 16 * t * h * d + 4 * t * h
