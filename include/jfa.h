@@ -1,0 +1,155 @@
+/*
+ * jfa.h -- C ABI of the jagged flash attention library for AMD MI355X (gfx950).
+ *
+ * Exact softmax attention, forward and backward, computed directly on packed
+ * variable-length ("jagged") Q/K/V whose sequence boundaries come from an offsets
+ * (cu_seqlens) array; no padding is materialised at any step.
+ *
+ * Sources (page title, section):
+ *  - "Using TLX to optimise jagged flash attention on Blackwell GPUs" (explore.n1n.ai),
+ *    section on the performance defects of padded tensors: the jagged layout (valid
+ *    tokens back to back) and the offsets array, e.g. lengths [128,4096,512,2048]
+ *    -> offsets [0,128,4224,4736,6784].
+ *  - "Jagged Flash Attention on TLX" (aixai.ru), "What is Jagged Flash Attention":
+ *    the attention runs on packed Q, K, V plus offsets; the broadcast-Q production
+ *    mode shares one dense Q across the batch and sums its gradient dQ over all
+ *    sequences.
+ *  - "TLX Block Attention" (bittide page), section 1: fixed 64-token groups that
+ *    attend only within themselves (block-diagonal mode); section 2.1, Listing 1: the
+ *    online-softmax forward and the log-sum-exp L = m + log(l) kept for the backward;
+ *    section 4: the backward with Di = rowsum(dO * O) computed inline; section 5:
+ *    persistent programs and host-side (CPU offsets) scheduling with no GPU sync.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are caller-allocated device buffers, contiguous, 16-byte aligned.
+ *    Element types: bf16 for q, k, v, o, dout, dq, dk, dv; fp32 for lse; int32 for
+ *    offsets.  Token-major layout [tokens, H, D] (row stride H*D elements).
+ *  - Shapes by mode (T = offsets[B], Mq = shape->num_q):
+ *        mode            q          k, v       o, dout       lse         dq
+ *        SELF            [T,H,D]    [T,H,D]    [T,H,D]       [H,T]       [T,H,D]
+ *        BROADCAST_Q     [Mq,H,D]   [T,H,D]    [B,Mq,H,D]    [B,H,Mq]    [Mq,H,D]
+ *        BLOCK_DIAG      [T,H,D]    [T,H,D]    [T,H,D]       [H,T]       [T,H,D]
+ *    dk, dv always have the shape of k, v.  lse is the natural-log log-sum-exp of the
+ *    scaled scores of each query row; a broadcast-Q sequence of length 0 gets
+ *    o = 0 and lse = -inf and contributes no gradient.
+ *  - offsets_dev / offsets_host: int32 [B+1], offsets[0] = 0, non-decreasing,
+ *    offsets[B] = shape->total_tokens.  offsets_host may be NULL: the library then
+ *    copies the device offsets to the host and synchronises the stream (slow path).
+ *    With host offsets the call performs no device synchronisation.
+ *  - workspace: caller-allocated device scratch of at least jfa_workspace_size()
+ *    bytes (256-byte aligned); its contents are overwritten.
+ *  - stream: a hipStream_t (NULL = the default stream).  Calls are asynchronous;
+ *    outputs are valid once the stream has reached them.  Host arrays are consumed
+ *    before the call returns.
+ *  - Return value: 0 on success or a negative JFA_ERR_* code.  Every argument check
+ *    runs before any device work is queued; a failed check queues nothing.
+ *    jfa_last_error_detail() returns a thread-local message about the last failure.
+ *    No C++ exception crosses this interface.
+ */
+#ifndef JFA_H_
+#define JFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JFA_VERSION 100 /* 1.0.0 */
+
+enum jfa_mode {
+  JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
+  JFA_MODE_BROADCAST_Q = 1, /* one shared Q [Mq,H,D] attends to every sequence's K/V */
+  JFA_MODE_BLOCK_DIAG = 2   /* 64-token groups of each sequence attend within themselves */
+};
+
+enum jfa_pass { JFA_PASS_FWD = 0, JFA_PASS_BWD = 1 };
+
+enum jfa_status {
+  JFA_OK = 0,
+  JFA_ERR_NULL_POINTER = -1,    /* a required pointer argument is NULL */
+  JFA_ERR_BAD_SHAPE = -2,       /* B < 0, H < 1, total_tokens < 0, Mq < 1 in broadcast-Q ... */
+  JFA_ERR_BAD_HEAD_DIM = -3,    /* head_dim not in {64, 128} */
+  JFA_ERR_BAD_MODE = -4,        /* mode not a jfa_mode, or pass not a jfa_pass */
+  JFA_ERR_BAD_OFFSETS = -5,     /* offsets[0] != 0, decreasing, or offsets[B] != T */
+  JFA_ERR_MISALIGNED = -6,      /* a tensor is not 16-byte aligned (workspace: 256) */
+  JFA_ERR_WORKSPACE = -7,       /* workspace smaller than jfa_workspace_size() */
+  JFA_ERR_BAD_OPTION = -8,      /* an option field out of range */
+  JFA_ERR_TOO_LARGE = -9,       /* sizes beyond the 32-bit tile / element indexing */
+  JFA_ERR_HIP = -10,            /* a HIP runtime call or kernel launch failed */
+  JFA_ERR_CAPACITY = -11        /* jfa_schedule: an output array is too small */
+};
+
+/* Problem sizes. */
+typedef struct jfa_shape {
+  int32_t num_seqs;     /* B >= 0 */
+  int32_t num_heads;    /* H >= 1 (query and key/value heads are the same) */
+  int32_t head_dim;     /* D in {64, 128} */
+  int32_t num_q;        /* Mq >= 1, broadcast-Q only (ignored otherwise) */
+  int64_t total_tokens; /* T = offsets[B] */
+} jfa_shape;
+
+/* Tuning options; pass NULL for the defaults (all zero). */
+typedef struct jfa_opts {
+  int32_t sched;        /* 0: static host schedule (sorted zigzag / head-pinned round robin /
+                           contiguous ranges); 1: same order, tiles taken at run time from an
+                           atomic counter (block-diagonal mode is always static) */
+  int32_t dq_path;      /* broadcast-Q backward only. 0: fp32 atomics into one [Mq,H,D]
+                           accumulator; 1: per-program fp32 partial slabs [P,Mq,D] reduced
+                           by a second kernel (run-to-run deterministic) */
+  int32_t num_programs; /* persistent workgroups; 0 = one per resident slot on the device */
+  int32_t reserved;     /* must be 0 */
+} jfa_opts;
+
+/* Bytes of workspace jfa_fwd (pass 0) or jfa_bwd (pass 1) needs for this shape and
+ * mode.  Depends on (B, H, D, Mq, T) and the options only, never on the individual
+ * lengths.  Returns 0 or an error code; *bytes is written on success. */
+int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opts* opts,
+                       size_t* bytes);
+
+/* Forward: o = softmax(scale * q k^T) v per sequence (per 64-token block in
+ * BLOCK_DIAG mode) and the per-row lse.  See the header comment for shapes. */
+int jfa_fwd(const jfa_shape* shape, int mode, float scale,
+            const void* q, const void* k, const void* v,
+            const int32_t* offsets_dev, const int32_t* offsets_host,
+            void* o, float* lse,
+            void* workspace, size_t workspace_bytes,
+            const jfa_opts* opts, void* stream);
+
+/* Backward of the forward above for upstream gradient dout: dq, dk, dv (bf16,
+ * accumulated in fp32).  P is recomputed from q, k and lse; Di = rowsum(dout * o) is
+ * computed inline.  `scale` must equal the forward's.  In BROADCAST_Q mode dq is the
+ * sum over all sequences. */
+int jfa_bwd(const jfa_shape* shape, int mode, float scale,
+            const void* q, const void* k, const void* v,
+            const void* o, const void* dout, const float* lse,
+            const int32_t* offsets_dev, const int32_t* offsets_host,
+            void* dq, void* dk, void* dv,
+            void* workspace, size_t workspace_bytes,
+            const jfa_opts* opts, void* stream);
+
+/* Host-only view of the tile schedule the calls above would run (no device needed).
+ * Tiles are (b, h, blk) triples: forward tiles are tile_rows query rows, backward
+ * tiles tile_rows key rows, block-diagonal tiles one 64-token block.  Static
+ * schedules list tiles program by program with one segment per program
+ * (seg_ptr[P+1]); dynamic schedules list the global order with one segment per
+ * counter group.  tiles (3*cap int32) and seg_ptr (seg_cap int32) may be NULL to
+ * query the counts only; JFA_ERR_CAPACITY if an array is too small. */
+int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,
+                 const jfa_opts* opts, int32_t* tiles, int64_t cap, int32_t* seg_ptr,
+                 int64_t seg_cap, int64_t* n_tiles, int32_t* n_segs, int32_t* n_programs,
+                 int32_t* tile_rows);
+
+/* Static message for a status code. */
+const char* jfa_error_string(int code);
+/* Thread-local detail about the last failed call on this thread ("" if none). */
+const char* jfa_last_error_detail(void);
+/* JFA_VERSION of the built library. */
+int jfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H_ */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every
+symbol include/jfa.h declares, rejects bad arguments before any device work, and its
+tile schedules equal the specification in oracle/schedule.py bit for bit."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import schedule as spec
+from variable_length_flash_jagged_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "jfa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(jfa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"jfa_fwd", "jfa_bwd", "jfa_workspace_size", "jfa_schedule", "jfa_error_string",
+            "jfa_last_error_detail", "jfa_version"} <= set(names)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.jfa_version() == 100
+
+
+def test_error_strings():
+    lib = B.lib()
+    for code in range(0, -12, -1):
+        assert lib.jfa_error_string(code)
+    assert b"unknown" in lib.jfa_error_string(-99)
+
+
+@pytest.mark.parametrize("kw,mode,code", [
+    (dict(num_seqs=-1), 0, -2),
+    (dict(num_heads=0), 0, -2),
+    (dict(head_dim=96), 0, -3),
+    (dict(), 7, -4),
+    (dict(num_q=0), 1, -2),
+    (dict(total_tokens=1 << 31), 0, -9),
+])
+def test_workspace_size_rejects_bad_shapes(kw, mode, code):
+    args = dict(num_seqs=2, num_heads=2, head_dim=64, total_tokens=10, num_q=4)
+    args.update(kw)
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(B.make_shape(**args), mode, 0)
+    assert e.value.code == code
+
+
+def test_bad_options_and_pass():
+    shape = B.make_shape(2, 2, 64, 10)
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(shape, 0, 0, B.make_opts(sched=3))
+    assert e.value.code == -8
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(shape, 0, 2)
+    assert e.value.code == -4
+
+
+@pytest.mark.parametrize("off,code", [([1, 4, 10], -5), ([0, 6, 4], -5), ([0, 4, 9], -5)])
+def test_schedule_rejects_bad_offsets(off, code):
+    with pytest.raises(B.JfaError) as e:
+        B.schedule(B.make_shape(2, 1, 64, 10), 0, 0, off)
+    assert e.value.code == code
+
+
+def test_fwd_rejects_null_pointers_before_any_device_work():
+    lib = B.lib()
+    shape = B.make_shape(1, 1, 64, 4)
+    off = np.array([0, 4], dtype=np.int32)
+    rc = lib.jfa_fwd(ctypes.byref(shape), 0, 0.125, None, None, None, None, off.ctypes.data, None, None, None, 0,
+                     None, None)
+    assert rc == -1
+    assert b"non-NULL" in lib.jfa_last_error_detail()
+
+
+def test_workspace_does_not_depend_on_individual_lengths():
+    # a function of (B, H, D, Mq, T) and the options only
+    s = B.make_shape(3, 4, 128, 1000)
+    a = B.workspace_size(s, 0, 1, B.make_opts(num_programs=64))
+    assert a == B.workspace_size(s, 0, 1, B.make_opts(num_programs=64))
+    assert a >= 1000 * 4 * 128 * 4  # fp32 dq accumulator
+
+
+def _lengths(rng, n, hi):
+    x = rng.integers(0, hi, size=n)
+    x[rng.random(n) < 0.15] = 0
+    x[rng.random(n) < 0.15] = 1
+    return x
+
+
+def _to_lists(tiles, seg):
+    return [tuple(int(v) for v in t) for t in tiles], [int(v) for v in seg]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("pass_", [0, 1])
+@pytest.mark.parametrize("sched", [0, 1])
+def test_schedule_matches_spec_bit_exactly(seed, mode, pass_, sched):
+    rng = np.random.default_rng(seed * 7 + mode)
+    lengths = _lengths(rng, int(rng.integers(1, 60)), 700)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    h, mq = int(rng.integers(1, 5)), int(rng.integers(1, 300))
+    nprog = int(rng.integers(1, 90))
+    shape = B.make_shape(len(lengths), h, 128, int(off[-1]), mq)
+    opts = B.make_opts(sched=sched, num_programs=nprog)
+    tiles, seg, progs, rows = B.schedule(shape, mode, pass_, off, opts)
+    got_t, got_s = _to_lists(tiles, seg)
+    lens = lengths.tolist()
+    if mode == 2:
+        want = spec.blockdiag_schedule(lens, h, nprog, 64)
+        assert rows == 64
+    elif pass_ == 0:
+        want = spec.fwd_schedule(lens, h, mode, mq, rows, nprog, dynamic=bool(sched))
+    else:
+        want = spec.bwd_schedule(lens, h, mode, rows, nprog, dynamic=bool(sched))
+    assert got_t == [tuple(t) for t in want[0]]
+    assert got_s == list(want[1])
+    assert progs == want[2]
+
+
+def test_schedule_tile_rows():
+    off = np.array([0, 300], dtype=np.int32)
+    shape = B.make_shape(1, 1, 128, 300)
+    assert B.schedule(shape, 0, 0, off)[3] == 128
+    assert B.schedule(shape, 0, 1, off)[3] == 128
+    assert B.schedule(shape, 2, 0, off)[3] == 64

@@ -1,0 +1,128 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle on seeded
+inputs, at sizes the oracle finishes in seconds: several tiles, ragged tails, empty
+and length-1 sequences, both head dims, all three modes, both schedules and both
+broadcast-Q dQ paths.  Tolerances are in tests/gpu_helpers.py."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import gpu_helpers as G
+from variable_length_flash_jagged_amd import binding as B
+from variable_length_flash_jagged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 5, 63, 64, 65, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_ragged(head_dim):
+    G.run_case(RAGGED, 2, head_dim, label=f"self ragged D{head_dim}")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_with_empty_sequences(head_dim):
+    G.run_case([0, 33, 0, 70, 0, 300, 0], 3, head_dim, seed=3, label="self empties")
+
+
+def test_self_dynamic_schedule():
+    G.run_case(RAGGED + [511, 2], 2, 128, opts=B.make_opts(sched=1), seed=4, label="self dynamic")
+
+
+def test_self_few_programs():
+    # many tiles per persistent workgroup
+    G.run_case(RAGGED, 2, 128, opts=B.make_opts(num_programs=3), seed=5, label="self 3 programs")
+
+
+def test_self_device_offsets_slow_path():
+    G.run_case([17, 130, 64], 1, 64, host_offsets=False, seed=6, label="self slow path")
+
+
+def test_length_one_gives_o_equal_v_bit_exact():
+    p = W.make_problem([1, 1, 1], 2, 128, seed=7, device="cpu", with_grad=False)
+    g = G.to_gpu(p)
+    o, lse = G.gpu_fwd(g)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), p["v"])
+    dots = (p["q"].float() * p["k"].float()).sum(-1).T * p["scale"]  # [H, T]
+    assert torch.allclose(lse.cpu(), dots, atol=1e-5)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("num_q", [1, 100, 256])
+@pytest.mark.parametrize("dq_path", [0, 1])
+def test_broadcast_q(head_dim, num_q, dq_path):
+    lengths = [1, 0, 64, 129, 300, 7, 0, 256]
+    G.run_case(lengths, 2, head_dim, W.MODE_BROADCAST_Q, num_q, seed=8,
+               opts=B.make_opts(dq_path=dq_path), label=f"bq D{head_dim} Mq{num_q} path{dq_path}")
+
+
+@pytest.mark.parametrize("sched", [0, 1])
+def test_broadcast_q_schedules_and_program_counts(sched):
+    lengths = [40, 300, 1, 129, 128]
+    for nprog in (2, 5, 64):
+        G.run_case(lengths, 3, 128, W.MODE_BROADCAST_Q, 70, seed=9,
+                   opts=B.make_opts(sched=sched, dq_path=1, num_programs=nprog), label=f"bq sched{sched} P{nprog}")
+
+
+def test_broadcast_q_partials_are_run_to_run_identical():
+    p = W.make_problem([90, 300, 17], 2, 128, W.MODE_BROADCAST_Q, 128, seed=10, device="cpu")
+    g = G.to_gpu(p)
+    opts = B.make_opts(dq_path=1)
+    o, lse = G.gpu_fwd(g, opts)
+    a = G.gpu_bwd(g, o, lse, opts)
+    b = G.gpu_bwd(g, o, lse, opts)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_block_diag(head_dim):
+    G.run_case([64, 130, 5, 0, 256, 1, 63], 3, head_dim, W.MODE_BLOCK_DIAG, seed=11, label=f"bd D{head_dim}")
+
+
+def test_block_diag_few_programs():
+    G.run_case([64 * 5, 64 * 3, 64], 4, 64, W.MODE_BLOCK_DIAG, seed=12, opts=B.make_opts(num_programs=2),
+               label="bd 2 programs")
+
+
+def test_bwd_from_oracle_forward():
+    """Feed the backward the oracle's O (rounded to bf16) and lse, isolating its error."""
+    p = W.make_problem(RAGGED, 2, 128, seed=13, device="cpu")
+    g = G.to_gpu(p)
+    o_ref, lse_ref = G.oracle_fwd(p)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(lse_ref).float().cuda()
+    grads = G.gpu_bwd(g, o, lse)
+    torch.cuda.synchronize()
+    G.check_bwd(grads, G.oracle_bwd(p), "bwd from oracle fwd")
+
+
+def test_outputs_leave_guard_canaries_untouched():
+    p = W.make_problem([70, 5, 200], 2, 64, seed=14, device="cpu")
+    g = G.to_gpu(p)
+    t, h, d = p["k"].shape
+    pad = 4096
+    sentinel = -12345.0
+    ob = torch.full((t * h * d + 2 * pad,), sentinel, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((t * h + 2 * pad,), sentinel, dtype=torch.float32, device="cuda")
+    o = ob[pad:pad + t * h * d].view(t, h, d)
+    lse = lb[pad:pad + t * h].view(h, t)
+    B.fwd(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], 0, g["scale"], None, o, lse)
+    bufs = [torch.full((t * h * d + 2 * pad,), sentinel, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    views = [b[pad:pad + t * h * d].view(t, h, d) for b in bufs]
+    B.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], 0, g["scale"], None, *views)
+    torch.cuda.synchronize()
+    for buf in [ob, lb] + bufs:
+        assert torch.all(buf[:pad] == sentinel) and torch.all(buf[-pad:] == sentinel)
+    G.check_fwd(o, lse, *G.oracle_fwd(p), "canary")
+
+
+@pytest.mark.parametrize("workload,num_seqs", [(1, None), (2, 16), (3, 24), (4, 2), (5, 24)])
+def test_workloads_reduced(workload, num_seqs):
+    w = W.WORKLOADS[workload]
+    lengths = W.workload_lengths(workload, 0, num_seqs)
+    G.run_case(lengths, w["num_heads"], w["head_dim"], w["mode"], w["num_q"], seed=workload,
+               label=f"workload {workload} ({w['name']}) reduced")

@@ -1,0 +1,202 @@
+"""ctypes binding over libjfa.so (argument marshalling only).
+
+Every function here forwards torch tensors' device pointers and the current HIP stream
+to the C ABI declared in include/jfa.h; all of the attention work runs in the
+library's kernels.  A missing library raises immediately: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libjfa.so")
+
+MODE_SELF = 0
+MODE_BROADCAST_Q = 1
+MODE_BLOCK_DIAG = 2
+PASS_FWD = 0
+PASS_BWD = 1
+
+
+class JfaError(RuntimeError):
+    def __init__(self, code, func, detail):
+        super().__init__(f"{func} failed with {code}: {detail}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_q", ctypes.c_int32), ("total_tokens", ctypes.c_int64)]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("sched", ctypes.c_int32), ("dq_path", ctypes.c_int32), ("num_programs", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m variable_length_flash_jagged_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sp, op = ctypes.POINTER(Shape), ctypes.POINTER(Opts)
+        i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+        L.jfa_version.restype = ctypes.c_int
+        L.jfa_error_string.restype = ctypes.c_char_p
+        L.jfa_error_string.argtypes = [ctypes.c_int]
+        L.jfa_last_error_detail.restype = ctypes.c_char_p
+        L.jfa_workspace_size.restype = ctypes.c_int
+        L.jfa_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.c_int, op, ctypes.POINTER(ctypes.c_size_t)]
+        L.jfa_fwd.restype = ctypes.c_int
+        L.jfa_fwd.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, op, vp]
+        L.jfa_bwd.restype = ctypes.c_int
+        L.jfa_bwd.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                              ctypes.c_size_t, op, vp]
+        L.jfa_schedule.restype = ctypes.c_int
+        L.jfa_schedule.argtypes = [sp, ctypes.c_int, ctypes.c_int, vp, op, vp, i64, vp, i64, i64p, i32p, i32p, i32p]
+        _lib = L
+    return _lib
+
+
+def _check(rc, func):
+    if rc != 0:
+        L = lib()
+        detail = L.jfa_last_error_detail().decode() or L.jfa_error_string(rc).decode()
+        raise JfaError(rc, func, detail)
+
+
+def make_shape(num_seqs, num_heads, head_dim, total_tokens, num_q=0):
+    return Shape(int(num_seqs), int(num_heads), int(head_dim), int(num_q), int(total_tokens))
+
+
+def make_opts(sched=0, dq_path=0, num_programs=0):
+    return Opts(int(sched), int(dq_path), int(num_programs), 0)
+
+
+def workspace_size(shape, mode, pass_, opts=None):
+    n = ctypes.c_size_t(0)
+    _check(lib().jfa_workspace_size(ctypes.byref(shape), mode, pass_, ctypes.byref(opts) if opts else None,
+                                    ctypes.byref(n)), "jfa_workspace_size")
+    return int(n.value)
+
+
+def schedule(shape, mode, pass_, offsets_host, opts=None):
+    """Host tile schedule: (tiles [N,3] int32, seg_ptr int32, programs, tile_rows)."""
+    off = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    L = lib()
+    n_tiles, n_segs = ctypes.c_int64(0), ctypes.c_int32(0)
+    n_prog, rows = ctypes.c_int32(0), ctypes.c_int32(0)
+    o = ctypes.byref(opts) if opts else None
+    _check(L.jfa_schedule(ctypes.byref(shape), mode, pass_, off.ctypes.data, o, None, 0, None, 0,
+                          ctypes.byref(n_tiles), ctypes.byref(n_segs), ctypes.byref(n_prog), ctypes.byref(rows)),
+           "jfa_schedule")
+    tiles = np.zeros((max(1, n_tiles.value), 3), dtype=np.int32)
+    seg = np.zeros(max(1, n_segs.value), dtype=np.int32)
+    _check(L.jfa_schedule(ctypes.byref(shape), mode, pass_, off.ctypes.data, o, tiles.ctypes.data, tiles.shape[0],
+                          seg.ctypes.data, seg.shape[0], ctypes.byref(n_tiles), ctypes.byref(n_segs),
+                          ctypes.byref(n_prog), ctypes.byref(rows)), "jfa_schedule")
+    return tiles[: n_tiles.value], seg[: n_segs.value], n_prog.value, rows.value
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensor(name, t, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _sizes(q, k, offsets, mode, num_q):
+    total, num_heads, head_dim = k.shape
+    nb = offsets.numel() - 1
+    mq = q.shape[0] if mode == MODE_BROADCAST_Q else 0
+    if mode == MODE_BROADCAST_Q and num_q and num_q != mq:
+        raise ValueError("num_q differs from q.shape[0]")
+    return nb, num_heads, head_dim, total, mq
+
+
+def alloc_workspace(shape, mode, pass_, opts, device):
+    import torch
+    n = workspace_size(shape, mode, pass_, opts)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, offsets, offsets_host=None, mode=MODE_SELF, scale=None, opts=None, o=None, lse=None,
+        workspace=None, stream=None):
+    """Forward.  Returns (o, lse) with the layouts of include/jfa.h."""
+    import torch
+    nb, h, d, t, mq = _sizes(q, k, offsets, mode, 0)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, mq)
+    if mode == MODE_BROADCAST_Q:
+        o_shape, lse_shape = (nb, mq, h, d), (nb, h, mq)
+    else:
+        o_shape, lse_shape = (t, h, d), (h, t)
+    if o is None:
+        o = torch.empty(o_shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, torch.bfloat16, o_shape)
+    _check_tensor("lse", lse, torch.float32, lse_shape)
+    if workspace is None:
+        workspace = alloc_workspace(shape, mode, PASS_FWD, opts, q.device)
+    host = None
+    if offsets_host is not None:
+        host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_fwd(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                         host.ctypes.data if host is not None else None, _ptr(o), _ptr(lse), _ptr(workspace),
+                         workspace.numel(), ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, offsets, offsets_host=None, mode=MODE_SELF, scale=None, opts=None, dq=None,
+        dk=None, dv=None, workspace=None, stream=None):
+    """Backward.  Returns (dq, dk, dv) with the shapes of (q, k, v)."""
+    import torch
+    nb, h, d, t, mq = _sizes(q, k, offsets, mode, 0)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("lse", lse, torch.float32)
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, mq)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = alloc_workspace(shape, mode, PASS_BWD, opts, q.device)
+    host = None
+    if offsets_host is not None:
+        host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_bwd(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                         _ptr(offsets), host.ctypes.data if host is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
+                         _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts else None,
+                         _stream(stream)), "jfa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,502 @@
+// C ABI of the jagged flash attention library: argument checks, offsets intake, host
+// scheduling, workspace layout, schedule upload and kernel launches.
+//
+// Offsets intake follows the jagged layout of the explore.n1n.ai page (section on the
+// performance defects of padded tensors): offsets[0] = 0, non-decreasing, offsets[B]
+// = T.  When the caller passes host offsets, every scalar of the schedule is computed
+// on the host before launch with no device synchronisation (bittide page, section 5).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "jfa.h"
+#include "jfa_internal.h"
+#include "jfa_sched.h"
+
+using namespace jfa;
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(JFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (256 if no device is visible: host-only use).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Opts {
+  int sched = 0, dq_path = 0, num_programs = 0;
+};
+
+int check_opts(const jfa_opts* o, Opts& out) {
+  out = Opts();
+  if (!o) return JFA_OK;
+  if (o->sched != 0 && o->sched != 1) return fail(JFA_ERR_BAD_OPTION, "opts.sched must be 0 or 1");
+  if (o->dq_path != 0 && o->dq_path != 1) return fail(JFA_ERR_BAD_OPTION, "opts.dq_path must be 0 or 1");
+  if (o->num_programs < 0 || o->num_programs > (1 << 20))
+    return fail(JFA_ERR_BAD_OPTION, "opts.num_programs out of range");
+  if (o->reserved != 0) return fail(JFA_ERR_BAD_OPTION, "opts.reserved must be 0");
+  out.sched = o->sched;
+  out.dq_path = o->dq_path;
+  out.num_programs = o->num_programs;
+  return JFA_OK;
+}
+
+int check_shape(const jfa_shape* s, int mode) {
+  if (!s) return fail(JFA_ERR_NULL_POINTER, "shape is NULL");
+  if (mode != JFA_MODE_SELF && mode != JFA_MODE_BROADCAST_Q && mode != JFA_MODE_BLOCK_DIAG)
+    return fail(JFA_ERR_BAD_MODE, "mode %d is not a jfa_mode", mode);
+  if (s->num_seqs < 0) return fail(JFA_ERR_BAD_SHAPE, "num_seqs < 0");
+  if (s->num_heads < 1 || s->num_heads > 127) return fail(JFA_ERR_BAD_SHAPE, "num_heads must be in [1, 127]");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(JFA_ERR_BAD_HEAD_DIM, "head_dim %d not in {64, 128}", s->head_dim);
+  if (s->total_tokens < 0) return fail(JFA_ERR_BAD_SHAPE, "total_tokens < 0");
+  if (mode == JFA_MODE_BROADCAST_Q && s->num_q < 1) return fail(JFA_ERR_BAD_SHAPE, "num_q < 1 in broadcast-Q mode");
+  // 32-bit limits: block indices < 2^24 in the tile encoding, tile counts < 2^31.
+  if (s->total_tokens >= (int64_t(1) << 30)) return fail(JFA_ERR_TOO_LARGE, "total_tokens >= 2^30");
+  if (mode == JFA_MODE_BROADCAST_Q && s->num_q >= (1 << 24)) return fail(JFA_ERR_TOO_LARGE, "num_q >= 2^24");
+  if (mode == JFA_MODE_BROADCAST_Q && (int64_t)s->num_seqs * s->num_q >= (int64_t(1) << 31))
+    return fail(JFA_ERR_TOO_LARGE, "num_seqs * num_q >= 2^31");
+  return JFA_OK;
+}
+
+int max_programs(const Opts& o, int wg_per_cu) {
+  return o.num_programs > 0 ? o.num_programs : device_cus() * wg_per_cu;
+}
+
+// Workspace layout (byte offsets, each region 256-byte aligned).
+struct Layout {
+  size_t counters = 0, seg = 0, tiles = 0, prefix = 0, acc = 0, total = 0;
+  int64_t seg_cap = 0, tile_cap = 0;
+  int programs_cap = 0;
+};
+
+void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L) {
+  const int64_t B = s->num_seqs, H = s->num_heads, D = s->head_dim, T = s->total_tokens;
+  const int64_t Mq = s->num_q;
+  size_t at = 0;
+  L.counters = at;
+  at += align_up(64 * sizeof(int32_t));
+  if (mode == JFA_MODE_BLOCK_DIAG) {
+    L.prefix = at;
+    at += align_up((B + 1) * sizeof(int32_t));
+    L.total = at;
+    return;
+  }
+  const int wg = pass == JFA_PASS_FWD ? kFwdWgPerCu : kBwdWgPerCu;
+  L.programs_cap = max_programs(o, wg);
+  L.seg_cap = std::max<int64_t>(L.programs_cap, H) + 1;
+  L.seg = at;
+  at += align_up(L.seg_cap * sizeof(int32_t));
+  if (pass == JFA_PASS_FWD) {
+    L.tile_cap = (mode == JFA_MODE_BROADCAST_Q) ? H * B * cdiv(Mq, kFwdRows) : H * (T / kFwdRows + B + 1);
+  } else {
+    L.tile_cap = H * (T / kBwdKeys + B + 1);
+  }
+  L.tiles = at;
+  at += align_up(L.tile_cap * sizeof(Tile));
+  if (pass == JFA_PASS_BWD) {
+    L.acc = at;
+    int64_t acc_elems;
+    if (mode == JFA_MODE_SELF)
+      acc_elems = T * H * D;
+    else if (o.dq_path == 0)
+      acc_elems = Mq * H * D;
+    else
+      acc_elems = (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
+    at += align_up(acc_elems * sizeof(float));
+  }
+  L.total = at;
+}
+
+// Lengths from host offsets (or the device copy on the slow path), validated.
+int intake_offsets(const jfa_shape* s, const int32_t* off_dev, const int32_t* off_host,
+                   hipStream_t stream, std::vector<int32_t>& lengths) {
+  const int B = s->num_seqs;
+  std::vector<int32_t> tmp;
+  const int32_t* off = off_host;
+  if (!off) {
+    if (!off_dev) return fail(JFA_ERR_NULL_POINTER, "offsets_dev and offsets_host are both NULL");
+    tmp.resize(B + 1);
+    hipError_t e = hipMemcpyAsync(tmp.data(), off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "copying device offsets to the host");
+    off = tmp.data();
+  }
+  if (off[0] != 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets[0] = %d, must be 0", off[0]);
+  lengths.resize(B);
+  for (int b = 0; b < B; ++b) {
+    if (off[b + 1] < off[b]) return fail(JFA_ERR_BAD_OFFSETS, "offsets decrease at index %d", b + 1);
+    lengths[b] = off[b + 1] - off[b];
+  }
+  if ((int64_t)off[B] != s->total_tokens)
+    return fail(JFA_ERR_BAD_OFFSETS, "offsets[B] = %d differs from total_tokens = %lld", off[B],
+                (long long)s->total_tokens);
+  return JFA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Pinned host staging ring for the asynchronous schedule upload.  A slot is reused
+// only after the copy that last read it has completed (its event).
+struct StagingRing {
+  static constexpr int kSlots = 8;
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  } slot[kSlots];
+  int next = 0;
+  std::mutex mu;
+};
+StagingRing g_ring[64];
+
+// Copy `bytes` from `src` into the workspace at `dst` on `stream` via a pinned slot.
+int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  if (bytes == 0) return JFA_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return hip_fail(e, "hipGetDevice");
+  StagingRing& ring = g_ring[dev];
+  std::lock_guard<std::mutex> lock(ring.mu);
+  StagingRing::Slot& s = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % StagingRing::kSlots;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return hip_fail(e, "waiting for a staging slot");
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (s.cap < bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 1 << 16);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
+    s.cap = cap;
+  }
+  memcpy(s.host, src, bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "uploading the schedule");
+  e = hipEventRecord(s.ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  s.pending = true;
+  return JFA_OK;
+}
+
+// Serialise [counters | seg_ptr | tiles] of a schedule for the device.
+void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf) {
+  const size_t tiles_bytes = sc.tiles.size() * sizeof(Tile);
+  buf.assign(L.tiles + tiles_bytes, 0);
+  memcpy(buf.data() + L.seg, sc.seg_ptr.data(), sc.seg_ptr.size() * sizeof(int32_t));
+  Tile* t = reinterpret_cast<Tile*>(buf.data() + L.tiles);
+  for (size_t i = 0; i < sc.tiles.size(); ++i)
+    t[i] = Tile{sc.tiles[i].b, (sc.tiles[i].h << 24) | sc.tiles[i].blk};
+}
+
+int launch_status(hipError_t e, const char* what) {
+  return e == hipSuccess ? JFA_OK : hip_fail(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int jfa_version(void) { return JFA_VERSION; }
+
+const char* jfa_last_error_detail(void) { return g_detail.c_str(); }
+
+const char* jfa_error_string(int code) {
+  switch (code) {
+    case JFA_OK: return "success";
+    case JFA_ERR_NULL_POINTER: return "a required pointer argument is NULL";
+    case JFA_ERR_BAD_SHAPE: return "invalid problem shape";
+    case JFA_ERR_BAD_HEAD_DIM: return "head_dim must be 64 or 128";
+    case JFA_ERR_BAD_MODE: return "invalid mode or pass";
+    case JFA_ERR_BAD_OFFSETS: return "invalid offsets (offsets[0] != 0, decreasing, or offsets[B] != T)";
+    case JFA_ERR_MISALIGNED: return "a tensor or the workspace is misaligned";
+    case JFA_ERR_WORKSPACE: return "workspace too small";
+    case JFA_ERR_BAD_OPTION: return "invalid option";
+    case JFA_ERR_TOO_LARGE: return "problem exceeds the 32-bit tile indexing";
+    case JFA_ERR_HIP: return "HIP runtime error";
+    case JFA_ERR_CAPACITY: return "output array too small";
+    default: return "unknown status code";
+  }
+}
+
+int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opts* opts, size_t* bytes) {
+  g_detail.clear();
+  int rc = check_shape(shape, mode);
+  if (rc) return rc;
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return fail(JFA_ERR_BAD_MODE, "pass must be 0 or 1");
+  if (!bytes) return fail(JFA_ERR_NULL_POINTER, "bytes is NULL");
+  Opts o;
+  if ((rc = check_opts(opts, o))) return rc;
+  Layout L;
+  layout_for(shape, mode, pass, o, L);
+  *bytes = L.total;
+  return JFA_OK;
+}
+
+int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,
+                 const jfa_opts* opts, int32_t* tiles, int64_t cap, int32_t* seg_ptr, int64_t seg_cap,
+                 int64_t* n_tiles, int32_t* n_segs, int32_t* n_programs, int32_t* tile_rows) {
+  g_detail.clear();
+  int rc = check_shape(shape, mode);
+  if (rc) return rc;
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return fail(JFA_ERR_BAD_MODE, "pass must be 0 or 1");
+  if (!offsets_host) return fail(JFA_ERR_NULL_POINTER, "jfa_schedule needs host offsets");
+  Opts o;
+  if ((rc = check_opts(opts, o))) return rc;
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, nullptr, offsets_host, nullptr, lengths))) return rc;
+  Schedule sc;
+  const bool dyn = o.sched == 1;
+  if (mode == JFA_MODE_BLOCK_DIAG)
+    schedule_blockdiag(lengths, shape->num_heads, kBlock, max_programs(o, kBdWgPerCu), sc);
+  else if (pass == JFA_PASS_FWD)
+    schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
+  else
+    schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys, max_programs(o, kBwdWgPerCu), dyn, sc);
+  if (n_tiles) *n_tiles = (int64_t)sc.tiles.size();
+  if (n_segs) *n_segs = (int32_t)sc.seg_ptr.size();
+  if (n_programs) *n_programs = sc.programs;
+  if (tile_rows) *tile_rows = sc.tile_rows;
+  if (tiles) {
+    if (cap < (int64_t)sc.tiles.size()) return fail(JFA_ERR_CAPACITY, "tiles capacity %lld < %zu", (long long)cap, sc.tiles.size());
+    for (size_t i = 0; i < sc.tiles.size(); ++i) {
+      tiles[3 * i] = sc.tiles[i].b;
+      tiles[3 * i + 1] = sc.tiles[i].h;
+      tiles[3 * i + 2] = sc.tiles[i].blk;
+    }
+  }
+  if (seg_ptr) {
+    if (seg_cap < (int64_t)sc.seg_ptr.size()) return fail(JFA_ERR_CAPACITY, "seg_ptr capacity too small");
+    memcpy(seg_ptr, sc.seg_ptr.data(), sc.seg_ptr.size() * sizeof(int32_t));
+  }
+  return JFA_OK;
+}
+
+int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+            const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse, void* workspace,
+            size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_shape(shape, mode);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q || !k || !v || !o || !lse || !offsets_dev || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "q, k, v, o, lse, offsets_dev and workspace must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(JFA_ERR_MISALIGNED, "q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  Layout L;
+  layout_for(shape, mode, JFA_PASS_FWD, op, L);
+  if (workspace_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  char* ws = (char*)workspace;
+  const int H = shape->num_heads, D = shape->head_dim;
+
+  if (mode == JFA_MODE_BLOCK_DIAG) {
+    std::vector<int32_t> prefix(shape->num_seqs + 1, 0);
+    for (int b = 0; b < shape->num_seqs; ++b) prefix[b + 1] = prefix[b] + (int32_t)cdiv(lengths[b], kBlock);
+    const int64_t ntiles = (int64_t)prefix.back() * H;
+    if (ntiles == 0) return JFA_OK;
+    if ((rc = upload(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix, stream))) return rc;
+    BdParams p{};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.offsets = offsets_dev;
+    p.blk_prefix = (const int32_t*)(ws + L.prefix);
+    p.num_seqs = shape->num_seqs;
+    p.num_heads = H;
+    p.total_tokens = shape->total_tokens;
+    p.num_tiles = ntiles;
+    p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2eHost;
+    return launch_status(launch_bd_fwd(p, D, stream), "block-diagonal forward launch");
+  }
+
+  Schedule sc;
+  schedule_fwd(lengths, H, mode, shape->num_q, kFwdRows, max_programs(op, kFwdWgPerCu), op.sched == 1, sc);
+  if (sc.tiles.empty()) return JFA_OK;
+  if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  std::vector<char> buf;
+  serialise(sc, L, buf);
+  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.offsets = offsets_dev;
+  p.tiles = (const Tile*)(ws + L.tiles);
+  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.counters = (int32_t*)(ws + L.counters);
+  p.num_seqs = shape->num_seqs;
+  p.num_heads = H;
+  p.num_q = shape->num_q;
+  p.num_programs = sc.programs;
+  p.total_tokens = shape->total_tokens;
+  p.dynamic = op.sched;
+  p.scale_log2 = scale * kLog2eHost;
+  return launch_status(launch_fwd(p, mode, D, stream), "forward launch");
+}
+
+int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+            const void* o, const void* dout, const float* lse, const int32_t* offsets_dev,
+            const int32_t* offsets_host, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_shape(shape, mode);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q || !k || !v || !o || !dout || !lse || !offsets_dev || !dq || !dk || !dv || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "tensor, offsets_dev and workspace pointers must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return fail(JFA_ERR_MISALIGNED, "bf16 tensors must be 16-byte aligned and lse 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  Layout L;
+  layout_for(shape, mode, JFA_PASS_BWD, op, L);
+  if (workspace_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  char* ws = (char*)workspace;
+  const int H = shape->num_heads, D = shape->head_dim;
+  const int64_t T = shape->total_tokens;
+
+  if (mode == JFA_MODE_BLOCK_DIAG) {
+    std::vector<int32_t> prefix(shape->num_seqs + 1, 0);
+    for (int b = 0; b < shape->num_seqs; ++b) prefix[b + 1] = prefix[b] + (int32_t)cdiv(lengths[b], kBlock);
+    const int64_t ntiles = (int64_t)prefix.back() * H;
+    if (ntiles == 0) return JFA_OK;
+    if ((rc = upload(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix, stream))) return rc;
+    BdParams p{};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o_in = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse_in = lse;
+    p.o = (uint16_t*)dq;
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    p.offsets = offsets_dev;
+    p.blk_prefix = (const int32_t*)(ws + L.prefix);
+    p.num_seqs = shape->num_seqs;
+    p.num_heads = H;
+    p.total_tokens = T;
+    p.num_tiles = ntiles;
+    p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2eHost;
+    return launch_status(launch_bd_bwd(p, D, stream), "block-diagonal backward launch");
+  }
+
+  Schedule sc;
+  schedule_bwd(lengths, H, mode, kBwdKeys, max_programs(op, kBwdWgPerCu), op.sched == 1, sc);
+  if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  const bool bq = mode == JFA_MODE_BROADCAST_Q;
+  const bool partials = bq && op.dq_path == 1;
+  const int64_t Mq = shape->num_q;
+  float* acc = (float*)(ws + L.acc);
+  const int ph = bq ? std::max(1, sc.programs / H) : 0;
+  const int64_t acc_elems = !bq ? T * H * D : (partials ? (int64_t)ph * H * Mq * D : Mq * H * D);
+  if (sc.tiles.empty() && !bq) return JFA_OK;
+  if (!sc.tiles.empty()) {
+    std::vector<char> buf;
+    serialise(sc, L, buf);
+    if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  }
+  if ((rc = launch_status(launch_fill_zero(acc, acc_elems, stream), "dq accumulator fill"))) return rc;
+  if (!sc.tiles.empty()) {
+    BwdParams p{};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o;
+    p.dout = (const uint16_t*)dout;
+    p.lse = lse;
+    p.offsets = offsets_dev;
+    p.tiles = (const Tile*)(ws + L.tiles);
+    p.seg_ptr = (const int32_t*)(ws + L.seg);
+    p.counters = (int32_t*)(ws + L.counters);
+    p.dk = (uint16_t*)dk;
+    p.dv = (uint16_t*)dv;
+    p.dq_acc = acc;
+    p.num_seqs = shape->num_seqs;
+    p.num_heads = H;
+    p.num_q = shape->num_q;
+    p.num_programs = sc.programs;
+    p.total_tokens = T;
+    p.dynamic = op.sched;
+    p.dq_partials = partials ? 1 : 0;
+    p.programs_per_head = ph;
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2eHost;
+    if ((rc = launch_status(launch_bwd(p, mode, D, stream), "backward launch"))) return rc;
+  }
+  if (partials)
+    return launch_status(launch_dq_reduce(acc, (uint16_t*)dq, (int)Mq, H, D, ph, scale, stream), "dq reduce");
+  return launch_status(launch_cast_scale(acc, (uint16_t*)dq, acc_elems, scale, stream), "dq cast");
+}
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// Block-diagonal jagged attention (fixed 64-token blocks) for gfx950, forward and
+// backward.
+//
+// What it computes ("TLX Block Attention", bittide page, sections 1, 2.1 and 4): every
+// sequence is cut into consecutive 64-token groups that attend only within
+// themselves.  With one query tile matching exactly one key/value tile, the forward is
+// a single S = Q K^T, a direct softmax (no running maximum, no correction factor, no
+// loop) and a single O = P V; the backward rebuilds P for the one tile, forms
+// Di = rowsum(dO * O) inline and finishes dQ, dK and dV of the block with no
+// cross-tile accumulation.  A trailing partial block of a sequence attends within
+// itself.
+//
+// How it maps to CDNA4: the work is memory bound (about 32 FLOP per byte at D=64, the
+// same point the page makes for its own kernel in section 3.3), so one wave owns one
+// (block, head) tile and the grid is persistent with balanced contiguous tile ranges
+// computed in closed form from divmod (same page, section 5).  Tiles are numbered with
+// the head fastest so the waves of a workgroup read one contiguous 64-token slab.
+// A tile's sequence is found with a fixed-step binary search over the per-sequence
+// block prefix sums.  Differences from the page's kernel: the backward reads the
+// forward's lse (4 bytes per row, about 1% of the traffic) instead of recomputing the
+// row maxima, because on this layout the keys of a row are spread across lanes.
+#include "jfa_device.h"
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+template <int D>
+struct BdCfg {
+  static constexpr int NW = (D == 64) ? 4 : 2;  // waves per workgroup (LDS budget)
+  static constexpr int RB = 2 * D;
+  static constexpr int NKS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int TBUF = kBlock * RB;       // one 64-row tile
+  static constexpr int SRB = 2 * kBlock;         // dS^T row bytes
+  static constexpr int SBUF = kBlock * SRB;
+  // backward per-wave LDS: Q, K, dO tiles, dS^T, lse2[64], Di[64]
+  static constexpr int W_Q = 0, W_K = TBUF, W_DO = 2 * TBUF, W_S = 3 * TBUF, W_LSE = 3 * TBUF + SBUF,
+                       W_DI = W_LSE + 256, W_BWD = W_DI + 256;
+};
+
+struct BdTile {
+  int64_t t0;  // first token of the block
+  int n;       // rows in the block (1..64)
+  int h;
+};
+
+// Tile g -> (block, head); block -> (sequence b, block j) by binary search over the
+// per-sequence block prefix sums.
+__device__ __forceinline__ BdTile locate(const BdParams& p, int64_t g) {
+  const int H = p.num_heads;
+  const int blk = (int)(g / H);
+  BdTile t;
+  t.h = (int)(g % H);
+  int lo = 0, hi = p.num_seqs;  // prefix[lo] <= blk < prefix[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.blk_prefix[mid] <= blk) lo = mid; else hi = mid;
+  }
+  const int j = blk - p.blk_prefix[lo];
+  const int64_t s0 = p.offsets[lo];
+  const int L = (int)(p.offsets[lo + 1] - s0);
+  t.t0 = s0 + (int64_t)j * kBlock;
+  t.n = min(kBlock, L - j * kBlock);
+  return t;
+}
+
+template <int D>
+__device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* vt, int lane) {
+  using C = BdCfg<D>;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t base = t.t0 * rs + (int64_t)t.h * D;
+  const int n = t.n;
+  const float c = p.scale_log2;
+  dma_tile<C::RB, kBlock, 1>(p.v + base, rs, n, vt, 0, lane);
+
+  bf16x8 qf[2][C::NKS], kf[2][C::NKS];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int row = bb * 32 + l32;
+    const uint16_t* qp = p.q + base + row * rs + 8 * half;
+    const uint16_t* kp = p.k + base + row * rs + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      qf[bb][ks] = as_bf16x8(row < n ? ld16(qp + 16 * ks) : zero16());
+      kf[bb][ks] = as_bf16x8(row < n ? ld16(kp + 16 * ks) : zero16());
+    }
+  }
+  // S^T = K Q^T, lane = query column.
+  f32x16 s[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) s[kb][qb] = mfma32(kf[kb][ks], qf[qb][ks], s[kb][qb]);
+    }
+  // Direct softmax over the block's keys.
+  float m[2], l[2];
+  bf16x8 pf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (key >= n) s[kb][qb][i] = -INFINITY;
+        mx = fmaxf(mx, s[kb][qb][i]);
+      }
+    m[qb] = half_max(mx);
+    const float mc = m[qb] * c;
+    float sum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(fmaf(s[kb][qb][i], c, -mc));
+        s[kb][qb][i] = pv;
+        sum += pv;
+      }
+    l[qb] = half_sum(sum);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x16& src = s[tt >> 1][qb];
+      const int r = 8 * (tt & 1);
+      pf[qb][tt] = pack8(src[r], src[r + 1], src[r + 2], src[r + 3], src[r + 4], src[r + 5], src[r + 6],
+                         src[r + 7]);
+    }
+  }
+  wait_vmem();
+  // O^T = V^T P^T.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qb * 32 + l32;
+    const float inv = 1.0f / l[qb];
+    f32x16 o[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) o[db] = mfma32(tr_operand<C::RB>(vt, 16 * tt, 32 * db, lane), pf[qb][tt], o[db]);
+    }
+    if (row < n) {
+      uint16_t* op = p.o + base + row * rs + 4 * half;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          st8(op + 32 * db + 8 * g4, pack4(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                                          o[db][4 * g4 + 3] * inv));
+      if (half == 0) p.lse[(int64_t)t.h * p.total_tokens + t.t0 + row] = (m[qb] * c + fast_log2(l[qb])) * kLn2;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* w, float* wf,
+                                            int lane) {
+  using C = BdCfg<D>;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t base = t.t0 * rs + (int64_t)t.h * D;
+  const int n = t.n;
+  const float c = p.scale_log2;
+  JFA_LDS char* qt = w + C::W_Q;
+  JFA_LDS char* kt = w + C::W_K;
+  JFA_LDS char* dot = w + C::W_DO;
+  JFA_LDS char* st = w + C::W_S;
+  float* lse2 = wf + C::W_LSE / 4;
+  float* di = wf + C::W_DI / 4;
+  dma_tile<C::RB, kBlock, 1>(p.q + base, rs, n, qt, 0, lane);
+  dma_tile<C::RB, kBlock, 1>(p.k + base, rs, n, kt, 0, lane);
+  dma_tile<C::RB, kBlock, 1>(p.dout + base, rs, n, dot, 0, lane);
+  const float lv = lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f;
+  wait_vmem();
+  // Di = rowsum(dO * O): lane = row of query block qb, half = which 8-column chunks.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qb * 32 + l32;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 d8 = as_bf16x8(lds_ld16(dot, swz_off<C::RB>(row, 2 * ks + half)));
+      const bf16x8 o8 = as_bf16x8(row < n ? ld16(p.o_in + base + row * rs + 16 * ks + 8 * half) : zero16());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)d8[e], (float)o8[e], acc);
+    }
+    acc = half_sum(acc);
+    if (half == 0) di[row] = acc;
+  }
+  lse2[lane] = lane < n ? lv * kLog2e : INFINITY;
+
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kb * 32 + l32;
+    const bool key_ok = key < n;
+    bf16x8 kf[C::NKS], vf[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      kf[ks] = as_bf16x8(lds_ld16(kt, swz_off<C::RB>(key, 2 * ks + half)));
+      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + key * rs + 16 * ks + 8 * half) : zero16());
+    }
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[qb][i] = dp[qb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        const int off = swz_off<C::RB>(qb * 32 + l32, 2 * ks + half);
+        s[qb] = mfma32(as_bf16x8(lds_ld16(qt, off)), kf[ks], s[qb]);
+        dp[qb] = mfma32(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp[qb]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r4 = qb * 32 + 8 * g4 + 4 * half;
+        const float4 la = *reinterpret_cast<const float4*>(lse2 + r4);
+        const float4 da = *reinterpret_cast<const float4*>(di + r4);
+        const float lz[4] = {la.x, la.y, la.z, la.w}, dz[4] = {da.x, da.y, da.z, da.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float pv = fast_exp2(fmaf(s[qb][i], c, -lz[e]));
+          pv = key_ok ? pv : 0.f;
+          s[qb][i] = pv;
+          dp[qb][i] = pv * (dp[qb][i] - dz[e]);
+        }
+      }
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int qb = tt >> 1, r = 8 * (tt & 1);
+      pf[tt] = pack8(s[qb][r], s[qb][r + 1], s[qb][r + 2], s[qb][r + 3], s[qb][r + 4], s[qb][r + 5], s[qb][r + 6],
+                     s[qb][r + 7]);
+      dsf[tt] = pack8(dp[qb][r], dp[qb][r + 1], dp[qb][r + 2], dp[qb][r + 3], dp[qb][r + 4], dp[qb][r + 5],
+                      dp[qb][r + 6], dp[qb][r + 7]);
+    }
+    // dS^T rows of these keys -> LDS for the dQ product.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int q = qb * 32 + 8 * g4 + 4 * half;
+        lds_st8(st, swz_off<C::SRB>(key, q >> 3) + (q & 7) * 2,
+                pack4(dp[qb][4 * g4], dp[qb][4 * g4 + 1], dp[qb][4 * g4 + 2], dp[qb][4 * g4 + 3]));
+      }
+    // dV^T = dO^T P and dK^T = Q^T dS for these 32 keys; complete after the single block.
+    f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        dv[db] = mfma32(tr_operand<C::RB>(dot, 16 * tt, 32 * db, lane), pf[tt], dv[db]);
+        dk[db] = mfma32(tr_operand<C::RB>(qt, 16 * tt, 32 * db, lane), dsf[tt], dk[db]);
+      }
+    }
+    if (key_ok) {
+      const int64_t row = base + key * rs + 4 * half;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * db + 8 * g4;
+          st8(p.dk + row + d, pack4(dk[db][4 * g4] * p.scale, dk[db][4 * g4 + 1] * p.scale,
+                                    dk[db][4 * g4 + 2] * p.scale, dk[db][4 * g4 + 3] * p.scale));
+          st8(p.dv + row + d, pack4(dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]));
+        }
+    }
+  }
+  // dQ^T = K^T dS^T: [head dim x queries], k = keys; lane = query column.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qb * 32 + l32;
+    f32x16 dq[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        dq[db] = mfma32(tr_operand<C::RB>(kt, 16 * tt, 32 * db, lane), tr_operand<C::SRB>(st, 16 * tt, 32 * qb, lane),
+                        dq[db]);
+    }
+    if (row < n) {
+      uint16_t* qp = p.o + base + row * rs + 4 * half;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          st8(qp + 32 * db + 8 * g4, pack4(dq[db][4 * g4] * p.scale, dq[db][4 * g4 + 1] * p.scale,
+                                          dq[db][4 * g4 + 2] * p.scale, dq[db][4 * g4 + 3] * p.scale));
+    }
+  }
+}
+
+// Program p owns tiles [p*q + min(p, r), (p+1)*q + min(p+1, r)), (q, r) = divmod(N, P);
+// its waves take every NW-th tile of the range.
+template <int D>
+__global__ void __launch_bounds__(BdCfg<D>::NW * 64) bd_fwd_kernel(BdParams p) {
+  using C = BdCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::NW * C::TBUF];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  const int64_t P = gridDim.x, q = p.num_tiles / P, r = p.num_tiles % P;
+  const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
+  JFA_LDS char* vt = (JFA_LDS char*)smem + wave * C::TBUF;
+  for (int64_t g = start + wave; g < end; g += C::NW) bd_fwd_tile<D>(p, locate(p, g), vt, lane);
+}
+
+template <int D>
+__global__ void __launch_bounds__(BdCfg<D>::NW * 64)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) bd_bwd_kernel(BdParams p) {
+  using C = BdCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::NW * C::W_BWD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  const int64_t P = gridDim.x, q = p.num_tiles / P, r = p.num_tiles % P;
+  const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
+  char* w = smem + wave * C::W_BWD;
+  for (int64_t g = start + wave; g < end; g += C::NW)
+    bd_bwd_tile<D>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
+}
+
+int bd_programs(const BdParams& p, int nw) {
+  const int64_t need = (p.num_tiles + nw - 1) / nw;
+  return (int)(need < p.num_programs ? need : p.num_programs);
+}
+
+}  // namespace
+
+hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s) {
+  if (p.num_tiles <= 0) return hipSuccess;
+  if (head_dim == 64) {
+    hipLaunchKernelGGL(bd_fwd_kernel<64>, dim3(bd_programs(p, BdCfg<64>::NW)), dim3(BdCfg<64>::NW * 64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(bd_fwd_kernel<128>, dim3(bd_programs(p, BdCfg<128>::NW)), dim3(BdCfg<128>::NW * 64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s) {
+  if (p.num_tiles <= 0) return hipSuccess;
+  if (head_dim == 64) {
+    hipLaunchKernelGGL(bd_bwd_kernel<64>, dim3(bd_programs(p, BdCfg<64>::NW)), dim3(BdCfg<64>::NW * 64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(bd_bwd_kernel<128>, dim3(bd_programs(p, BdCfg<128>::NW)), dim3(BdCfg<128>::NW * 64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace jfa

@@ -1,0 +1,159 @@
+// Device-side building blocks for the gfx950 (CDNA4) kernels: MFMA operand types,
+// LDS transposed reads, bf16 packing, wave-level exchanges and the XCD-aware
+// program numbering.  Internal header; not part of the C ABI.
+//
+// Lane layouts (wave64) of the two matrix instructions used here, for A (m x k),
+// B (k x n), C (m x n), with lane l, half = l / 32:
+//   v_mfma_f32_32x32x16_bf16: A slot j -> (m = l % 32, k = 8*half + j), j < 8
+//                             B slot j -> (k = 8*half + j, n = l % 32)
+//                             C reg  i -> (m = 8*(i/4) + 4*half + i%4, n = l % 32), i < 16
+// ds_read_b64_tr_b16 (per 16-lane group, source lane s reads 4 consecutive bf16 at its
+// own address): result lane i, element j = element (i & 3) read by source lane
+// (i >> 2) + 4*j.  With source lane s pointing at row r0 + (s >> 2), column c0 + 4*(s & 3)
+// of a row-major tile, result lane i holds column c0 + i of rows r0 .. r0+3: a
+// transposed fetch of a 4 x 16 block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define JFA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// 16-byte global load / store.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// LDS 16-byte read / write (byte offsets into a __shared__ array).
+__device__ __forceinline__ u32x4 lds_ld16(const JFA_LDS char* base, int byte_off) {
+  return *reinterpret_cast<const JFA_LDS u32x4*>(base + byte_off);
+}
+__device__ __forceinline__ void lds_st16(JFA_LDS char* base, int byte_off, const u32x4& v) {
+  *reinterpret_cast<JFA_LDS u32x4*>(base + byte_off) = v;
+}
+__device__ __forceinline__ void lds_st8(JFA_LDS char* base, int byte_off, const u32x2& v) {
+  *reinterpret_cast<JFA_LDS u32x2*>(base + byte_off) = v;
+}
+
+// Direct global -> LDS copy (global_load_lds_dwordx4): every lane fetches 16 bytes
+// from its own global address; the wave's 64 results land contiguously at
+// lds_base + 16 * lane.  lds_base must be the same for the whole wave.  Completion is
+// tracked by vmcnt: wait_vmem() then a barrier before any wave reads the data.
+__device__ __forceinline__ void dma16(const void* gptr, JFA_LDS char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (JFA_LDS void*)lds_base, 16, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposed 4 x 16 fetch (see the header comment); `byte_off` is this lane's source
+// address.
+__device__ __forceinline__ v4i16 lds_tr4(const JFA_LDS char* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (JFA_LDS v4i16*)(const_cast<JFA_LDS char*>(base) + byte_off));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const v4i16& lo, const v4i16& hi) {
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Pack 8 fp32 values into a bf16x8 operand (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+  bf16x8 r = {(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3, (bf16)a4, (bf16)a5, (bf16)a6, (bf16)a7};
+  return r;
+}
+
+__device__ __forceinline__ u32x2 pack4(float a0, float a1, float a2, float a3) {
+  bf16x4 r = {(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3};
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Combine a per-lane value with the same lane of the other wave half (lane ^ 32) via
+// v_permlane32_swap: both halves get op(x[l], x[l ^ 32]).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Swizzled row-major tiles in LDS: a tile row of RB bytes holds RB/16 chunks of 16
+// bytes; chunk c of row r is stored at chunk position c ^ (r mod RB/16), so that the
+// rows read together by one MFMA operand fetch fall on different LDS banks.
+template <int RB>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  constexpr int CPR = RB / 16;
+  return r * RB + ((c ^ (r & (CPR - 1))) << 4);
+}
+
+// Copy ROWS rows of RB bytes (a row starts every `row_stride` elements at `g`) into a
+// swizzled LDS tile with the 1 KB wave-wide direct copies, split over NW waves.  Rows
+// at or past `rows_valid` repeat row rows_valid-1, so every read stays inside the
+// caller's valid rows; the caller masks their contribution.
+template <int RB, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(const uint16_t* g, int64_t row_stride, int rows_valid,
+                                         JFA_LDS char* lds, int wave, int lane) {
+  constexpr int CPR = RB / 16;
+  constexpr int RPC = 1024 / RB;            // rows per copy
+  constexpr int COPIES = ROWS * RB / 1024;  // copies per tile
+  static_assert(COPIES % NW == 0, "copies must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < COPIES / NW; ++j) {
+    const int gi = wave * (COPIES / NW) + j;
+    const int r = gi * RPC + lane / CPR;
+    const int c = (lane % CPR) ^ (r & (CPR - 1));
+    dma16(g + (int64_t)min(r, rows_valid - 1) * row_stride + c * 8, lds + gi * 1024);
+  }
+}
+
+// Transposed MFMA operand from a swizzled row-major bf16 tile (RB bytes per row):
+// lane l of 16-lane group g gets column col0 + 16*(g & 1) + (l & 15) of rows
+// row0 + 4*(g >> 1) + {0..3} (slots 0-3) and the same rows + 8 (slots 4-7).  This is
+// the operand whose k index runs over tile rows in the order a 32x32 C layout hands
+// them over (register 8u+j <-> row 16u' + 8*(j/4) + 4*half + j%4).
+template <int RB>
+__device__ __forceinline__ bf16x8 tr_operand(const JFA_LDS char* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, s16 = lane & 15;
+  const int r = row0 + 4 * (g >> 1) + (s16 >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s16 & 3);
+  const int w8 = (col & 7) * 2;
+  return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8),
+                 lds_tr4(tile, swz_off<RB>(r + 8, col >> 3) + w8));
+}
+
+// Workgroups are dealt to the 8 XCDs round robin by workgroup id; number the programs
+// so that consecutive program ids share an XCD (and its L2).
+__device__ __forceinline__ int xcd_program_id(int wg, int num_wg) {
+  const int x = wg & 7, j = wg >> 3;
+  const int q8 = num_wg >> 3, r8 = num_wg & 7;
+  return x * q8 + min(x, r8) + j;
+}
+
+}  // namespace jfa

@@ -1,0 +1,114 @@
+// Internal interface between the host runtime (jfa_api.cpp) and the kernels
+// (jfa_*.hip): launch parameter blocks, tile sizes and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2 };
+
+// Tile geometry.  A forward tile is kFwdRows query rows of one (sequence, head); its
+// key/value loop streams kFwdKeys keys at a time.  A backward tile is kBwdKeys key
+// rows of one (sequence, head); its loop streams kBwdRows query rows at a time.
+// Block-diagonal tiles are one kBlock-token block of one head, one tile per wave.
+constexpr int kFwdWaves = 2;      // waves per forward workgroup
+constexpr int kFwdQPerWave = 64;  // query rows per wave (two 32-row MFMA blocks)
+constexpr int kFwdRows = kFwdWaves * kFwdQPerWave;
+constexpr int kFwdKeys = 64;
+constexpr int kBwdWaves = 4;      // waves per backward workgroup, 32 keys each
+constexpr int kBwdKeys = kBwdWaves * 32;
+constexpr int kBwdRows = 64;
+constexpr int kBlock = 64;
+constexpr int kBdWaves = 4;
+
+// Persistent workgroups resident per CU (used for the default program count).
+constexpr int kFwdWgPerCu = 2;
+constexpr int kBwdWgPerCu = 1;
+constexpr int kBdWgPerCu = 2;
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// A scheduled tile: b = sequence, hb = (head << 24) | block index.
+struct Tile {
+  int32_t b;
+  int32_t hb;
+};
+
+// Forward (self / broadcast-Q).  Pointers to bf16 data are typed as uint16_t here.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* offsets;  // [B+1]
+  const Tile* tiles;       // schedule
+  const int32_t* seg_ptr;  // static: [P+1] per program; dynamic: [G+1] per counter group
+  int32_t* counters;       // dynamic: one int32 per group (zeroed by the schedule upload)
+  int32_t num_seqs, num_heads, num_q, num_programs;
+  int64_t total_tokens;
+  int32_t dynamic;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Backward (self / broadcast-Q).
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* offsets;
+  const Tile* tiles;
+  const int32_t* seg_ptr;
+  int32_t* counters;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;  // self: [T,H,D] fp32; broadcast-Q atomics: [Mq,H,D]; partials: [P,Mq,D]
+  int32_t num_seqs, num_heads, num_q, num_programs;
+  int64_t total_tokens;
+  int32_t dynamic;
+  int32_t dq_partials;  // broadcast-Q: 1 = per-program slabs (plain read-modify-write)
+  int32_t programs_per_head;  // broadcast-Q head-pinned groups
+  float scale;
+  float scale_log2;
+};
+
+// Block-diagonal forward / backward.
+struct BdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o_in;   // backward: forward output
+  const uint16_t* dout;   // backward
+  const float* lse_in;    // backward
+  uint16_t* o;            // forward output / backward dq
+  float* lse;             // forward
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* offsets;      // [B+1]
+  const int32_t* blk_prefix;   // [B+1]: blocks before sequence b
+  int32_t num_seqs, num_heads, num_programs;
+  int64_t total_tokens;
+  int64_t num_tiles;  // blocks * heads
+  float scale;
+  float scale_log2;
+};
+
+// Launchers (defined next to their kernels).  head_dim selects the instantiation.
+hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
+hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
+hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
+// dst[i] = bf16(scale * src[i]), i < n (n multiple of 8).
+hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float scale, hipStream_t s);
+// Broadcast-Q partial slabs [P, Mq, D] (programs h*ph .. h*ph+ph-1 hold head h) ->
+// dq[Mq, H, D] = bf16(scale * sum).
+hipError_t launch_dq_reduce(const float* partials, uint16_t* dq, int num_q, int num_heads,
+                            int head_dim, int programs_per_head, float scale, hipStream_t s);
+
+}  // namespace jfa

@@ -1,0 +1,146 @@
+// Host tile scheduler; see jfa_sched.h for the rules and their sources.
+#include "jfa_sched.h"
+
+#include <algorithm>
+#include <numeric>
+
+namespace jfa {
+namespace {
+
+constexpr int kSelfMode = 0;
+constexpr int kBroadcastMode = 1;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tiles sorted by (-L_b, b, h, blk): sequences ordered by decreasing length (stable in
+// b), each sequence's tiles in (h, blk) order.
+void sorted_tiles(const std::vector<int32_t>& lengths, int num_heads, int rows,
+                  const std::vector<int32_t>& rows_of, std::vector<HostTile>& order) {
+  const int nb = (int)lengths.size();
+  std::vector<int32_t> seq(nb);
+  std::iota(seq.begin(), seq.end(), 0);
+  std::stable_sort(seq.begin(), seq.end(),
+                   [&](int32_t a, int32_t b) { return lengths[a] > lengths[b]; });
+  int64_t n = 0;
+  for (int b = 0; b < nb; ++b) n += num_heads * cdiv(rows_of[b], rows);
+  order.clear();
+  order.reserve(n);
+  for (int32_t b : seq) {
+    const int32_t nblk = (int32_t)cdiv(rows_of[b], rows);
+    for (int h = 0; h < num_heads; ++h)
+      for (int32_t i = 0; i < nblk; ++i) order.push_back({b, h, i});
+  }
+}
+
+// Zigzag dealing: sorted position n -> program pos (even pass) or P-1-pos (odd pass).
+void deal_zigzag(const std::vector<HostTile>& order, int max_programs, Schedule& out) {
+  const int64_t n = (int64_t)order.size();
+  const int p = (int)std::min<int64_t>(max_programs, n);
+  out.programs = p;
+  out.groups = 0;
+  out.seg_ptr.assign(p + 1, 0);
+  out.tiles.resize(n);
+  if (p == 0) return;
+  auto prog_of = [p](int64_t i) {
+    const int64_t r = i / p, pos = i % p;
+    return (int)((r & 1) ? p - 1 - pos : pos);
+  };
+  for (int64_t i = 0; i < n; ++i) out.seg_ptr[prog_of(i) + 1]++;
+  for (int i = 0; i < p; ++i) out.seg_ptr[i + 1] += out.seg_ptr[i];
+  std::vector<int32_t> fill(out.seg_ptr.begin(), out.seg_ptr.end() - 1);
+  for (int64_t i = 0; i < n; ++i) out.tiles[fill[prog_of(i)]++] = order[i];
+}
+
+}  // namespace
+
+void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int num_q,
+                  int rows, int max_programs, bool dynamic, Schedule& out) {
+  std::vector<int32_t> rows_of(lengths.size());
+  for (size_t b = 0; b < lengths.size(); ++b)
+    rows_of[b] = (mode == kBroadcastMode) ? num_q : lengths[b];
+  std::vector<HostTile> order;
+  sorted_tiles(lengths, num_heads, rows, rows_of, order);
+  out.tile_rows = rows;
+  if (dynamic) {
+    out.programs = (int)std::min<int64_t>(max_programs, (int64_t)order.size());
+    out.groups = 1;
+    out.seg_ptr = {0, (int32_t)order.size()};
+    out.tiles = std::move(order);
+    return;
+  }
+  deal_zigzag(order, max_programs, out);
+}
+
+void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
+                  int max_programs, bool dynamic, Schedule& out) {
+  out.tile_rows = rows;
+  if (mode == kSelfMode) {
+    std::vector<HostTile> order;
+    sorted_tiles(lengths, num_heads, rows, lengths, order);
+    if (dynamic) {
+      out.programs = (int)std::min<int64_t>(max_programs, (int64_t)order.size());
+      out.groups = 1;
+      out.seg_ptr = {0, (int32_t)order.size()};
+      out.tiles = std::move(order);
+      return;
+    }
+    deal_zigzag(order, max_programs, out);
+    return;
+  }
+  // Broadcast-Q: head-pinned round robin.
+  const int nb = (int)lengths.size();
+  int64_t n_head = 0;
+  for (int b = 0; b < nb; ++b) n_head += cdiv(lengths[b], rows);
+  out.tiles.clear();
+  if (n_head == 0) {
+    out.programs = 0;
+    out.groups = dynamic ? 1 : 0;
+    out.seg_ptr = {0};
+    return;
+  }
+  const int ph = (int)std::max<int64_t>(1, std::min<int64_t>(max_programs / num_heads, n_head));
+  out.programs = ph * num_heads;
+  out.tiles.reserve(n_head * num_heads);
+  if (dynamic) {
+    out.groups = num_heads;
+    out.seg_ptr.assign(1, 0);
+    for (int h = 0; h < num_heads; ++h) {
+      for (int b = 0; b < nb; ++b)
+        for (int32_t j = 0; j < (int32_t)cdiv(lengths[b], rows); ++j) out.tiles.push_back({b, h, j});
+      out.seg_ptr.push_back((int32_t)out.tiles.size());
+    }
+    return;
+  }
+  out.groups = 0;
+  out.seg_ptr.assign(1, 0);
+  for (int h = 0; h < num_heads; ++h) {
+    // program h*ph + r receives tiles r, r + ph, r + 2 ph, ... of head h
+    std::vector<HostTile> head;
+    head.reserve(n_head);
+    for (int b = 0; b < nb; ++b)
+      for (int32_t j = 0; j < (int32_t)cdiv(lengths[b], rows); ++j) head.push_back({b, h, j});
+    for (int r = 0; r < ph; ++r) {
+      for (int64_t i = r; i < n_head; i += ph) out.tiles.push_back(head[i]);
+      out.seg_ptr.push_back((int32_t)out.tiles.size());
+    }
+  }
+}
+
+void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int block,
+                        int max_programs, Schedule& out) {
+  out.tile_rows = block;
+  out.groups = 0;
+  out.tiles.clear();
+  for (int b = 0; b < (int)lengths.size(); ++b)
+    for (int32_t j = 0; j < (int32_t)cdiv(lengths[b], block); ++j)
+      for (int h = 0; h < num_heads; ++h) out.tiles.push_back({b, h, j});
+  const int64_t n = (int64_t)out.tiles.size();
+  const int p = (int)std::min<int64_t>(max_programs, n);
+  out.programs = p;
+  out.seg_ptr.assign(p + 1, 0);
+  if (p == 0) return;
+  const int64_t q = n / p, r = n % p;
+  for (int i = 0; i <= p; ++i) out.seg_ptr[i] = (int32_t)(i * q + std::min<int64_t>(i, r));
+}
+
+}  // namespace jfa

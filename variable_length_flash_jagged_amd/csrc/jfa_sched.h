@@ -1,0 +1,45 @@
+// Host tile scheduler (pure C++; no HIP calls).
+//
+// Rules (aixai.ru page, "Tile balancing and Cluster Launch Control"; yuxiaoba page,
+// "load balancing needs a static and a dynamic layer"; bittide page, section 5):
+//  * forward tiles cost in proportion to their sequence's key length: sort by that
+//    cost, largest first (ties by (b, h, blk)), deal in zigzag (even passes from the
+//    first program to the last, odd passes back);
+//  * self-attention backward tiles cost in proportion to L_b as well and take the same
+//    rule; broadcast-Q backward tiles all cost the same (each loops over the shared
+//    queries) and are dealt round robin within head-pinned program groups;
+//  * only valid (non-empty) tiles are listed, except broadcast-Q forward tiles of an
+//    empty sequence, which still write O = 0 and lse = -inf;
+//  * dynamic mode keeps the same order and lets programs take tiles from an atomic
+//    counter (one per group);
+//  * block-diagonal tiles (one 64-token block of one head, head fastest) get balanced
+//    contiguous ranges from divmod.
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+namespace jfa {
+
+struct HostTile {
+  int32_t b, h, blk;
+};
+
+struct Schedule {
+  std::vector<HostTile> tiles;   // static: program-major; dynamic: global order
+  std::vector<int32_t> seg_ptr;  // static: [P+1]; dynamic: [G+1]
+  int32_t programs = 0;          // workgroups to launch
+  int32_t tile_rows = 0;         // rows per tile (query rows fwd, key rows bwd, block)
+  int32_t groups = 0;            // dynamic: counter groups; static: 0
+};
+
+// lengths: L_b for b < B (validated by the caller).
+void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int num_q,
+                  int rows, int max_programs, bool dynamic, Schedule& out);
+void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
+                  int max_programs, bool dynamic, Schedule& out);
+void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int block,
+                        int max_programs, Schedule& out);
+
+}  // namespace jfa
