@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the jagged flash attention hot path on one MI355X.
+
+A step is one forward plus one backward (jfa_fwd + jfa_bwd through the C ABI: offsets
+intake, host schedule, schedule upload, attention kernels, dQ accumulation and cast)
+over one batch of the production-shaped jagged self-attention workload: B=1152
+sequences with log-normal lengths (median ~600, clipped to [1, 4000]), H=4, D=128,
+bf16 N(0,1) inputs drawn with seed 0, already resident in HBM.  The reported value is
+valid-token TFLOPS (forward 4*H*D*sum L^2 plus backward 2.5x that) per step.
+
+Prints one JSON line.  ``--workload N`` benchmarks another numbered workload (see
+variable_length_flash_jagged_amd/workloads.py) instead.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "valid-token TFLOPS fwd+bwd (bf16, D=128 jagged) and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--sched", type=int, default=0)
+    ap.add_argument("--dq-path", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
+    """Time the fp64 oracle on the first sequences of the same batch (bounded sample)."""
+    import numpy as np
+    import oracle
+    from variable_length_flash_jagged_amd import metrics as M
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done, flops, spent, b = 0, 0, 0.0, 0
+    chunk = 8
+    while b < len(lengths) and spent < target_s:
+        e = min(len(lengths), b + chunk)
+        q, k, v, do, off = p_cpu_fn(b, e)
+        t0 = time.perf_counter()
+        oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
+        oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
+        spent += time.perf_counter() - t0
+        sub = lengths[b:e]
+        flops += M.fwd_flops(sub, mode, num_heads, head_dim, num_q) + M.bwd_flops(sub, mode, num_heads, head_dim, num_q)
+        done, b = e, e
+    return {
+        "value": round(flops / spent / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
+                  f"one fp64 forward + backward each, {spent:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from variable_length_flash_jagged_amd import binding as B
+    from variable_length_flash_jagged_amd import metrics as M
+    from variable_length_flash_jagged_amd import workloads as W
+
+    torch.cuda.init()
+    w = W.WORKLOADS[args.workload]
+    p = W.make_workload(args.workload, seed=args.seed, device="cuda")
+    mode, h, d, mq = p["mode"], p["num_heads"], p["head_dim"], p["num_q"]
+    lengths = p["lengths"]
+    opts = B.make_opts(sched=args.sched, dq_path=args.dq_path)
+    shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq)
+    q, k, v, do, off, off_h = p["q"], p["k"], p["v"], p["do"], p["offsets"], p["offsets_host"]
+    if mode == W.MODE_BROADCAST_Q:
+        o = torch.empty((p["num_seqs"], mq, h, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((p["num_seqs"], h, mq), dtype=torch.float32, device="cuda")
+    else:
+        o = torch.empty_like(k)
+        lse = torch.empty((h, p["total_tokens"]), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
+    ws_b = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
+    scale = p["scale"]
+
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for n in ("f0", "f1", "b1")}
+
+    def step(i=None):
+        if i is not None:
+            ev["f0"][i].record()
+        B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
+        if i is not None:
+            ev["f1"][i].record()
+        B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
+        if i is not None:
+            ev["b1"][i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.kernel_timing(True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(ev["f0"][i].elapsed_time(ev["f1"][i]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(ev["f1"][i].elapsed_time(ev["b1"][i]) for i in range(args.steps)) / args.steps
+    nf, kf_ms = B.kernel_times(B.PASS_FWD)
+    nb, kb_ms = B.kernel_times(B.PASS_BWD)
+    B.kernel_timing(False)
+
+    ff = M.fwd_flops(lengths, mode, h, d, mq)
+    fb = M.bwd_flops(lengths, mode, h, d, mq)
+    bytes_f = M.fwd_bytes(lengths, mode, h, d, mq)
+    bytes_b = M.bwd_bytes(lengths, mode, h, d, mq)
+    value = (ff + fb) / (ms_step * 1e-3) / 1e12
+    kern_f = kf_ms / max(nf, 1)
+    kern_b = kb_ms / max(nb, 1)
+    hbm_bound = mode == W.MODE_BLOCK_DIAG
+    # dominant kernel: the one with the larger total time per step
+    if kern_b >= kern_f:
+        dom, dom_ms, dom_flops, dom_bytes = "bwd", kern_b, fb, bytes_b
+    else:
+        dom, dom_ms, dom_flops, dom_bytes = "fwd", kern_f, ff, bytes_f
+    if hbm_bound:
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = f"{dom}_kernel"
+    roof["kernel_ms"] = round(dom_ms, 4)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w["name"],
+            "mode": ["self", "broadcast_q", "block_diag"][mode],
+            "num_seqs": int(p["num_seqs"]), "num_heads": h, "head_dim": d, "num_q": mq,
+            "total_tokens": int(p["total_tokens"]), "max_len": int(max(lengths)),
+            "sched": ["static", "dynamic"][args.sched], "dq_path": args.dq_path, "seed": args.seed,
+        },
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
+                "kernel_ms": round(kern_f, 4), "kernel_tflops": round(ff / (kern_f * 1e-3) / 1e12, 1),
+                "kernel_gbs": round(bytes_f / (kern_f * 1e-3) / 1e9, 1), "flops": ff, "bytes": bytes_f},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 1),
+                "kernel_ms": round(kern_b, 4), "kernel_tflops": round(fb / (kern_b * 1e-3) / 1e12, 1),
+                "kernel_gbs": round(bytes_b / (kern_b * 1e-3) / 1e9, 1), "flops": fb, "bytes": bytes_b},
+        "roofline": roof,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        offs = np.asarray(off_h, dtype=np.int64)
+
+        def sub_problem(b0, b1):
+            s, e = int(offs[b0]), int(offs[b1])
+            f = lambda t: t[s:e].float().cpu().numpy().astype(np.float64)
+            sub_off = offs[b0:b1 + 1] - s
+            if mode == W.MODE_BROADCAST_Q:
+                return (q.float().cpu().numpy().astype(np.float64), f(k), f(v),
+                        do[b0:b1].float().cpu().numpy().astype(np.float64), sub_off)
+            return f(q), f(k), f(v), f(do), sub_off
+
+        out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -141,6 +141,16 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
                  int64_t seg_cap, int64_t* n_tiles, int32_t* n_segs, int32_t* n_programs,
                  int32_t* tile_rows);
 
+/* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd call records a
+ * pair of HIP events on its stream immediately around its main attention kernel
+ * (not the schedule upload or the dQ fill / cast / reduce kernels).  jfa_kernel_times
+ * waits for the events recorded so far for `pass` (JFA_PASS_FWD or JFA_PASS_BWD) and
+ * returns the number of launches and their summed duration in milliseconds; reset != 0
+ * then forgets them.  Enabling or disabling also forgets them.  Events are created by
+ * the library on the calling thread's current device and released when forgotten. */
+int jfa_kernel_timing(int enable);
+int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset);
+
 /* Static message for a status code. */
 const char* jfa_error_string(int code);
 /* Thread-local detail about the last failed call on this thread ("" if none). */

@@ -60,6 +60,10 @@ def lib():
         L.jfa_bwd.restype = ctypes.c_int
         L.jfa_bwd.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               ctypes.c_size_t, op, vp]
+        L.jfa_kernel_timing.restype = ctypes.c_int
+        L.jfa_kernel_timing.argtypes = [ctypes.c_int]
+        L.jfa_kernel_times.restype = ctypes.c_int
+        L.jfa_kernel_times.argtypes = [ctypes.c_int, i64p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         L.jfa_schedule.restype = ctypes.c_int
         L.jfa_schedule.argtypes = [sp, ctypes.c_int, ctypes.c_int, vp, op, vp, i64, vp, i64, i64p, i32p, i32p, i32p]
         _lib = L
@@ -104,6 +108,18 @@ def schedule(shape, mode, pass_, offsets_host, opts=None):
                           seg.ctypes.data, seg.shape[0], ctypes.byref(n_tiles), ctypes.byref(n_segs),
                           ctypes.byref(n_prog), ctypes.byref(rows)), "jfa_schedule")
     return tiles[: n_tiles.value], seg[: n_segs.value], n_prog.value, rows.value
+
+
+def kernel_timing(enable):
+    """Turn the library's per-launch kernel event timing on or off (forgets old events)."""
+    _check(lib().jfa_kernel_timing(1 if enable else 0), "jfa_kernel_timing")
+
+
+def kernel_times(pass_, reset=False):
+    """(launches, total_ms) of the main kernel of pass_ since the last reset."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().jfa_kernel_times(pass_, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0), "jfa_kernel_times")
+    return int(n.value), float(ms.value)
 
 
 def _ptr(t):

@@ -242,11 +242,84 @@ int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
 
+// Kernel timing hook (see jfa_kernel_timing in jfa.h).
+struct KernelTimer {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[2];
+  void forget_locked() {
+    for (auto& v : ev) {
+      for (auto& pr : v) {
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
+      }
+      v.clear();
+    }
+  }
+} g_timer;
+
+// Launch `fn` (returning hipError_t) between two recorded events when timing is on.
+template <class F>
+hipError_t timed_launch(int pass, hipStream_t s, F fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  {
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    on = g_timer.enabled;
+  }
+  if (on) {
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e == hipSuccess) e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = fn();
+  if (on) {
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    g_timer.ev[pass].push_back({a, b});
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
 
 int jfa_version(void) { return JFA_VERSION; }
+
+int jfa_kernel_timing(int enable) {
+  g_detail.clear();
+  std::lock_guard<std::mutex> lock(g_timer.mu);
+  g_timer.forget_locked();
+  g_timer.enabled = enable != 0;
+  return JFA_OK;
+}
+
+int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
+  g_detail.clear();
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return fail(JFA_ERR_BAD_MODE, "pass must be 0 or 1");
+  if (!launches || !total_ms) return fail(JFA_ERR_NULL_POINTER, "launches and total_ms must be non-NULL");
+  std::lock_guard<std::mutex> lock(g_timer.mu);
+  double sum = 0.0;
+  for (auto& pr : g_timer.ev[pass]) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_fail(e, "reading kernel timing events");
+    sum += ms;
+  }
+  *launches = (int64_t)g_timer.ev[pass].size();
+  *total_ms = sum;
+  if (reset) {
+    for (auto& pr : g_timer.ev[pass]) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    g_timer.ev[pass].clear();
+  }
+  return JFA_OK;
+}
 
 const char* jfa_last_error_detail(void) { return g_detail.c_str(); }
 
@@ -366,7 +439,8 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
-    return launch_status(launch_bd_fwd(p, D, stream), "block-diagonal forward launch");
+    return launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_bd_fwd(p, D, stream); }),
+                         "block-diagonal forward launch");
   }
 
   Schedule sc;
@@ -393,7 +467,8 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   p.total_tokens = shape->total_tokens;
   p.dynamic = op.sched;
   p.scale_log2 = scale * kLog2eHost;
-  return launch_status(launch_fwd(p, mode, D, stream), "forward launch");
+  return launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_fwd(p, mode, D, stream); }),
+                       "forward launch");
 }
 
 int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
@@ -448,7 +523,8 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
-    return launch_status(launch_bd_bwd(p, D, stream), "block-diagonal backward launch");
+    return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bd_bwd(p, D, stream); }),
+                         "block-diagonal backward launch");
   }
 
   Schedule sc;
@@ -492,7 +568,9 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.programs_per_head = ph;
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
-    if ((rc = launch_status(launch_bwd(p, mode, D, stream), "backward launch"))) return rc;
+    if ((rc = launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd(p, mode, D, stream); }),
+                            "backward launch")))
+      return rc;
   }
   if (partials)
     return launch_status(launch_dq_reduce(acc, (uint16_t*)dq, (int)Mq, H, D, ph, scale, stream), "dq reduce");
