@@ -80,12 +80,14 @@ def test_fwd_rejects_null_pointers_before_any_device_work():
     assert b"non-NULL" in lib.jfa_last_error_detail()
 
 
-def test_workspace_does_not_depend_on_individual_lengths():
-    # a function of (B, H, D, Mq, T) and the options only
-    s = B.make_shape(3, 4, 128, 1000)
-    a = B.workspace_size(s, 0, 1, B.make_opts(num_programs=64))
-    assert a == B.workspace_size(s, 0, 1, B.make_opts(num_programs=64))
-    assert a >= 1000 * 4 * 128 * 4  # fp32 dq accumulator
+def test_workspace_sizes():
+    # a function of (B, H, D, Mq, T) and the options only, never of B * max L
+    s = B.make_shape(3, 4, 128, 100000)
+    self_ws = B.workspace_size(s, 0, 1, B.make_opts(num_programs=64))
+    assert self_ws < 100000 * 4 * 128  # self backward keeps no dQ accumulator
+    bq = B.make_shape(3, 4, 128, 100000, num_q=256)
+    assert B.workspace_size(bq, 1, 1, B.make_opts(num_programs=64)) >= 256 * 4 * 128 * 4
+    assert B.workspace_size(bq, 1, 1, B.make_opts(dq_path=1, num_programs=64)) >= 64 * 256 * 128 * 4
 
 
 def _lengths(rng, n, hi):

@@ -105,9 +105,9 @@ int max_programs(const Opts& o, int wg_per_cu) {
 
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct Layout {
-  size_t counters = 0, seg = 0, tiles = 0, prefix = 0, acc = 0, total = 0;
-  int64_t seg_cap = 0, tile_cap = 0;
-  int programs_cap = 0;
+  size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, prefix = 0, acc = 0, total = 0;
+  int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
+  int programs_cap = 0, programs2_cap = 0;
 };
 
 void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L) {
@@ -134,15 +134,18 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
   }
   L.tiles = at;
   at += align_up(L.tile_cap * sizeof(Tile));
-  if (pass == JFA_PASS_BWD) {
+  if (pass == JFA_PASS_BWD && mode == JFA_MODE_SELF) {
+    // second schedule: the dQ kernel's query-row tiles (forward tiling)
+    L.programs2_cap = max_programs(o, kDqWgPerCu);
+    L.seg2_cap = L.programs2_cap + 1;
+    L.seg2 = at;
+    at += align_up(L.seg2_cap * sizeof(int32_t));
+    L.tile2_cap = H * (T / kFwdRows + B + 1);
+    L.tiles2 = at;
+    at += align_up(L.tile2_cap * sizeof(Tile));
+  } else if (pass == JFA_PASS_BWD) {
     L.acc = at;
-    int64_t acc_elems;
-    if (mode == JFA_MODE_SELF)
-      acc_elems = T * H * D;
-    else if (o.dq_path == 0)
-      acc_elems = Mq * H * D;
-    else
-      acc_elems = (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
+    const int64_t acc_elems = (o.dq_path == 0) ? Mq * H * D : (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
     at += align_up(acc_elems * sizeof(float));
   }
   L.total = at;
@@ -228,14 +231,21 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   return JFA_OK;
 }
 
-// Serialise [counters | seg_ptr | tiles] of a schedule for the device.
-void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf) {
-  const size_t tiles_bytes = sc.tiles.size() * sizeof(Tile);
-  buf.assign(L.tiles + tiles_bytes, 0);
-  memcpy(buf.data() + L.seg, sc.seg_ptr.data(), sc.seg_ptr.size() * sizeof(int32_t));
-  Tile* t = reinterpret_cast<Tile*>(buf.data() + L.tiles);
+// Serialise [counters | seg_ptr | tiles (| seg_ptr2 | tiles2)] of one or two schedules
+// for the device (counters start at zero).
+void put_schedule(const Schedule& sc, size_t seg_off, size_t tiles_off, std::vector<char>& buf) {
+  memcpy(buf.data() + seg_off, sc.seg_ptr.data(), sc.seg_ptr.size() * sizeof(int32_t));
+  Tile* t = reinterpret_cast<Tile*>(buf.data() + tiles_off);
   for (size_t i = 0; i < sc.tiles.size(); ++i)
     t[i] = Tile{sc.tiles[i].b, (sc.tiles[i].h << 24) | sc.tiles[i].blk};
+}
+
+void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf, const Schedule* sc2 = nullptr) {
+  size_t end = L.tiles + sc.tiles.size() * sizeof(Tile);
+  if (sc2) end = L.tiles2 + sc2->tiles.size() * sizeof(Tile);
+  buf.assign(end, 0);
+  put_schedule(sc, L.seg, L.tiles, buf);
+  if (sc2) put_schedule(*sc2, L.seg2, L.tiles2, buf);
 }
 
 int launch_status(hipError_t e, const char* what) {
@@ -530,13 +540,51 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   Schedule sc;
   schedule_bwd(lengths, H, mode, kBwdKeys, max_programs(op, kBwdWgPerCu), op.sched == 1, sc);
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
-  const bool bq = mode == JFA_MODE_BROADCAST_Q;
-  const bool partials = bq && op.dq_path == 1;
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.offsets = offsets_dev;
+  p.tiles = (const Tile*)(ws + L.tiles);
+  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.counters = (int32_t*)(ws + L.counters);
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.num_seqs = shape->num_seqs;
+  p.num_heads = H;
+  p.num_q = shape->num_q;
+  p.num_programs = sc.programs;
+  p.total_tokens = T;
+  p.dynamic = op.sched;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2eHost;
+
+  if (mode == JFA_MODE_SELF) {
+    if (sc.tiles.empty()) return JFA_OK;
+    Schedule sq;
+    schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kFwdRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
+    if ((int64_t)sq.tiles.size() > L.tile2_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+    std::vector<char> buf;
+    serialise(sc, L, buf, &sq);
+    if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+    p.dq = (uint16_t*)dq;
+    p.dq_tiles = (const Tile*)(ws + L.tiles2);
+    p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
+    p.dq_programs = sq.programs;
+    return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self(p, D, stream); }),
+                         "backward launch");
+  }
+
+  // Broadcast-Q: one fused kernel; dQ summed over all sequences through fp32 atomics
+  // (path 0) or per-program partial slabs and a reduce kernel (path 1).
+  const bool partials = op.dq_path == 1;
   const int64_t Mq = shape->num_q;
   float* acc = (float*)(ws + L.acc);
-  const int ph = bq ? std::max(1, sc.programs / H) : 0;
-  const int64_t acc_elems = !bq ? T * H * D : (partials ? (int64_t)ph * H * Mq * D : Mq * H * D);
-  if (sc.tiles.empty() && !bq) return JFA_OK;
+  const int ph = std::max(1, sc.programs / H);
+  const int64_t acc_elems = partials ? (int64_t)ph * H * Mq * D : Mq * H * D;
   if (!sc.tiles.empty()) {
     std::vector<char> buf;
     serialise(sc, L, buf);
@@ -544,30 +592,9 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   }
   if ((rc = launch_status(launch_fill_zero(acc, acc_elems, stream), "dq accumulator fill"))) return rc;
   if (!sc.tiles.empty()) {
-    BwdParams p{};
-    p.q = (const uint16_t*)q;
-    p.k = (const uint16_t*)k;
-    p.v = (const uint16_t*)v;
-    p.o = (const uint16_t*)o;
-    p.dout = (const uint16_t*)dout;
-    p.lse = lse;
-    p.offsets = offsets_dev;
-    p.tiles = (const Tile*)(ws + L.tiles);
-    p.seg_ptr = (const int32_t*)(ws + L.seg);
-    p.counters = (int32_t*)(ws + L.counters);
-    p.dk = (uint16_t*)dk;
-    p.dv = (uint16_t*)dv;
     p.dq_acc = acc;
-    p.num_seqs = shape->num_seqs;
-    p.num_heads = H;
-    p.num_q = shape->num_q;
-    p.num_programs = sc.programs;
-    p.total_tokens = T;
-    p.dynamic = op.sched;
     p.dq_partials = partials ? 1 : 0;
     p.programs_per_head = ph;
-    p.scale = scale;
-    p.scale_log2 = scale * kLog2eHost;
     if ((rc = launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd(p, mode, D, stream); }),
                             "backward launch")))
       return rc;

@@ -168,9 +168,6 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, Tile tile, int prog
   for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = as_bf16x8(lds_ld16(kt, swz_off<C::RB>(my_key, 2 * ks + half)));
   const int dq_db = (C::NDB >= C::NW) ? wave : (wave % C::NDB);
   const int dq_qb0 = (C::NDB >= C::NW) ? 0 : (wave / C::NDB);
-  bf16x8 ktf[C::NK16];
-#pragma unroll
-  for (int t = 0; t < C::NK16; ++t) ktf[t] = tr_operand<C::RB>(kt, 16 * t, 32 * dq_db, lane);
   finish_step<D>(pre, smem + C::OFF_DO, lse2, di, min(C::QB, Lq), tid);
   __syncthreads();
 
@@ -191,27 +188,23 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, Tile tile, int prog
       prefetch_step<D>(qb, dob, ob, lseb, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
                        smem + C::OFF_DO + (cur ^ 1) * C::QBUF, pre, tid, wave, lane);
 
-    // S = Q K^T and dP = dO V^T: [queries x keys], C layout -> lane = key.
-    f32x16 s[C::NQB], dp[C::NQB];
-#pragma unroll
-    for (int qq = 0; qq < C::NQB; ++qq)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[qq][i] = dp[qq][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-#pragma unroll
-      for (int qq = 0; qq < C::NQB; ++qq) {
-        const int off = swz_off<C::RB>(qq * 32 + l32, 2 * ks + half);
-        s[qq] = mfma32(as_bf16x8(lds_ld16(qt, off)), kf[ks], s[qq]);
-        dp[qq] = mfma32(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp[qq]);
-      }
-    }
-
-    // P = 2^(S*c - lse2), zero for keys past the end; dS = P * (dP - Di).
+    // One 32-row query block at a time: S = Q K^T and dP = dO V^T ([queries x keys],
+    // C layout -> lane = key), P = 2^(S*c - lse2) (zero for keys past the end),
+    // dS = P * (dP - Di), then dV^T += dO^T P and dK^T += Q^T dS ([head dim x keys],
+    // k = query rows) and dS^T -> LDS.
     const float* l2 = lse2 + cur * C::QB;
     const float* dd = di + cur * C::QB;
 #pragma unroll
     for (int qq = 0; qq < C::NQB; ++qq) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        const int off = swz_off<C::RB>(qq * 32 + l32, 2 * ks + half);
+        s = mfma32(as_bf16x8(lds_ld16(qt, off)), kf[ks], s);
+        dp = mfma32(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp);
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int r4 = qq * 32 + 8 * g4 + 4 * half;
@@ -222,54 +215,56 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, Tile tile, int prog
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
-          float pv = fast_exp2(fmaf(s[qq][i], c, -la[e]));
+          float pv = fast_exp2(fmaf(s[i], c, -la[e]));
           pv = key_ok ? pv : 0.f;
-          s[qq][i] = pv;
-          dp[qq][i] = pv * (dp[qq][i] - da[e]);
+          s[i] = pv;
+          dp[i] = pv * (dp[i] - da[e]);
         }
       }
-    }
-    bf16x8 pf[C::NT16], dsf[C::NT16];
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int t = 0; t < C::NT16; ++t) {
-      const int qq = t >> 1, r = 8 * (t & 1);
-      pf[t] = pack8(s[qq][r], s[qq][r + 1], s[qq][r + 2], s[qq][r + 3], s[qq][r + 4], s[qq][r + 5],
-                    s[qq][r + 6], s[qq][r + 7]);
-      dsf[t] = pack8(dp[qq][r], dp[qq][r + 1], dp[qq][r + 2], dp[qq][r + 3], dp[qq][r + 4], dp[qq][r + 5],
-                     dp[qq][r + 6], dp[qq][r + 7]);
-    }
-
-    // dV^T += dO^T P, dK^T += Q^T dS: [head dim x keys], k = query rows.
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int t = 0; t < C::NT16; ++t) {
-        dv[db] = mfma32(tr_operand<C::RB>(dot, 16 * t, 32 * db, lane), pf[t], dv[db]);
-        dk[db] = mfma32(tr_operand<C::RB>(qt, 16 * t, 32 * db, lane), dsf[t], dk[db]);
+      for (int u = 0; u < 2; ++u) {
+        const int r = 8 * u;
+        pf[u] = pack8(s[r], s[r + 1], s[r + 2], s[r + 3], s[r + 4], s[r + 5], s[r + 6], s[r + 7]);
+        dsf[u] = pack8(dp[r], dp[r + 1], dp[r + 2], dp[r + 3], dp[r + 4], dp[r + 5], dp[r + 6], dp[r + 7]);
       }
-    }
-
-    // dS^T (bf16) -> LDS: row = key, 4 consecutive queries per 8-byte store.
 #pragma unroll
-    for (int qq = 0; qq < C::NQB; ++qq)
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int t = 2 * qq + u;
+          dv[db] = mfma32(tr_operand<C::RB>(dot, 16 * t, 32 * db, lane), pf[u], dv[db]);
+          dk[db] = mfma32(tr_operand<C::RB>(qt, 16 * t, 32 * db, lane), dsf[u], dk[db]);
+        }
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int q = qq * 32 + 8 * g4 + 4 * half;
         lds_st8(st, swz_off<C::SRB>(my_key, q >> 3) + (q & 7) * 2,
-                pack4(dp[qq][4 * g4], dp[qq][4 * g4 + 1], dp[qq][4 * g4 + 2], dp[qq][4 * g4 + 3]));
+                pack4(dp[4 * g4], dp[4 * g4 + 1], dp[4 * g4 + 2], dp[4 * g4 + 3]));
       }
+    }
     wait_vmem();
     __syncthreads();
 
-    // dQ block(s) of this wave: [queries x head dim] over all 128 keys of the tile.
+    // dQ block(s) of this wave: [queries x head dim] over all 128 keys of the tile;
+    // the K^T operand comes from the K tile that stays in LDS for the whole tile.
+    f32x16 dqa[C::DQ_NQB];
+#pragma unroll
+    for (int u = 0; u < C::DQ_NQB; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dqa[u][i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NK16; ++t) {
+      const bf16x8 kt_op = tr_operand<C::RB>(kt, 16 * t, 32 * dq_db, lane);
+#pragma unroll
+      for (int u = 0; u < C::DQ_NQB; ++u)
+        dqa[u] = mfma32(tr_operand<C::SRB>(st, 16 * t, 32 * (dq_qb0 + u), lane), kt_op, dqa[u]);
+    }
 #pragma unroll
     for (int u = 0; u < C::DQ_NQB; ++u) {
       const int qq = dq_qb0 + u;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < C::NK16; ++t) acc = mfma32(tr_operand<C::SRB>(st, 16 * t, 32 * qq, lane), ktf[t], acc);
+      const f32x16& acc = dqa[u];
       const int d = 32 * dq_db + l32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -398,7 +393,7 @@ int grid_for(int64_t work, int block) {
 
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
-  if (mode == kSelf) return head_dim == 64 ? launch<64, kSelf>(p, s) : launch<128, kSelf>(p, s);
+  if (mode != kBroadcastQ) return hipErrorInvalidValue;  // self mode: launch_bwd_self
   return head_dim == 64 ? launch<64, kBroadcastQ>(p, s) : launch<128, kBroadcastQ>(p, s);
 }
 

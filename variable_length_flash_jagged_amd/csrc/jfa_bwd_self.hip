@@ -1,0 +1,433 @@
+// Self-attention backward for gfx950 as two persistent kernels with no dQ atomics.
+//
+// What it computes: the analytic gradient of sum(O * dO) per sequence and head, with
+// P rebuilt from the forward's log-sum-exp, P = exp(scale * Q K^T - L) (the L kept for
+// the backward, "TLX Block Attention", bittide page, section 2.1), and
+// Di = rowsum(dO * O) formed inline in each kernel rather than in a preprocessing
+// launch (same page, sections 2.1 and 4):
+//   dV = P^T dO, dP = dO V^T, dS = P * (dP - Di), dK = scale dS^T Q, dQ = scale dS K.
+//
+// How it maps to CDNA4.  A fused kernel that owns a key/value block must hand its dQ
+// contribution to every query row of the sequence; on MI355X coalesced fp32 atomics
+// retire at roughly 3.4e11 per second device-wide, so for long jagged batches the
+// dQ hand-off alone would outweigh the matrix work.  The self-attention backward is
+// therefore split by ownership:
+//  * dkdv_kernel: one workgroup = one tile of kBwdKeys (128) keys of one (sequence,
+//    head); wave w owns keys 32w..32w+31 with their K, V operands and fp32 dK^T, dV^T
+//    accumulators in registers; 64 query rows stream through double-buffered,
+//    swizzled LDS tiles (direct global->LDS copies issued one step ahead).  Four
+//    products per step: S = Q K^T and dP = dO V^T (C layout: lane = key), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed from LDS
+//    (ds_read_b64_tr_b16).  dK and dV are written once, by their owner.
+//  * dq_kernel: one workgroup = one tile of kFwdRows query rows (32 per wave), the
+//    forward's tiling and zigzag schedule; the loop streams 64-key K and V tiles
+//    through the same LDS ring as the forward.  Three products per step:
+//    S^T = K Q^T and dP^T = V dO^T (C layout: lane = query, so lse and Di are one
+//    scalar per lane), then dQ^T += K^T dS^T with K^T read transposed from LDS and dS^T
+//    straight from registers.  dQ is written once, by its owner.
+// The split recomputes S and dP once more (seven products per query-key block
+// instead of five) in exchange for no atomics and no fp32 dQ accumulator in HBM.
+#include "jfa_device.h"
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+// ----------------------------------------------------------------------------- dQ
+
+template <int D>
+struct DqCfg {
+  static constexpr int NW = kFwdWaves;
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = kFwdRows;
+  static constexpr int BN = kFwdKeys;
+  static constexpr int NKB = BN / 32;
+  static constexpr int NKS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int NT16 = BN / 16;
+  static constexpr int RB = 2 * D;
+  static constexpr int BUF = BN * RB;
+};
+
+// One key/value tile for this wave's 32 query rows.  MASK: keys >= keys_valid lie past
+// the end of the sequence.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf,
+                                        const bf16x8 (&qf)[DqCfg<D>::NKS], const bf16x8 (&dof)[DqCfg<D>::NKS],
+                                        f32x16 (&dq)[DqCfg<D>::NDB], float lse2, float di, int lane,
+                                        int keys_valid, float c) {
+  using C = DqCfg<D>;
+  const int l32 = lane & 31, half = lane >> 5;
+  f32x16 s[C::NKB], dp[C::NKB];
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int off = swz_off<C::RB>(kb * 32 + l32, 2 * ks + half);
+      s[kb] = mfma32(as_bf16x8(lds_ld16(kbuf, off)), qf[ks], s[kb]);
+      dp[kb] = mfma32(as_bf16x8(lds_ld16(vbuf, off)), dof[ks], dp[kb]);
+    }
+  }
+  // P^T = 2^(S^T c - lse2), dS^T = P^T (dP^T - Di); lane = query, register i <-> key.
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float pv = fast_exp2(fmaf(s[kb][i], c, -lse2));
+      if (MASK) {
+        const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        pv = key < keys_valid ? pv : 0.f;
+      }
+      dp[kb][i] = pv * (dp[kb][i] - di);
+    }
+  // dQ^T += K^T dS^T: A = K^T (transposed LDS read), B = dS^T from the C layout.
+#pragma unroll
+  for (int t = 0; t < C::NT16; ++t) {
+    const f32x16& src = dp[t >> 1];
+    const int r = 8 * (t & 1);
+    const bf16x8 b = pack8(src[r], src[r + 1], src[r + 2], src[r + 3], src[r + 4], src[r + 5], src[r + 6], src[r + 7]);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dq[db] = mfma32(tr_operand<C::RB>(kbuf, 16 * t, 32 * db, lane), b, dq[db]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, int tid) {
+  using C = DqCfg<D>;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t s0 = p.offsets[b];
+  const int L = (int)(p.offsets[b + 1] - s0);
+  const int row = blk * C::BM + wave * 32 + l32;
+  const bool row_ok = row < L;
+  const float c = p.scale_log2;
+
+  // Q and dO rows as B operands; Di = rowsum(dO * O) and lse2 for this lane's row.
+  bf16x8 qf[C::NKS], dof[C::NKS];
+  float di = 0.f;
+  {
+    const int64_t base = (s0 + row) * rs + (int64_t)h * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      qf[ks] = as_bf16x8(row_ok ? ld16(p.q + base + 16 * ks) : zero16());
+      dof[ks] = as_bf16x8(row_ok ? ld16(p.dout + base + 16 * ks) : zero16());
+      const bf16x8 o8 = as_bf16x8(row_ok ? ld16(p.o + base + 16 * ks) : zero16());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di = fmaf((float)dof[ks][e], (float)o8[e], di);
+    }
+    di = half_sum(di);
+  }
+  const float lse2 = row_ok ? p.lse[(int64_t)h * p.total_tokens + s0 + row] * kLog2e : INFINITY;
+
+  f32x16 dq[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+  const int n_full = L / C::BN, tail = L % C::BN;
+  const int n_kv = n_full + (tail != 0);
+  const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
+  const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
+  dma_tile<C::RB, C::BN, C::NW>(kp, rs, min(C::BN, L), smem, wave, lane);
+  dma_tile<C::RB, C::BN, C::NW>(vp, rs, min(C::BN, L), smem + C::BUF, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < n_full; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n_kv) {
+      const int64_t nxt = (int64_t)(it + 1) * C::BN;
+      const int rv = min(C::BN, L - (it + 1) * C::BN);
+      JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
+      dma_tile<C::RB, C::BN, C::NW>(kp + nxt * rs, rs, rv, nbuf, wave, lane);
+      dma_tile<C::RB, C::BN, C::NW>(vp + nxt * rs, rs, rv, nbuf + C::BUF, wave, lane);
+    }
+    JFA_LDS char* kbuf = smem + cur * 2 * C::BUF;
+    dq_step<D, false>(kbuf, kbuf + C::BUF, qf, dof, dq, lse2, di, lane, C::BN, c);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (tail) {
+    JFA_LDS char* kbuf = smem + (n_full & 1) * 2 * C::BUF;
+    dq_step<D, true>(kbuf, kbuf + C::BUF, qf, dof, dq, lse2, di, lane, tail, c);
+    __syncthreads();
+  }
+  if (row_ok) {
+    uint16_t* qp = p.dq + (s0 + row) * rs + (int64_t)h * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        st8(qp + 32 * db + 8 * g4, pack4(dq[db][4 * g4] * p.scale, dq[db][4 * g4 + 1] * p.scale,
+                                        dq[db][4 * g4 + 2] * p.scale, dq[db][4 * g4 + 3] * p.scale));
+  }
+}
+
+// ---------------------------------------------------------------------------- dK, dV
+
+template <int D>
+struct KvCfg {
+  static constexpr int NW = kBwdWaves;
+  static constexpr int NT = NW * 64;
+  static constexpr int BN = kBwdKeys;
+  static constexpr int QB = kBwdRows;
+  static constexpr int NQB = QB / 32;
+  static constexpr int NKS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int RB = 2 * D;
+  static constexpr int QBUF = QB * RB;
+  static constexpr int CPR = D / 8;
+  static constexpr int DI_ROWS_PER_PASS = NT / CPR;
+  static constexpr int DI_PASSES = QB / DI_ROWS_PER_PASS;
+  static constexpr int OFF_Q = 0;                      // [2][QBUF]
+  static constexpr int OFF_DO = OFF_Q + 2 * QBUF;      // [2][QBUF]
+  static constexpr int OFF_LSE = OFF_DO + 2 * QBUF;    // float [2][QB]
+  static constexpr int OFF_DI = OFF_LSE + 2 * QB * 4;  // float [2][QB]
+  static constexpr int SMEM = OFF_DI + 2 * QB * 4;
+};
+
+template <int D>
+struct KvPrefetch {
+  u32x4 o[KvCfg<D>::DI_PASSES];
+  float lse;
+};
+
+// Issue the next step's copies (Q, dO -> LDS) and register loads (O rows, lse).
+template <int D>
+__device__ __forceinline__ void kv_prefetch(const uint16_t* qb, const uint16_t* dob, const uint16_t* ob,
+                                            const float* lseb, int64_t rs, int row0, int rows_valid,
+                                            JFA_LDS char* qbuf, JFA_LDS char* dobuf, KvPrefetch<D>& pf, int tid,
+                                            int wave, int lane) {
+  using C = KvCfg<D>;
+  dma_tile<C::RB, C::QB, C::NW>(qb + (int64_t)row0 * rs, rs, rows_valid, qbuf, wave, lane);
+  dma_tile<C::RB, C::QB, C::NW>(dob + (int64_t)row0 * rs, rs, rows_valid, dobuf, wave, lane);
+  const int cc = tid % C::CPR;
+#pragma unroll
+  for (int j = 0; j < C::DI_PASSES; ++j) {
+    const int r = tid / C::CPR + j * C::DI_ROWS_PER_PASS;
+    pf.o[j] = r < rows_valid ? ld16(ob + (int64_t)(row0 + r) * rs + cc * 8) : zero16();
+  }
+  pf.lse = (tid < C::QB && tid < rows_valid) ? lseb[row0 + tid] : 0.f;
+}
+
+// Di = rowsum(dO * O) (dO from its LDS tile, O from registers) and lse in base 2 (+inf
+// for rows past the end, which zeroes their probabilities).
+template <int D>
+__device__ __forceinline__ void kv_finish(const KvPrefetch<D>& pf, const JFA_LDS char* dobuf, float* lse2,
+                                          float* di, int rows_valid, int tid) {
+  using C = KvCfg<D>;
+  const int cc = tid % C::CPR;
+#pragma unroll
+  for (int j = 0; j < C::DI_PASSES; ++j) {
+    const int r = tid / C::CPR + j * C::DI_ROWS_PER_PASS;
+    const bf16x8 d8 = as_bf16x8(lds_ld16(dobuf, swz_off<C::RB>(r, cc)));
+    const bf16x8 o8 = as_bf16x8(pf.o[j]);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)d8[e], (float)o8[e], acc);
+#pragma unroll
+    for (int m = C::CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (cc == 0) di[r] = acc;
+  }
+  if (tid < C::QB) lse2[tid] = tid < rows_valid ? pf.lse * kLog2e : INFINITY;
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, int tid) {
+  using C = KvCfg<D>;
+  JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int b = tile.b, h = tile.hb >> 24, j = tile.hb & 0xFFFFFF;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t s0 = p.offsets[b];
+  const int L = (int)(p.offsets[b + 1] - s0);
+  const int key0 = j * C::BN;
+  const int my_key = wave * 32 + l32;
+  const bool key_ok = my_key < L - key0;
+  const float c = p.scale_log2;
+  const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
+  const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
+  const uint16_t* ob = p.o + s0 * rs + (int64_t)h * D;
+  const float* lseb = p.lse + (int64_t)h * p.total_tokens + s0;
+  float* lse2 = (float*)(smem_raw + C::OFF_LSE);
+  float* di = (float*)(smem_raw + C::OFF_DI);
+  const int nq = (L + C::QB - 1) / C::QB;
+
+  // This wave's keys as B operands, straight from global (rows past the end -> 0).
+  bf16x8 kf[C::NKS], vf[C::NKS];
+  {
+    const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      kf[ks] = as_bf16x8(key_ok ? ld16(p.k + base + 16 * ks) : zero16());
+      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
+    }
+  }
+  KvPrefetch<D> pre;
+  kv_prefetch<D>(qb, dob, ob, lseb, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, pre, tid, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  kv_finish<D>(pre, smem + C::OFF_DO, lse2, di, min(C::QB, L), tid);
+  __syncthreads();
+
+  f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+
+  for (int it = 0; it < nq; ++it) {
+    const int cur = it & 1;
+    const int row0 = it * C::QB;
+    JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
+    JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
+    const bool has_next = it + 1 < nq;
+    const int next_rows = min(C::QB, L - row0 - C::QB);
+    if (has_next)
+      kv_prefetch<D>(qb, dob, ob, lseb, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
+                     smem + C::OFF_DO + (cur ^ 1) * C::QBUF, pre, tid, wave, lane);
+    const float* l2 = lse2 + cur * C::QB;
+    const float* dd = di + cur * C::QB;
+#pragma unroll
+    for (int qq = 0; qq < C::NQB; ++qq) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        const int off = swz_off<C::RB>(qq * 32 + l32, 2 * ks + half);
+        s = mfma32(as_bf16x8(lds_ld16(qt, off)), kf[ks], s);
+        dp = mfma32(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp);
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r4 = qq * 32 + 8 * g4 + 4 * half;
+        const float4 lv = *reinterpret_cast<const float4*>(l2 + r4);
+        const float4 dv4 = *reinterpret_cast<const float4*>(dd + r4);
+        const float la[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float pv = fast_exp2(fmaf(s[i], c, -la[e]));
+          pv = key_ok ? pv : 0.f;
+          s[i] = pv;
+          dp[i] = pv * (dp[i] - da[e]);
+        }
+      }
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 8 * u;
+        pf[u] = pack8(s[r], s[r + 1], s[r + 2], s[r + 3], s[r + 4], s[r + 5], s[r + 6], s[r + 7]);
+        dsf[u] = pack8(dp[r], dp[r + 1], dp[r + 2], dp[r + 3], dp[r + 4], dp[r + 5], dp[r + 6], dp[r + 7]);
+      }
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int t = 2 * qq + u;
+          dv[db] = mfma32(tr_operand<C::RB>(dot, 16 * t, 32 * db, lane), pf[u], dv[db]);
+          dk[db] = mfma32(tr_operand<C::RB>(qt, 16 * t, 32 * db, lane), dsf[u], dk[db]);
+        }
+      }
+    }
+    if (has_next) {
+      wait_vmem();
+      __syncthreads();
+      kv_finish<D>(pre, smem + C::OFF_DO + (cur ^ 1) * C::QBUF, lse2 + (cur ^ 1) * C::QB, di + (cur ^ 1) * C::QB,
+                   next_rows, tid);
+    }
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4;
+        st8(p.dk + row + d, pack4(dk[db][4 * g4] * p.scale, dk[db][4 * g4 + 1] * p.scale,
+                                  dk[db][4 * g4 + 2] * p.scale, dk[db][4 * g4 + 3] * p.scale));
+        st8(p.dv + row + d, pack4(dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]));
+      }
+  }
+}
+
+// Persistent tile loop shared by both kernels: static per-program lists or one
+// atomic counter (group 0 of `counters`).
+template <class F>
+__device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles, const int32_t* seg_ptr,
+                                          int32_t* counter, int* next_tile, F&& body) {
+  const int tid = threadIdx.x;
+  const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  int idx, end;
+  if (!p.dynamic) {
+    idx = seg_ptr[prog];
+    end = seg_ptr[prog + 1];
+  } else {
+    idx = prog;
+    end = seg_ptr[1];
+  }
+  while (idx < end) {
+    body(tiles[idx]);
+    if (!p.dynamic) {
+      ++idx;
+    } else {
+      if (tid == 0) *next_tile = gridDim.x + atomicAdd(counter, 1);
+      __syncthreads();
+      idx = *next_tile;
+      __syncthreads();
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kFwdWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(kDqWgPerCu * kFwdWaves / 4, kDqWgPerCu * kFwdWaves / 4)))
+    dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * DqCfg<D>::BUF];
+  __shared__ int next_tile;
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
+            [&](Tile t) { dq_tile<D>(p, t, (JFA_LDS char*)smem, threadIdx.x); });
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBwdWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(1, 1))) dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM];
+  __shared__ int next_tile;
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
+            [&](Tile t) { dkdv_tile<D>(p, t, smem, threadIdx.x); });
+}
+
+}  // namespace
+
+hipError_t launch_bwd_self(const BwdParams& p, int head_dim, hipStream_t s) {
+  if (p.dq_programs > 0) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.num_programs > 0) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace jfa

@@ -256,7 +256,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
 
 template <int D, int MODE>
 __global__ void __launch_bounds__(kFwdWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(1, 1))) fwd_kernel(FwdParams p) {
+    __attribute__((amdgpu_waves_per_eu(kFwdWgPerCu * kFwdWaves / 4, kFwdWgPerCu * kFwdWaves / 4))) fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * C::BUF];
   __shared__ int next_tile;

@@ -13,8 +13,8 @@ enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2 };
 // key/value loop streams kFwdKeys keys at a time.  A backward tile is kBwdKeys key
 // rows of one (sequence, head); its loop streams kBwdRows query rows at a time.
 // Block-diagonal tiles are one kBlock-token block of one head, one tile per wave.
-constexpr int kFwdWaves = 2;      // waves per forward workgroup
-constexpr int kFwdQPerWave = 64;  // query rows per wave (two 32-row MFMA blocks)
+constexpr int kFwdWaves = 4;      // waves per forward workgroup
+constexpr int kFwdQPerWave = 32;  // query rows per wave (one 32-row MFMA block)
 constexpr int kFwdRows = kFwdWaves * kFwdQPerWave;
 constexpr int kFwdKeys = 64;
 constexpr int kBwdWaves = 4;      // waves per backward workgroup, 32 keys each
@@ -24,8 +24,9 @@ constexpr int kBlock = 64;
 constexpr int kBdWaves = 4;
 
 // Persistent workgroups resident per CU (used for the default program count).
-constexpr int kFwdWgPerCu = 2;
+constexpr int kFwdWgPerCu = 2;    // two resident workgroups: 2 waves per SIMD
 constexpr int kBwdWgPerCu = 1;
+constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel (forward tiling)
 constexpr int kBdWgPerCu = 2;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
@@ -67,7 +68,11 @@ struct BwdParams {
   int32_t* counters;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;  // self: [T,H,D] fp32; broadcast-Q atomics: [Mq,H,D]; partials: [P,Mq,D]
+  float* dq_acc;  // broadcast-Q atomics: [Mq,H,D] fp32; partials: [P,Mq,D] fp32
+  uint16_t* dq;   // self: bf16 [T,H,D], written by the dQ kernel
+  const Tile* dq_tiles;      // self: query-row tiles of the dQ kernel
+  const int32_t* dq_seg_ptr;
+  int32_t dq_programs;
   int32_t num_seqs, num_heads, num_q, num_programs;
   int64_t total_tokens;
   int32_t dynamic;
@@ -101,6 +106,8 @@ struct BdParams {
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
+// Self-attention backward: dQ kernel (query tiles) then dK/dV kernel (key tiles).
+hipError_t launch_bwd_self(const BwdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
