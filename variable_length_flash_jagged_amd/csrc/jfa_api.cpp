@@ -105,7 +105,7 @@ int max_programs(const Opts& o, int wg_per_cu) {
 
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct Layout {
-  size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, prefix = 0, acc = 0, total = 0;
+  size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, stats = 0, prefix = 0, acc = 0, total = 0;
   int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
@@ -122,7 +122,7 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.total = at;
     return;
   }
-  const int wg = pass == JFA_PASS_FWD ? kFwdWgPerCu : kBwdWgPerCu;
+  const int wg = pass == JFA_PASS_FWD ? kFwdWgPerCu : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
   L.programs_cap = max_programs(o, wg);
   L.seg_cap = std::max<int64_t>(L.programs_cap, H) + 1;
   L.seg = at;
@@ -143,6 +143,8 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.tile2_cap = H * (T / kFwdRows + B + 1);
     L.tiles2 = at;
     at += align_up(L.tile2_cap * sizeof(Tile));
+    L.stats = at;  // per query row (lse * log2 e, Di), float2 [H, T]
+    at += align_up(H * T * 2 * sizeof(float));
   } else if (pass == JFA_PASS_BWD) {
     L.acc = at;
     const int64_t acc_elems = (o.dq_path == 0) ? Mq * H * D : (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
@@ -384,7 +386,8 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
   else if (pass == JFA_PASS_FWD)
     schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
   else
-    schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys, max_programs(o, kBwdWgPerCu), dyn, sc);
+    schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys,
+                 max_programs(o, mode == JFA_MODE_SELF ? dkdv_wg_per_cu(shape->head_dim) : kBqWgPerCu), dyn, sc);
   if (n_tiles) *n_tiles = (int64_t)sc.tiles.size();
   if (n_segs) *n_segs = (int32_t)sc.seg_ptr.size();
   if (n_programs) *n_programs = sc.programs;
@@ -538,7 +541,8 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   }
 
   Schedule sc;
-  schedule_bwd(lengths, H, mode, kBwdKeys, max_programs(op, kBwdWgPerCu), op.sched == 1, sc);
+  schedule_bwd(lengths, H, mode, kBwdKeys,
+               max_programs(op, mode == JFA_MODE_SELF ? dkdv_wg_per_cu(D) : kBqWgPerCu), op.sched == 1, sc);
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
   BwdParams p{};
   p.q = (const uint16_t*)q;
@@ -571,6 +575,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     serialise(sc, L, buf, &sq);
     if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
     p.dq = (uint16_t*)dq;
+    p.row_stats = (float2*)(ws + L.stats);
     p.dq_tiles = (const Tile*)(ws + L.tiles2);
     p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
     p.dq_programs = sq.programs;

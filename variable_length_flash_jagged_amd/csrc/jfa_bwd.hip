@@ -305,7 +305,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& p, Tile tile, int prog
 
 template <int D, int MODE>
 __global__ void __launch_bounds__(kBwdWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_kernel(BwdParams p) {
+    __attribute__((amdgpu_waves_per_eu(kBqWgPerCu, kBqWgPerCu))) bwd_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int next_tile;

@@ -12,19 +12,22 @@
 // retire at roughly 3.4e11 per second device-wide, so for long jagged batches the
 // dQ hand-off alone would outweigh the matrix work.  The self-attention backward is
 // therefore split by ownership:
+//  * dq_kernel (runs first): one workgroup = one tile of kFwdRows query rows (32 per
+//    wave), the forward's tiling and zigzag schedule; the loop streams 64-key K and V
+//    tiles through the same LDS ring as the forward.  Each lane owns one query row,
+//    so Di = rowsum(dO * O) and lse are one scalar per lane; the kernel also stores
+//    (lse * log2 e, Di) for its rows (8 bytes per row) for the second kernel.  Three
+//    products per step: S^T = K Q^T and dP^T = V dO^T (C layout: lane = query), then
+//    dQ^T += K^T dS^T with K^T read transposed from LDS and dS^T straight from
+//    registers.  dQ is written once, by its owner.
 //  * dkdv_kernel: one workgroup = one tile of kBwdKeys (128) keys of one (sequence,
 //    head); wave w owns keys 32w..32w+31 with their K, V operands and fp32 dK^T, dV^T
 //    accumulators in registers; 64 query rows stream through double-buffered,
-//    swizzled LDS tiles (direct global->LDS copies issued one step ahead).  Four
-//    products per step: S = Q K^T and dP = dO V^T (C layout: lane = key), then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed from LDS
-//    (ds_read_b64_tr_b16).  dK and dV are written once, by their owner.
-//  * dq_kernel: one workgroup = one tile of kFwdRows query rows (32 per wave), the
-//    forward's tiling and zigzag schedule; the loop streams 64-key K and V tiles
-//    through the same LDS ring as the forward.  Three products per step:
-//    S^T = K Q^T and dP^T = V dO^T (C layout: lane = query, so lse and Di are one
-//    scalar per lane), then dQ^T += K^T dS^T with K^T read transposed from LDS and dS^T
-//    straight from registers.  dQ is written once, by its owner.
+//    swizzled LDS tiles (direct global->LDS copies issued one step ahead) together
+//    with their (lse * log2 e, Di) pairs.  Four products per step: S = Q K^T and
+//    dP = dO V^T (C layout: lane = key), then dV^T += dO^T P and dK^T += Q^T dS with
+//    dO^T, Q^T read transposed from LDS (ds_read_b64_tr_b16).  dK and dV are written
+//    once, by their owner.
 // The split recomputes S and dP once more (seven products per query-key block
 // instead of five) in exchange for no atomics and no fp32 dQ accumulator in HBM.
 #include "jfa_device.h"
@@ -124,6 +127,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     di = half_sum(di);
   }
   const float lse2 = row_ok ? p.lse[(int64_t)h * p.total_tokens + s0 + row] * kLog2e : INFINITY;
+  if (row_ok && half == 0) p.row_stats[(int64_t)h * p.total_tokens + s0 + row] = make_float2(lse2, di);
 
   f32x16 dq[C::NDB];
 #pragma unroll
@@ -182,9 +186,6 @@ struct KvCfg {
   static constexpr int NDB = D / 32;
   static constexpr int RB = 2 * D;
   static constexpr int QBUF = QB * RB;
-  static constexpr int CPR = D / 8;
-  static constexpr int DI_ROWS_PER_PASS = NT / CPR;
-  static constexpr int DI_PASSES = QB / DI_ROWS_PER_PASS;
   static constexpr int OFF_Q = 0;                      // [2][QBUF]
   static constexpr int OFF_DO = OFF_Q + 2 * QBUF;      // [2][QBUF]
   static constexpr int OFF_LSE = OFF_DO + 2 * QBUF;    // float [2][QB]
@@ -192,50 +193,24 @@ struct KvCfg {
   static constexpr int SMEM = OFF_DI + 2 * QB * 4;
 };
 
+// Issue the next step's copies (Q, dO -> LDS) and its (lse * log2 e, Di) pairs.
 template <int D>
-struct KvPrefetch {
-  u32x4 o[KvCfg<D>::DI_PASSES];
-  float lse;
-};
-
-// Issue the next step's copies (Q, dO -> LDS) and register loads (O rows, lse).
-template <int D>
-__device__ __forceinline__ void kv_prefetch(const uint16_t* qb, const uint16_t* dob, const uint16_t* ob,
-                                            const float* lseb, int64_t rs, int row0, int rows_valid,
-                                            JFA_LDS char* qbuf, JFA_LDS char* dobuf, KvPrefetch<D>& pf, int tid,
-                                            int wave, int lane) {
+__device__ __forceinline__ float2 kv_prefetch(const uint16_t* qb, const uint16_t* dob, const float2* stats, int64_t rs,
+                                              int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
+                                              int tid, int wave, int lane) {
   using C = KvCfg<D>;
   dma_tile<C::RB, C::QB, C::NW>(qb + (int64_t)row0 * rs, rs, rows_valid, qbuf, wave, lane);
   dma_tile<C::RB, C::QB, C::NW>(dob + (int64_t)row0 * rs, rs, rows_valid, dobuf, wave, lane);
-  const int cc = tid % C::CPR;
-#pragma unroll
-  for (int j = 0; j < C::DI_PASSES; ++j) {
-    const int r = tid / C::CPR + j * C::DI_ROWS_PER_PASS;
-    pf.o[j] = r < rows_valid ? ld16(ob + (int64_t)(row0 + r) * rs + cc * 8) : zero16();
-  }
-  pf.lse = (tid < C::QB && tid < rows_valid) ? lseb[row0 + tid] : 0.f;
+  return (tid < C::QB && tid < rows_valid) ? stats[row0 + tid] : make_float2(INFINITY, 0.f);
 }
 
-// Di = rowsum(dO * O) (dO from its LDS tile, O from registers) and lse in base 2 (+inf
-// for rows past the end, which zeroes their probabilities).
+// Rows past the end get lse2 = +inf, which zeroes their probabilities.
 template <int D>
-__device__ __forceinline__ void kv_finish(const KvPrefetch<D>& pf, const JFA_LDS char* dobuf, float* lse2,
-                                          float* di, int rows_valid, int tid) {
-  using C = KvCfg<D>;
-  const int cc = tid % C::CPR;
-#pragma unroll
-  for (int j = 0; j < C::DI_PASSES; ++j) {
-    const int r = tid / C::CPR + j * C::DI_ROWS_PER_PASS;
-    const bf16x8 d8 = as_bf16x8(lds_ld16(dobuf, swz_off<C::RB>(r, cc)));
-    const bf16x8 o8 = as_bf16x8(pf.o[j]);
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)d8[e], (float)o8[e], acc);
-#pragma unroll
-    for (int m = C::CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (cc == 0) di[r] = acc;
+__device__ __forceinline__ void kv_finish(float2 st, float* lse2, float* di, int tid) {
+  if (tid < KvCfg<D>::QB) {
+    lse2[tid] = st.x;
+    di[tid] = st.y;
   }
-  if (tid < C::QB) lse2[tid] = tid < rows_valid ? pf.lse * kLog2e : INFINITY;
 }
 
 template <int D>
@@ -254,8 +229,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   const float c = p.scale_log2;
   const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
   const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
-  const uint16_t* ob = p.o + s0 * rs + (int64_t)h * D;
-  const float* lseb = p.lse + (int64_t)h * p.total_tokens + s0;
+  const float2* stats = p.row_stats + (int64_t)h * p.total_tokens + s0;
   float* lse2 = (float*)(smem_raw + C::OFF_LSE);
   float* di = (float*)(smem_raw + C::OFF_DI);
   const int nq = (L + C::QB - 1) / C::QB;
@@ -270,11 +244,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
       vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
     }
   }
-  KvPrefetch<D> pre;
-  kv_prefetch<D>(qb, dob, ob, lseb, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, pre, tid, wave, lane);
+  float2 pre = kv_prefetch<D>(qb, dob, stats, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, tid, wave,
+                              lane);
+  kv_finish<D>(pre, lse2, di, tid);
   wait_vmem();
-  __syncthreads();
-  kv_finish<D>(pre, smem + C::OFF_DO, lse2, di, min(C::QB, L), tid);
   __syncthreads();
 
   f32x16 dk[C::NDB], dv[C::NDB];
@@ -291,8 +264,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     const bool has_next = it + 1 < nq;
     const int next_rows = min(C::QB, L - row0 - C::QB);
     if (has_next)
-      kv_prefetch<D>(qb, dob, ob, lseb, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
-                     smem + C::OFF_DO + (cur ^ 1) * C::QBUF, pre, tid, wave, lane);
+      pre = kv_prefetch<D>(qb, dob, stats, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
+                           smem + C::OFF_DO + (cur ^ 1) * C::QBUF, tid, wave, lane);
     const float* l2 = lse2 + cur * C::QB;
     const float* dd = di + cur * C::QB;
 #pragma unroll
@@ -339,12 +312,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
         }
       }
     }
-    if (has_next) {
-      wait_vmem();
-      __syncthreads();
-      kv_finish<D>(pre, smem + C::OFF_DO + (cur ^ 1) * C::QBUF, lse2 + (cur ^ 1) * C::QB, di + (cur ^ 1) * C::QB,
-                   next_rows, tid);
-    }
+    if (has_next) kv_finish<D>(pre, lse2 + (cur ^ 1) * C::QB, di + (cur ^ 1) * C::QB, tid);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -402,7 +371,8 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
 
 template <int D>
 __global__ void __launch_bounds__(kBwdWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(1, 1))) dkdv_kernel(BwdParams p) {
+    __attribute__((amdgpu_waves_per_eu(dkdv_wg_per_cu(D) * kBwdWaves / 4, dkdv_wg_per_cu(D) * kBwdWaves / 4)))
+    dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM];
   __shared__ int next_tile;
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,

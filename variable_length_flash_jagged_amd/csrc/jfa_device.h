@@ -60,10 +60,18 @@ __device__ __forceinline__ void lds_st8(JFA_LDS char* base, int byte_off, const 
 
 // Direct global -> LDS copy (global_load_lds_dwordx4): every lane fetches 16 bytes
 // from its own global address; the wave's 64 results land contiguously at
-// lds_base + 16 * lane.  lds_base must be the same for the whole wave.  Completion is
-// tracked by vmcnt: wait_vmem() then a barrier before any wave reads the data.
+// lds_base + 16 * lane.  lds_base must be the same for the whole wave (it goes to M0).
+// Completion is tracked by vmcnt: wait_vmem() then a barrier before any wave reads the
+// data.  The instruction is issued from inline assembly on purpose: the compiler
+// cannot tell which LDS bytes the copy writes, and when it sees the copy it waits for
+// it (vmcnt(0)) before the next LDS read of the other ring slot, which would serialise
+// every prefetch with the compute it is meant to overlap.  The explicit wait_vmem() +
+// barrier at the end of each ring step orders the copy against every read of its
+// slot; copies the compiler does not see only make its own vmcnt waits more
+// conservative, never less.
 __device__ __forceinline__ void dma16(const void* gptr, JFA_LDS char* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (JFA_LDS void*)lds_base, 16, 0, 0);
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -105,12 +113,27 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 // Swizzled row-major tiles in LDS: a tile row of RB bytes holds RB/16 chunks of 16
-// bytes; chunk c of row r is stored at chunk position c ^ (r mod RB/16), so that the
-// rows read together by one MFMA operand fetch fall on different LDS banks.
+// bytes; chunk c of row r is stored at chunk position c ^ f(r).  f is chosen so that
+// both access patterns of the kernels hit distinct banks (64 banks of 4 bytes):
+//  * a row-wise operand fetch (ds_read_b128): 16 lanes read one chunk of 16
+//    consecutive rows;
+//  * a transposed fetch (ds_read_b64_tr_b16): 32 lanes read 4 consecutive chunks of 4
+//    consecutive rows (row base a multiple of 4, chunk base a multiple of 4).
+// For 256-byte rows (16 chunks) f(r) swaps the two low 2-bit fields of r; for 128-byte
+// rows (8 chunks, two rows per 256-byte bank line) f acts on x = (r/2) mod 8 as
+// (x mod 2) * 4 + x / 2.  (The plain f(r) = r mod 16 is conflict free for the first
+// pattern but costs about six extra cycles per transposed fetch.)
+template <int RB>
+__device__ __forceinline__ int swz_f(int r) {
+  static_assert(RB == 256 || RB == 128, "tile row must be 128 or 256 bytes");
+  if (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
 template <int RB>
 __device__ __forceinline__ int swz_off(int r, int c) {
-  constexpr int CPR = RB / 16;
-  return r * RB + ((c ^ (r & (CPR - 1))) << 4);
+  return r * RB + ((c ^ swz_f<RB>(r)) << 4);
 }
 
 // Copy ROWS rows of RB bytes (a row starts every `row_stride` elements at `g`) into a
@@ -124,12 +147,22 @@ __device__ __forceinline__ void dma_tile(const uint16_t* g, int64_t row_stride, 
   constexpr int RPC = 1024 / RB;            // rows per copy
   constexpr int COPIES = ROWS * RB / 1024;  // copies per tile
   static_assert(COPIES % NW == 0, "copies must split evenly over the waves");
+  if (rows_valid >= ROWS) {
 #pragma unroll
-  for (int j = 0; j < COPIES / NW; ++j) {
-    const int gi = wave * (COPIES / NW) + j;
-    const int r = gi * RPC + lane / CPR;
-    const int c = (lane % CPR) ^ (r & (CPR - 1));
-    dma16(g + (int64_t)min(r, rows_valid - 1) * row_stride + c * 8, lds + gi * 1024);
+    for (int j = 0; j < COPIES / NW; ++j) {
+      const int gi = wave * (COPIES / NW) + j;
+      const int r = gi * RPC + lane / CPR;
+      const int c = (lane % CPR) ^ swz_f<RB>(r);  // position -> logical chunk (f is an XOR)
+      dma16(g + (int64_t)r * row_stride + c * 8, lds + gi * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < COPIES / NW; ++j) {
+      const int gi = wave * (COPIES / NW) + j;
+      const int r = gi * RPC + lane / CPR;
+      const int c = (lane % CPR) ^ swz_f<RB>(r);
+      dma16(g + (int64_t)min(r, rows_valid - 1) * row_stride + c * 8, lds + gi * 1024);
+    }
   }
 }
 

@@ -25,7 +25,11 @@ constexpr int kBdWaves = 4;
 
 // Persistent workgroups resident per CU (used for the default program count).
 constexpr int kFwdWgPerCu = 2;    // two resident workgroups: 2 waves per SIMD
-constexpr int kBwdWgPerCu = 1;
+constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound over head dims
+// Resident dK/dV workgroups per CU by head dim: D=64 fits 2 waves per SIMD in 256
+// registers; D=128 needs the full 512 (1 wave per SIMD) to avoid spilling.
+constexpr int dkdv_wg_per_cu(int head_dim) { return head_dim == 64 ? 2 : 1; }
+constexpr int kBqWgPerCu = 1;     // broadcast-Q fused backward
 constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel (forward tiling)
 constexpr int kBdWgPerCu = 2;
 
@@ -70,6 +74,7 @@ struct BwdParams {
   uint16_t* dv;
   float* dq_acc;  // broadcast-Q atomics: [Mq,H,D] fp32; partials: [P,Mq,D] fp32
   uint16_t* dq;   // self: bf16 [T,H,D], written by the dQ kernel
+  float2* row_stats;         // self: [H,T] (lse * log2 e, Di) per query row, written by the dQ kernel
   const Tile* dq_tiles;      // self: query-row tiles of the dQ kernel
   const int32_t* dq_seg_ptr;
   int32_t dq_programs;
