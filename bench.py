@@ -13,11 +13,15 @@ variable_length_flash_jagged_amd/workloads.py) instead.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "valid-token TFLOPS fwd+bwd (bf16, D=128 jagged) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -36,7 +40,63 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scales HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench with "
+                         "--calibrate-copy-mib into profiles/traffic_<workload>.json and exit")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """Digest of the kernel sources; traffic counters are only reported for the build
+    they were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "variable_length_flash_jagged_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_NAMES = {"fwd_kernel": "fwd_kernel<", "dq_kernel": "dq_kernel<", "dkdv_kernel": "dkdv_kernel<",
+                "bwd_kernel": "bwd_kernel<", "bd_fwd_kernel": "bd_fwd_kernel<", "bd_bwd_kernel": "bd_bwd_kernel<"}
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, copy_mib):
+    """Per-kernel average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) and the scale factors
+    that map the counters onto the bytes of the calibration copy."""
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+    out = {"workload": workload, "src_digest": kernel_source_digest(), "calibration_copy_mib": copy_mib}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        out[f"{counter}_scale"] = (copy_mib * 1024.0) / max(copies) if copies and max(copies) > 0 else None
+        for short, key in KERNEL_NAMES.items():
+            vals = [v for n, v in rows if key in n]
+            if vals:
+                out.setdefault("kernels", {}).setdefault(short, {})[counter + "_kib"] = sum(vals) / len(vals)
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(path)
+
+
+def traffic_bytes(workload, kernel):
+    """Calibrated HBM bytes per launch of `kernel` from profiles/, or None when absent or
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    k = t.get("kernels", {}).get(kernel)
+    if t.get("src_digest") != kernel_source_digest() or not k or not t.get("FETCH_SIZE_scale") \
+            or not t.get("WRITE_SIZE_scale"):
+        return None
+    return int(1024 * (k["FETCH_SIZE_kib"] * t["FETCH_SIZE_scale"] + k["WRITE_SIZE_kib"] * t["WRITE_SIZE_scale"]))
 
 
 def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
@@ -73,6 +133,11 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        from variable_length_flash_jagged_amd import workloads as W
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], W.WORKLOADS[args.workload]["name"],
+                      args.calibrate_copy_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -139,8 +204,8 @@ def main():
     ms_step = total_ms / args.steps
     fwd_ms = sum(ev["f0"][i].elapsed_time(ev["f1"][i]) for i in range(args.steps)) / args.steps
     bwd_ms = sum(ev["f1"][i].elapsed_time(ev["b1"][i]) for i in range(args.steps)) / args.steps
-    nf, kf_ms = B.kernel_times(B.PASS_FWD)
-    nb, kb_ms = B.kernel_times(B.PASS_BWD)
+    kt = {name: B.kernel_times(kid) for name, kid in
+          (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ))}
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
@@ -148,24 +213,43 @@ def main():
     bytes_f = M.fwd_bytes(lengths, mode, h, d, mq)
     bytes_b = M.bwd_bytes(lengths, mode, h, d, mq)
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
-    kern_f = kf_ms / max(nf, 1)
-    kern_b = kb_ms / max(nb, 1)
-    hbm_bound = mode == W.MODE_BLOCK_DIAG
-    # dominant kernel: the one with the larger total time per step
-    if kern_b >= kern_f:
-        dom, dom_ms, dom_flops, dom_bytes = "bwd", kern_b, fb, bytes_b
+    # Per attention kernel: average launch time and the algorithmic work of one launch.
+    # Self mode runs the backward as a dQ kernel (S, dP, dQ: 3 of the 5 products plus
+    # the 2 it recomputes) and a dK/dV kernel (S, dP, dV, dK).
+    work = {"fwd": (ff, bytes_f)}
+    if mode == W.MODE_SELF:
+        pairs = M.valid_pairs(lengths, mode)
+        t = int(p["total_tokens"])
+        work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 12 * t * h)
+        work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 8 * t * h)
     else:
-        dom, dom_ms, dom_flops, dom_bytes = "fwd", kern_f, ff, bytes_f
+        work["bwd"] = (fb, bytes_b)
+    kernels = {}
+    for name, (fl, by) in work.items():
+        n, tot = kt[name]
+        if n == 0:
+            continue
+        ms = tot / n
+        kernels[name] = {"launches_per_step": n // args.steps, "ms": round(ms, 4), "flops": fl, "bytes": by,
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+    hbm_bound = mode == W.MODE_BLOCK_DIAG
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
     if hbm_bound:
-        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        achieved = kd["bytes"] / (kd["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+        achieved = kd["flops"] / (kd["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = f"{dom}_kernel"
-    roof["kernel_ms"] = round(dom_ms, 4)
+    roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
+                      ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
+                      "bwd_dq": "dq_kernel"}[dom]
+    if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
+        roof["kernel"] = "bd_fwd_kernel"
+    roof["kernel_ms"] = kd["ms"]
+    roof["traffic"] = traffic_bytes(w["name"], roof["kernel"])
 
     out = {
         "metric": METRIC,
@@ -189,11 +273,12 @@ def main():
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
-                "kernel_ms": round(kern_f, 4), "kernel_tflops": round(ff / (kern_f * 1e-3) / 1e12, 1),
-                "kernel_gbs": round(bytes_f / (kern_f * 1e-3) / 1e9, 1), "flops": ff, "bytes": bytes_f},
+                "pct_of_peak": round(100 * ff / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "flops": ff, "bytes": bytes_f},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 1),
-                "kernel_ms": round(kern_b, 4), "kernel_tflops": round(fb / (kern_b * 1e-3) / 1e12, 1),
-                "kernel_gbs": round(bytes_b / (kern_b * 1e-3) / 1e9, 1), "flops": fb, "bytes": bytes_b},
+                "pct_of_peak": round(100 * fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "flops": fb, "bytes": bytes_b},
+        "kernels": kernels,
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }

@@ -141,15 +141,23 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
                  int64_t seg_cap, int64_t* n_tiles, int32_t* n_segs, int32_t* n_programs,
                  int32_t* tile_rows);
 
+/* Attention kernels timed by the measurement hook below. */
+enum jfa_kernel {
+  JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd */
+  JFA_KERNEL_BWD = 1,    /* the main backward kernel of jfa_bwd: the dK/dV kernel in self
+                            mode, the fused kernel in broadcast-Q and block-diagonal modes */
+  JFA_KERNEL_BWD_DQ = 2  /* self mode only: the dQ kernel of jfa_bwd */
+};
+
 /* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd call records a
- * pair of HIP events on its stream immediately around its main attention kernel
+ * pair of HIP events on its stream immediately around each of its attention kernels
  * (not the schedule upload or the dQ fill / cast / reduce kernels).  jfa_kernel_times
- * waits for the events recorded so far for `pass` (JFA_PASS_FWD or JFA_PASS_BWD) and
- * returns the number of launches and their summed duration in milliseconds; reset != 0
- * then forgets them.  Enabling or disabling also forgets them.  Events are created by
- * the library on the calling thread's current device and released when forgotten. */
+ * waits for the events recorded so far for `kernel` (a jfa_kernel) and returns the
+ * number of launches and their summed duration in milliseconds; reset != 0 then
+ * forgets them.  Enabling or disabling also forgets them.  Events are created by the
+ * library on the calling thread's current device and released when forgotten. */
 int jfa_kernel_timing(int enable);
-int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset);
+int jfa_kernel_times(int kernel, int64_t* launches, double* total_ms, int reset);
 
 /* Static message for a status code. */
 const char* jfa_error_string(int code);

@@ -1,0 +1,62 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+Each workload is generated at full size on the GPU and run through jfa_fwd / jfa_bwd
+with default options (the bench's static schedule; both broadcast-Q dQ paths).  The
+oracle then checks sampled sequences one by one -- the longest, the shortest, the
+median and a few seeded picks -- since in self and block-diagonal attention every
+sequence's outputs and gradients depend on that sequence alone.  Broadcast-Q (whose
+dQ sums over all sequences) is small enough to check whole."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import gpu_helpers as G
+from variable_length_flash_jagged_amd import binding as B
+from variable_length_flash_jagged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_sequences(lengths, k, seed):
+    order = np.argsort(lengths, kind="stable")
+    picks = {int(order[-1]), int(order[0]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(seed)
+    while len(picks) < min(k, len(lengths)):
+        picks.add(int(rng.integers(0, len(lengths))))
+    return sorted(picks)
+
+
+def _run(workload, opts=None):
+    print(f"[case] full-size workload {workload} opts={opts}", flush=True)
+    p = W.make_workload(workload, seed=0, device="cuda")
+    o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts)
+    grads = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"], p["scale"],
+                  opts)
+    torch.cuda.synchronize()
+    return p, o, lse, grads
+
+
+@pytest.mark.parametrize("workload,samples", [(1, 4), (3, 6), (4, 1), (5, 6)])
+def test_full_size_sampled_sequences(workload, samples):
+    p, o, lse, (dq, dk, dv) = _run(workload)
+    off = p["offsets_host"].astype(np.int64)
+    mode = p["mode"]
+    for b in _sample_sequences(p["lengths"], samples, workload):
+        s, e = int(off[b]), int(off[b + 1])
+        sub = lambda t: G.f64(t[s:e])
+        q, k, v, do = sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"])
+        sub_off = [0, e - s]
+        o_ref, lse_ref = oracle.attention_forward(q, k, v, sub_off, mode, p["scale"])
+        G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"workload {workload} seq {b} (L={e - s})")
+        refs = oracle.attention_backward(q, k, v, do, sub_off, mode, p["scale"])
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload {workload} seq {b} (L={e - s})")
+
+
+@pytest.mark.parametrize("dq_path", [0, 1])
+def test_full_size_broadcast_q(dq_path):
+    p, o, lse, grads = _run(2, B.make_opts(dq_path=dq_path))
+    o_ref, lse_ref = G.oracle_fwd(p)
+    G.check_fwd(o, lse, o_ref, lse_ref, "workload 2 full")
+    G.check_bwd(grads, G.oracle_bwd(p), "workload 2 full")

@@ -18,6 +18,9 @@ MODE_BROADCAST_Q = 1
 MODE_BLOCK_DIAG = 2
 PASS_FWD = 0
 PASS_BWD = 1
+KERNEL_FWD = 0
+KERNEL_BWD = 1
+KERNEL_BWD_DQ = 2
 
 
 class JfaError(RuntimeError):
@@ -115,10 +118,10 @@ def kernel_timing(enable):
     _check(lib().jfa_kernel_timing(1 if enable else 0), "jfa_kernel_timing")
 
 
-def kernel_times(pass_, reset=False):
-    """(launches, total_ms) of the main kernel of pass_ since the last reset."""
+def kernel_times(kernel, reset=False):
+    """(launches, total_ms) of one attention kernel (KERNEL_*) since the last reset."""
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
-    _check(lib().jfa_kernel_times(pass_, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0), "jfa_kernel_times")
+    _check(lib().jfa_kernel_times(kernel, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0), "jfa_kernel_times")
     return int(n.value), float(ms.value)
 
 

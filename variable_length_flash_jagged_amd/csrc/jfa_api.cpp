@@ -258,7 +258,7 @@ int launch_status(hipError_t e, const char* what) {
 struct KernelTimer {
   std::mutex mu;
   bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[2];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[3];
   void forget_locked() {
     for (auto& v : ev) {
       for (auto& pr : v) {
@@ -310,7 +310,8 @@ int jfa_kernel_timing(int enable) {
 
 int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
   g_detail.clear();
-  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return fail(JFA_ERR_BAD_MODE, "pass must be 0 or 1");
+  if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ)
+    return fail(JFA_ERR_BAD_MODE, "kernel must be JFA_KERNEL_FWD, JFA_KERNEL_BWD or JFA_KERNEL_BWD_DQ");
   if (!launches || !total_ms) return fail(JFA_ERR_NULL_POINTER, "launches and total_ms must be non-NULL");
   std::lock_guard<std::mutex> lock(g_timer.mu);
   double sum = 0.0;
@@ -579,8 +580,11 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.dq_tiles = (const Tile*)(ws + L.tiles2);
     p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
     p.dq_programs = sq.programs;
-    return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self(p, D, stream); }),
-                         "backward launch");
+    if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq(p, D, stream); }),
+                            "backward dQ launch")))
+      return rc;
+    return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                         "backward dK/dV launch");
   }
 
   // Broadcast-Q: one fused kernel; dQ summed over all sequences through fp32 atomics

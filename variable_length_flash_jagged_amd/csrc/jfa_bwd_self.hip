@@ -381,23 +381,22 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
 
 }  // namespace
 
-hipError_t launch_bwd_self(const BwdParams& p, int head_dim, hipStream_t s) {
-  if (p.dq_programs > 0) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
-    else
-      hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.num_programs > 0) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
-    else
-      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s) {
+  if (p.dq_programs <= 0) return hipSuccess;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s) {
+  if (p.num_programs <= 0) return hipSuccess;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(dkdv_kernel<64>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL(dkdv_kernel<128>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace jfa

@@ -111,8 +111,10 @@ struct BdParams {
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
-// Self-attention backward: dQ kernel (query tiles) then dK/dV kernel (key tiles).
-hipError_t launch_bwd_self(const BwdParams& p, int head_dim, hipStream_t s);
+// Self-attention backward: dQ kernel (query tiles; also writes the per-row stats the
+// dK/dV kernel reads, so it runs first) and dK/dV kernel (key tiles).
+hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s);
+hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
