@@ -52,15 +52,23 @@ struct DqCfg {
   static constexpr int BUF = BN * RB;
 };
 
+// Per-lane constants of the dQ loop: LDS operand offsets and ring-copy offsets.
+template <int D>
+struct DqLane {
+  RowOperands<DqCfg<D>::RB, DqCfg<D>::NKS> row;  // K, V rows as A operands of S^T, dP^T
+  TrOperands<DqCfg<D>::RB, DqCfg<D>::NDB> ktr;   // K^T as the A operand of dQ^T
+  TileCopy<DqCfg<D>::RB, DqCfg<D>::BN, DqCfg<D>::NW> copy;
+};
+
 // One key/value tile for this wave's 32 query rows.  MASK: keys >= keys_valid lie past
 // the end of the sequence.
 template <int D, bool MASK>
-__device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf,
+__device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf, const DqLane<D>& ln,
                                         const bf16x8 (&qf)[DqCfg<D>::NKS], const bf16x8 (&dof)[DqCfg<D>::NKS],
                                         f32x16 (&dq)[DqCfg<D>::NDB], float lse2, float di, int lane,
                                         int keys_valid, float c) {
   using C = DqCfg<D>;
-  const int l32 = lane & 31, half = lane >> 5;
+  const int half = lane >> 5;
   f32x16 s[C::NKB], dp[C::NKB];
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb)
@@ -70,9 +78,8 @@ __device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS 
   for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
-      const int off = swz_off<C::RB>(kb * 32 + l32, 2 * ks + half);
-      s[kb] = mfma32(as_bf16x8(lds_ld16(kbuf, off)), qf[ks], s[kb]);
-      dp[kb] = mfma32(as_bf16x8(lds_ld16(vbuf, off)), dof[ks], dp[kb]);
+      s[kb] = mfma32(ln.row.read(kbuf, kb * 32, ks), qf[ks], s[kb]);
+      dp[kb] = mfma32(ln.row.read(vbuf, kb * 32, ks), dof[ks], dp[kb]);
     }
   }
   // P^T = 2^(S^T c - lse2), dS^T = P^T (dP^T - Di); lane = query, register i <-> key.
@@ -94,12 +101,13 @@ __device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS 
     const int r = 8 * (t & 1);
     const bf16x8 b = pack8(src[r], src[r + 1], src[r + 2], src[r + 3], src[r + 4], src[r + 5], src[r + 6], src[r + 7]);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) dq[db] = mfma32(tr_operand<C::RB>(kbuf, 16 * t, 32 * db, lane), b, dq[db]);
+    for (int db = 0; db < C::NDB; ++db) dq[db] = mfma32(ln.ktr.read(kbuf, 16 * t, db), b, dq[db]);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, int tid) {
+__device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, const DqLane<D>& ln,
+                                        int tid) {
   using C = DqCfg<D>;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -139,27 +147,28 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
   const int n_kv = n_full + (tail != 0);
   const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
   const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
-  dma_tile<C::RB, C::BN, C::NW>(kp, rs, min(C::BN, L), smem, wave, lane);
-  dma_tile<C::RB, C::BN, C::NW>(vp, rs, min(C::BN, L), smem + C::BUF, wave, lane);
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  ln.copy.issue_rows(kp, rsb, min(C::BN, L), smem, wave, lane);
+  ln.copy.issue_rows(vp, rsb, min(C::BN, L), smem + C::BUF, wave, lane);
   wait_vmem();
   __syncthreads();
   for (int it = 0; it < n_full; ++it) {
     const int cur = it & 1;
     if (it + 1 < n_kv) {
-      const int64_t nxt = (int64_t)(it + 1) * C::BN;
+      const int64_t nxt = (int64_t)(it + 1) * C::BN * rs;
       const int rv = min(C::BN, L - (it + 1) * C::BN);
       JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
-      dma_tile<C::RB, C::BN, C::NW>(kp + nxt * rs, rs, rv, nbuf, wave, lane);
-      dma_tile<C::RB, C::BN, C::NW>(vp + nxt * rs, rs, rv, nbuf + C::BUF, wave, lane);
+      ln.copy.issue_rows(kp + nxt, rsb, rv, nbuf, wave, lane);
+      ln.copy.issue_rows(vp + nxt, rsb, rv, nbuf + C::BUF, wave, lane);
     }
     JFA_LDS char* kbuf = smem + cur * 2 * C::BUF;
-    dq_step<D, false>(kbuf, kbuf + C::BUF, qf, dof, dq, lse2, di, lane, C::BN, c);
+    dq_step<D, false>(kbuf, kbuf + C::BUF, ln, qf, dof, dq, lse2, di, lane, C::BN, c);
     wait_vmem();
     __syncthreads();
   }
   if (tail) {
     JFA_LDS char* kbuf = smem + (n_full & 1) * 2 * C::BUF;
-    dq_step<D, true>(kbuf, kbuf + C::BUF, qf, dof, dq, lse2, di, lane, tail, c);
+    dq_step<D, true>(kbuf, kbuf + C::BUF, ln, qf, dof, dq, lse2, di, lane, tail, c);
     __syncthreads();
   }
   if (row_ok) {
@@ -193,14 +202,23 @@ struct KvCfg {
   static constexpr int SMEM = OFF_DI + 2 * QB * 4;
 };
 
+// Per-lane constants of the dK/dV loop: LDS operand offsets and ring-copy offsets.
+template <int D>
+struct KvLane {
+  RowOperands<KvCfg<D>::RB, KvCfg<D>::NKS> row;  // Q, dO rows as A operands of S, dP
+  TrOperands<KvCfg<D>::RB, KvCfg<D>::NDB> tr;    // Q^T, dO^T as A operands of dK^T, dV^T
+  TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, KvCfg<D>::NW> copy;
+};
+
 // Issue the next step's copies (Q, dO -> LDS) and its (lse * log2 e, Di) pairs.
 template <int D>
-__device__ __forceinline__ float2 kv_prefetch(const uint16_t* qb, const uint16_t* dob, const float2* stats, int64_t rs,
-                                              int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
-                                              int tid, int wave, int lane) {
+__device__ __forceinline__ float2 kv_prefetch(const KvLane<D>& ln, const uint16_t* qb, const uint16_t* dob,
+                                              const float2* stats, int64_t rs, int row0, int rows_valid,
+                                              JFA_LDS char* qbuf, JFA_LDS char* dobuf, int tid, int wave, int lane) {
   using C = KvCfg<D>;
-  dma_tile<C::RB, C::QB, C::NW>(qb + (int64_t)row0 * rs, rs, rows_valid, qbuf, wave, lane);
-  dma_tile<C::RB, C::QB, C::NW>(dob + (int64_t)row0 * rs, rs, rows_valid, dobuf, wave, lane);
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rows_valid, qbuf, wave, lane);
+  ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rows_valid, dobuf, wave, lane);
   return (tid < C::QB && tid < rows_valid) ? stats[row0 + tid] : make_float2(INFINITY, 0.f);
 }
 
@@ -214,7 +232,8 @@ __device__ __forceinline__ void kv_finish(float2 st, float* lse2, float* di, int
 }
 
 template <int D>
-__device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, int tid) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D>& ln,
+                                          int tid) {
   using C = KvCfg<D>;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int lane = tid & 63, wave = tid >> 6;
@@ -244,8 +263,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
       vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
     }
   }
-  float2 pre = kv_prefetch<D>(qb, dob, stats, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, tid, wave,
-                              lane);
+  float2 pre = kv_prefetch<D>(ln, qb, dob, stats, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, tid,
+                              wave, lane);
   kv_finish<D>(pre, lse2, di, tid);
   wait_vmem();
   __syncthreads();
@@ -264,7 +283,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     const bool has_next = it + 1 < nq;
     const int next_rows = min(C::QB, L - row0 - C::QB);
     if (has_next)
-      pre = kv_prefetch<D>(qb, dob, stats, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
+      pre = kv_prefetch<D>(ln, qb, dob, stats, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
                            smem + C::OFF_DO + (cur ^ 1) * C::QBUF, tid, wave, lane);
     const float* l2 = lse2 + cur * C::QB;
     const float* dd = di + cur * C::QB;
@@ -275,9 +294,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
-        const int off = swz_off<C::RB>(qq * 32 + l32, 2 * ks + half);
-        s = mfma32(as_bf16x8(lds_ld16(qt, off)), kf[ks], s);
-        dp = mfma32(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp);
+        s = mfma32(ln.row.read(qt, qq * 32, ks), kf[ks], s);
+        dp = mfma32(ln.row.read(dot, qq * 32, ks), vf[ks], dp);
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -307,8 +325,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int t = 2 * qq + u;
-          dv[db] = mfma32(tr_operand<C::RB>(dot, 16 * t, 32 * db, lane), pf[u], dv[db]);
-          dk[db] = mfma32(tr_operand<C::RB>(qt, 16 * t, 32 * db, lane), dsf[u], dk[db]);
+          dv[db] = mfma32(ln.tr.read(dot, 16 * t, db), pf[u], dv[db]);
+          dk[db] = mfma32(ln.tr.read(qt, 16 * t, db), dsf[u], dk[db]);
         }
       }
     }
@@ -365,8 +383,12 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[4 * DqCfg<D>::BUF];
   __shared__ int next_tile;
+  DqLane<D> ln;
+  ln.row.init(threadIdx.x & 63);
+  ln.ktr.init(threadIdx.x & 63);
+  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
-            [&](Tile t) { dq_tile<D>(p, t, (JFA_LDS char*)smem, threadIdx.x); });
+            [&](Tile t) { dq_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
 template <int D>
@@ -375,8 +397,12 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
     dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM];
   __shared__ int next_tile;
+  KvLane<D> ln;
+  ln.row.init(threadIdx.x & 63);
+  ln.tr.init(threadIdx.x & 63);
+  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
-            [&](Tile t) { dkdv_tile<D>(p, t, smem, threadIdx.x); });
+            [&](Tile t) { dkdv_tile<D>(p, t, smem, ln, threadIdx.x); });
 }
 
 }  // namespace

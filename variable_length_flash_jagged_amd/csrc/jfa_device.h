@@ -58,20 +58,29 @@ __device__ __forceinline__ void lds_st8(JFA_LDS char* base, int byte_off, const 
   *reinterpret_cast<JFA_LDS u32x2*>(base + byte_off) = v;
 }
 
-// Direct global -> LDS copy (global_load_lds_dwordx4): every lane fetches 16 bytes
-// from its own global address; the wave's 64 results land contiguously at
-// lds_base + 16 * lane.  lds_base must be the same for the whole wave (it goes to M0).
-// Completion is tracked by vmcnt: wait_vmem() then a barrier before any wave reads the
-// data.  The instruction is issued from inline assembly on purpose: the compiler
-// cannot tell which LDS bytes the copy writes, and when it sees the copy it waits for
-// it (vmcnt(0)) before the next LDS read of the other ring slot, which would serialise
-// every prefetch with the compute it is meant to overlap.  The explicit wait_vmem() +
-// barrier at the end of each ring step orders the copy against every read of its
-// slot; copies the compiler does not see only make its own vmcnt waits more
-// conservative, never less.
-__device__ __forceinline__ void dma16(const void* gptr, JFA_LDS char* lds_base) {
+// A pointer the whole wave agrees on, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global -> LDS copy (global_load_lds_dwordx4): every lane fetches 16 bytes at
+// sbase + voff (sbase in scalar registers, voff a per-lane byte offset); the wave's 64
+// results land contiguously at lds_base + 16 * lane.  sbase and lds_base must be the
+// same for the whole wave (lds_base goes to M0).  Completion is tracked by vmcnt:
+// wait_vmem() then a barrier before any wave reads the data.  The instruction is
+// issued from inline assembly on purpose: the compiler cannot tell which LDS bytes the
+// copy writes, and when it sees the copy it waits for it (vmcnt(0)) before the next LDS
+// read of the other ring slot, which would serialise every prefetch with the compute
+// it is meant to overlap.  The explicit wait_vmem() + barrier at the end of each ring
+// step orders the copy against every read of its slot; copies the compiler does not
+// see only make its own vmcnt waits more conservative, never less.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, JFA_LDS char* lds_base) {
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -136,49 +145,110 @@ __device__ __forceinline__ int swz_off(int r, int c) {
   return r * RB + ((c ^ swz_f<RB>(r)) << 4);
 }
 
-// Copy ROWS rows of RB bytes (a row starts every `row_stride` elements at `g`) into a
-// swizzled LDS tile with the 1 KB wave-wide direct copies, split over NW waves.  Rows
-// at or past `rows_valid` repeat row rows_valid-1, so every read stays inside the
-// caller's valid rows; the caller masks their contribution.
+// Copies of a ROWS x RB-byte tile (a row starts every row_stride_bytes in global memory)
+// into a swizzled LDS tile with the 1 KB wave-wide direct copies, split over NW waves.
+// init() precomputes this lane's byte offsets once per kernel, so a full-tile copy
+// costs no vector ALU work; rows at or past rows_valid (tail tiles) repeat row
+// rows_valid-1, so every read stays inside the caller's valid rows -- the caller masks
+// their contribution.
+template <int RB, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int CPR = RB / 16;            // chunks per row
+  static constexpr int RPC = 1024 / RB;          // rows per copy
+  static constexpr int COPIES = ROWS * RB / 1024;
+  static constexpr int J = COPIES / NW;          // copies per wave
+  static_assert(COPIES % NW == 0, "copies must split evenly over the waves");
+  uint32_t off[J];
+  __device__ __forceinline__ static int row_of(int wave, int j, int lane) { return (wave * J + j) * RPC + lane / CPR; }
+  __device__ __forceinline__ static int chunk_of(int r, int lane) { return (lane % CPR) ^ swz_f<RB>(r); }
+  __device__ __forceinline__ void init(uint32_t row_stride_bytes, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int r = row_of(wave, j, lane);
+      off[j] = (uint32_t)r * row_stride_bytes + (uint32_t)chunk_of(r, lane) * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(const void* gbase, JFA_LDS char* lds, int wave) const {
+    const void* b = uniform_ptr(gbase);
+#pragma unroll
+    for (int j = 0; j < J; ++j) dma16(b, off[j], lds + (wave * J + j) * 1024);
+  }
+  __device__ __forceinline__ static void issue_clamped(const void* gbase, uint32_t row_stride_bytes, int rows_valid,
+                                                       JFA_LDS char* lds, int wave, int lane) {
+    const void* b = uniform_ptr(gbase);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int r = row_of(wave, j, lane);
+      const uint32_t o = (uint32_t)min(r, rows_valid - 1) * row_stride_bytes + (uint32_t)chunk_of(r, lane) * 16u;
+      dma16(b, o, lds + (wave * J + j) * 1024);
+    }
+  }
+  __device__ __forceinline__ void issue_rows(const void* gbase, uint32_t row_stride_bytes, int rows_valid,
+                                             JFA_LDS char* lds, int wave, int lane) const {
+    if (rows_valid >= ROWS) issue(gbase, lds, wave);
+    else issue_clamped(gbase, row_stride_bytes, rows_valid, lds, wave, lane);
+  }
+};
+
+// Byte pointer arithmetic on bf16 data.
+__device__ __forceinline__ const void* bf16_at(const uint16_t* base, int64_t elems) { return base + elems; }
+
+// Row-wise MFMA operand fetch (A or B: lane = row l%32 of a 32-row block, slots =
+// head-dim chunk 2*ks + half) from a swizzled tile; offsets precomputed per lane.  The
+// swizzle of row rbase + l%32 equals that of l%32 because rbase is a multiple of 32.
+template <int RB, int NKS>
+struct RowOperands {
+  int off[NKS];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) off[ks] = l32 * RB + (((2 * ks + half) ^ swz_f<RB>(l32)) << 4);
+  }
+  __device__ __forceinline__ bf16x8 read(const JFA_LDS char* tile, int rbase, int ks) const {
+    return as_bf16x8(lds_ld16(tile, rbase * RB + off[ks]));
+  }
+};
+
+// Transposed MFMA operand (ds_read_b64_tr_b16) from a swizzled row-major bf16 tile:
+// lane l of 16-lane group g gets column 32*cb + 16*(g & 1) + (l & 15) of rows
+// row0 + 4*(g >> 1) + {0..3} (slots 0-3) and the same rows + 8 (slots 4-7) -- the
+// operand whose k index runs over tile rows in the order a 32x32 C layout hands them
+// over (register 8u+j <-> row 16u + 8*(j/4) + 4*half + j%4).  row0 is a multiple of
+// 16, so the swizzle of each source row depends on the lane only.
+template <int RB, int NCB>
+struct TrOperands {
+  int off[NCB][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, s16 = lane & 15;
+    const int rr = 4 * (g >> 1) + (s16 >> 2);
+    const int cc = 16 * (g & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = rr + 8 * hi, col = 32 * cb + cc;
+        off[cb][hi] = r * RB + (((col >> 3) ^ swz_f<RB>(r)) << 4) + (col & 7) * 2;
+      }
+  }
+  __device__ __forceinline__ bf16x8 read(const JFA_LDS char* tile, int row0, int cb) const {
+    return join_tr(lds_tr4(tile, row0 * RB + off[cb][0]), lds_tr4(tile, row0 * RB + off[cb][1]));
+  }
+};
+
+// Generic forms (offsets computed per call) for the less hot kernels.
 template <int RB, int ROWS, int NW>
 __device__ __forceinline__ void dma_tile(const uint16_t* g, int64_t row_stride, int rows_valid,
                                          JFA_LDS char* lds, int wave, int lane) {
-  constexpr int CPR = RB / 16;
-  constexpr int RPC = 1024 / RB;            // rows per copy
-  constexpr int COPIES = ROWS * RB / 1024;  // copies per tile
-  static_assert(COPIES % NW == 0, "copies must split evenly over the waves");
-  if (rows_valid >= ROWS) {
-#pragma unroll
-    for (int j = 0; j < COPIES / NW; ++j) {
-      const int gi = wave * (COPIES / NW) + j;
-      const int r = gi * RPC + lane / CPR;
-      const int c = (lane % CPR) ^ swz_f<RB>(r);  // position -> logical chunk (f is an XOR)
-      dma16(g + (int64_t)r * row_stride + c * 8, lds + gi * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < COPIES / NW; ++j) {
-      const int gi = wave * (COPIES / NW) + j;
-      const int r = gi * RPC + lane / CPR;
-      const int c = (lane % CPR) ^ swz_f<RB>(r);
-      dma16(g + (int64_t)min(r, rows_valid - 1) * row_stride + c * 8, lds + gi * 1024);
-    }
-  }
+  TileCopy<RB, ROWS, NW>::issue_clamped(g, (uint32_t)(row_stride * 2), rows_valid, lds, wave, lane);
 }
 
-// Transposed MFMA operand from a swizzled row-major bf16 tile (RB bytes per row):
-// lane l of 16-lane group g gets column col0 + 16*(g & 1) + (l & 15) of rows
-// row0 + 4*(g >> 1) + {0..3} (slots 0-3) and the same rows + 8 (slots 4-7).  This is
-// the operand whose k index runs over tile rows in the order a 32x32 C layout hands
-// them over (register 8u+j <-> row 16u' + 8*(j/4) + 4*half + j%4).
 template <int RB>
 __device__ __forceinline__ bf16x8 tr_operand(const JFA_LDS char* tile, int row0, int col0, int lane) {
   const int g = lane >> 4, s16 = lane & 15;
   const int r = row0 + 4 * (g >> 1) + (s16 >> 2);
   const int col = col0 + 16 * (g & 1) + 4 * (s16 & 3);
   const int w8 = (col & 7) * 2;
-  return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8),
-                 lds_tr4(tile, swz_off<RB>(r + 8, col >> 3) + w8));
+  return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8), lds_tr4(tile, swz_off<RB>(r + 8, col >> 3) + w8));
 }
 
 // Workgroups are dealt to the 8 XCDs round robin by workgroup id; number the programs

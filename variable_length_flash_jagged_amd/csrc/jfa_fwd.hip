@@ -52,16 +52,24 @@ struct FwdCfg {
   static_assert(NT16 == 2 * NKB, "key steps");
 };
 
+// Per-lane constants of the loop: LDS operand offsets and ring-copy offsets.
+template <int D>
+struct FwdLane {
+  RowOperands<FwdCfg<D>::RB, FwdCfg<D>::NKS> krow;  // K rows as the A operand of S^T
+  TrOperands<FwdCfg<D>::RB, FwdCfg<D>::NDB> vtr;     // V^T as the A operand of O^T
+  TileCopy<FwdCfg<D>::RB, FwdCfg<D>::BN, FwdCfg<D>::NW> copy;
+};
+
 // One key/value tile for this wave's query rows.  MASK: keys >= keys_valid lie past
 // the end of the sequence (tail tile only).
 template <int D, bool MASK>
-__device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf,
+__device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf, const FwdLane<D>& ln,
                                          const bf16x8 (&qf)[FwdCfg<D>::NQB][FwdCfg<D>::NKS],
                                          f32x16 (&o)[FwdCfg<D>::NDB][FwdCfg<D>::NQB],
                                          float (&m)[FwdCfg<D>::NQB], float (&l)[FwdCfg<D>::NQB],
                                          int lane, int keys_valid, float c) {
   using C = FwdCfg<D>;
-  const int l32 = lane & 31, half = lane >> 5;
+  const int half = lane >> 5;
 
   // S^T = K Q^T : [keys x queries]; C layout -> lane = query column,
   // register i of key block kb <-> key 32*kb + 8*(i/4) + 4*half + i%4.
@@ -76,7 +84,7 @@ __device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS
   for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
-      const bf16x8 a = as_bf16x8(lds_ld16(kbuf, swz_off<C::RB>(kb * 32 + l32, 2 * ks + half)));
+      const bf16x8 a = ln.krow.read(kbuf, kb * 32, ks);
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) s[kb][qb] = mfma32(a, qf[qb][ks], s[kb][qb]);
     }
@@ -151,7 +159,7 @@ __device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS
   for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
     for (int t = 0; t < C::NT16; ++t) {
-      const bf16x8 a = tr_operand<C::RB>(vbuf, 16 * t, 32 * db, lane);
+      const bf16x8 a = ln.vtr.read(vbuf, 16 * t, db);
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) o[db][qb] = mfma32(a, pf[qb][t], o[db][qb]);
     }
@@ -159,7 +167,7 @@ __device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS
 }
 
 template <int D, int MODE>
-__device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS char* smem,
+__device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS char* smem, const FwdLane<D>& ln,
                                          int tid) {
   using C = FwdCfg<D>;
   const int lane = tid & 63, wave = tid >> 6;
@@ -200,29 +208,30 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const int n_full = L / C::BN, tail = L % C::BN;
   const int n_kv = n_full + (tail != 0);
   if (n_kv > 0) {
+    const uint32_t rsb = (uint32_t)(row_stride * 2);
     const uint16_t* kp = p.k + s0 * row_stride + (int64_t)h * D;
     const uint16_t* vp = p.v + s0 * row_stride + (int64_t)h * D;
-    dma_tile<C::RB, C::BN, C::NW>(kp, row_stride, min(C::BN, L), smem, wave, lane);
-    dma_tile<C::RB, C::BN, C::NW>(vp, row_stride, min(C::BN, L), smem + C::BUF, wave, lane);
+    ln.copy.issue_rows(kp, rsb, min(C::BN, L), smem, wave, lane);
+    ln.copy.issue_rows(vp, rsb, min(C::BN, L), smem + C::BUF, wave, lane);
     wait_vmem();
     __syncthreads();
     for (int it = 0; it < n_full; ++it) {
       const int cur = it & 1;
       if (it + 1 < n_kv) {
-        const int64_t nxt = (int64_t)(it + 1) * C::BN;
-        JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
+        const int64_t nxt = (int64_t)(it + 1) * C::BN * row_stride;
         const int rv = min(C::BN, L - (it + 1) * C::BN);
-        dma_tile<C::RB, C::BN, C::NW>(kp + nxt * row_stride, row_stride, rv, nbuf, wave, lane);
-        dma_tile<C::RB, C::BN, C::NW>(vp + nxt * row_stride, row_stride, rv, nbuf + C::BUF, wave, lane);
+        JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
+        ln.copy.issue_rows(kp + nxt, rsb, rv, nbuf, wave, lane);
+        ln.copy.issue_rows(vp + nxt, rsb, rv, nbuf + C::BUF, wave, lane);
       }
       JFA_LDS char* kbuf = smem + cur * 2 * C::BUF;
-      fwd_step<D, false>(kbuf, kbuf + C::BUF, qf, o, m, l, lane, C::BN, c);
+      fwd_step<D, false>(kbuf, kbuf + C::BUF, ln, qf, o, m, l, lane, C::BN, c);
       wait_vmem();
       __syncthreads();
     }
     if (tail) {
       JFA_LDS char* kbuf = smem + (n_full & 1) * 2 * C::BUF;
-      fwd_step<D, true>(kbuf, kbuf + C::BUF, qf, o, m, l, lane, tail, c);
+      fwd_step<D, true>(kbuf, kbuf + C::BUF, ln, qf, o, m, l, lane, tail, c);
       __syncthreads();
     }
   }
@@ -263,6 +272,10 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int tid = threadIdx.x;
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  FwdLane<D> ln;
+  ln.krow.init(tid & 63);
+  ln.vtr.init(tid & 63);
+  ln.copy.init((uint32_t)(p.num_heads * D * 2), tid >> 6, tid & 63);
   int idx, end;
   if (!p.dynamic) {
     idx = p.seg_ptr[prog];
@@ -272,7 +285,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     end = p.seg_ptr[1];
   }
   while (idx < end) {
-    fwd_tile<D, MODE>(p, p.tiles[idx], smem, tid);
+    fwd_tile<D, MODE>(p, p.tiles[idx], smem, ln, tid);
     if (!p.dynamic) {
       ++idx;
     } else {
