@@ -140,7 +140,7 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.seg2_cap = L.programs2_cap + 1;
     L.seg2 = at;
     at += align_up(L.seg2_cap * sizeof(int32_t));
-    L.tile2_cap = H * (T / kFwdRows + B + 1);
+    L.tile2_cap = H * (T / kDqRows + B + 1);
     L.tiles2 = at;
     at += align_up(L.tile2_cap * sizeof(Tile));
     L.stats = at;  // per query row (lse * log2 e, Di), float2 [H, T]
@@ -570,7 +570,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   if (mode == JFA_MODE_SELF) {
     if (sc.tiles.empty()) return JFA_OK;
     Schedule sq;
-    schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kFwdRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
+    schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDqRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
     if ((int64_t)sq.tiles.size() > L.tile2_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
     std::vector<char> buf;
     serialise(sc, L, buf, &sq);

@@ -12,8 +12,8 @@
 // retire at roughly 3.4e11 per second device-wide, so for long jagged batches the
 // dQ hand-off alone would outweigh the matrix work.  The self-attention backward is
 // therefore split by ownership:
-//  * dq_kernel (runs first): one workgroup = one tile of kFwdRows query rows (32 per
-//    wave), the forward's tiling and zigzag schedule; the loop streams 64-key K and V
+//  * dq_kernel (runs first): one workgroup = one tile of kDqRows query rows (32 per
+//    wave) under the forward's sort + zigzag rule; the loop streams 64-key K and V
 //    tiles through the same LDS ring as the forward.  Each lane owns one query row,
 //    so Di = rowsum(dO * O) and lse are one scalar per lane; the kernel also stores
 //    (lse * log2 e, Di) for its rows (8 bytes per row) for the second kernel.  Three
@@ -40,9 +40,9 @@ namespace {
 
 template <int D>
 struct DqCfg {
-  static constexpr int NW = kFwdWaves;
+  static constexpr int NW = kDqWaves;
   static constexpr int NT = NW * 64;
-  static constexpr int BM = kFwdRows;
+  static constexpr int BM = kDqRows;
   static constexpr int BN = kFwdKeys;
   static constexpr int NKB = BN / 32;
   static constexpr int NKS = D / 16;
@@ -378,8 +378,8 @@ __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles,
 }
 
 template <int D>
-__global__ void __launch_bounds__(kFwdWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(kDqWgPerCu * kFwdWaves / 4, kDqWgPerCu * kFwdWaves / 4)))
+__global__ void __launch_bounds__(kDqWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(kDqWgPerCu * kDqWaves / 4, kDqWgPerCu * kDqWaves / 4)))
     dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[4 * DqCfg<D>::BUF];
   __shared__ int next_tile;
@@ -410,9 +410,9 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
 hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s) {
   if (p.dq_programs <= 0) return hipSuccess;
   if (head_dim == 64)
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kDqWaves * 64), 0, s, p);
   else
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kFwdWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kDqWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 

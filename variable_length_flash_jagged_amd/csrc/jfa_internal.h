@@ -17,6 +17,8 @@ constexpr int kFwdWaves = 4;      // waves per forward workgroup
 constexpr int kFwdQPerWave = 32;  // query rows per wave (one 32-row MFMA block)
 constexpr int kFwdRows = kFwdWaves * kFwdQPerWave;
 constexpr int kFwdKeys = 64;
+constexpr int kDqWaves = 4;       // self-attention dQ kernel: 32 query rows per wave
+constexpr int kDqRows = kDqWaves * 32;
 constexpr int kBwdWaves = 4;      // waves per backward workgroup, 32 keys each
 constexpr int kBwdKeys = kBwdWaves * 32;
 constexpr int kBwdRows = 64;
@@ -30,7 +32,7 @@ constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound ov
 // registers; D=128 needs the full 512 (1 wave per SIMD) to avoid spilling.
 constexpr int dkdv_wg_per_cu(int head_dim) { return head_dim == 64 ? 2 : 1; }
 constexpr int kBqWgPerCu = 1;     // broadcast-Q fused backward
-constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel (forward tiling)
+constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel
 constexpr int kBdWgPerCu = 2;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
