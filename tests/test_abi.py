@@ -131,6 +131,6 @@ def test_schedule_matches_spec_bit_exactly(seed, mode, pass_, sched):
 def test_schedule_tile_rows():
     off = np.array([0, 300], dtype=np.int32)
     shape = B.make_shape(1, 1, 128, 300)
-    assert B.schedule(shape, 0, 0, off)[3] == 128
+    assert B.schedule(shape, 0, 0, off)[3] == 256
     assert B.schedule(shape, 0, 1, off)[3] == 128
     assert B.schedule(shape, 2, 0, off)[3] == 64

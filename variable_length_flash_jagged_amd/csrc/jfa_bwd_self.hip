@@ -43,7 +43,7 @@ struct DqCfg {
   static constexpr int NW = kDqWaves;
   static constexpr int NT = NW * 64;
   static constexpr int BM = kDqRows;
-  static constexpr int BN = kFwdKeys;
+  static constexpr int BN = kDqKeys;
   static constexpr int NKB = BN / 32;
   static constexpr int NKS = D / 16;
   static constexpr int NDB = D / 32;

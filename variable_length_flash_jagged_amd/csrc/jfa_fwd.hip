@@ -8,21 +8,28 @@
 // 3.2, Fig. 1): scores are scaled by scale*log2(e) and v_exp_f32 (2^x) is used.
 //
 // How it maps to CDNA4:
-//  * One workgroup = kFwdWaves waves = one tile of kFwdRows query rows of one
-//    (sequence, head); each wave owns 64 query rows as two 32-column MFMA blocks.
+//  * One workgroup = 8 waves = one tile of kFwdRows (256) query rows of one
+//    (sequence, head), 32 rows per wave, one workgroup per CU (2 waves per SIMD).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows held in
-//    registers for the whole tile).  In the C layout every lane then owns one query
-//    column, so the row max / row sum are in-lane plus one permlane32 swap.
-//  * O^T += V^T P^T: the probabilities leave the first product already in the B
-//    operand layout (after a bf16 pack); V^T is fetched from the row-major V tile in
-//    LDS with ds_read_b64_tr_b16.  The key order inside each 16-key step is the one
-//    the C layout hands over, and the transposed fetch reads V rows in that order.
-//  * K/V tiles of kFwdKeys keys are loaded with coalesced 16-byte global loads into a
-//    2-slot LDS ring: the next tile's loads are in flight while the current tile
-//    computes ("K/V multi-buffering", aixai.ru page, "Skeleton").
-//  * Only the last key tile of a sequence is range-limited: full tiles run a
-//    branch-free body, the tail runs a separately instantiated masked body (loop
-//    peeling, aixai.ru page, "Loop splitting against register spills").
+//    registers for the whole tile).  In the C layout every lane owns one query column,
+//    so the row max / row sum are in-lane plus one permlane32 swap.
+//  * O^T += V^T P^T: the probabilities leave the first product already in the B operand
+//    layout (after a bf16 pack); V^T is fetched from the row-major V tile in LDS with
+//    ds_read_b64_tr_b16, in the key order the C layout hands over.
+//  * Ping-pong between the two waves of each SIMD.  Waves w and w+4 of a workgroup are
+//    placed on the same SIMD; waves 0-3 (group A, rows 0-127) and 4-7 (group B, rows
+//    128-255) run the same sequence of phases one phase apart: a matrix phase
+//    (O += V(i-1) P(i-1), then S(i) = K(i) Q^T) and a vector phase (row max, lazy
+//    rescale, P(i) = 2^(S(i) c - m c), row sums).  Workgroup barriers between phases
+//    keep the offset, so on every SIMD one wave feeds the matrix core while the other
+//    keeps the vector unit busy (the producer / consumer overlap of matrix and softmax
+//    work the TLX page describes for its forward pipeline, section 3.2, Fig. 1, mapped
+//    onto SIMD pairs).
+//  * Stage i = {K(i), V(i-1)} is needed by group A in phase 2i and by group B in phase
+//    2i+1.  Stages reach LDS by direct global->LDS copies into a 3-slot ring, issued
+//    four phases ahead ("K/V multi-buffering", aixai.ru page, "Skeleton").  Only the
+//    last key tile of a sequence is range-limited; its scores past the end are masked
+//    in a branch taken on that tile alone.
 //  * The output is rescaled lazily: only when some row maximum grows by more than a
 //    factor 2^8 (still exact: the final division uses the same stale maximum).
 //  * Persistent grid: each workgroup walks its host-scheduled tile list, or takes
@@ -34,135 +41,185 @@
 namespace jfa {
 namespace {
 
+// Marks a rarely taken branch body as having side effects so that the compiler keeps
+// the branch instead of executing the body unconditionally under a select.
+#define JFA_KEEP_BRANCH() asm volatile("" ::: "memory")
+
 template <int D>
 struct FwdCfg {
   static constexpr int NW = kFwdWaves;
-  static constexpr int NT = NW * 64;
-  static constexpr int QPW = kFwdQPerWave;
-  static constexpr int NQB = QPW / 32;
   static constexpr int BM = kFwdRows;
   static constexpr int BN = kFwdKeys;
-  static constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  static constexpr int NKS = D / 16;         // MFMA k-steps over the head dim
-  static constexpr int NDB = D / 32;         // 32-wide head-dim blocks of O
-  static constexpr int NT16 = BN / 16;       // 16-key k-steps of the PV product
-  static constexpr int RB = D * 2;           // bytes per tile row
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int BUF = BN * RB;        // one K or V slot
+  static constexpr int NS = kFwdStages;   // ring slots
+  static constexpr int NKB = BN / 32;     // 32-key blocks per tile
+  static constexpr int NKS = D / 16;      // MFMA k-steps over the head dim
+  static constexpr int NDB = D / 32;      // 32-wide head-dim blocks of O
+  static constexpr int NT16 = BN / 16;    // 16-key k-steps of the PV product
+  static constexpr int RB = D * 2;        // bytes per tile row
+  static constexpr int TILE = BN * RB;    // one K or V tile
+  static constexpr int STAGE = 2 * TILE;  // ring slot: [K(i) | V(i-1)]
+  using Copy = TileCopy<RB, BN, NW>;
+  static constexpr int DMA_PER_STAGE = 2 * Copy::J;  // copies one wave issues per stage
+  static_assert(NW == 8 && kFwdQPerWave == 32 && BM == 256, "two groups of four 32-row waves");
   static_assert(NT16 == 2 * NKB, "key steps");
+  static_assert(DMA_PER_STAGE < 16, "vmcnt immediate");
 };
 
-// Per-lane constants of the loop: LDS operand offsets and ring-copy offsets.
+// Per-lane constants: LDS operand offsets and ring-copy offsets.
 template <int D>
 struct FwdLane {
   RowOperands<FwdCfg<D>::RB, FwdCfg<D>::NKS> krow;  // K rows as the A operand of S^T
   TrOperands<FwdCfg<D>::RB, FwdCfg<D>::NDB> vtr;     // V^T as the A operand of O^T
-  TileCopy<FwdCfg<D>::RB, FwdCfg<D>::BN, FwdCfg<D>::NW> copy;
+  typename FwdCfg<D>::Copy copy;
 };
 
-// One key/value tile for this wave's query rows.  MASK: keys >= keys_valid lie past
-// the end of the sequence (tail tile only).
-template <int D, bool MASK>
-__device__ __forceinline__ void fwd_step(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf, const FwdLane<D>& ln,
-                                         const bf16x8 (&qf)[FwdCfg<D>::NQB][FwdCfg<D>::NKS],
-                                         f32x16 (&o)[FwdCfg<D>::NDB][FwdCfg<D>::NQB],
-                                         float (&m)[FwdCfg<D>::NQB], float (&l)[FwdCfg<D>::NQB],
-                                         int lane, int keys_valid, float c) {
+// State of one wave's 32 query rows.
+template <int D>
+struct FwdWave {
   using C = FwdCfg<D>;
-  const int half = lane >> 5;
+  bf16x8 qf[C::NKS];     // Q rows (B operands)
+  f32x16 o[C::NDB];      // O^T accumulators
+  f32x16 s[C::NKB];      // scores of the current key tile, then its probabilities
+  bf16x8 pf[C::NT16];    // probabilities as B operands of the PV product
+  float m, l;            // running max (raw score units) and sum
+};
 
-  // S^T = K Q^T : [keys x queries]; C layout -> lane = query column,
-  // register i of key block kb <-> key 32*kb + 8*(i/4) + 4*half + i%4.
-  f32x16 s[C::NKB][C::NQB];
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier between phases.  The LDS reads of a phase are consumed inside it;
+// the lgkmcnt(0) makes sure none is still in flight when another wave's copy reuses
+// its ring slot.  Copies are ordered explicitly with wait_vmem* before the barrier
+// that publishes them.
+// The scheduling fences keep register-only work (MFMA, VALU) of one phase from being
+// moved into the next.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Issue order of the matrix phase: the operands of the first kAhead MFMAs, then every
+// MFMA followed by the LDS reads of the operand kAhead MFMAs later (2 transposed reads
+// per V^T operand, 1 row read per K operand), so that each read has several MFMAs'
+// time to land and only a few operands occupy registers.
+template <int D>
+__device__ __forceinline__ void order_matrix_phase() {
+  using C = FwdCfg<D>;
+  constexpr int kAhead = 4;
+  constexpr int NPV = C::NT16 * C::NDB, NSK = C::NKS * C::NKB;
+  static_assert(NPV >= kAhead, "prefetch window inside the PV product");
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+  for (int k = 0; k < NPV + NSK; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k + kAhead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else if (k + kAhead < NPV + NSK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// Pins a phase's results before its closing barrier: an empty asm that reads and
+// writes them, so that no pass sinks their computation into the next phase (which
+// would put one wave's vector and matrix work back into the same phase).
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+template <int D>
+__device__ __forceinline__ void pin_vector_phase(FwdWave<D>& w) {
+#pragma unroll
+  for (int t = 0; t < FwdCfg<D>::NT16; ++t) pin(w.pf[t]);
+#pragma unroll
+  for (int db = 0; db < FwdCfg<D>::NDB; ++db) pin(w.o[db]);
+  pin(w.m);
+  pin(w.l);
+}
+
+template <int D>
+__device__ __forceinline__ void pin_matrix_phase(FwdWave<D>& w) {
+#pragma unroll
+  for (int kb = 0; kb < FwdCfg<D>::NKB; ++kb) pin(w.s[kb]);
+#pragma unroll
+  for (int db = 0; db < FwdCfg<D>::NDB; ++db) pin(w.o[db]);
+}
+
+// O^T += V^T P^T over one key tile (V tile row-major in LDS, fetched transposed).
+template <int D>
+__device__ __forceinline__ void mma_pv(const JFA_LDS char* vbuf, const FwdLane<D>& ln, FwdWave<D>& w) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::NT16; ++t)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) w.o[db] = mfma32(ln.vtr.read(vbuf, 16 * t, db), w.pf[t], w.o[db]);
+}
+
+// S^T = K Q^T for one key tile ([keys x queries], C layout: lane = query column,
+// register i of key block kb <-> key 32*kb + 8*(i/4) + 4*half + i%4).
+template <int D>
+__device__ __forceinline__ void mma_s(const JFA_LDS char* kbuf, const FwdLane<D>& ln, FwdWave<D>& w) {
+  using C = FwdCfg<D>;
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
+    for (int i = 0; i < 16; ++i) w.s[kb][i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+  for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      const bf16x8 a = ln.krow.read(kbuf, kb * 32, ks);
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) s[kb][qb] = mfma32(a, qf[qb][ks], s[kb][qb]);
-    }
-  }
+    for (int kb = 0; kb < C::NKB; ++kb) w.s[kb] = mfma32(ln.krow.read(kbuf, kb * 32, ks), w.qf[ks], w.s[kb]);
+}
 
-  if (MASK) {
+// Vector phase for one key tile: mask (tail tile only), row max, lazy rescale,
+// probabilities, row sums, bf16 pack.
+template <int D>
+__device__ __forceinline__ void softmax_phase(FwdWave<D>& w, int keys_valid, int half, float c) {
+  using C = FwdCfg<D>;
+  if (keys_valid < C::BN) {
+    JFA_KEEP_BRANCH();
+    // key 32*kb + 8*(i/4) + 4*half + i%4 is past the end iff its lane-independent
+    // part reaches keys_valid - 4*half (compared against immediates)
+    const int kv = keys_valid - 4 * half;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (key >= keys_valid) {
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) s[kb][qb][i] = -INFINITY;
-        }
-      }
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= kv) w.s[kb][i] = -INFINITY;
   }
-
-  // Row maxima (raw scores; scale > 0 commutes with max) and the lazy rescale.
-  float mnew[C::NQB];
-  bool grow = false;
+  float mx = w.s[0][0];
 #pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    float mx = s[0][qb][0];
+  for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, w.s[kb][i]);
+  const float mnew = fmaxf(w.m, half_max(mx));  // raw scores: scale > 0 commutes with max
+  if (__ballot((mnew - w.m) * c > 8.0f)) {
+    JFA_KEEP_BRANCH();
+    const float alpha = fast_exp2((w.m - mnew) * c);
+    w.m = mnew;
+    w.l *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-    mx = half_max(mx);
-    mnew[qb] = fmaxf(m[qb], mx);
-    grow |= (mnew[qb] - m[qb]) * c > 8.0f;
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
   }
-  if (__ballot(grow)) {
+  const float mc = w.m * c;
+  float sum = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      const float alpha = fast_exp2((m[qb] - mnew[qb]) * c);
-      m[qb] = mnew[qb];
-      l[qb] *= alpha;
+  for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
+    for (int i = 0; i < 16; ++i) {
+      const float pv = fast_exp2(fmaf(w.s[kb][i], c, -mc));
+      w.s[kb][i] = pv;
+      sum += pv;
     }
-  }
-
-  // P = 2^(S*c - m*c); row sums; pack P into B operands of the PV product.
-  bf16x8 pf[C::NQB][C::NT16];
+  w.l += sum;
 #pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    const float mc = m[qb] * c;
-    float sum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[kb][qb][i], c, -mc));
-        s[kb][qb][i] = pv;
-        sum += pv;
-      }
-    l[qb] += sum;
-#pragma unroll
-    for (int t = 0; t < C::NT16; ++t) {
-      const f32x16& src = s[t >> 1][qb];
-      const int r = 8 * (t & 1);
-      pf[qb][t] = pack8(src[r], src[r + 1], src[r + 2], src[r + 3], src[r + 4], src[r + 5],
-                        src[r + 6], src[r + 7]);
-    }
-  }
-
-  // O^T += V^T P^T with V^T fetched transposed from the row-major V tile.
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-    for (int t = 0; t < C::NT16; ++t) {
-      const bf16x8 a = ln.vtr.read(vbuf, 16 * t, db);
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) o[db][qb] = mfma32(a, pf[qb][t], o[db][qb]);
-    }
+  for (int t = 0; t < C::NT16; ++t) {
+    const f32x16& x = w.s[t >> 1];
+    const int r = 8 * (t & 1);
+    w.pf[t] = pack8(x[r], x[r + 1], x[r + 2], x[r + 3], x[r + 4], x[r + 5], x[r + 6], x[r + 7]);
   }
 }
 
@@ -170,95 +227,117 @@ template <int D, int MODE>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS char* smem, const FwdLane<D>& ln,
                                          int tid) {
   using C = FwdCfg<D>;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
+  const int g = wave >> 2;  // 0: group A, 1: group B (same SIMD as wave - 4)
   const int l32 = lane & 31, half = lane >> 5;
   const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
   const int H = p.num_heads;
-  const int64_t row_stride = (int64_t)H * D;
+  const int64_t rs = (int64_t)H * D;
+  const uint32_t rsb = (uint32_t)(rs * 2);
   const int64_t s0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - s0);
   const int Lq = (MODE == kSelf) ? L : p.num_q;
-  const int row0 = blk * C::BM + wave * C::QPW;
+  const int row = blk * C::BM + wave * 32 + l32;
   const float c = p.scale_log2;
 
-  // Q rows of this wave as B operands, kept in registers for the whole tile.
-  bf16x8 qf[C::NQB][C::NKS];
-#pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    const int row = row0 + qb * 32 + l32;
+  FwdWave<D> w;
+  {
     const int64_t qrow = (MODE == kSelf) ? s0 + row : (int64_t)row;
-    const uint16_t* qp = p.q + qrow * row_stride + (int64_t)h * D + half * 8;
+    const uint16_t* qp = p.q + qrow * rs + (int64_t)h * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks)
-      qf[qb][ks] = as_bf16x8(row < Lq ? ld16(qp + ks * 16) : zero16());
+    for (int ks = 0; ks < C::NKS; ++ks) w.qf[ks] = as_bf16x8(row < Lq ? ld16(qp + ks * 16) : zero16());
   }
+  w.m = -INFINITY;
+  w.l = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w.o[db][i] = 0.f;
 
-  f32x16 o[C::NDB][C::NQB];
-  float m[C::NQB], l[C::NQB];
-#pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.f;
-  }
+  const int n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
+  if (n > 0) {
+    const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
+    const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
+    auto rows_of = [&](int j) { return min(C::BN, L - j * C::BN); };
+    // Stage i into slot i % NS.  Stage 0 has no V tile and stage n no K tile; those
+    // halves repeat a neighbouring tile instead, so every stage is the same number of
+    // copies and the counted waits below stay exact.
+    auto issue = [&](int i) {
+      JFA_LDS char* slot = smem + (i % C::NS) * C::STAGE;
+      const int kt = min(i, n - 1), vt = max(i - 1, 0);
+      ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rs, rsb, rows_of(kt), slot, wave, lane);
+      ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rs, rsb, rows_of(vt), slot + C::TILE, wave, lane);
+    };
+    issue(0);
+    wait_vmem();  // Q and stage 0
+    issue(1);
+    phase_barrier();
 
-  const int n_full = L / C::BN, tail = L % C::BN;
-  const int n_kv = n_full + (tail != 0);
-  if (n_kv > 0) {
-    const uint32_t rsb = (uint32_t)(row_stride * 2);
-    const uint16_t* kp = p.k + s0 * row_stride + (int64_t)h * D;
-    const uint16_t* vp = p.v + s0 * row_stride + (int64_t)h * D;
-    ln.copy.issue_rows(kp, rsb, min(C::BN, L), smem, wave, lane);
-    ln.copy.issue_rows(vp, rsb, min(C::BN, L), smem + C::BUF, wave, lane);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < n_full; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < n_kv) {
-        const int64_t nxt = (int64_t)(it + 1) * C::BN * row_stride;
-        const int rv = min(C::BN, L - (it + 1) * C::BN);
-        JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
-        ln.copy.issue_rows(kp + nxt, rsb, rv, nbuf, wave, lane);
-        ln.copy.issue_rows(vp + nxt, rsb, rv, nbuf + C::BUF, wave, lane);
+    // Phase ph (0 .. 2n+1): group A runs matrix phase i in phase 2i and vector phase i
+    // in phase 2i+1; group B runs the same one phase later.  Every wave passes 2n+2
+    // barriers: group B idles through phase 0, group A through phase 2n+1.
+    int ph = 0;
+    auto end_phase = [&]() {
+      if (ph & 1) {
+        // stage ph/2 + 1 is read from the next phase on; stage ph/2 + 2 may still be
+        // in flight
+        if ((ph >> 1) + 2 <= n) wait_vmem_n<C::DMA_PER_STAGE>();
+        else wait_vmem();
       }
-      JFA_LDS char* kbuf = smem + cur * 2 * C::BUF;
-      fwd_step<D, false>(kbuf, kbuf + C::BUF, ln, qf, o, m, l, lane, C::BN, c);
-      wait_vmem();
-      __syncthreads();
+      phase_barrier();
+      ++ph;
+      if (!(ph & 1) && (ph >> 1) + 2 <= n) issue((ph >> 1) + 2);
+    };
+    if (2 <= n) issue(2);
+    if (g) end_phase();
+    // matrix phase 0: S(0) only
+    mma_s<D>(smem, ln, w);
+    pin_matrix_phase<D>(w);
+    end_phase();
+    int slot_off = 0;  // ring offset of stage i - 1
+    for (int i = 1; i < n; ++i) {
+      softmax_phase<D>(w, C::BN, half, c);  // tiles before the last are full
+      pin_vector_phase<D>(w);
+      end_phase();
+      slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
+      const JFA_LDS char* slot = smem + slot_off;
+      mma_pv<D>(slot + C::TILE, ln, w);
+      mma_s<D>(slot, ln, w);
+      order_matrix_phase<D>();
+      pin_matrix_phase<D>(w);
+      end_phase();
     }
-    if (tail) {
-      JFA_LDS char* kbuf = smem + (n_full & 1) * 2 * C::BUF;
-      fwd_step<D, true>(kbuf, kbuf + C::BUF, ln, qf, o, m, l, lane, tail, c);
-      __syncthreads();
-    }
+    softmax_phase<D>(w, rows_of(n - 1), half, c);
+    pin_vector_phase<D>(w);
+    end_phase();
+    // matrix phase n: O += V(n-1) P(n-1) only
+    slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
+    mma_pv<D>(smem + slot_off + C::TILE, ln, w);
+    pin_matrix_phase<D>(w);
+    end_phase();
+    if (!g) end_phase();
   }
 
   // Epilogue: O / l in bf16, lse = ln 2 * (m*c + log2 l); empty rows give 0 and -inf.
+  const float lt = half_sum(w.l);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (row < Lq) {
+    const int64_t orow = (MODE == kSelf) ? s0 + row : (int64_t)b * p.num_q + row;
+    uint16_t* op = p.o + orow * rs + (int64_t)h * D + 4 * half;
 #pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    const float lt = half_sum(l[qb]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const float lse = lt > 0.f ? (m[qb] * c + fast_log2(lt)) * kLn2 : -INFINITY;
-    const int row = row0 + qb * 32 + l32;
-    if (row < Lq) {
-      const int64_t orow = (MODE == kSelf) ? s0 + row : (int64_t)b * p.num_q + row;
-      uint16_t* op = p.o + orow * row_stride + (int64_t)h * D + 4 * half;
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16& a = o[db][qb];
-          st8(op + 32 * db + 8 * g4,
-              pack4(a[4 * g4] * inv, a[4 * g4 + 1] * inv, a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv));
-        }
-      if (half == 0) {
-        const int64_t li = (MODE == kSelf) ? (int64_t)h * p.total_tokens + s0 + row
-                                           : ((int64_t)b * H + h) * p.num_q + row;
-        p.lse[li] = lse;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& x = w.o[db];
+        st8(op + 32 * db + 8 * g4,
+            pack4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv));
       }
+    if (half == 0) {
+      const int64_t li = (MODE == kSelf) ? (int64_t)h * p.total_tokens + s0 + row
+                                         : ((int64_t)b * H + h) * p.num_q + row;
+      p.lse[li] = lse;
     }
   }
 }
@@ -267,7 +346,7 @@ template <int D, int MODE>
 __global__ void __launch_bounds__(kFwdWaves * 64)
     __attribute__((amdgpu_waves_per_eu(kFwdWgPerCu * kFwdWaves / 4, kFwdWgPerCu * kFwdWaves / 4))) fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * C::BUF];
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::NS * C::STAGE];
   __shared__ int next_tile;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int tid = threadIdx.x;

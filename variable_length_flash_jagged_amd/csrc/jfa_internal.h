@@ -13,12 +13,14 @@ enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2 };
 // key/value loop streams kFwdKeys keys at a time.  A backward tile is kBwdKeys key
 // rows of one (sequence, head); its loop streams kBwdRows query rows at a time.
 // Block-diagonal tiles are one kBlock-token block of one head, one tile per wave.
-constexpr int kFwdWaves = 4;      // waves per forward workgroup
+constexpr int kFwdWaves = 8;      // waves per forward workgroup: two groups of four
 constexpr int kFwdQPerWave = 32;  // query rows per wave (one 32-row MFMA block)
 constexpr int kFwdRows = kFwdWaves * kFwdQPerWave;
 constexpr int kFwdKeys = 64;
+constexpr int kFwdStages = 3;     // K/V ring slots of the forward
 constexpr int kDqWaves = 4;       // self-attention dQ kernel: 32 query rows per wave
 constexpr int kDqRows = kDqWaves * 32;
+constexpr int kDqKeys = 64;       // keys per step of the dQ kernel
 constexpr int kBwdWaves = 4;      // waves per backward workgroup, 32 keys each
 constexpr int kBwdKeys = kBwdWaves * 32;
 constexpr int kBwdRows = 64;
@@ -26,7 +28,7 @@ constexpr int kBlock = 64;
 constexpr int kBdWaves = 4;
 
 // Persistent workgroups resident per CU (used for the default program count).
-constexpr int kFwdWgPerCu = 2;    // two resident workgroups: 2 waves per SIMD
+constexpr int kFwdWgPerCu = 1;    // one 8-wave workgroup: 2 waves per SIMD
 constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound over head dims
 // Resident dK/dV workgroups per CU by head dim: D=64 fits 2 waves per SIMD in 256
 // registers; D=128 needs the full 512 (1 wave per SIMD) to avoid spilling.
