@@ -188,11 +188,19 @@ __device__ __forceinline__ void softmax_phase(FwdWave<D>& w, int keys_valid, int
       for (int i = 0; i < 16; ++i)
         if (kb * 32 + 8 * (i >> 2) + (i & 3) >= kv) w.s[kb][i] = -INFINITY;
   }
-  float mx = w.s[0][0];
+  // row max as a tree (short dependency chains: one wave issues this phase alone)
+  float mk[C::NKB];
 #pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb)
+  for (int kb = 0; kb < C::NKB; ++kb) {
+    const f32x16& x = w.s[kb];
+    float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+    float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+    float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+    mk[kb] = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
+  }
+  float mx = mk[0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, w.s[kb][i]);
+  for (int kb = 1; kb < C::NKB; ++kb) mx = fmaxf(mx, mk[kb]);
   const float mnew = fmaxf(w.m, half_max(mx));  // raw scores: scale > 0 commutes with max
   if (__ballot((mnew - w.m) * c > 8.0f)) {
     JFA_KEEP_BRANCH();
@@ -205,16 +213,16 @@ __device__ __forceinline__ void softmax_phase(FwdWave<D>& w, int keys_valid, int
       for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
   }
   const float mc = w.m * c;
-  float sum = 0.f;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float pv = fast_exp2(fmaf(w.s[kb][i], c, -mc));
       w.s[kb][i] = pv;
-      sum += pv;
+      sum[i & 3] += pv;
     }
-  w.l += sum;
+  w.l += (sum[0] + sum[1]) + (sum[2] + sum[3]);
 #pragma unroll
   for (int t = 0; t < C::NT16; ++t) {
     const f32x16& x = w.s[t >> 1];
