@@ -29,6 +29,14 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The dK/dV kernel runs at one wave per SIMD, where the
+# compiler would otherwise put every MFMA result in accumulation registers and copy
+# the scores out for the vector work (and the accumulators back and forth) on every
+# step; the VGPR form keeps scores in VGPRs and uses the accumulation registers only
+# for values that do not fit.
+EXTRA_FLAGS = {"jfa_bwd_self.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc():
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -38,7 +46,7 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     if r.returncode != 0:

@@ -297,6 +297,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
         s = mfma32(ln.row.read(qt, qq * 32, ks), kf[ks], s);
         dp = mfma32(ln.row.read(dot, qq * 32, ks), vf[ks], dp);
       }
+      // P and dS into fresh registers (the MFMA results are only read): writing them
+      // back in place would make the compiler copy them between register files.
+      // Keys past the end of the sequence need no mask here: their P and dS only feed
+      // their own dK, dV rows, which are never stored.
+      float pr[16], dsr[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int r4 = qq * 32 + 8 * g4 + 4 * half;
@@ -307,18 +312,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
-          float pv = fast_exp2(fmaf(s[i], c, -la[e]));
-          pv = key_ok ? pv : 0.f;
-          s[i] = pv;
-          dp[i] = pv * (dp[i] - da[e]);
+          pr[i] = fast_exp2(fmaf(s[i], c, -la[e]));
+          dsr[i] = pr[i] * (dp[i] - da[e]);
         }
       }
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = 8 * u;
-        pf[u] = pack8(s[r], s[r + 1], s[r + 2], s[r + 3], s[r + 4], s[r + 5], s[r + 6], s[r + 7]);
-        dsf[u] = pack8(dp[r], dp[r + 1], dp[r + 2], dp[r + 3], dp[r + 4], dp[r + 5], dp[r + 6], dp[r + 7]);
+        pf[u] = pack8(pr[r], pr[r + 1], pr[r + 2], pr[r + 3], pr[r + 4], pr[r + 5], pr[r + 6], pr[r + 7]);
+        dsf[u] = pack8(dsr[r], dsr[r + 1], dsr[r + 2], dsr[r + 3], dsr[r + 4], dsr[r + 5], dsr[r + 6], dsr[r + 7]);
       }
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
