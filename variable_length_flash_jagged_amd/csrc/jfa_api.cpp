@@ -143,8 +143,8 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.tile2_cap = H * (T / kDqRows + B + 1);
     L.tiles2 = at;
     at += align_up(L.tile2_cap * sizeof(Tile));
-    L.stats = at;  // per query row (lse * log2 e, Di), float2 [H, T]
-    at += align_up(H * T * 2 * sizeof(float));
+    L.stats = at;  // per query row 16-byte term (-lse/scale, -Di in bf16 high/low), [H, T, 8], + sentinel
+    at += align_up((H * T + 1) * 16);
   } else if (pass == JFA_PASS_BWD) {
     L.acc = at;
     const int64_t acc_elems = (o.dq_path == 0) ? Mq * H * D : (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
@@ -576,7 +576,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     serialise(sc, L, buf, &sq);
     if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
     p.dq = (uint16_t*)dq;
-    p.row_stats = (float2*)(ws + L.stats);
+    p.row_aug = (uint16_t*)(ws + L.stats);
     p.dq_tiles = (const Tile*)(ws + L.tiles2);
     p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
     p.dq_programs = sq.programs;

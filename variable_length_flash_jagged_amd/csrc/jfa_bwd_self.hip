@@ -134,8 +134,24 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     }
     di = half_sum(di);
   }
-  const float lse2 = row_ok ? p.lse[(int64_t)h * p.total_tokens + s0 + row] * kLog2e : INFINITY;
-  if (row_ok && half == 0) p.row_stats[(int64_t)h * p.total_tokens + s0 + row] = make_float2(lse2, di);
+  const float lse = row_ok ? p.lse[(int64_t)h * p.total_tokens + s0 + row] : INFINITY;
+  const float lse2 = lse * kLog2e;
+  if (blockIdx.x == 0 && tid == 0) {
+    // sentinel row term for query rows past the end of a sequence (P = dS = 0)
+    const bf16 z = (bf16)0.0f;
+    const bf16x8 t = {(bf16)(-1e30f), z, z, z, z, z, z, z};
+    st16(p.row_aug + (int64_t)p.num_heads * p.total_tokens * 8, __builtin_bit_cast(u32x4, t));
+  }
+  if (row_ok && half == 0) {
+    // Row term for the dK/dV kernel: -lse/scale and -Di as bf16 high + low parts
+    // (S - lse/scale scaled by c = scale log2 e is the exponent of P in base 2).
+    const float x = -lse / p.scale, y = -di;
+    const bf16 xh = (bf16)x, yh = (bf16)y;
+    const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
+    const bf16 z = (bf16)0.0f;
+    const bf16x8 t = {xh, xl, z, z, yh, yl, z, z};
+    st16(p.row_aug + ((int64_t)h * p.total_tokens + s0 + row) * 8, __builtin_bit_cast(u32x4, t));
+  }
 
   f32x16 dq[C::NDB];
 #pragma unroll
@@ -195,40 +211,138 @@ struct KvCfg {
   static constexpr int NDB = D / 32;
   static constexpr int RB = 2 * D;
   static constexpr int QBUF = QB * RB;
+  static constexpr int ABUF = QB * 16;                 // one 16-byte row term per query row
   static constexpr int OFF_Q = 0;                      // [2][QBUF]
   static constexpr int OFF_DO = OFF_Q + 2 * QBUF;      // [2][QBUF]
-  static constexpr int OFF_LSE = OFF_DO + 2 * QBUF;    // float [2][QB]
-  static constexpr int OFF_DI = OFF_LSE + 2 * QB * 4;  // float [2][QB]
-  static constexpr int SMEM = OFF_DI + 2 * QB * 4;
+  static constexpr int OFF_AUG = OFF_DO + 2 * QBUF;    // [2][ABUF]
+  static constexpr int SMEM = OFF_AUG + 2 * ABUF;
+  static_assert(QB == 64, "one 64-lane copy moves a step's row terms");
 };
 
-// Per-lane constants of the dK/dV loop: LDS operand offsets and ring-copy offsets.
+// Per-lane constants of the dK/dV loop: LDS operand offsets, ring-copy offsets and the
+// B operands of the row-term MFMAs.
 template <int D>
 struct KvLane {
   RowOperands<KvCfg<D>::RB, KvCfg<D>::NKS> row;  // Q, dO rows as A operands of S, dP
   TrOperands<KvCfg<D>::RB, KvCfg<D>::NDB> tr;    // Q^T, dO^T as A operands of dK^T, dV^T
   TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, KvCfg<D>::NW> copy;
+  bf16x8 pick_s, pick_dp;  // k-slots 0,1 (S) and 4,5 (dP) of the row term, lanes 0-31
+  __device__ __forceinline__ void init_pick(int lane) {
+    const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
+    const bool lo = lane < 32;
+    pick_s = bf16x8{lo ? one : zero, lo ? one : zero, zero, zero, zero, zero, zero, zero};
+    pick_dp = bf16x8{zero, zero, zero, zero, lo ? one : zero, lo ? one : zero, zero, zero};
+  }
 };
 
-// Issue the next step's copies (Q, dO -> LDS) and its (lse * log2 e, Di) pairs.
+// Issue the copies of a step: Q and dO rows (all waves; rows past rows_valid repeat the
+// last valid row) and the 16-byte row terms (wave 0, one row per lane; rows past
+// rows_valid take the sentinel term at index sentinel, whose -lse/scale part is
+// -1e30, so that their P and dS are exactly zero).
 template <int D>
-__device__ __forceinline__ float2 kv_prefetch(const KvLane<D>& ln, const uint16_t* qb, const uint16_t* dob,
-                                              const float2* stats, int64_t rs, int row0, int rows_valid,
-                                              JFA_LDS char* qbuf, JFA_LDS char* dobuf, int tid, int wave, int lane) {
-  using C = KvCfg<D>;
+__device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb, const uint16_t* dob,
+                                         const uint16_t* aug, int64_t rs, int64_t aug_row0, int64_t sentinel,
+                                         int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
+                                         JFA_LDS char* augbuf, int wave, int lane) {
   const uint32_t rsb = (uint32_t)(rs * 2);
   ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rows_valid, qbuf, wave, lane);
   ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rows_valid, dobuf, wave, lane);
-  return (tid < C::QB && tid < rows_valid) ? stats[row0 + tid] : make_float2(INFINITY, 0.f);
+  if (wave == 0) {
+    const int64_t r = lane < rows_valid ? aug_row0 + row0 + lane : sentinel;
+    dma16(uniform_ptr(aug), (uint32_t)(r * 16), augbuf);
+  }
 }
 
-// Rows past the end get lse2 = +inf, which zeroes their probabilities.
+// The row terms ride on one extra k-step of S and dP: each query row's 16-byte term
+// holds -lse/scale and -Di split into bf16 high and low parts, and the B operand picks
+// the pair that belongs to each product, so that S' = Q K^T - lse/scale and
+// dP' = dO V^T - Di come out of the MFMAs and P = 2^(c S'), dS = P dP' need no per-row
+// operands in the vector unit.  C layout of S', dP' ([queries x keys]): lane = key,
+// register i <-> query 32*qq + 8*(i/4) + 4*half + i%4.
+//
+// One 32-row query block runs as four regions whose vector work hides under the next
+// region's MFMAs (no extra registers: each region only needs the previous one):
+//   S' | dP' + (P = 2^(c S'), pack P) | dV^T += dO^T P + (dS = P dP', pack dS)
+//   | dK^T += Q^T dS
+// Keys past the end of the sequence need no mask: their P and dS only feed their own
+// dK, dV rows, which are never stored; query rows past the end carry the sentinel row
+// term and get P = dS = 0.
 template <int D>
-__device__ __forceinline__ void kv_finish(float2 st, float* lse2, float* di, int tid) {
-  if (tid < KvCfg<D>::QB) {
-    lse2[tid] = st.x;
-    di[tid] = st.y;
+__device__ __forceinline__ void kv_block(const JFA_LDS char* qt, const JFA_LDS char* dot, const JFA_LDS char* augt,
+                                         int qq, const KvLane<D>& ln, const bf16x8 (&kf)[KvCfg<D>::NKS],
+                                         const bf16x8 (&vf)[KvCfg<D>::NKS], f32x16 (&dk)[KvCfg<D>::NDB],
+                                         f32x16 (&dv)[KvCfg<D>::NDB], int l32, float c) {
+  using C = KvCfg<D>;
+  const bf16x8 term = as_bf16x8(lds_ld16(augt, (qq * 32 + l32) * 16));
+  // region 1: S'
+  f32x16 s, dp;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+  s = mfma32(term, ln.pick_s, s);
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) s = mfma32(ln.row.read(qt, qq * 32, ks), kf[ks], s);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int k = 0; k <= C::NKS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 2: dP' + P
+  dp = mfma32(term, ln.pick_dp, dp);
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) dp = mfma32(ln.row.read(dot, qq * 32, ks), vf[ks], dp);
+  float pr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(s[i] * c);
+  bf16x8 pf[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 8 * u;
+    pf[u] = pack8(pr[r], pr[r + 1], pr[r + 2], pr[r + 3], pr[r + 4], pr[r + 5], pr[r + 6], pr[r + 7]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int k = 0; k <= C::NKS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 3: dV^T + dS
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dv[db] = mfma32(ln.tr.read(dot, 16 * (2 * qq + u), db), pf[u], dv[db]);
+  float dsr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dsr[i] = pr[i] * dp[i];
+  bf16x8 dsf[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 8 * u;
+    dsf[u] = pack8(dsr[r], dsr[r + 1], dsr[r + 2], dsr[r + 3], dsr[r + 4], dsr[r + 5], dsr[r + 6], dsr[r + 7]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int k = 0; k < 2 * C::NDB; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 4: dK^T
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dk[db] = mfma32(ln.tr.read(qt, 16 * (2 * qq + u), db), dsf[u], dk[db]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int k = 0; k < 2 * C::NDB; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
@@ -248,9 +362,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   const float c = p.scale_log2;
   const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
   const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
-  const float2* stats = p.row_stats + (int64_t)h * p.total_tokens + s0;
-  float* lse2 = (float*)(smem_raw + C::OFF_LSE);
-  float* di = (float*)(smem_raw + C::OFF_DI);
+  const int64_t aug_row0 = (int64_t)h * p.total_tokens + s0;
+  const int64_t sentinel = (int64_t)p.num_heads * p.total_tokens;
   const int nq = (L + C::QB - 1) / C::QB;
 
   // This wave's keys as B operands, straight from global (rows past the end -> 0).
@@ -263,9 +376,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
       vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
     }
   }
-  float2 pre = kv_prefetch<D>(ln, qb, dob, stats, rs, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO, tid,
-                              wave, lane);
-  kv_finish<D>(pre, lse2, di, tid);
+  kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO,
+              smem + C::OFF_AUG, wave, lane);
   wait_vmem();
   __syncthreads();
 
@@ -278,62 +390,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   for (int it = 0; it < nq; ++it) {
     const int cur = it & 1;
     const int row0 = it * C::QB;
-    JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
-    JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
-    const bool has_next = it + 1 < nq;
-    const int next_rows = min(C::QB, L - row0 - C::QB);
-    if (has_next)
-      pre = kv_prefetch<D>(ln, qb, dob, stats, rs, row0 + C::QB, next_rows, smem + C::OFF_Q + (cur ^ 1) * C::QBUF,
-                           smem + C::OFF_DO + (cur ^ 1) * C::QBUF, tid, wave, lane);
-    const float* l2 = lse2 + cur * C::QB;
-    const float* dd = di + cur * C::QB;
+    if (it + 1 < nq)
+      kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0 + C::QB, min(C::QB, L - row0 - C::QB),
+                  smem + C::OFF_Q + (cur ^ 1) * C::QBUF, smem + C::OFF_DO + (cur ^ 1) * C::QBUF,
+                  smem + C::OFF_AUG + (cur ^ 1) * C::ABUF, wave, lane);
+    const JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
+    const JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
+    const JFA_LDS char* augt = smem + C::OFF_AUG + cur * C::ABUF;
 #pragma unroll
-    for (int qq = 0; qq < C::NQB; ++qq) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        s = mfma32(ln.row.read(qt, qq * 32, ks), kf[ks], s);
-        dp = mfma32(ln.row.read(dot, qq * 32, ks), vf[ks], dp);
-      }
-      // P and dS into fresh registers (the MFMA results are only read): writing them
-      // back in place would make the compiler copy them between register files.
-      // Keys past the end of the sequence need no mask here: their P and dS only feed
-      // their own dK, dV rows, which are never stored.
-      float pr[16], dsr[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r4 = qq * 32 + 8 * g4 + 4 * half;
-        const float4 lv = *reinterpret_cast<const float4*>(l2 + r4);
-        const float4 dv4 = *reinterpret_cast<const float4*>(dd + r4);
-        const float la[4] = {lv.x, lv.y, lv.z, lv.w};
-        const float da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          pr[i] = fast_exp2(fmaf(s[i], c, -la[e]));
-          dsr[i] = pr[i] * (dp[i] - da[e]);
-        }
-      }
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = 8 * u;
-        pf[u] = pack8(pr[r], pr[r + 1], pr[r + 2], pr[r + 3], pr[r + 4], pr[r + 5], pr[r + 6], pr[r + 7]);
-        dsf[u] = pack8(dsr[r], dsr[r + 1], dsr[r + 2], dsr[r + 3], dsr[r + 4], dsr[r + 5], dsr[r + 6], dsr[r + 7]);
-      }
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int t = 2 * qq + u;
-          dv[db] = mfma32(ln.tr.read(dot, 16 * t, db), pf[u], dv[db]);
-          dk[db] = mfma32(ln.tr.read(qt, 16 * t, db), dsf[u], dk[db]);
-        }
-      }
-    }
-    if (has_next) kv_finish<D>(pre, lse2 + (cur ^ 1) * C::QB, di + (cur ^ 1) * C::QB, tid);
+    for (int qq = 0; qq < C::NQB; ++qq) kv_block<D>(qt, dot, augt, qq, ln, kf, vf, dk, dv, l32, c);
     wait_vmem();
     __syncthreads();
   }
@@ -403,6 +468,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
   KvLane<D> ln;
   ln.row.init(threadIdx.x & 63);
   ln.tr.init(threadIdx.x & 63);
+  ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
             [&](Tile t) { dkdv_tile<D>(p, t, smem, ln, threadIdx.x); });

@@ -78,7 +78,7 @@ struct BwdParams {
   uint16_t* dv;
   float* dq_acc;  // broadcast-Q atomics: [Mq,H,D] fp32; partials: [P,Mq,D] fp32
   uint16_t* dq;   // self: bf16 [T,H,D], written by the dQ kernel
-  float2* row_stats;         // self: [H,T] (lse * log2 e, Di) per query row, written by the dQ kernel
+  uint16_t* row_aug;         // self: [H,T,8] bf16 row terms (-lse/scale, -Di as high/low pairs), written by the dQ kernel
   const Tile* dq_tiles;      // self: query-row tiles of the dQ kernel
   const int32_t* dq_seg_ptr;
   int32_t dq_programs;
