@@ -220,8 +220,11 @@ def main():
     if mode == W.MODE_SELF:
         pairs = M.valid_pairs(lengths, mode)
         t = int(p["total_tokens"])
-        work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 12 * t * h)
-        work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 8 * t * h)
+        # dQ kernel: Q, K, V, O, dO in, dQ out (2 bytes each), lse in (4) and the
+        # 16-byte row term out per (row, head); dK/dV kernel: Q, K, V, dO in, dK, dV
+        # out, the row term in.
+        work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 20 * t * h)
+        work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
     else:
         work["bwd"] = (fb, bytes_b)
     kernels = {}
