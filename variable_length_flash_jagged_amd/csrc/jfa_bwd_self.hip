@@ -30,6 +30,8 @@
 //    once, by their owner.
 // The split recomputes S and dP once more (seven products per query-key block
 // instead of five) in exchange for no atomics and no fp32 dQ accumulator in HBM.
+#include <utility>
+
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -260,90 +262,163 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
 // operands in the vector unit.  C layout of S', dP' ([queries x keys]): lane = key,
 // register i <-> query 32*qq + 8*(i/4) + 4*half + i%4.
 //
-// One 32-row query block runs as four regions whose vector work hides under the next
-// region's MFMAs (no extra registers: each region only needs the previous one):
-//   S' | dP' + (P = 2^(c S'), pack P) | dV^T += dO^T P + (dS = P dP', pack dS)
-//   | dK^T += Q^T dS
 // Keys past the end of the sequence need no mask: their P and dS only feed their own
 // dK, dV rows, which are never stored; query rows past the end carry the sentinel row
 // term and get P = dS = 0.
+//
+// One 64-row step as a single stream of MFMAs.  Per 32-row query block (qq) the
+// stream is
+//   S' row term, S' k-steps | dP' row term, dP' k-steps | dV^T (u, db) | dK^T (u, db)
+// and the two blocks follow each other.  Every operand that comes from LDS is read
+// AHEAD stream positions before its MFMA, across region and block boundaries, into a
+// small register ring, so that no region starts by waiting for LDS.  The vector work
+// is cut into slices placed between MFMAs: P = 2^(c S') (one slice per dP' k-step,
+// from the first one after the dP' row term, when S' has left the pipeline) and
+// dS = P dP' (during the dV products, from their third slot on).  The pack of P (dS) into B operands
+// completes before the first dV (dK) MFMA that needs it.
 template <int D>
-__device__ __forceinline__ void kv_block(const JFA_LDS char* qt, const JFA_LDS char* dot, const JFA_LDS char* augt,
-                                         int qq, const KvLane<D>& ln, const bf16x8 (&kf)[KvCfg<D>::NKS],
-                                         const bf16x8 (&vf)[KvCfg<D>::NKS], f32x16 (&dk)[KvCfg<D>::NDB],
-                                         f32x16 (&dv)[KvCfg<D>::NDB], int l32, float c) {
+struct KvStream {
   using C = KvCfg<D>;
-  const bf16x8 term = as_bf16x8(lds_ld16(augt, (qq * 32 + l32) * 16));
-  // region 1: S'
+  static constexpr int NKS = C::NKS, NDB = C::NDB;
+  static constexpr int S0 = 0;                    // S' row term
+  static constexpr int DP0 = NKS + 1;             // dP' row term
+  static constexpr int DV0 = 2 * NKS + 2;         // first dV^T product
+  static constexpr int DK0 = DV0 + 2 * NDB;       // first dK^T product
+  static constexpr int PER = DK0 + 2 * NDB;       // MFMAs per query block
+  static constexpr int N = C::NQB * PER;          // MFMAs per step
+  static constexpr int AHEAD = 4, NBUF = AHEAD + 1;
+  static constexpr int P_PER = 16 / NKS;          // P values per slice (one slice per dP' k-step)
+  static constexpr int DS_SL = 2 * NDB - 2;       // dS slices (dV slots 2 .. 2*NDB-1)
+  static constexpr int DS_PER = (16 + DS_SL - 1) / DS_SL;
+
+  const JFA_LDS char *qt, *dot, *augt;
+  const KvLane<D>& ln;
+  const bf16x8 (&kf)[NKS];
+  const bf16x8 (&vf)[NKS];
+  f32x16 (&dk)[NDB];
+  f32x16 (&dv)[NDB];
+  const int l32;
+  const float c;
+  bf16x8 buf[NBUF];
+  bf16x8 term;
   f32x16 s, dp;
+  float pr[16], dsr[16];
+  bf16x8 pf[2], dsf[2];
+
+  __device__ __forceinline__ KvStream(const JFA_LDS char* qt_, const JFA_LDS char* dot_, const JFA_LDS char* augt_,
+                                      const KvLane<D>& ln_, const bf16x8 (&kf_)[NKS], const bf16x8 (&vf_)[NKS],
+                                      f32x16 (&dk_)[NDB], f32x16 (&dv_)[NDB], int l32_, float c_)
+      : qt(qt_), dot(dot_), augt(augt_), ln(ln_), kf(kf_), vf(vf_), dk(dk_), dv(dv_), l32(l32_), c(c_) {}
+
+  // LDS read(s) of stream position K (none for the dP' row term, which reuses the S'
+  // one); reads<K>() counts them.
+  template <int K>
+  __device__ __forceinline__ void read() {
+    constexpr int qq = K / PER, k = K % PER;
+    if constexpr (k == S0) {
+      buf[K % NBUF] = as_bf16x8(lds_ld16(augt, (qq * 32 + l32) * 16));
+    } else if constexpr (k < DP0) {
+      buf[K % NBUF] = ln.row.read(qt, qq * 32, k - 1);
+    } else if constexpr (k == DP0) {
+    } else if constexpr (k < DV0) {
+      buf[K % NBUF] = ln.row.read(dot, qq * 32, k - DP0 - 1);
+    } else if constexpr (k < DK0) {
+      constexpr int u = (k - DV0) / NDB, db = (k - DV0) % NDB;
+      buf[K % NBUF] = ln.tr.read(dot, 16 * (2 * qq + u), db);
+    } else {
+      constexpr int u = (k - DK0) / NDB, db = (k - DK0) % NDB;
+      buf[K % NBUF] = ln.tr.read(qt, 16 * (2 * qq + u), db);
+    }
+  }
+  template <int K>
+  static constexpr int reads() {
+    constexpr int k = K % PER;
+    return k == DP0 ? 0 : (k < DV0 ? 1 : 2);
+  }
+
+  template <int K>
+  __device__ __forceinline__ void mfma() {
+    constexpr int k = K % PER;
+    if constexpr (k == S0) {
+      term = buf[K % NBUF];
+      s = mfma32(term, ln.pick_s, f32x16{});
+    } else if constexpr (k < DP0) {
+      s = mfma32(buf[K % NBUF], kf[k - 1], s);
+    } else if constexpr (k == DP0) {
+      dp = mfma32(term, ln.pick_dp, f32x16{});
+    } else if constexpr (k < DV0) {
+      dp = mfma32(buf[K % NBUF], vf[k - DP0 - 1], dp);
+    } else if constexpr (k < DK0) {
+      constexpr int u = (k - DV0) / NDB, db = (k - DV0) % NDB;
+      dv[db] = mfma32(buf[K % NBUF], pf[u], dv[db]);
+    } else {
+      constexpr int u = (k - DK0) / NDB, db = (k - DK0) % NDB;
+      dk[db] = mfma32(buf[K % NBUF], dsf[u], dk[db]);
+    }
+  }
+
+  // Vector slice placed after MFMA K; valus<K>() is its VALU instruction count (for the
+  // issue-order hints).
+  template <int K>
+  __device__ __forceinline__ void valu() {
+    constexpr int k = K % PER;
+    if constexpr (k >= DP0 + 1 && k < DV0) {
+      constexpr int j = k - DP0 - 1;  // 0 .. NKS-1
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-  s = mfma32(term, ln.pick_s, s);
+      for (int e = 0; e < P_PER; ++e) pr[j * P_PER + e] = fast_exp2(s[j * P_PER + e] * c);
+      if constexpr ((j + 1) * P_PER == 8) pf[0] = pack8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+      if constexpr ((j + 1) * P_PER == 16)
+        pf[1] = pack8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+    } else if constexpr (k >= DV0 + 2 && k < DK0) {
+      constexpr int j = k - DV0 - 2;  // 0 .. DS_SL-1
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) s = mfma32(ln.row.read(qt, qq * 32, ks), kf[ks], s);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int k = 0; k <= C::NKS; ++k) {
+      for (int e = 0; e < DS_PER; ++e) {
+        const int i = j * DS_PER + e;
+        if (i < 16) dsr[i] = pr[i] * dp[i];
+      }
+      if constexpr ((j + 1) * DS_PER >= 8 && j * DS_PER < 8)
+        dsf[0] = pack8(dsr[0], dsr[1], dsr[2], dsr[3], dsr[4], dsr[5], dsr[6], dsr[7]);
+      if constexpr (j == DS_SL - 1)
+        dsf[1] = pack8(dsr[8], dsr[9], dsr[10], dsr[11], dsr[12], dsr[13], dsr[14], dsr[15]);
+    }
+  }
+  template <int K>
+  static constexpr int valus() {
+    constexpr int k = K % PER;
+    if (k >= DP0 + 1 && k < DV0) return 2 * P_PER + ((k - DP0) * P_PER % 8 == 0 ? 4 : 0);
+    if (k >= DV0 + 2 && k < DK0) return DS_PER + 2;
+    return 0;
+  }
+
+  template <int K>
+  __device__ __forceinline__ void order() {
+    if constexpr (K == 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (valus<K>() > 0) __builtin_amdgcn_sched_group_barrier(0x002, valus<K>(), 0);
+    if constexpr (K + AHEAD < N && reads<K + AHEAD>() > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, reads<K + AHEAD>(), 0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // region 2: dP' + P
-  dp = mfma32(term, ln.pick_dp, dp);
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) dp = mfma32(ln.row.read(dot, qq * 32, ks), vf[ks], dp);
-  float pr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(s[i] * c);
-  bf16x8 pf[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 8 * u;
-    pf[u] = pack8(pr[r], pr[r + 1], pr[r + 2], pr[r + 3], pr[r + 4], pr[r + 5], pr[r + 6], pr[r + 7]);
+
+  template <int K>
+  __device__ __forceinline__ void step() {
+    mfma<K>();
+    valu<K>();
+    if constexpr (K + AHEAD < N) read<K + AHEAD>();
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int k = 0; k <= C::NKS; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+
+  __device__ __forceinline__ void go() {
+    prologue(std::make_integer_sequence<int, AHEAD>{});
+    body(std::make_integer_sequence<int, N>{});
+    orders(std::make_integer_sequence<int, N>{});
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // region 3: dV^T + dS
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) dv[db] = mfma32(ln.tr.read(dot, 16 * (2 * qq + u), db), pf[u], dv[db]);
-  float dsr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dsr[i] = pr[i] * dp[i];
-  bf16x8 dsf[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 8 * u;
-    dsf[u] = pack8(dsr[r], dsr[r + 1], dsr[r + 2], dsr[r + 3], dsr[r + 4], dsr[r + 5], dsr[r + 6], dsr[r + 7]);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-  for (int k = 0; k < 2 * C::NDB; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // region 4: dK^T
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) dk[db] = mfma32(ln.tr.read(qt, 16 * (2 * qq + u), db), dsf[u], dk[db]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-  for (int k = 0; k < 2 * C::NDB; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
+  template <int... K>
+  __device__ __forceinline__ void prologue(std::integer_sequence<int, K...>) { (read<K>(), ...); }
+  template <int... K>
+  __device__ __forceinline__ void body(std::integer_sequence<int, K...>) { (step<K>(), ...); }
+  template <int... K>
+  __device__ __forceinline__ void orders(std::integer_sequence<int, K...>) { (order<K>(), ...); }
+};
 
 template <int D>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D>& ln,
@@ -397,8 +472,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     const JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
     const JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
     const JFA_LDS char* augt = smem + C::OFF_AUG + cur * C::ABUF;
-#pragma unroll
-    for (int qq = 0; qq < C::NQB; ++qq) kv_block<D>(qt, dot, augt, qq, ln, kf, vf, dk, dv, l32, c);
+    KvStream<D>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c).go();
     wait_vmem();
     __syncthreads();
   }
