@@ -85,6 +85,31 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, JFA_LDS 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier between the phases of a two-group (ping-pong) kernel.  The LDS
+// reads of a phase are consumed inside it; the lgkmcnt(0) makes sure none is still in
+// flight when another wave's copy reuses its ring slot.  Copies are ordered explicitly
+// with wait_vmem* before the barrier that publishes them.  The scheduling fences keep
+// register-only work (MFMA, VALU) of one phase from being moved into the next.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pins a phase's results before its closing barrier: an empty asm that reads and
+// writes them, so that no pass sinks their computation into the next phase (which
+// would put one wave's vector and matrix work back into the same phase).
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // Transposed 4 x 16 fetch (see the header comment); `byte_off` is this lane's source
 // address.
 __device__ __forceinline__ v4i16 lds_tr4(const JFA_LDS char* base, int byte_off) {

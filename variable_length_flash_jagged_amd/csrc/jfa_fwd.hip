@@ -84,25 +84,6 @@ struct FwdWave {
   float m, l;            // running max (raw score units) and sum
 };
 
-// s_waitcnt vmcnt(N) with expcnt and lgkmcnt unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// Workgroup barrier between phases.  The LDS reads of a phase are consumed inside it;
-// the lgkmcnt(0) makes sure none is still in flight when another wave's copy reuses
-// its ring slot.  Copies are ordered explicitly with wait_vmem* before the barrier
-// that publishes them.
-// The scheduling fences keep register-only work (MFMA, VALU) of one phase from being
-// moved into the next.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Issue order of the matrix phase: the operands of the first kAhead MFMAs, then every
 // MFMA followed by the LDS reads of the operand kAhead MFMAs later (2 transposed reads
 // per V^T operand, 1 row read per K operand), so that each read has several MFMAs'
@@ -121,13 +102,6 @@ __device__ __forceinline__ void order_matrix_phase() {
     else if (k + kAhead < NPV + NSK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
-
-// Pins a phase's results before its closing barrier: an empty asm that reads and
-// writes them, so that no pass sinks their computation into the next phase (which
-// would put one wave's vector and matrix work back into the same phase).
-__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 template <int D>
 __device__ __forceinline__ void pin_vector_phase(FwdWave<D>& w) {
