@@ -270,7 +270,7 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
 // stream is
 //   S' row term, S' k-steps | dP' row term, dP' k-steps | dV^T (u, db) | dK^T (u, db)
 // and the two blocks follow each other.  Every operand that comes from LDS is read
-// AHEAD stream positions before its MFMA, across region and block boundaries, into a
+// AHEAD (six) stream positions before its MFMA, across region and block boundaries, into a
 // small register ring, so that no region starts by waiting for LDS.  The vector work
 // is cut into slices placed between MFMAs: P = 2^(c S') (one slice per dP' k-step,
 // from the first one after the dP' row term, when S' has left the pipeline) and
@@ -286,7 +286,7 @@ struct KvStream {
   static constexpr int DK0 = DV0 + 2 * NDB;       // first dK^T product
   static constexpr int PER = DK0 + 2 * NDB;       // MFMAs per query block
   static constexpr int N = C::NQB * PER;          // MFMAs per step
-  static constexpr int AHEAD = 4, NBUF = AHEAD + 1;
+  static constexpr int AHEAD = 6, NBUF = AHEAD + 1;
   static constexpr int P_PER = 16 / NKS;          // P values per slice (one slice per dP' k-step)
   static constexpr int DS_SL = 2 * NDB - 2;       // dS slices (dV slots 2 .. 2*NDB-1)
   static constexpr int DS_PER = (16 + DS_SL - 1) / DS_SL;
