@@ -145,9 +145,9 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     st16(p.row_aug + (int64_t)p.num_heads * p.total_tokens * 8, __builtin_bit_cast(u32x4, t));
   }
   if (row_ok && half == 0) {
-    // Row term for the dK/dV kernel: -lse/scale and -Di as bf16 high + low parts
-    // (S - lse/scale scaled by c = scale log2 e is the exponent of P in base 2).
-    const float x = -lse / p.scale, y = -di;
+    // Row term for the dK/dV kernel: -lse log2 e and -Di as bf16 high + low parts
+    // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2).
+    const float x = -lse * kLog2e, y = -di;
     const bf16 xh = (bf16)x, yh = (bf16)y;
     const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
     const bf16 z = (bf16)0.0f;
@@ -239,7 +239,7 @@ struct KvLane {
 
 // Issue the copies of a step: Q and dO rows (all waves; rows past rows_valid repeat the
 // last valid row) and the 16-byte row terms (wave 0, one row per lane; rows past
-// rows_valid take the sentinel term at index sentinel, whose -lse/scale part is
+// rows_valid take the sentinel term at index sentinel, whose -lse log2 e part is
 // -1e30, so that their P and dS are exactly zero).
 template <int D>
 __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb, const uint16_t* dob,
@@ -256,9 +256,9 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
 }
 
 // The row terms ride on one extra k-step of S and dP: each query row's 16-byte term
-// holds -lse/scale and -Di split into bf16 high and low parts, and the B operand picks
-// the pair that belongs to each product, so that S' = Q K^T - lse/scale and
-// dP' = dO V^T - Di come out of the MFMAs and P = 2^(c S'), dS = P dP' need no per-row
+// holds -lse log2 e and -Di split into bf16 high and low parts, and the B operand picks
+// the pair that belongs to each product, so that S' = Q (cK)^T - lse log2 e and
+// dP' = dO V^T - Di come out of the MFMAs and P = 2^S', dS = P dP' need no per-row
 // operands in the vector unit.  C layout of S', dP' ([queries x keys]): lane = key,
 // register i <-> query 32*qq + 8*(i/4) + 4*half + i%4.
 //
@@ -272,7 +272,7 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
 // and the two blocks follow each other.  Every operand that comes from LDS is read
 // AHEAD (six) stream positions before its MFMA, across region and block boundaries, into a
 // small register ring, so that no region starts by waiting for LDS.  The vector work
-// is cut into slices placed between MFMAs: P = 2^(c S') (one slice per dP' k-step,
+// is cut into slices placed between MFMAs: P = 2^S' (one slice per dP' k-step,
 // from the first one after the dP' row term, when S' has left the pipeline) and
 // dS = P dP' (during the dV products, from their third slot on).  The pack of P (dS) into B operands
 // completes before the first dV (dK) MFMA that needs it.
@@ -365,7 +365,7 @@ struct KvStream {
     if constexpr (k >= DP0 + 1 && k < DV0) {
       constexpr int j = k - DP0 - 1;  // 0 .. NKS-1
 #pragma unroll
-      for (int e = 0; e < P_PER; ++e) pr[j * P_PER + e] = fast_exp2(s[j * P_PER + e] * c);
+      for (int e = 0; e < P_PER; ++e) pr[j * P_PER + e] = fast_exp2(s[j * P_PER + e]);
       if constexpr ((j + 1) * P_PER == 8) pf[0] = pack8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
       if constexpr ((j + 1) * P_PER == 16)
         pf[1] = pack8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
@@ -447,7 +447,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      kf[ks] = as_bf16x8(key_ok ? ld16(p.k + base + 16 * ks) : zero16());
+      // K pre-scaled by c = scale log2 e (rounded to bf16) so that S' = Q (cK)^T -
+      // lse log2 e is already the base-2 exponent of P
+      const bf16x8 kr = as_bf16x8(key_ok ? ld16(p.k + base + 16 * ks) : zero16());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)kr[e] * c);
       vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
     }
   }
