@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--sched", type=int, default=0)
     ap.add_argument("--dq-path", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--stored-ds", action="store_true",
+                    help="self attention: grant the dS workspace so that the backward keeps dS in HBM "
+                         "(stored-dS path) instead of recomputing it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -57,6 +60,7 @@ def kernel_source_digest():
 
 
 KERNEL_NAMES = {"fwd_kernel": "fwd_kernel<", "dq_kernel": "dq_kernel<", "dkdv_kernel": "dkdv_kernel<",
+                "dq_ds_kernel": "dq_ds_kernel<", "prep_kernel": "prep_kernel<",
                 "bwd_kernel": "bwd_kernel<", "bd_fwd_kernel": "bd_fwd_kernel<", "bd_bwd_kernel": "bd_bwd_kernel<"}
 
 
@@ -153,8 +157,8 @@ def main():
     p = W.make_workload(args.workload, seed=args.seed, device="cuda")
     mode, h, d, mq = p["mode"], p["num_heads"], p["head_dim"], p["num_q"]
     lengths = p["lengths"]
-    opts = B.make_opts(sched=args.sched, dq_path=args.dq_path)
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq)
+    opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, stored_ds=args.stored_ds)
     q, k, v, do, off, off_h = p["q"], p["k"], p["v"], p["do"], p["offsets"], p["offsets_host"]
     if mode == W.MODE_BROADCAST_Q:
         o = torch.empty((p["num_seqs"], mq, h, d), dtype=torch.bfloat16, device="cuda")
@@ -205,7 +209,7 @@ def main():
     fwd_ms = sum(ev["f0"][i].elapsed_time(ev["f1"][i]) for i in range(args.steps)) / args.steps
     bwd_ms = sum(ev["f1"][i].elapsed_time(ev["b1"][i]) for i in range(args.steps)) / args.steps
     kt = {name: B.kernel_times(kid) for name, kid in
-          (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ))}
+          (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ), ("bwd_prep", B.KERNEL_BWD_PREP))}
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
@@ -214,15 +218,24 @@ def main():
     bytes_b = M.bwd_bytes(lengths, mode, h, d, mq)
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     # Per attention kernel: average launch time and the algorithmic work of one launch.
-    # Self mode runs the backward as a dQ kernel (S, dP, dQ: 3 of the 5 products plus
-    # the 2 it recomputes) and a dK/dV kernel (S, dP, dV, dK).
     work = {"fwd": (ff, bytes_f)}
-    if mode == W.MODE_SELF:
+    stored_ds = kt["bwd_prep"][0] > 0
+    if mode == W.MODE_SELF and stored_ds:
+        # Stored-dS backward: row-term kernel (O, dO in, lse in, 16-byte term out per
+        # row and head), dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, dK, dV out, the
+        # row term in, dS out as bf16 per valid pair) and dQ = dS K (dS and K in, dQ out).
         pairs = M.valid_pairs(lengths, mode)
         t = int(p["total_tokens"])
-        # dQ kernel: Q, K, V, O, dO in, dQ out (2 bytes each), lse in (4) and the
-        # 16-byte row term out per (row, head); dK/dV kernel: Q, K, V, dO in, dK, dV
-        # out, the row term in.
+        work["bwd_prep"] = (2 * t * h * d, 4 * t * h * d + 20 * t * h)
+        work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h + 2 * h * pairs)
+        work["bwd_dq"] = (2 * h * d * pairs, 4 * t * h * d + 2 * h * pairs)
+    elif mode == W.MODE_SELF:
+        # Recompute backward: a dQ kernel (S, dP, dQ: 3 of the 5 products plus the 2 it
+        # recomputes; Q, K, V, O, dO in, dQ out, lse in and the 16-byte row term out per
+        # row and head) and a dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, dK, dV out,
+        # the row term in).
+        pairs = M.valid_pairs(lengths, mode)
+        t = int(p["total_tokens"])
         work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 20 * t * h)
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
     else:
@@ -248,7 +261,7 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
                       ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
-                      "bwd_dq": "dq_kernel"}[dom]
+                      "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel", "bwd_prep": "prep_kernel"}[dom]
     if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
         roof["kernel"] = "bd_fwd_kernel"
     roof["kernel_ms"] = kd["ms"]
@@ -273,6 +286,8 @@ def main():
             "num_seqs": int(p["num_seqs"]), "num_heads": h, "head_dim": d, "num_q": mq,
             "total_tokens": int(p["total_tokens"]), "max_len": int(max(lengths)),
             "sched": ["static", "dynamic"][args.sched], "dq_path": args.dq_path, "seed": args.seed,
+            "self_bwd": ("stored_ds" if stored_ds else "recompute") if mode == W.MODE_SELF else None,
+            "ds_budget_mib": int(opts.ds_budget_mib),
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 1),

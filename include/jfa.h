@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 100 /* 1.0.0 */
+#define JFA_VERSION 110 /* 1.1.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -99,14 +99,29 @@ typedef struct jfa_opts {
                            accumulator; 1: per-program fp32 partial slabs [P,Mq,D] reduced
                            by a second kernel (run-to-run deterministic) */
   int32_t num_programs; /* persistent workgroups; 0 = one per resident slot on the device */
-  int32_t reserved;     /* must be 0 */
+  int32_t ds_budget_mib; /* self-mode backward only: MiB of workspace the backward may use
+                           to keep dS (bf16) in HBM, >= 0.  0: recompute path (a dQ kernel
+                           rebuilds S and dP, seven matrix products per query-key block).
+                           > 0: when jfa_ds_bytes() of the call's lengths fits the budget,
+                           the dK/dV kernel stores dS and dQ = scale dS K is read back from
+                           it (five products plus two bytes of HBM traffic each way per
+                           pair); otherwise the recompute path runs.  Both paths give the
+                           same result up to fp32 summation order. */
 } jfa_opts;
 
 /* Bytes of workspace jfa_fwd (pass 0) or jfa_bwd (pass 1) needs for this shape and
- * mode.  Depends on (B, H, D, Mq, T) and the options only, never on the individual
- * lengths.  Returns 0 or an error code; *bytes is written on success. */
+ * mode.  Depends on (B, H, D, Mq, T) and the options only (a self-mode backward adds
+ * opts->ds_budget_mib MiB), never on the individual lengths.  Returns 0 or an error
+ * code; *bytes is written on success. */
 int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opts* opts,
                        size_t* bytes);
+
+/* Bytes of dS storage the self-mode backward's stored-dS path needs for these lengths:
+ * sum over sequences of H * ceil(L/128)*128 * ceil(L/64)*64 * 2 (dS of every
+ * (query, key) pair of each sequence and head in bf16, keys padded to 128 and queries
+ * to 64).  A budget of at least ceil(bytes / 2^20) MiB selects that path.  Host only;
+ * offsets_host is required.  Returns 0 or an error code. */
+int jfa_ds_bytes(const jfa_shape* shape, const int32_t* offsets_host, size_t* bytes);
 
 /* Forward: o = softmax(scale * q k^T) v per sequence (per 64-token block in
  * BLOCK_DIAG mode) and the per-row lse.  See the header comment for shapes. */
@@ -119,8 +134,8 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale,
 
 /* Backward of the forward above for upstream gradient dout: dq, dk, dv (bf16,
  * accumulated in fp32).  P is recomputed from q, k and lse; Di = rowsum(dout * o) is
- * computed inline.  `scale` must equal the forward's.  In BROADCAST_Q mode dq is the
- * sum over all sequences. */
+ * computed inline (in a small row-term kernel on the stored-dS path).  `scale` must
+ * equal the forward's.  In BROADCAST_Q mode dq is the sum over all sequences. */
 int jfa_bwd(const jfa_shape* shape, int mode, float scale,
             const void* q, const void* k, const void* v,
             const void* o, const void* dout, const float* lse,
@@ -146,7 +161,8 @@ enum jfa_kernel {
   JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd */
   JFA_KERNEL_BWD = 1,    /* the main backward kernel of jfa_bwd: the dK/dV kernel in self
                             mode, the fused kernel in broadcast-Q and block-diagonal modes */
-  JFA_KERNEL_BWD_DQ = 2  /* self mode only: the dQ kernel of jfa_bwd */
+  JFA_KERNEL_BWD_DQ = 2,  /* self mode only: the dQ kernel of jfa_bwd (recompute or stored-dS) */
+  JFA_KERNEL_BWD_PREP = 3 /* self mode, stored-dS path only: the row-term kernel (Di, lse) */
 };
 
 /* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd call records a

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 100
+    assert lib.jfa_version() == 110
 
 
 def test_error_strings():
@@ -78,6 +78,33 @@ def test_fwd_rejects_null_pointers_before_any_device_work():
                      None, None)
     assert rc == -1
     assert b"non-NULL" in lib.jfa_last_error_detail()
+
+
+def test_ds_budget_option_range():
+    shape = B.make_shape(2, 2, 64, 10)
+    for bad in (-1, (1 << 20) + 1):
+        with pytest.raises(B.JfaError) as e:
+            B.workspace_size(shape, 0, 1, B.make_opts(ds_budget_mib=bad))
+        assert e.value.code == -8
+    # the budget is added to the self-mode backward's workspace only
+    base = B.workspace_size(shape, 0, 1)
+    assert B.workspace_size(shape, 0, 1, B.make_opts(ds_budget_mib=3)) >= base + 3 * (1 << 20)
+    assert B.workspace_size(shape, 0, 0, B.make_opts(ds_budget_mib=3)) == B.workspace_size(shape, 0, 0)
+    assert B.workspace_size(shape, 2, 1, B.make_opts(ds_budget_mib=3)) == B.workspace_size(shape, 2, 1)
+
+
+@pytest.mark.parametrize("lengths", [[0], [1], [64, 65, 128, 129], [600, 4000, 1, 0, 257]])
+@pytest.mark.parametrize("heads", [1, 4])
+def test_ds_bytes_formula(lengths, heads):
+    # dS of every (query, key) pair per head in bf16, keys padded to 128, queries to 64
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), heads, 128, int(off[-1]))
+    want = sum(heads * (-(-n // 128) * 128) * (-(-n // 64) * 64) * 2 for n in lengths)
+    assert B.ds_bytes(shape, off) == want
+    assert B.ds_budget_mib(shape, off) == max(1, -(-want // (1 << 20)))
+    with pytest.raises(B.JfaError) as e:
+        B.ds_bytes(shape, off + 1)
+    assert e.value.code == -5
 
 
 def test_workspace_sizes():

@@ -1,8 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is generated at full size on the GPU and run through jfa_fwd / jfa_bwd
-with default options (the bench's static schedule; both broadcast-Q dQ paths).  The
-oracle then checks sampled sequences one by one -- the longest, the shortest, the
+with the options bench.py uses by default (static schedule, recompute self-attention
+backward; both broadcast-Q dQ paths), and workload 3 also with the stored-dS backward.
+The oracle then checks sampled sequences one by one -- the longest, the shortest, the
 median and a few seeded picks -- since in self and block-diagonal attention every
 sequence's outputs and gradients depend on that sequence alone.  Broadcast-Q (whose
 dQ sums over all sequences) is small enough to check whole."""
@@ -28,9 +29,17 @@ def _sample_sequences(lengths, k, seed):
     return sorted(picks)
 
 
-def _run(workload, opts=None):
-    print(f"[case] full-size workload {workload} opts={opts}", flush=True)
+def _shape(p):
+    return B.make_shape(p["num_seqs"], p["num_heads"], p["head_dim"], p["total_tokens"], p["num_q"])
+
+
+def _run(workload, opts=None, bench=False, stored_ds=False):
     p = W.make_workload(workload, seed=0, device="cuda")
+    if bench:
+        opts = B.bench_opts(p["mode"], _shape(p), p["offsets_host"], stored_ds=stored_ds)
+    print(f"[case] full-size workload {workload} opts=({opts.sched if opts else 0}, "
+          f"{opts.dq_path if opts else 0}, {opts.num_programs if opts else 0}, "
+          f"{opts.ds_budget_mib if opts else 0})", flush=True)
     o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts)
     grads = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"], p["scale"],
                   opts)
@@ -38,9 +47,10 @@ def _run(workload, opts=None):
     return p, o, lse, grads
 
 
-@pytest.mark.parametrize("workload,samples", [(1, 4), (3, 6), (4, 1), (5, 6)])
-def test_full_size_sampled_sequences(workload, samples):
-    p, o, lse, (dq, dk, dv) = _run(workload)
+@pytest.mark.parametrize("workload,samples,stored_ds", [(1, 4, False), (3, 6, False), (4, 1, False), (5, 6, False),
+                                                       (3, 4, True)])
+def test_full_size_sampled_sequences(workload, samples, stored_ds):
+    p, o, lse, (dq, dk, dv) = _run(workload, bench=True, stored_ds=stored_ds)
     off = p["offsets_host"].astype(np.int64)
     mode = p["mode"]
     for b in _sample_sequences(p["lengths"], samples, workload):

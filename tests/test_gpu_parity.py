@@ -35,6 +35,68 @@ def test_self_few_programs():
     G.run_case(RAGGED, 2, 128, opts=B.make_opts(num_programs=3), seed=5, label="self 3 programs")
 
 
+def _ds_opts(lengths, heads, head_dim, **kw):
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), heads, head_dim, int(off[-1]))
+    return B.make_opts(ds_budget_mib=B.ds_budget_mib(shape, off), **kw)
+
+
+def _ran_stored_ds(fn):
+    """Run fn() with kernel timing on; True when the stored-dS row-term kernel ran."""
+    B.kernel_timing(True)
+    try:
+        fn()
+        return B.kernel_times(B.KERNEL_BWD_PREP)[0] > 0
+    finally:
+        B.kernel_timing(False)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_stored_ds_ragged(head_dim):
+    opts = _ds_opts(RAGGED, 2, head_dim)
+    assert _ran_stored_ds(lambda: G.run_case(RAGGED, 2, head_dim, opts=opts, seed=21,
+                                             label=f"self stored dS D{head_dim}"))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_stored_ds_empties_and_long(head_dim):
+    lengths = [0, 33, 0, 70, 1, 0, 700, 2, 383, 0]
+    G.run_case(lengths, 3, head_dim, opts=_ds_opts(lengths, 3, head_dim), seed=22, label="self stored dS empties")
+
+
+def test_self_stored_ds_dynamic_and_few_programs():
+    lengths = RAGGED + [511, 2]
+    G.run_case(lengths, 2, 128, opts=_ds_opts(lengths, 2, 128, sched=1), seed=23, label="stored dS dynamic")
+    G.run_case(lengths, 2, 128, opts=_ds_opts(lengths, 2, 128, num_programs=3), seed=24, label="stored dS 3 progs")
+
+
+def test_self_stored_ds_budget_too_small_falls_back():
+    lengths = [2000, 700]
+    opts = B.make_opts(ds_budget_mib=1)  # needs 2 * 2048 * 2048 * 2 + ... bytes > 1 MiB
+    assert not _ran_stored_ds(lambda: G.run_case(lengths, 2, 128, opts=opts, seed=25, label="budget too small"))
+
+
+def test_self_stored_ds_and_recompute_paths_on_one_forward():
+    """Both backward paths on the same forward outputs.  dV comes from the same dK/dV
+    arithmetic on both (bit-identical); dK differs only in the summation order of Di;
+    dQ is formed from a bf16 dS on both paths, rounded from P computed in two different
+    kernels, so the two dQ agree only to bf16 rounding -- each is checked against the
+    oracle."""
+    lengths = [130, 1, 640, 64, 257]
+    p = W.make_problem(lengths, 2, 128, seed=26, device="cpu")
+    g = G.to_gpu(p)
+    o, lse = G.gpu_fwd(g)
+    a = G.gpu_bwd(g, o, lse)
+    b = G.gpu_bwd(g, o, lse, _ds_opts(lengths, 2, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(a[2], b[2])
+    assert G.rel_l2(G.f64(b[1]), G.f64(a[1])) < 1e-3
+    refs = G.oracle_bwd(p)
+    ea = G.check_bwd(a, refs, "recompute path")
+    eb = G.check_bwd(b, refs, "stored-dS path")
+    print(f"rel-L2 vs oracle: recompute {ea}, stored dS {eb}", flush=True)
+
+
 def test_self_device_offsets_slow_path():
     G.run_case([17, 130, 64], 1, 64, host_offsets=False, seed=6, label="self slow path")
 

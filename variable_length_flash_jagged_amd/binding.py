@@ -21,6 +21,7 @@ PASS_BWD = 1
 KERNEL_FWD = 0
 KERNEL_BWD = 1
 KERNEL_BWD_DQ = 2
+KERNEL_BWD_PREP = 3
 
 
 class JfaError(RuntimeError):
@@ -36,7 +37,7 @@ class Shape(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("sched", ctypes.c_int32), ("dq_path", ctypes.c_int32), ("num_programs", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("ds_budget_mib", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,6 +68,8 @@ def lib():
         L.jfa_kernel_timing.argtypes = [ctypes.c_int]
         L.jfa_kernel_times.restype = ctypes.c_int
         L.jfa_kernel_times.argtypes = [ctypes.c_int, i64p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        L.jfa_ds_bytes.restype = ctypes.c_int
+        L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
         L.jfa_schedule.argtypes = [sp, ctypes.c_int, ctypes.c_int, vp, op, vp, i64, vp, i64, i64p, i32p, i32p, i32p]
         _lib = L
@@ -84,8 +87,8 @@ def make_shape(num_seqs, num_heads, head_dim, total_tokens, num_q=0):
     return Shape(int(num_seqs), int(num_heads), int(head_dim), int(num_q), int(total_tokens))
 
 
-def make_opts(sched=0, dq_path=0, num_programs=0):
-    return Opts(int(sched), int(dq_path), int(num_programs), 0)
+def make_opts(sched=0, dq_path=0, num_programs=0, ds_budget_mib=0):
+    return Opts(int(sched), int(dq_path), int(num_programs), int(ds_budget_mib))
 
 
 def workspace_size(shape, mode, pass_, opts=None):
@@ -93,6 +96,26 @@ def workspace_size(shape, mode, pass_, opts=None):
     _check(lib().jfa_workspace_size(ctypes.byref(shape), mode, pass_, ctypes.byref(opts) if opts else None,
                                     ctypes.byref(n)), "jfa_workspace_size")
     return int(n.value)
+
+
+def ds_bytes(shape, offsets_host):
+    """Bytes of dS storage the stored-dS self-attention backward needs (jfa_ds_bytes)."""
+    off = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    n = ctypes.c_size_t(0)
+    _check(lib().jfa_ds_bytes(ctypes.byref(shape), off.ctypes.data, ctypes.byref(n)), "jfa_ds_bytes")
+    return int(n.value)
+
+
+def ds_budget_mib(shape, offsets_host):
+    """Smallest ds_budget_mib that selects the stored-dS path for these lengths."""
+    return max(1, -(-ds_bytes(shape, offsets_host) // (1 << 20)))
+
+
+def bench_opts(mode, shape, offsets_host, sched=0, dq_path=0, stored_ds=False):
+    """Options the benchmark runs with: the given schedule and broadcast-Q dQ path and,
+    with stored_ds in self attention, a dS budget that selects the stored-dS backward."""
+    budget = ds_budget_mib(shape, offsets_host) if (stored_ds and mode == MODE_SELF) else 0
+    return make_opts(sched=sched, dq_path=dq_path, ds_budget_mib=budget)
 
 
 def schedule(shape, mode, pass_, offsets_host, opts=None):

@@ -65,6 +65,7 @@ int device_cus() {
 
 struct Opts {
   int sched = 0, dq_path = 0, num_programs = 0;
+  int64_t ds_budget = 0;  // bytes
 };
 
 int check_opts(const jfa_opts* o, Opts& out) {
@@ -74,10 +75,12 @@ int check_opts(const jfa_opts* o, Opts& out) {
   if (o->dq_path != 0 && o->dq_path != 1) return fail(JFA_ERR_BAD_OPTION, "opts.dq_path must be 0 or 1");
   if (o->num_programs < 0 || o->num_programs > (1 << 20))
     return fail(JFA_ERR_BAD_OPTION, "opts.num_programs out of range");
-  if (o->reserved != 0) return fail(JFA_ERR_BAD_OPTION, "opts.reserved must be 0");
+  if (o->ds_budget_mib < 0 || o->ds_budget_mib > (1 << 20))
+    return fail(JFA_ERR_BAD_OPTION, "opts.ds_budget_mib must be in [0, 2^20]");
   out.sched = o->sched;
   out.dq_path = o->dq_path;
   out.num_programs = o->num_programs;
+  out.ds_budget = (int64_t)o->ds_budget_mib << 20;
   return JFA_OK;
 }
 
@@ -105,7 +108,8 @@ int max_programs(const Opts& o, int wg_per_cu) {
 
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct Layout {
-  size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, stats = 0, prefix = 0, acc = 0, total = 0;
+  size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, ds_base = 0, stats = 0, ds = 0, prefix = 0, acc = 0,
+         total = 0;
   int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
@@ -135,7 +139,9 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
   L.tiles = at;
   at += align_up(L.tile_cap * sizeof(Tile));
   if (pass == JFA_PASS_BWD && mode == JFA_MODE_SELF) {
-    // second schedule: the dQ kernel's query-row tiles (forward tiling)
+    // second schedule: the dQ kernel's query-row tiles (kDqRows rows on the recompute
+    // path, kDsRows on the stored-dS path; the capacities cover both)
+    static_assert(kDqRows <= kDsRows && kDsWgPerCu <= kDqWgPerCu, "dQ schedule capacity");
     L.programs2_cap = max_programs(o, kDqWgPerCu);
     L.seg2_cap = L.programs2_cap + 1;
     L.seg2 = at;
@@ -143,8 +149,14 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.tile2_cap = H * (T / kDqRows + B + 1);
     L.tiles2 = at;
     at += align_up(L.tile2_cap * sizeof(Tile));
-    L.stats = at;  // per query row 16-byte term (-lse/scale, -Di in bf16 high/low), [H, T, 8], + sentinel
+    L.ds_base = at;  // stored-dS path: first dS block of each sequence, int64 [B+1]
+    at += align_up((B + 1) * sizeof(int64_t));
+    L.stats = at;  // per query row 16-byte term (-lse log2 e, -Di in bf16 high/low), [H, T, 8], + sentinel
     at += align_up((H * T + 1) * 16);
+    if (o.ds_budget > 0) {
+      L.ds = at;  // stored dS, up to the budget
+      at += align_up((size_t)o.ds_budget);
+    }
   } else if (pass == JFA_PASS_BWD) {
     L.acc = at;
     const int64_t acc_elems = (o.dq_path == 0) ? Mq * H * D : (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
@@ -180,6 +192,10 @@ int intake_offsets(const jfa_shape* s, const int32_t* off_dev, const int32_t* of
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Stored-dS blocks (kBwdKeys keys x kBwdRows queries) of one head of a sequence of
+// length len.
+int64_t ds_blocks(int64_t len) { return cdiv(len, kBwdKeys) * cdiv(len, kBwdRows); }
 
 // Pinned host staging ring for the asynchronous schedule upload.  A slot is reused
 // only after the copy that last read it has completed (its event).
@@ -242,12 +258,15 @@ void put_schedule(const Schedule& sc, size_t seg_off, size_t tiles_off, std::vec
     t[i] = Tile{sc.tiles[i].b, (sc.tiles[i].h << 24) | sc.tiles[i].blk};
 }
 
-void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf, const Schedule* sc2 = nullptr) {
+void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf, const Schedule* sc2 = nullptr,
+               const std::vector<int64_t>* ds_base = nullptr) {
   size_t end = L.tiles + sc.tiles.size() * sizeof(Tile);
   if (sc2) end = L.tiles2 + sc2->tiles.size() * sizeof(Tile);
+  if (ds_base) end = L.ds_base + ds_base->size() * sizeof(int64_t);
   buf.assign(end, 0);
   put_schedule(sc, L.seg, L.tiles, buf);
   if (sc2) put_schedule(*sc2, L.seg2, L.tiles2, buf);
+  if (ds_base) memcpy(buf.data() + L.ds_base, ds_base->data(), ds_base->size() * sizeof(int64_t));
 }
 
 int launch_status(hipError_t e, const char* what) {
@@ -258,7 +277,7 @@ int launch_status(hipError_t e, const char* what) {
 struct KernelTimer {
   std::mutex mu;
   bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[3];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[4];
   void forget_locked() {
     for (auto& v : ev) {
       for (auto& pr : v) {
@@ -310,8 +329,8 @@ int jfa_kernel_timing(int enable) {
 
 int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
   g_detail.clear();
-  if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ)
-    return fail(JFA_ERR_BAD_MODE, "kernel must be JFA_KERNEL_FWD, JFA_KERNEL_BWD or JFA_KERNEL_BWD_DQ");
+  if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ && pass != JFA_KERNEL_BWD_PREP)
+    return fail(JFA_ERR_BAD_MODE, "kernel must be a jfa_kernel");
   if (!launches || !total_ms) return fail(JFA_ERR_NULL_POINTER, "launches and total_ms must be non-NULL");
   std::lock_guard<std::mutex> lock(g_timer.mu);
   double sum = 0.0;
@@ -365,6 +384,19 @@ int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opt
   Layout L;
   layout_for(shape, mode, pass, o, L);
   *bytes = L.total;
+  return JFA_OK;
+}
+
+int jfa_ds_bytes(const jfa_shape* shape, const int32_t* offsets_host, size_t* bytes) {
+  g_detail.clear();
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  if (!offsets_host || !bytes) return fail(JFA_ERR_NULL_POINTER, "offsets_host and bytes must be non-NULL");
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, nullptr, offsets_host, nullptr, lengths))) return rc;
+  int64_t blocks = 0;
+  for (int32_t len : lengths) blocks += ds_blocks(len);
+  *bytes = (size_t)blocks * shape->num_heads * kDsBlockBytes;
   return JFA_OK;
 }
 
@@ -569,6 +601,35 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
 
   if (mode == JFA_MODE_SELF) {
     if (sc.tiles.empty()) return JFA_OK;
+    // Stored-dS path when the caller's budget holds dS of every sequence and head.
+    std::vector<int64_t> ds_base(shape->num_seqs + 1, 0);
+    for (int b = 0; b < shape->num_seqs; ++b) ds_base[b + 1] = ds_base[b] + ds_blocks(lengths[b]) * H;
+    if (op.ds_budget > 0 && ds_base.back() * kDsBlockBytes <= op.ds_budget) {
+      Schedule sq;
+      schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDsRows, max_programs(op, kDsWgPerCu), op.sched == 1, sq);
+      if ((int64_t)sq.tiles.size() > L.tile2_cap || sq.programs > L.programs2_cap)
+        return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+      std::vector<char> buf;
+      serialise(sc, L, buf, &sq, &ds_base);
+      if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+      p.dq = (uint16_t*)dq;
+      p.row_aug = (uint16_t*)(ws + L.stats);
+      p.ds = ws + L.ds;
+      p.ds_base = (const int64_t*)(ws + L.ds_base);
+      p.dq_tiles = (const Tile*)(ws + L.tiles2);
+      p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
+      p.dq_programs = sq.programs;
+      if ((rc = launch_status(
+               timed_launch(JFA_KERNEL_BWD_PREP, stream, [&] { return launch_bwd_self_prep(p, D, stream); }),
+               "backward row-term launch")))
+        return rc;
+      if ((rc = launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                              "backward dK/dV launch")))
+        return rc;
+      return launch_status(
+          timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq_ds(p, D, stream); }),
+          "backward dQ launch");
+    }
     Schedule sq;
     schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDqRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
     if ((int64_t)sq.tiles.size() > L.tile2_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");

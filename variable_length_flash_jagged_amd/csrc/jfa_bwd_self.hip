@@ -22,14 +22,20 @@
 //    registers.  dQ is written once, by its owner.
 //  * dkdv_kernel: one workgroup = one tile of kBwdKeys (128) keys of one (sequence,
 //    head); wave w owns keys 32w..32w+31 with their K, V operands and fp32 dK^T, dV^T
-//    accumulators in registers; 64 query rows stream through double-buffered,
-//    swizzled LDS tiles (direct global->LDS copies issued one step ahead) together
-//    with their (lse * log2 e, Di) pairs.  Four products per step: S = Q K^T and
+//    accumulators in registers; 64 query rows stream through a three-slot ring of
+//    swizzled LDS tiles (direct global->LDS copies issued two steps ahead) together
+//    with their (lse * log2 e, Di) row terms.  Four products per step: S = Q K^T and
 //    dP = dO V^T (C layout: lane = key), then dV^T += dO^T P and dK^T += Q^T dS with
 //    dO^T, Q^T read transposed from LDS (ds_read_b64_tr_b16).  dK and dV are written
 //    once, by their owner.
 // The split recomputes S and dP once more (seven products per query-key block
 // instead of five) in exchange for no atomics and no fp32 dQ accumulator in HBM.
+//
+// Stored-dS variant (when the caller grants the workspace): prep_kernel writes the row
+// terms, the dK/dV kernel also stores dS (bf16, two bytes per query-key pair) and
+// dq_ds_kernel forms dQ = scale dS K from it -- five products per block plus the dS
+// round trip through HBM instead of seven products.
+#include <algorithm>
 #include <utility>
 
 #include "jfa_device.h"
@@ -214,10 +220,11 @@ struct KvCfg {
   static constexpr int RB = 2 * D;
   static constexpr int QBUF = QB * RB;
   static constexpr int ABUF = QB * 16;                 // one 16-byte row term per query row
-  static constexpr int OFF_Q = 0;                      // [2][QBUF]
-  static constexpr int OFF_DO = OFF_Q + 2 * QBUF;      // [2][QBUF]
-  static constexpr int OFF_AUG = OFF_DO + 2 * QBUF;    // [2][ABUF]
-  static constexpr int SMEM = OFF_AUG + 2 * ABUF;
+  static constexpr int NS = kBwdStages;
+  static constexpr int OFF_Q = 0;                      // [NS][QBUF]
+  static constexpr int OFF_DO = OFF_Q + NS * QBUF;     // [NS][QBUF]
+  static constexpr int OFF_AUG = OFF_DO + NS * QBUF;   // [NS][ABUF]
+  static constexpr int SMEM = OFF_AUG + NS * ABUF;
   static_assert(QB == 64, "one 64-lane copy moves a step's row terms");
 };
 
@@ -227,7 +234,8 @@ template <int D>
 struct KvLane {
   RowOperands<KvCfg<D>::RB, KvCfg<D>::NKS> row;  // Q, dO rows as A operands of S, dP
   TrOperands<KvCfg<D>::RB, KvCfg<D>::NDB> tr;    // Q^T, dO^T as A operands of dK^T, dV^T
-  TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, KvCfg<D>::NW> copy;
+  using Copy = TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, KvCfg<D>::NW>;
+  Copy copy;
   bf16x8 pick_s, pick_dp;  // k-slots 0,1 (S) and 4,5 (dP) of the row term, lanes 0-31
   __device__ __forceinline__ void init_pick(int lane) {
     const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
@@ -255,6 +263,37 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
   }
 }
 
+// Stored dS (the stored-dS path).  dS of (sequence b, head h) is kept as blocks of 128
+// keys (one dK/dV tile j) x 64 queries (one step it), NJ = ceil(L/128) x NQ = ceil(L/64)
+// of them, block (j, it) at index ds_base[b] + (h NJ + j) NQ + it, 16 KB each.  Inside a
+// block, dS[key 32w + r][query 32qq + 16x + 8y + 4e + i] (r < 32; x, y, e < 2; i < 4)
+// sits at
+//   byte w*4096 + qq*2048 + x*1024 + 16*(32e + (r ^ (8x + 4e))) + 8y + 2i.
+// This is the order the dK/dV kernel produces it in: in wave w, lane (half e, key r)
+// holds the packed dS of queries 32qq + 16x + 8y + 4e + i for y, i as one 16-byte
+// register per (qq, x), so each of its four stores per step writes 1 KB contiguous.
+// The XOR term makes the transposed LDS fetches of the dQ kernel (per half-wave: 4 keys
+// x 8 query quads = 32 distinct 8-byte slots of a 256-byte bank line) conflict free.
+__device__ __forceinline__ uint32_t ds_store_offset(int wave, int lane) {
+  const int r = lane & 31, e = lane >> 5;
+  return (uint32_t)(wave * 4096 + 512 * e + 16 * (r ^ (4 * e)));
+}
+
+// Store of register x of query block qq (unit offsets as above; x flips bit 7).
+__device__ __forceinline__ void store_ds_unit(char* blk, uint32_t off, int qq, int x, const bf16x8& v) {
+  st16_global_nt(blk, (off ^ (uint32_t)(x << 7)) + qq * 2048 + x * 1024, __builtin_bit_cast(u32x4, v));
+}
+
+// The four stores of one step.
+template <int NQB>
+__device__ __forceinline__ void store_ds(char* blk, uint32_t off, const bf16x8 (&keep)[NQB][2]) {
+  char* b = (char*)uniform_ptr(blk);
+#pragma unroll
+  for (int qq = 0; qq < NQB; ++qq)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) store_ds_unit(b, off, qq, x, keep[qq][x]);
+}
+
 // The row terms ride on one extra k-step of S and dP: each query row's 16-byte term
 // holds -lse log2 e and -Di split into bf16 high and low parts, and the B operand picks
 // the pair that belongs to each product, so that S' = Q (cK)^T - lse log2 e and
@@ -276,7 +315,7 @@ __device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb
 // from the first one after the dP' row term, when S' has left the pipeline) and
 // dS = P dP' (during the dV products, from their third slot on).  The pack of P (dS) into B operands
 // completes before the first dV (dK) MFMA that needs it.
-template <int D>
+template <int D, bool STORE>
 struct KvStream {
   using C = KvCfg<D>;
   static constexpr int NKS = C::NKS, NDB = C::NDB;
@@ -304,11 +343,37 @@ struct KvStream {
   f32x16 s, dp;
   float pr[16], dsr[16];
   bf16x8 pf[2], dsf[2];
+  // STORE: keep[qq] holds the packed dS of query block qq.  The previous step's values
+  // are stored from inside this step's stream, spread over MFMA slots (block 0 before
+  // slot DK0 - 1, where this step overwrites it; block 1 after), so that the stores
+  // never queue behind the step's ring copies at the step start.
+  bf16x8 (&keep)[C::NQB][2];
+  char* sblk;       // wave-uniform: the stored block of the previous step
+  uint32_t soff;    // this lane's store offset (ds_store_offset)
+  static constexpr int ST0 = 6, ST0_STEP = (DK0 - 2 - ST0);       // block 0 stores: ST0 + x ST0_STEP
+  static constexpr int ST1 = DK0 + 4, ST1_STEP = (PER + DK0 - 2 - ST1);
+  static_assert(ST0_STEP >= 1 && ST0 + ST0_STEP < DK0 - 1 && ST1 + ST1_STEP < PER + DK0 - 1, "store slots");
 
   __device__ __forceinline__ KvStream(const JFA_LDS char* qt_, const JFA_LDS char* dot_, const JFA_LDS char* augt_,
                                       const KvLane<D>& ln_, const bf16x8 (&kf_)[NKS], const bf16x8 (&vf_)[NKS],
-                                      f32x16 (&dk_)[NDB], f32x16 (&dv_)[NDB], int l32_, float c_)
-      : qt(qt_), dot(dot_), augt(augt_), ln(ln_), kf(kf_), vf(vf_), dk(dk_), dv(dv_), l32(l32_), c(c_) {}
+                                      f32x16 (&dk_)[NDB], f32x16 (&dv_)[NDB], int l32_, float c_,
+                                      bf16x8 (&keep_)[C::NQB][2], char* sblk_, uint32_t soff_)
+      : qt(qt_), dot(dot_), augt(augt_), ln(ln_), kf(kf_), vf(vf_), dk(dk_), dv(dv_), l32(l32_), c(c_),
+        keep(keep_), sblk(sblk_), soff(soff_) {}
+
+  // Store slot of stream position K: query block (0 or 1) * 2 + register x, or -1.
+  template <int K>
+  static constexpr int store_slot() {
+    if (!STORE) return -1;
+    if (K == ST0 || K == ST0 + ST0_STEP) return (K - ST0) / ST0_STEP;
+    if (K == ST1 || K == ST1 + ST1_STEP) return 2 + (K - ST1) / ST1_STEP;
+    return -1;
+  }
+  template <int K>
+  __device__ __forceinline__ void store() {
+    constexpr int sl = store_slot<K>();
+    if constexpr (sl >= 0) store_ds_unit(sblk, soff, sl >> 1, sl & 1, keep[sl >> 1][sl & 1]);
+  }
 
   // LDS read(s) of stream position K (none for the dP' row term, which reuses the S'
   // one); reads<K>() counts them.
@@ -378,8 +443,13 @@ struct KvStream {
       }
       if constexpr ((j + 1) * DS_PER >= 8 && j * DS_PER < 8)
         dsf[0] = pack8(dsr[0], dsr[1], dsr[2], dsr[3], dsr[4], dsr[5], dsr[6], dsr[7]);
-      if constexpr (j == DS_SL - 1)
+      if constexpr (j == DS_SL - 1) {
         dsf[1] = pack8(dsr[8], dsr[9], dsr[10], dsr[11], dsr[12], dsr[13], dsr[14], dsr[15]);
+        if constexpr (STORE) {
+          keep[K / PER][0] = dsf[0];
+          keep[K / PER][1] = dsf[1];
+        }
+      }
     }
   }
   template <int K>
@@ -397,6 +467,7 @@ struct KvStream {
     if constexpr (valus<K>() > 0) __builtin_amdgcn_sched_group_barrier(0x002, valus<K>(), 0);
     if constexpr (K + AHEAD < N && reads<K + AHEAD>() > 0)
       __builtin_amdgcn_sched_group_barrier(0x100, reads<K + AHEAD>(), 0);
+    if constexpr (store_slot<K>() >= 0) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
   }
 
   template <int K>
@@ -404,6 +475,7 @@ struct KvStream {
     mfma<K>();
     valu<K>();
     if constexpr (K + AHEAD < N) read<K + AHEAD>();
+    store<K>();
   }
 
   __device__ __forceinline__ void go() {
@@ -420,7 +492,7 @@ struct KvStream {
   __device__ __forceinline__ void orders(std::integer_sequence<int, K...>) { (order<K>(), ...); }
 };
 
-template <int D>
+template <int D, bool STORE>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D>& ln,
                                           int tid) {
   using C = KvCfg<D>;
@@ -455,9 +527,26 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
       vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
     }
   }
-  kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, 0, min(C::QB, L), smem + C::OFF_Q, smem + C::OFF_DO,
-              smem + C::OFF_AUG, wave, lane);
-  wait_vmem();
+  // Three-slot ring: step it+2 is copied while step it is computed, so each copy has two
+  // steps to land.  The wait that closes a step leaves only the newest step's copies
+  // outstanding (vector-memory loads return in issue order, so the older step's copies
+  // have landed; dS stores that may still be in flight do not matter here).  Wave 0
+  // issues one more copy (the row terms) than the others; waiting for all but 2J lets
+  // it wait for one copy of the newest step as well, which is harmless.
+  auto issue = [&](int it, int slot) {
+    const int row0 = it * C::QB;
+    kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, L - row0),
+                smem + C::OFF_Q + slot * C::QBUF, smem + C::OFF_DO + slot * C::QBUF,
+                smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
+  };
+  constexpr int COPIES = 2 * KvLane<D>::Copy::J;
+  issue(0, 0);
+  if (nq > 1) {
+    issue(1, 1);
+    wait_vmem_n<COPIES>();
+  } else {
+    wait_vmem();
+  }
   __syncthreads();
 
   f32x16 dk[C::NDB], dv[C::NDB];
@@ -466,20 +555,35 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  for (int it = 0; it < nq; ++it) {
-    const int cur = it & 1;
-    const int row0 = it * C::QB;
-    if (it + 1 < nq)
-      kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0 + C::QB, min(C::QB, L - row0 - C::QB),
-                  smem + C::OFF_Q + (cur ^ 1) * C::QBUF, smem + C::OFF_DO + (cur ^ 1) * C::QBUF,
-                  smem + C::OFF_AUG + (cur ^ 1) * C::ABUF, wave, lane);
+  // Stored dS: this tile's blocks (j, 0 .. nq-1) and this lane's store offset.  A step's
+  // dS is stored during the next step (see KvStream), the last one after the loop.  The
+  // first step stores the zero-initialised registers into block 0, which the second
+  // step (or the store after the loop) then overwrites -- stores of one lane to the
+  // same address land in program order.
+  bf16x8 keep[C::NQB][2];
+  char* ds_row = nullptr;
+  uint32_t ds_off = 0;
+  if constexpr (STORE) {
+    const int64_t nj = (L + C::BN - 1) / C::BN;
+    ds_row = (char*)uniform_ptr(p.ds + (p.ds_base[b] + ((int64_t)h * nj + j) * nq) * kDsBlockBytes);
+    ds_off = ds_store_offset(wave, lane);
+#pragma unroll
+    for (int qq = 0; qq < C::NQB; ++qq) keep[qq][0] = keep[qq][1] = as_bf16x8(zero16());
+  }
+
+  for (int it = 0, cur = 0; it < nq; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
+    if (it + 2 < nq) issue(it + 2, cur == 0 ? C::NS - 1 : cur - 1);
     const JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
     const JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
     const JFA_LDS char* augt = smem + C::OFF_AUG + cur * C::ABUF;
-    KvStream<D>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c).go();
-    wait_vmem();
+    KvStream<D, STORE>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c, keep,
+                       ds_row + (int64_t)max(it - 1, 0) * kDsBlockBytes, ds_off)
+        .go();
+    if (it + 2 < nq) wait_vmem_n<COPIES>();
+    else wait_vmem();
     __syncthreads();
   }
+  if constexpr (STORE) store_ds(ds_row + (int64_t)(nq - 1) * kDsBlockBytes, ds_off, keep);
 
   if (key_ok) {
     const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D + 4 * half;
@@ -537,7 +641,7 @@ __global__ void __launch_bounds__(kDqWaves * 64)
             [&](Tile t) { dq_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
-template <int D>
+template <int D, bool STORE>
 __global__ void __launch_bounds__(kBwdWaves * 64)
     __attribute__((amdgpu_waves_per_eu(dkdv_wg_per_cu(D) * kBwdWaves / 4, dkdv_wg_per_cu(D) * kBwdWaves / 4)))
     dkdv_kernel(BwdParams p) {
@@ -549,7 +653,231 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
-            [&](Tile t) { dkdv_tile<D>(p, t, smem, ln, threadIdx.x); });
+            [&](Tile t) { dkdv_tile<D, STORE>(p, t, smem, ln, threadIdx.x); });
+}
+
+// --------------------------------------------------------- stored-dS path: row terms
+
+// Row terms for the dK/dV kernel when no dQ kernel runs before it: D/8 lanes per (token,
+// head) row load 16 bytes each of O and dO, Di = rowsum(dO * O) in fp32, and the row's
+// group leader writes (-lse log2 e, -Di) as bf16 high + low parts, the same 16-byte term
+// as dq_tile.  Block 0 writes the sentinel term.
+template <int D>
+__global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int64_t H = p.num_heads, T = p.total_tokens;
+  const int64_t rows = T * H;
+  const int sub = threadIdx.x % LPR;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const bf16 z = (bf16)0.0f;
+    const bf16x8 t = {(bf16)(-1e30f), z, z, z, z, z, z, z};
+    st16(p.row_aug + H * T * 8, __builtin_bit_cast(u32x4, t));
+  }
+  for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
+    const bf16x8 o8 = as_bf16x8(ld16(p.o + r * D + 8 * sub));
+    const bf16x8 d8 = as_bf16x8(ld16(p.dout + r * D + 8 * sub));
+    float di = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) di = fmaf((float)d8[e], (float)o8[e], di);
+#pragma unroll
+    for (int m = LPR / 2; m > 0; m >>= 1) di += __shfl_xor(di, m, LPR);
+    if (sub == 0) {
+      const int64_t t = r / H, h = r - t * H;
+      const float x = -p.lse[h * T + t] * kLog2e, y = -di;
+      const bf16 xh = (bf16)x, yh = (bf16)y;
+      const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
+      const bf16 z = (bf16)0.0f;
+      const bf16x8 v = {xh, xl, z, z, yh, yl, z, z};
+      st16(p.row_aug + (h * T + t) * 8, __builtin_bit_cast(u32x4, v));
+    }
+  }
+}
+
+// ---------------------------------------------------------- stored-dS path: dQ = dS K
+
+// dQ = scale dS K from the stored dS: one workgroup = kDsRows (256) query rows of one
+// (sequence, head), wave w owning rows 64w .. 64w+63 -- exactly the queries of one
+// stored block column it = 4 blk + w -- as two 32-row column blocks of fp32 dQ^T
+// accumulators.  The loop streams 64 keys at a time (half of a stored block) through a
+// three-slot LDS ring: the K rows (swizzled tile, shared by the waves) and each wave's
+// own 8 KB dS slice (a linear copy of the stored bytes).  Per 16-key k-step:
+// dQ^T += K^T dS^T with A = K^T (transposed fetch of the K tile) and B = dS^T
+// (transposed fetch of the slice, 4 keys x 16 queries per 16-lane group).  The kernel
+// moves two bytes of dS per (query, key) pair for 2 D flops, so HBM, not the matrix
+// unit, bounds it; the ring keeps two slots of copies in flight.
+template <int D>
+struct DsCfg {
+  static constexpr int NW = kDsWaves;
+  static constexpr int BM = kDsRows;
+  static constexpr int BK = 64;                          // keys per step
+  static constexpr int NDB = D / 32;
+  static constexpr int RB = 2 * D;
+  static constexpr int KBUF = BK * RB;                   // K rows of a step
+  static constexpr int SLICE = kDsBlockBytes / 2;        // one wave's dS: 64 keys x 64 queries
+  static constexpr int STAGE = KBUF + NW * SLICE;
+  static constexpr int NS = 3;
+  static constexpr int SMEM = NS * STAGE;
+  using Copy = TileCopy<RB, BK, NW>;
+  static constexpr int SLICE_COPIES = SLICE / 1024;
+  static_assert(BK * 2 == kBwdKeys && kBwdRows == 64 && BM == NW * kBwdRows, "slices are halves of stored blocks");
+};
+
+template <int D>
+struct DsLane {
+  TrOperands<DsCfg<D>::RB, DsCfg<D>::NDB> ktr;  // K^T as the A operand
+  typename DsCfg<D>::Copy copy;
+  int boff[2][2];  // dS^T fetch offsets by (k-step parity, upper 8 keys)
+  __device__ __forceinline__ void init(int lane) {
+    // Source lane (group g16, s16) of a transposed fetch points at key
+    // 16t + 8hi + 4(g16 >> 1) + (s16 >> 2) and the query quad 16(g16 & 1) + 4(s16 & 3) of
+    // column block cb; in stored-block terms that is row r = 16(t & 1) + 8hi +
+    // 4(g16 >> 1) + (s16 >> 2) of key group w = t >> 1, quad x = g16 & 1,
+    // y = (s16 >> 1) & 1, e = s16 & 1.
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int x = g16 & 1, y = (s16 >> 1) & 1, e = s16 & 1;
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 16 * tl + 8 * hi + 4 * (g16 >> 1) + (s16 >> 2);
+        boff[tl][hi] = x * 1024 + 16 * (32 * e + (r ^ (8 * x + 4 * e))) + 8 * y;
+      }
+  }
+  // B operand of k-step t (keys 16t .. 16t+15 of the step) for column block cb.
+  __device__ __forceinline__ bf16x8 ds(const JFA_LDS char* slice, int t, int cb) const {
+    const int c = 4096 * (t >> 1) + 2048 * cb;
+    return join_tr(lds_tr4(slice, boff[t & 1][0] + c), lds_tr4(slice, boff[t & 1][1] + c));
+  }
+};
+
+// Zero the B slots of keys >= keys_valid (the tail step of a sequence): slot j of a lane
+// in half `half` is key 16t + 8(j/4) + 4 half + j%4; the stored dS of keys past the end
+// is not meaningful (the dK/dV kernel computes it from zero K, V rows).
+__device__ __forceinline__ bf16x8 mask_keys(const bf16x8& b, int t, int half, int keys_valid) {
+  u32x4 u = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int k0 = 16 * t + 8 * (m >> 1) + 4 * half + 2 * (m & 1);
+    const uint32_t keep = (k0 < keys_valid ? 0x0000FFFFu : 0u) | (k0 + 1 < keys_valid ? 0xFFFF0000u : 0u);
+    u[m] &= keep;
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_ds_step(const JFA_LDS char* kbuf, const JFA_LDS char* slice, const DsLane<D>& ln,
+                                           f32x16 (&acc)[2][DsCfg<D>::NDB], int half, int keys_valid) {
+  using C = DsCfg<D>;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x8 b0 = ln.ds(slice, t, 0), b1 = ln.ds(slice, t, 1);
+    if (MASK) {
+      b0 = mask_keys(b0, t, half, keys_valid);
+      b1 = mask_keys(b1, t, half, keys_valid);
+    }
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16x8 a = ln.ktr.read(kbuf, 16 * t, db);
+      acc[0][db] = mfma32(a, b0, acc[0][db]);
+      acc[1][db] = mfma32(a, b1, acc[1][db]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, const DsLane<D>& ln,
+                                           int tid) {
+  using C = DsCfg<D>;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t s0 = p.offsets[b];
+  const int L = (int)(p.offsets[b + 1] - s0);
+  const int nq = (L + kBwdRows - 1) / kBwdRows, nj = (L + kBwdKeys - 1) / kBwdKeys;
+  const int it = blk * (C::BM / kBwdRows) + wave;  // this wave's stored block column
+  const bool live = it < nq;                       // wave-uniform: rows past the end only
+  const int nkb = (L + C::BK - 1) / C::BK;
+  const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  // block (j, it) of this (b, h) is at ds_col + j * nq blocks
+  const char* ds_col = p.ds + (p.ds_base[b] + (int64_t)h * nj * nq + it) * kDsBlockBytes;
+
+  auto issue = [&](int kb) {
+    JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
+    ln.copy.issue_rows(kp + (int64_t)kb * C::BK * rs, rsb, min(C::BK, L - kb * C::BK), st, wave, lane);
+    if (live) {
+      const void* src = uniform_ptr(ds_col + ((int64_t)(kb >> 1) * nq * kDsBlockBytes + (kb & 1) * C::SLICE));
+      JFA_LDS char* dst = st + C::KBUF + wave * C::SLICE;
+#pragma unroll
+      for (int c = 0; c < C::SLICE_COPIES; ++c) dma16(src, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
+    }
+  };
+  // Wait until at most the copies of one more step are outstanding (vector-memory
+  // returns are in order, so the older step has landed).
+  auto wait_one_behind = [&]() {
+    if (live) wait_vmem_n<C::Copy::J + C::SLICE_COPIES>();
+    else wait_vmem_n<C::Copy::J>();
+  };
+
+  f32x16 acc[2][C::NDB];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][db][i] = 0.f;
+
+  issue(0);
+  if (nkb > 1) {
+    issue(1);
+    wait_one_behind();
+  } else {
+    wait_vmem();
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 2 < nkb) issue(kb + 2);
+    const JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
+    const int kv = L - kb * C::BK;
+    if (live) {
+      if (kv >= C::BK) dq_ds_step<D, false>(st, st + C::KBUF + wave * C::SLICE, ln, acc, half, C::BK);
+      else dq_ds_step<D, true>(st, st + C::KBUF + wave * C::SLICE, ln, acc, half, kv);
+    }
+    if (kb + 2 < nkb) wait_one_behind();
+    else wait_vmem();
+    __syncthreads();
+  }
+
+  // dQ^T C layout: register i <-> head-dim element 32db + 8(i/4) + 4 half + i%4, lane
+  // l32 <-> query row 64 wave + 32 cb + l32 of the tile.
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int row = blk * C::BM + wave * 64 + cb * 32 + l32;
+    if (row < L) {
+      uint16_t* qp = p.dq + (s0 + row) * rs + (int64_t)h * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          st8(qp + 32 * db + 8 * g4, pack4(acc[cb][db][4 * g4] * p.scale, acc[cb][db][4 * g4 + 1] * p.scale,
+                                          acc[cb][db][4 * g4 + 2] * p.scale, acc[cb][db][4 * g4 + 3] * p.scale));
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    dq_ds_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[DsCfg<D>::SMEM];
+  __shared__ int next_tile;
+  DsLane<D> ln;
+  ln.ktr.init(threadIdx.x & 63);
+  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
+  ln.init(threadIdx.x & 63);
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
+            [&](Tile t) { dq_ds_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
 }  // namespace
@@ -565,10 +893,34 @@ hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
+  const dim3 grid(p.num_programs), block(kBwdWaves * 64);
+  if (head_dim == 64) {
+    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<64, false>), grid, block, 0, s, p);
+  } else {
+    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<128, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_self_prep(const BwdParams& p, int head_dim, hipStream_t s) {
+  const int64_t rows = p.total_tokens * p.num_heads;
+  const int64_t rows_per_block = 256 / (head_dim / 8);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((rows + rows_per_block - 1) / rows_per_block, 4096));
   if (head_dim == 64)
-    hipLaunchKernelGGL(dkdv_kernel<64>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(prep_kernel<64>, dim3(grid), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(dkdv_kernel<128>, dim3(p.num_programs), dim3(kBwdWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(prep_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_self_dq_ds(const BwdParams& p, int head_dim, hipStream_t s) {
+  if (p.dq_programs <= 0) return hipSuccess;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(dq_ds_kernel<64>, dim3(p.dq_programs), dim3(kDsWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL(dq_ds_kernel<128>, dim3(p.dq_programs), dim3(kDsWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -45,6 +45,16 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cas
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// 16-byte streaming (non-temporal) store at base + off, for data that is not read
+// again soon, through a global (address space 1) pointer: a generic pointer whose
+// origin the compiler cannot trace (e.g. one passed through readfirstlane) would become
+// a flat store, which also counts against lgkmcnt, so that every later LDS wait would
+// wait for the store to complete as well.
+#define JFA_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ void st16_global_nt(char* base, uint32_t off, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<JFA_GLOBAL u32x4*>((JFA_GLOBAL char*)base + off));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 // LDS 16-byte read / write (byte offsets into a __shared__ array).

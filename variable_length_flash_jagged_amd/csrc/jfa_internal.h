@@ -24,6 +24,13 @@ constexpr int kDqKeys = 64;       // keys per step of the dQ kernel
 constexpr int kBwdWaves = 4;      // waves per backward workgroup, 32 keys each
 constexpr int kBwdKeys = kBwdWaves * 32;
 constexpr int kBwdRows = 64;
+constexpr int kBwdStages = 3;     // Q / dO ring slots of the dK/dV kernel
+// Stored-dS self-attention backward: the dK/dV kernel writes dS in blocks of kBwdKeys
+// keys x kBwdRows queries (bf16, 16 KB each) and a dQ = scale dS K kernel reads them
+// back, kDsRows query rows per tile (kDsWaves waves of 64 rows).
+constexpr int kDsBlockBytes = kBwdKeys * kBwdRows * 2;
+constexpr int kDsWaves = 4;
+constexpr int kDsRows = kDsWaves * 64;
 constexpr int kBlock = 64;
 constexpr int kBdWaves = 4;
 
@@ -35,6 +42,7 @@ constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound ov
 constexpr int dkdv_wg_per_cu(int head_dim) { return head_dim == 64 ? 2 : 1; }
 constexpr int kBqWgPerCu = 1;     // broadcast-Q fused backward
 constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel
+constexpr int kDsWgPerCu = 1;     // stored-dS dQ kernel (three 48 KB LDS stages)
 constexpr int kBdWgPerCu = 2;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
@@ -78,8 +86,10 @@ struct BwdParams {
   uint16_t* dv;
   float* dq_acc;  // broadcast-Q atomics: [Mq,H,D] fp32; partials: [P,Mq,D] fp32
   uint16_t* dq;   // self: bf16 [T,H,D], written by the dQ kernel
-  uint16_t* row_aug;         // self: [H,T,8] bf16 row terms (-lse/scale, -Di as high/low pairs), written by the dQ kernel
+  uint16_t* row_aug;         // self: [H,T,8] bf16 row terms (-lse log2 e, -Di as high/low pairs), written by the dQ (or row-term) kernel
   const Tile* dq_tiles;      // self: query-row tiles of the dQ kernel
+  char* ds;                  // self, stored-dS path: dS blocks (null on the recompute path)
+  const int64_t* ds_base;    // self, stored-dS path: [B+1] first dS block of each sequence
   const int32_t* dq_seg_ptr;
   int32_t dq_programs;
   int32_t num_seqs, num_heads, num_q, num_programs;
@@ -119,6 +129,10 @@ hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s)
 // dK/dV kernel reads, so it runs first) and dK/dV kernel (key tiles).
 hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s);
+// Stored-dS path: row terms (Di and lse per query row), then the dK/dV kernel with dS
+// stores (p.ds non-null), then dQ from the stored dS.
+hipError_t launch_bwd_self_prep(const BwdParams& p, int head_dim, hipStream_t s);
+hipError_t launch_bwd_self_dq_ds(const BwdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
