@@ -103,7 +103,7 @@ def traffic_bytes(workload, kernel):
     return int(1024 * (k["FETCH_SIZE_kib"] * t["FETCH_SIZE_scale"] + k["WRITE_SIZE_kib"] * t["WRITE_SIZE_scale"]))
 
 
-def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
+def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False):
     """Time the fp64 oracle on the first sequences of the same batch (bounded sample)."""
     import numpy as np
     import oracle
@@ -120,10 +120,13 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
         q, k, v, do, off = p_cpu_fn(b, e)
         t0 = time.perf_counter()
         oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
-        oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
+        if not fwd_only:
+            oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
         spent += time.perf_counter() - t0
         sub = lengths[b:e]
-        flops += M.fwd_flops(sub, mode, num_heads, head_dim, num_q) + M.bwd_flops(sub, mode, num_heads, head_dim, num_q)
+        flops += M.fwd_flops(sub, mode, num_heads, head_dim, num_q)
+        if not fwd_only:
+            flops += M.bwd_flops(sub, mode, num_heads, head_dim, num_q)
         done, b = e, e
     return {
         "value": round(flops / spent / 1e12, 6),
@@ -131,7 +134,7 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
-                  f"one fp64 forward + backward each, {spent:.1f} s",
+                  f"one fp64 {'forward' if fwd_only else 'forward + backward'} each, {spent:.1f} s",
     }
 
 
@@ -156,19 +159,21 @@ def main():
     w = W.WORKLOADS[args.workload]
     p = W.make_workload(args.workload, seed=args.seed, device="cuda")
     mode, h, d, mq = p["mode"], p["num_heads"], p["head_dim"], p["num_q"]
+    hkv = p["num_kv_heads"]
+    fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention: forward only
     lengths = p["lengths"]
-    shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq)
+    shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
     opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, stored_ds=args.stored_ds)
     q, k, v, do, off, off_h = p["q"], p["k"], p["v"], p["do"], p["offsets"], p["offsets_host"]
     if mode == W.MODE_BROADCAST_Q:
         o = torch.empty((p["num_seqs"], mq, h, d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((p["num_seqs"], h, mq), dtype=torch.float32, device="cuda")
     else:
-        o = torch.empty_like(k)
+        o = torch.empty_like(q)
         lse = torch.empty((h, p["total_tokens"]), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
-    ws_b = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
+    ws_b = None if fwd_only else B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
     scale = p["scale"]
 
     ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for n in ("f0", "f1", "b1")}
@@ -179,7 +184,8 @@ def main():
         B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
         if i is not None:
             ev["f1"][i].record()
-        B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
+        if not fwd_only:
+            B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
         if i is not None:
             ev["b1"][i].record()
 
@@ -213,9 +219,9 @@ def main():
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
-    fb = M.bwd_flops(lengths, mode, h, d, mq)
-    bytes_f = M.fwd_bytes(lengths, mode, h, d, mq)
-    bytes_b = M.bwd_bytes(lengths, mode, h, d, mq)
+    fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
+    bytes_f = M.fwd_bytes(lengths, mode, h, d, mq, hkv)
+    bytes_b = 0 if fwd_only else M.bwd_bytes(lengths, mode, h, d, mq)
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     # Per attention kernel: average launch time and the algorithmic work of one launch.
     work = {"fwd": (ff, bytes_f)}
@@ -229,7 +235,7 @@ def main():
         work["bwd_prep"] = (2 * t * h * d, 4 * t * h * d + 20 * t * h)
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h + 2 * h * pairs)
         work["bwd_dq"] = (2 * h * d * pairs, 4 * t * h * d + 2 * h * pairs)
-    elif mode == W.MODE_SELF:
+    elif mode == W.MODE_SELF and not fwd_only:
         # Recompute backward: a dQ kernel (S, dP, dQ: 3 of the 5 products plus the 2 it
         # recomputes; Q, K, V, O, dO in, dQ out, lse in and the 16-byte row term out per
         # row and head) and a dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, dK, dV out,
@@ -238,7 +244,7 @@ def main():
         t = int(p["total_tokens"])
         work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 20 * t * h)
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
-    else:
+    elif not fwd_only:
         work["bwd"] = (fb, bytes_b)
     kernels = {}
     for name, (fl, by) in work.items():
@@ -283,7 +289,8 @@ def main():
         "config": {
             "workload": w["name"],
             "mode": ["self", "broadcast_q", "block_diag"][mode],
-            "num_seqs": int(p["num_seqs"]), "num_heads": h, "head_dim": d, "num_q": mq,
+            "num_seqs": int(p["num_seqs"]), "num_heads": h, "num_kv_heads": hkv, "head_dim": d, "num_q": mq,
+            "passes": "fwd" if fwd_only else "fwd+bwd",
             "total_tokens": int(p["total_tokens"]), "max_len": int(max(lengths)),
             "sched": ["static", "dynamic"][args.sched], "dq_path": args.dq_path, "seed": args.seed,
             "self_bwd": ("stored_ds" if stored_ds else "recompute") if mode == W.MODE_SELF else None,
@@ -293,9 +300,10 @@ def main():
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
                 "pct_of_peak": round(100 * ff / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                 "flops": ff, "bytes": bytes_f},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 1),
-                "pct_of_peak": round(100 * fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                "flops": fb, "bytes": bytes_b},
+        "bwd": None if fwd_only else {
+            "ms": round(bwd_ms, 4), "tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 1),
+            "pct_of_peak": round(100 * fb / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "flops": fb, "bytes": bytes_b},
         "kernels": kernels,
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
@@ -310,9 +318,10 @@ def main():
             if mode == W.MODE_BROADCAST_Q:
                 return (q.float().cpu().numpy().astype(np.float64), f(k), f(v),
                         do[b0:b1].float().cpu().numpy().astype(np.float64), sub_off)
-            return f(q), f(k), f(v), f(do), sub_off
+            return f(q), f(k), f(v), (None if do is None else f(do)), sub_off
 
-        out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds,
+                                           fwd_only)
     print(json.dumps(out), flush=True)
 
 

@@ -29,9 +29,10 @@
  *        SELF            [T,H,D]    [T,H,D]    [T,H,D]       [H,T]       [T,H,D]
  *        BROADCAST_Q     [Mq,H,D]   [T,H,D]    [B,Mq,H,D]    [B,H,Mq]    [Mq,H,D]
  *        BLOCK_DIAG      [T,H,D]    [T,H,D]    [T,H,D]       [H,T]       [T,H,D]
- *    dk, dv always have the shape of k, v.  lse is the natural-log log-sum-exp of the
- *    scaled scores of each query row; a broadcast-Q sequence of length 0 gets
- *    o = 0 and lse = -inf and contributes no gradient.
+ *    k, v carry Hkv = shape->num_kv_heads heads where the table says H (forward only,
+ *    see jfa_shape).  dk, dv always have the shape of k, v.  lse is the natural-log
+ *    log-sum-exp of the scaled scores of each query row; a broadcast-Q sequence of
+ *    length 0 gets o = 0 and lse = -inf and contributes no gradient.
  *  - offsets_dev / offsets_host: int32 [B+1], offsets[0] = 0, non-decreasing,
  *    offsets[B] = shape->total_tokens.  offsets_host may be NULL: the library then
  *    copies the device offsets to the host and synchronises the stream (slow path).
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 110 /* 1.1.0 */
+#define JFA_VERSION 120 /* 1.2.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -69,7 +70,8 @@ enum jfa_pass { JFA_PASS_FWD = 0, JFA_PASS_BWD = 1 };
 enum jfa_status {
   JFA_OK = 0,
   JFA_ERR_NULL_POINTER = -1,    /* a required pointer argument is NULL */
-  JFA_ERR_BAD_SHAPE = -2,       /* B < 0, H < 1, total_tokens < 0, Mq < 1 in broadcast-Q ... */
+  JFA_ERR_BAD_SHAPE = -2,       /* B < 0, H < 1, total_tokens < 0, Mq < 1 in broadcast-Q,
+                                   H % Hkv != 0, Hkv != H in jfa_bwd ... */
   JFA_ERR_BAD_HEAD_DIM = -3,    /* head_dim not in {64, 128} */
   JFA_ERR_BAD_MODE = -4,        /* mode not a jfa_mode, or pass not a jfa_pass */
   JFA_ERR_BAD_OFFSETS = -5,     /* offsets[0] != 0, decreasing, or offsets[B] != T */
@@ -84,10 +86,18 @@ enum jfa_status {
 /* Problem sizes. */
 typedef struct jfa_shape {
   int32_t num_seqs;     /* B >= 0 */
-  int32_t num_heads;    /* H >= 1 (query and key/value heads are the same) */
+  int32_t num_heads;    /* H >= 1 query heads (and output heads) */
   int32_t head_dim;     /* D in {64, 128} */
   int32_t num_q;        /* Mq >= 1, broadcast-Q only (ignored otherwise) */
   int64_t total_tokens; /* T = offsets[B] */
+  int32_t num_kv_heads; /* Hkv: key/value heads; 0 means H.  Grouped-query attention
+                           when Hkv < H: H % Hkv == 0 and query head h reads key/value
+                           head h / (H / Hkv) ("Jagged Flash Attention on TLX"
+                           (aixai.ru), list of supported features: GQA in the forward,
+                           the backward only with one query group per key/value head).
+                           k, v (and dk, dv) then have Hkv heads; jfa_bwd requires
+                           Hkv == H. */
+  int32_t reserved;     /* must be 0 */
 } jfa_shape;
 
 /* Tuning options; pass NULL for the defaults (all zero). */

@@ -21,7 +21,12 @@ lengths change the problem"; bittide page, section 1):
 * MODE_BLOCK_DIAG (2): each sequence is cut into fixed 64-token groups that attend
   only within themselves; shapes as in MODE_SELF.
 
-Readings where the pages are silent (listed in the design doc too):
+Grouped-query attention (aixai.ru page, list of supported features: GQA in the
+forward, the backward only with one query group): k and v may carry Hkv heads with
+H % Hkv == 0; query head h then attends with key/value head h // (H // Hkv).  The
+forward takes this form; the backward requires Hkv == H.
+
+Readings where the pages are silent:
 
 * lse is in natural-log units of the scaled scores, fp32 on the device, laid out
   [H, T] for MODE_SELF / MODE_BLOCK_DIAG and [B, H, Mq] for MODE_BROADCAST_Q.
@@ -96,7 +101,11 @@ def attention_forward(q, k, v, offsets, mode=MODE_SELF, scale=None, block=64):
     Returns (o, lse) in the library's layouts: MODE_SELF / MODE_BLOCK_DIAG:
     o [T, H, D], lse [H, T]; MODE_BROADCAST_Q: o [B, Mq, H, D], lse [B, H, Mq]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    t, h, d = k.shape
+    t, hkv, d = k.shape
+    h = q.shape[1]
+    if v.shape != k.shape or q.shape[2] != d or h % hkv:
+        raise ValueError("q [., H, D], k and v [T, Hkv, D] with H a multiple of Hkv")
+    group = h // hkv  # query heads per key/value head
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     if mode == MODE_BROADCAST_Q:
@@ -107,12 +116,13 @@ def attention_forward(q, k, v, offsets, mode=MODE_SELF, scale=None, block=64):
         for b in range(nb):
             s, e = off[b], off[b + 1]
             for hh in range(h):
-                ob, lb, _ = sequence_forward(q[:, hh], k[s:e, hh], v[s:e, hh], scale)
+                hk = hh // group
+                ob, lb, _ = sequence_forward(q[:, hh], k[s:e, hk], v[s:e, hk], scale)
                 o[b, :, hh] = ob
                 lse[b, hh] = lb
         return o, lse
-    if q.shape != k.shape:
-        raise ValueError("self / block-diagonal attention needs q, k, v of one shape")
+    if q.shape[0] != t:
+        raise ValueError("self / block-diagonal attention needs q and k of one length")
     validate_offsets(offsets, t)
     seg = _segments(offsets, mode, block)
     o = np.zeros((t, h, d))
@@ -122,7 +132,8 @@ def attention_forward(q, k, v, offsets, mode=MODE_SELF, scale=None, block=64):
         if e == s:
             continue
         for hh in range(h):
-            ob, lb, _ = sequence_forward(q[s:e, hh], k[s:e, hh], v[s:e, hh], scale)
+            hk = hh // group
+            ob, lb, _ = sequence_forward(q[s:e, hh], k[s:e, hk], v[s:e, hk], scale)
             o[s:e, hh] = ob
             lse[hh, s:e] = lb
     return o, lse
@@ -134,6 +145,8 @@ def attention_backward(q, k, v, do, offsets, mode=MODE_SELF, scale=None, block=6
     [B, Mq, H, D]."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     t, h, d = k.shape
+    if q.shape[1] != h:
+        raise ValueError("the backward needs one query head per key/value head")
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     dq = np.zeros_like(q)

@@ -17,7 +17,7 @@ What the pages fix:
   program gets a balanced contiguous range computed in closed form with divmod
   (bittide page, section 5).
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave the rule open:
 
 * Tiles are tuples (b, h, blk).  A forward tile is ``rows`` query rows of one (b, h);
   a self-attention backward tile is ``rows`` key rows of one (b, h).

@@ -83,10 +83,11 @@ def check_bwd(grads, refs, label=""):
 
 
 def run_case(lengths, num_heads, head_dim, mode=W.MODE_SELF, num_q=0, seed=0, opts=None, bwd=True,
-             host_offsets=True, label=""):
+             host_offsets=True, label="", num_kv_heads=None):
     print(f"[case] {label} lengths={list(lengths)[:12]}{'...' if len(lengths) > 12 else ''} H={num_heads} "
-          f"D={head_dim} mode={mode} Mq={num_q} seed={seed}", flush=True)
-    p = W.make_problem(lengths, num_heads, head_dim, mode, num_q, seed, device="cpu", with_grad=bwd)
+          f"Hkv={num_kv_heads or num_heads} D={head_dim} mode={mode} Mq={num_q} seed={seed}", flush=True)
+    p = W.make_problem(lengths, num_heads, head_dim, mode, num_q, seed, device="cpu", with_grad=bwd,
+                       num_kv_heads=num_kv_heads)
     g = to_gpu(p)
     o, lse = gpu_fwd(g, opts, host_offsets)
     torch.cuda.synchronize()

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 110
+    assert lib.jfa_version() == 120
 
 
 def test_error_strings():
@@ -51,6 +51,34 @@ def test_workspace_size_rejects_bad_shapes(kw, mode, code):
     with pytest.raises(B.JfaError) as e:
         B.workspace_size(B.make_shape(**args), mode, 0)
     assert e.value.code == code
+
+
+@pytest.mark.parametrize("hkv,code", [(0, 0), (1, 0), (2, 0), (4, 0), (3, -2), (5, -2), (-1, -2)])
+def test_kv_heads_must_divide_query_heads(hkv, code):
+    shape = B.make_shape(2, 4, 64, 10, num_kv_heads=hkv)
+    if code == 0:
+        assert B.workspace_size(shape, 0, 0) > 0
+    else:
+        with pytest.raises(B.JfaError) as e:
+            B.workspace_size(shape, 0, 0)
+        assert e.value.code == code
+    bad = B.make_shape(2, 4, 64, 10)
+    bad.reserved = 1
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(bad, 0, 0)
+    assert e.value.code == -2
+
+
+def test_backward_refuses_grouped_query_heads_before_device_work():
+    lib = B.lib()
+    shape = B.make_shape(1, 4, 64, 4, num_kv_heads=2)
+    off = np.array([0, 4], dtype=np.int32)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the check fails first
+    lse = ctypes.c_void_p(1 << 20)
+    rc = lib.jfa_bwd(ctypes.byref(shape), 0, 0.125, fake, fake, fake, fake, fake, lse, fake, off.ctypes.data,
+                     fake, fake, fake, fake, 1 << 30, None, None)
+    assert rc == -2
+    assert b"num_kv_heads" in lib.jfa_last_error_detail()
 
 
 def test_bad_options_and_pass():

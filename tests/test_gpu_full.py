@@ -30,36 +30,46 @@ def _sample_sequences(lengths, k, seed):
 
 
 def _shape(p):
-    return B.make_shape(p["num_seqs"], p["num_heads"], p["head_dim"], p["total_tokens"], p["num_q"])
+    hkv = p["num_kv_heads"]
+    return B.make_shape(p["num_seqs"], p["num_heads"], p["head_dim"], p["total_tokens"], p["num_q"],
+                        hkv if hkv != p["num_heads"] else 0)
 
 
 def _run(workload, opts=None, bench=False, stored_ds=False):
     p = W.make_workload(workload, seed=0, device="cuda")
     if bench:
         opts = B.bench_opts(p["mode"], _shape(p), p["offsets_host"], stored_ds=stored_ds)
+    if p["do"] is None:
+        print("[case] forward only (grouped-query attention)", flush=True)
     print(f"[case] full-size workload {workload} opts=({opts.sched if opts else 0}, "
           f"{opts.dq_path if opts else 0}, {opts.num_programs if opts else 0}, "
           f"{opts.ds_budget_mib if opts else 0})", flush=True)
     o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts)
-    grads = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"], p["scale"],
-                  opts)
+    grads = None
+    if p["do"] is not None:
+        grads = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"],
+                      p["scale"], opts)
     torch.cuda.synchronize()
     return p, o, lse, grads
 
 
 @pytest.mark.parametrize("workload,samples,stored_ds", [(1, 4, False), (3, 6, False), (4, 1, False), (5, 6, False),
-                                                       (3, 4, True)])
+                                                       (3, 4, True), (6, 4, False)])
 def test_full_size_sampled_sequences(workload, samples, stored_ds):
-    p, o, lse, (dq, dk, dv) = _run(workload, bench=True, stored_ds=stored_ds)
+    p, o, lse, grads = _run(workload, bench=True, stored_ds=stored_ds)
     off = p["offsets_host"].astype(np.int64)
     mode = p["mode"]
     for b in _sample_sequences(p["lengths"], samples, workload):
         s, e = int(off[b]), int(off[b + 1])
         sub = lambda t: G.f64(t[s:e])
-        q, k, v, do = sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"])
+        q, k, v = sub(p["q"]), sub(p["k"]), sub(p["v"])
+        do = sub(p["do"]) if grads is not None else None
         sub_off = [0, e - s]
         o_ref, lse_ref = oracle.attention_forward(q, k, v, sub_off, mode, p["scale"])
         G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"workload {workload} seq {b} (L={e - s})")
+        if grads is None:
+            continue
+        dq, dk, dv = grads
         refs = oracle.attention_backward(q, k, v, do, sub_off, mode, p["scale"])
         G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload {workload} seq {b} (L={e - s})")
 

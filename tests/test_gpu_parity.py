@@ -97,6 +97,31 @@ def test_self_stored_ds_and_recompute_paths_on_one_forward():
     print(f"rel-L2 vs oracle: recompute {ea}, stored dS {eb}", flush=True)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("num_kv_heads", [1, 2])
+def test_grouped_query_forward(head_dim, num_kv_heads):
+    G.run_case(RAGGED + [511], 4, head_dim, bwd=False, seed=31, num_kv_heads=num_kv_heads,
+               label=f"gqa self D{head_dim} Hkv{num_kv_heads}")
+
+
+def test_grouped_query_forward_broadcast_q_and_block_diag():
+    G.run_case([1, 0, 64, 129, 300, 7], 4, 128, W.MODE_BROADCAST_Q, 100, bwd=False, seed=32, num_kv_heads=2,
+               label="gqa broadcast-q")
+    G.run_case([64, 130, 5, 0, 256, 1, 63], 4, 64, W.MODE_BLOCK_DIAG, bwd=False, seed=33, num_kv_heads=1,
+               label="gqa block-diag")
+    G.run_case(RAGGED, 6, 128, bwd=False, seed=34, num_kv_heads=3, opts=B.make_opts(sched=1, num_programs=5),
+               label="gqa dynamic schedule")
+
+
+def test_grouped_query_backward_is_refused():
+    p = W.make_problem([5, 9], 4, 64, seed=35, device="cpu", num_kv_heads=2)
+    g = G.to_gpu(p)
+    o, lse = G.gpu_fwd(g)
+    with pytest.raises(B.JfaError) as e:
+        G.gpu_bwd(g, o, lse)
+    assert e.value.code == -2
+
+
 def test_self_device_offsets_slow_path():
     G.run_case([17, 130, 64], 1, 64, host_offsets=False, seed=6, label="self slow path")
 

@@ -63,9 +63,10 @@ def _padded_sdpa(q, k, v, offsets, scale, block=None, requires_grad=False):
     nb = len(off) - 1
     lmax = max(1, max(off[b + 1] - off[b] for b in range(nb)))
     h, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
     qp = torch.zeros(nb, h, lmax, d, dtype=torch.float64)
-    kp = torch.zeros_like(qp)
-    vp = torch.zeros_like(qp)
+    kp = torch.zeros(nb, hkv, lmax, d, dtype=torch.float64)
+    vp = torch.zeros_like(kp)
     mask = torch.zeros(nb, 1, lmax, lmax, dtype=torch.bool)
     for b in range(nb):
         s, e = off[b], off[b + 1]
@@ -83,7 +84,8 @@ def _padded_sdpa(q, k, v, offsets, scale, block=None, requires_grad=False):
         qp.requires_grad_(True)
         kp.requires_grad_(True)
         vp.requires_grad_(True)
-    o = torch.nn.functional.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, scale=scale)
+    o = torch.nn.functional.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, scale=scale,
+                                                         enable_gqa=hkv != h)
     return o, (qp, kp, vp), off
 
 
@@ -94,13 +96,14 @@ def _check_forward(fwd, q, k, v, offsets, scale, mode=A.MODE_SELF, block=64):
         s, e = off[b], off[b + 1]
         ref = ot[b, :, : e - s].permute(1, 0, 2).numpy()
         np.testing.assert_allclose(o[s:e], ref, rtol=1e-11, atol=1e-12)
+        group = q.shape[1] // k.shape[1]
         for hh in range(q.shape[1]):
             for i in range(e - s):
                 lo, hi = (s, e)
                 if mode == A.MODE_BLOCK_DIAG:
                     lo = s + (i // block) * block
                     hi = min(lo + block, e)
-                scores = scale * (k[lo:hi, hh] @ q[s + i, hh])
+                scores = scale * (k[lo:hi, hh // group] @ q[s + i, hh])
                 np.testing.assert_allclose(lse[hh, s + i], logsumexp(scores), rtol=1e-12, atol=1e-12)
 
 
@@ -133,6 +136,54 @@ def _jagged_inputs(lengths, h, d):
 def test_forward_equals_padded_masked_brute_force():
     q, k, v, _, off = _jagged_inputs(**JAGGED)
     _check_forward(A.attention_forward, q, k, v, off, 0.37)
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+@pytest.mark.parametrize("mode", [A.MODE_SELF, A.MODE_BLOCK_DIAG])
+def test_grouped_query_forward_equals_library_gqa_attention(hkv, mode):
+    # torch's own grouped-query attention (enable_gqa) on the padded, masked batch
+    lengths = [5, 1, 7, 0, 3] if mode == A.MODE_SELF else [70, 3, 129]
+    off = oracle.offsets_from_lengths(lengths)
+    t = int(off[-1])
+    q, k, v = _rand(t, 4, 8), _rand(t, hkv, 8), _rand(t, hkv, 8)
+    _check_forward(A.attention_forward, q, k, v, off, 0.41, mode=mode)
+
+
+def test_grouped_query_heads_see_only_their_key_value_head():
+    off = oracle.offsets_from_lengths([6, 4])
+    q, k, v = _rand(10, 6, 8), _rand(10, 3, 8), _rand(10, 3, 8)
+    o, lse = A.attention_forward(q, k, v, off, A.MODE_SELF, 0.3)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1] += 1.0
+    v2[:, 1] -= 2.0
+    o2, lse2 = A.attention_forward(q, k2, v2, off, A.MODE_SELF, 0.3)
+    changed = [not np.allclose(o[:, hh], o2[:, hh]) for hh in range(6)]
+    assert changed == [False, False, True, True, False, False]  # heads 2, 3 read key/value head 1
+    # identical queries in one group give identical rows within the group
+    q3 = q.copy()
+    q3[:, 1] = q3[:, 0]
+    o3, _ = A.attention_forward(q3, k, v, off, A.MODE_SELF, 0.3)
+    np.testing.assert_array_equal(o3[:, 0], o3[:, 1])
+
+
+def test_grouped_query_broadcast_q_equals_per_head_cross_attention():
+    off = oracle.offsets_from_lengths([4, 0, 6])
+    q, k, v = _rand(5, 4, 8), _rand(10, 2, 8), _rand(10, 2, 8)
+    o, lse = A.attention_forward(q, k, v, off, A.MODE_BROADCAST_Q, 0.5)
+    for b, (s, e) in enumerate([(0, 4), (4, 4), (4, 10)]):
+        for hh in range(4):
+            if e == s:
+                assert np.all(o[b, :, hh] == 0) and np.all(np.isneginf(lse[b, hh]))
+                continue
+            scores = 0.5 * q[:, hh] @ k[s:e, hh // 2].T
+            p = np.exp(scores - logsumexp(scores, axis=1, keepdims=True))
+            np.testing.assert_allclose(o[b, :, hh], p @ v[s:e, hh // 2], rtol=1e-12, atol=1e-13)
+
+
+def test_grouped_query_backward_is_refused():
+    off = oracle.offsets_from_lengths([3])
+    with pytest.raises(ValueError):
+        A.attention_backward(_rand(3, 4, 8), _rand(3, 2, 8), _rand(3, 2, 8), _rand(3, 4, 8), off)
 
 
 def test_backward_equals_torch_autograd():

@@ -32,7 +32,8 @@ class JfaError(RuntimeError):
 
 class Shape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("num_q", ctypes.c_int32), ("total_tokens", ctypes.c_int64)]
+                ("num_q", ctypes.c_int32), ("total_tokens", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class Opts(ctypes.Structure):
@@ -83,8 +84,8 @@ def _check(rc, func):
         raise JfaError(rc, func, detail)
 
 
-def make_shape(num_seqs, num_heads, head_dim, total_tokens, num_q=0):
-    return Shape(int(num_seqs), int(num_heads), int(head_dim), int(num_q), int(total_tokens))
+def make_shape(num_seqs, num_heads, head_dim, total_tokens, num_q=0, num_kv_heads=0):
+    return Shape(int(num_seqs), int(num_heads), int(head_dim), int(num_q), int(total_tokens), int(num_kv_heads), 0)
 
 
 def make_opts(sched=0, dq_path=0, num_programs=0, ds_budget_mib=0):
@@ -172,13 +173,16 @@ def _check_tensor(name, t, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _sizes(q, k, offsets, mode, num_q):
-    total, num_heads, head_dim = k.shape
+def _sizes(q, k, v, offsets, mode):
+    """(B, H, D, T, Mq, Hkv): query heads from q, key/value heads from k."""
+    total, kv_heads, head_dim = k.shape
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k has {tuple(k.shape)}")
+    if q.dim() != 3 or q.shape[2] != head_dim:
+        raise ValueError(f"q has shape {tuple(q.shape)}; expected [rows, H, {head_dim}]")
     nb = offsets.numel() - 1
     mq = q.shape[0] if mode == MODE_BROADCAST_Q else 0
-    if mode == MODE_BROADCAST_Q and num_q and num_q != mq:
-        raise ValueError("num_q differs from q.shape[0]")
-    return nb, num_heads, head_dim, total, mq
+    return nb, q.shape[1], head_dim, total, mq, kv_heads
 
 
 def alloc_workspace(shape, mode, pass_, opts, device):
@@ -191,12 +195,12 @@ def fwd(q, k, v, offsets, offsets_host=None, mode=MODE_SELF, scale=None, opts=No
         workspace=None, stream=None):
     """Forward.  Returns (o, lse) with the layouts of include/jfa.h."""
     import torch
-    nb, h, d, t, mq = _sizes(q, k, offsets, mode, 0)
+    nb, h, d, t, mq, hkv = _sizes(q, k, v, offsets, mode)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     for name, x in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, x, torch.bfloat16)
     _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
-    shape = make_shape(nb, h, d, t, mq)
+    shape = make_shape(nb, h, d, t, mq, hkv if hkv != h else 0)
     if mode == MODE_BROADCAST_Q:
         o_shape, lse_shape = (nb, mq, h, d), (nb, h, mq)
     else:
@@ -222,13 +226,13 @@ def bwd(q, k, v, o, do, lse, offsets, offsets_host=None, mode=MODE_SELF, scale=N
         dk=None, dv=None, workspace=None, stream=None):
     """Backward.  Returns (dq, dk, dv) with the shapes of (q, k, v)."""
     import torch
-    nb, h, d, t, mq = _sizes(q, k, offsets, mode, 0)
+    nb, h, d, t, mq, hkv = _sizes(q, k, v, offsets, mode)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     for name, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_tensor(name, x, torch.bfloat16)
     _check_tensor("lse", lse, torch.float32)
     _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
-    shape = make_shape(nb, h, d, t, mq)
+    shape = make_shape(nb, h, d, t, mq, hkv if hkv != h else 0)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

@@ -43,6 +43,7 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int kv_heads(const jfa_shape* s) { return s->num_kv_heads > 0 ? s->num_kv_heads : s->num_heads; }
 
 // Compute units of the current device (256 if no device is visible: host-only use).
 int device_cus() {
@@ -93,6 +94,9 @@ int check_shape(const jfa_shape* s, int mode) {
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(JFA_ERR_BAD_HEAD_DIM, "head_dim %d not in {64, 128}", s->head_dim);
   if (s->total_tokens < 0) return fail(JFA_ERR_BAD_SHAPE, "total_tokens < 0");
+  if (s->reserved != 0) return fail(JFA_ERR_BAD_SHAPE, "shape.reserved must be 0");
+  if (s->num_kv_heads < 0 || s->num_kv_heads > s->num_heads || (s->num_kv_heads > 0 && s->num_heads % s->num_kv_heads))
+    return fail(JFA_ERR_BAD_SHAPE, "num_kv_heads %d must be 0 or divide num_heads %d", s->num_kv_heads, s->num_heads);
   if (mode == JFA_MODE_BROADCAST_Q && s->num_q < 1) return fail(JFA_ERR_BAD_SHAPE, "num_q < 1 in broadcast-Q mode");
   // 32-bit limits: block indices < 2^24 in the tile encoding, tile counts < 2^31.
   if (s->total_tokens >= (int64_t(1) << 30)) return fail(JFA_ERR_TOO_LARGE, "total_tokens >= 2^30");
@@ -480,6 +484,7 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.blk_prefix = (const int32_t*)(ws + L.prefix);
     p.num_seqs = shape->num_seqs;
     p.num_heads = H;
+    p.num_kv_heads = kv_heads(shape);
     p.total_tokens = shape->total_tokens;
     p.num_tiles = ntiles;
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
@@ -508,6 +513,7 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   p.counters = (int32_t*)(ws + L.counters);
   p.num_seqs = shape->num_seqs;
   p.num_heads = H;
+  p.num_kv_heads = kv_heads(shape);
   p.num_q = shape->num_q;
   p.num_programs = sc.programs;
   p.total_tokens = shape->total_tokens;
@@ -534,6 +540,9 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     return fail(JFA_ERR_MISALIGNED, "bf16 tensors must be 16-byte aligned and lse 4-byte aligned");
   if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  if (kv_heads(shape) != shape->num_heads)
+    return fail(JFA_ERR_BAD_SHAPE, "the backward needs one query head per key/value head (num_kv_heads %d != num_heads %d)",
+                shape->num_kv_heads, shape->num_heads);
   Layout L;
   layout_for(shape, mode, JFA_PASS_BWD, op, L);
   if (workspace_bytes < L.total)
@@ -564,6 +573,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.blk_prefix = (const int32_t*)(ws + L.prefix);
     p.num_seqs = shape->num_seqs;
     p.num_heads = H;
+    p.num_kv_heads = H;
     p.total_tokens = T;
     p.num_tiles = ntiles;
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));

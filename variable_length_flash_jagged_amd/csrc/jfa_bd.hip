@@ -69,18 +69,20 @@ template <int D>
 __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* vt, int lane) {
   using C = BdCfg<D>;
   const int l32 = lane & 31, half = lane >> 5;
-  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t rs = (int64_t)p.num_heads * D;                              // q, o row stride
   const int64_t base = t.t0 * rs + (int64_t)t.h * D;
+  const int64_t rkv = (int64_t)p.num_kv_heads * D;                          // k, v row stride
+  const int64_t kvbase = t.t0 * rkv + (int64_t)(t.h / (p.num_heads / p.num_kv_heads)) * D;
   const int n = t.n;
   const float c = p.scale_log2;
-  dma_tile<C::RB, kBlock, 1>(p.v + base, rs, n, vt, 0, lane);
+  dma_tile<C::RB, kBlock, 1>(p.v + kvbase, rkv, n, vt, 0, lane);
 
   bf16x8 qf[2][C::NKS], kf[2][C::NKS];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int row = bb * 32 + l32;
     const uint16_t* qp = p.q + base + row * rs + 8 * half;
-    const uint16_t* kp = p.k + base + row * rs + 8 * half;
+    const uint16_t* kp = p.k + kvbase + row * rkv + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       qf[bb][ks] = as_bf16x8(row < n ? ld16(qp + 16 * ks) : zero16());

@@ -215,8 +215,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const int l32 = lane & 31, half = lane >> 5;
   const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
   const int H = p.num_heads;
-  const int64_t rs = (int64_t)H * D;
-  const uint32_t rsb = (uint32_t)(rs * 2);
+  const int64_t rs = (int64_t)H * D;                   // q, o row stride
+  const int64_t rkv = (int64_t)p.num_kv_heads * D;     // k, v row stride
+  const uint32_t rkvb = (uint32_t)(rkv * 2);
+  const int hkv = h / (H / p.num_kv_heads);            // key/value head of query head h
   const int64_t s0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - s0);
   const int Lq = (MODE == kSelf) ? L : p.num_q;
@@ -239,8 +241,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
 
   const int n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
   if (n > 0) {
-    const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
-    const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
+    const uint16_t* kp = p.k + s0 * rkv + (int64_t)hkv * D;
+    const uint16_t* vp = p.v + s0 * rkv + (int64_t)hkv * D;
     auto rows_of = [&](int j) { return min(C::BN, L - j * C::BN); };
     // Stage i into slot i % NS.  Stage 0 has no V tile and stage n no K tile; those
     // halves repeat a neighbouring tile instead, so every stage is the same number of
@@ -248,8 +250,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
     auto issue = [&](int i) {
       JFA_LDS char* slot = smem + (i % C::NS) * C::STAGE;
       const int kt = min(i, n - 1), vt = max(i - 1, 0);
-      ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rs, rsb, rows_of(kt), slot, wave, lane);
-      ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rs, rsb, rows_of(vt), slot + C::TILE, wave, lane);
+      ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rkv, rkvb, rows_of(kt), slot, wave, lane);
+      ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rkv, rkvb, rows_of(vt), slot + C::TILE, wave, lane);
     };
     issue(0);
     wait_vmem();  // Q and stage 0
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
   FwdLane<D> ln;
   ln.krow.init(tid & 63);
   ln.vtr.init(tid & 63);
-  ln.copy.init((uint32_t)(p.num_heads * D * 2), tid >> 6, tid & 63);
+  ln.copy.init((uint32_t)(p.num_kv_heads * D * 2), tid >> 6, tid & 63);  // k, v row stride
   int idx, end;
   if (!p.dynamic) {
     idx = p.seg_ptr[prog];

@@ -67,6 +67,7 @@ struct FwdParams {
   int32_t num_seqs, num_heads, num_q, num_programs;
   int64_t total_tokens;
   int32_t dynamic;
+  int32_t num_kv_heads;  // key/value heads (divides num_heads)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -116,6 +117,7 @@ struct BdParams {
   const int32_t* offsets;      // [B+1]
   const int32_t* blk_prefix;   // [B+1]: blocks before sequence b
   int32_t num_seqs, num_heads, num_programs;
+  int32_t num_kv_heads;  // forward: key/value heads (divides num_heads); backward: num_heads
   int64_t total_tokens;
   int64_t num_tiles;  // blocks * heads
   float scale;

@@ -40,13 +40,16 @@ def bwd_flops(lengths, mode, num_heads, head_dim, num_q=0):
     return 10 * num_heads * head_dim * valid_pairs(lengths, mode, num_q)
 
 
-def fwd_bytes(lengths, mode, num_heads, head_dim, num_q=0):
+def fwd_bytes(lengths, mode, num_heads, head_dim, num_q=0, num_kv_heads=None):
+    """Q (or the shared Q) and K, V in, O and lse out; K, V carry num_kv_heads heads
+    (grouped-query attention), the rest num_heads."""
     t = int(np.asarray(lengths, dtype=np.int64).sum())
     h, d = num_heads, head_dim
+    hkv = h if num_kv_heads is None else num_kv_heads
     if mode == MODE_BROADCAST_Q:
         b = len(lengths)
-        return 2 * num_q * h * d + 4 * t * h * d + 2 * b * num_q * h * d + 4 * b * h * num_q
-    return 8 * t * h * d + 4 * t * h
+        return 2 * num_q * h * d + 4 * t * hkv * d + 2 * b * num_q * h * d + 4 * b * h * num_q
+    return 4 * t * h * d + 4 * t * hkv * d + 4 * t * h
 
 
 def bwd_bytes(lengths, mode, num_heads, head_dim, num_q=0):

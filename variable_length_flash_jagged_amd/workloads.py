@@ -17,6 +17,8 @@ generators stand in for them):
 4. ``dense_equivalent``: self-attention, B=16 sequences of 4096, H=8, D=128.
 5. ``block_diag``: 64-token block-diagonal attention, B=1152, L = 64 * n with
    n ~ U{1..63}, H=4, D=64.
+6. ``production_jagged_gqa``: the lengths of workload 3 with H=4 query heads sharing
+   one key/value head (grouped-query attention, forward only).
 
 Draw order: lengths (numpy ``default_rng(seed)``), then q, k, v, dO from one
 ``torch.Generator`` seeded with ``seed`` on the target device, each drawn in fp32 and
@@ -37,6 +39,8 @@ WORKLOADS = {
     3: dict(name="production_jagged", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0),
     4: dict(name="dense_equivalent", mode=MODE_SELF, num_heads=8, head_dim=128, num_q=0),
     5: dict(name="block_diag", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0),
+    6: dict(name="production_jagged_gqa", mode=MODE_SELF, num_heads=4, num_kv_heads=1, head_dim=128, num_q=0,
+            fwd_only=True),
 }
 
 
@@ -51,7 +55,7 @@ def workload_lengths(workload, seed=0, num_seqs=None):
         n = 64 if num_seqs is None else num_seqs
         u = rng.uniform(0.0, math.log(4097.0), size=n)
         return np.clip(np.floor(np.exp(u)), 1, 4096).astype(np.int64)
-    if workload == 3:
+    if workload in (3, 6):
         n = 1152 if num_seqs is None else num_seqs
         x = rng.normal(math.log(600.0), 1.0, size=n)
         return np.clip(np.rint(np.exp(x)), 1, 4000).astype(np.int64)
@@ -71,11 +75,12 @@ def pack_offsets(lengths):
 
 
 def make_problem(lengths, num_heads, head_dim, mode=MODE_SELF, num_q=0, seed=0,
-                 device="cpu", with_grad=True):
+                 device="cpu", with_grad=True, num_kv_heads=None):
     """Draw q, k, v (and dO) for the given lengths.
 
     Returns a dict with torch bf16 tensors ``q`` ([T,H,D], or [Mq,H,D] in broadcast-Q
-    mode), ``k``, ``v`` ([T,H,D]), ``do`` (shape of o: [T,H,D] or [B,Mq,H,D]),
+    mode), ``k``, ``v`` ([T,Hkv,D], Hkv = ``num_kv_heads`` or H), ``do`` (shape of o:
+    [T,H,D] or [B,Mq,H,D]),
     ``offsets`` (int32 tensor on ``device``), ``offsets_host`` (int32 numpy),
     ``lengths``, and the problem sizes.  ``scale`` is 1/sqrt(D)."""
     import torch
@@ -95,8 +100,9 @@ def make_problem(lengths, num_heads, head_dim, mode=MODE_SELF, num_q=0, seed=0,
         q = draw(num_q, num_heads, head_dim)
     else:
         q = draw(total, num_heads, head_dim)
-    k = draw(total, num_heads, head_dim)
-    v = draw(total, num_heads, head_dim)
+    hkv = num_heads if num_kv_heads is None else int(num_kv_heads)
+    k = draw(total, hkv, head_dim)
+    v = draw(total, hkv, head_dim)
     do = None
     if with_grad:
         if mode == MODE_BROADCAST_Q:
@@ -107,7 +113,7 @@ def make_problem(lengths, num_heads, head_dim, mode=MODE_SELF, num_q=0, seed=0,
         q=q, k=k, v=v, do=do,
         offsets=torch.as_tensor(offsets.astype(np.int32), device=device),
         offsets_host=offsets.astype(np.int32),
-        lengths=lengths, mode=mode, num_heads=num_heads, head_dim=head_dim,
+        lengths=lengths, mode=mode, num_heads=num_heads, num_kv_heads=hkv, head_dim=head_dim,
         num_q=num_q, num_seqs=nb, total_tokens=total, scale=1.0 / math.sqrt(head_dim),
     )
 
@@ -117,7 +123,7 @@ def make_workload(workload, seed=0, device="cpu", num_seqs=None, with_grad=True)
     w = WORKLOADS[workload]
     lengths = workload_lengths(workload, seed, num_seqs)
     p = make_problem(lengths, w["num_heads"], w["head_dim"], w["mode"], w["num_q"], seed,
-                     device, with_grad)
+                     device, with_grad and not w.get("fwd_only", False), w.get("num_kv_heads"))
     p["workload"] = workload
     p["workload_name"] = w["name"]
     return p
