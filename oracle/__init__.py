@@ -23,9 +23,11 @@ Modules:
 * ``attention`` -- softmax attention forward/backward by plain definition, fp64.
 * ``schedule``  -- the tile scheduler rules written out (sorted zigzag, round robin,
   contiguous divmod ranges) as the bit-exact specification of the host scheduler.
+* ``block_sparse`` -- the block-sparse top-k variant (pooled query and key blocks,
+  top-k key blocks per query block, attention over the kept blocks).
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` and
-``tests/test_schedule_spec.py`` (worked example printed on the pages, independent
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_schedule_spec.py`` and ``tests/test_oracle_block_sparse.py`` (worked example printed on the pages, independent
 library routines, closed forms, finite differences, brute force).  Nothing here is
 "parity unpinned".
 """
@@ -36,6 +38,7 @@ from .offsets import (  # noqa: F401
     validate_offsets,
     block_offsets,
 )
+from . import block_sparse  # noqa: F401
 from .attention import (  # noqa: F401
     MODE_SELF,
     MODE_BROADCAST_Q,
