@@ -13,6 +13,7 @@ variable_length_flash_jagged_amd/workloads.py) instead.
 """
 
 import argparse
+import math
 import csv
 import glob
 import hashlib
@@ -103,7 +104,7 @@ def traffic_bytes(workload, kernel):
     return int(1024 * (k["FETCH_SIZE_kib"] * t["FETCH_SIZE_scale"] + k["WRITE_SIZE_kib"] * t["WRITE_SIZE_scale"]))
 
 
-def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False):
+def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False, sparse_ratio=None):
     """Time the fp64 oracle on the first sequences of the same batch (bounded sample)."""
     import numpy as np
     import oracle
@@ -119,6 +120,17 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         e = min(len(lengths), b + chunk)
         q, k, v, do, off = p_cpu_fn(b, e)
         t0 = time.perf_counter()
+        if sparse_ratio is not None:
+            from oracle import block_sparse as S
+            sel = S.select_blocks(q, k, off, sparse_ratio)
+            S.block_sparse_forward(q, k, v, off, sel, 1.0 / np.sqrt(head_dim))
+            spent += time.perf_counter() - t0
+            sub = lengths[b:e]
+            keep = [S.keep_count(n, sparse_ratio) for n in sub]
+            flat = [j for per_b in sel for per_h in per_b for lst in per_h for j in lst]
+            flops += 4 * head_dim * M.block_sparse_pairs(sub, num_heads, keep, flat)  # pairs over heads
+            done, b = e, e
+            continue
         oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
         if not fwd_only:
             oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
@@ -134,7 +146,8 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
-                  f"one fp64 {'forward' if fwd_only else 'forward + backward'} each, {spent:.1f} s",
+                  f"one fp64 {'block-sparse forward' if sparse_ratio else 'forward' if fwd_only else 'forward + backward'}"
+                  f" each, {spent:.1f} s",
     }
 
 
@@ -160,7 +173,8 @@ def main():
     p = W.make_workload(args.workload, seed=args.seed, device="cuda")
     mode, h, d, mq = p["mode"], p["num_heads"], p["head_dim"], p["num_q"]
     hkv = p["num_kv_heads"]
-    fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention: forward only
+    fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention, block-sparse variant: forward only
+    ratio = w.get("sparse_ratio")
     lengths = p["lengths"]
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
     opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, stored_ds=args.stored_ds)
@@ -172,7 +186,11 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty((h, p["total_tokens"]), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
+    ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD_SPARSE if ratio else B.PASS_FWD, opts, "cuda")
+    sel = None
+    if ratio:
+        sel = torch.empty(max(1, B.block_sparse_entries(shape, p["offsets_host"], ratio)), dtype=torch.int32,
+                          device="cuda")
     ws_b = None if fwd_only else B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
     scale = p["scale"]
 
@@ -181,7 +199,10 @@ def main():
     def step(i=None):
         if i is not None:
             ev["f0"][i].record()
-        B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
+        if ratio:
+            B.fwd_block_sparse(q, k, v, off, off_h, ratio, scale, opts, o, lse, sel, ws_f)
+        else:
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
         if i is not None:
             ev["f1"][i].record()
         if not fwd_only:
@@ -215,10 +236,27 @@ def main():
     fwd_ms = sum(ev["f0"][i].elapsed_time(ev["f1"][i]) for i in range(args.steps)) / args.steps
     bwd_ms = sum(ev["f1"][i].elapsed_time(ev["b1"][i]) for i in range(args.steps)) / args.steps
     kt = {name: B.kernel_times(kid) for name, kid in
-          (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ), ("bwd_prep", B.KERNEL_BWD_PREP))}
+          (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ), ("bwd_prep", B.KERNEL_BWD_PREP),
+           ("select", B.KERNEL_SPARSE_SELECT))}
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
+    dense = None
+    if ratio:
+        # attended pairs only; the dense forward of the same batch is timed for context
+        keep = [max(1, math.ceil(float(np.float32(ratio)) * -(-int(n) // 64))) if n else 0 for n in lengths]
+        ff = 4 * d * M.block_sparse_pairs(lengths, h, keep, sel.cpu().numpy())  # pairs summed over heads
+        ws_d = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
+        for _ in range(args.warmup):
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record()
+        for _ in range(args.steps):
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
+        d1.record()
+        torch.cuda.synchronize()
+        dense = d0.elapsed_time(d1) / args.steps
     fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
     bytes_f = M.fwd_bytes(lengths, mode, h, d, mq, hkv)
     bytes_b = 0 if fwd_only else M.bwd_bytes(lengths, mode, h, d, mq)
@@ -246,12 +284,15 @@ def main():
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
     elif not fwd_only:
         work["bwd"] = (fb, bytes_b)
+    if ratio:
+        # stage 1 reads Q and K once (the block means and lists are small)
+        work["select"] = (0, 2 * int(p["total_tokens"]) * (h + hkv) * d)
     kernels = {}
     for name, (fl, by) in work.items():
         n, tot = kt[name]
         if n == 0:
             continue
-        ms = tot / n
+        ms = tot / (args.steps if name == "select" else n)  # stage 1 of the sparse forward: 3 launches a step
         kernels[name] = {"launches_per_step": n // args.steps, "ms": round(ms, 4), "flops": fl, "bytes": by,
                          "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
     hbm_bound = mode == W.MODE_BLOCK_DIAG
@@ -267,7 +308,8 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
                       ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
-                      "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel", "bwd_prep": "prep_kernel"}[dom]
+                      "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel", "bwd_prep": "prep_kernel",
+                      "select": "select_kernel"}[dom]
     if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
         roof["kernel"] = "bd_fwd_kernel"
     roof["kernel_ms"] = kd["ms"]
@@ -307,6 +349,9 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
+        "block_sparse": None if not ratio else {
+            "ratio": ratio, "attended_pairs_fraction": round(ff / M.fwd_flops(lengths, mode, h, d, mq), 4),
+            "dense_fwd_ms": round(dense, 4), "speedup_vs_dense_fwd": round(dense / fwd_ms, 3)},
     }
     if not args.no_cpu_baseline:
         offs = np.asarray(off_h, dtype=np.int64)
@@ -321,7 +366,7 @@ def main():
             return f(q), f(k), f(v), (None if do is None else f(do)), sub_off
 
         out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds,
-                                           fwd_only)
+                                           fwd_only, ratio)
     print(json.dumps(out), flush=True)
 
 

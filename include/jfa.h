@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 120 /* 1.2.0 */
+#define JFA_VERSION 130 /* 1.3.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -65,7 +65,11 @@ enum jfa_mode {
   JFA_MODE_BLOCK_DIAG = 2   /* 64-token groups of each sequence attend within themselves */
 };
 
-enum jfa_pass { JFA_PASS_FWD = 0, JFA_PASS_BWD = 1 };
+enum jfa_pass {
+  JFA_PASS_FWD = 0,
+  JFA_PASS_BWD = 1,
+  JFA_PASS_FWD_SPARSE = 2 /* jfa_fwd_block_sparse (self mode only) */
+};
 
 enum jfa_status {
   JFA_OK = 0,
@@ -154,6 +158,33 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale,
             void* workspace, size_t workspace_bytes,
             const jfa_opts* opts, void* stream);
 
+/* Block-sparse top-k self attention, forward ("Jagged Flash Attention on TLX"
+ * (aixai.ru), closing section on variants: a cheap first stage averages blocks of Q
+ * and K and keeps the most relevant ones for the attention kernel).  Stage 1 pools
+ * every 256-row query block and every 64-key block of each (sequence, head) to the
+ * mean of its rows and keeps, per query block, the k = max(1, ceil(ratio * nkb)) key
+ * blocks (nkb = ceil(L/64); ratio * nkb formed in double from the float ratio) whose
+ * mean has the largest dot product with the query block's mean, ties going to the
+ * lower block index.  Stage 2 is the forward of jfa_fwd restricted to the kept blocks
+ * (an exact softmax over their keys).  ratio in (0, 1]; ratio 1 keeps every block and
+ * gives exactly jfa_fwd's result.  Self mode only; grouped key/value heads allowed.
+ * A sequence may have at most 2048 key blocks (131072 tokens): JFA_ERR_TOO_LARGE
+ * otherwise.
+ *
+ * selection: device int32 array of at least jfa_block_sparse_entries() entries; the
+ * call writes the kept block indices, for sequence b, head h and query block i at
+ * [base_b + (h * nqb_b + i) * k_b, ... + k_b) in ascending order, where nqb_b =
+ * ceil(L_b/256), k_b the count above and base_b the sum of H * nqb * k over earlier
+ * sequences.  workspace: jfa_workspace_size(shape, JFA_MODE_SELF,
+ * JFA_PASS_FWD_SPARSE, opts) bytes.  Other conventions as jfa_fwd. */
+int jfa_block_sparse_entries(const jfa_shape* shape, const int32_t* offsets_host, float ratio, int64_t* entries);
+int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
+                         const void* q, const void* k, const void* v,
+                         const int32_t* offsets_dev, const int32_t* offsets_host,
+                         void* o, float* lse, int32_t* selection, int64_t selection_entries,
+                         void* workspace, size_t workspace_bytes,
+                         const jfa_opts* opts, void* stream);
+
 /* Host-only view of the tile schedule the calls above would run (no device needed).
  * Tiles are (b, h, blk) triples: forward tiles are tile_rows query rows, backward
  * tiles tile_rows key rows, block-diagonal tiles one 64-token block.  Static
@@ -168,14 +199,17 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
 
 /* Attention kernels timed by the measurement hook below. */
 enum jfa_kernel {
-  JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd */
+  JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd (and jfa_fwd_block_sparse) */
   JFA_KERNEL_BWD = 1,    /* the main backward kernel of jfa_bwd: the dK/dV kernel in self
                             mode, the fused kernel in broadcast-Q and block-diagonal modes */
   JFA_KERNEL_BWD_DQ = 2,  /* self mode only: the dQ kernel of jfa_bwd (recompute or stored-dS) */
-  JFA_KERNEL_BWD_PREP = 3 /* self mode, stored-dS path only: the row-term kernel (Di, lse) */
+  JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path only: the row-term kernel (Di, lse) */
+  JFA_KERNEL_SPARSE_SELECT = 4 /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
+                                  select launch (each recorded as one launch) */
 };
 
-/* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd call records a
+/* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd /
+ * jfa_fwd_block_sparse call records a
  * pair of HIP events on its stream immediately around each of its attention kernels
  * (not the schedule upload or the dQ fill / cast / reduce kernels).  jfa_kernel_times
  * waits for the events recorded so far for `kernel` (a jfa_kernel) and returns the

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 120
+    assert lib.jfa_version() == 130
 
 
 def test_error_strings():
@@ -81,13 +81,45 @@ def test_backward_refuses_grouped_query_heads_before_device_work():
     assert b"num_kv_heads" in lib.jfa_last_error_detail()
 
 
+@pytest.mark.parametrize("lengths", [[0], [1], [300, 0, 65], [4000, 600, 64]])
+@pytest.mark.parametrize("ratio", [1.0, 0.5, 0.25, 0.3])
+def test_block_sparse_entries_formula(lengths, ratio):
+    import math
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), 3, 128, int(off[-1]))
+    want = 0
+    for n in lengths:
+        if n:
+            nkb = -(-n // 64)
+            want += 3 * (-(-n // 256)) * max(1, math.ceil(float(np.float32(ratio)) * nkb))
+    assert B.block_sparse_entries(shape, off, ratio) == want
+
+
+def test_block_sparse_argument_errors():
+    off = np.array([0, 300], dtype=np.int32)
+    shape = B.make_shape(1, 2, 64, 300)
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(B.JfaError) as e:
+            B.block_sparse_entries(shape, off, bad)
+        assert e.value.code == -8
+    big = np.array([0, 64 * 2048 + 1], dtype=np.int32)  # 2049 key blocks
+    with pytest.raises(B.JfaError) as e:
+        B.block_sparse_entries(B.make_shape(1, 1, 64, int(big[-1])), big, 0.5)
+    assert e.value.code == -9
+    assert B.block_sparse_entries(B.make_shape(1, 1, 64, 64 * 2048), np.array([0, 64 * 2048], np.int32), 0.5) > 0
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(shape, 2, B.PASS_FWD_SPARSE)  # self mode only
+    assert e.value.code == -4
+    assert B.workspace_size(shape, 0, B.PASS_FWD_SPARSE) > B.workspace_size(shape, 0, B.PASS_FWD)
+
+
 def test_bad_options_and_pass():
     shape = B.make_shape(2, 2, 64, 10)
     with pytest.raises(B.JfaError) as e:
         B.workspace_size(shape, 0, 0, B.make_opts(sched=3))
     assert e.value.code == -8
     with pytest.raises(B.JfaError) as e:
-        B.workspace_size(shape, 0, 2)
+        B.workspace_size(shape, 0, 3)
     assert e.value.code == -4
 
 

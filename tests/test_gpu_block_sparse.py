@@ -1,0 +1,131 @@
+"""GPU parity of the block-sparse top-k forward (jfa_fwd_block_sparse) against the
+fp64 oracle (oracle/block_sparse.py).
+
+The kept key blocks are decided from fp32 block means on the GPU; where two blocks'
+relevance differ by less than fp32 rounding either choice is correct.  So the
+selection is checked for validity against the oracle's fp64 relevance (right count,
+ascending, no duplicates, and no dropped block beats a kept one by more than a bound
+on the fp32 error), and the attention is checked element by element against the
+oracle run on the GPU's own selection.  With ratio 1 every block is kept and the
+result must equal the dense forward bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block_sparse as S
+from tests import gpu_helpers as G
+from variable_length_flash_jagged_amd import binding as B
+from variable_length_flash_jagged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [1, 63, 64, 65, 300, 520, 777, 1030, 0, 2049]
+
+
+def _split_selection(sel, lengths, heads, ratio):
+    """GPU selection array -> list over sequences of [H][nqb] lists."""
+    sel = sel.cpu().numpy()
+    out, at = [], 0
+    for n in lengths:
+        nqb, kk = -(-n // S.Q_BLOCK), S.keep_count(n, ratio)
+        per_h = []
+        for _ in range(heads):
+            rows = []
+            for _ in range(nqb):
+                rows.append(sel[at:at + kk].tolist())
+                at += kk
+            per_h.append(rows)
+        out.append(per_h)
+    return out, at
+
+
+def _check_selection(p, gpu_sel, ratio):
+    q, k = G.f64(p["q"]), G.f64(p["k"])
+    scores = S.block_scores(q, k, p["offsets_host"])
+    ref = S.select_blocks(q, k, p["offsets_host"], ratio)
+    exact = total = 0
+    for b, n in enumerate(p["lengths"]):
+        if n == 0:
+            continue
+        nkb, kk = -(-int(n) // S.K_BLOCK), S.keep_count(int(n), ratio)
+        qb = S.pooled_blocks(q, int(p["offsets_host"][b]), int(p["offsets_host"][b + 1]), S.Q_BLOCK)
+        kb = S.pooled_blocks(k, int(p["offsets_host"][b]), int(p["offsets_host"][b + 1]), S.K_BLOCK)
+        group = q.shape[1] // k.shape[1]
+        for hh in range(q.shape[1]):
+            for i in range(scores[b].shape[1]):
+                got = gpu_sel[b][hh][i]
+                assert len(got) == kk and got == sorted(set(got)) and all(0 <= j < nkb for j in got), (b, hh, i, got)
+                s = scores[b][hh, i]
+                dropped = [j for j in range(nkb) if j not in got]
+                tol = 1e-4 * np.linalg.norm(qb[i, hh]) * max(np.linalg.norm(kb[j, hh // group]) for j in range(nkb))
+                if dropped:
+                    assert min(s[got]) >= max(s[dropped]) - tol - 1e-9, (b, hh, i)
+                exact += got == ref[b][hh][i]
+                total += 1
+    print(f"selection identical to the oracle's on {exact}/{total} query blocks", flush=True)
+
+
+def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, label=""):
+    print(f"[case] block sparse {label} lengths={lengths} H={heads} Hkv={num_kv_heads or heads} D={head_dim} "
+          f"ratio={ratio} seed={seed}", flush=True)
+    p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=False, num_kv_heads=num_kv_heads)
+    g = G.to_gpu(p)
+    o, lse, sel = B.fwd_block_sparse(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], ratio, g["scale"],
+                                     opts)
+    torch.cuda.synchronize()
+    gpu_sel, used = _split_selection(sel, p["lengths"], heads, ratio)
+    assert used == B.block_sparse_entries(B.make_shape(len(lengths), heads, head_dim, p["total_tokens"], 0,
+                                                       num_kv_heads or 0), p["offsets_host"], ratio)
+    _check_selection(p, gpu_sel, ratio)
+    o_ref, lse_ref = S.block_sparse_forward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), p["offsets_host"],
+                                            gpu_sel, p["scale"])
+    G.check_fwd(o, lse, o_ref, lse_ref, label)
+    return p, g, o, lse
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("ratio", [0.5, 0.25])
+def test_block_sparse_forward(head_dim, ratio):
+    _run(LENGTHS, 2, head_dim, ratio, seed=41, label=f"D{head_dim} r{ratio}")
+
+
+def test_block_sparse_grouped_query_and_dynamic_schedule():
+    _run(LENGTHS, 4, 128, 0.5, seed=42, num_kv_heads=2, label="gqa")
+    _run(LENGTHS, 2, 128, 0.5, seed=43, opts=B.make_opts(sched=1, num_programs=7), label="dynamic")
+
+
+def test_block_sparse_ratio_one_equals_dense_forward_bit_exactly():
+    p, g, o, lse = _run(LENGTHS, 2, 128, 1.0, seed=44, label="ratio 1")
+    o_d, lse_d = G.gpu_fwd(g)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_d)
+    assert torch.equal(lse, lse_d)
+
+
+def test_block_sparse_production_lengths_reduced():
+    lengths = W.workload_lengths(3, 0, 48).tolist()
+    _run(lengths, 4, 128, 0.5, seed=45, label="production lengths, 48 sequences")
+
+
+def test_block_sparse_full_production_workload_sampled():
+    """Workload 7 at full size, in the launch configuration bench.py times; the oracle
+    checks sampled sequences (every sequence's selection and output depend on that
+    sequence alone)."""
+    print("[case] block sparse full-size workload 7", flush=True)
+    p = W.make_workload(7, seed=0, device="cuda")
+    ratio = W.WORKLOADS[7]["sparse_ratio"]
+    o, lse, sel = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], ratio, p["scale"])
+    torch.cuda.synchronize()
+    gpu_sel, _ = _split_selection(sel, p["lengths"], p["num_heads"], ratio)
+    off = p["offsets_host"].astype(np.int64)
+    order = np.argsort(p["lengths"], kind="stable")
+    picks = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]), 7, 500})
+    for b in picks:
+        s, e = int(off[b]), int(off[b + 1])
+        sub = {"q": p["q"][s:e].cpu(), "k": p["k"][s:e].cpu(), "v": p["v"][s:e].cpu(), "lengths": [e - s],
+               "offsets_host": np.array([0, e - s])}
+        _check_selection(sub, [gpu_sel[b]], ratio)
+        o_ref, lse_ref = S.block_sparse_forward(G.f64(sub["q"]), G.f64(sub["k"]), G.f64(sub["v"]), [0, e - s],
+                                                [gpu_sel[b]], p["scale"])
+        G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"workload 7 seq {b} (L={e - s})")

@@ -29,3 +29,20 @@ def test_flop_and_byte_counts():
     assert M.valid_pairs([3, 5], M.MODE_BROADCAST_Q, num_q=7) == 56
     assert M.fwd_bytes([4, 2], M.MODE_SELF, 2, 8) == 8 * 6 * 16 + 4 * 12
     assert M.bwd_bytes([4, 2], M.MODE_SELF, 2, 8) == 16 * 6 * 16 + 4 * 12
+
+
+def test_block_sparse_pairs_full_selection_is_dense_and_half_is_counted_exactly():
+    lengths = [300, 1, 64, 65, 0, 700]
+    keep = [-(-n // 64) if n else 0 for n in lengths]
+    full, half, want_half = [], [], 0
+    for n, kk in zip(lengths, keep):
+        if n == 0:
+            continue
+        nqb = -(-n // 256)
+        for _ in range(2):
+            for i in range(nqb):
+                full += list(range(kk))
+                half += [0]  # first key block only: 64 keys (or n if shorter)
+                want_half += min(256, n - 256 * i) * min(64, n)
+    assert M.block_sparse_pairs(lengths, 2, keep, full) == 2 * M.valid_pairs(lengths, M.MODE_SELF)
+    assert M.block_sparse_pairs(lengths, 2, [1 if n else 0 for n in lengths], half) == want_half

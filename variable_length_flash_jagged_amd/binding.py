@@ -18,10 +18,12 @@ MODE_BROADCAST_Q = 1
 MODE_BLOCK_DIAG = 2
 PASS_FWD = 0
 PASS_BWD = 1
+PASS_FWD_SPARSE = 2
 KERNEL_FWD = 0
 KERNEL_BWD = 1
 KERNEL_BWD_DQ = 2
 KERNEL_BWD_PREP = 3
+KERNEL_SPARSE_SELECT = 4
 
 
 class JfaError(RuntimeError):
@@ -69,6 +71,11 @@ def lib():
         L.jfa_kernel_timing.argtypes = [ctypes.c_int]
         L.jfa_kernel_times.restype = ctypes.c_int
         L.jfa_kernel_times.argtypes = [ctypes.c_int, i64p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        L.jfa_block_sparse_entries.restype = ctypes.c_int
+        L.jfa_block_sparse_entries.argtypes = [sp, vp, f32, i64p]
+        L.jfa_fwd_block_sparse.restype = ctypes.c_int
+        L.jfa_fwd_block_sparse.argtypes = [sp, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t,
+                                           op, vp]
         L.jfa_ds_bytes.restype = ctypes.c_int
         L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
@@ -246,3 +253,43 @@ def bwd(q, k, v, o, do, lse, offsets, offsets_host=None, mode=MODE_SELF, scale=N
                          _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts else None,
                          _stream(stream)), "jfa_bwd")
     return dq, dk, dv
+
+
+def block_sparse_entries(shape, offsets_host, ratio):
+    """Selection entries jfa_fwd_block_sparse writes for these lengths and ratio."""
+    off = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    n = ctypes.c_int64(0)
+    _check(lib().jfa_block_sparse_entries(ctypes.byref(shape), off.ctypes.data, float(ratio), ctypes.byref(n)),
+           "jfa_block_sparse_entries")
+    return int(n.value)
+
+
+def fwd_block_sparse(q, k, v, offsets, offsets_host, ratio, scale=None, opts=None, o=None, lse=None, selection=None,
+                     workspace=None, stream=None):
+    """Block-sparse top-k self-attention forward.  Returns (o, lse, selection) with the
+    layouts of include/jfa.h (selection: int32 kept key-block lists)."""
+    import torch
+    nb, h, d, t, _, hkv = _sizes(q, k, v, offsets, MODE_SELF)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, 0, hkv if hkv != h else 0)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    entries = block_sparse_entries(shape, host, ratio)
+    if o is None:
+        o = torch.empty((t, h, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((h, t), dtype=torch.float32, device=q.device)
+    if selection is None:
+        selection = torch.empty(max(entries, 1), dtype=torch.int32, device=q.device)
+    _check_tensor("o", o, torch.bfloat16, (t, h, d))
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    _check_tensor("selection", selection, torch.int32)
+    if workspace is None:
+        workspace = alloc_workspace(shape, MODE_SELF, PASS_FWD_SPARSE, opts, q.device)
+    _check(lib().jfa_fwd_block_sparse(ctypes.byref(shape), scale, float(ratio), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(offsets), host.ctypes.data, _ptr(o), _ptr(lse), _ptr(selection),
+                                      selection.numel(), _ptr(workspace), workspace.numel(),
+                                      ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_fwd_block_sparse")
+    return o, lse, selection

@@ -114,6 +114,10 @@ int max_programs(const Opts& o, int wg_per_cu) {
 struct Layout {
   size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, ds_base = 0, stats = 0, ds = 0, prefix = 0, acc = 0,
          total = 0;
+  // block-sparse forward: per-sequence arrays (uploaded with the schedule) and the
+  // block means
+  size_t sp_qt = 0, sp_kb = 0, sp_base = 0, sp_k = 0, sp_qbar = 0, sp_kbar = 0;
+  int64_t sp_nqt_cap = 0, sp_nkb_cap = 0;
   int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
@@ -130,18 +134,36 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     L.total = at;
     return;
   }
-  const int wg = pass == JFA_PASS_FWD ? kFwdWgPerCu : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
+  const bool fwd = pass != JFA_PASS_BWD;
+  const int wg = fwd ? kFwdWgPerCu : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
   L.programs_cap = max_programs(o, wg);
   L.seg_cap = std::max<int64_t>(L.programs_cap, H) + 1;
   L.seg = at;
   at += align_up(L.seg_cap * sizeof(int32_t));
-  if (pass == JFA_PASS_FWD) {
+  if (fwd) {
     L.tile_cap = (mode == JFA_MODE_BROADCAST_Q) ? H * B * cdiv(Mq, kFwdRows) : H * (T / kFwdRows + B + 1);
   } else {
     L.tile_cap = H * (T / kBwdKeys + B + 1);
   }
   L.tiles = at;
   at += align_up(L.tile_cap * sizeof(Tile));
+  if (pass == JFA_PASS_FWD_SPARSE) {
+    const int64_t Hkv = s->num_kv_heads > 0 ? s->num_kv_heads : H;
+    L.sp_qt = at;
+    at += align_up((B + 1) * sizeof(int32_t));
+    L.sp_kb = at;
+    at += align_up((B + 1) * sizeof(int32_t));
+    L.sp_base = at;
+    at += align_up((B + 1) * sizeof(int64_t));
+    L.sp_k = at;
+    at += align_up((B + 1) * sizeof(int32_t));
+    L.sp_nqt_cap = T / kSparseQBlock + B + 1;
+    L.sp_nkb_cap = T / kSparseKBlock + B + 1;
+    L.sp_qbar = at;
+    at += align_up((size_t)(H * L.sp_nqt_cap * D) * sizeof(float));
+    L.sp_kbar = at;
+    at += align_up((size_t)(Hkv * L.sp_nkb_cap * D) * sizeof(float));
+  }
   if (pass == JFA_PASS_BWD && mode == JFA_MODE_SELF) {
     // second schedule: the dQ kernel's query-row tiles (kDqRows rows on the recompute
     // path, kDsRows on the stored-dS path; the capacities cover both)
@@ -273,6 +295,35 @@ void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf, cons
   if (ds_base) memcpy(buf.data() + L.ds_base, ds_base->data(), ds_base->size() * sizeof(int64_t));
 }
 
+// Block-sparse forward: per-sequence query / key block prefixes, kept blocks per query
+// block and the first selection entry of each sequence.
+struct SparsePlan {
+  std::vector<int32_t> qt_prefix, kb_prefix, sel_k;
+  std::vector<int64_t> sel_base;
+};
+
+int sparse_plan(const jfa_shape* s, const std::vector<int32_t>& lengths, float ratio, SparsePlan& P) {
+  if (!(ratio > 0.f && ratio <= 1.f)) return fail(JFA_ERR_BAD_OPTION, "ratio must be in (0, 1]");
+  const size_t B = lengths.size();
+  P.qt_prefix.assign(B + 1, 0);
+  P.kb_prefix.assign(B + 1, 0);
+  P.sel_base.assign(B + 1, 0);
+  P.sel_k.assign(B + 1, 0);
+  for (size_t b = 0; b < B; ++b) {
+    const int64_t len = lengths[b];
+    const int64_t nqt = cdiv(len, kSparseQBlock), nkb = cdiv(len, kSparseKBlock);
+    if (nkb > kSparseMaxKeyBlocks)
+      return fail(JFA_ERR_TOO_LARGE, "sequence %zu has %lld key blocks; the block-sparse forward takes at most %d", b,
+                  (long long)nkb, kSparseMaxKeyBlocks);
+    const int32_t k = len > 0 ? std::max<int32_t>(1, (int32_t)std::ceil((double)ratio * (double)nkb)) : 0;
+    P.qt_prefix[b + 1] = P.qt_prefix[b] + (int32_t)nqt;
+    P.kb_prefix[b + 1] = P.kb_prefix[b] + (int32_t)nkb;
+    P.sel_k[b] = k;
+    P.sel_base[b + 1] = P.sel_base[b] + (int64_t)s->num_heads * nqt * k;
+  }
+  return JFA_OK;
+}
+
 int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
@@ -281,7 +332,7 @@ int launch_status(hipError_t e, const char* what) {
 struct KernelTimer {
   std::mutex mu;
   bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[4];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[5];
   void forget_locked() {
     for (auto& v : ev) {
       for (auto& pr : v) {
@@ -333,7 +384,8 @@ int jfa_kernel_timing(int enable) {
 
 int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
   g_detail.clear();
-  if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ && pass != JFA_KERNEL_BWD_PREP)
+  if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ && pass != JFA_KERNEL_BWD_PREP &&
+      pass != JFA_KERNEL_SPARSE_SELECT)
     return fail(JFA_ERR_BAD_MODE, "kernel must be a jfa_kernel");
   if (!launches || !total_ms) return fail(JFA_ERR_NULL_POINTER, "launches and total_ms must be non-NULL");
   std::lock_guard<std::mutex> lock(g_timer.mu);
@@ -381,7 +433,10 @@ int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opt
   g_detail.clear();
   int rc = check_shape(shape, mode);
   if (rc) return rc;
-  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD) return fail(JFA_ERR_BAD_MODE, "pass must be 0 or 1");
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_FWD_SPARSE)
+    return fail(JFA_ERR_BAD_MODE, "pass must be a jfa_pass");
+  if (pass == JFA_PASS_FWD_SPARSE && mode != JFA_MODE_SELF)
+    return fail(JFA_ERR_BAD_MODE, "the block-sparse forward is self mode only");
   if (!bytes) return fail(JFA_ERR_NULL_POINTER, "bytes is NULL");
   Opts o;
   if ((rc = check_opts(opts, o))) return rc;
@@ -402,6 +457,120 @@ int jfa_ds_bytes(const jfa_shape* shape, const int32_t* offsets_host, size_t* by
   for (int32_t len : lengths) blocks += ds_blocks(len);
   *bytes = (size_t)blocks * shape->num_heads * kDsBlockBytes;
   return JFA_OK;
+}
+
+int jfa_block_sparse_entries(const jfa_shape* shape, const int32_t* offsets_host, float ratio, int64_t* entries) {
+  g_detail.clear();
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  if (!offsets_host || !entries) return fail(JFA_ERR_NULL_POINTER, "offsets_host and entries must be non-NULL");
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, nullptr, offsets_host, nullptr, lengths))) return rc;
+  SparsePlan P;
+  if ((rc = sparse_plan(shape, lengths, ratio, P))) return rc;
+  *entries = P.sel_base.back();
+  return JFA_OK;
+}
+
+int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const void* q, const void* k, const void* v,
+                         const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse,
+                         int32_t* selection, int64_t selection_entries, void* workspace, size_t workspace_bytes,
+                         const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q || !k || !v || !o || !lse || !offsets_dev || !selection || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "q, k, v, o, lse, offsets_dev, selection and workspace must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(selection, 4))
+    return fail(JFA_ERR_MISALIGNED, "q, k, v, o must be 16-byte aligned, lse and selection 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  Layout L;
+  layout_for(shape, JFA_MODE_SELF, JFA_PASS_FWD_SPARSE, op, L);
+  if (workspace_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  SparsePlan P;
+  if ((rc = sparse_plan(shape, lengths, ratio, P))) return rc;
+  if (selection_entries < P.sel_base.back())
+    return fail(JFA_ERR_CAPACITY, "selection holds %lld entries, %lld needed", (long long)selection_entries,
+                (long long)P.sel_base.back());
+  const int H = shape->num_heads, D = shape->head_dim, Hkv = kv_heads(shape);
+  const int B = shape->num_seqs;
+  Schedule sc;
+  schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kFwdRows, max_programs(op, kFwdWgPerCu), op.sched == 1, sc);
+  if (sc.tiles.empty()) return JFA_OK;
+  if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  if (P.qt_prefix.back() > L.sp_nqt_cap || P.kb_prefix.back() > L.sp_nkb_cap)
+    return fail(JFA_ERR_WORKSPACE, "internal: block capacity");
+  std::vector<char> buf;
+  serialise(sc, L, buf);
+  buf.resize(L.sp_k + (B + 1) * sizeof(int32_t), 0);
+  memcpy(buf.data() + L.sp_qt, P.qt_prefix.data(), (B + 1) * sizeof(int32_t));
+  memcpy(buf.data() + L.sp_kb, P.kb_prefix.data(), (B + 1) * sizeof(int32_t));
+  memcpy(buf.data() + L.sp_base, P.sel_base.data(), (B + 1) * sizeof(int64_t));
+  memcpy(buf.data() + L.sp_k, P.sel_k.data(), (B + 1) * sizeof(int32_t));
+  char* ws = (char*)workspace;
+  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+
+  const int32_t* qt_prefix = (const int32_t*)(ws + L.sp_qt);
+  const int32_t* kb_prefix = (const int32_t*)(ws + L.sp_kb);
+  float* qbar = (float*)(ws + L.sp_qbar);
+  float* kbar = (float*)(ws + L.sp_kbar);
+  const PoolParams pq{(const uint16_t*)q, qbar, offsets_dev, qt_prefix, B, H, kSparseQBlock, P.qt_prefix.back()};
+  const PoolParams pk{(const uint16_t*)k, kbar, offsets_dev, kb_prefix, B, Hkv, kSparseKBlock, P.kb_prefix.back()};
+  SelectParams ps{};
+  ps.qbar = qbar;
+  ps.kbar = kbar;
+  ps.offsets = offsets_dev;
+  ps.qt_prefix = qt_prefix;
+  ps.kb_prefix = kb_prefix;
+  ps.sel_base = (const int64_t*)(ws + L.sp_base);
+  ps.sel_k = (const int32_t*)(ws + L.sp_k);
+  ps.sel = selection;
+  ps.num_seqs = B;
+  ps.num_heads = H;
+  ps.num_kv_heads = Hkv;
+  ps.nqt = P.qt_prefix.back();
+  ps.nkb = P.kb_prefix.back();
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_SPARSE_SELECT, stream, [&] { return launch_pool(pq, D, stream); }),
+                          "query-block pooling launch")))
+    return rc;
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_SPARSE_SELECT, stream, [&] { return launch_pool(pk, D, stream); }),
+                          "key-block pooling launch")))
+    return rc;
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_SPARSE_SELECT, stream, [&] { return launch_select(ps, D, stream); }),
+                          "block selection launch")))
+    return rc;
+
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.offsets = offsets_dev;
+  p.tiles = (const Tile*)(ws + L.tiles);
+  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.counters = (int32_t*)(ws + L.counters);
+  p.num_seqs = B;
+  p.num_heads = H;
+  p.num_kv_heads = Hkv;
+  p.num_q = 0;
+  p.num_programs = sc.programs;
+  p.total_tokens = shape->total_tokens;
+  p.dynamic = op.sched;
+  p.scale_log2 = scale * kLog2eHost;
+  p.sel = selection;
+  p.sel_base = ps.sel_base;
+  p.sel_k = ps.sel_k;
+  return launch_status(timed_launch(JFA_KERNEL_FWD, stream, [&] { return launch_fwd(p, kSelfSparse, D, stream); }),
+                       "block-sparse forward launch");
 }
 
 int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,

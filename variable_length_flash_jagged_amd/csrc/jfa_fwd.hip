@@ -221,13 +221,14 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const int hkv = h / (H / p.num_kv_heads);            // key/value head of query head h
   const int64_t s0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - s0);
-  const int Lq = (MODE == kSelf) ? L : p.num_q;
+  constexpr bool SELF = MODE != kBroadcastQ;           // self attention (dense or block sparse)
+  const int Lq = SELF ? L : p.num_q;
   const int row = blk * C::BM + wave * 32 + l32;
   const float c = p.scale_log2;
 
   FwdWave<D> w;
   {
-    const int64_t qrow = (MODE == kSelf) ? s0 + row : (int64_t)row;
+    const int64_t qrow = SELF ? s0 + row : (int64_t)row;
     const uint16_t* qp = p.q + qrow * rs + (int64_t)h * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) w.qf[ks] = as_bf16x8(row < Lq ? ld16(qp + ks * 16) : zero16());
@@ -239,7 +240,16 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
 #pragma unroll
     for (int i = 0; i < 16; ++i) w.o[db][i] = 0.f;
 
-  const int n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
+  // Key tiles visited: all ceil(L/BN) of the sequence, or (block sparse) the tile's
+  // ascending list of kept key tiles.  Only a sequence's last key tile can be partial,
+  // and in an ascending list it comes last, so the masking rule below is unchanged.
+  int n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
+  const int32_t* list = nullptr;
+  if constexpr (MODE == kSelfSparse) {
+    n = L > 0 ? p.sel_k[b] : 0;
+    list = p.sel + p.sel_base[b] + ((int64_t)h * ((L + C::BM - 1) / C::BM) + blk) * n;
+  }
+  auto tile_of = [&](int i) { return MODE == kSelfSparse ? list[i] : i; };
   if (n > 0) {
     const uint16_t* kp = p.k + s0 * rkv + (int64_t)hkv * D;
     const uint16_t* vp = p.v + s0 * rkv + (int64_t)hkv * D;
@@ -249,7 +259,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
     // copies and the counted waits below stay exact.
     auto issue = [&](int i) {
       JFA_LDS char* slot = smem + (i % C::NS) * C::STAGE;
-      const int kt = min(i, n - 1), vt = max(i - 1, 0);
+      const int kt = tile_of(min(i, n - 1)), vt = tile_of(max(i - 1, 0));
       ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rkv, rkvb, rows_of(kt), slot, wave, lane);
       ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rkv, rkvb, rows_of(vt), slot + C::TILE, wave, lane);
     };
@@ -292,7 +302,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
       pin_matrix_phase<D>(w);
       end_phase();
     }
-    softmax_phase<D>(w, rows_of(n - 1), half, c);
+    softmax_phase<D>(w, rows_of(tile_of(n - 1)), half, c);
     pin_vector_phase<D>(w);
     end_phase();
     // matrix phase n: O += V(n-1) P(n-1) only
@@ -308,7 +318,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
   if (row < Lq) {
-    const int64_t orow = (MODE == kSelf) ? s0 + row : (int64_t)b * p.num_q + row;
+    const int64_t orow = SELF ? s0 + row : (int64_t)b * p.num_q + row;
     uint16_t* op = p.o + orow * rs + (int64_t)h * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -319,8 +329,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
             pack4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv));
       }
     if (half == 0) {
-      const int64_t li = (MODE == kSelf) ? (int64_t)h * p.total_tokens + s0 + row
-                                         : ((int64_t)b * H + h) * p.num_q + row;
+      const int64_t li = SELF ? (int64_t)h * p.total_tokens + s0 + row : ((int64_t)b * H + h) * p.num_q + row;
       p.lse[li] = lse;
     }
   }
@@ -371,6 +380,7 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
   if (mode == kSelf) return head_dim == 64 ? launch<64, kSelf>(p, s) : launch<128, kSelf>(p, s);
+  if (mode == kSelfSparse) return head_dim == 64 ? launch<64, kSelfSparse>(p, s) : launch<128, kSelfSparse>(p, s);
   return head_dim == 64 ? launch<64, kBroadcastQ>(p, s) : launch<128, kBroadcastQ>(p, s);
 }
 

@@ -7,7 +7,7 @@
 
 namespace jfa {
 
-enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2 };
+enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2, kSelfSparse = 3 };
 
 // Tile geometry.  A forward tile is kFwdRows query rows of one (sequence, head); its
 // key/value loop streams kFwdKeys keys at a time.  A backward tile is kBwdKeys key
@@ -33,6 +33,11 @@ constexpr int kDsWaves = 4;
 constexpr int kDsRows = kDsWaves * 64;
 constexpr int kBlock = 64;
 constexpr int kBdWaves = 4;
+// Block-sparse variant: query blocks are forward tiles, key blocks forward key tiles;
+// the select kernel ranks up to kSparseMaxKeyBlocks key blocks of a sequence in LDS.
+constexpr int kSparseQBlock = kFwdRows;
+constexpr int kSparseKBlock = kFwdKeys;
+constexpr int kSparseMaxKeyBlocks = 2048;
 
 // Persistent workgroups resident per CU (used for the default program count).
 constexpr int kFwdWgPerCu = 1;    // one 8-wave workgroup: 2 waves per SIMD
@@ -69,6 +74,35 @@ struct FwdParams {
   int32_t dynamic;
   int32_t num_kv_heads;  // key/value heads (divides num_heads)
   float scale_log2;  // scale * log2(e)
+  // block-sparse self attention (kSelfSparse): tile (b, h, blk) attends to the key
+  // tiles sel[sel_base[b] + (h * ceil(L_b / kSparseQBlock) + blk) * sel_k[b] + 0 ..
+  // sel_k[b] - 1], ascending
+  const int32_t* sel;
+  const int64_t* sel_base;
+  const int32_t* sel_k;
+};
+
+// Block means of a bf16 [T, heads, D] tensor: out[h][blk][d] (fp32) over consecutive
+// `block`-row groups of every sequence.
+struct PoolParams {
+  const uint16_t* x;
+  float* out;
+  const int32_t* offsets;     // [B+1]
+  const int32_t* blk_prefix;  // [B+1]: blocks before sequence b
+  int32_t num_seqs, heads, block, nblocks;
+};
+
+// Top-k key blocks per query block (block-sparse variant).
+struct SelectParams {
+  const float* qbar;          // [H][nqt][D] query-block means
+  const float* kbar;          // [Hkv][nkb][D] key-block means
+  const int32_t* offsets;     // [B+1]
+  const int32_t* qt_prefix;   // [B+1]: query blocks before sequence b
+  const int32_t* kb_prefix;   // [B+1]: key blocks before sequence b
+  const int64_t* sel_base;    // [B+1]: first list entry of sequence b
+  const int32_t* sel_k;       // [B]: kept key blocks per query block of sequence b
+  int32_t* sel;               // out: ascending key-block lists
+  int32_t num_seqs, num_heads, num_kv_heads, nqt, nkb;
 };
 
 // Backward (self / broadcast-Q).
@@ -138,6 +172,9 @@ hipError_t launch_bwd_self_dq_ds(const BwdParams& p, int head_dim, hipStream_t s
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
+// Block-sparse variant, stage 1.
+hipError_t launch_pool(const PoolParams& p, int head_dim, hipStream_t s);
+hipError_t launch_select(const SelectParams& p, int head_dim, hipStream_t s);
 // dst[i] = bf16(scale * src[i]), i < n (n multiple of 8).
 hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float scale, hipStream_t s);
 // Broadcast-Q partial slabs [P, Mq, D] (programs h*ph .. h*ph+ph-1 hold head h) ->

@@ -59,3 +59,22 @@ def bwd_bytes(lengths, mode, num_heads, head_dim, num_q=0):
         b = len(lengths)
         return 4 * num_q * h * d + 8 * t * h * d + 4 * b * num_q * h * d + 4 * b * h * num_q
     return 16 * t * h * d + 4 * t * h
+
+
+def block_sparse_pairs(lengths, num_heads, keep, selection, q_block=256, k_block=64):
+    """Query-key pairs the block-sparse forward attends: for every (sequence, head,
+    query block) the block's rows times the keys of its kept key blocks.  ``keep`` is
+    the kept count per sequence and ``selection`` the flat int32 kept-block lists in
+    the layout jfa_fwd_block_sparse writes (sequence, then head, then query block)."""
+    sel = np.asarray(selection, dtype=np.int64)
+    pairs, at = 0, 0
+    for n, kk in zip(np.asarray(lengths, dtype=np.int64).tolist(), keep):
+        if n == 0:
+            continue
+        nqb = -(-n // q_block)
+        rows = np.minimum(q_block, n - q_block * np.arange(nqb))
+        blocks = sel[at:at + num_heads * nqb * kk].reshape(num_heads, nqb, kk)
+        at += num_heads * nqb * kk
+        keys = np.minimum(k_block, n - k_block * blocks).sum(axis=2)  # [H, nqb]
+        pairs += int((keys * rows[None, :]).sum())
+    return pairs

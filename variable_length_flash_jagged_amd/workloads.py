@@ -19,6 +19,8 @@ generators stand in for them):
    n ~ U{1..63}, H=4, D=64.
 6. ``production_jagged_gqa``: the lengths of workload 3 with H=4 query heads sharing
    one key/value head (grouped-query attention, forward only).
+7. ``production_jagged_sparse``: workload 3 through the block-sparse top-k forward at
+   ratio 0.5 (forward only).
 
 Draw order: lengths (numpy ``default_rng(seed)``), then q, k, v, dO from one
 ``torch.Generator`` seeded with ``seed`` on the target device, each drawn in fp32 and
@@ -41,6 +43,8 @@ WORKLOADS = {
     5: dict(name="block_diag", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0),
     6: dict(name="production_jagged_gqa", mode=MODE_SELF, num_heads=4, num_kv_heads=1, head_dim=128, num_q=0,
             fwd_only=True),
+    7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0, fwd_only=True,
+            sparse_ratio=0.5),
 }
 
 
@@ -55,7 +59,7 @@ def workload_lengths(workload, seed=0, num_seqs=None):
         n = 64 if num_seqs is None else num_seqs
         u = rng.uniform(0.0, math.log(4097.0), size=n)
         return np.clip(np.floor(np.exp(u)), 1, 4096).astype(np.int64)
-    if workload in (3, 6):
+    if workload in (3, 6, 7):
         n = 1152 if num_seqs is None else num_seqs
         x = rng.normal(math.log(600.0), 1.0, size=n)
         return np.clip(np.rint(np.exp(x)), 1, 4000).astype(np.int64)
