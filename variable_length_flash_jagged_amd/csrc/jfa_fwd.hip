@@ -285,9 +285,14 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
     };
     if (2 <= n) issue(2);
     if (g) end_phase();
-    // matrix phase 0: S(0) only
+    // matrix phase 0: S(0) only.  Matrix phases run at raised wave priority: when both
+    // waves of a SIMD have an instruction ready, the one feeding the matrix core goes
+    // first (measured: 1.7 % faster than equal priorities; raising the vector phase
+    // instead changes nothing).
+    __builtin_amdgcn_s_setprio(2);
     mma_s<D>(smem, ln, w);
     pin_matrix_phase<D>(w);
+    __builtin_amdgcn_s_setprio(0);
     end_phase();
     int slot_off = 0;  // ring offset of stage i - 1
     for (int i = 1; i < n; ++i) {
@@ -296,10 +301,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
       end_phase();
       slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
       const JFA_LDS char* slot = smem + slot_off;
+      __builtin_amdgcn_s_setprio(2);
       mma_pv<D>(slot + C::TILE, ln, w);
       mma_s<D>(slot, ln, w);
       order_matrix_phase<D>();
       pin_matrix_phase<D>(w);
+      __builtin_amdgcn_s_setprio(0);
       end_phase();
     }
     softmax_phase<D>(w, rows_of(tile_of(n - 1)), half, c);
@@ -307,8 +314,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
     end_phase();
     // matrix phase n: O += V(n-1) P(n-1) only
     slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
+    __builtin_amdgcn_s_setprio(2);
     mma_pv<D>(smem + slot_off + C::TILE, ln, w);
     pin_matrix_phase<D>(w);
+    __builtin_amdgcn_s_setprio(0);
     end_phase();
     if (!g) end_phase();
   }
