@@ -213,3 +213,28 @@ def test_workloads_reduced(workload, num_seqs):
     lengths = W.workload_lengths(workload, 0, num_seqs)
     G.run_case(lengths, w["num_heads"], w["head_dim"], w["mode"], w["num_q"], seed=workload,
                label=f"workload {workload} ({w['name']}) reduced")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_configurations(seed):
+    """Seeded random sweep over modes, head dims, head counts, grouped key/value heads,
+    schedules, program counts and length mixes (including empty and 1-token sequences
+    and lengths around tile edges)."""
+    rng = np.random.default_rng(1000 + seed)
+    mode = int(rng.integers(0, 3))
+    d = int(rng.choice([64, 128]))
+    h = int(rng.choice([1, 2, 3, 4]))
+    nb = int(rng.integers(1, 9))
+    edges = [1, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+    lengths = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(0, 700)) for _ in range(nb)]
+    if mode == W.MODE_BLOCK_DIAG and rng.random() < 0.5:
+        lengths = [64 * int(rng.integers(0, 9)) for _ in range(nb)]
+    opts = B.make_opts(sched=int(rng.integers(0, 2)), num_programs=int(rng.choice([0, 1, 3, 17])),
+                       dq_path=int(rng.integers(0, 2)))
+    num_q = int(rng.integers(1, 300)) if mode == W.MODE_BROADCAST_Q else 0
+    hkv = int(rng.choice([x for x in range(1, h + 1) if h % x == 0]))
+    gqa = hkv != h and rng.random() < 0.5
+    G.run_case(lengths, h, d, mode, num_q, seed=2000 + seed, opts=opts, bwd=not gqa,
+               num_kv_heads=hkv if gqa else None,
+               label=f"random mode{mode} D{d} H{h} Hkv{hkv if gqa else h} opts=({opts.sched},{opts.num_programs},"
+                     f"{opts.dq_path})")
