@@ -697,30 +697,31 @@ __global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
 // ---------------------------------------------------------- stored-dS path: dQ = dS K
 
 // dQ = scale dS K from the stored dS: one workgroup = kDsRows (256) query rows of one
-// (sequence, head), wave w owning rows 64w .. 64w+63 -- exactly the queries of one
-// stored block column it = 4 blk + w -- as two 32-row column blocks of fp32 dQ^T
-// accumulators.  The loop streams 64 keys at a time (half of a stored block) through a
-// three-slot LDS ring: the K rows (swizzled tile, shared by the waves) and each wave's
-// own 8 KB dS slice (a linear copy of the stored bytes).  Per 16-key k-step:
-// dQ^T += K^T dS^T with A = K^T (transposed fetch of the K tile) and B = dS^T
-// (transposed fetch of the slice, 4 keys x 16 queries per 16-lane group).  The kernel
-// moves two bytes of dS per (query, key) pair for 2 D flops, so HBM, not the matrix
-// unit, bounds it; the ring keeps two slots of copies in flight.
+// (sequence, head).  Waves 2c and 2c+1 share stored block column it = 4 blk + c (64
+// query rows) and each owns one 32-row column block of fp32 dQ^T accumulators; two
+// waves per SIMD keep more copies in flight and hide the LDS latency (measured 4.6
+// against 3.6 TB/s with one wave of 64 rows per SIMD).  The loop streams 64 keys at a
+// time (half of a stored block) through a three-slot LDS ring: the K rows (swizzled
+// tile, shared by the waves) and each block column's 8 KB dS slice (each wave copies
+// the half with its column block).  Per 16-key k-step: dQ^T += K^T dS^T with A = K^T
+// (transposed fetch of the K tile) and B = dS^T (transposed fetch of the slice, 4 keys
+// x 16 queries per 16-lane group).  The kernel moves two bytes of dS per (query, key)
+// pair for 2 D flops, so HBM, not the matrix unit, bounds it.
 template <int D>
 struct DsCfg {
-  static constexpr int NW = kDsWaves;
+  static constexpr int NW = kDsWaves;                    // two waves per stored block column
   static constexpr int BM = kDsRows;
   static constexpr int BK = 64;                          // keys per step
   static constexpr int NDB = D / 32;
   static constexpr int RB = 2 * D;
   static constexpr int KBUF = BK * RB;                   // K rows of a step
   static constexpr int SLICE = kDsBlockBytes / 2;        // one wave's dS: 64 keys x 64 queries
-  static constexpr int STAGE = KBUF + NW * SLICE;
+  static constexpr int STAGE = KBUF + (NW / 2) * SLICE;
   static constexpr int NS = 3;
   static constexpr int SMEM = NS * STAGE;
   using Copy = TileCopy<RB, BK, NW>;
-  static constexpr int SLICE_COPIES = SLICE / 1024;
-  static_assert(BK * 2 == kBwdKeys && kBwdRows == 64 && BM == NW * kBwdRows, "slices are halves of stored blocks");
+  static constexpr int SLICE_COPIES = SLICE / 1024 / 2;  // each wave copies its column block's half
+  static_assert(BK * 2 == kBwdKeys && kBwdRows == 64 && BM == (NW / 2) * kBwdRows, "slices are halves of stored blocks");
 };
 
 template <int D>
@@ -767,21 +768,14 @@ __device__ __forceinline__ bf16x8 mask_keys(const bf16x8& b, int t, int half, in
 
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_ds_step(const JFA_LDS char* kbuf, const JFA_LDS char* slice, const DsLane<D>& ln,
-                                           f32x16 (&acc)[2][DsCfg<D>::NDB], int half, int keys_valid) {
+                                           f32x16 (&acc)[DsCfg<D>::NDB], int half, int keys_valid, int cb) {
   using C = DsCfg<D>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    bf16x8 b0 = ln.ds(slice, t, 0), b1 = ln.ds(slice, t, 1);
-    if (MASK) {
-      b0 = mask_keys(b0, t, half, keys_valid);
-      b1 = mask_keys(b1, t, half, keys_valid);
-    }
+    bf16x8 b0 = ln.ds(slice, t, cb);
+    if (MASK) b0 = mask_keys(b0, t, half, keys_valid);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 a = ln.ktr.read(kbuf, 16 * t, db);
-      acc[0][db] = mfma32(a, b0, acc[0][db]);
-      acc[1][db] = mfma32(a, b1, acc[1][db]);
-    }
+    for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(ln.ktr.read(kbuf, 16 * t, db), b0, acc[db]);
   }
 }
 
@@ -796,7 +790,8 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
   const int64_t s0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - s0);
   const int nq = (L + kBwdRows - 1) / kBwdRows, nj = (L + kBwdKeys - 1) / kBwdKeys;
-  const int it = blk * (C::BM / kBwdRows) + wave;  // this wave's stored block column
+  const int pair = wave >> 1, cb = wave & 1;
+  const int it = blk * (C::BM / kBwdRows) + pair;  // this wave's stored block column
   const bool live = it < nq;                       // wave-uniform: rows past the end only
   const int nkb = (L + C::BK - 1) / C::BK;
   const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
@@ -809,9 +804,14 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
     ln.copy.issue_rows(kp + (int64_t)kb * C::BK * rs, rsb, min(C::BK, L - kb * C::BK), st, wave, lane);
     if (live) {
       const void* src = uniform_ptr(ds_col + ((int64_t)(kb >> 1) * nq * kDsBlockBytes + (kb & 1) * C::SLICE));
-      JFA_LDS char* dst = st + C::KBUF + wave * C::SLICE;
+      JFA_LDS char* dst = st + C::KBUF + pair * C::SLICE;
 #pragma unroll
-      for (int c = 0; c < C::SLICE_COPIES; ++c) dma16(src, (uint32_t)(c * 1024 + lane * 16), dst + c * 1024);
+      for (int w2 = 0; w2 < 2; ++w2)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int o = w2 * 4096 + cb * 2048 + c * 1024;
+          dma16(src, (uint32_t)(o + lane * 16), dst + o);
+        }
     }
   };
   // Wait until at most the copies of one more step are outstanding (vector-memory
@@ -821,13 +821,11 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
     else wait_vmem_n<C::Copy::J>();
   };
 
-  f32x16 acc[2][C::NDB];
+  f32x16 acc[C::NDB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[cb][db][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   issue(0);
   if (nkb > 1) {
@@ -842,8 +840,8 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
     const JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
     const int kv = L - kb * C::BK;
     if (live) {
-      if (kv >= C::BK) dq_ds_step<D, false>(st, st + C::KBUF + wave * C::SLICE, ln, acc, half, C::BK);
-      else dq_ds_step<D, true>(st, st + C::KBUF + wave * C::SLICE, ln, acc, half, kv);
+      if (kv >= C::BK) dq_ds_step<D, false>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, C::BK, cb);
+      else dq_ds_step<D, true>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, kv, cb);
     }
     if (kb + 2 < nkb) wait_one_behind();
     else wait_vmem();
@@ -852,23 +850,22 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
 
   // dQ^T C layout: register i <-> head-dim element 32db + 8(i/4) + 4 half + i%4, lane
   // l32 <-> query row 64 wave + 32 cb + l32 of the tile.
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int row = blk * C::BM + wave * 64 + cb * 32 + l32;
+  {
+    const int row = blk * C::BM + pair * 64 + cb * 32 + l32;
     if (row < L) {
       uint16_t* qp = p.dq + (s0 + row) * rs + (int64_t)h * D + 4 * half;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          st8(qp + 32 * db + 8 * g4, pack4(acc[cb][db][4 * g4] * p.scale, acc[cb][db][4 * g4 + 1] * p.scale,
-                                          acc[cb][db][4 * g4 + 2] * p.scale, acc[cb][db][4 * g4 + 3] * p.scale));
+          st8(qp + 32 * db + 8 * g4, pack4(acc[db][4 * g4] * p.scale, acc[db][4 * g4 + 1] * p.scale,
+                                          acc[db][4 * g4 + 2] * p.scale, acc[db][4 * g4 + 3] * p.scale));
     }
   }
 }
 
 template <int D>
-__global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     dq_ds_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem[DsCfg<D>::SMEM];
   __shared__ int next_tile;

@@ -27,10 +27,11 @@ constexpr int kBwdRows = 64;
 constexpr int kBwdStages = 3;     // Q / dO ring slots of the dK/dV kernel
 // Stored-dS self-attention backward: the dK/dV kernel writes dS in blocks of kBwdKeys
 // keys x kBwdRows queries (bf16, 16 KB each) and a dQ = scale dS K kernel reads them
-// back, kDsRows query rows per tile (kDsWaves waves of 64 rows).
+// back, kDsRows query rows per tile (kDsWaves waves of 32 rows, two per stored block
+// column of 64 rows).
 constexpr int kDsBlockBytes = kBwdKeys * kBwdRows * 2;
-constexpr int kDsWaves = 4;
-constexpr int kDsRows = kDsWaves * 64;
+constexpr int kDsWaves = 8;
+constexpr int kDsRows = kDsWaves * 32;
 constexpr int kBlock = 64;
 constexpr int kBdWaves = 4;
 // Block-sparse variant: query blocks are forward tiles, key blocks forward key tiles;
@@ -47,7 +48,7 @@ constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound ov
 constexpr int dkdv_wg_per_cu(int head_dim) { return head_dim == 64 ? 2 : 1; }
 constexpr int kBqWgPerCu = 1;     // broadcast-Q fused backward
 constexpr int kDqWgPerCu = 2;     // self-attention dQ kernel
-constexpr int kDsWgPerCu = 1;     // stored-dS dQ kernel (three 48 KB LDS stages)
+constexpr int kDsWgPerCu = 1;     // stored-dS dQ kernel (8 waves, three 48 KB LDS stages)
 constexpr int kBdWgPerCu = 2;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
