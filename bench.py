@@ -2,8 +2,9 @@
 """Benchmark of the jagged flash attention hot path on one MI355X.
 
 A step is one forward plus one backward (jfa_fwd + jfa_bwd through the C ABI: offsets
-intake, host schedule, schedule upload, attention kernels, dQ accumulation and cast)
-over one batch of the production-shaped jagged self-attention workload: B=1152
+intake, host schedule, schedule upload, attention kernels; the self-attention backward
+at head_dim 128 takes the stored-dS path, whose workspace the bench grants) over one
+batch of the production-shaped jagged self-attention workload: B=1152
 sequences with log-normal lengths (median ~600, clipped to [1, 4000]), H=4, D=128,
 bf16 N(0,1) inputs drawn with seed 0, already resident in HBM.  The reported value is
 valid-token TFLOPS (forward 4*H*D*sum L^2 plus backward 2.5x that) per step.
@@ -37,9 +38,9 @@ def parse():
     ap.add_argument("--sched", type=int, default=0)
     ap.add_argument("--dq-path", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--stored-ds", action="store_true",
-                    help="self attention: grant the dS workspace so that the backward keeps dS in HBM "
-                         "(stored-dS path) instead of recomputing it")
+    ap.add_argument("--self-bwd", choices=("auto", "stored", "recompute"), default="auto",
+                    help="self-attention backward: stored-dS (the bench grants the dS workspace), recompute, "
+                         "or auto (stored-dS at head_dim 128, recompute at 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -177,7 +178,7 @@ def main():
     ratio = w.get("sparse_ratio")
     lengths = p["lengths"]
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
-    opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, stored_ds=args.stored_ds)
+    opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, self_bwd=args.self_bwd)
     q, k, v, do, off, off_h = p["q"], p["k"], p["v"], p["do"], p["offsets"], p["offsets_host"]
     if mode == W.MODE_BROADCAST_Q:
         o = torch.empty((p["num_seqs"], mq, h, d), dtype=torch.bfloat16, device="cuda")

@@ -1,8 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is generated at full size on the GPU and run through jfa_fwd / jfa_bwd
-with the options bench.py uses by default (static schedule, recompute self-attention
-backward; both broadcast-Q dQ paths), and workload 3 also with the stored-dS backward.
+with the options bench.py uses by default (static schedule; the stored-dS
+self-attention backward at head_dim 128, the recompute one at 64; both broadcast-Q dQ
+paths), and workload 3 also with the recompute backward.
 The oracle then checks sampled sequences one by one -- the longest, the shortest, the
 median and a few seeded picks -- since in self and block-diagonal attention every
 sequence's outputs and gradients depend on that sequence alone.  Broadcast-Q (whose
@@ -35,10 +36,10 @@ def _shape(p):
                         hkv if hkv != p["num_heads"] else 0)
 
 
-def _run(workload, opts=None, bench=False, stored_ds=False):
+def _run(workload, opts=None, bench=False, self_bwd="auto"):
     p = W.make_workload(workload, seed=0, device="cuda")
     if bench:
-        opts = B.bench_opts(p["mode"], _shape(p), p["offsets_host"], stored_ds=stored_ds)
+        opts = B.bench_opts(p["mode"], _shape(p), p["offsets_host"], self_bwd=self_bwd)
     if p["do"] is None:
         print("[case] forward only (grouped-query attention)", flush=True)
     print(f"[case] full-size workload {workload} opts=({opts.sched if opts else 0}, "
@@ -53,10 +54,10 @@ def _run(workload, opts=None, bench=False, stored_ds=False):
     return p, o, lse, grads
 
 
-@pytest.mark.parametrize("workload,samples,stored_ds", [(1, 4, False), (3, 6, False), (4, 1, False), (5, 6, False),
-                                                       (3, 4, True), (6, 4, False)])
-def test_full_size_sampled_sequences(workload, samples, stored_ds):
-    p, o, lse, grads = _run(workload, bench=True, stored_ds=stored_ds)
+@pytest.mark.parametrize("workload,samples,self_bwd", [(1, 4, "auto"), (3, 6, "auto"), (4, 1, "auto"), (5, 6, "auto"),
+                                                      (3, 4, "recompute"), (6, 4, "auto")])
+def test_full_size_sampled_sequences(workload, samples, self_bwd):
+    p, o, lse, grads = _run(workload, bench=True, self_bwd=self_bwd)
     off = p["offsets_host"].astype(np.int64)
     mode = p["mode"]
     for b in _sample_sequences(p["lengths"], samples, workload):

@@ -119,10 +119,15 @@ def ds_budget_mib(shape, offsets_host):
     return max(1, -(-ds_bytes(shape, offsets_host) // (1 << 20)))
 
 
-def bench_opts(mode, shape, offsets_host, sched=0, dq_path=0, stored_ds=False):
+def bench_opts(mode, shape, offsets_host, sched=0, dq_path=0, self_bwd="auto"):
     """Options the benchmark runs with: the given schedule and broadcast-Q dQ path and,
-    with stored_ds in self attention, a dS budget that selects the stored-dS backward."""
-    budget = ds_budget_mib(shape, offsets_host) if (stored_ds and mode == MODE_SELF) else 0
+    for self attention, the backward path: "stored" grants the dS workspace (stored-dS
+    backward), "recompute" does not, "auto" takes the stored-dS backward at head_dim 128
+    (measured faster there) and the recompute backward at 64."""
+    if self_bwd not in ("auto", "stored", "recompute"):
+        raise ValueError(f"self_bwd must be auto, stored or recompute, got {self_bwd!r}")
+    stored = self_bwd == "stored" or (self_bwd == "auto" and shape.head_dim == 128)
+    budget = ds_budget_mib(shape, offsets_host) if (stored and mode == MODE_SELF) else 0
     return make_opts(sched=sched, dq_path=dq_path, ds_budget_mib=budget)
 
 
