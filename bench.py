@@ -51,13 +51,41 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed (string and
+    character literals kept as they are), so that an edit to a comment leaves the
+    digest of the code unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest():
-    """Digest of the kernel sources; traffic counters are only reported for the build
-    they were taken on."""
+    """Digest of the kernel sources' code (comments excluded); traffic counters are only
+    reported for the code they were taken on."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "variable_length_flash_jagged_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+    csrc = os.path.join(ROOT, "variable_length_flash_jagged_amd", "csrc")
+    for f in sorted(sum((glob.glob(os.path.join(csrc, "*" + ext)) for ext in (".hip", ".cpp", ".h")), [])):
+        with open(f, encoding="utf-8", errors="replace") as fh:
+            h.update(os.path.basename(f).encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -849,7 +849,7 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
   }
 
   // dQ^T C layout: register i <-> head-dim element 32db + 8(i/4) + 4 half + i%4, lane
-  // l32 <-> query row 64 wave + 32 cb + l32 of the tile.
+  // l32 <-> query row 64 pair + 32 cb + l32 of the tile.
   {
     const int row = blk * C::BM + pair * 64 + cb * 32 + l32;
     if (row < L) {
