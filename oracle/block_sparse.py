@@ -21,13 +21,21 @@ paragraph is silent (each one a parameter here):
 
 Grouped-query attention: k, v may carry Hkv heads (query head h reads key/value head
 h // (H // Hkv)), as in ``attention.attention_forward``.  Self attention only.
+
+Backward: the paragraph names the variant's speed-up for the forward only.  Read
+plainly, the backward of the variant is the gradient of sum(O * dO) with the selection
+held fixed (the pooling and top-k choose which keys take part; that discrete choice
+carries no gradient), i.e. for every (sequence, head, query block) the exact-attention
+gradient over the kept keys, the key and value gradients summed over the query blocks
+that kept them.  One query/key-value head per key-value head (H == Hkv), as for the
+dense backward.
 """
 
 import math
 
 import numpy as np
 
-from .attention import sequence_forward
+from .attention import sequence_backward, sequence_forward
 from .offsets import validate_offsets
 
 Q_BLOCK = 256
@@ -117,3 +125,28 @@ def block_sparse_forward(q, k, v, offsets, selection, scale=None, q_block=Q_BLOC
                 o[r0:r1, hh] = ob
                 lse[hh, r0:r1] = lb
     return o, lse
+
+
+def block_sparse_backward(q, k, v, do, offsets, selection, scale=None, q_block=Q_BLOCK, k_block=K_BLOCK):
+    """Gradient of sum(O * dO) of ``block_sparse_forward`` for a fixed selection.
+    Returns (dq, dk, dv), each [T, H, D]."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    t, h, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
+        raise ValueError("the block-sparse backward takes q, k, v, do all [T, H, D] (no grouped heads)")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    off = validate_offsets(offsets, t)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(off) - 1):
+        s, e = off[b], off[b + 1]
+        for hh in range(h):
+            for i, r0 in enumerate(range(s, e, q_block)):
+                r1 = min(r0 + q_block, e)
+                keys = np.concatenate([np.arange(s + j * k_block, min(s + (j + 1) * k_block, e))
+                                       for j in selection[b][hh][i]]).astype(np.int64)
+                g_q, g_k, g_v = sequence_backward(q[r0:r1, hh], k[keys, hh], v[keys, hh], do[r0:r1, hh], scale)
+                dq[r0:r1, hh] = g_q
+                dk[keys, hh] += g_k
+                dv[keys, hh] += g_v
+    return dq, dk, dv

@@ -133,3 +133,82 @@ def test_planted_selection_mistake_is_caught():
     shifted = [[[min(j + 1, 8) for j in lst] for lst in per_h] for per_h in sel[0]]
     o, _ = S.block_sparse_forward(q, k, v, off, [shifted], 0.4)
     assert not np.allclose(o, _masked_sdpa(q, k, v, off, sel, 0.4), rtol=1e-6, atol=1e-8)
+
+
+def _masked_sdpa_grads(q, k, v, do, offsets, selection, scale):
+    """Independent reference for the backward: torch autograd through fp64 attention
+    with the same boolean key mask as _masked_sdpa."""
+    off = [int(x) for x in offsets]
+    grads = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+    for b in range(len(off) - 1):
+        s, e = off[b], off[b + 1]
+        n = e - s
+        if n == 0:
+            continue
+        h = q.shape[1]
+        mask = torch.zeros(h, n, n, dtype=torch.bool)
+        for hh in range(h):
+            for i, r0 in enumerate(range(0, n, S.Q_BLOCK)):
+                for j in selection[b][hh][i]:
+                    mask[hh, r0:min(r0 + S.Q_BLOCK, n), j * S.K_BLOCK:min((j + 1) * S.K_BLOCK, n)] = True
+        ts = [torch.from_numpy(np.ascontiguousarray(x[s:e].transpose(1, 0, 2)))[None].requires_grad_() for x in (q, k, v)]
+        ot = torch.nn.functional.scaled_dot_product_attention(*ts, attn_mask=mask[None], scale=scale)
+        ot.backward(torch.from_numpy(np.ascontiguousarray(do[s:e].transpose(1, 0, 2)))[None])
+        for g, tt in zip(grads, ts):
+            g[s:e] = tt.grad[0].permute(1, 0, 2).numpy()
+    return grads
+
+
+def test_sparse_backward_equals_autograd_of_masked_attention():
+    lengths = [300, 1, 70, 0, 520, 64]
+    off = oracle.offsets_from_lengths(lengths)
+    t = int(off[-1])
+    q, k, v, do = _rand(t, 2, 8), _rand(t, 2, 8), _rand(t, 2, 8), _rand(t, 2, 8)
+    sel = _random_selection(lengths, 2, 0.5)
+    sel[4][0] = [[0, 1, 2, 3, 4], [0, 1, 2, 3, 5], [1, 2, 3, 4, 5]]   # key blocks 6-8 kept by no query block
+    got = S.block_sparse_backward(q, k, v, do, off, sel, 0.4)
+    want = _masked_sdpa_grads(q, k, v, do, off, sel, 0.4)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12)
+    # a key block that no query block kept gets zero dK, dV
+    for jb in (6, 7, 8):
+        r = slice(int(off[4]) + 64 * jb, min(int(off[4]) + 64 * (jb + 1), int(off[5])))
+        assert not got[1][r, 0].any() and not got[2][r, 0].any()
+
+
+def test_sparse_backward_ratio_one_equals_dense_backward():
+    lengths = [300, 5, 129]
+    off = oracle.offsets_from_lengths(lengths)
+    t = int(off[-1])
+    q, k, v, do = _rand(t, 2, 8), _rand(t, 2, 8), _rand(t, 2, 8), _rand(t, 2, 8)
+    sel = S.select_blocks(q, k, off, 1.0)
+    got = S.block_sparse_backward(q, k, v, do, off, sel, 0.3)
+    want = oracle.attention_backward(q, k, v, do, off, oracle.MODE_SELF, 0.3)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_backward_finite_difference():
+    """d/dx of sum(O * dO) by central differences at a few coordinates of q, k, v."""
+    lengths = [300]
+    off = oracle.offsets_from_lengths(lengths)
+    q, k, v, do = _rand(300, 1, 4), _rand(300, 1, 4), _rand(300, 1, 4), _rand(300, 1, 4)
+    sel = [[[[0, 3, 4], [1, 4]]]]
+    grads = S.block_sparse_backward(q, k, v, do, off, sel, 0.5)
+    f = lambda qq, kk, vv: float((S.block_sparse_forward(qq, kk, vv, off, sel, 0.5)[0] * do).sum())
+    eps = 1e-6
+    for which, (r, c) in [(0, (5, 1)), (0, (290, 3)), (1, (10, 0)), (1, (260, 2)), (2, (70, 1)), (2, (299, 0))]:
+        args = [q, k, v]
+        plus = [a.copy() for a in args]
+        minus = [a.copy() for a in args]
+        plus[which][r, 0, c] += eps
+        minus[which][r, 0, c] -= eps
+        fd = (f(*plus) - f(*minus)) / (2 * eps)
+        assert abs(fd - grads[which][r, 0, c]) < 1e-6 * max(1.0, abs(fd)), (which, r, c)
+
+
+def test_sparse_backward_refuses_grouped_heads():
+    off = oracle.offsets_from_lengths([70])
+    with pytest.raises(ValueError):
+        S.block_sparse_backward(_rand(70, 2, 8), _rand(70, 1, 8), _rand(70, 1, 8), _rand(70, 2, 8), off,
+                                [[[[0]], [[0]]]], 0.3)
