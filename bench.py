@@ -90,7 +90,7 @@ def kernel_source_digest():
 
 
 KERNEL_NAMES = {"fwd_kernel": "fwd_kernel<", "dq_kernel": "dq_kernel<", "dkdv_kernel": "dkdv_kernel<",
-                "dq_ds_kernel": "dq_ds_kernel<", "prep_kernel": "prep_kernel<",
+                "dq_ds_kernel": "dq_ds_kernel<", "prep_kernel": "prep_kernel<", "mark_kernel": "mark_kernel",
                 "bwd_kernel": "bwd_kernel<", "bd_fwd_kernel": "bd_fwd_kernel<", "bd_bwd_kernel": "bd_bwd_kernel<"}
 
 
@@ -153,11 +153,14 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
             from oracle import block_sparse as S
             sel = S.select_blocks(q, k, off, sparse_ratio)
             S.block_sparse_forward(q, k, v, off, sel, 1.0 / np.sqrt(head_dim))
+            if not fwd_only:
+                S.block_sparse_backward(q, k, v, do, off, sel, 1.0 / np.sqrt(head_dim))
             spent += time.perf_counter() - t0
             sub = lengths[b:e]
             keep = [S.keep_count(n, sparse_ratio) for n in sub]
             flat = [j for per_b in sel for per_h in per_b for lst in per_h for j in lst]
-            flops += 4 * head_dim * M.block_sparse_pairs(sub, num_heads, keep, flat)  # pairs over heads
+            pairs = M.block_sparse_pairs(sub, num_heads, keep, flat)  # pairs over heads
+            flops += (4 if fwd_only else 14) * head_dim * pairs
             done, b = e, e
             continue
         oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
@@ -175,7 +178,7 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
-                  f"one fp64 {'block-sparse forward' if sparse_ratio else 'forward' if fwd_only else 'forward + backward'}"
+                  f"one fp64 {'block-sparse ' if sparse_ratio else ''}{'forward' if fwd_only else 'forward + backward'}"
                   f" each, {spent:.1f} s",
     }
 
@@ -202,7 +205,7 @@ def main():
     p = W.make_workload(args.workload, seed=args.seed, device="cuda")
     mode, h, d, mq = p["mode"], p["num_heads"], p["head_dim"], p["num_q"]
     hkv = p["num_kv_heads"]
-    fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention, block-sparse variant: forward only
+    fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention: forward only
     ratio = w.get("sparse_ratio")
     lengths = p["lengths"]
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
@@ -220,7 +223,13 @@ def main():
     if ratio:
         sel = torch.empty(max(1, B.block_sparse_entries(shape, p["offsets_host"], ratio)), dtype=torch.int32,
                           device="cuda")
-    ws_b = None if fwd_only else B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
+    if fwd_only:
+        ws_b = None
+    elif ratio:
+        ws_b = torch.empty(B.bwd_block_sparse_workspace_size(shape, p["offsets_host"], opts), dtype=torch.uint8,
+                           device="cuda")
+    else:
+        ws_b = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
     scale = p["scale"]
 
     ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for n in ("f0", "f1", "b1")}
@@ -234,7 +243,9 @@ def main():
             B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
         if i is not None:
             ev["f1"][i].record()
-        if not fwd_only:
+        if ratio:
+            B.bwd_block_sparse(q, k, v, o, do, lse, off, off_h, ratio, sel, scale, opts, dq, dk, dv, ws_b)
+        elif not fwd_only:
             B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
         if i is not None:
             ev["b1"][i].record()
@@ -270,30 +281,48 @@ def main():
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
+    fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
     dense = None
     if ratio:
-        # attended pairs only; the dense forward of the same batch is timed for context
+        # attended pairs only; the dense forward and backward of the same batch (the
+        # bench's dense options) are timed for context
         keep = [max(1, math.ceil(float(np.float32(ratio)) * -(-int(n) // 64))) if n else 0 for n in lengths]
-        ff = 4 * d * M.block_sparse_pairs(lengths, h, keep, sel.cpu().numpy())  # pairs summed over heads
+        sel_h = sel.cpu().numpy()
+        sp_pairs = M.block_sparse_pairs(lengths, h, keep, sel_h)  # pairs summed over heads
+        ff, fb = 4 * d * sp_pairs, 10 * d * sp_pairs
+        tile_pairs = M.block_sparse_tile_pairs(lengths, h, keep, sel_h)
         ws_d = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
+        ws_db = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
+        evd = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         for _ in range(args.warmup):
             B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        d0.record()
+            B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_db)
+        dense = [0.0, 0.0]
         for _ in range(args.steps):
+            evd[0].record()
             B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
-        d1.record()
-        torch.cuda.synchronize()
-        dense = d0.elapsed_time(d1) / args.steps
-    fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
+            evd[1].record()
+            B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_db)
+            evd[2].record()
+            torch.cuda.synchronize()
+            dense[0] += evd[0].elapsed_time(evd[1]) / args.steps
+            dense[1] += evd[1].elapsed_time(evd[2]) / args.steps
+        del ws_db
     bytes_f = M.fwd_bytes(lengths, mode, h, d, mq, hkv)
     bytes_b = 0 if fwd_only else M.bwd_bytes(lengths, mode, h, d, mq)
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     # Per attention kernel: average launch time and the algorithmic work of one launch.
     work = {"fwd": (ff, bytes_f)}
-    stored_ds = kt["bwd_prep"][0] > 0
-    if mode == W.MODE_SELF and stored_ds:
+    stored_ds = not ratio and kt["bwd_prep"][0] > 0
+    if ratio:
+        # Block-sparse backward: mark kernel (selection in, bitmaps out), dQ kernel over
+        # the kept blocks (S, dP, dQ on attended pairs), dK/dV kernel (S, dP, dV, dK on
+        # attended pairs; it executes whole 128-key tiles, see block_sparse.tile_pairs).
+        t = int(p["total_tokens"])
+        work["bwd_prep"] = (0, 4 * int(sel.numel()))
+        work["bwd_dq"] = (6 * d * sp_pairs, 12 * t * h * d + 20 * t * h)
+        work["bwd"] = (8 * d * sp_pairs, 12 * t * h * d + 16 * t * h)
+    elif mode == W.MODE_SELF and stored_ds:
         # Stored-dS backward: row-term kernel (O, dO in, lse in, 16-byte term out per
         # row and head), dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, dK, dV out, the
         # row term in, dS out as bf16 per valid pair) and dQ = dS K (dS and K in, dQ out).
@@ -337,7 +366,8 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
                       ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
-                      "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel", "bwd_prep": "prep_kernel",
+                      "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel",
+                      "bwd_prep": "mark_kernel" if ratio else "prep_kernel",
                       "select": "select_kernel"}[dom]
     if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
         roof["kernel"] = "bd_fwd_kernel"
@@ -380,7 +410,10 @@ def main():
         "wall_s_timed": round(wall, 3),
         "block_sparse": None if not ratio else {
             "ratio": ratio, "attended_pairs_fraction": round(ff / M.fwd_flops(lengths, mode, h, d, mq), 4),
-            "dense_fwd_ms": round(dense, 4), "speedup_vs_dense_fwd": round(dense / fwd_ms, 3)},
+            "dkdv_executed_pairs_fraction": round(tile_pairs / M.valid_pairs(lengths, mode) / h, 4),
+            "dense_fwd_ms": round(dense[0], 4), "speedup_vs_dense_fwd": round(dense[0] / fwd_ms, 3),
+            "dense_bwd_ms": round(dense[1], 4), "speedup_vs_dense_bwd": round(dense[1] / bwd_ms, 3),
+            "speedup_vs_dense_step": round((dense[0] + dense[1]) / ms_step, 3)},
     }
     if not args.no_cpu_baseline:
         offs = np.asarray(off_h, dtype=np.int64)

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 130 /* 1.3.0 */
+#define JFA_VERSION 140 /* 1.4.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -185,6 +185,31 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
                          void* workspace, size_t workspace_bytes,
                          const jfa_opts* opts, void* stream);
 
+/* Block-sparse top-k self attention, backward: the gradient of sum(O * dout) for the
+ * forward of jfa_fwd_block_sparse with its selection held fixed (the pooling and top-k
+ * only choose which keys take part and carry no gradient): per (sequence, head, query
+ * block) the exact-attention gradient over the kept keys, dK and dV summed over the
+ * query blocks that kept them ("Jagged Flash Attention on TLX" (aixai.ru), closing
+ * section on variants, names the variant for the forward; this is the plain reading of
+ * its backward).  selection / selection_entries / ratio: exactly what the forward call
+ * took and wrote (selection is read only; an entry outside [0, nkb) gives wrong
+ * results but no access outside the sequence).  o, lse: that forward's outputs.
+ * Recompute path (opts.ds_budget_mib is ignored).  H == Hkv required.  workspace:
+ * jfa_bwd_block_sparse_workspace_size() bytes for these offsets (the recompute
+ * backward's workspace plus a bitmap of ceil(L/128) * 2 * ceil(ceil(L/256)/32) words
+ * per sequence and head).  dq, dk, dv: [T, H, D] bf16, fully written (keys no query
+ * block kept get dK = dV = 0).  Other conventions as jfa_bwd. */
+int jfa_bwd_block_sparse_workspace_size(const jfa_shape* shape, const int32_t* offsets_host,
+                                        const jfa_opts* opts, size_t* bytes);
+int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
+                         const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         const int32_t* offsets_dev, const int32_t* offsets_host,
+                         const int32_t* selection, int64_t selection_entries,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         const jfa_opts* opts, void* stream);
+
 /* Host-only view of the tile schedule the calls above would run (no device needed).
  * Tiles are (b, h, blk) triples: forward tiles are tile_rows query rows, backward
  * tiles tile_rows key rows, block-diagonal tiles one 64-token block.  Static
@@ -201,15 +226,18 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
 enum jfa_kernel {
   JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd (and jfa_fwd_block_sparse) */
   JFA_KERNEL_BWD = 1,    /* the main backward kernel of jfa_bwd: the dK/dV kernel in self
-                            mode, the fused kernel in broadcast-Q and block-diagonal modes */
-  JFA_KERNEL_BWD_DQ = 2,  /* self mode only: the dQ kernel of jfa_bwd (recompute or stored-dS) */
-  JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path only: the row-term kernel (Di, lse) */
+                            mode (and in jfa_bwd_block_sparse), the fused kernel in
+                            broadcast-Q and block-diagonal modes */
+  JFA_KERNEL_BWD_DQ = 2,  /* self mode only: the dQ kernel of jfa_bwd (recompute or stored-dS) and of
+                             jfa_bwd_block_sparse */
+  JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path: the row-term kernel (Di, lse);
+                                 jfa_bwd_block_sparse: the selection-bitmap (mark) kernel */
   JFA_KERNEL_SPARSE_SELECT = 4 /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
                                   select launch (each recorded as one launch) */
 };
 
 /* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd /
- * jfa_fwd_block_sparse call records a
+ * jfa_fwd_block_sparse / jfa_bwd_block_sparse call records a
  * pair of HIP events on its stream immediately around each of its attention kernels
  * (not the schedule upload or the dQ fill / cast / reduce kernels).  jfa_kernel_times
  * waits for the events recorded so far for `kernel` (a jfa_kernel) and returns the

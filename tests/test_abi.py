@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 130
+    assert lib.jfa_version() == 140
 
 
 def test_error_strings():
@@ -221,3 +221,40 @@ def test_schedule_tile_rows():
     assert B.schedule(shape, 0, 0, off)[3] == 256
     assert B.schedule(shape, 0, 1, off)[3] == 128
     assert B.schedule(shape, 2, 0, off)[3] == 64
+
+
+def test_block_sparse_backward_workspace_size():
+    lengths = [300, 0, 65, 4000]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), 3, 128, int(off[-1]))
+    base = B.workspace_size(shape, 0, B.PASS_BWD)
+    words = sum(3 * (-(-n // 128)) * 2 * (-(-(-(-n // 256)) // 32)) for n in lengths)
+    got = B.bwd_block_sparse_workspace_size(shape, off)
+    assert base + 4 * words <= got <= base + 4 * words + 4 * 256 + 3 * 8 * (len(lengths) + 1)
+    # the dS budget does not enlarge it (the block-sparse backward recomputes dS)
+    assert B.bwd_block_sparse_workspace_size(shape, off, B.make_opts(ds_budget_mib=64)) == got
+    with pytest.raises(B.JfaError) as e:
+        B.bwd_block_sparse_workspace_size(shape, np.array([0, 300, 300, 365, 4364], np.int32))
+    assert e.value.code == -5
+
+
+def _sparse_bwd_rc(shape, off, ratio=0.5, entries=1 << 20, ws_bytes=1 << 40, ptr=1 << 20):
+    lib = B.lib()
+    p = ctypes.c_void_p(ptr)
+    return lib.jfa_bwd_block_sparse(ctypes.byref(shape), 0.125, ratio, p, p, p, p, p, p, p, off.ctypes.data, p,
+                                    entries, p, p, p, p, ws_bytes, None, None)
+
+
+def test_block_sparse_backward_argument_errors_before_device_work():
+    off = np.array([0, 300], dtype=np.int32)
+    shape = B.make_shape(1, 2, 64, 300)
+    assert _sparse_bwd_rc(B.make_shape(1, 4, 64, 300, num_kv_heads=2), off) == -2
+    assert _sparse_bwd_rc(shape, off, ptr=0) == -1
+    assert _sparse_bwd_rc(shape, off, ptr=(1 << 20) + 2) == -6
+    for bad in (0.0, 1.5, float("nan")):
+        assert _sparse_bwd_rc(shape, off, ratio=bad) == -8
+    need = B.block_sparse_entries(shape, off, 0.5)
+    assert _sparse_bwd_rc(shape, off, entries=need - 1) == -11
+    ws = B.bwd_block_sparse_workspace_size(shape, off)
+    assert _sparse_bwd_rc(shape, off, ws_bytes=ws - 1) == -7
+    assert _sparse_bwd_rc(shape, np.array([0, 299], np.int32)) == -5

@@ -7,7 +7,11 @@ selection is checked for validity against the oracle's fp64 relevance (right cou
 ascending, no duplicates, and no dropped block beats a kept one by more than a bound
 on the fp32 error), and the attention is checked element by element against the
 oracle run on the GPU's own selection.  With ratio 1 every block is kept and the
-result must equal the dense forward bit for bit."""
+result must equal the dense forward bit for bit.
+
+The backward (jfa_bwd_block_sparse) is checked against the oracle's backward for the
+same (GPU) selection; at ratio 1 it walks every query and key step in the dense
+recompute backward's order and must equal jfa_bwd (no dS budget) bit for bit."""
 
 import numpy as np
 import pytest
@@ -66,10 +70,10 @@ def _check_selection(p, gpu_sel, ratio):
     print(f"selection identical to the oracle's on {exact}/{total} query blocks", flush=True)
 
 
-def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, label=""):
+def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, label="", bwd=False):
     print(f"[case] block sparse {label} lengths={lengths} H={heads} Hkv={num_kv_heads or heads} D={head_dim} "
-          f"ratio={ratio} seed={seed}", flush=True)
-    p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=False, num_kv_heads=num_kv_heads)
+          f"ratio={ratio} seed={seed} bwd={bwd}", flush=True)
+    p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=bwd, num_kv_heads=num_kv_heads)
     g = G.to_gpu(p)
     o, lse, sel = B.fwd_block_sparse(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], ratio, g["scale"],
                                      opts)
@@ -81,6 +85,14 @@ def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, la
     o_ref, lse_ref = S.block_sparse_forward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), p["offsets_host"],
                                             gpu_sel, p["scale"])
     G.check_fwd(o, lse, o_ref, lse_ref, label)
+    if bwd:
+        grads = B.bwd_block_sparse(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], ratio,
+                                   sel, g["scale"], opts)
+        torch.cuda.synchronize()
+        refs = S.block_sparse_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
+                                       p["offsets_host"], gpu_sel, p["scale"])
+        G.check_bwd(grads, refs, label + " bwd")
+        return p, g, o, lse, sel, grads
     return p, g, o, lse
 
 
@@ -129,3 +141,54 @@ def test_block_sparse_full_production_workload_sampled():
         o_ref, lse_ref = S.block_sparse_forward(G.f64(sub["q"]), G.f64(sub["k"]), G.f64(sub["v"]), [0, e - s],
                                                 [gpu_sel[b]], p["scale"])
         G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"workload 7 seq {b} (L={e - s})")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("ratio", [0.5, 0.25])
+def test_block_sparse_backward(head_dim, ratio):
+    _run(LENGTHS, 2, head_dim, ratio, seed=51, label=f"D{head_dim} r{ratio}", bwd=True)
+
+
+def test_block_sparse_backward_dynamic_schedule_and_few_programs():
+    _run(LENGTHS, 3, 128, 0.5, seed=52, opts=B.make_opts(sched=1, num_programs=5), label="dynamic", bwd=True)
+    _run(LENGTHS, 2, 64, 0.3, seed=53, opts=B.make_opts(num_programs=3), label="3 programs", bwd=True)
+
+
+def test_block_sparse_backward_ratio_one_equals_dense_backward_bit_exactly():
+    for d in (64, 128):
+        p, g, o, lse, sel, grads = _run(LENGTHS, 2, d, 1.0, seed=54, label=f"ratio 1 D{d}", bwd=True)
+        dense = G.gpu_bwd(g, o, lse)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), grads, dense):
+            assert torch.equal(a, b), name
+
+
+def test_block_sparse_backward_long_sequences():
+    # 8448 keys: 33 query blocks, so the tiles' bitmaps take two words
+    _run([8448, 3, 2500], 1, 128, 0.25, seed=55, label="long", bwd=True)
+
+
+def test_block_sparse_backward_production_lengths_reduced():
+    lengths = W.workload_lengths(3, 0, 48).tolist()
+    _run(lengths, 4, 128, 0.5, seed=57, label="production lengths, 48 sequences", bwd=True)
+
+
+def test_block_sparse_backward_full_production_workload_sampled():
+    """Workload 7 (forward + backward) at full size in the launch configuration bench.py
+    times; sampled sequences checked against the oracle."""
+    print("[case] block sparse backward full-size workload 7", flush=True)
+    p = W.make_workload(7, seed=0, device="cuda")
+    ratio = W.WORKLOADS[7]["sparse_ratio"]
+    o, lse, sel = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], ratio, p["scale"])
+    dq, dk, dv = B.bwd_block_sparse(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], ratio,
+                                    sel, p["scale"])
+    torch.cuda.synchronize()
+    gpu_sel, _ = _split_selection(sel, p["lengths"], p["num_heads"], ratio)
+    off = p["offsets_host"].astype(np.int64)
+    order = np.argsort(p["lengths"], kind="stable")
+    for b in sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]), 11, 600}):
+        s, e = int(off[b]), int(off[b + 1])
+        sub = lambda t: G.f64(t[s:e])
+        refs = S.block_sparse_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s],
+                                       [gpu_sel[b]], p["scale"])
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 7 bwd seq {b} (L={e - s})")

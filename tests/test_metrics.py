@@ -46,3 +46,24 @@ def test_block_sparse_pairs_full_selection_is_dense_and_half_is_counted_exactly(
                 want_half += min(256, n - 256 * i) * min(64, n)
     assert M.block_sparse_pairs(lengths, 2, keep, full) == 2 * M.valid_pairs(lengths, M.MODE_SELF)
     assert M.block_sparse_pairs(lengths, 2, [1 if n else 0 for n in lengths], half) == want_half
+
+
+def test_block_sparse_tile_pairs():
+    """Full selection: every tile runs whole, so the executed pairs are the valid pairs.
+    One kept block per query block: the whole 128-key tile that holds it runs."""
+    lengths = [300, 1, 64, 65, 0, 700]
+    keep = [-(-n // 64) if n else 0 for n in lengths]
+    full, one, want_one = [], [], 0
+    for n, kk in zip(lengths, keep):
+        if n == 0:
+            continue
+        nqb = -(-n // 256)
+        for _ in range(2):
+            for i in range(nqb):
+                full += list(range(kk))
+                jb = min(3, kk - 1)       # key block 3 (or the last) -> tile 1 (or 0)
+                one += [jb]
+                t = jb // 2
+                want_one += min(256, n - 256 * i) * min(128, n - 128 * t)
+    assert M.block_sparse_tile_pairs(lengths, 2, keep, full) == 2 * M.valid_pairs(lengths, M.MODE_SELF)
+    assert M.block_sparse_tile_pairs(lengths, 2, [1 if n else 0 for n in lengths], one) == want_one

@@ -76,6 +76,11 @@ def lib():
         L.jfa_fwd_block_sparse.restype = ctypes.c_int
         L.jfa_fwd_block_sparse.argtypes = [sp, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t,
                                            op, vp]
+        L.jfa_bwd_block_sparse_workspace_size.restype = ctypes.c_int
+        L.jfa_bwd_block_sparse_workspace_size.argtypes = [sp, vp, op, ctypes.POINTER(ctypes.c_size_t)]
+        L.jfa_bwd_block_sparse.restype = ctypes.c_int
+        L.jfa_bwd_block_sparse.argtypes = [sp, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
+                                           ctypes.c_size_t, op, vp]
         L.jfa_ds_bytes.restype = ctypes.c_int
         L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
@@ -298,3 +303,41 @@ def fwd_block_sparse(q, k, v, offsets, offsets_host, ratio, scale=None, opts=Non
                                       selection.numel(), _ptr(workspace), workspace.numel(),
                                       ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_fwd_block_sparse")
     return o, lse, selection
+
+
+def bwd_block_sparse_workspace_size(shape, offsets_host, opts=None):
+    """Workspace bytes jfa_bwd_block_sparse needs for these offsets."""
+    out = ctypes.c_size_t()
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_bwd_block_sparse_workspace_size(ctypes.byref(shape), host.ctypes.data,
+                                                     ctypes.byref(opts) if opts else None, ctypes.byref(out)),
+           "jfa_bwd_block_sparse_workspace_size")
+    return out.value
+
+
+def bwd_block_sparse(q, k, v, o, do, lse, offsets, offsets_host, ratio, selection, scale=None, opts=None, dq=None,
+                     dk=None, dv=None, workspace=None, stream=None):
+    """Backward of the block-sparse top-k forward for the selection it wrote.  Returns
+    (dq, dk, dv) with the shapes of (q, k, v)."""
+    import torch
+    nb, h, d, t, _, hkv = _sizes(q, k, v, offsets, MODE_SELF)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    _check_tensor("selection", selection, torch.int32)
+    shape = make_shape(nb, h, d, t, 0, hkv if hkv != h else 0)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        n = bwd_block_sparse_workspace_size(shape, host, opts)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().jfa_bwd_block_sparse(ctypes.byref(shape), scale, float(ratio), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                      _ptr(do), _ptr(lse), _ptr(offsets), host.ctypes.data, _ptr(selection),
+                                      selection.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                      workspace.numel(), ctypes.byref(opts) if opts else None, _stream(stream)),
+           "jfa_bwd_block_sparse")
+    return dq, dk, dv

@@ -324,6 +324,37 @@ int sparse_plan(const jfa_shape* s, const std::vector<int32_t>& lengths, float r
   return JFA_OK;
 }
 
+// Block-sparse backward: the recompute backward's workspace (no dS budget) followed by
+// the selection plan (sel_base, sel_k) and the dK/dV tiles' query-block bitmaps.
+struct SparseBwdLayout {
+  Layout base;
+  size_t sel_base = 0, sel_k = 0, bits_base = 0, bits = 0, total = 0;
+  std::vector<int64_t> bits_prefix;  // [B+1] first bitmap word of each sequence
+};
+
+void sparse_bwd_layout(const jfa_shape* s, const std::vector<int32_t>& lengths, const Opts& o, SparseBwdLayout& S) {
+  Opts plain = o;
+  plain.ds_budget = 0;
+  layout_for(s, JFA_MODE_SELF, JFA_PASS_BWD, plain, S.base);
+  const size_t B = lengths.size();
+  S.bits_prefix.assign(B + 1, 0);
+  for (size_t b = 0; b < B; ++b) {
+    const int64_t len = lengths[b];
+    const int64_t words = cdiv(len, kBwdKeys) * 2 * cdiv(cdiv(len, kSparseQBlock), 32);
+    S.bits_prefix[b + 1] = S.bits_prefix[b] + words * s->num_heads;
+  }
+  size_t at = S.base.total;
+  S.sel_base = at;
+  at += align_up((B + 1) * sizeof(int64_t));
+  S.sel_k = at;
+  at += align_up((B + 1) * sizeof(int32_t));
+  S.bits_base = at;
+  at += align_up((B + 1) * sizeof(int64_t));
+  S.bits = at;
+  at += align_up((size_t)S.bits_prefix.back() * sizeof(uint32_t));
+  S.total = at;
+}
+
 int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
@@ -571,6 +602,125 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   p.sel_k = ps.sel_k;
   return launch_status(timed_launch(JFA_KERNEL_FWD, stream, [&] { return launch_fwd(p, kSelfSparse, D, stream); }),
                        "block-sparse forward launch");
+}
+
+int jfa_bwd_block_sparse_workspace_size(const jfa_shape* shape, const int32_t* offsets_host, const jfa_opts* opts,
+                                        size_t* bytes) {
+  g_detail.clear();
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  if (!offsets_host || !bytes) return fail(JFA_ERR_NULL_POINTER, "offsets_host and bytes must be non-NULL");
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, nullptr, offsets_host, nullptr, lengths))) return rc;
+  SparseBwdLayout S;
+  sparse_bwd_layout(shape, lengths, op, S);
+  *bytes = S.total;
+  return JFA_OK;
+}
+
+int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse,
+                         const int32_t* offsets_dev, const int32_t* offsets_host, const int32_t* selection,
+                         int64_t selection_entries, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q || !k || !v || !o || !dout || !lse || !offsets_dev || !selection || !dq || !dk || !dv || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "tensor, offsets_dev, selection and workspace pointers must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(selection, 4))
+    return fail(JFA_ERR_MISALIGNED, "bf16 tensors must be 16-byte aligned, lse and selection 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  if (kv_heads(shape) != shape->num_heads)
+    return fail(JFA_ERR_BAD_SHAPE, "the backward needs one query head per key/value head (num_kv_heads %d != num_heads %d)",
+                shape->num_kv_heads, shape->num_heads);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  SparsePlan P;
+  if ((rc = sparse_plan(shape, lengths, ratio, P))) return rc;
+  if (selection_entries < P.sel_base.back())
+    return fail(JFA_ERR_CAPACITY, "selection holds %lld entries, %lld needed", (long long)selection_entries,
+                (long long)P.sel_base.back());
+  SparseBwdLayout S;
+  sparse_bwd_layout(shape, lengths, op, S);
+  if (workspace_bytes < S.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, S.total);
+  const Layout& L = S.base;
+  const int H = shape->num_heads, D = shape->head_dim, B = shape->num_seqs;
+  Schedule sc, sq;
+  schedule_bwd(lengths, H, JFA_MODE_SELF, kBwdKeys, max_programs(op, dkdv_wg_per_cu(D)), op.sched == 1, sc);
+  if (sc.tiles.empty()) return JFA_OK;
+  schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDqRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
+  if ((int64_t)sc.tiles.size() > L.tile_cap || (int64_t)sq.tiles.size() > L.tile2_cap)
+    return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  std::vector<char> buf;
+  serialise(sc, L, buf, &sq);
+  char* ws = (char*)workspace;
+  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  // the per-sequence arrays are contiguous: [sel_base | sel_k | bits_base]
+  std::vector<char> arr(S.bits - S.sel_base, 0);
+  memcpy(arr.data(), P.sel_base.data(), (B + 1) * sizeof(int64_t));
+  memcpy(arr.data() + (S.sel_k - S.sel_base), P.sel_k.data(), (B + 1) * sizeof(int32_t));
+  memcpy(arr.data() + (S.bits_base - S.sel_base), S.bits_prefix.data(), (B + 1) * sizeof(int64_t));
+  if ((rc = upload(arr.data(), arr.size(), ws + S.sel_base, stream))) return rc;
+  uint32_t* bits = (uint32_t*)(ws + S.bits);
+  if ((rc = launch_status(launch_fill_zero((float*)bits, S.bits_prefix.back(), stream), "bitmap fill"))) return rc;
+  MarkParams mp{};
+  mp.sel = selection;
+  mp.sel_base = (const int64_t*)(ws + S.sel_base);
+  mp.sel_k = (const int32_t*)(ws + S.sel_k);
+  mp.offsets = offsets_dev;
+  mp.bits_base = (const int64_t*)(ws + S.bits_base);
+  mp.bits = bits;
+  mp.num_seqs = B;
+  mp.num_heads = H;
+  mp.entries = P.sel_base.back();
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_PREP, stream, [&] { return launch_mark(mp, stream); }),
+                          "block-sparse mark launch")))
+    return rc;
+
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.offsets = offsets_dev;
+  p.tiles = (const Tile*)(ws + L.tiles);
+  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.counters = (int32_t*)(ws + L.counters);
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.dq = (uint16_t*)dq;
+  p.row_aug = (uint16_t*)(ws + L.stats);
+  p.dq_tiles = (const Tile*)(ws + L.tiles2);
+  p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
+  p.dq_programs = sq.programs;
+  p.sel = selection;
+  p.sel_base = mp.sel_base;
+  p.sel_k = mp.sel_k;
+  p.sp_bits = bits;
+  p.sp_bits_base = mp.bits_base;
+  p.num_seqs = B;
+  p.num_heads = H;
+  p.num_programs = sc.programs;
+  p.total_tokens = shape->total_tokens;
+  p.dynamic = op.sched;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2eHost;
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq(p, D, stream); }),
+                          "block-sparse dQ launch")))
+    return rc;
+  return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                       "block-sparse dK/dV launch");
 }
 
 int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,

@@ -35,6 +35,14 @@
 // terms, the dK/dV kernel also stores dS (bf16, two bytes per query-key pair) and
 // dq_ds_kernel forms dQ = scale dS K from it -- five products per block plus the dS
 // round trip through HBM instead of seven products.
+//
+// Block-sparse variant (the backward of the block-sparse top-k forward with its
+// selection held fixed): the dQ kernel walks its query block's kept key blocks instead
+// of all of them; the dK/dV kernel walks only the query blocks that kept one of the
+// tile's two 64-key blocks (from a bitmap built by the mark kernel), and where a query
+// block kept only one of them, the waves of the other block turn P (hence dV, dS, dK)
+// to zero through the row-term MFMA: every row term carries -1 in one extra k-slot,
+// which those waves' B operand scales by 1e30.
 #include <algorithm>
 #include <utility>
 
@@ -113,7 +121,9 @@ __device__ __forceinline__ void dq_step(const JFA_LDS char* kbuf, const JFA_LDS 
   }
 }
 
-template <int D>
+// SPARSE: the tile's rows lie in one block-sparse query block, whose kept key blocks
+// (ascending, one 64-key step each) replace the full key range.
+template <int D, bool SPARSE>
 __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, const DqLane<D>& ln,
                                         int tid) {
   using C = DqCfg<D>;
@@ -147,17 +157,18 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
   if (blockIdx.x == 0 && tid == 0) {
     // sentinel row term for query rows past the end of a sequence (P = dS = 0)
     const bf16 z = (bf16)0.0f;
-    const bf16x8 t = {(bf16)(-1e30f), z, z, z, z, z, z, z};
+    const bf16x8 t = {(bf16)(-1e30f), z, (bf16)(-1.0f), z, z, z, z, z};
     st16(p.row_aug + (int64_t)p.num_heads * p.total_tokens * 8, __builtin_bit_cast(u32x4, t));
   }
   if (row_ok && half == 0) {
     // Row term for the dK/dV kernel: -lse log2 e and -Di as bf16 high + low parts
-    // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2).
+    // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2), and the
+    // constant -1 the block-sparse key mask multiplies.
     const float x = -lse * kLog2e, y = -di;
     const bf16 xh = (bf16)x, yh = (bf16)y;
     const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
     const bf16 z = (bf16)0.0f;
-    const bf16x8 t = {xh, xl, z, z, yh, yl, z, z};
+    const bf16x8 t = {xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
     st16(p.row_aug + ((int64_t)h * p.total_tokens + s0 + row) * 8, __builtin_bit_cast(u32x4, t));
   }
 
@@ -167,20 +178,41 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-  const int n_full = L / C::BN, tail = L % C::BN;
-  const int n_kv = n_full + (tail != 0);
+  // Key steps: all of them, or (SPARSE) the kept blocks; only the last step can hold
+  // the sequence's partial block (the kept list is ascending).  List entries are
+  // clamped into [0, nkb) so that no copy leaves the sequence.
+  int n_full = L / C::BN, tail = L % C::BN;
+  int n_kv = n_full + (tail != 0);
+  const int32_t* list = nullptr;
+  const int nkb = (L + C::BN - 1) / C::BN;
+  if constexpr (SPARSE) {
+    static_assert(kSparseKBlock == C::BN && kSparseQBlock % C::BM == 0, "sparse blocks vs dQ tiles");
+    const int nqb = (L + kSparseQBlock - 1) / kSparseQBlock;
+    const int kk = p.sel_k[b];
+    list = p.sel + p.sel_base[b] + ((int64_t)h * nqb + (blk * C::BM) / kSparseQBlock) * kk;
+    const int last = min(max(list[kk - 1], 0), nkb - 1);
+    const bool part = tail != 0 && last == nkb - 1;
+    n_kv = kk;
+    n_full = kk - (part ? 1 : 0);
+    tail = part ? tail : 0;
+  }
+  auto key0_of = [&](int it) { return (SPARSE ? min(max(list[it], 0), nkb - 1) : it) * C::BN; };
   const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
   const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
   const uint32_t rsb = (uint32_t)(rs * 2);
-  ln.copy.issue_rows(kp, rsb, min(C::BN, L), smem, wave, lane);
-  ln.copy.issue_rows(vp, rsb, min(C::BN, L), smem + C::BUF, wave, lane);
+  {
+    const int k0 = key0_of(0);
+    ln.copy.issue_rows(kp + (int64_t)k0 * rs, rsb, min(C::BN, L - k0), smem, wave, lane);
+    ln.copy.issue_rows(vp + (int64_t)k0 * rs, rsb, min(C::BN, L - k0), smem + C::BUF, wave, lane);
+  }
   wait_vmem();
   __syncthreads();
   for (int it = 0; it < n_full; ++it) {
     const int cur = it & 1;
     if (it + 1 < n_kv) {
-      const int64_t nxt = (int64_t)(it + 1) * C::BN * rs;
-      const int rv = min(C::BN, L - (it + 1) * C::BN);
+      const int k1 = key0_of(it + 1);
+      const int64_t nxt = (int64_t)k1 * rs;
+      const int rv = min(C::BN, L - k1);
       JFA_LDS char* nbuf = smem + (cur ^ 1) * 2 * C::BUF;
       ln.copy.issue_rows(kp + nxt, rsb, rv, nbuf, wave, lane);
       ln.copy.issue_rows(vp + nxt, rsb, rv, nbuf + C::BUF, wave, lane);
@@ -338,6 +370,7 @@ struct KvStream {
   f32x16 (&dv)[NDB];
   const int l32;
   const float c;
+  const bf16x8 pick;  // B operand of the S' row-term MFMA (KvLane::pick_s, or the masking one)
   bf16x8 buf[NBUF];
   bf16x8 term;
   f32x16 s, dp;
@@ -357,9 +390,10 @@ struct KvStream {
   __device__ __forceinline__ KvStream(const JFA_LDS char* qt_, const JFA_LDS char* dot_, const JFA_LDS char* augt_,
                                       const KvLane<D>& ln_, const bf16x8 (&kf_)[NKS], const bf16x8 (&vf_)[NKS],
                                       f32x16 (&dk_)[NDB], f32x16 (&dv_)[NDB], int l32_, float c_,
-                                      bf16x8 (&keep_)[C::NQB][2], char* sblk_, uint32_t soff_)
+                                      bf16x8 (&keep_)[C::NQB][2], char* sblk_, uint32_t soff_,
+                                      const bf16x8& pick_)
       : qt(qt_), dot(dot_), augt(augt_), ln(ln_), kf(kf_), vf(vf_), dk(dk_), dv(dv_), l32(l32_), c(c_),
-        keep(keep_), sblk(sblk_), soff(soff_) {}
+        pick(pick_), keep(keep_), sblk(sblk_), soff(soff_) {}
 
   // Store slot of stream position K: query block (0 or 1) * 2 + register x, or -1.
   template <int K>
@@ -406,7 +440,7 @@ struct KvStream {
     constexpr int k = K % PER;
     if constexpr (k == S0) {
       term = buf[K % NBUF];
-      s = mfma32(term, ln.pick_s, f32x16{});
+      s = mfma32(term, pick, f32x16{});
     } else if constexpr (k < DP0) {
       s = mfma32(buf[K % NBUF], kf[k - 1], s);
     } else if constexpr (k == DP0) {
@@ -492,9 +526,48 @@ struct KvStream {
   __device__ __forceinline__ void orders(std::integer_sequence<int, K...>) { (order<K>(), ...); }
 };
 
-template <int D, bool STORE>
+// Block-sparse step list: wave 0 turns the tile's two query-block bitmaps into the
+// ascending list of its 64-row query steps, entry = step | (halves kept) << 24, at
+// steps[0 .. n) with n at steps[kSparseMaxSteps].  Returns n (all waves).
+template <int QB>
+__device__ __forceinline__ int sparse_steps(const BwdParams& p, int b, int h, int j, int L, int nq, JFA_LDS int* steps,
+                                            int wave, int lane) {
+  constexpr int SPQ = kSparseQBlock / QB;  // query steps per query block
+  const int nqb = (L + kSparseQBlock - 1) / kSparseQBlock, nw = (nqb + 31) / 32;
+  const int64_t nj = (L + kBwdKeys - 1) / kBwdKeys;
+  const uint32_t* bm = p.sp_bits + p.sp_bits_base[b] + ((int64_t)h * nj + j) * 2 * nw;
+  __syncthreads();  // the previous tile's readers are done with the list
+  if (wave == 0) {
+    int count = 0;
+    bool last_kept = false;
+    for (int i0 = 0; i0 < nqb; i0 += 64) {
+      const int i = i0 + lane;
+      int m = 0;
+      if (i < nqb) m = ((bm[i >> 5] >> (i & 31)) & 1) | (((bm[nw + (i >> 5)] >> (i & 31)) & 1) << 1);
+      const uint64_t kept = __ballot(m != 0);
+      const int pos = count + __popcll(kept & ((1ull << lane) - 1));
+      if (m != 0) {
+#pragma unroll
+        for (int t = 0; t < SPQ; ++t) {
+          const int it = SPQ * i + t;
+          if (it < nq && SPQ * pos + t < kSparseMaxSteps) steps[SPQ * pos + t] = it | (m << 24);
+        }
+      }
+      count += __popcll(kept);
+      last_kept = last_kept || __ballot(m != 0 && i == nqb - 1) != 0;
+    }
+    if (lane == 0) steps[kSparseMaxSteps] = min(SPQ * count - (last_kept ? SPQ * nqb - nq : 0), kSparseMaxSteps);
+  }
+  __syncthreads();
+  return steps[kSparseMaxSteps];
+}
+
+// SPARSE: only the query steps of the block-sparse step list (see sparse_steps); the
+// waves whose 64-key block a step's query block did not keep use the masking pick.
+template <int D, bool STORE, bool SPARSE>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D>& ln,
                                           int tid) {
+  static_assert(!(STORE && SPARSE), "the block-sparse backward recomputes dS");
   using C = KvCfg<D>;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int lane = tid & 63, wave = tid >> 6;
@@ -540,20 +613,31 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
                 smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
   };
   constexpr int COPIES = 2 * KvLane<D>::Copy::J;
-  issue(0, 0);
-  if (nq > 1) {
-    issue(1, 1);
-    wait_vmem_n<COPIES>();
-  } else {
-    wait_vmem();
+  int n = nq;
+  JFA_LDS int* steps = (JFA_LDS int*)(smem + C::SMEM);
+  bf16x8 pick_mask = ln.pick_s;
+  if constexpr (SPARSE) {
+    static_assert(kSparseKBlock * 2 == C::BN && kSparseQBlock % C::QB == 0, "sparse blocks vs dK/dV tiles");
+    n = sparse_steps<C::QB>(p, b, h, j, L, nq, steps, wave, lane);
+    // k-slot 2 (lanes 0-31) scales the row term's -1 by 1e30: S' -> -1e30, P = 0
+    pick_mask[2] = lane < 32 ? (bf16)1e30f : (bf16)0.0f;
   }
-  __syncthreads();
-
+  auto step_of = [&](int s) { return SPARSE ? (steps[s] & 0xFFFFFF) : s; };
   f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+  if (n > 0) {
+    issue(step_of(0), 0);
+    if (n > 1) {
+      issue(step_of(1), 1);
+      wait_vmem_n<COPIES>();
+    } else {
+      wait_vmem();
+    }
+    __syncthreads();
+  }
 
   // Stored dS: this tile's blocks (j, 0 .. nq-1) and this lane's store offset.  A step's
   // dS is stored during the next step (see KvStream), the last one after the loop.  The
@@ -571,15 +655,17 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     for (int qq = 0; qq < C::NQB; ++qq) keep[qq][0] = keep[qq][1] = as_bf16x8(zero16());
   }
 
-  for (int it = 0, cur = 0; it < nq; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
-    if (it + 2 < nq) issue(it + 2, cur == 0 ? C::NS - 1 : cur - 1);
+  for (int it = 0, cur = 0; it < n; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
+    if (it + 2 < n) issue(step_of(it + 2), cur == 0 ? C::NS - 1 : cur - 1);
     const JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
     const JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
     const JFA_LDS char* augt = smem + C::OFF_AUG + cur * C::ABUF;
+    bool keep_keys = true;
+    if constexpr (SPARSE) keep_keys = ((steps[it] >> (24 + (wave >> 1))) & 1) != 0;
     KvStream<D, STORE>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c, keep,
-                       ds_row + (int64_t)max(it - 1, 0) * kDsBlockBytes, ds_off)
+                       ds_row + (int64_t)max(it - 1, 0) * kDsBlockBytes, ds_off, keep_keys ? ln.pick_s : pick_mask)
         .go();
-    if (it + 2 < nq) wait_vmem_n<COPIES>();
+    if (it + 2 < n) wait_vmem_n<COPIES>();
     else wait_vmem();
     __syncthreads();
   }
@@ -627,7 +713,7 @@ __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles,
   }
 }
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ void __launch_bounds__(kDqWaves * 64)
     __attribute__((amdgpu_waves_per_eu(kDqWgPerCu * kDqWaves / 4, kDqWgPerCu * kDqWaves / 4)))
     dq_kernel(BwdParams p) {
@@ -638,14 +724,15 @@ __global__ void __launch_bounds__(kDqWaves * 64)
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
-            [&](Tile t) { dq_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
+            [&](Tile t) { dq_tile<D, SPARSE>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
-template <int D, bool STORE>
+template <int D, bool STORE, bool SPARSE>
 __global__ void __launch_bounds__(kBwdWaves * 64)
     __attribute__((amdgpu_waves_per_eu(dkdv_wg_per_cu(D) * kBwdWaves / 4, dkdv_wg_per_cu(D) * kBwdWaves / 4)))
     dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM];
+  // SPARSE: the step list (kSparseMaxSteps entries + its length) follows the rings
+  __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM + (SPARSE ? (kSparseMaxSteps + 1) * 4 : 0)];
   __shared__ int next_tile;
   KvLane<D> ln;
   ln.row.init(threadIdx.x & 63);
@@ -653,7 +740,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
-            [&](Tile t) { dkdv_tile<D, STORE>(p, t, smem, ln, threadIdx.x); });
+            [&](Tile t) { dkdv_tile<D, STORE, SPARSE>(p, t, smem, ln, threadIdx.x); });
 }
 
 // --------------------------------------------------------- stored-dS path: row terms
@@ -671,7 +758,7 @@ __global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
   const int sub = threadIdx.x % LPR;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     const bf16 z = (bf16)0.0f;
-    const bf16x8 t = {(bf16)(-1e30f), z, z, z, z, z, z, z};
+    const bf16x8 t = {(bf16)(-1e30f), z, (bf16)(-1.0f), z, z, z, z, z};
     st16(p.row_aug + H * T * 8, __builtin_bit_cast(u32x4, t));
   }
   for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
@@ -688,7 +775,7 @@ __global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
       const bf16 xh = (bf16)x, yh = (bf16)y;
       const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
       const bf16 z = (bf16)0.0f;
-      const bf16x8 v = {xh, xl, z, z, yh, yl, z, z};
+      const bf16x8 v = {xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
       st16(p.row_aug + (h * T + t) * 8, __builtin_bit_cast(u32x4, v));
     }
   }
@@ -881,22 +968,29 @@ __global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per
 
 hipError_t launch_bwd_self_dq(const BwdParams& p, int head_dim, hipStream_t s) {
   if (p.dq_programs <= 0) return hipSuccess;
-  if (head_dim == 64)
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(p.dq_programs), dim3(kDqWaves * 64), 0, s, p);
-  else
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(p.dq_programs), dim3(kDqWaves * 64), 0, s, p);
+  const dim3 grid(p.dq_programs), block(kDqWaves * 64);
+  if (head_dim == 64) {
+    if (p.sel) hipLaunchKernelGGL((dq_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dq_kernel<64, false>), grid, block, 0, s, p);
+  } else {
+    if (p.sel) hipLaunchKernelGGL((dq_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dq_kernel<128, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
   const dim3 grid(p.num_programs), block(kBwdWaves * 64);
+  if (p.ds && p.sel) return hipErrorInvalidValue;  // stored dS and block sparsity do not combine
   if (head_dim == 64) {
-    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dkdv_kernel<64, false>), grid, block, 0, s, p);
+    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<64, true, false>), grid, block, 0, s, p);
+    else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<64, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<64, false, false>), grid, block, 0, s, p);
   } else {
-    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((dkdv_kernel<128, false>), grid, block, 0, s, p);
+    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true, false>), grid, block, 0, s, p);
+    else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<128, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dkdv_kernel<128, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

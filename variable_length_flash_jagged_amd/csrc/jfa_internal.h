@@ -39,6 +39,9 @@ constexpr int kBdWaves = 4;
 constexpr int kSparseQBlock = kFwdRows;
 constexpr int kSparseKBlock = kFwdKeys;
 constexpr int kSparseMaxKeyBlocks = 2048;
+// Block-sparse backward: a dK/dV tile's list of 64-row query steps holds at most this
+// many entries (a sequence of kSparseMaxKeyBlocks key blocks).
+constexpr int kSparseMaxSteps = kSparseMaxKeyBlocks * kSparseKBlock / kBwdRows;
 
 // Persistent workgroups resident per CU (used for the default program count).
 constexpr int kFwdWgPerCu = 1;    // one 8-wave workgroup: 2 waves per SIMD
@@ -106,6 +109,19 @@ struct SelectParams {
   int32_t num_seqs, num_heads, num_kv_heads, nqt, nkb;
 };
 
+// Block-sparse backward: marks, for every selection entry (b, h, query block i, key
+// block kb), bit i of the bitmap of dK/dV tile kb / 2, half kb % 2 (BwdParams::sp_bits).
+struct MarkParams {
+  const int32_t* sel;
+  const int64_t* sel_base;    // [B+1]
+  const int32_t* sel_k;       // [B]
+  const int32_t* offsets;     // [B+1]
+  const int64_t* bits_base;   // [B+1]
+  uint32_t* bits;             // zeroed by the caller
+  int32_t num_seqs, num_heads;
+  int64_t entries;            // sel_base[B]
+};
+
 // Backward (self / broadcast-Q).
 struct BwdParams {
   const uint16_t* q;
@@ -126,6 +142,16 @@ struct BwdParams {
   const Tile* dq_tiles;      // self: query-row tiles of the dQ kernel
   char* ds;                  // self, stored-dS path: dS blocks (null on the recompute path)
   const int64_t* ds_base;    // self, stored-dS path: [B+1] first dS block of each sequence
+  // Block-sparse backward (sel non-null): the forward's selection lists (layout as in
+  // FwdParams) for the dQ kernel, and per dK/dV tile (b, h, j) two bitmaps over the
+  // query blocks of the sequence -- bit i of half x set when query block i kept key
+  // block 2j + x -- at sp_bits[sp_bits_base[b] + ((h nj + j) 2 + x) nw + i / 32],
+  // nj = ceil(L_b / kBwdKeys), nw = ceil(ceil(L_b / kSparseQBlock) / 32).
+  const int32_t* sel;
+  const int64_t* sel_base;
+  const int32_t* sel_k;
+  const uint32_t* sp_bits;
+  const int64_t* sp_bits_base;
   const int32_t* dq_seg_ptr;
   int32_t dq_programs;
   int32_t num_seqs, num_heads, num_q, num_programs;
@@ -176,6 +202,7 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 // Block-sparse variant, stage 1.
 hipError_t launch_pool(const PoolParams& p, int head_dim, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int head_dim, hipStream_t s);
+hipError_t launch_mark(const MarkParams& p, hipStream_t s);
 // dst[i] = bf16(scale * src[i]), i < n (n multiple of 8).
 hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float scale, hipStream_t s);
 // Broadcast-Q partial slabs [P, Mq, D] (programs h*ph .. h*ph+ph-1 hold head h) ->

@@ -122,6 +122,34 @@ __global__ void __launch_bounds__(256) select_kernel(SelectParams p) {
   }
 }
 
+// Block-sparse backward, inverse of the selection: one thread per selection entry sets
+// the bit of its query block in the bitmap of the key block's dK/dV tile half.  Bits
+// are only ever set (atomic OR), so the result does not depend on the order of the
+// threads.  Entries outside [0, nkb) are ignored (they cannot come from the select
+// kernel), so no write leaves the sequence's bitmaps.
+__global__ void __launch_bounds__(256) mark_kernel(MarkParams p) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < p.entries; e += stride) {
+    int lo = 0, hi = p.num_seqs;  // sequence b: sel_base[b] <= e < sel_base[b + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.sel_base[mid] <= e) lo = mid;
+      else hi = mid;
+    }
+    const int b = lo;
+    const int L = p.offsets[b + 1] - p.offsets[b];
+    const int nqb = (L + kSparseQBlock - 1) / kSparseQBlock, nkb = (L + kSparseKBlock - 1) / kSparseKBlock;
+    const int nj = (L + kBwdKeys - 1) / kBwdKeys, nw = (nqb + 31) / 32;
+    const int64_t r = e - p.sel_base[b];
+    const int64_t list = r / p.sel_k[b];
+    const int h = (int)(list / nqb), i = (int)(list - (int64_t)h * nqb);
+    const int kb = p.sel[e];
+    if (kb < 0 || kb >= nkb) continue;
+    uint32_t* w = p.bits + p.bits_base[b] + (((int64_t)h * nj + (kb >> 1)) * 2 + (kb & 1)) * nw + (i >> 5);
+    atomicOr(w, 1u << (i & 31));
+  }
+}
+
 template <class K, class P>
 hipError_t launch_grid(K kernel, const P& p, int64_t waves, hipStream_t s) {
   if (waves <= 0) return hipSuccess;
@@ -140,6 +168,13 @@ hipError_t launch_pool(const PoolParams& p, int head_dim, hipStream_t s) {
 hipError_t launch_select(const SelectParams& p, int head_dim, hipStream_t s) {
   const int64_t waves = (int64_t)p.nqt * p.num_heads;
   return head_dim == 64 ? launch_grid(select_kernel<64>, p, waves, s) : launch_grid(select_kernel<128>, p, waves, s);
+}
+
+hipError_t launch_mark(const MarkParams& p, hipStream_t s) {
+  if (p.entries <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((p.entries + 255) / 256, 8192);
+  hipLaunchKernelGGL(mark_kernel, dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace jfa

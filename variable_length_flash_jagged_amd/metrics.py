@@ -78,3 +78,25 @@ def block_sparse_pairs(lengths, num_heads, keep, selection, q_block=256, k_block
         keys = np.minimum(k_block, n - k_block * blocks).sum(axis=2)  # [H, nqb]
         pairs += int((keys * rows[None, :]).sum())
     return pairs
+
+
+def block_sparse_tile_pairs(lengths, num_heads, keep, selection, q_block=256, k_block=64, tile_keys=128):
+    """Query-key pairs the block-sparse dK/dV kernel executes: it works on tiles of
+    ``tile_keys`` keys (two key blocks), so a query block that kept either block of a
+    tile costs the block's rows times all of the tile's keys (the other block's share is
+    masked to zero)."""
+    sel = np.asarray(selection, dtype=np.int64)
+    pairs, at = 0, 0
+    per_tile = tile_keys // k_block
+    for n, kk in zip(np.asarray(lengths, dtype=np.int64).tolist(), keep):
+        if n == 0:
+            continue
+        nqb = -(-n // q_block)
+        rows = np.minimum(q_block, n - q_block * np.arange(nqb))
+        blocks = sel[at:at + num_heads * nqb * kk].reshape(num_heads, nqb, kk)
+        at += num_heads * nqb * kk
+        for hh in range(num_heads):
+            for i in range(nqb):
+                tiles = np.unique(blocks[hh, i] // per_tile)
+                pairs += int(rows[i] * np.minimum(tile_keys, n - tile_keys * tiles).sum())
+    return pairs

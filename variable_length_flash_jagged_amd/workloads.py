@@ -43,7 +43,7 @@ WORKLOADS = {
     5: dict(name="block_diag", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0),
     6: dict(name="production_jagged_gqa", mode=MODE_SELF, num_heads=4, num_kv_heads=1, head_dim=128, num_q=0,
             fwd_only=True),
-    7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0, fwd_only=True,
+    7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0,
             sparse_ratio=0.5),
 }
 
