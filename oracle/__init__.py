@@ -25,9 +25,12 @@ Modules:
   contiguous divmod ranges) as the bit-exact specification of the host scheduler.
 * ``block_sparse`` -- the block-sparse top-k variant (pooled query and key blocks,
   top-k key blocks per query block, attention over the kept blocks).
+* ``rotary`` -- block-diagonal attention with the rotary position embedding fused in
+  (rotation of q and k, and its transpose on dQ and dK).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_schedule_spec.py`` and ``tests/test_oracle_block_sparse.py`` (worked example printed on the pages, independent
+``tests/test_schedule_spec.py``, ``tests/test_oracle_block_sparse.py`` and
+``tests/test_oracle_rotary.py`` (worked example printed on the pages, independent
 library routines, closed forms, finite differences, brute force).  Nothing here is
 "parity unpinned".
 """
@@ -39,6 +42,7 @@ from .offsets import (  # noqa: F401
     block_offsets,
 )
 from . import block_sparse  # noqa: F401
+from . import rotary  # noqa: F401
 from .attention import (  # noqa: F401
     MODE_SELF,
     MODE_BROADCAST_Q,
