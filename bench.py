@@ -133,7 +133,8 @@ def traffic_bytes(workload, kernel):
     return int(1024 * (k["FETCH_SIZE_kib"] * t["FETCH_SIZE_scale"] + k["WRITE_SIZE_kib"] * t["WRITE_SIZE_scale"]))
 
 
-def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False, sparse_ratio=None):
+def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False, sparse_ratio=None,
+                 rotary=False):
     """Time the fp64 oracle on the first sequences of the same batch (bounded sample)."""
     import numpy as np
     import oracle
@@ -163,9 +164,15 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
             flops += (4 if fwd_only else 14) * head_dim * pairs
             done, b = e, e
             continue
-        oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
-        if not fwd_only:
-            oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
+        if rotary:
+            from oracle import rotary as R
+            tab = R.rope_table(max(1, int(max(lengths[b:e]))), head_dim)
+            R.rotary_block_forward(q, k, v, off, tab, 1.0 / np.sqrt(head_dim))
+            R.rotary_block_backward(q, k, v, do, off, tab, 1.0 / np.sqrt(head_dim))
+        else:
+            oracle.attention_forward(q, k, v, off, mode, 1.0 / np.sqrt(head_dim))
+            if not fwd_only:
+                oracle.attention_backward(q, k, v, do, off, mode, 1.0 / np.sqrt(head_dim))
         spent += time.perf_counter() - t0
         sub = lengths[b:e]
         flops += M.fwd_flops(sub, mode, num_heads, head_dim, num_q)
@@ -178,7 +185,8 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
-                  f"one fp64 {'block-sparse ' if sparse_ratio else ''}{'forward' if fwd_only else 'forward + backward'}"
+                  f"one fp64 {'block-sparse ' if sparse_ratio else 'rotary ' if rotary else ''}"
+                  f"{'forward' if fwd_only else 'forward + backward'}"
                   f" each, {spent:.1f} s",
     }
 
@@ -207,7 +215,9 @@ def main():
     hkv = p["num_kv_heads"]
     fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention: forward only
     ratio = w.get("sparse_ratio")
+    rotary = bool(w.get("rotary", False))
     lengths = p["lengths"]
+    rope = B.rope_table(int(max(lengths)), d, device="cuda") if rotary else None
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
     opts = B.bench_opts(mode, shape, p["offsets_host"], args.sched, args.dq_path, self_bwd=args.self_bwd)
     q, k, v, do, off, off_h = p["q"], p["k"], p["v"], p["do"], p["offsets"], p["offsets_host"]
@@ -239,12 +249,16 @@ def main():
             ev["f0"][i].record()
         if ratio:
             B.fwd_block_sparse(q, k, v, off, off_h, ratio, scale, opts, o, lse, sel, ws_f)
+        elif rotary:
+            B.fwd_rotary(q, k, v, off, off_h, rope, scale, opts, o, lse, ws_f)
         else:
             B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
         if i is not None:
             ev["f1"][i].record()
         if ratio:
             B.bwd_block_sparse(q, k, v, o, do, lse, off, off_h, ratio, sel, scale, opts, dq, dk, dv, ws_b)
+        elif rotary:
+            B.bwd_rotary(q, k, v, o, do, lse, off, off_h, rope, scale, opts, dq, dk, dv, ws_b)
         elif not fwd_only:
             B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
         if i is not None:
@@ -283,6 +297,23 @@ def main():
     ff = M.fwd_flops(lengths, mode, h, d, mq)
     fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
     dense = None
+    plain = None
+    if rotary:
+        # the same batch through the plain block-diagonal kernels, for the rotary's cost
+        evp = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(args.warmup):
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
+            B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
+        plain = [0.0, 0.0]
+        for _ in range(args.steps):
+            evp[0].record()
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
+            evp[1].record()
+            B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
+            evp[2].record()
+            torch.cuda.synchronize()
+            plain[0] += evp[0].elapsed_time(evp[1]) / args.steps
+            plain[1] += evp[1].elapsed_time(evp[2]) / args.steps
     if ratio:
         # attended pairs only; the dense forward and backward of the same batch (the
         # bench's dense options) are timed for context
@@ -414,6 +445,9 @@ def main():
             "dense_fwd_ms": round(dense[0], 4), "speedup_vs_dense_fwd": round(dense[0] / fwd_ms, 3),
             "dense_bwd_ms": round(dense[1], 4), "speedup_vs_dense_bwd": round(dense[1] / bwd_ms, 3),
             "speedup_vs_dense_step": round((dense[0] + dense[1]) / ms_step, 3)},
+        "rotary": None if not rotary else {
+            "table_rows": int(rope.shape[0]), "plain_fwd_ms": round(plain[0], 4), "plain_bwd_ms": round(plain[1], 4),
+            "fwd_cost_vs_plain": round(fwd_ms / plain[0], 3), "bwd_cost_vs_plain": round(bwd_ms / plain[1], 3)},
     }
     if not args.no_cpu_baseline:
         offs = np.asarray(off_h, dtype=np.int64)
@@ -428,7 +462,7 @@ def main():
             return f(q), f(k), f(v), (None if do is None else f(do)), sub_off
 
         out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds,
-                                           fwd_only, ratio)
+                                           fwd_only, ratio, rotary)
     print(json.dumps(out), flush=True)
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 140 /* 1.4.0 */
+#define JFA_VERSION 150 /* 1.5.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -184,6 +184,36 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
                          void* o, float* lse, int32_t* selection, int64_t selection_entries,
                          void* workspace, size_t workspace_bytes,
                          const jfa_opts* opts, void* stream);
+
+/* Block-diagonal attention with a rotary position embedding fused in ("TLX Block
+ * Attention" (bittide page), opening summary: the rotary embedding fused into the
+ * attention kernel, attention plus rotary backward about 3.5x the unfused baseline).
+ * The pages give no formula; this is RoFormer's rotation (Su et al.) in the
+ * rotate-half pairing: for a token at position p inside its own sequence (0 .. L-1)
+ * and i < D/2, the pair (x_i, x_{i+D/2}) of q and of k becomes
+ * (x_i cos - x_{i+D/2} sin, x_{i+D/2} cos + x_i sin) with (cos, sin) =
+ * rope_cos_sin[(p * D/2 + i) * 2 + {0, 1}] (fp32 device array, 16-byte aligned,
+ * caller-owned; usually cos and sin of p * base^(-2i/D)).  The forward returns
+ * attention(rope(q), rope(k), v) with lse; the backward returns the gradients with
+ * respect to the un-rotated q and k (the rotation's transpose applied to dQ and dK in
+ * the kernel) and v.  mode must be JFA_MODE_BLOCK_DIAG (JFA_ERR_BAD_MODE otherwise);
+ * rope_positions (rows of the table) must be at least the longest sequence
+ * (JFA_ERR_BAD_SHAPE).  Workspace and all other conventions as jfa_fwd / jfa_bwd. */
+int jfa_fwd_rotary(const jfa_shape* shape, int mode, float scale,
+                   const void* q, const void* k, const void* v,
+                   const float* rope_cos_sin, int32_t rope_positions,
+                   const int32_t* offsets_dev, const int32_t* offsets_host,
+                   void* o, float* lse,
+                   void* workspace, size_t workspace_bytes,
+                   const jfa_opts* opts, void* stream);
+int jfa_bwd_rotary(const jfa_shape* shape, int mode, float scale,
+                   const void* q, const void* k, const void* v,
+                   const void* o, const void* dout, const float* lse,
+                   const float* rope_cos_sin, int32_t rope_positions,
+                   const int32_t* offsets_dev, const int32_t* offsets_host,
+                   void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   const jfa_opts* opts, void* stream);
 
 /* Block-sparse top-k self attention, backward: the gradient of sum(O * dout) for the
  * forward of jfa_fwd_block_sparse with its selection held fixed (the pooling and top-k

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 140
+    assert lib.jfa_version() == 150
 
 
 def test_error_strings():
@@ -258,3 +258,31 @@ def test_block_sparse_backward_argument_errors_before_device_work():
     ws = B.bwd_block_sparse_workspace_size(shape, off)
     assert _sparse_bwd_rc(shape, off, ws_bytes=ws - 1) == -7
     assert _sparse_bwd_rc(shape, np.array([0, 299], np.int32)) == -5
+
+
+def _rotary_rc(fn, shape, mode, off, rows, ptr=1 << 20):
+    lib = B.lib()
+    p = ctypes.c_void_p(ptr)
+    if fn == "fwd":
+        return lib.jfa_fwd_rotary(ctypes.byref(shape), mode, 0.125, p, p, p, p, rows, p, off.ctypes.data, p, p, p,
+                                  1 << 40, None, None)
+    return lib.jfa_bwd_rotary(ctypes.byref(shape), mode, 0.125, p, p, p, p, p, p, p, rows, p, off.ctypes.data, p, p,
+                              p, p, 1 << 40, None, None)
+
+
+@pytest.mark.parametrize("fn", ["fwd", "bwd"])
+def test_rotary_argument_errors_before_device_work(fn):
+    off = np.array([0, 300, 364], dtype=np.int32)
+    shape = B.make_shape(2, 2, 64, 364)
+    assert _rotary_rc(fn, shape, 0, off, 300) == -4          # self mode: not built
+    assert _rotary_rc(fn, shape, 2, off, 299) == -2          # table shorter than the longest sequence
+    assert b"rope_positions" in B.lib().jfa_last_error_detail()
+    assert _rotary_rc(fn, shape, 2, off, 300, ptr=0) == -1   # NULL table (and tensors)
+    assert _rotary_rc(fn, shape, 2, off, 300, ptr=(1 << 20) + 4) == -6
+
+
+def test_rope_table_values():
+    tab = B.rope_table(5, 8).numpy()
+    assert tab.shape == (5, 4, 2) and tab.dtype == np.float32
+    np.testing.assert_allclose(tab[3, 0], [np.cos(3.0), np.sin(3.0)], rtol=1e-7)
+    np.testing.assert_allclose(tab[4, 2], [np.cos(0.04), np.sin(0.04)], rtol=1e-7)

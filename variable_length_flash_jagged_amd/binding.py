@@ -81,6 +81,12 @@ def lib():
         L.jfa_bwd_block_sparse.restype = ctypes.c_int
         L.jfa_bwd_block_sparse.argtypes = [sp, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
                                            ctypes.c_size_t, op, vp]
+        L.jfa_fwd_rotary.restype = ctypes.c_int
+        L.jfa_fwd_rotary.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, op, vp]
+        L.jfa_bwd_rotary.restype = ctypes.c_int
+        L.jfa_bwd_rotary.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
+                                     vp, vp, vp, ctypes.c_size_t, op, vp]
         L.jfa_ds_bytes.restype = ctypes.c_int
         L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
@@ -340,4 +346,69 @@ def bwd_block_sparse(q, k, v, o, do, lse, offsets, offsets_host, ratio, selectio
                                       selection.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                       workspace.numel(), ctypes.byref(opts) if opts else None, _stream(stream)),
            "jfa_bwd_block_sparse")
+    return dq, dk, dv
+
+
+def rope_table(max_positions, head_dim, base=10000.0, device=None):
+    """The cos / sin table jfa_fwd_rotary takes: [max_positions, D/2, 2] fp32 with
+    (cos, sin) of p * base^(-2i/D), formed in float64 and rounded once."""
+    import torch
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(max_positions, dtype=np.float64)[:, None] * np.power(float(base), -2.0 * i / head_dim)[None, :]
+    tab = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(tab))
+    return t.to(device) if device is not None else t
+
+
+def fwd_rotary(q, k, v, offsets, offsets_host, rope, scale=None, opts=None, o=None, lse=None, workspace=None,
+               stream=None, mode=MODE_BLOCK_DIAG):
+    """Block-diagonal forward of rope(q), rope(k), v; rope from rope_table().  Returns (o, lse)."""
+    import torch
+    nb, h, d, t, _, hkv = _sizes(q, k, v, offsets, mode)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("rope", rope, torch.float32)
+    if rope.dim() != 3 or rope.shape[1:] != (d // 2, 2):
+        raise ValueError(f"rope must be [P, {d // 2}, 2], got {tuple(rope.shape)}")
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, 0, hkv if hkv != h else 0)
+    o = torch.empty((t, h, d), dtype=torch.bfloat16, device=q.device) if o is None else o
+    lse = torch.empty((h, t), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("o", o, torch.bfloat16, (t, h, d))
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    if workspace is None:
+        workspace = alloc_workspace(shape, mode, PASS_FWD, opts, q.device)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_fwd_rotary(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
+                                rope.shape[0], _ptr(offsets), host.ctypes.data, _ptr(o), _ptr(lse), _ptr(workspace),
+                                workspace.numel(), ctypes.byref(opts) if opts else None, _stream(stream)),
+           "jfa_fwd_rotary")
+    return o, lse
+
+
+def bwd_rotary(q, k, v, o, do, lse, offsets, offsets_host, rope, scale=None, opts=None, dq=None, dk=None, dv=None,
+               workspace=None, stream=None, mode=MODE_BLOCK_DIAG):
+    """Backward of fwd_rotary: gradients with respect to the un-rotated q, k and v."""
+    import torch
+    nb, h, d, t, _, hkv = _sizes(q, k, v, offsets, mode)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    _check_tensor("rope", rope, torch.float32)
+    if rope.dim() != 3 or rope.shape[1:] != (d // 2, 2):
+        raise ValueError(f"rope must be [P, {d // 2}, 2], got {tuple(rope.shape)}")
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, 0, hkv if hkv != h else 0)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = alloc_workspace(shape, mode, PASS_BWD, opts, q.device)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_bwd_rotary(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                _ptr(lse), _ptr(rope), rope.shape[0], _ptr(offsets), host.ctypes.data, _ptr(dq),
+                                _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_bwd_rotary")
     return dq, dk, dv

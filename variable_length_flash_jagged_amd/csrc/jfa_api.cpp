@@ -355,6 +355,17 @@ void sparse_bwd_layout(const jfa_shape* s, const std::vector<int32_t>& lengths, 
   S.total = at;
 }
 
+// Fused rotary embedding: a [rope_positions][D/2][2] fp32 cos/sin table, 16-byte
+// aligned, covering every position (0 .. L-1 of each sequence).
+int check_rope(const float* rope, int32_t rope_positions, const std::vector<int32_t>& lengths) {
+  if (!aligned(rope, 16)) return fail(JFA_ERR_MISALIGNED, "rope_cos_sin must be 16-byte aligned");
+  int32_t max_len = 0;
+  for (int32_t len : lengths) max_len = std::max(max_len, len);
+  if (rope_positions < max_len)
+    return fail(JFA_ERR_BAD_SHAPE, "rope_positions %d < longest sequence %d", rope_positions, max_len);
+  return JFA_OK;
+}
+
 int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
@@ -763,13 +774,17 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
   return JFA_OK;
 }
 
-int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
-            const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse, void* workspace,
-            size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+// jfa_fwd, and jfa_fwd_rotary with rope non-null (block-diagonal mode only).
+static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+                     const float* rope, int32_t rope_positions, const int32_t* offsets_dev,
+                     const int32_t* offsets_host, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     const jfa_opts* opts, void* stream_) {
   g_detail.clear();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
   if (rc) return rc;
+  if (rope && mode != JFA_MODE_BLOCK_DIAG)
+    return fail(JFA_ERR_BAD_MODE, "the fused rotary embedding is built for the block-diagonal mode only");
   Opts op;
   if ((rc = check_opts(opts, op))) return rc;
   if (!q || !k || !v || !o || !lse || !offsets_dev || !workspace)
@@ -784,6 +799,7 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
   std::vector<int32_t> lengths;
   if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  if (rope && (rc = check_rope(rope, rope_positions, lengths))) return rc;
   char* ws = (char*)workspace;
   const int H = shape->num_heads, D = shape->head_dim;
 
@@ -809,6 +825,7 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
+    p.rope = rope;
     return launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_bd_fwd(p, D, stream); }),
                          "block-diagonal forward launch");
   }
@@ -842,14 +859,36 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
                        "forward launch");
 }
 
-int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
-            const void* o, const void* dout, const float* lse, const int32_t* offsets_dev,
-            const int32_t* offsets_host, void* dq, void* dk, void* dv, void* workspace,
-            size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+            const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse, void* workspace,
+            size_t workspace_bytes, const jfa_opts* opts, void* stream) {
+  return fwd_entry(shape, mode, scale, q, k, v, nullptr, 0, offsets_dev, offsets_host, o, lse, workspace,
+                   workspace_bytes, opts, stream);
+}
+
+int jfa_fwd_rotary(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+                   const float* rope_cos_sin, int32_t rope_positions, const int32_t* offsets_dev,
+                   const int32_t* offsets_host, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                   const jfa_opts* opts, void* stream) {
+  if (!rope_cos_sin) {
+    g_detail.clear();
+    return fail(JFA_ERR_NULL_POINTER, "rope_cos_sin is NULL");
+  }
+  return fwd_entry(shape, mode, scale, q, k, v, rope_cos_sin, rope_positions, offsets_dev, offsets_host, o, lse,
+                   workspace, workspace_bytes, opts, stream);
+}
+
+// jfa_bwd, and jfa_bwd_rotary with rope non-null (block-diagonal mode only).
+static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse, const float* rope, int32_t rope_positions,
+                     const int32_t* offsets_dev, const int32_t* offsets_host, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
   if (rc) return rc;
+  if (rope && mode != JFA_MODE_BLOCK_DIAG)
+    return fail(JFA_ERR_BAD_MODE, "the fused rotary embedding is built for the block-diagonal mode only");
   Opts op;
   if ((rc = check_opts(opts, op))) return rc;
   if (!q || !k || !v || !o || !dout || !lse || !offsets_dev || !dq || !dk || !dv || !workspace)
@@ -868,6 +907,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
   std::vector<int32_t> lengths;
   if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  if (rope && (rc = check_rope(rope, rope_positions, lengths))) return rc;
   char* ws = (char*)workspace;
   const int H = shape->num_heads, D = shape->head_dim;
   const int64_t T = shape->total_tokens;
@@ -898,6 +938,7 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
     p.num_programs = (int)std::min<int64_t>(max_programs(op, kBdWgPerCu), cdiv(ntiles, kBdWaves));
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
+    p.rope = rope;
     return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bd_bwd(p, D, stream); }),
                          "block-diagonal backward launch");
   }
@@ -1001,6 +1042,27 @@ int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
   if (partials)
     return launch_status(launch_dq_reduce(acc, (uint16_t*)dq, (int)Mq, H, D, ph, scale, stream), "dq reduce");
   return launch_status(launch_cast_scale(acc, (uint16_t*)dq, acc_elems, scale, stream), "dq cast");
+}
+
+int jfa_bwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+            const void* o, const void* dout, const float* lse, const int32_t* offsets_dev,
+            const int32_t* offsets_host, void* dq, void* dk, void* dv, void* workspace,
+            size_t workspace_bytes, const jfa_opts* opts, void* stream) {
+  return bwd_entry(shape, mode, scale, q, k, v, o, dout, lse, nullptr, 0, offsets_dev, offsets_host, dq, dk, dv,
+                   workspace, workspace_bytes, opts, stream);
+}
+
+int jfa_bwd_rotary(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+                   const void* o, const void* dout, const float* lse, const float* rope_cos_sin,
+                   int32_t rope_positions, const int32_t* offsets_dev, const int32_t* offsets_host, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes, const jfa_opts* opts,
+                   void* stream) {
+  if (!rope_cos_sin) {
+    g_detail.clear();
+    return fail(JFA_ERR_NULL_POINTER, "rope_cos_sin is NULL");
+  }
+  return bwd_entry(shape, mode, scale, q, k, v, o, dout, lse, rope_cos_sin, rope_positions, offsets_dev,
+                   offsets_host, dq, dk, dv, workspace, workspace_bytes, opts, stream);
 }
 
 }  // extern "C"

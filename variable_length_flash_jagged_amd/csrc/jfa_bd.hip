@@ -19,6 +19,16 @@
 // block prefix sums.  Differences from the page's kernel: the backward reads the
 // forward's lse (4 bytes per row, about 1% of the traffic) instead of recomputing the
 // row maxima, because on this layout the keys of a row are spread across lanes.
+//
+// Fused rotary embedding (BdParams::rope non-null; the same page's opening summary
+// reports the attention plus rotary backward fused into the attention kernel).  The
+// rotation (RoFormer's: pair (x_i, x_{i+D/2}) turned by the angle p theta_i, p the
+// token's index inside its sequence, cos and sin from the caller's table) is applied
+// where q and k enter the kernel -- to the register fragments in the forward, to the
+// Q and K LDS tiles in the backward (one lane per row, before any product reads them)
+// -- and its transpose is applied to the dQ and dK accumulators before they are stored,
+// so the caller receives the gradients with respect to the un-rotated q and k.  On
+// both layouts a column c < D/2 and its partner c + D/2 sit in the same lane.
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -43,6 +53,7 @@ struct BdTile {
   int64_t t0;  // first token of the block
   int n;       // rows in the block (1..64)
   int h;
+  int pos0;    // position of the block's first token inside its sequence
 };
 
 // Tile g -> (block, head); block -> (sequence b, block j) by binary search over the
@@ -62,10 +73,107 @@ __device__ __forceinline__ BdTile locate(const BdParams& p, int64_t g) {
   const int L = (int)(p.offsets[lo + 1] - s0);
   t.t0 = s0 + (int64_t)j * kBlock;
   t.n = min(kBlock, L - j * kBlock);
+  t.pos0 = j * kBlock;
   return t;
 }
 
+// (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin), and its transpose.
+__device__ __forceinline__ void rot2(float& x1, float& x2, float c, float s) {
+  const float y1 = fmaf(x1, c, -x2 * s), y2 = fmaf(x2, c, x1 * s);
+  x1 = y1;
+  x2 = y2;
+}
+
+// Eight (cos, sin) pairs of table row `tab` starting at pair i0.
+__device__ __forceinline__ void rope_pairs8(const float* tab, int i0, float (&cs)[16]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 w = *reinterpret_cast<const float4*>(tab + 2 * i0 + 4 * u);
+    cs[4 * u] = w.x;
+    cs[4 * u + 1] = w.y;
+    cs[4 * u + 2] = w.z;
+    cs[4 * u + 3] = w.w;
+  }
+}
+
+// Forward: rotate this lane's q and k fragments of one row (columns 16 ks + 8 half + e;
+// column c < D/2 is in fragment ks < NKS/2, its partner in fragment ks + NKS/2).
+template <int NKS>
+__device__ __forceinline__ void rope_fragments(bf16x8 (&a)[NKS], bf16x8 (&b)[NKS], const float* tab, int half) {
+#pragma unroll
+  for (int ks = 0; ks < NKS / 2; ++ks) {
+    float cs[16];
+    rope_pairs8(tab, 16 * ks + 8 * half, cs);
+    float a1[8], a2[8], b1[8], b2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a1[e] = (float)a[ks][e];
+      a2[e] = (float)a[ks + NKS / 2][e];
+      b1[e] = (float)b[ks][e];
+      b2[e] = (float)b[ks + NKS / 2][e];
+      rot2(a1[e], a2[e], cs[2 * e], cs[2 * e + 1]);
+      rot2(b1[e], b2[e], cs[2 * e], cs[2 * e + 1]);
+    }
+    a[ks] = pack8(a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]);
+    a[ks + NKS / 2] = pack8(a2[0], a2[1], a2[2], a2[3], a2[4], a2[5], a2[6], a2[7]);
+    b[ks] = pack8(b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]);
+    b[ks + NKS / 2] = pack8(b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]);
+  }
+}
+
+// Backward: rotate row r of the swizzled Q and K LDS tiles in place (chunk c of 8
+// columns pairs with chunk c + D/16).
 template <int D>
+__device__ __forceinline__ void rope_lds_row(JFA_LDS char* qt, JFA_LDS char* kt, const float* tab, int r) {
+  constexpr int RB = 2 * D, NC = D / 16;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float cs[16];
+    rope_pairs8(tab, 8 * c, cs);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      JFA_LDS char* tile = tt == 0 ? qt : kt;
+      const bf16x8 x = as_bf16x8(lds_ld16(tile, swz_off<RB>(r, c)));
+      const bf16x8 y = as_bf16x8(lds_ld16(tile, swz_off<RB>(r, c + NC)));
+      float x1[8], x2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x1[e] = (float)x[e];
+        x2[e] = (float)y[e];
+        rot2(x1[e], x2[e], cs[2 * e], cs[2 * e + 1]);
+      }
+      lds_st16(tile, swz_off<RB>(r, c),
+               __builtin_bit_cast(u32x4, pack8(x1[0], x1[1], x1[2], x1[3], x1[4], x1[5], x1[6], x1[7])));
+      lds_st16(tile, swz_off<RB>(r, c + NC),
+               __builtin_bit_cast(u32x4, pack8(x2[0], x2[1], x2[2], x2[3], x2[4], x2[5], x2[6], x2[7])));
+    }
+  }
+}
+
+// Backward epilogue: the transpose rotation on dQ^T / dK^T accumulators (register i of
+// block db <-> column 32 db + 8 (i/4) + 4 half + i%4; partner in block db + NDB/2).
+template <int NDB>
+__device__ __forceinline__ void unrope_acc(f32x16 (&g)[NDB], const float* tab, int half) {
+#pragma unroll
+  for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c0 = 32 * db + 8 * g4 + 4 * half;
+      const float4 w0 = *reinterpret_cast<const float4*>(tab + 2 * c0);
+      const float4 w1 = *reinterpret_cast<const float4*>(tab + 2 * c0 + 4);
+      const float cs[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g4 + e;
+        float x1 = g[db][i], x2 = g[db + NDB / 2][i];
+        rot2(x1, x2, cs[2 * e], -cs[2 * e + 1]);
+        g[db][i] = x1;
+        g[db + NDB / 2][i] = x2;
+      }
+    }
+}
+
+template <int D, bool ROPE>
 __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* vt, int lane) {
   using C = BdCfg<D>;
   const int l32 = lane & 31, half = lane >> 5;
@@ -87,6 +195,9 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
     for (int ks = 0; ks < C::NKS; ++ks) {
       qf[bb][ks] = as_bf16x8(row < n ? ld16(qp + 16 * ks) : zero16());
       kf[bb][ks] = as_bf16x8(row < n ? ld16(kp + 16 * ks) : zero16());
+    }
+    if constexpr (ROPE) {
+      if (row < n) rope_fragments<C::NKS>(qf[bb], kf[bb], p.rope + (int64_t)(t.pos0 + row) * D, half);
     }
   }
   // S^T = K Q^T, lane = query column.
@@ -161,7 +272,7 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
   }
 }
 
-template <int D>
+template <int D, bool ROPE>
 __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* w, float* wf,
                                             int lane) {
   using C = BdCfg<D>;
@@ -181,6 +292,12 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
   dma_tile<C::RB, kBlock, 1>(p.dout + base, rs, n, dot, 0, lane);
   const float lv = lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f;
   wait_vmem();
+  if constexpr (ROPE) {
+    // rows past the block's end stay as copied (their P and dS are zero)
+    if (lane < n) rope_lds_row<D>(qt, kt, p.rope + (int64_t)(t.pos0 + lane) * D, lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+  }
   // Di = rowsum(dO * O): lane = row of query block qb, half = which 8-column chunks.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -267,6 +384,7 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
       }
     }
     if (key_ok) {
+      if constexpr (ROPE) unrope_acc<C::NDB>(dk, p.rope + (int64_t)(t.pos0 + key) * D, half);
       const int64_t row = base + key * rs + 4 * half;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -294,6 +412,7 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
                         dq[db]);
     }
     if (row < n) {
+      if constexpr (ROPE) unrope_acc<C::NDB>(dq, p.rope + (int64_t)(t.pos0 + row) * D, half);
       uint16_t* qp = p.o + base + row * rs + 4 * half;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -307,8 +426,10 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
 
 // Program p owns tiles [p*q + min(p, r), (p+1)*q + min(p+1, r)), (q, r) = divmod(N, P);
 // its waves take every NW-th tile of the range.
-template <int D>
-__global__ void __launch_bounds__(BdCfg<D>::NW * 64) bd_fwd_kernel(BdParams p) {
+// Two waves per SIMD at D = 64 (the rotary variant needs the cap to stay there).
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(BdCfg<D>::NW * 64)
+    __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) bd_fwd_kernel(BdParams p) {
   using C = BdCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::NW * C::TBUF];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -316,10 +437,10 @@ __global__ void __launch_bounds__(BdCfg<D>::NW * 64) bd_fwd_kernel(BdParams p) {
   const int64_t P = gridDim.x, q = p.num_tiles / P, r = p.num_tiles % P;
   const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
   JFA_LDS char* vt = (JFA_LDS char*)smem + wave * C::TBUF;
-  for (int64_t g = start + wave; g < end; g += C::NW) bd_fwd_tile<D>(p, locate(p, g), vt, lane);
+  for (int64_t g = start + wave; g < end; g += C::NW) bd_fwd_tile<D, ROPE>(p, locate(p, g), vt, lane);
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(BdCfg<D>::NW * 64)
     __attribute__((amdgpu_waves_per_eu(1, 1))) bd_bwd_kernel(BdParams p) {
   using C = BdCfg<D>;
@@ -330,7 +451,7 @@ __global__ void __launch_bounds__(BdCfg<D>::NW * 64)
   const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
   char* w = smem + wave * C::W_BWD;
   for (int64_t g = start + wave; g < end; g += C::NW)
-    bd_bwd_tile<D>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
+    bd_bwd_tile<D, ROPE>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
 }
 
 int bd_programs(const BdParams& p, int nw) {
@@ -342,20 +463,28 @@ int bd_programs(const BdParams& p, int nw) {
 
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s) {
   if (p.num_tiles <= 0) return hipSuccess;
+  const dim3 g64(bd_programs(p, BdCfg<64>::NW)), b64(BdCfg<64>::NW * 64);
+  const dim3 g128(bd_programs(p, BdCfg<128>::NW)), b128(BdCfg<128>::NW * 64);
   if (head_dim == 64) {
-    hipLaunchKernelGGL(bd_fwd_kernel<64>, dim3(bd_programs(p, BdCfg<64>::NW)), dim3(BdCfg<64>::NW * 64), 0, s, p);
+    if (p.rope) hipLaunchKernelGGL((bd_fwd_kernel<64, true>), g64, b64, 0, s, p);
+    else hipLaunchKernelGGL((bd_fwd_kernel<64, false>), g64, b64, 0, s, p);
   } else {
-    hipLaunchKernelGGL(bd_fwd_kernel<128>, dim3(bd_programs(p, BdCfg<128>::NW)), dim3(BdCfg<128>::NW * 64), 0, s, p);
+    if (p.rope) hipLaunchKernelGGL((bd_fwd_kernel<128, true>), g128, b128, 0, s, p);
+    else hipLaunchKernelGGL((bd_fwd_kernel<128, false>), g128, b128, 0, s, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s) {
   if (p.num_tiles <= 0) return hipSuccess;
+  const dim3 g64(bd_programs(p, BdCfg<64>::NW)), b64(BdCfg<64>::NW * 64);
+  const dim3 g128(bd_programs(p, BdCfg<128>::NW)), b128(BdCfg<128>::NW * 64);
   if (head_dim == 64) {
-    hipLaunchKernelGGL(bd_bwd_kernel<64>, dim3(bd_programs(p, BdCfg<64>::NW)), dim3(BdCfg<64>::NW * 64), 0, s, p);
+    if (p.rope) hipLaunchKernelGGL((bd_bwd_kernel<64, true>), g64, b64, 0, s, p);
+    else hipLaunchKernelGGL((bd_bwd_kernel<64, false>), g64, b64, 0, s, p);
   } else {
-    hipLaunchKernelGGL(bd_bwd_kernel<128>, dim3(bd_programs(p, BdCfg<128>::NW)), dim3(BdCfg<128>::NW * 64), 0, s, p);
+    if (p.rope) hipLaunchKernelGGL((bd_bwd_kernel<128, true>), g128, b128, 0, s, p);
+    else hipLaunchKernelGGL((bd_bwd_kernel<128, false>), g128, b128, 0, s, p);
   }
   return hipGetLastError();
 }

@@ -183,6 +183,9 @@ struct BdParams {
   int64_t num_tiles;  // blocks * heads
   float scale;
   float scale_log2;
+  // fused rotary embedding (null: none): cos, sin of p theta_i at rope[(p D/2 + i) 2 + {0, 1}],
+  // p = position inside the sequence, i < D/2; q, k pairs (i, i + D/2) are rotated
+  const float* rope;
 };
 
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.

@@ -19,8 +19,10 @@ generators stand in for them):
    n ~ U{1..63}, H=4, D=64.
 6. ``production_jagged_gqa``: the lengths of workload 3 with H=4 query heads sharing
    one key/value head (grouped-query attention, forward only).
-7. ``production_jagged_sparse``: workload 3 through the block-sparse top-k forward at
-   ratio 0.5 (forward only).
+7. ``production_jagged_sparse``: workload 3 through the block-sparse top-k forward and
+   backward at ratio 0.5.
+8. ``block_diag_rotary``: workload 5 with the rotary position embedding fused into the
+   block-diagonal attention (cos/sin table of the longest sequence's positions).
 
 Draw order: lengths (numpy ``default_rng(seed)``), then q, k, v, dO from one
 ``torch.Generator`` seeded with ``seed`` on the target device, each drawn in fp32 and
@@ -45,6 +47,7 @@ WORKLOADS = {
             fwd_only=True),
     7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0,
             sparse_ratio=0.5),
+    8: dict(name="block_diag_rotary", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0, rotary=True),
 }
 
 
@@ -66,7 +69,7 @@ def workload_lengths(workload, seed=0, num_seqs=None):
     if workload == 4:
         n = 16 if num_seqs is None else num_seqs
         return np.full(n, 4096, dtype=np.int64)
-    if workload == 5:
+    if workload in (5, 8):
         n = 1152 if num_seqs is None else num_seqs
         return (64 * rng.integers(1, 64, size=n)).astype(np.int64)
     raise ValueError(f"unknown workload {workload}")
