@@ -96,14 +96,21 @@ __device__ __forceinline__ void rope_pairs8(const float* tab, int i0, float (&cs
   }
 }
 
+// Forward: the (cos, sin) pairs of this lane's columns of one row: pairs 16 ks + 8 half
+// + e, ks < NKS/2.
+template <int NKS>
+__device__ __forceinline__ void rope_row_pairs(const float* tab, int half, float (&cs)[NKS / 2][16]) {
+#pragma unroll
+  for (int ks = 0; ks < NKS / 2; ++ks) rope_pairs8(tab, 16 * ks + 8 * half, cs[ks]);
+}
+
 // Forward: rotate this lane's q and k fragments of one row (columns 16 ks + 8 half + e;
 // column c < D/2 is in fragment ks < NKS/2, its partner in fragment ks + NKS/2).
 template <int NKS>
-__device__ __forceinline__ void rope_fragments(bf16x8 (&a)[NKS], bf16x8 (&b)[NKS], const float* tab, int half) {
+__device__ __forceinline__ void rope_fragments(bf16x8 (&a)[NKS], bf16x8 (&b)[NKS], const float (&pairs)[NKS / 2][16]) {
 #pragma unroll
   for (int ks = 0; ks < NKS / 2; ++ks) {
-    float cs[16];
-    rope_pairs8(tab, 16 * ks + 8 * half, cs);
+    const float (&cs)[16] = pairs[ks];
     float a1[8], a2[8], b1[8], b2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -123,13 +130,21 @@ __device__ __forceinline__ void rope_fragments(bf16x8 (&a)[NKS], bf16x8 (&b)[NKS
 
 // Backward: rotate row r of the swizzled Q and K LDS tiles in place (chunk c of 8
 // columns pairs with chunk c + D/16).
-template <int D>
-__device__ __forceinline__ void rope_lds_row(JFA_LDS char* qt, JFA_LDS char* kt, const float* tab, int r) {
+// PRE: the row's pairs were loaded into `pre` beforehand; otherwise they are loaded
+// from `tab` chunk by chunk.
+template <int D, bool PRE>
+__device__ __forceinline__ void rope_lds_row(JFA_LDS char* qt, JFA_LDS char* kt, const float* tab,
+                                             const float (&pre)[PRE ? D / 16 : 1][16], int r) {
   constexpr int RB = 2 * D, NC = D / 16;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float cs[16];
-    rope_pairs8(tab, 8 * c, cs);
+    if constexpr (PRE) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cs[u] = pre[c][u];
+    } else {
+      rope_pairs8(tab, 8 * c, cs);
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       JFA_LDS char* tile = tt == 0 ? qt : kt;
@@ -150,10 +165,10 @@ __device__ __forceinline__ void rope_lds_row(JFA_LDS char* qt, JFA_LDS char* kt,
   }
 }
 
-// Backward epilogue: the transpose rotation on dQ^T / dK^T accumulators (register i of
-// block db <-> column 32 db + 8 (i/4) + 4 half + i%4; partner in block db + NDB/2).
+// Backward epilogue: the (cos, sin) pairs of a row's accumulator columns (register i of
+// block db <-> column 32 db + 8 (i/4) + 4 half + i%4, db < NDB/2).
 template <int NDB>
-__device__ __forceinline__ void unrope_acc(f32x16 (&g)[NDB], const float* tab, int half) {
+__device__ __forceinline__ void acc_pairs(const float* tab, int half, float (&cs)[NDB / 2][4][8]) {
 #pragma unroll
   for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
@@ -161,7 +176,21 @@ __device__ __forceinline__ void unrope_acc(f32x16 (&g)[NDB], const float* tab, i
       const int c0 = 32 * db + 8 * g4 + 4 * half;
       const float4 w0 = *reinterpret_cast<const float4*>(tab + 2 * c0);
       const float4 w1 = *reinterpret_cast<const float4*>(tab + 2 * c0 + 4);
-      const float cs[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cs[db][g4][u] = v[u];
+    }
+}
+
+// The transpose rotation on dQ^T / dK^T accumulators (partner of block db is block
+// db + NDB/2, same register).
+template <int NDB>
+__device__ __forceinline__ void unrope_acc(f32x16 (&g)[NDB], const float (&pairs)[NDB / 2][4][8]) {
+#pragma unroll
+  for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float (&cs)[8] = pairs[db][g4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g4 + e;
@@ -185,6 +214,17 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
   const float c = p.scale_log2;
   dma_tile<C::RB, kBlock, 1>(p.v + kvbase, rkv, n, vt, 0, lane);
 
+  // D = 64: the table pairs of both rows are loaded before q and k, so their latency
+  // overlaps (at D = 128 the registers are not there; each row loads its own).
+  constexpr bool PRE = ROPE && D == 64;
+  float pre[PRE ? 2 : 1][C::NKS / 2][16];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int row = bb * 32 + l32;
+      rope_row_pairs<C::NKS>(p.rope + (int64_t)(t.pos0 + min(row, n - 1)) * D, half, pre[bb]);
+    }
+  }
   bf16x8 qf[2][C::NKS], kf[2][C::NKS];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
@@ -196,8 +236,14 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
       qf[bb][ks] = as_bf16x8(row < n ? ld16(qp + 16 * ks) : zero16());
       kf[bb][ks] = as_bf16x8(row < n ? ld16(kp + 16 * ks) : zero16());
     }
-    if constexpr (ROPE) {
-      if (row < n) rope_fragments<C::NKS>(qf[bb], kf[bb], p.rope + (int64_t)(t.pos0 + row) * D, half);
+    if constexpr (PRE) {
+      if (row < n) rope_fragments<C::NKS>(qf[bb], kf[bb], pre[bb]);
+    } else if constexpr (ROPE) {
+      if (row < n) {
+        float cs[C::NKS / 2][16];
+        rope_row_pairs<C::NKS>(p.rope + (int64_t)(t.pos0 + row) * D, half, cs);
+        rope_fragments<C::NKS>(qf[bb], kf[bb], cs);
+      }
     }
   }
   // S^T = K Q^T, lane = query column.
@@ -291,10 +337,24 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
   dma_tile<C::RB, kBlock, 1>(p.k + base, rs, n, kt, 0, lane);
   dma_tile<C::RB, kBlock, 1>(p.dout + base, rs, n, dot, 0, lane);
   const float lv = lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f;
+  // D = 64: this lane's table row is loaded while the tiles are in flight
+  constexpr bool PRE = ROPE && D == 64;
+  const float* tab_row = ROPE ? p.rope + (int64_t)(t.pos0 + min(lane, n - 1)) * D : nullptr;
+  float pre[PRE ? D / 16 : 1][16];
+  // and the epilogue's pairs of rows l32 and 32 + l32 (key rows of key block kb, query
+  // rows of query block qb)
+  float epi[PRE ? 2 : 1][C::NDB / 2][4][8];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) rope_pairs8(tab_row, 8 * c, pre[c]);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      acc_pairs<C::NDB>(p.rope + (int64_t)(t.pos0 + min(rb * 32 + l32, n - 1)) * D, half, epi[rb]);
+  }
   wait_vmem();
   if constexpr (ROPE) {
     // rows past the block's end stay as copied (their P and dS are zero)
-    if (lane < n) rope_lds_row<D>(qt, kt, p.rope + (int64_t)(t.pos0 + lane) * D, lane);
+    if (lane < n) rope_lds_row<D, PRE>(qt, kt, tab_row, pre, lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
   }
@@ -384,7 +444,13 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
       }
     }
     if (key_ok) {
-      if constexpr (ROPE) unrope_acc<C::NDB>(dk, p.rope + (int64_t)(t.pos0 + key) * D, half);
+      if constexpr (PRE) {
+        unrope_acc<C::NDB>(dk, epi[kb]);
+      } else if constexpr (ROPE) {
+        float cs[C::NDB / 2][4][8];
+        acc_pairs<C::NDB>(p.rope + (int64_t)(t.pos0 + key) * D, half, cs);
+        unrope_acc<C::NDB>(dk, cs);
+      }
       const int64_t row = base + key * rs + 4 * half;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -412,7 +478,13 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
                         dq[db]);
     }
     if (row < n) {
-      if constexpr (ROPE) unrope_acc<C::NDB>(dq, p.rope + (int64_t)(t.pos0 + row) * D, half);
+      if constexpr (PRE) {
+        unrope_acc<C::NDB>(dq, epi[qb]);
+      } else if constexpr (ROPE) {
+        float cs[C::NDB / 2][4][8];
+        acc_pairs<C::NDB>(p.rope + (int64_t)(t.pos0 + row) * D, half, cs);
+        unrope_acc<C::NDB>(dq, cs);
+      }
       uint16_t* qp = p.o + base + row * rs + 4 * half;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
