@@ -27,10 +27,12 @@ Modules:
   top-k key blocks per query block, attention over the kept blocks).
 * ``rotary`` -- block-diagonal attention with the rotary position embedding fused in
   (rotation of q and k, and its transpose on dQ and dK).
+* ``mxfp8`` -- the MXFP8 variant (OCP MX quantisation of Q, K, V; attention of the
+  dequantised inputs; a bound for quantising P).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_schedule_spec.py``, ``tests/test_oracle_block_sparse.py`` and
-``tests/test_oracle_rotary.py`` (worked example printed on the pages, independent
+``tests/test_oracle_rotary.py``, ``tests/test_oracle_mxfp8.py`` (worked example printed on the pages, independent
 library routines, closed forms, finite differences, brute force).  Nothing here is
 "parity unpinned".
 """
@@ -43,6 +45,7 @@ from .offsets import (  # noqa: F401
 )
 from . import block_sparse  # noqa: F401
 from . import rotary  # noqa: F401
+from . import mxfp8  # noqa: F401
 from .attention import (  # noqa: F401
     MODE_SELF,
     MODE_BROADCAST_Q,
