@@ -26,6 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "valid-token TFLOPS fwd+bwd (bf16, D=128 jagged) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -91,6 +92,7 @@ def kernel_source_digest():
 
 KERNEL_NAMES = {"fwd_kernel": "fwd_kernel<", "dq_kernel": "dq_kernel<", "dkdv_kernel": "dkdv_kernel<",
                 "dq_ds_kernel": "dq_ds_kernel<", "prep_kernel": "prep_kernel<", "mark_kernel": "mark_kernel",
+                "mx_fwd_kernel": "mx_fwd_kernel<",
                 "bwd_kernel": "bwd_kernel<", "bd_fwd_kernel": "bd_fwd_kernel<", "bd_bwd_kernel": "bd_bwd_kernel<"}
 
 
@@ -134,7 +136,7 @@ def traffic_bytes(workload, kernel):
 
 
 def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, fwd_only=False, sparse_ratio=None,
-                 rotary=False):
+                 rotary=False, mxfp8=False):
     """Time the fp64 oracle on the first sequences of the same batch (bounded sample)."""
     import numpy as np
     import oracle
@@ -164,7 +166,14 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
             flops += (4 if fwd_only else 14) * head_dim * pairs
             done, b = e, e
             continue
-        if rotary:
+        if mxfp8:
+            from oracle import mxfp8 as MX
+            qv, qx = MX.quantise_qk(q)
+            kv, kx = MX.quantise_qk(k)
+            vv, vx = MX.quantise_v(v, off)
+            MX.mxfp8_forward(MX.dequantise_qk(qv, qx), MX.dequantise_qk(kv, kx), MX.dequantise_v(vv, vx, off), off,
+                             1.0 / np.sqrt(head_dim))
+        elif rotary:
             from oracle import rotary as R
             tab = R.rope_table(max(1, int(max(lengths[b:e]))), head_dim)
             R.rotary_block_forward(q, k, v, off, tab, 1.0 / np.sqrt(head_dim))
@@ -185,7 +194,7 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
-                  f"one fp64 {'block-sparse ' if sparse_ratio else 'rotary ' if rotary else ''}"
+                  f"one fp64 {'block-sparse ' if sparse_ratio else 'rotary ' if rotary else 'MXFP8 ' if mxfp8 else ''}"
                   f"{'forward' if fwd_only else 'forward + backward'}"
                   f" each, {spent:.1f} s",
     }
@@ -216,6 +225,7 @@ def main():
     fwd_only = bool(w.get("fwd_only", False))  # grouped-query attention: forward only
     ratio = w.get("sparse_ratio")
     rotary = bool(w.get("rotary", False))
+    mxfp8 = bool(w.get("mxfp8", False))
     lengths = p["lengths"]
     rope = B.rope_table(int(max(lengths)), d, device="cuda") if rotary else None
     shape = B.make_shape(p["num_seqs"], h, d, p["total_tokens"], mq, hkv if hkv != h else 0)
@@ -241,6 +251,19 @@ def main():
     else:
         ws_b = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
     scale = p["scale"]
+    mx = None
+    if mxfp8:
+        # inputs are resident in MXFP8: quantised once, before the timed region (the
+        # quantisers are timed once below, for context)
+        B.kernel_timing(True)
+        q8, qs = B.mxfp8_quantize_qk(q)
+        k8, ks = B.mxfp8_quantize_qk(k)
+        v8, vs, tp = B.mxfp8_quantize_v(v, off, off_h)
+        torch.cuda.synchronize()
+        nq, tq = B.kernel_times(B.KERNEL_MX_QUANT)
+        B.kernel_timing(False)
+        ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD_MXFP8, opts, "cuda")
+        mx = dict(q8=q8, qs=qs, k8=k8, ks=ks, v8=v8, vs=vs, tp=tp, quant_ms=tq, quant_launches=nq)
 
     ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for n in ("f0", "f1", "b1")}
 
@@ -251,6 +274,9 @@ def main():
             B.fwd_block_sparse(q, k, v, off, off_h, ratio, scale, opts, o, lse, sel, ws_f)
         elif rotary:
             B.fwd_rotary(q, k, v, off, off_h, rope, scale, opts, o, lse, ws_f)
+        elif mxfp8:
+            B.fwd_mxfp8(mx["q8"], mx["qs"], mx["k8"], mx["ks"], mx["v8"], mx["vs"], mx["tp"], off, off_h, scale, opts,
+                        o, lse, ws_f)
         else:
             B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_f)
         if i is not None:
@@ -298,6 +324,19 @@ def main():
     fb = 0 if fwd_only else M.bwd_flops(lengths, mode, h, d, mq)
     dense = None
     plain = None
+    if mxfp8:
+        # the bf16 forward of the same batch, for context
+        ws_d = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
+        for _ in range(args.warmup):
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            B.fwd(q, k, v, off, off_h, mode, scale, opts, o, lse, ws_d)
+        e1.record()
+        torch.cuda.synchronize()
+        plain = [e0.elapsed_time(e1) / args.steps, 0.0]
     if rotary:
         # the same batch through the plain block-diagonal kernels, for the rotary's cost
         evp = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -393,8 +432,9 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         achieved = kd["flops"] / (kd["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        peak = PEAK_FP8_TFLOPS if (mxfp8 and dom == "fwd") else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
     roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
                       ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
                       "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel",
@@ -402,6 +442,8 @@ def main():
                       "select": "select_kernel"}[dom]
     if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
         roof["kernel"] = "bd_fwd_kernel"
+    if mxfp8 and dom == "fwd":
+        roof["kernel"] = "mx_fwd_kernel"
     roof["kernel_ms"] = kd["ms"]
     roof["traffic"] = traffic_bytes(w["name"], roof["kernel"])
 
@@ -416,7 +458,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 (e4m3, e8m0 scales), fp32 accumulate" if mxfp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": w["name"],
@@ -445,6 +487,10 @@ def main():
             "dense_fwd_ms": round(dense[0], 4), "speedup_vs_dense_fwd": round(dense[0] / fwd_ms, 3),
             "dense_bwd_ms": round(dense[1], 4), "speedup_vs_dense_bwd": round(dense[1] / bwd_ms, 3),
             "speedup_vs_dense_step": round((dense[0] + dense[1]) / ms_step, 3)},
+        "mxfp8": None if not mxfp8 else {
+            "v_tokens": int(mx["tp"]), "quantise_ms": round(mx["quant_ms"], 4),
+            "quantise_launches": int(mx["quant_launches"]), "bf16_fwd_ms": round(plain[0], 4),
+            "speedup_vs_bf16_fwd": round(plain[0] / fwd_ms, 3)},
         "rotary": None if not rotary else {
             "table_rows": int(rope.shape[0]), "plain_fwd_ms": round(plain[0], 4), "plain_bwd_ms": round(plain[1], 4),
             "fwd_cost_vs_plain": round(fwd_ms / plain[0], 3), "bwd_cost_vs_plain": round(bwd_ms / plain[1], 3)},
@@ -462,7 +508,7 @@ def main():
             return f(q), f(k), f(v), (None if do is None else f(do)), sub_off
 
         out["cpu_baseline"] = cpu_baseline(sub_problem, [int(x) for x in lengths], mode, h, d, mq, args.cpu_seconds,
-                                           fwd_only, ratio, rotary)
+                                           fwd_only, ratio, rotary, mxfp8)
     print(json.dumps(out), flush=True)
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JFA_VERSION 150 /* 1.5.0 */
+#define JFA_VERSION 160 /* 1.6.0 */
 
 enum jfa_mode {
   JFA_MODE_SELF = 0,        /* each packed sequence attends to itself */
@@ -68,7 +68,8 @@ enum jfa_mode {
 enum jfa_pass {
   JFA_PASS_FWD = 0,
   JFA_PASS_BWD = 1,
-  JFA_PASS_FWD_SPARSE = 2 /* jfa_fwd_block_sparse (self mode only) */
+  JFA_PASS_FWD_SPARSE = 2, /* jfa_fwd_block_sparse (self mode only) */
+  JFA_PASS_FWD_MXFP8 = 3   /* jfa_fwd_mxfp8 and jfa_mxfp8_quantize_v (self mode only) */
 };
 
 enum jfa_status {
@@ -185,6 +186,40 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
                          void* workspace, size_t workspace_bytes,
                          const jfa_opts* opts, void* stream);
 
+/* MXFP8 self-attention forward ("Jagged Flash Attention on TLX" (aixai.ru), closing
+ * section on variants: MXFP8 inputs with block scales, P quantised on the fly, the
+ * same pipeline).  MXFP8 is the OCP Microscaling format: 32 elements share an E8M0
+ * scale 2^X (byte X + 127) and each element is FP8 E4M3 (OCP E4M3FN byte).  The
+ * quantisers follow the OCP rule: X = floor(log2 max|x|) - 8 (0 for an all-zero
+ * block), elements x / 2^X rounded to nearest E4M3, ties to even, clamped to +-448.
+ *  - jfa_mxfp8_quantize_qk: q or k [T, H, D] bf16 -> codes [T, H, D] (16-byte aligned)
+ *    and scales [T, H, D/32], blocks of 32 consecutive elements along D.
+ *  - jfa_mxfp8_v_tokens: Tp, the token count of the transposed V layout: every
+ *    sequence padded to a multiple of 64 keys (sequence b starts at the sum of its
+ *    predecessors' padded lengths).
+ *  - jfa_mxfp8_quantize_v: v [T, H, D] bf16 -> codes [H][D][Tp] (V transposed per
+ *    head; zero past each sequence's end) and scales [H][D][Tp/32], blocks of 32 keys
+ *    of one sequence from its start.  tokens must equal jfa_mxfp8_v_tokens().
+ *  - jfa_fwd_mxfp8: o [T, H, D] bf16 and lse [H, T] (natural log) of self attention over
+ *    the dequantised inputs, S and the softmax statistics in fp32, P quantised per 32
+ *    keys of a row with the smallest power-of-two scale that keeps the block maximum
+ *    at most 448 before the P V product.  D in {64, 128}; one key/value head per query
+ *    head (JFA_ERR_BAD_SHAPE otherwise); static schedule of 128-row tiles.
+ * workspace (quantize_v and the forward): jfa_workspace_size(shape, JFA_MODE_SELF,
+ * JFA_PASS_FWD_MXFP8, opts) bytes.  Other conventions as jfa_fwd. */
+int jfa_mxfp8_v_tokens(const jfa_shape* shape, const int32_t* offsets_host, int64_t* tokens);
+int jfa_mxfp8_quantize_qk(const jfa_shape* shape, const void* x, uint8_t* codes, uint8_t* scales, void* stream);
+int jfa_mxfp8_quantize_v(const jfa_shape* shape, const void* v, const int32_t* offsets_dev,
+                         const int32_t* offsets_host, uint8_t* codes, uint8_t* scales, int64_t tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int jfa_fwd_mxfp8(const jfa_shape* shape, float scale,
+                  const uint8_t* q8, const uint8_t* q_scales, const uint8_t* k8, const uint8_t* k_scales,
+                  const uint8_t* v8t, const uint8_t* v_scales, int64_t v_tokens,
+                  const int32_t* offsets_dev, const int32_t* offsets_host,
+                  void* o, float* lse,
+                  void* workspace, size_t workspace_bytes,
+                  const jfa_opts* opts, void* stream);
+
 /* Block-diagonal attention with a rotary position embedding fused in ("TLX Block
  * Attention" (bittide page), opening summary: the rotary embedding fused into the
  * attention kernel, attention plus rotary backward about 3.5x the unfused baseline).
@@ -262,8 +297,9 @@ enum jfa_kernel {
                              jfa_bwd_block_sparse */
   JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path: the row-term kernel (Di, lse);
                                  jfa_bwd_block_sparse: the selection-bitmap (mark) kernel */
-  JFA_KERNEL_SPARSE_SELECT = 4 /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
+  JFA_KERNEL_SPARSE_SELECT = 4, /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
                                   select launch (each recorded as one launch) */
+  JFA_KERNEL_MX_QUANT = 5   /* the MXFP8 quantisation kernels (jfa_mxfp8_quantize_qk / _v) */
 };
 
 /* Measurement hook.  While enabled (enable != 0), every jfa_fwd / jfa_bwd /

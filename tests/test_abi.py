@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.jfa_version() == 150
+    assert lib.jfa_version() == 160
 
 
 def test_error_strings():
@@ -119,7 +119,7 @@ def test_bad_options_and_pass():
         B.workspace_size(shape, 0, 0, B.make_opts(sched=3))
     assert e.value.code == -8
     with pytest.raises(B.JfaError) as e:
-        B.workspace_size(shape, 0, 3)
+        B.workspace_size(shape, 0, 4)
     assert e.value.code == -4
 
 
@@ -286,3 +286,25 @@ def test_rope_table_values():
     assert tab.shape == (5, 4, 2) and tab.dtype == np.float32
     np.testing.assert_allclose(tab[3, 0], [np.cos(3.0), np.sin(3.0)], rtol=1e-7)
     np.testing.assert_allclose(tab[4, 2], [np.cos(0.04), np.sin(0.04)], rtol=1e-7)
+
+
+def test_mxfp8_v_tokens_and_argument_errors():
+    lengths = [300, 0, 64, 65, 1]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), 2, 128, int(off[-1]))
+    assert B.mxfp8_v_tokens(shape, off) == 320 + 0 + 64 + 128 + 64
+    with pytest.raises(B.JfaError) as e:
+        B.mxfp8_v_tokens(B.make_shape(len(lengths), 4, 128, int(off[-1]), num_kv_heads=2), off)
+    assert e.value.code == -2
+    assert B.workspace_size(shape, 0, B.PASS_FWD_MXFP8) > 0
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(shape, 2, B.PASS_FWD_MXFP8)   # self mode only
+    assert e.value.code == -4
+    lib = B.lib()
+    p = ctypes.c_void_p(1 << 20)
+    rc = lib.jfa_fwd_mxfp8(ctypes.byref(shape), 0.1, p, p, p, p, p, p, 575, p, off.ctypes.data, p, p, p, 1 << 40,
+                           None, None)
+    assert rc == -2 and b"v_tokens" in lib.jfa_last_error_detail()   # 575 != 576
+    rc = lib.jfa_fwd_mxfp8(ctypes.byref(shape), 0.1, p, p, p, p, p, p, 576, p, off.ctypes.data, p, p, p, 16,
+                           None, None)
+    assert rc == -7                                                    # workspace too small

@@ -19,11 +19,13 @@ MODE_BLOCK_DIAG = 2
 PASS_FWD = 0
 PASS_BWD = 1
 PASS_FWD_SPARSE = 2
+PASS_FWD_MXFP8 = 3
 KERNEL_FWD = 0
 KERNEL_BWD = 1
 KERNEL_BWD_DQ = 2
 KERNEL_BWD_PREP = 3
 KERNEL_SPARSE_SELECT = 4
+KERNEL_MX_QUANT = 5
 
 
 class JfaError(RuntimeError):
@@ -87,6 +89,14 @@ def lib():
         L.jfa_bwd_rotary.restype = ctypes.c_int
         L.jfa_bwd_rotary.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
                                      vp, vp, vp, ctypes.c_size_t, op, vp]
+        L.jfa_mxfp8_v_tokens.restype = ctypes.c_int
+        L.jfa_mxfp8_v_tokens.argtypes = [sp, vp, i64p]
+        L.jfa_mxfp8_quantize_qk.restype = ctypes.c_int
+        L.jfa_mxfp8_quantize_qk.argtypes = [sp, vp, vp, vp, vp]
+        L.jfa_mxfp8_quantize_v.restype = ctypes.c_int
+        L.jfa_mxfp8_quantize_v.argtypes = [sp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.jfa_fwd_mxfp8.restype = ctypes.c_int
+        L.jfa_fwd_mxfp8.argtypes = [sp, f32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, op, vp]
         L.jfa_ds_bytes.restype = ctypes.c_int
         L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
@@ -412,3 +422,74 @@ def bwd_rotary(q, k, v, o, do, lse, offsets, offsets_host, rope, scale=None, opt
                                 _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                                 ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_bwd_rotary")
     return dq, dk, dv
+
+
+def mxfp8_v_tokens(shape, offsets_host):
+    """Token count of the transposed MXFP8 V layout (sequences padded to 64 keys)."""
+    out = ctypes.c_int64()
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_mxfp8_v_tokens(ctypes.byref(shape), host.ctypes.data, ctypes.byref(out)), "jfa_mxfp8_v_tokens")
+    return out.value
+
+
+def mxfp8_quantize_qk(x, stream=None):
+    """q or k [T, H, D] bf16 -> (codes uint8 [T, H, D], scales uint8 [T, H, D/32])."""
+    import torch
+    _check_tensor("x", x, torch.bfloat16)
+    t, h, d = x.shape
+    shape = make_shape(1, h, d, t)
+    codes = torch.empty((t, h, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((t, h, d // 32), dtype=torch.uint8, device=x.device)
+    if t:
+        _check(lib().jfa_mxfp8_quantize_qk(ctypes.byref(shape), _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
+               "jfa_mxfp8_quantize_qk")
+    return codes, scales
+
+
+def mxfp8_quantize_v(v, offsets, offsets_host, workspace=None, stream=None):
+    """v [T, H, D] bf16 -> (codes uint8 [H, D, Tp], scales uint8 [H, D, Tp/32], Tp)."""
+    import torch
+    _check_tensor("v", v, torch.bfloat16)
+    t, h, d = v.shape
+    nb = len(offsets_host) - 1
+    shape = make_shape(nb, h, d, t)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    tp = mxfp8_v_tokens(shape, host)
+    codes = torch.empty((h, d, max(tp, 64)), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((h, d, max(tp, 64) // 32), dtype=torch.uint8, device=v.device)
+    if workspace is None:
+        workspace = alloc_workspace(shape, MODE_SELF, PASS_FWD_MXFP8, None, v.device)
+    _check(lib().jfa_mxfp8_quantize_v(ctypes.byref(shape), _ptr(v), _ptr(offsets), host.ctypes.data, _ptr(codes),
+                                      _ptr(scales), tp, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "jfa_mxfp8_quantize_v")
+    return codes[:, :, :tp], scales[:, :, :tp // 32], tp
+
+
+def fwd_mxfp8(q8, q_scales, k8, k_scales, v8t, v_scales, v_tokens, offsets, offsets_host, scale=None, opts=None,
+              o=None, lse=None, workspace=None, stream=None):
+    """MXFP8 self-attention forward over quantised inputs.  Returns (o bf16 [T, H, D], lse [H, T])."""
+    import torch
+    t, h, d = q8.shape
+    nb = len(offsets_host) - 1
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q8", q8), ("q_scales", q_scales), ("k8", k8), ("k_scales", k_scales), ("v8t", v8t),
+                    ("v_scales", v_scales)):
+        _check_tensor(name, x, torch.uint8)
+    if k8.shape != q8.shape or q_scales.shape != (t, h, d // 32) or k_scales.shape != (t, h, d // 32):
+        raise ValueError("q8, k8 [T, H, D] and their scales [T, H, D/32]")
+    if v8t.shape != (h, d, v_tokens) or v_scales.shape != (h, d, v_tokens // 32):
+        raise ValueError("v8t [H, D, Tp] and v_scales [H, D, Tp/32]")
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t)
+    o = torch.empty((t, h, d), dtype=torch.bfloat16, device=q8.device) if o is None else o
+    lse = torch.empty((h, t), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check_tensor("o", o, torch.bfloat16, (t, h, d))
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    if workspace is None:
+        workspace = alloc_workspace(shape, MODE_SELF, PASS_FWD_MXFP8, opts, q8.device)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_fwd_mxfp8(ctypes.byref(shape), scale, _ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales),
+                               _ptr(v8t), _ptr(v_scales), v_tokens, _ptr(offsets), host.ctypes.data, _ptr(o), _ptr(lse),
+                               _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts else None,
+                               _stream(stream)), "jfa_fwd_mxfp8")
+    return o, lse

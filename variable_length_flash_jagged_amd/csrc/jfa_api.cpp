@@ -135,7 +135,9 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     return;
   }
   const bool fwd = pass != JFA_PASS_BWD;
-  const int wg = fwd ? kFwdWgPerCu : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
+  const int wg = pass == JFA_PASS_FWD_MXFP8 ? kMxWgPerCu
+                 : fwd                       ? kFwdWgPerCu
+                                             : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
   L.programs_cap = max_programs(o, wg);
   L.seg_cap = std::max<int64_t>(L.programs_cap, H) + 1;
   L.seg = at;
@@ -147,6 +149,16 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
   }
   L.tiles = at;
   at += align_up(L.tile_cap * sizeof(Tile));
+  if (pass == JFA_PASS_FWD_MXFP8) {
+    // tiles of kMxRows query rows and the padded V start of each sequence
+    L.tile_cap = H * (T / kMxRows + B + 1);
+    L.tiles = at;
+    at += align_up(L.tile_cap * sizeof(Tile));
+    L.ds_base = at;
+    at += align_up((B + 1) * sizeof(int64_t));
+    L.total = at;
+    return;
+  }
   if (pass == JFA_PASS_FWD_SPARSE) {
     const int64_t Hkv = s->num_kv_heads > 0 ? s->num_kv_heads : H;
     L.sp_qt = at;
@@ -366,6 +378,21 @@ int check_rope(const float* rope, int32_t rope_positions, const std::vector<int3
   return JFA_OK;
 }
 
+// MXFP8: padded start of each sequence in the transposed V codes.
+std::vector<int64_t> mx_vbase(const std::vector<int32_t>& lengths) {
+  std::vector<int64_t> vb(lengths.size() + 1, 0);
+  for (size_t b = 0; b < lengths.size(); ++b) vb[b + 1] = vb[b] + cdiv(lengths[b], kMxVPad) * kMxVPad;
+  return vb;
+}
+
+int check_mx_shape(const jfa_shape* shape) {
+  int rc = check_shape(shape, JFA_MODE_SELF);
+  if (rc) return rc;
+  if (kv_heads(shape) != shape->num_heads)
+    return fail(JFA_ERR_BAD_SHAPE, "the MXFP8 path needs one query head per key/value head");
+  return JFA_OK;
+}
+
 int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
@@ -374,7 +401,7 @@ int launch_status(hipError_t e, const char* what) {
 struct KernelTimer {
   std::mutex mu;
   bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[5];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[6];
   void forget_locked() {
     for (auto& v : ev) {
       for (auto& pr : v) {
@@ -427,7 +454,7 @@ int jfa_kernel_timing(int enable) {
 int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
   g_detail.clear();
   if (pass != JFA_KERNEL_FWD && pass != JFA_KERNEL_BWD && pass != JFA_KERNEL_BWD_DQ && pass != JFA_KERNEL_BWD_PREP &&
-      pass != JFA_KERNEL_SPARSE_SELECT)
+      pass != JFA_KERNEL_SPARSE_SELECT && pass != JFA_KERNEL_MX_QUANT)
     return fail(JFA_ERR_BAD_MODE, "kernel must be a jfa_kernel");
   if (!launches || !total_ms) return fail(JFA_ERR_NULL_POINTER, "launches and total_ms must be non-NULL");
   std::lock_guard<std::mutex> lock(g_timer.mu);
@@ -475,10 +502,10 @@ int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opt
   g_detail.clear();
   int rc = check_shape(shape, mode);
   if (rc) return rc;
-  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_FWD_SPARSE)
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_FWD_SPARSE && pass != JFA_PASS_FWD_MXFP8)
     return fail(JFA_ERR_BAD_MODE, "pass must be a jfa_pass");
-  if (pass == JFA_PASS_FWD_SPARSE && mode != JFA_MODE_SELF)
-    return fail(JFA_ERR_BAD_MODE, "the block-sparse forward is self mode only");
+  if ((pass == JFA_PASS_FWD_SPARSE || pass == JFA_PASS_FWD_MXFP8) && mode != JFA_MODE_SELF)
+    return fail(JFA_ERR_BAD_MODE, "the block-sparse and MXFP8 forwards are self mode only");
   if (!bytes) return fail(JFA_ERR_NULL_POINTER, "bytes is NULL");
   Opts o;
   if ((rc = check_opts(opts, o))) return rc;
@@ -732,6 +759,132 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
     return rc;
   return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
                        "block-sparse dK/dV launch");
+}
+
+int jfa_mxfp8_v_tokens(const jfa_shape* shape, const int32_t* offsets_host, int64_t* tokens) {
+  g_detail.clear();
+  int rc = check_mx_shape(shape);
+  if (rc) return rc;
+  if (!offsets_host || !tokens) return fail(JFA_ERR_NULL_POINTER, "offsets_host and tokens must be non-NULL");
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, nullptr, offsets_host, nullptr, lengths))) return rc;
+  *tokens = mx_vbase(lengths).back();
+  return JFA_OK;
+}
+
+int jfa_mxfp8_quantize_qk(const jfa_shape* shape, const void* x, uint8_t* codes, uint8_t* scales, void* stream) {
+  g_detail.clear();
+  int rc = check_mx_shape(shape);
+  if (rc) return rc;
+  if (!x || !codes || !scales) return fail(JFA_ERR_NULL_POINTER, "x, codes and scales must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(JFA_ERR_MISALIGNED, "x and codes must be 16-byte aligned");
+  MxQuantParams p{};
+  p.x = (const uint16_t*)x;
+  p.codes = codes;
+  p.scales = scales;
+  p.rows = shape->total_tokens * shape->num_heads;
+  p.num_heads = shape->num_heads;
+  p.head_dim = shape->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_status(timed_launch(JFA_KERNEL_MX_QUANT, s, [&] { return launch_mx_quant_qk(p, s); }),
+                       "MXFP8 quantisation launch");
+}
+
+int jfa_mxfp8_quantize_v(const jfa_shape* shape, const void* v, const int32_t* offsets_dev,
+                         const int32_t* offsets_host, uint8_t* codes, uint8_t* scales, int64_t tokens,
+                         void* workspace, size_t workspace_bytes, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_mx_shape(shape);
+  if (rc) return rc;
+  if (!v || !offsets_dev || !codes || !scales || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "v, offsets_dev, codes, scales and workspace must be non-NULL");
+  if (!aligned(v, 2) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(workspace, kAlign))
+    return fail(JFA_ERR_MISALIGNED, "codes must be 16-byte aligned, scales 2-byte, workspace 256-byte");
+  Layout L;
+  layout_for(shape, JFA_MODE_SELF, JFA_PASS_FWD_MXFP8, Opts(), L);
+  if (workspace_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  const std::vector<int64_t> vb = mx_vbase(lengths);
+  if (tokens != vb.back())
+    return fail(JFA_ERR_BAD_SHAPE, "tokens %lld differs from jfa_mxfp8_v_tokens() = %lld", (long long)tokens,
+                (long long)vb.back());
+  if (vb.back() == 0) return JFA_OK;
+  char* ws = (char*)workspace;
+  if ((rc = upload(vb.data(), vb.size() * sizeof(int64_t), ws + L.ds_base, stream))) return rc;
+  MxQuantParams p{};
+  p.x = (const uint16_t*)v;
+  p.codes = codes;
+  p.scales = scales;
+  p.num_heads = shape->num_heads;
+  p.head_dim = shape->head_dim;
+  p.num_seqs = shape->num_seqs;
+  p.offsets = offsets_dev;
+  p.vbase = (const int64_t*)(ws + L.ds_base);
+  p.tp = vb.back();
+  return launch_status(timed_launch(JFA_KERNEL_MX_QUANT, stream, [&] { return launch_mx_quant_v(p, stream); }),
+                       "MXFP8 V quantisation launch");
+}
+
+int jfa_fwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const uint8_t* q_scales,
+                  const uint8_t* k8, const uint8_t* k_scales, const uint8_t* v8t, const uint8_t* v_scales,
+                  int64_t v_tokens, const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_mx_shape(shape);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q8 || !q_scales || !k8 || !k_scales || !v8t || !v_scales || !offsets_dev || !o || !lse || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "codes, scales, offsets_dev, o, lse and workspace must be non-NULL");
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8t, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 2) ||
+      !aligned(o, 16) || !aligned(lse, 4) || !aligned(workspace, kAlign))
+    return fail(JFA_ERR_MISALIGNED, "codes and o 16-byte aligned, k_scales 4, v_scales 2, lse 4, workspace 256");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  Layout L;
+  layout_for(shape, JFA_MODE_SELF, JFA_PASS_FWD_MXFP8, op, L);
+  if (workspace_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  const std::vector<int64_t> vb = mx_vbase(lengths);
+  if (v_tokens != vb.back())
+    return fail(JFA_ERR_BAD_SHAPE, "v_tokens %lld differs from jfa_mxfp8_v_tokens() = %lld", (long long)v_tokens,
+                (long long)vb.back());
+  const int H = shape->num_heads, D = shape->head_dim;
+  Schedule sc;
+  schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kMxRows, max_programs(op, kMxWgPerCu), false, sc);
+  if (sc.tiles.empty()) return JFA_OK;
+  if ((int64_t)sc.tiles.size() > L.tile_cap || (int64_t)sc.seg_ptr.size() > L.seg_cap)
+    return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  std::vector<char> buf;
+  serialise(sc, L, buf, nullptr, &vb);
+  char* ws = (char*)workspace;
+  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  MxParams p{};
+  p.q8 = q8;
+  p.qsc = q_scales;
+  p.k8 = k8;
+  p.ksc = k_scales;
+  p.v8t = v8t;
+  p.vsc = v_scales;
+  p.vbase = (const int64_t*)(ws + L.ds_base);
+  p.tp = vb.back();
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.offsets = offsets_dev;
+  p.tiles = (const Tile*)(ws + L.tiles);
+  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.num_heads = H;
+  p.num_programs = sc.programs;
+  p.total_tokens = shape->total_tokens;
+  p.scale_log2 = scale * kLog2eHost;
+  return launch_status(timed_launch(JFA_KERNEL_FWD, stream, [&] { return launch_mx_fwd(p, D, stream); }),
+                       "MXFP8 forward launch");
 }
 
 int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,

@@ -43,6 +43,13 @@ constexpr int kSparseMaxKeyBlocks = 2048;
 // many entries (a sequence of kSparseMaxKeyBlocks key blocks).
 constexpr int kSparseMaxSteps = kSparseMaxKeyBlocks * kSparseKBlock / kBwdRows;
 
+// MXFP8 forward: kMxWaves waves of 32 query rows per workgroup (tiles of kMxRows rows).
+constexpr int kMxWaves = 4;
+constexpr int kMxRows = kMxWaves * 32;
+constexpr int kMxWgPerCu = 2;
+// MXFP8 V layout: each sequence's keys padded to a multiple of this in the transposed codes.
+constexpr int kMxVPad = 64;
+
 // Persistent workgroups resident per CU (used for the default program count).
 constexpr int kFwdWgPerCu = 1;    // one 8-wave workgroup: 2 waves per SIMD
 constexpr int kBwdWgPerCu = 2;    // self-attention dK/dV kernel, upper bound over head dims
@@ -188,6 +195,39 @@ struct BdParams {
   const float* rope;
 };
 
+// MXFP8 quantisation: Q / K rows (rows = T * heads, blocks along the head dimension),
+// or V (transposed per head, blocks along each sequence's keys, vbase / tp / offsets).
+struct MxQuantParams {
+  const uint16_t* x;       // bf16 [T, H, D]
+  uint8_t* codes;          // Q/K: [T, H, D]; V: [H][D][tp]
+  uint8_t* scales;         // Q/K: [T, H, D/32]; V: [H][D][tp/32] (E8M0 codes)
+  int64_t rows;            // Q/K: T * H
+  int32_t num_heads, head_dim, num_seqs;
+  const int32_t* offsets;  // V: [B+1]
+  const int64_t* vbase;    // V: [B+1] padded start of each sequence
+  int64_t tp;              // V: padded total (multiple of kMxVPad)
+};
+
+// MXFP8 forward (self attention; one key/value head per query head).
+struct MxParams {
+  const uint8_t* q8;
+  const uint8_t* qsc;
+  const uint8_t* k8;
+  const uint8_t* ksc;
+  const uint8_t* v8t;
+  const uint8_t* vsc;
+  const int64_t* vbase;
+  int64_t tp;
+  uint16_t* o;
+  float* lse;
+  const int32_t* offsets;
+  const Tile* tiles;
+  const int32_t* seg_ptr;
+  int32_t num_heads, num_programs;
+  int64_t total_tokens;
+  float scale_log2;
+};
+
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
@@ -206,6 +246,9 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_pool(const PoolParams& p, int head_dim, hipStream_t s);
 hipError_t launch_select(const SelectParams& p, int head_dim, hipStream_t s);
 hipError_t launch_mark(const MarkParams& p, hipStream_t s);
+hipError_t launch_mx_quant_qk(const MxQuantParams& p, hipStream_t s);
+hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s);
+hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s);
 // dst[i] = bf16(scale * src[i]), i < n (n multiple of 8).
 hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float scale, hipStream_t s);
 // Broadcast-Q partial slabs [P, Mq, D] (programs h*ph .. h*ph+ph-1 hold head h) ->

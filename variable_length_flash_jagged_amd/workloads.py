@@ -23,6 +23,8 @@ generators stand in for them):
    backward at ratio 0.5.
 8. ``block_diag_rotary``: workload 5 with the rotary position embedding fused into the
    block-diagonal attention (cos/sin table of the longest sequence's positions).
+9. ``production_jagged_mxfp8``: the lengths and shape of workload 3 through the MXFP8
+   forward (inputs quantised to OCP MXFP8 before the timed region).
 
 Draw order: lengths (numpy ``default_rng(seed)``), then q, k, v, dO from one
 ``torch.Generator`` seeded with ``seed`` on the target device, each drawn in fp32 and
@@ -48,6 +50,8 @@ WORKLOADS = {
     7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0,
             sparse_ratio=0.5),
     8: dict(name="block_diag_rotary", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0, rotary=True),
+    9: dict(name="production_jagged_mxfp8", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0, fwd_only=True,
+            mxfp8=True),
 }
 
 
@@ -62,7 +66,7 @@ def workload_lengths(workload, seed=0, num_seqs=None):
         n = 64 if num_seqs is None else num_seqs
         u = rng.uniform(0.0, math.log(4097.0), size=n)
         return np.clip(np.floor(np.exp(u)), 1, 4096).astype(np.int64)
-    if workload in (3, 6, 7):
+    if workload in (3, 6, 7, 9):
         n = 1152 if num_seqs is None else num_seqs
         x = rng.normal(math.log(600.0), 1.0, size=n)
         return np.clip(np.rint(np.exp(x)), 1, 4000).astype(np.int64)
