@@ -360,7 +360,8 @@ def main():
         sel_h = sel.cpu().numpy()
         sp_pairs = M.block_sparse_pairs(lengths, h, keep, sel_h)  # pairs summed over heads
         ff, fb = 4 * d * sp_pairs, 10 * d * sp_pairs
-        tile_pairs = M.block_sparse_tile_pairs(lengths, h, keep, sel_h)
+        # the dK/dV kernel runs 64-key tiles at head_dim 128, 128-key tiles otherwise
+        tile_pairs = M.block_sparse_tile_pairs(lengths, h, keep, sel_h, tile_keys=64 if d == 128 else 128)
         ws_d = B.alloc_workspace(shape, mode, B.PASS_FWD, opts, "cuda")
         ws_db = B.alloc_workspace(shape, mode, B.PASS_BWD, opts, "cuda")
         evd = [torch.cuda.Event(enable_timing=True) for _ in range(3)]

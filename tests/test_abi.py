@@ -230,7 +230,11 @@ def test_block_sparse_backward_workspace_size():
     base = B.workspace_size(shape, 0, B.PASS_BWD)
     words = sum(3 * (-(-n // 128)) * 2 * (-(-(-(-n // 256)) // 32)) for n in lengths)
     got = B.bwd_block_sparse_workspace_size(shape, off)
-    assert base + 4 * words <= got <= base + 4 * words + 4 * 256 + 3 * 8 * (len(lengths) + 1)
+    # + the per-sequence arrays and the dK/dV schedule (64-key tiles at head_dim 128:
+    # 8 bytes per tile, at most H (T/64 + B + 1) tiles, and a segment array)
+    tiles = 3 * (int(off[-1]) // 64 + len(lengths) + 1)
+    assert base + 4 * words + 8 * tiles <= got <= base + 4 * words + 8 * tiles + 6 * 256 + 3 * 8 * (len(lengths) + 1) \
+        + 4 * 4096
     # the dS budget does not enlarge it (the block-sparse backward recomputes dS)
     assert B.bwd_block_sparse_workspace_size(shape, off, B.make_opts(ds_budget_mib=64)) == got
     with pytest.raises(B.JfaError) as e:

@@ -336,11 +336,15 @@ int sparse_plan(const jfa_shape* s, const std::vector<int32_t>& lengths, float r
   return JFA_OK;
 }
 
-// Block-sparse backward: the recompute backward's workspace (no dS budget) followed by
-// the selection plan (sel_base, sel_k) and the dK/dV tiles' query-block bitmaps.
+// Block-sparse backward: the recompute backward's workspace (no dS budget; its dQ
+// schedule is used) followed by the selection plan (sel_base, sel_k), the dK/dV
+// schedule (64-key tiles of two waves at head_dim 128, 128-key tiles otherwise) and the
+// dK/dV tiles' query-block bitmaps.
 struct SparseBwdLayout {
   Layout base;
-  size_t sel_base = 0, sel_k = 0, bits_base = 0, bits = 0, total = 0;
+  size_t sel_base = 0, sel_k = 0, bits_base = 0, kv_seg = 0, kv_tiles = 0, bits = 0, total = 0;
+  int64_t kv_seg_cap = 0, kv_tile_cap = 0;
+  int tile_keys = 0, programs = 0;
   std::vector<int64_t> bits_prefix;  // [B+1] first bitmap word of each sequence
 };
 
@@ -349,6 +353,12 @@ void sparse_bwd_layout(const jfa_shape* s, const std::vector<int32_t>& lengths, 
   plain.ds_budget = 0;
   layout_for(s, JFA_MODE_SELF, JFA_PASS_BWD, plain, S.base);
   const size_t B = lengths.size();
+  const int64_t H = s->num_heads, T = s->total_tokens;
+  const bool narrow = s->head_dim == 128;
+  S.tile_keys = narrow ? kSparseKBlock : kBwdKeys;
+  S.programs = max_programs(o, (narrow ? kBwdKeys / kSparseKBlock : 1) * dkdv_wg_per_cu(s->head_dim));
+  S.kv_seg_cap = std::max<int64_t>(S.programs, H) + 1;
+  S.kv_tile_cap = H * (T / S.tile_keys + (int64_t)B + 1);
   S.bits_prefix.assign(B + 1, 0);
   for (size_t b = 0; b < B; ++b) {
     const int64_t len = lengths[b];
@@ -362,6 +372,10 @@ void sparse_bwd_layout(const jfa_shape* s, const std::vector<int32_t>& lengths, 
   at += align_up((B + 1) * sizeof(int32_t));
   S.bits_base = at;
   at += align_up((B + 1) * sizeof(int64_t));
+  S.kv_seg = at;
+  at += align_up(S.kv_seg_cap * sizeof(int32_t));
+  S.kv_tiles = at;
+  at += align_up(S.kv_tile_cap * sizeof(Tile));
   S.bits = at;
   at += align_up((size_t)S.bits_prefix.back() * sizeof(uint32_t));
   S.total = at;
@@ -693,21 +707,28 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   const Layout& L = S.base;
   const int H = shape->num_heads, D = shape->head_dim, B = shape->num_seqs;
   Schedule sc, sq;
-  schedule_bwd(lengths, H, JFA_MODE_SELF, kBwdKeys, max_programs(op, dkdv_wg_per_cu(D)), op.sched == 1, sc);
+  schedule_bwd(lengths, H, JFA_MODE_SELF, S.tile_keys, S.programs, op.sched == 1, sc);
   if (sc.tiles.empty()) return JFA_OK;
   schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDqRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
-  if ((int64_t)sc.tiles.size() > L.tile_cap || (int64_t)sq.tiles.size() > L.tile2_cap)
+  if ((int64_t)sc.tiles.size() > S.kv_tile_cap || (int64_t)sc.seg_ptr.size() > S.kv_seg_cap ||
+      (int64_t)sq.tiles.size() > L.tile2_cap || (int64_t)sq.seg_ptr.size() > L.seg2_cap)
     return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
-  std::vector<char> buf;
-  serialise(sc, L, buf, &sq);
   char* ws = (char*)workspace;
-  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
-  // the per-sequence arrays are contiguous: [sel_base | sel_k | bits_base]
-  std::vector<char> arr(S.bits - S.sel_base, 0);
-  memcpy(arr.data(), P.sel_base.data(), (B + 1) * sizeof(int64_t));
-  memcpy(arr.data() + (S.sel_k - S.sel_base), P.sel_k.data(), (B + 1) * sizeof(int32_t));
-  memcpy(arr.data() + (S.bits_base - S.sel_base), S.bits_prefix.data(), (B + 1) * sizeof(int64_t));
-  if ((rc = upload(arr.data(), arr.size(), ws + S.sel_base, stream))) return rc;
+  {
+    // [counters (zero) .. dQ schedule]
+    std::vector<char> buf(L.tiles2 + sq.tiles.size() * sizeof(Tile), 0);
+    put_schedule(sq, L.seg2, L.tiles2, buf);
+    if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  }
+  {
+    // [sel_base | sel_k | bits_base | dK/dV schedule]
+    std::vector<char> arr(S.kv_tiles + sc.tiles.size() * sizeof(Tile) - S.sel_base, 0);
+    memcpy(arr.data(), P.sel_base.data(), (B + 1) * sizeof(int64_t));
+    memcpy(arr.data() + (S.sel_k - S.sel_base), P.sel_k.data(), (B + 1) * sizeof(int32_t));
+    memcpy(arr.data() + (S.bits_base - S.sel_base), S.bits_prefix.data(), (B + 1) * sizeof(int64_t));
+    put_schedule(sc, S.kv_seg - S.sel_base, S.kv_tiles - S.sel_base, arr);
+    if ((rc = upload(arr.data(), arr.size(), ws + S.sel_base, stream))) return rc;
+  }
   uint32_t* bits = (uint32_t*)(ws + S.bits);
   if ((rc = launch_status(launch_fill_zero((float*)bits, S.bits_prefix.back(), stream), "bitmap fill"))) return rc;
   MarkParams mp{};
@@ -732,13 +753,14 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   p.dout = (const uint16_t*)dout;
   p.lse = lse;
   p.offsets = offsets_dev;
-  p.tiles = (const Tile*)(ws + L.tiles);
-  p.seg_ptr = (const int32_t*)(ws + L.seg);
+  p.tiles = (const Tile*)(ws + S.kv_tiles);
+  p.seg_ptr = (const int32_t*)(ws + S.kv_seg);
   p.counters = (int32_t*)(ws + L.counters);
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
   p.dq = (uint16_t*)dq;
   p.row_aug = (uint16_t*)(ws + L.stats);
+  p.sparse_narrow = S.tile_keys == kSparseKBlock ? 1 : 0;
   p.dq_tiles = (const Tile*)(ws + L.tiles2);
   p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
   p.dq_programs = sq.programs;

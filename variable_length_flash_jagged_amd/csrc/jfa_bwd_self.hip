@@ -240,11 +240,11 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
 
 // ---------------------------------------------------------------------------- dK, dV
 
-template <int D>
+template <int D, int NW_ = kBwdWaves, int NS_ = kBwdStages>
 struct KvCfg {
-  static constexpr int NW = kBwdWaves;
+  static constexpr int NW = NW_;
   static constexpr int NT = NW * 64;
-  static constexpr int BN = kBwdKeys;
+  static constexpr int BN = NW * 32;  // keys per tile
   static constexpr int QB = kBwdRows;
   static constexpr int NQB = QB / 32;
   static constexpr int NKS = D / 16;
@@ -252,7 +252,7 @@ struct KvCfg {
   static constexpr int RB = 2 * D;
   static constexpr int QBUF = QB * RB;
   static constexpr int ABUF = QB * 16;                 // one 16-byte row term per query row
-  static constexpr int NS = kBwdStages;
+  static constexpr int NS = NS_;
   static constexpr int OFF_Q = 0;                      // [NS][QBUF]
   static constexpr int OFF_DO = OFF_Q + NS * QBUF;     // [NS][QBUF]
   static constexpr int OFF_AUG = OFF_DO + NS * QBUF;   // [NS][ABUF]
@@ -262,11 +262,11 @@ struct KvCfg {
 
 // Per-lane constants of the dK/dV loop: LDS operand offsets, ring-copy offsets and the
 // B operands of the row-term MFMAs.
-template <int D>
+template <int D, int NW = kBwdWaves>
 struct KvLane {
   RowOperands<KvCfg<D>::RB, KvCfg<D>::NKS> row;  // Q, dO rows as A operands of S, dP
   TrOperands<KvCfg<D>::RB, KvCfg<D>::NDB> tr;    // Q^T, dO^T as A operands of dK^T, dV^T
-  using Copy = TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, KvCfg<D>::NW>;
+  using Copy = TileCopy<KvCfg<D>::RB, KvCfg<D>::QB, NW>;
   Copy copy;
   bf16x8 pick_s, pick_dp;  // k-slots 0,1 (S) and 4,5 (dP) of the row term, lanes 0-31
   __device__ __forceinline__ void init_pick(int lane) {
@@ -281,8 +281,8 @@ struct KvLane {
 // last valid row) and the 16-byte row terms (wave 0, one row per lane; rows past
 // rows_valid take the sentinel term at index sentinel, whose -lse log2 e part is
 // -1e30, so that their P and dS are exactly zero).
-template <int D>
-__device__ __forceinline__ void kv_issue(const KvLane<D>& ln, const uint16_t* qb, const uint16_t* dob,
+template <int D, int NW>
+__device__ __forceinline__ void kv_issue(const KvLane<D, NW>& ln, const uint16_t* qb, const uint16_t* dob,
                                          const uint16_t* aug, int64_t rs, int64_t aug_row0, int64_t sentinel,
                                          int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
                                          JFA_LDS char* augbuf, int wave, int lane) {
@@ -347,7 +347,7 @@ __device__ __forceinline__ void store_ds(char* blk, uint32_t off, const bf16x8 (
 // from the first one after the dP' row term, when S' has left the pipeline) and
 // dS = P dP' (during the dV products, from their third slot on).  The pack of P (dS) into B operands
 // completes before the first dV (dK) MFMA that needs it.
-template <int D, bool STORE>
+template <int D, bool STORE, int NW = kBwdWaves>
 struct KvStream {
   using C = KvCfg<D>;
   static constexpr int NKS = C::NKS, NDB = C::NDB;
@@ -363,7 +363,7 @@ struct KvStream {
   static constexpr int DS_PER = (16 + DS_SL - 1) / DS_SL;
 
   const JFA_LDS char *qt, *dot, *augt;
-  const KvLane<D>& ln;
+  const KvLane<D, NW>& ln;
   const bf16x8 (&kf)[NKS];
   const bf16x8 (&vf)[NKS];
   f32x16 (&dk)[NDB];
@@ -388,7 +388,7 @@ struct KvStream {
   static_assert(ST0_STEP >= 1 && ST0 + ST0_STEP < DK0 - 1 && ST1 + ST1_STEP < PER + DK0 - 1, "store slots");
 
   __device__ __forceinline__ KvStream(const JFA_LDS char* qt_, const JFA_LDS char* dot_, const JFA_LDS char* augt_,
-                                      const KvLane<D>& ln_, const bf16x8 (&kf_)[NKS], const bf16x8 (&vf_)[NKS],
+                                      const KvLane<D, NW>& ln_, const bf16x8 (&kf_)[NKS], const bf16x8 (&vf_)[NKS],
                                       f32x16 (&dk_)[NDB], f32x16 (&dv_)[NDB], int l32_, float c_,
                                       bf16x8 (&keep_)[C::NQB][2], char* sblk_, uint32_t soff_,
                                       const bf16x8& pick_)
@@ -529,13 +529,16 @@ struct KvStream {
 // Block-sparse step list: wave 0 turns the tile's two query-block bitmaps into the
 // ascending list of its 64-row query steps, entry = step | (halves kept) << 24, at
 // steps[0 .. n) with n at steps[kSparseMaxSteps].  Returns n (all waves).
-template <int QB>
+// TB = key blocks per tile: 2 (128-key tile j, both bitmaps) or 1 (64-key tile j: the
+// bitmap of half j % 2 of 128-key tile j / 2; every listed step keeps the whole tile).
+template <int QB, int TB>
 __device__ __forceinline__ int sparse_steps(const BwdParams& p, int b, int h, int j, int L, int nq, JFA_LDS int* steps,
                                             int wave, int lane) {
   constexpr int SPQ = kSparseQBlock / QB;  // query steps per query block
   const int nqb = (L + kSparseQBlock - 1) / kSparseQBlock, nw = (nqb + 31) / 32;
   const int64_t nj = (L + kBwdKeys - 1) / kBwdKeys;
-  const uint32_t* bm = p.sp_bits + p.sp_bits_base[b] + ((int64_t)h * nj + j) * 2 * nw;
+  const uint32_t* bm = p.sp_bits + p.sp_bits_base[b] + ((int64_t)h * nj + (TB == 2 ? j : j >> 1)) * 2 * nw;
+  if (TB == 1) bm += (j & 1) * nw;
   __syncthreads();  // the previous tile's readers are done with the list
   if (wave == 0) {
     int count = 0;
@@ -543,7 +546,10 @@ __device__ __forceinline__ int sparse_steps(const BwdParams& p, int b, int h, in
     for (int i0 = 0; i0 < nqb; i0 += 64) {
       const int i = i0 + lane;
       int m = 0;
-      if (i < nqb) m = ((bm[i >> 5] >> (i & 31)) & 1) | (((bm[nw + (i >> 5)] >> (i & 31)) & 1) << 1);
+      if (i < nqb) {
+        m = (bm[i >> 5] >> (i & 31)) & 1;
+        if (TB == 2) m |= ((bm[nw + (i >> 5)] >> (i & 31)) & 1) << 1;
+      }
       const uint64_t kept = __ballot(m != 0);
       const int pos = count + __popcll(kept & ((1ull << lane) - 1));
       if (m != 0) {
@@ -564,11 +570,15 @@ __device__ __forceinline__ int sparse_steps(const BwdParams& p, int b, int h, in
 
 // SPARSE: only the query steps of the block-sparse step list (see sparse_steps); the
 // waves whose 64-key block a step's query block did not keep use the masking pick.
-template <int D, bool STORE, bool SPARSE>
-__device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D>& ln,
+// NW waves of 32 keys (tile of NW*32 keys) and an NS-slot ring (NS = 3: copies two
+// steps ahead; NS = 2: one step ahead).
+template <int D, bool STORE, bool SPARSE, int NW = kBwdWaves, int NS = kBwdStages>
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* smem_raw, const KvLane<D, NW>& ln,
                                           int tid) {
   static_assert(!(STORE && SPARSE), "the block-sparse backward recomputes dS");
-  using C = KvCfg<D>;
+  static_assert(NS == 2 || NS == 3, "ring of two or three slots");
+  static_assert(!STORE || NW == kBwdWaves, "the stored-dS layout assumes the 128-key tile");
+  using C = KvCfg<D, NW, NS>;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -608,17 +618,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   // it wait for one copy of the newest step as well, which is harmless.
   auto issue = [&](int it, int slot) {
     const int row0 = it * C::QB;
-    kv_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, L - row0),
+    kv_issue<D, NW>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, L - row0),
                 smem + C::OFF_Q + slot * C::QBUF, smem + C::OFF_DO + slot * C::QBUF,
                 smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
   };
-  constexpr int COPIES = 2 * KvLane<D>::Copy::J;
+  constexpr int COPIES = 2 * KvLane<D, NW>::Copy::J;
   int n = nq;
   JFA_LDS int* steps = (JFA_LDS int*)(smem + C::SMEM);
   bf16x8 pick_mask = ln.pick_s;
   if constexpr (SPARSE) {
-    static_assert(kSparseKBlock * 2 == C::BN && kSparseQBlock % C::QB == 0, "sparse blocks vs dK/dV tiles");
-    n = sparse_steps<C::QB>(p, b, h, j, L, nq, steps, wave, lane);
+    static_assert((kSparseKBlock * 2 == C::BN || kSparseKBlock == C::BN) && kSparseQBlock % C::QB == 0,
+                  "sparse blocks vs dK/dV tiles");
+    n = sparse_steps<C::QB, C::BN / kSparseKBlock>(p, b, h, j, L, nq, steps, wave, lane);
     // k-slot 2 (lanes 0-31) scales the row term's -1 by 1e30: S' -> -1e30, P = 0
     pick_mask[2] = lane < 32 ? (bf16)1e30f : (bf16)0.0f;
   }
@@ -630,12 +641,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
   if (n > 0) {
     issue(step_of(0), 0);
-    if (n > 1) {
-      issue(step_of(1), 1);
-      wait_vmem_n<COPIES>();
-    } else {
-      wait_vmem();
+    bool waited = false;
+    if constexpr (NS == 3) {
+      if (n > 1) {
+        issue(step_of(1), 1);
+        wait_vmem_n<COPIES>();
+        waited = true;
+      }
     }
+    if (!waited) wait_vmem();
     __syncthreads();
   }
 
@@ -655,18 +669,23 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
     for (int qq = 0; qq < C::NQB; ++qq) keep[qq][0] = keep[qq][1] = as_bf16x8(zero16());
   }
 
+  constexpr int AHEAD = NS - 1;  // steps a copy is issued ahead of its use
   for (int it = 0, cur = 0; it < n; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
-    if (it + 2 < n) issue(step_of(it + 2), cur == 0 ? C::NS - 1 : cur - 1);
+    if (it + AHEAD < n) issue(step_of(it + AHEAD), cur == 0 ? C::NS - 1 : cur - 1);
     const JFA_LDS char* qt = smem + C::OFF_Q + cur * C::QBUF;
     const JFA_LDS char* dot = smem + C::OFF_DO + cur * C::QBUF;
     const JFA_LDS char* augt = smem + C::OFF_AUG + cur * C::ABUF;
     bool keep_keys = true;
-    if constexpr (SPARSE) keep_keys = ((steps[it] >> (24 + (wave >> 1))) & 1) != 0;
-    KvStream<D, STORE>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c, keep,
+    if constexpr (SPARSE && NW == kBwdWaves) keep_keys = ((steps[it] >> (24 + (wave >> 1))) & 1) != 0;
+    KvStream<D, STORE, NW>(qt, dot, augt, ln, kf, vf, dk, dv, l32, c, keep,
                        ds_row + (int64_t)max(it - 1, 0) * kDsBlockBytes, ds_off, keep_keys ? ln.pick_s : pick_mask)
         .go();
-    if (it + 2 < n) wait_vmem_n<COPIES>();
-    else wait_vmem();
+    if constexpr (NS == 3) {
+      if (it + 2 < n) wait_vmem_n<COPIES>();
+      else wait_vmem();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
   }
   if constexpr (STORE) store_ds(ds_row + (int64_t)(nq - 1) * kDsBlockBytes, ds_off, keep);
@@ -727,20 +746,21 @@ __global__ void __launch_bounds__(kDqWaves * 64)
             [&](Tile t) { dq_tile<D, SPARSE>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
-template <int D, bool STORE, bool SPARSE>
-__global__ void __launch_bounds__(kBwdWaves * 64)
+// NW < kBwdWaves runs kBwdWaves / NW times as many workgroups per CU (same waves per SIMD).
+template <int D, bool STORE, bool SPARSE, int NW = kBwdWaves, int NS = kBwdStages>
+__global__ void __launch_bounds__(NW * 64)
     __attribute__((amdgpu_waves_per_eu(dkdv_wg_per_cu(D) * kBwdWaves / 4, dkdv_wg_per_cu(D) * kBwdWaves / 4)))
     dkdv_kernel(BwdParams p) {
   // SPARSE: the step list (kSparseMaxSteps entries + its length) follows the rings
-  __shared__ __attribute__((aligned(16))) char smem[KvCfg<D>::SMEM + (SPARSE ? (kSparseMaxSteps + 1) * 4 : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[KvCfg<D, NW, NS>::SMEM + (SPARSE ? (kSparseMaxSteps + 1) * 4 : 0)];
   __shared__ int next_tile;
-  KvLane<D> ln;
+  KvLane<D, NW> ln;
   ln.row.init(threadIdx.x & 63);
   ln.tr.init(threadIdx.x & 63);
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
-            [&](Tile t) { dkdv_tile<D, STORE, SPARSE>(p, t, smem, ln, threadIdx.x); });
+            [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
 // --------------------------------------------------------- stored-dS path: row terms
@@ -983,6 +1003,12 @@ hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s)
   if (p.num_programs <= 0) return hipSuccess;
   const dim3 grid(p.num_programs), block(kBwdWaves * 64);
   if (p.ds && p.sel) return hipErrorInvalidValue;  // stored dS and block sparsity do not combine
+  if (p.sel && p.sparse_narrow) {
+    // block-sparse, 64-key tiles of two waves (head_dim 128 only)
+    if (head_dim != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dkdv_kernel<128, false, true, 2, 2>), grid, dim3(2 * 64), 0, s, p);
+    return hipGetLastError();
+  }
   if (head_dim == 64) {
     if (p.ds) hipLaunchKernelGGL((dkdv_kernel<64, true, false>), grid, block, 0, s, p);
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<64, false, true>), grid, block, 0, s, p);

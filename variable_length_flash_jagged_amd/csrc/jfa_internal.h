@@ -159,6 +159,7 @@ struct BwdParams {
   const int32_t* sel_k;
   const uint32_t* sp_bits;
   const int64_t* sp_bits_base;
+  int32_t sparse_narrow;     // block-sparse: 1 = 64-key dK/dV tiles of two waves (head_dim 128)
   const int32_t* dq_seg_ptr;
   int32_t dq_programs;
   int32_t num_seqs, num_heads, num_q, num_programs;
