@@ -135,7 +135,7 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     return;
   }
   const bool fwd = pass != JFA_PASS_BWD;
-  const int wg = pass == JFA_PASS_FWD_MXFP8 ? kMxWgPerCu
+  const int wg = pass == JFA_PASS_FWD_MXFP8 ? mx_wg_per_cu(s->head_dim)
                  : fwd                       ? kFwdWgPerCu
                                              : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
   L.programs_cap = max_programs(o, wg);
@@ -150,8 +150,8 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
   L.tiles = at;
   at += align_up(L.tile_cap * sizeof(Tile));
   if (pass == JFA_PASS_FWD_MXFP8) {
-    // tiles of kMxRows query rows and the padded V start of each sequence
-    L.tile_cap = H * (T / kMxRows + B + 1);
+    // tiles of mx_rows(D) query rows and the padded V start of each sequence
+    L.tile_cap = H * (T / kMxMinRows + B + 1);
     L.tiles = at;
     at += align_up(L.tile_cap * sizeof(Tile));
     L.ds_base = at;
@@ -879,7 +879,7 @@ int jfa_fwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const 
                 (long long)vb.back());
   const int H = shape->num_heads, D = shape->head_dim;
   Schedule sc;
-  schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kMxRows, max_programs(op, kMxWgPerCu), false, sc);
+  schedule_fwd(lengths, H, JFA_MODE_SELF, 0, mx_rows(D), max_programs(op, mx_wg_per_cu(D)), false, sc);
   if (sc.tiles.empty()) return JFA_OK;
   if ((int64_t)sc.tiles.size() > L.tile_cap || (int64_t)sc.seg_ptr.size() > L.seg_cap)
     return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");

@@ -43,10 +43,12 @@ constexpr int kSparseMaxKeyBlocks = 2048;
 // many entries (a sequence of kSparseMaxKeyBlocks key blocks).
 constexpr int kSparseMaxSteps = kSparseMaxKeyBlocks * kSparseKBlock / kBwdRows;
 
-// MXFP8 forward: kMxWaves waves of 32 query rows per workgroup (tiles of kMxRows rows).
-constexpr int kMxWaves = 4;
-constexpr int kMxRows = kMxWaves * 32;
-constexpr int kMxWgPerCu = 2;
+// MXFP8 forward: mx_waves(D) waves of 32 query rows per workgroup (tiles of
+// mx_rows(D) rows), mx_wg_per_cu(D) workgroups per CU (two waves per SIMD).
+constexpr int mx_waves(int head_dim) { return head_dim == 128 ? 8 : 4; }
+constexpr int mx_rows(int head_dim) { return mx_waves(head_dim) * 32; }
+constexpr int mx_wg_per_cu(int head_dim) { return 8 / mx_waves(head_dim); }
+constexpr int kMxMinRows = 128;  // smallest tile over the head dims (tile capacity)
 // MXFP8 V layout: each sequence's keys padded to a multiple of this in the transposed codes.
 constexpr int kMxVPad = 64;
 

@@ -24,7 +24,8 @@
 // softmax to the second product without leaving registers, and a block's 32 values sit
 // in lanes n and n + 32, whose maxima are combined with one lane swap.  V is stored
 // transposed per head ([D][keys], each sequence padded to 64 keys), so V^T's A operand
-// is two plain 16-byte reads of one LDS row.  One workgroup = 4 waves x 32 query rows;
+// is two plain 16-byte reads of one LDS row.  One workgroup = 8 (D = 128) or 4 (D = 64)
+// waves x 32 query rows, two waves per SIMD;
 // each 64-key step's K tile, V^T tile and their scales are loaded into registers one
 // step ahead and written to XOR-swizzled LDS tiles between two barriers.
 #include <algorithm>
@@ -135,7 +136,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
 
 template <int D>
 struct MxCfg {
-  static constexpr int NW = kMxWaves;
+  static constexpr int NW = mx_waves(D);
   static constexpr int BM = NW * 32;   // query rows per tile
   static constexpr int BN = 64;        // keys per step
   static constexpr int KS = D / 64;    // k-steps of S
@@ -366,8 +367,8 @@ __device__ __forceinline__ void mx_tile(const MxParams& p, Tile tile, JFA_LDS ch
 }
 
 template <int D>
-__global__ void __launch_bounds__(kMxWaves * 64)
-    __attribute__((amdgpu_waves_per_eu(kMxWgPerCu * kMxWaves / 4, kMxWgPerCu * kMxWaves / 4))) mx_fwd_kernel(MxParams p) {
+__global__ void __launch_bounds__(mx_waves(D) * 64)
+    __attribute__((amdgpu_waves_per_eu(2, 2))) mx_fwd_kernel(MxParams p) {
   __shared__ __attribute__((aligned(16))) char smem[MxCfg<D>::SMEM];
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
   for (int idx = p.seg_ptr[prog]; idx < p.seg_ptr[prog + 1]; ++idx)
@@ -394,9 +395,9 @@ hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s) {
 hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
   if (head_dim == 64)
-    hipLaunchKernelGGL(mx_fwd_kernel<64>, dim3(p.num_programs), dim3(kMxWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(mx_fwd_kernel<64>, dim3(p.num_programs), dim3(mx_waves(64) * 64), 0, s, p);
   else
-    hipLaunchKernelGGL(mx_fwd_kernel<128>, dim3(p.num_programs), dim3(kMxWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(mx_fwd_kernel<128>, dim3(p.num_programs), dim3(mx_waves(128) * 64), 0, s, p);
   return hipGetLastError();
 }
 
