@@ -253,13 +253,14 @@ def main():
     scale = p["scale"]
     mx = None
     if mxfp8:
-        # inputs are resident in MXFP8: quantised once, before the timed region (the
-        # quantisers are timed once below, for context)
-        B.kernel_timing(True)
-        q8, qs = B.mxfp8_quantize_qk(q)
-        k8, ks = B.mxfp8_quantize_qk(k)
-        v8, vs, tp = B.mxfp8_quantize_v(v, off, off_h)
-        torch.cuda.synchronize()
+        # inputs are resident in MXFP8: quantised before the timed region (the quantisers
+        # are timed on a second, warm call, for context)
+        for rep in range(2):
+            B.kernel_timing(rep == 1)
+            q8, qs = B.mxfp8_quantize_qk(q)
+            k8, ks = B.mxfp8_quantize_qk(k)
+            v8, vs, tp = B.mxfp8_quantize_v(v, off, off_h)
+            torch.cuda.synchronize()
         nq, tq = B.kernel_times(B.KERNEL_MX_QUANT)
         B.kernel_timing(False)
         ws_f = B.alloc_workspace(shape, mode, B.PASS_FWD_MXFP8, opts, "cuda")

@@ -156,6 +156,8 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     at += align_up(L.tile_cap * sizeof(Tile));
     L.ds_base = at;
     at += align_up((B + 1) * sizeof(int64_t));
+    L.prefix = at;  // V quantiser: sequence of each padded 64-key group
+    at += align_up((T / kMxVPad + B + 1) * sizeof(int32_t));
     L.total = at;
     return;
   }
@@ -836,7 +838,12 @@ int jfa_mxfp8_quantize_v(const jfa_shape* shape, const void* v, const int32_t* o
                 (long long)vb.back());
   if (vb.back() == 0) return JFA_OK;
   char* ws = (char*)workspace;
-  if ((rc = upload(vb.data(), vb.size() * sizeof(int64_t), ws + L.ds_base, stream))) return rc;
+  std::vector<char> buf(L.prefix - L.ds_base + (size_t)(vb.back() / kMxVPad) * sizeof(int32_t), 0);
+  memcpy(buf.data(), vb.data(), vb.size() * sizeof(int64_t));
+  int32_t* gs = reinterpret_cast<int32_t*>(buf.data() + (L.prefix - L.ds_base));
+  for (size_t b = 0; b < lengths.size(); ++b)
+    for (int64_t g = vb[b] / kMxVPad; g < vb[b + 1] / kMxVPad; ++g) gs[g] = (int32_t)b;
+  if ((rc = upload(buf.data(), buf.size(), ws + L.ds_base, stream))) return rc;
   MxQuantParams p{};
   p.x = (const uint16_t*)v;
   p.codes = codes;
@@ -846,6 +853,7 @@ int jfa_mxfp8_quantize_v(const jfa_shape* shape, const void* v, const int32_t* o
   p.num_seqs = shape->num_seqs;
   p.offsets = offsets_dev;
   p.vbase = (const int64_t*)(ws + L.ds_base);
+  p.group_seq = (const int32_t*)(ws + L.prefix);
   p.tp = vb.back();
   return launch_status(timed_launch(JFA_KERNEL_MX_QUANT, stream, [&] { return launch_mx_quant_v(p, stream); }),
                        "MXFP8 V quantisation launch");

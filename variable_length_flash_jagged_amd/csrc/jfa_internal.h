@@ -208,6 +208,7 @@ struct MxQuantParams {
   int32_t num_heads, head_dim, num_seqs;
   const int32_t* offsets;  // V: [B+1]
   const int64_t* vbase;    // V: [B+1] padded start of each sequence
+  const int32_t* group_seq;  // V: [tp / kMxVPad] sequence of each padded 64-key group
   int64_t tp;              // V: padded total (multiple of kMxVPad)
 };
 

@@ -94,33 +94,31 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(MxQuantParams p) {
 }
 
 // V [T, H, D] bf16 -> codes [H][D][Tp] (keys of sequence b at vbase[b] .. + 64 ceil(L/64),
-// zero past L) and exponents + 127 [H][D][Tp/32]: one thread per (32-key block, head,
-// dimension); neighbouring threads read neighbouring dimensions.
+// zero past L) and exponents + 127 [H][D][Tp/32].  2 D threads take one (64-key group,
+// head): thread (half, d) quantises keys 32 half .. + 31 of the group in dimension d, so
+// a wave's loads cover 64 neighbouring dimensions of one key row; the group's sequence
+// comes from the host-built map group_seq.
 __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
   const int H = p.num_heads, D = p.head_dim;
-  const int64_t nkb = p.tp / 32;  // padded 32-key blocks over all sequences
-  const int64_t total = nkb * H * D;
-  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
-    const int d = (int)(g % D);
-    const int h = (int)((g / D) % H);
-    const int64_t kb = g / ((int64_t)D * H);
-    const int64_t key0 = kb * 32;  // padded token index
-    int lo = 0, hi = p.num_seqs;   // sequence: vbase[lo] <= key0 < vbase[lo + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.vbase[mid] <= key0) lo = mid;
-      else hi = mid;
-    }
-    const int64_t s0 = p.offsets[lo];
-    const int L = (int)(p.offsets[lo + 1] - s0);
-    const int j0 = (int)(key0 - p.vbase[lo]);  // first key of the block inside the sequence
+  const int per = 2 * D, slots = 256 / per;
+  const int sub = threadIdx.x / per, t = threadIdx.x % per;
+  const int d = t % D, hf = t / D;
+  const int64_t ngroups = p.tp / kMxVPad;
+  for (int64_t gh = (int64_t)blockIdx.x * slots + sub; gh < ngroups * H; gh += (int64_t)gridDim.x * slots) {
+    const int64_t grp = gh / H;
+    const int h = (int)(gh - grp * H);
+    const int b = p.group_seq[grp];
+    const int64_t s0 = p.offsets[b];
+    const int L = (int)(p.offsets[b + 1] - s0);
+    const int64_t key0 = grp * kMxVPad + 32 * hf;  // padded token index of the block
+    const int j0 = (int)(key0 - p.vbase[b]);       // its first key inside the sequence
     float v[32];
     float amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int j = j0 + t;
-      v[t] = j < L ? __uint_as_float((uint32_t)p.x[((s0 + j) * H + h) * D + d] << 16) : 0.f;
-      amax = fmaxf(amax, fabsf(v[t]));
+    for (int u = 0; u < 32; ++u) {
+      const int j = j0 + u;
+      v[u] = j < L ? __uint_as_float((uint32_t)p.x[((s0 + j) * H + h) * D + d] << 16) : 0.f;
+      amax = fmaxf(amax, fabsf(v[u]));
     }
     const int x = mx_exponent(amax);
     uint32_t q[8];
@@ -128,7 +126,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
     u32x4* dst = reinterpret_cast<u32x4*>(p.codes + ((int64_t)h * D + d) * p.tp + key0);
     dst[0] = u32x4{q[0], q[1], q[2], q[3]};
     dst[1] = u32x4{q[4], q[5], q[6], q[7]};
-    p.scales[((int64_t)h * D + d) * (p.tp / 32) + kb] = (uint8_t)(x + 127);
+    p.scales[((int64_t)h * D + d) * (p.tp / 32) + key0 / 32] = (uint8_t)(x + 127);
   }
 }
 
@@ -389,7 +387,7 @@ hipError_t launch_mx_quant_qk(const MxQuantParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s) {
-  return grid_launch(quant_v_kernel, p, (p.tp / 32) * p.num_heads * p.head_dim, s);
+  return grid_launch(quant_v_kernel, p, (p.tp / kMxVPad) * p.num_heads * 2 * p.head_dim, s);
 }
 
 hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s) {
