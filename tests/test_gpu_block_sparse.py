@@ -192,3 +192,36 @@ def test_block_sparse_backward_full_production_workload_sampled():
         refs = S.block_sparse_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s],
                                        [gpu_sel[b]], p["scale"])
         G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 7 bwd seq {b} (L={e - s})")
+
+
+def test_block_sparse_largest_sequence():
+    """One sequence of 2048 key blocks (131072 tokens), the most the variant takes: at
+    ratio 1 forward and backward equal the dense kernels bit for bit; at ratio 0.5 the
+    selections of sampled query blocks are valid against fp64 relevance computed for
+    those blocks only."""
+    n = 64 * 2048
+    print(f"[case] block sparse largest sequence L={n} H=1 D=64", flush=True)
+    p = W.make_problem([n], 1, 64, seed=58, device="cuda", with_grad=True)
+    o1, l1, sel1 = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], 1.0, p["scale"])
+    od, ld = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], W.MODE_SELF, p["scale"])
+    gs = B.bwd_block_sparse(p["q"], p["k"], p["v"], o1, p["do"], l1, p["offsets"], p["offsets_host"], 1.0, sel1,
+                            p["scale"])
+    gd = B.bwd(p["q"], p["k"], p["v"], od, p["do"], ld, p["offsets"], p["offsets_host"], W.MODE_SELF, p["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, od) and torch.equal(l1, ld)
+    for name, a, b in zip(("dq", "dk", "dv"), gs, gd):
+        assert torch.equal(a, b), name
+    _, _, sel = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], 0.5, p["scale"])
+    torch.cuda.synchronize()
+    kk = S.keep_count(n, 0.5)
+    sel = sel.cpu().numpy()
+    q, k = G.f64(p["q"]), G.f64(p["k"])
+    kb = S.pooled_blocks(k, 0, n, S.K_BLOCK)[:, 0]          # [2048, D]
+    for i in (0, 1, 255, 511):
+        got = sel[i * kk:(i + 1) * kk].tolist()
+        assert len(got) == kk and got == sorted(set(got)) and all(0 <= j < 2048 for j in got)
+        qb = q[i * S.Q_BLOCK:(i + 1) * S.Q_BLOCK, 0].mean(axis=0)
+        s = kb @ qb
+        dropped = np.setdiff1d(np.arange(2048), got)
+        tol = 1e-4 * np.linalg.norm(qb) * np.linalg.norm(kb, axis=1).max()
+        assert s[got].min() >= s[dropped].max() - tol - 1e-9, i
