@@ -208,7 +208,7 @@ def main():
                       args.calibrate_copy_mib or 1024)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
