@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--sched", type=int, default=0)
-    ap.add_argument("--dq-path", type=int, default=0)
+    ap.add_argument("--dq-path", type=int, default=2,
+                    help="broadcast-Q backward: 0 fused kernel + fp32 atomics, 1 fused kernel + per-program slabs, "
+                         "2 dQ and dK/dV kernels + key-chunk slabs")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--self-bwd", choices=("auto", "stored", "recompute"), default="auto",
                     help="self-attention backward: stored-dS (the bench grants the dS workspace), recompute, "
@@ -412,6 +414,14 @@ def main():
         t = int(p["total_tokens"])
         work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 20 * t * h)
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
+    elif mode == W.MODE_BROADCAST_Q and not fwd_only and kt["bwd_dq"][0] > 0:
+        # Broadcast-Q through the dQ and dK/dV kernels (dq_path 2): a dQ kernel (S, dP,
+        # dQ; Q, K, V, O, dO in, lse in, dQ out, the 16-byte row term out per row) and a
+        # dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, the row term in, dK, dV out).
+        sl = int(sum(lengths))
+        nb = len(lengths)
+        work["bwd_dq"] = (6 * h * d * mq * sl, 4 * mq * h * d + 4 * sl * h * d + 4 * nb * mq * h * d + 20 * nb * h * mq)
+        work["bwd"] = (8 * h * d * mq * sl, 2 * mq * h * d + 8 * sl * h * d + 2 * nb * mq * h * d + 16 * nb * h * mq)
     elif not fwd_only:
         work["bwd"] = (fb, bytes_b)
     if ratio:
@@ -437,7 +447,7 @@ def main():
         peak = PEAK_FP8_TFLOPS if (mxfp8 and dom == "fwd") else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
-    roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF else
+    roof["kernel"] = {"fwd": "fwd_kernel", "bwd": "dkdv_kernel" if mode == W.MODE_SELF or "bwd_dq" in work else
                       ("bd_bwd_kernel" if mode == W.MODE_BLOCK_DIAG else "bwd_kernel"),
                       "bwd_dq": "dq_ds_kernel" if stored_ds else "dq_kernel",
                       "bwd_prep": "mark_kernel" if ratio else "prep_kernel",

@@ -175,6 +175,11 @@ def test_workspace_sizes():
     bq = B.make_shape(3, 4, 128, 100000, num_q=256)
     assert B.workspace_size(bq, 1, 1, B.make_opts(num_programs=64)) >= 256 * 4 * 128 * 4
     assert B.workspace_size(bq, 1, 1, B.make_opts(dq_path=1, num_programs=64)) >= 64 * 256 * 128 * 4
+    # split path: per-sequence fp32 dQ slabs [B, Mq, H, D] and row terms [B, H, Mq, 8] bf16
+    assert B.workspace_size(bq, 1, 1, B.make_opts(dq_path=2, num_programs=64)) >= 3 * 256 * 4 * 128 * 4 + 3 * 4 * 256 * 16
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(bq, 1, 1, B.make_opts(dq_path=3))
+    assert "dq_path" in str(e.value)
 
 
 def _lengths(rng, n, hi):

@@ -75,7 +75,7 @@ def test_full_size_sampled_sequences(workload, samples, self_bwd):
         G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload {workload} seq {b} (L={e - s})")
 
 
-@pytest.mark.parametrize("dq_path", [0, 1])
+@pytest.mark.parametrize("dq_path", [0, 1, 2])
 def test_full_size_broadcast_q(dq_path):
     p, o, lse, grads = _run(2, B.make_opts(dq_path=dq_path))
     o_ref, lse_ref = G.oracle_fwd(p)

@@ -138,7 +138,7 @@ def test_length_one_gives_o_equal_v_bit_exact():
 
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("num_q", [1, 100, 256])
-@pytest.mark.parametrize("dq_path", [0, 1])
+@pytest.mark.parametrize("dq_path", [0, 1, 2])
 def test_broadcast_q(head_dim, num_q, dq_path):
     lengths = [1, 0, 64, 129, 300, 7, 0, 256]
     G.run_case(lengths, 2, head_dim, W.MODE_BROADCAST_Q, num_q, seed=8,
@@ -146,17 +146,36 @@ def test_broadcast_q(head_dim, num_q, dq_path):
 
 
 @pytest.mark.parametrize("sched", [0, 1])
-def test_broadcast_q_schedules_and_program_counts(sched):
+@pytest.mark.parametrize("dq_path", [1, 2])
+def test_broadcast_q_schedules_and_program_counts(sched, dq_path):
     lengths = [40, 300, 1, 129, 128]
     for nprog in (2, 5, 64):
         G.run_case(lengths, 3, 128, W.MODE_BROADCAST_Q, 70, seed=9,
-                   opts=B.make_opts(sched=sched, dq_path=1, num_programs=nprog), label=f"bq sched{sched} P{nprog}")
+                   opts=B.make_opts(sched=sched, dq_path=dq_path, num_programs=nprog),
+                   label=f"bq sched{sched} path{dq_path} P{nprog}")
 
 
-def test_broadcast_q_partials_are_run_to_run_identical():
+@pytest.mark.parametrize("sched", [0, 1])
+def test_broadcast_q_split_path_key_chunks(sched):
+    # the dQ kernel cuts long sequences into key chunks (one fp32 slab each): a long
+    # sequence among short ones, a ragged query tail, chunks with and without a tail
+    for nprog in (0, 7):
+        G.run_case([2500, 3, 0, 900, 64], 2, 128, W.MODE_BROADCAST_Q, 300, seed=18,
+                   opts=B.make_opts(sched=sched, dq_path=2, num_programs=nprog),
+                   label=f"bq path2 chunks sched{sched} P{nprog}")
+
+
+def test_broadcast_q_split_path_many_heads_dynamic():
+    # more head groups than the old 64-counter region held (one counter per head group)
+    G.run_case([33, 0, 200], 70, 64, W.MODE_BROADCAST_Q, 40, seed=19,
+               opts=B.make_opts(sched=1, dq_path=2, num_programs=140), label="bq path2 H70 dynamic")
+
+
+@pytest.mark.parametrize("dq_path", [1, 2])
+def test_broadcast_q_partials_are_run_to_run_identical(dq_path):
     p = W.make_problem([90, 300, 17], 2, 128, W.MODE_BROADCAST_Q, 128, seed=10, device="cpu")
     g = G.to_gpu(p)
-    opts = B.make_opts(dq_path=1)
+    opts = B.make_opts(dq_path=dq_path)
     o, lse = G.gpu_fwd(g, opts)
     a = G.gpu_bwd(g, o, lse, opts)
     b = G.gpu_bwd(g, o, lse, opts)
@@ -230,7 +249,7 @@ def test_random_configurations(seed):
     if mode == W.MODE_BLOCK_DIAG and rng.random() < 0.5:
         lengths = [64 * int(rng.integers(0, 9)) for _ in range(nb)]
     opts = B.make_opts(sched=int(rng.integers(0, 2)), num_programs=int(rng.choice([0, 1, 3, 17])),
-                       dq_path=int(rng.integers(0, 2)))
+                       dq_path=int(rng.integers(0, 3)))
     num_q = int(rng.integers(1, 300)) if mode == W.MODE_BROADCAST_Q else 0
     hkv = int(rng.choice([x for x in range(1, h + 1) if h % x == 0]))
     gqa = hkv != h and rng.random() < 0.5

@@ -3,10 +3,16 @@
 Usage: ``python -m variable_length_flash_jagged_amd.build`` (or ``build()``).  Every
 call recompiles all sources; objects go to ``_build/`` next to this file and the
 library to ``libjfa.so`` in this package directory.
+
+``python -m variable_length_flash_jagged_amd.build --resource-usage OUT.md`` instead
+compiles every device source once more with the compiler's kernel resource remarks and
+writes, per kernel, its registers (VGPR, AGPR, SGPR), spills, scratch, LDS and
+occupancy as a Markdown table (no library is linked).
 """
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,16 +51,57 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, extra=(), obj=None):
+    obj = obj or os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [_hipcc()] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    return obj
+    return msgs if extra else obj
+
+
+_FIELDS = [("VGPRs", "VGPR"), ("AGPRs", "AGPR"), ("TotalSGPRs", "SGPR"), ("VGPRs Spill", "VGPR spill"),
+           ("SGPRs Spill", "SGPR spill"), ("ScratchSize [bytes/lane]", "scratch B/lane"),
+           ("LDS Size [bytes/block]", "LDS B/block"), ("Occupancy [waves/SIMD]", "waves/SIMD")]
+
+
+def _demangle(names):
+    r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+    out = r.stdout.splitlines() if r.returncode == 0 else []
+    return out if len(out) == len(names) else list(names)
+
+
+def resource_usage(out_path):
+    """Write the compiler's per-kernel resource report of every device source."""
+    os.makedirs(BUILD, exist_ok=True)
+    rows = []
+    for src in (s for s in SOURCES if s.endswith(".hip")):
+        msgs = _compile(src, False, ["-Rpass-analysis=kernel-resource-usage"],
+                        os.path.join(BUILD, src + ".ru.o"))
+        cur = None
+        for ln in msgs:
+            m = re.search(r"remark:\s+(.*?): (.*?) \[-Rpass-analysis", ln)
+            if not m:
+                continue
+            key, val = m.group(1).strip(), m.group(2).strip()
+            if key == "Function Name":
+                cur = {"src": src, "name": val}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key] = val
+    names = _demangle([r["name"] for r in rows])
+    lines = ["| source | kernel | " + " | ".join(h for _, h in _FIELDS) + " |",
+             "|---|---|" + "---|" * len(_FIELDS)]
+    for r, n in zip(rows, names):
+        n = re.sub(r"^jfa::\(anonymous namespace\)::", "", n)
+        n = re.sub(r"\(jfa::[A-Za-z]+Params\)$", "", n)
+        lines.append(f"| {r['src']} | `{n}` | " + " | ".join(r.get(k, "") for k, _ in _FIELDS) + " |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
 
 
 def build(verbose=False, jobs=None):
@@ -73,4 +120,7 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-usage" in sys.argv:
+        print(resource_usage(sys.argv[sys.argv.index("--resource-usage") + 1]))
+    else:
+        print(build(verbose="-v" in sys.argv))

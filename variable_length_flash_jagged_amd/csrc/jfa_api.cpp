@@ -73,7 +73,7 @@ int check_opts(const jfa_opts* o, Opts& out) {
   out = Opts();
   if (!o) return JFA_OK;
   if (o->sched != 0 && o->sched != 1) return fail(JFA_ERR_BAD_OPTION, "opts.sched must be 0 or 1");
-  if (o->dq_path != 0 && o->dq_path != 1) return fail(JFA_ERR_BAD_OPTION, "opts.dq_path must be 0 or 1");
+  if (o->dq_path < 0 || o->dq_path > 2) return fail(JFA_ERR_BAD_OPTION, "opts.dq_path must be 0, 1 or 2");
   if (o->num_programs < 0 || o->num_programs > (1 << 20))
     return fail(JFA_ERR_BAD_OPTION, "opts.num_programs out of range");
   if (o->ds_budget_mib < 0 || o->ds_budget_mib > (1 << 20))
@@ -119,15 +119,43 @@ struct Layout {
   size_t sp_qt = 0, sp_kb = 0, sp_base = 0, sp_k = 0, sp_qbar = 0, sp_kbar = 0;
   int64_t sp_nqt_cap = 0, sp_nkb_cap = 0;
   int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
+  // broadcast-Q split backward: key-chunk table and its capacity
+  size_t chunks = 0;
+  int64_t chunk_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
+
+// Broadcast-Q split backward: the most key chunks any lengths with these (B, T) give.
+int64_t bq_chunk_cap(int64_t B, int64_t T) { return B + T / (kBqChunkMinSteps * kDqKeys) + 1; }
+
+// Key chunks of the broadcast-Q dQ kernel: every non-empty sequence is cut into chunks
+// of `keys` keys (the last one shorter), keys = kDqKeys * max(kBqChunkMinSteps, the
+// key steps of one program's fair share of all dQ tiles), so that no dQ tile walks far
+// more keys than the average program does.  Table: [sequence | first key | keys].
+std::vector<int32_t> bq_chunks(const std::vector<int32_t>& lengths, int64_t H, int64_t Mq, int programs) {
+  int64_t steps = 0;
+  for (int32_t len : lengths) steps += cdiv(len, kDqKeys);
+  const int64_t share = cdiv(H * cdiv(Mq, kDqRows) * steps, std::max(1, programs));
+  const int64_t keys = kDqKeys * std::max<int64_t>(kBqChunkMinSteps, share);
+  std::vector<int32_t> b_of, k0_of, len_of;
+  for (int b = 0; b < (int)lengths.size(); ++b)
+    for (int64_t k0 = 0; k0 < lengths[b]; k0 += keys) {
+      b_of.push_back(b);
+      k0_of.push_back((int32_t)k0);
+      len_of.push_back((int32_t)std::min<int64_t>(keys, lengths[b] - k0));
+    }
+  std::vector<int32_t> t(b_of);
+  t.insert(t.end(), k0_of.begin(), k0_of.end());
+  t.insert(t.end(), len_of.begin(), len_of.end());
+  return t;
+}
 
 void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L) {
   const int64_t B = s->num_seqs, H = s->num_heads, D = s->head_dim, T = s->total_tokens;
   const int64_t Mq = s->num_q;
   size_t at = 0;
   L.counters = at;
-  at += align_up(64 * sizeof(int32_t));
+  at += align_up(kCounterSlots * sizeof(int32_t));
   if (mode == JFA_MODE_BLOCK_DIAG) {
     L.prefix = at;
     at += align_up((B + 1) * sizeof(int32_t));
@@ -135,9 +163,10 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     return;
   }
   const bool fwd = pass != JFA_PASS_BWD;
+  const bool bq_split = pass == JFA_PASS_BWD && mode == JFA_MODE_BROADCAST_Q && o.dq_path == 2;
   const int wg = pass == JFA_PASS_FWD_MXFP8 ? mx_wg_per_cu(s->head_dim)
                  : fwd                       ? kFwdWgPerCu
-                                             : (mode == JFA_MODE_SELF ? kBwdWgPerCu : kBqWgPerCu);
+                                             : (mode == JFA_MODE_SELF || bq_split ? kBwdWgPerCu : kBqWgPerCu);
   L.programs_cap = max_programs(o, wg);
   L.seg_cap = std::max<int64_t>(L.programs_cap, H) + 1;
   L.seg = at;
@@ -197,6 +226,24 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
       L.ds = at;  // stored dS, up to the budget
       at += align_up((size_t)o.ds_budget);
     }
+  } else if (bq_split) {
+    // dQ kernel schedule (kDqRows-row tiles of the shared queries against one key chunk
+    // each), the key-chunk table int32 [3, NC], the row terms [B, H, Mq, 8] + sentinel,
+    // and the chunks' dQ slabs [NC, Mq, H, D] fp32 (NC <= B + T / minimum chunk)
+    L.chunk_cap = bq_chunk_cap(B, T);
+    L.programs2_cap = max_programs(o, kDqWgPerCu);
+    L.seg2_cap = L.programs2_cap + 1;
+    L.seg2 = at;
+    at += align_up(L.seg2_cap * sizeof(int32_t));
+    L.tile2_cap = H * cdiv(Mq, kDqRows) * L.chunk_cap;
+    L.tiles2 = at;
+    at += align_up(L.tile2_cap * sizeof(Tile));
+    L.chunks = at;
+    at += align_up(3 * L.chunk_cap * sizeof(int32_t));
+    L.stats = at;
+    at += align_up((B * H * Mq + 1) * 16);
+    L.acc = at;
+    at += align_up((size_t)(L.chunk_cap * Mq * H * D) * sizeof(float));
   } else if (pass == JFA_PASS_BWD) {
     L.acc = at;
     const int64_t acc_elems = (o.dq_path == 0) ? Mq * H * D : (int64_t)std::max<int64_t>(L.programs_cap, H) * Mq * D;
@@ -299,14 +346,16 @@ void put_schedule(const Schedule& sc, size_t seg_off, size_t tiles_off, std::vec
 }
 
 void serialise(const Schedule& sc, const Layout& L, std::vector<char>& buf, const Schedule* sc2 = nullptr,
-               const std::vector<int64_t>* ds_base = nullptr) {
+               const std::vector<int64_t>* ds_base = nullptr, const std::vector<int32_t>* chunks = nullptr) {
   size_t end = L.tiles + sc.tiles.size() * sizeof(Tile);
   if (sc2) end = L.tiles2 + sc2->tiles.size() * sizeof(Tile);
   if (ds_base) end = L.ds_base + ds_base->size() * sizeof(int64_t);
+  if (chunks) end = L.chunks + chunks->size() * sizeof(int32_t);
   buf.assign(end, 0);
   put_schedule(sc, L.seg, L.tiles, buf);
   if (sc2) put_schedule(*sc2, L.seg2, L.tiles2, buf);
   if (ds_base) memcpy(buf.data() + L.ds_base, ds_base->data(), ds_base->size() * sizeof(int64_t));
+  if (chunks) memcpy(buf.data() + L.chunks, chunks->data(), chunks->size() * sizeof(int32_t));
 }
 
 // Block-sparse forward: per-sequence query / key block prefixes, kept blocks per query
@@ -1126,9 +1175,11 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
                          "block-diagonal backward launch");
   }
 
+  const bool bq_split = mode == JFA_MODE_BROADCAST_Q && op.dq_path == 2;
   Schedule sc;
   schedule_bwd(lengths, H, mode, kBwdKeys,
-               max_programs(op, mode == JFA_MODE_SELF ? dkdv_wg_per_cu(D) : kBqWgPerCu), op.sched == 1, sc);
+               max_programs(op, mode == JFA_MODE_SELF || bq_split ? dkdv_wg_per_cu(D) : kBqWgPerCu), op.sched == 1,
+               sc);
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
   BwdParams p{};
   p.q = (const uint16_t*)q;
@@ -1199,6 +1250,43 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
       return rc;
     return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
                          "backward dK/dV launch");
+  }
+
+  if (bq_split) {
+    // Broadcast-Q through the dQ and dK/dV kernels: the dQ kernel (tiles of the shared
+    // queries against one sequence's keys) writes each sequence's fp32 dQ contribution
+    // and the row terms, the dK/dV kernel (head-pinned key tiles) reads the row terms,
+    // and a reduce kernel sums the contributions over the sequences.
+    const int64_t Mq = shape->num_q;
+    const int p2 = max_programs(op, kDqWgPerCu);
+    const std::vector<int32_t> chunks = bq_chunks(lengths, H, Mq, p2);
+    const int nc = (int)(chunks.size() / 3);
+    if (nc > L.chunk_cap) return fail(JFA_ERR_WORKSPACE, "internal: chunk capacity");
+    std::vector<int32_t> chunk_len(chunks.begin() + 2 * nc, chunks.end());
+    Schedule sq;  // tiles (chunk, h, query block), longest chunks first, zigzag
+    schedule_fwd(chunk_len, H, JFA_MODE_BROADCAST_Q, (int)Mq, kDqRows, p2, op.sched == 1, sq);
+    if ((int64_t)sq.tiles.size() > L.tile2_cap || sq.programs > L.programs2_cap)
+      return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+    std::vector<char> buf;
+    serialise(sc, L, buf, &sq, nullptr, &chunks);
+    if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+    p.bq = 1;
+    p.bq_chunks = (const int32_t*)(ws + L.chunks);
+    p.num_chunks = nc;
+    p.dq_acc = (float*)(ws + L.acc);
+    p.row_aug = (uint16_t*)(ws + L.stats);
+    p.dq_tiles = (const Tile*)(ws + L.tiles2);
+    p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
+    p.dq_programs = sq.programs;
+    p.programs_per_head = std::max(1, sc.programs / H);
+    if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq(p, D, stream); }),
+                            "backward dQ launch")))
+      return rc;
+    if (!sc.tiles.empty() &&
+        (rc = launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                            "backward dK/dV launch")))
+      return rc;
+    return launch_status(launch_dq_seq_reduce(p.dq_acc, (uint16_t*)dq, nc, Mq * H * D, scale, stream), "dq reduce");
   }
 
   // Broadcast-Q: one fused kernel; dQ summed over all sequences through fp32 atomics

@@ -129,38 +129,51 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
   using C = DqCfg<D>;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  const int h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  // Self attention: the tile's rows are the sequence's own tokens and its keys all of
+  // the sequence's keys.  Broadcast-Q: the rows are rows of the shared q (o, dO, lse
+  // and the row terms per sequence) and the keys one chunk of the sequence's keys.
+  const bool bq = p.bq != 0;
+  const int chunk = tile.b;
+  const int b = bq ? p.bq_chunks[chunk] : tile.b;
   const int64_t rs = (int64_t)p.num_heads * D;
   const int64_t s0 = p.offsets[b];
-  const int L = (int)(p.offsets[b + 1] - s0);
+  const int kstart = bq ? p.bq_chunks[p.num_chunks + chunk] : 0;
+  const int L = bq ? p.bq_chunks[2 * p.num_chunks + chunk] : (int)(p.offsets[b + 1] - s0);  // keys of the tile
   const int row = blk * C::BM + wave * 32 + l32;
-  const bool row_ok = row < L;
+  const int Lq = bq ? p.num_q : L;
+  const bool row_ok = row < Lq;
+  const int64_t qrow = bq ? (int64_t)row : s0 + row;
+  const int64_t orow = bq ? (int64_t)b * p.num_q + row : s0 + row;
+  const int64_t lrow = bq ? ((int64_t)b * p.num_heads + h) * p.num_q + row : (int64_t)h * p.total_tokens + s0 + row;
+  const int64_t aug_rows = bq ? (int64_t)p.num_seqs * p.num_heads * p.num_q : (int64_t)p.num_heads * p.total_tokens;
   const float c = p.scale_log2;
 
   // Q and dO rows as B operands; Di = rowsum(dO * O) and lse2 for this lane's row.
   bf16x8 qf[C::NKS], dof[C::NKS];
   float di = 0.f;
   {
-    const int64_t base = (s0 + row) * rs + (int64_t)h * D + 8 * half;
+    const int64_t qbase = qrow * rs + (int64_t)h * D + 8 * half;
+    const int64_t obase = orow * rs + (int64_t)h * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      qf[ks] = as_bf16x8(row_ok ? ld16(p.q + base + 16 * ks) : zero16());
-      dof[ks] = as_bf16x8(row_ok ? ld16(p.dout + base + 16 * ks) : zero16());
-      const bf16x8 o8 = as_bf16x8(row_ok ? ld16(p.o + base + 16 * ks) : zero16());
+      qf[ks] = as_bf16x8(row_ok ? ld16(p.q + qbase + 16 * ks) : zero16());
+      dof[ks] = as_bf16x8(row_ok ? ld16(p.dout + obase + 16 * ks) : zero16());
+      const bf16x8 o8 = as_bf16x8(row_ok ? ld16(p.o + obase + 16 * ks) : zero16());
 #pragma unroll
       for (int e = 0; e < 8; ++e) di = fmaf((float)dof[ks][e], (float)o8[e], di);
     }
     di = half_sum(di);
   }
-  const float lse = row_ok ? p.lse[(int64_t)h * p.total_tokens + s0 + row] : INFINITY;
+  const float lse = row_ok ? p.lse[lrow] : INFINITY;
   const float lse2 = lse * kLog2e;
   if (blockIdx.x == 0 && tid == 0) {
     // sentinel row term for query rows past the end of a sequence (P = dS = 0)
     const bf16 z = (bf16)0.0f;
     const bf16x8 t = {(bf16)(-1e30f), z, (bf16)(-1.0f), z, z, z, z, z};
-    st16(p.row_aug + (int64_t)p.num_heads * p.total_tokens * 8, __builtin_bit_cast(u32x4, t));
+    st16(p.row_aug + aug_rows * 8, __builtin_bit_cast(u32x4, t));
   }
-  if (row_ok && half == 0) {
+  if (row_ok && half == 0 && kstart == 0) {
     // Row term for the dK/dV kernel: -lse log2 e and -Di as bf16 high + low parts
     // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2), and the
     // constant -1 the block-sparse key mask multiplies.
@@ -169,7 +182,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
     const bf16 z = (bf16)0.0f;
     const bf16x8 t = {xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
-    st16(p.row_aug + ((int64_t)h * p.total_tokens + s0 + row) * 8, __builtin_bit_cast(u32x4, t));
+    st16(p.row_aug + lrow * 8, __builtin_bit_cast(u32x4, t));
   }
 
   f32x16 dq[C::NDB];
@@ -197,10 +210,10 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     tail = part ? tail : 0;
   }
   auto key0_of = [&](int it) { return (SPARSE ? min(max(list[it], 0), nkb - 1) : it) * C::BN; };
-  const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
-  const uint16_t* vp = p.v + s0 * rs + (int64_t)h * D;
+  const uint16_t* kp = p.k + (s0 + kstart) * rs + (int64_t)h * D;
+  const uint16_t* vp = p.v + (s0 + kstart) * rs + (int64_t)h * D;
   const uint32_t rsb = (uint32_t)(rs * 2);
-  {
+  if (n_kv > 0) {  // (broadcast-Q tiles of an empty sequence have no keys: dQ = 0)
     const int k0 = key0_of(0);
     ln.copy.issue_rows(kp + (int64_t)k0 * rs, rsb, min(C::BN, L - k0), smem, wave, lane);
     ln.copy.issue_rows(vp + (int64_t)k0 * rs, rsb, min(C::BN, L - k0), smem + C::BUF, wave, lane);
@@ -227,7 +240,16 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     dq_step<D, true>(kbuf, kbuf + C::BUF, ln, qf, dof, dq, lse2, di, lane, tail, c);
     __syncthreads();
   }
-  if (row_ok) {
+  if (row_ok && bq) {
+    // this sequence's unscaled contribution, summed over the sequences by a reduce kernel
+    float* ap = p.dq_acc + ((int64_t)chunk * p.num_q + row) * rs + (int64_t)h * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(ap + 32 * db + 8 * g4) =
+            make_float4(dq[db][4 * g4], dq[db][4 * g4 + 1], dq[db][4 * g4 + 2], dq[db][4 * g4 + 3]);
+  } else if (row_ok) {
     uint16_t* qp = p.dq + (s0 + row) * rs + (int64_t)h * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -590,11 +612,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   const int my_key = wave * 32 + l32;
   const bool key_ok = my_key < L - key0;
   const float c = p.scale_log2;
-  const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
-  const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
-  const int64_t aug_row0 = (int64_t)h * p.total_tokens + s0;
-  const int64_t sentinel = (int64_t)p.num_heads * p.total_tokens;
-  const int nq = (L + C::QB - 1) / C::QB;
+  // Query rows: the sequence's own tokens, or (broadcast-Q) the shared q rows with this
+  // sequence's dO and row terms.
+  const bool bq = p.bq != 0;
+  const int Lq = bq ? p.num_q : L;
+  const uint16_t* qb = p.q + (bq ? 0 : s0 * rs) + (int64_t)h * D;
+  const uint16_t* dob = p.dout + (bq ? (int64_t)b * p.num_q : s0) * rs + (int64_t)h * D;
+  const int64_t aug_row0 = bq ? ((int64_t)b * p.num_heads + h) * p.num_q : (int64_t)h * p.total_tokens + s0;
+  const int64_t sentinel = bq ? (int64_t)p.num_seqs * p.num_heads * p.num_q : (int64_t)p.num_heads * p.total_tokens;
+  const int nq = (Lq + C::QB - 1) / C::QB;
 
   // This wave's keys as B operands, straight from global (rows past the end -> 0).
   bf16x8 kf[C::NKS], vf[C::NKS];
@@ -618,7 +644,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   // it wait for one copy of the newest step as well, which is harmless.
   auto issue = [&](int it, int slot) {
     const int row0 = it * C::QB;
-    kv_issue<D, NW>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, L - row0),
+    kv_issue<D, NW>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, Lq - row0),
                 smem + C::OFF_Q + slot * C::QBUF, smem + C::OFF_DO + slot * C::QBUF,
                 smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
   };
@@ -704,27 +730,30 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   }
 }
 
-// Persistent tile loop shared by both kernels: static per-program lists or one
-// atomic counter (group 0 of `counters`).
+// Persistent tile loop shared by the kernels: static per-program lists, or (dynamic)
+// groups of gsize consecutive programs, group g taking tiles seg_ptr[g] .. seg_ptr[g+1]
+// first one each, then from its atomic counter counters[g].
 template <class F>
 __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles, const int32_t* seg_ptr,
-                                          int32_t* counter, int* next_tile, F&& body) {
+                                          int32_t* counters, int gsize, int* next_tile, F&& body) {
   const int tid = threadIdx.x;
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
-  int idx, end;
+  const int grp = prog / gsize;
+  int idx, end, base = 0;
   if (!p.dynamic) {
     idx = seg_ptr[prog];
     end = seg_ptr[prog + 1];
   } else {
-    idx = prog;
-    end = seg_ptr[1];
+    base = seg_ptr[grp];
+    end = seg_ptr[grp + 1];
+    idx = base + prog % gsize;
   }
   while (idx < end) {
     body(tiles[idx]);
     if (!p.dynamic) {
       ++idx;
     } else {
-      if (tid == 0) *next_tile = gridDim.x + atomicAdd(counter, 1);
+      if (tid == 0) *next_tile = base + gsize + atomicAdd(counters + grp, 1);
       __syncthreads();
       idx = *next_tile;
       __syncthreads();
@@ -742,7 +771,7 @@ __global__ void __launch_bounds__(kDqWaves * 64)
   ln.row.init(threadIdx.x & 63);
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, (int)gridDim.x, &next_tile,
             [&](Tile t) { dq_tile<D, SPARSE>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
@@ -759,7 +788,8 @@ __global__ void __launch_bounds__(NW * 64)
   ln.tr.init(threadIdx.x & 63);
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, &next_tile,
+  // broadcast-Q: head-pinned groups of programs_per_head programs
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : (int)gridDim.x, &next_tile,
             [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
@@ -980,7 +1010,7 @@ __global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   ln.init(threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + 1, &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, (int)gridDim.x, &next_tile,
             [&](Tile t) { dq_ds_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 

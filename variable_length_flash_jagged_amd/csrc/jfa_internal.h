@@ -65,6 +65,12 @@ constexpr int kBdWgPerCu = 2;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Workspace run-time tile counters (zeroed by every schedule upload).  The dK/dV (and
+// forward) kernels use counters 0 .. G-1, one per program group (G <= 127 heads); a dQ
+// kernel that runs in the same call uses its own counter.
+constexpr int kCounterSlots = 256;
+constexpr int kDqCounter = 128;
+
 // A scheduled tile: b = sequence, hb = (head << 24) | block index.
 struct Tile {
   int32_t b;
@@ -168,6 +174,15 @@ struct BwdParams {
   int64_t total_tokens;
   int32_t dynamic;
   int32_t dq_partials;  // broadcast-Q: 1 = per-program slabs (plain read-modify-write)
+  // Broadcast-Q through the dQ and dK/dV kernels (dq_path 2): the queries are the
+  // shared q [Mq,H,D]; o, dout are [B,Mq,H,D]; lse and the row terms are [B,H,Mq(,8)].
+  // The dQ kernel's tiles cover key chunks: chunk c is keys bq_chunks[NC + c] ..
+  // + bq_chunks[2 NC + c] of sequence bq_chunks[c] (NC = num_chunks); the tile writes
+  // the chunk's unscaled fp32 contribution to dq_acc [NC,Mq,H,D] (the chunk starting at
+  // key 0 also writes the row terms) and a reduce kernel sums the chunks.
+  int32_t bq;
+  const int32_t* bq_chunks;
+  int32_t num_chunks;
   int32_t programs_per_head;  // broadcast-Q head-pinned groups
   float scale;
   float scale_log2;
@@ -259,5 +274,11 @@ hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float s
 // dq[Mq, H, D] = bf16(scale * sum).
 hipError_t launch_dq_reduce(const float* partials, uint16_t* dq, int num_q, int num_heads,
                             int head_dim, int programs_per_head, float scale, hipStream_t s);
+// Broadcast-Q key-chunk slabs [NC, Mq, H, D] -> dq[Mq, H, D] = bf16(scale * sum over the
+// chunks), in a fixed (deterministic) order; the slabs are overwritten (0 slabs: dq = 0).
+hipError_t launch_dq_seq_reduce(float* slabs, uint16_t* dq, int num_slabs, int64_t slab_elems,
+                                float scale, hipStream_t s);
+// Keys per broadcast-Q dQ chunk: at least kBqChunkMinSteps steps of kDqKeys.
+constexpr int kBqChunkMinSteps = 4;
 
 }  // namespace jfa
