@@ -110,9 +110,16 @@ typedef struct jfa_opts {
   int32_t sched;        /* 0: static host schedule (sorted zigzag / head-pinned round robin /
                            contiguous ranges); 1: same order, tiles taken at run time from an
                            atomic counter (block-diagonal mode is always static) */
-  int32_t dq_path;      /* broadcast-Q backward only. 0: fp32 atomics into one [Mq,H,D]
-                           accumulator; 1: per-program fp32 partial slabs [P,Mq,D] reduced
-                           by a second kernel (run-to-run deterministic) */
+  int32_t dq_path;      /* broadcast-Q backward only. 0: one fused kernel, dQ by fp32
+                           atomics into one [Mq,H,D] accumulator; 1: the fused kernel with
+                           per-program fp32 partial slabs [P,Mq,D] reduced by a second kernel
+                           (run-to-run deterministic); 2 (fastest): the self-attention
+                           backward's two kernels -- a dQ kernel over tiles of the shared
+                           queries against one chunk of one sequence's keys (long sequences
+                           cut into chunks so that no tile walks far more keys than a
+                           program's fair share), each chunk's fp32 dQ in a slab
+                           [chunks,Mq,H,D], and a dK/dV kernel over head-pinned key tiles --
+                           then a two-level reduce of the slabs (run-to-run deterministic) */
   int32_t num_programs; /* persistent workgroups; 0 = one per resident slot on the device */
   int32_t ds_budget_mib; /* self-mode backward only: MiB of workspace the backward may use
                            to keep dS (bf16) in HBM, >= 0.  0: recompute path (a dQ kernel
@@ -291,10 +298,11 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
 enum jfa_kernel {
   JFA_KERNEL_FWD = 0,    /* the forward attention kernel of jfa_fwd (and jfa_fwd_block_sparse) */
   JFA_KERNEL_BWD = 1,    /* the main backward kernel of jfa_bwd: the dK/dV kernel in self
-                            mode (and in jfa_bwd_block_sparse), the fused kernel in
-                            broadcast-Q and block-diagonal modes */
-  JFA_KERNEL_BWD_DQ = 2,  /* self mode only: the dQ kernel of jfa_bwd (recompute or stored-dS) and of
-                             jfa_bwd_block_sparse */
+                            mode, in broadcast-Q mode with dq_path 2 (and in
+                            jfa_bwd_block_sparse), the fused kernel in broadcast-Q mode with
+                            dq_path 0 or 1 and in block-diagonal mode */
+  JFA_KERNEL_BWD_DQ = 2,  /* the dQ kernel of jfa_bwd in self mode (recompute or stored-dS) and
+                             in broadcast-Q mode with dq_path 2, and of jfa_bwd_block_sparse */
   JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path: the row-term kernel (Di, lse);
                                  jfa_bwd_block_sparse: the selection-bitmap (mark) kernel */
   JFA_KERNEL_SPARSE_SELECT = 4, /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
