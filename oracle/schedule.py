@@ -36,6 +36,17 @@ Readings where the pages leave the rule open:
 * Dynamic mode keeps the same global order; program p starts with tile p of its group
   and then takes tiles from a per-group atomic counter.  Its output here is that
   global order with one segment per counter group.
+* Broadcast-Q forward key chunks: with a few hundred tiles (one per sequence, head and
+  query block), zigzag dealing cannot help when the tiles of the longest sequence
+  alone take longer than the average program's share, so such a sequence's keys are
+  cut into chunks and every chunk is a tile "sequence" of its own (cost key: the
+  chunk's keys); the chunks' partial outputs are merged by their log-sum-exp
+  afterwards, which gives the same attention (the softmax over a union of key sets).
+  A chunk is ``key_step * max(min_steps, share)`` keys, share = the key steps of one
+  program's fair share of all tiles, ceil(H * ceil(Mq / rows) * sum_b
+  ceil(L_b / key_step) / P).  Chunks are listed in sequence order; an empty sequence
+  keeps one chunk of zero keys.  When no sequence is longer than one chunk the
+  schedule is exactly the unchunked one.
 
 Every function returns plain Python lists so that a reader can compare them by eye.
 """
@@ -80,15 +91,34 @@ def _deal_zigzag(order, num_programs):
     return tiles, ptr, p_used
 
 
+def bq_key_chunks(lengths, num_heads, num_q, rows, num_programs, key_step=64, min_steps=4):
+    """Key chunks of the broadcast-Q forward tiles: a list of (b, first_key, keys) in
+    sequence order (see the module docstring for the rule)."""
+    steps = sum(_cdiv(int(n), key_step) for n in lengths)
+    share = _cdiv(num_heads * _cdiv(num_q, rows) * steps, max(1, num_programs))
+    keys = key_step * max(min_steps, share)
+    chunks = []
+    for b, n in enumerate(lengths):
+        n = int(n)
+        if n == 0:
+            chunks.append((b, 0, 0))
+        for k0 in range(0, n, keys):
+            chunks.append((b, k0, min(keys, n - k0)))
+    return chunks
+
+
 def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=False):
     """Forward schedule for MODE_SELF / MODE_BROADCAST_Q.
 
     Returns (tiles, segment_ptr, programs).  Static: tiles in program-major order and
-    one segment per program.  Dynamic: the sorted global order and one segment."""
+    one segment per program.  Dynamic: the sorted global order and one segment.  In
+    broadcast-Q mode a tile's first entry is the index of its key chunk in
+    bq_key_chunks(...) (the sequence index when no sequence is cut)."""
     if mode == MODE_SELF:
         order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(lengths[b]))
     elif mode == MODE_BROADCAST_Q:
-        order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(num_q))
+        keys = [c[2] for c in bq_key_chunks(lengths, num_heads, num_q, rows, num_programs)]
+        order = sorted_cost_tiles(keys, num_heads, rows, lambda c: int(num_q))
     else:
         raise ValueError("fwd_schedule covers the self and broadcast-Q modes")
     if dynamic:

@@ -317,3 +317,17 @@ def test_mxfp8_v_tokens_and_argument_errors():
     rc = lib.jfa_fwd_mxfp8(ctypes.byref(shape), 0.1, p, p, p, p, p, p, 576, p, off.ctypes.data, p, p, p, 16,
                            None, None)
     assert rc == -7                                                    # workspace too small
+
+
+@pytest.mark.parametrize("sched", [0, 1])
+def test_broadcast_q_forward_key_chunks_match_spec(sched):
+    # long sequences among short ones with many programs: the forward cuts keys into chunks
+    lengths = [4096, 10, 0, 700, 300, 2000]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), 4, 128, int(off[-1]), 256)
+    tiles, seg, progs, rows = B.schedule(shape, 1, 0, off, B.make_opts(sched=sched, num_programs=256))
+    chunks = spec.bq_key_chunks(lengths, 4, 256, rows, 256)
+    assert len(chunks) > len(lengths)  # some sequence is cut
+    want = spec.fwd_schedule(lengths, 4, 1, 256, rows, 256, dynamic=bool(sched))
+    got_t, got_s = _to_lists(tiles, seg)
+    assert got_t == [tuple(t) for t in want[0]] and got_s == list(want[1]) and progs == want[2]

@@ -119,3 +119,44 @@ def test_empty_batch():
     # broadcast-Q forward keeps tiles of empty sequences (they write O = 0)
     t, _, _ = S.fwd_schedule([0, 0], 1, S.MODE_BROADCAST_Q, 64, 64, 8)
     assert sorted(t) == [(0, 0, 0), (1, 0, 0)]
+
+
+def test_bq_key_chunks_hand_example():
+    # 16 + 1 key steps of 64; one 256-row query block, one head, 8 programs:
+    # share = ceil(17 / 8) = 3 steps < 4, so chunks are 4 steps = 256 keys
+    ch = S.bq_key_chunks([1000, 10, 0], 1, 256, 256, 8)
+    assert ch == [(0, 0, 256), (0, 256, 256), (0, 512, 256), (0, 768, 232), (1, 0, 10), (2, 0, 0)]
+    tiles, ptr, p = S.fwd_schedule([1000, 10, 0], 1, S.MODE_BROADCAST_Q, 256, 256, 8)
+    # chunk costs 256, 256, 256, 232, 10, 0: one tile per program in sorted order
+    assert p == 6 and tiles == [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0), (4, 0, 0), (5, 0, 0)]
+    assert ptr == [0, 1, 2, 3, 4, 5, 6]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_bq_key_chunks_cover_every_key_once(seed):
+    rng = np.random.default_rng(300 + seed)
+    lengths = (rng.integers(0, 5000, size=20) * (rng.random(20) < 0.8)).tolist()
+    h, mq, rows, nprog = int(rng.integers(1, 5)), int(rng.integers(1, 600)), 256, int(rng.integers(1, 300))
+    ch = S.bq_key_chunks(lengths, h, mq, rows, nprog)
+    steps = sum(_cdiv(n, 64) for n in lengths)
+    keys = 64 * max(4, _cdiv(h * _cdiv(mq, rows) * steps, nprog))
+    assert [c[0] for c in ch] == sorted(c[0] for c in ch)
+    for b, n in enumerate(lengths):
+        mine = [c for c in ch if c[0] == b]
+        if n == 0:
+            assert mine == [(b, 0, 0)]
+            continue
+        assert [c[1] for c in mine] == list(range(0, n, keys))
+        assert sum(c[2] for c in mine) == n and all(0 < c[2] <= keys for c in mine)
+    # every (chunk, head, query block) tile once
+    tiles, ptr, p = S.fwd_schedule(lengths, h, S.MODE_BROADCAST_Q, mq, rows, nprog)
+    assert sorted(tiles) == sorted((c, hh, i) for c in range(len(ch)) for hh in range(h)
+                                   for i in range(_cdiv(mq, rows)))
+
+
+def test_bq_fwd_schedule_unchunked_when_no_sequence_exceeds_a_share():
+    lengths = [300, 0, 1, 129, 4000]
+    h, mq, rows, nprog = 2, 300, 256, 1  # one program: its share is all the work
+    assert S.bq_key_chunks(lengths, h, mq, rows, nprog) == [(b, 0, n) for b, n in enumerate(lengths)]
+    tiles, _, _ = S.fwd_schedule(lengths, h, S.MODE_BROADCAST_Q, mq, rows, nprog, dynamic=True)
+    assert tiles == S.sorted_cost_tiles(lengths, h, rows, lambda b: mq)

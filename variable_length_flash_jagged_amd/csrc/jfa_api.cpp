@@ -119,35 +119,61 @@ struct Layout {
   size_t sp_qt = 0, sp_kb = 0, sp_base = 0, sp_k = 0, sp_qbar = 0, sp_kbar = 0;
   int64_t sp_nqt_cap = 0, sp_nkb_cap = 0;
   int64_t seg_cap = 0, tile_cap = 0, seg2_cap = 0, tile2_cap = 0;
-  // broadcast-Q split backward: key-chunk table and its capacity
-  size_t chunks = 0;
-  int64_t chunk_cap = 0;
+  // broadcast-Q key chunks (forward; split backward): chunk table and its capacity;
+  // forward: partial-result slots of cut sequences (O [S,Mq,H,D], lse [S,H,Mq], fp32)
+  size_t chunks = 0, part_o = 0, part_lse = 0;
+  int64_t chunk_cap = 0, fwd_slot_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
 
-// Broadcast-Q split backward: the most key chunks any lengths with these (B, T) give.
-int64_t bq_chunk_cap(int64_t B, int64_t T) { return B + T / (kBqChunkMinSteps * kDqKeys) + 1; }
+// Key chunks of broadcast-Q tiles (the forward's and the split backward's dQ kernel):
+// a sequence longer than one program's fair share of key steps is cut into chunks of
+// kKeyStep * max(kBqChunkMinSteps, share) keys, share = ceil(H * ceil(Mq / rows) *
+// sum_b ceil(L_b / kKeyStep) / programs), so that no tile walks far more keys than the
+// average program; each chunk is then a tile "sequence" of its own (cost key: its
+// keys) and the chunks' partial results are merged afterwards.  Chunks are listed in
+// sequence order; keep_empty gives an empty sequence one chunk of zero keys.
+constexpr int kKeyStep = 64;
+static_assert(kKeyStep == kFwdKeys && kKeyStep == kDqKeys, "one key step for both chunk rules");
 
-// Key chunks of the broadcast-Q dQ kernel: every non-empty sequence is cut into chunks
-// of `keys` keys (the last one shorter), keys = kDqKeys * max(kBqChunkMinSteps, the
-// key steps of one program's fair share of all dQ tiles), so that no dQ tile walks far
-// more keys than the average program does.  Table: [sequence | first key | keys].
-std::vector<int32_t> bq_chunks(const std::vector<int32_t>& lengths, int64_t H, int64_t Mq, int programs) {
+struct KeyChunks {
+  std::vector<int32_t> b, k0, len;
+  int64_t keys = 0;  // chunk size
+};
+
+void bq_key_chunks(const std::vector<int32_t>& lengths, int64_t H, int64_t Mq, int rows, int programs,
+                   bool keep_empty, KeyChunks& out) {
   int64_t steps = 0;
-  for (int32_t len : lengths) steps += cdiv(len, kDqKeys);
-  const int64_t share = cdiv(H * cdiv(Mq, kDqRows) * steps, std::max(1, programs));
-  const int64_t keys = kDqKeys * std::max<int64_t>(kBqChunkMinSteps, share);
-  std::vector<int32_t> b_of, k0_of, len_of;
-  for (int b = 0; b < (int)lengths.size(); ++b)
-    for (int64_t k0 = 0; k0 < lengths[b]; k0 += keys) {
-      b_of.push_back(b);
-      k0_of.push_back((int32_t)k0);
-      len_of.push_back((int32_t)std::min<int64_t>(keys, lengths[b] - k0));
+  for (int32_t len : lengths) steps += cdiv(len, kKeyStep);
+  const int64_t share = cdiv(H * cdiv(Mq, rows) * steps, std::max(1, programs));
+  out.keys = kKeyStep * std::max<int64_t>(kBqChunkMinSteps, share);
+  out.b.clear();
+  out.k0.clear();
+  out.len.clear();
+  for (int b = 0; b < (int)lengths.size(); ++b) {
+    if (lengths[b] == 0 && keep_empty) {
+      out.b.push_back(b);
+      out.k0.push_back(0);
+      out.len.push_back(0);
     }
-  std::vector<int32_t> t(b_of);
-  t.insert(t.end(), k0_of.begin(), k0_of.end());
-  t.insert(t.end(), len_of.begin(), len_of.end());
-  return t;
+    for (int64_t k0 = 0; k0 < lengths[b]; k0 += out.keys) {
+      out.b.push_back(b);
+      out.k0.push_back((int32_t)k0);
+      out.len.push_back((int32_t)std::min<int64_t>(out.keys, lengths[b] - k0));
+    }
+  }
+}
+
+// Split backward: the most key chunks any lengths with these (B, T) give (chunks are at
+// least kBqChunkMinSteps * kKeyStep keys).
+int64_t bq_chunk_cap(int64_t B, int64_t T) { return B + T / (kBqChunkMinSteps * kKeyStep) + 1; }
+
+// Forward: the most partial-result slots (chunks of sequences cut into two or more):
+// a cut sequence has L > keys >= max(256, H * ceil(Mq / rows) * T / P), so its
+// ceil(L / keys) < 2 L / keys chunks sum to less than 2 T / keys.
+int64_t bq_fwd_slot_cap(int64_t H, int64_t Mq, int64_t T, int programs) {
+  return std::min<int64_t>(2 * (int64_t)programs / std::max<int64_t>(1, H * cdiv(Mq, kFwdRows)),
+                           2 * T / (kBqChunkMinSteps * kKeyStep)) + 1;
 }
 
 void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L) {
@@ -172,7 +198,14 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
   L.seg = at;
   at += align_up(L.seg_cap * sizeof(int32_t));
   if (fwd) {
-    L.tile_cap = (mode == JFA_MODE_BROADCAST_Q) ? H * B * cdiv(Mq, kFwdRows) : H * (T / kFwdRows + B + 1);
+    if (mode == JFA_MODE_BROADCAST_Q) {
+      // key chunks: every sequence plus the extra chunks of cut sequences
+      L.fwd_slot_cap = bq_fwd_slot_cap(H, Mq, T, L.programs_cap);
+      L.chunk_cap = B + L.fwd_slot_cap;
+      L.tile_cap = H * L.chunk_cap * cdiv(Mq, kFwdRows);
+    } else {
+      L.tile_cap = H * (T / kFwdRows + B + 1);
+    }
   } else {
     L.tile_cap = H * (T / kBwdKeys + B + 1);
   }
@@ -189,6 +222,14 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     at += align_up((T / kMxVPad + B + 1) * sizeof(int32_t));
     L.total = at;
     return;
+  }
+  if (pass == JFA_PASS_FWD && mode == JFA_MODE_BROADCAST_Q) {
+    L.chunks = at;  // [sequence | first key | keys | slot] per chunk, then (b, first slot, slots) per cut sequence
+    at += align_up((4 * L.chunk_cap + 3 * B) * sizeof(int32_t));
+    L.part_o = at;
+    at += align_up((size_t)(L.fwd_slot_cap * Mq * H * D) * sizeof(float));
+    L.part_lse = at;
+    at += align_up((size_t)(L.fwd_slot_cap * H * Mq) * sizeof(float));
   }
   if (pass == JFA_PASS_FWD_SPARSE) {
     const int64_t Hkv = s->num_kv_heads > 0 ? s->num_kv_heads : H;
@@ -982,7 +1023,11 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
   const bool dyn = o.sched == 1;
   if (mode == JFA_MODE_BLOCK_DIAG)
     schedule_blockdiag(lengths, shape->num_heads, kBlock, max_programs(o, kBdWgPerCu), sc);
-  else if (pass == JFA_PASS_FWD)
+  else if (pass == JFA_PASS_FWD && mode == JFA_MODE_BROADCAST_Q) {
+    KeyChunks kc;
+    bq_key_chunks(lengths, shape->num_heads, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), true, kc);
+    schedule_fwd(kc.len, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
+  } else if (pass == JFA_PASS_FWD)
     schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
   else
     schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys,
@@ -1063,13 +1108,48 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   }
 
   Schedule sc;
-  schedule_fwd(lengths, H, mode, shape->num_q, kFwdRows, max_programs(op, kFwdWgPerCu), op.sched == 1, sc);
+  const int P = max_programs(op, kFwdWgPerCu);
+  std::vector<int32_t> table;  // broadcast-Q: key chunks and cut sequences
+  int nc = 0, ncut = 0;
+  if (mode == JFA_MODE_BROADCAST_Q) {
+    KeyChunks kc;
+    bq_key_chunks(lengths, H, shape->num_q, kFwdRows, P, true, kc);
+    nc = (int)kc.b.size();
+    // partial-result slots for the chunks of cut sequences, consecutive per sequence
+    std::vector<int32_t> slot(nc, -1), cuts;
+    int nslot = 0;
+    for (int c = 0; c < nc;) {
+      int e = c + 1;
+      while (e < nc && kc.b[e] == kc.b[c]) ++e;
+      if (e - c > 1) {
+        cuts.insert(cuts.end(), {kc.b[c], nslot, e - c});
+        for (int i = c; i < e; ++i) slot[i] = nslot++;
+      }
+      c = e;
+    }
+    ncut = (int)cuts.size() / 3;
+    if (nc > L.chunk_cap || nslot > L.fwd_slot_cap) return fail(JFA_ERR_WORKSPACE, "internal: chunk capacity");
+    table = kc.b;
+    table.insert(table.end(), kc.k0.begin(), kc.k0.end());
+    table.insert(table.end(), kc.len.begin(), kc.len.end());
+    table.insert(table.end(), slot.begin(), slot.end());
+    table.insert(table.end(), cuts.begin(), cuts.end());
+    schedule_fwd(kc.len, H, mode, shape->num_q, kFwdRows, P, op.sched == 1, sc);
+  } else {
+    schedule_fwd(lengths, H, mode, shape->num_q, kFwdRows, P, op.sched == 1, sc);
+  }
   if (sc.tiles.empty()) return JFA_OK;
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
   std::vector<char> buf;
-  serialise(sc, L, buf);
+  serialise(sc, L, buf, nullptr, nullptr, table.empty() ? nullptr : &table);
   if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
   FwdParams p{};
+  if (mode == JFA_MODE_BROADCAST_Q) {
+    p.chunks = (const int32_t*)(ws + L.chunks);
+    p.num_chunks = nc;
+    p.part_o = (float*)(ws + L.part_o);
+    p.part_lse = (float*)(ws + L.part_lse);
+  }
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -1087,8 +1167,11 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   p.total_tokens = shape->total_tokens;
   p.dynamic = op.sched;
   p.scale_log2 = scale * kLog2eHost;
-  return launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_fwd(p, mode, D, stream); }),
-                       "forward launch");
+  if ((rc = launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_fwd(p, mode, D, stream); }),
+                          "forward launch")))
+    return rc;
+  if (ncut == 0) return JFA_OK;
+  return launch_status(launch_bq_combine(p, ncut, D, stream), "forward chunk merge");
 }
 
 int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
@@ -1259,12 +1342,15 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     // and a reduce kernel sums the contributions over the sequences.
     const int64_t Mq = shape->num_q;
     const int p2 = max_programs(op, kDqWgPerCu);
-    const std::vector<int32_t> chunks = bq_chunks(lengths, H, Mq, p2);
-    const int nc = (int)(chunks.size() / 3);
+    KeyChunks kc;
+    bq_key_chunks(lengths, H, Mq, kDqRows, p2, false, kc);
+    const int nc = (int)kc.b.size();
     if (nc > L.chunk_cap) return fail(JFA_ERR_WORKSPACE, "internal: chunk capacity");
-    std::vector<int32_t> chunk_len(chunks.begin() + 2 * nc, chunks.end());
+    std::vector<int32_t> chunks(kc.b);  // [sequence | first key | keys]
+    chunks.insert(chunks.end(), kc.k0.begin(), kc.k0.end());
+    chunks.insert(chunks.end(), kc.len.begin(), kc.len.end());
     Schedule sq;  // tiles (chunk, h, query block), longest chunks first, zigzag
-    schedule_fwd(chunk_len, H, JFA_MODE_BROADCAST_Q, (int)Mq, kDqRows, p2, op.sched == 1, sq);
+    schedule_fwd(kc.len, H, JFA_MODE_BROADCAST_Q, (int)Mq, kDqRows, p2, op.sched == 1, sq);
     if ((int64_t)sq.tiles.size() > L.tile2_cap || sq.programs > L.programs2_cap)
       return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
     std::vector<char> buf;

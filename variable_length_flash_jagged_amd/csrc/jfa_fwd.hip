@@ -213,15 +213,24 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int g = wave >> 2;  // 0: group A, 1: group B (same SIMD as wave - 4)
   const int l32 = lane & 31, half = lane >> 5;
-  const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  const int h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
   const int H = p.num_heads;
   const int64_t rs = (int64_t)H * D;                   // q, o row stride
   const int64_t rkv = (int64_t)p.num_kv_heads * D;     // k, v row stride
   const uint32_t rkvb = (uint32_t)(rkv * 2);
   const int hkv = h / (H / p.num_kv_heads);            // key/value head of query head h
-  const int64_t s0 = p.offsets[b];
-  const int L = (int)(p.offsets[b + 1] - s0);
   constexpr bool SELF = MODE != kBroadcastQ;           // self attention (dense or block sparse)
+  // Broadcast-Q: the tile covers one key chunk (keys kst .. kst + L - 1 of sequence b);
+  // slot >= 0 marks a chunk of a cut sequence, whose partial O and lse go to the slot.
+  int b = tile.b, kst = 0, slot = -1;
+  if constexpr (!SELF) {
+    const int ch = tile.b, nc = p.num_chunks;
+    b = p.chunks[ch];
+    kst = p.chunks[nc + ch];
+    slot = p.chunks[3 * nc + ch];
+  }
+  const int64_t s0 = p.offsets[b];
+  const int L = SELF ? (int)(p.offsets[b + 1] - s0) : p.chunks[2 * p.num_chunks + tile.b];  // keys visited
   const int Lq = SELF ? L : p.num_q;
   const int row = blk * C::BM + wave * 32 + l32;
   const float c = p.scale_log2;
@@ -251,8 +260,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   }
   auto tile_of = [&](int i) { return MODE == kSelfSparse ? list[i] : i; };
   if (n > 0) {
-    const uint16_t* kp = p.k + s0 * rkv + (int64_t)hkv * D;
-    const uint16_t* vp = p.v + s0 * rkv + (int64_t)hkv * D;
+    const uint16_t* kp = p.k + (s0 + kst) * rkv + (int64_t)hkv * D;
+    const uint16_t* vp = p.v + (s0 + kst) * rkv + (int64_t)hkv * D;
     auto rows_of = [&](int j) { return min(C::BN, L - j * C::BN); };
     // Stage i into slot i % NS.  Stage 0 has no V tile and stage n no K tile; those
     // halves repeat a neighbouring tile instead, so every stage is the same number of
@@ -326,7 +335,19 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   const float lt = half_sum(w.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
-  if (row < Lq) {
+  if (!SELF && slot >= 0 && row < Lq) {
+    // chunk of a cut sequence: fp32 O / l and lse of this chunk, merged afterwards
+    float* po = p.part_o + (((int64_t)slot * p.num_q + row) * H + h) * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& x = w.o[db];
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * g4) =
+            make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
+      }
+    if (half == 0) p.part_lse[((int64_t)slot * H + h) * p.num_q + row] = lse;
+  } else if (row < Lq) {
     const int64_t orow = SELF ? s0 + row : (int64_t)b * p.num_q + row;
     uint16_t* op = p.o + orow * rs + (int64_t)h * D + 4 * half;
 #pragma unroll
@@ -384,7 +405,51 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Merge of the chunk partials of cut broadcast-Q sequences: for cut sequence i with
+// slots f .. f + n - 1 and each (query row, head), lse = log sum_c exp(lse_c) and
+// O = sum_c exp(lse_c - lse) O_c (each O_c normalised by its own row sum, so the
+// weights are the chunks' shares of the full row sum).  One thread per 8 head-dim
+// columns of a (cut sequence, row, head).
+__global__ void bq_combine_kernel(FwdParams p, int cuts, int D) {
+  const int nc = p.num_chunks, H = p.num_heads, Mq = p.num_q, nd8 = D / 8;
+  const int64_t total = (int64_t)cuts * Mq * H * nd8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int d8 = (int)(i % nd8);
+    const int h = (int)((i / nd8) % H);
+    const int row = (int)((i / ((int64_t)nd8 * H)) % Mq);
+    const int cut = (int)(i / ((int64_t)nd8 * H * Mq));
+    const int* t = p.chunks + 4 * nc + 3 * cut;
+    const int b = t[0], first = t[1], n = t[2];
+    float m = -INFINITY;
+    for (int c = 0; c < n; ++c) m = fmaxf(m, p.part_lse[((int64_t)(first + c) * H + h) * Mq + row]);
+    float sum = 0.f;
+    for (int c = 0; c < n; ++c) sum += expf(p.part_lse[((int64_t)(first + c) * H + h) * Mq + row] - m);
+    const float lse = m + logf(sum);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c) {
+      const float wgt = expf(p.part_lse[((int64_t)(first + c) * H + h) * Mq + row] - lse);
+      const float* src = p.part_o + (((int64_t)(first + c) * Mq + row) * H + h) * D + 8 * d8;
+      const float4 a = reinterpret_cast<const float4*>(src)[0];
+      const float4 e = reinterpret_cast<const float4*>(src)[1];
+      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
+      acc[4] += wgt * e.x; acc[5] += wgt * e.y; acc[6] += wgt * e.z; acc[7] += wgt * e.w;
+    }
+    const int64_t orow = (int64_t)b * Mq + row;
+    st16(p.o + (orow * H + h) * D + 8 * d8,
+         __builtin_bit_cast(u32x4, pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7])));
+    if (d8 == 0) p.lse[((int64_t)b * H + h) * Mq + row] = lse;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bq_combine(const FwdParams& p, int cuts, int head_dim, hipStream_t s) {
+  const int64_t total = (int64_t)cuts * p.num_q * p.num_heads * (head_dim / 8);
+  if (total <= 0) return hipSuccess;
+  const int64_t g = (total + 255) / 256;
+  hipLaunchKernelGGL(bq_combine_kernel, dim3((unsigned)(g < 4096 ? g : 4096)), dim3(256), 0, s, p, cuts, head_dim);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;

@@ -99,6 +99,16 @@ struct FwdParams {
   const int32_t* sel;
   const int64_t* sel_base;
   const int32_t* sel_k;
+  // broadcast-Q key chunks: tile b field = chunk c; chunk c covers keys chunks[nc + c] ..
+  // + chunks[2 nc + c] of sequence chunks[c] (nc = num_chunks).  chunks[3 nc + c] is -1
+  // when the chunk is its sequence's only one (the tile writes o and lse) or a slot s
+  // of part_o [S, Mq, H, D] / part_lse [S, H, Mq] (fp32: O normalised by the chunk's own
+  // row sum, and the chunk's natural-log lse); then follow, per cut sequence i,
+  // chunks[4 nc + 3 i + 0..2] = (b, first slot, slots), merged by launch_bq_combine.
+  const int32_t* chunks;
+  int32_t num_chunks;
+  float* part_o;
+  float* part_lse;
 };
 
 // Block means of a bf16 [T, heads, D] tensor: out[h][blk][d] (fp32) over consecutive
@@ -249,6 +259,8 @@ struct MxParams {
 
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
+// Broadcast-Q forward: merge the chunk partials of the `cuts` cut sequences into o, lse.
+hipError_t launch_bq_combine(const FwdParams& p, int cuts, int head_dim, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
 // Self-attention backward: dQ kernel (query tiles; also writes the per-row stats the
 // dK/dV kernel reads, so it runs first) and dK/dV kernel (key tiles).
