@@ -318,9 +318,70 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
   }
 }
 
-template <int D, bool ROPE>
+// Backward operands of one tile held in registers: the Q, K and dO rows (16-byte chunks,
+// lane l holding chunks l, l + 64, ... of the row-major 64-row tile; rows past the
+// block's end are zero), this lane's V rows as the B operands of dP, its O rows for Di
+// and its lse.  The kernel loads the next tile's into one of these while the current
+// tile computes, so that the wave -- alone on its SIMD -- does not wait out a full
+// memory round trip per tile.
+template <int D>
+struct BdBwdRegs {
+  static constexpr int CPR = 2 * D / 16;       // 16-byte chunks per row
+  static constexpr int CH = kBlock * CPR / 64;  // chunks per lane per tile
+  u32x4 q[CH], k[CH], dout[CH];
+  bf16x8 vf[2][D / 16];
+  u32x4 o[2][D / 16];
+  float lse;
+};
+
+template <int D>
+__device__ __forceinline__ void bd_bwd_load(const BdParams& p, const BdTile& t, BdBwdRegs<D>& x, int lane) {
+  using R = BdBwdRegs<D>;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t base = t.t0 * rs + (int64_t)t.h * D;
+  const int n = t.n;
+#pragma unroll
+  for (int j = 0; j < R::CH; ++j) {
+    const int idx = j * 64 + lane, r = idx / R::CPR, c = idx % R::CPR;
+    const int64_t off = base + r * rs + 8 * c;
+    x.q[j] = r < n ? ld16(p.q + off) : zero16();
+    x.k[j] = r < n ? ld16(p.k + off) : zero16();
+    x.dout[j] = r < n ? ld16(p.dout + off) : zero16();
+  }
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+    const int r = b2 * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int64_t off = base + r * rs + 16 * ks + 8 * half;
+      x.vf[b2][ks] = as_bf16x8(r < n ? ld16(p.v + off) : zero16());
+      x.o[b2][ks] = r < n ? ld16(p.o_in + off) : zero16();
+    }
+  }
+  x.lse = lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f;
+}
+
+// Q, K, dO chunks -> this wave's swizzled LDS tiles.
+template <int D>
+__device__ __forceinline__ void bd_bwd_stage(const BdBwdRegs<D>& x, JFA_LDS char* qt, JFA_LDS char* kt,
+                                             JFA_LDS char* dot, int lane) {
+  using R = BdBwdRegs<D>;
+#pragma unroll
+  for (int j = 0; j < R::CH; ++j) {
+    const int idx = j * 64 + lane, r = idx / R::CPR, c = idx % R::CPR;
+    const int off = swz_off<2 * D>(r, c);
+    lds_st16(qt, off, x.q[j]);
+    lds_st16(kt, off, x.k[j]);
+    lds_st16(dot, off, x.dout[j]);
+  }
+}
+
+// PF: the tile's Q, K, dO are already in the wave's LDS tiles and its V, O rows and lse
+// come in `pf` (registers loaded one tile ahead); otherwise the tile loads them itself.
+template <int D, bool ROPE, bool PF = false>
 __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, JFA_LDS char* w, float* wf,
-                                            int lane) {
+                                            int lane, const BdBwdRegs<D>* pf = nullptr) {
   using C = BdCfg<D>;
   const int l32 = lane & 31, half = lane >> 5;
   const int64_t rs = (int64_t)p.num_heads * D;
@@ -333,10 +394,12 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
   JFA_LDS char* st = w + C::W_S;
   float* lse2 = wf + C::W_LSE / 4;
   float* di = wf + C::W_DI / 4;
-  dma_tile<C::RB, kBlock, 1>(p.q + base, rs, n, qt, 0, lane);
-  dma_tile<C::RB, kBlock, 1>(p.k + base, rs, n, kt, 0, lane);
-  dma_tile<C::RB, kBlock, 1>(p.dout + base, rs, n, dot, 0, lane);
-  const float lv = lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f;
+  if constexpr (!PF) {
+    dma_tile<C::RB, kBlock, 1>(p.q + base, rs, n, qt, 0, lane);
+    dma_tile<C::RB, kBlock, 1>(p.k + base, rs, n, kt, 0, lane);
+    dma_tile<C::RB, kBlock, 1>(p.dout + base, rs, n, dot, 0, lane);
+  }
+  const float lv = PF ? pf->lse : (lane < n ? p.lse_in[(int64_t)t.h * p.total_tokens + t.t0 + lane] : 0.f);
   // D = 64: this lane's table row is loaded while the tiles are in flight
   constexpr bool PRE = ROPE && D == 64;
   const float* tab_row = ROPE ? p.rope + (int64_t)(t.pos0 + min(lane, n - 1)) * D : nullptr;
@@ -351,7 +414,7 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
     for (int rb = 0; rb < 2; ++rb)
       acc_pairs<C::NDB>(p.rope + (int64_t)(t.pos0 + min(rb * 32 + l32, n - 1)) * D, half, epi[rb]);
   }
-  wait_vmem();
+  if constexpr (!PF) wait_vmem();
   if constexpr (ROPE) {
     // rows past the block's end stay as copied (their P and dS are zero)
     if (lane < n) rope_lds_row<D, PRE>(qt, kt, tab_row, pre, lane);
@@ -366,7 +429,8 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       const bf16x8 d8 = as_bf16x8(lds_ld16(dot, swz_off<C::RB>(row, 2 * ks + half)));
-      const bf16x8 o8 = as_bf16x8(row < n ? ld16(p.o_in + base + row * rs + 16 * ks + 8 * half) : zero16());
+      const bf16x8 o8 =
+          as_bf16x8(PF ? pf->o[qb][ks] : (row < n ? ld16(p.o_in + base + row * rs + 16 * ks + 8 * half) : zero16()));
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)d8[e], (float)o8[e], acc);
     }
@@ -382,7 +446,8 @@ __device__ __forceinline__ void bd_bwd_tile(const BdParams& p, const BdTile& t, 
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
       kf[ks] = as_bf16x8(lds_ld16(kt, swz_off<C::RB>(key, 2 * ks + half)));
-      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + key * rs + 16 * ks + 8 * half) : zero16());
+      if constexpr (PF) vf[ks] = pf->vf[kb][ks];
+      else vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + key * rs + 16 * ks + 8 * half) : zero16());
     }
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -522,8 +587,33 @@ __global__ void __launch_bounds__(BdCfg<D>::NW * 64)
   const int64_t P = gridDim.x, q = p.num_tiles / P, r = p.num_tiles % P;
   const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
   char* w = smem + wave * C::W_BWD;
-  for (int64_t g = start + wave; g < end; g += C::NW)
-    bd_bwd_tile<D, ROPE>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
+  if constexpr (D == 64) {
+    // software pipeline over the wave's tiles: stage tile g's operands (loaded during
+    // the previous tile), issue the loads of tile g + NW, then compute tile g
+    int64_t g = start + wave;
+    if (g >= end) return;
+    BdTile t = locate(p, g);
+    BdBwdRegs<D> nx;
+    bd_bwd_load<D>(p, t, nx, lane);
+    JFA_LDS char* lw = (JFA_LDS char*)w;
+    while (true) {
+      bd_bwd_stage<D>(nx, lw + C::W_Q, lw + C::W_K, lw + C::W_DO, lane);
+      const BdBwdRegs<D> cur = nx;
+      const int64_t gn = g + C::NW;
+      BdTile tn = t;
+      if (gn < end) {
+        tn = locate(p, gn);
+        bd_bwd_load<D>(p, tn, nx, lane);
+      }
+      bd_bwd_tile<D, ROPE, true>(p, t, lw, (float*)w, lane, &cur);
+      if (gn >= end) break;
+      g = gn;
+      t = tn;
+    }
+  } else {
+    for (int64_t g = start + wave; g < end; g += C::NW)
+      bd_bwd_tile<D, ROPE>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
+  }
 }
 
 int bd_programs(const BdParams& p, int nw) {
