@@ -622,20 +622,6 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   const int64_t sentinel = bq ? (int64_t)p.num_seqs * p.num_heads * p.num_q : (int64_t)p.num_heads * p.total_tokens;
   const int nq = (Lq + C::QB - 1) / C::QB;
 
-  // This wave's keys as B operands, straight from global (rows past the end -> 0).
-  bf16x8 kf[C::NKS], vf[C::NKS];
-  {
-    const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      // K pre-scaled by c = scale log2 e (rounded to bf16) so that S' = Q (cK)^T -
-      // lse log2 e is already the base-2 exponent of P
-      const bf16x8 kr = as_bf16x8(key_ok ? ld16(p.k + base + 16 * ks) : zero16());
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)kr[e] * c);
-      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
-    }
-  }
   // Three-slot ring: step it+2 is copied while step it is computed, so each copy has two
   // steps to land.  The wait that closes a step leaves only the newest step's copies
   // outstanding (vector-memory loads return in issue order, so the older step's copies
@@ -665,17 +651,31 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+  // The ring's first copies go out before this wave's key rows are loaded, so that the
+  // tile start waits out one memory round trip, not two.
   if (n > 0) {
     issue(step_of(0), 0);
-    bool waited = false;
     if constexpr (NS == 3) {
-      if (n > 1) {
-        issue(step_of(1), 1);
-        wait_vmem_n<COPIES>();
-        waited = true;
-      }
+      if (n > 1) issue(step_of(1), 1);
     }
-    if (!waited) wait_vmem();
+  }
+  // This wave's keys as B operands, straight from global (rows past the end -> 0).
+  bf16x8 kf[C::NKS], vf[C::NKS];
+  {
+    const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      // K pre-scaled by c = scale log2 e (rounded to bf16) so that S' = Q (cK)^T -
+      // lse log2 e is already the base-2 exponent of P
+      const bf16x8 kr = as_bf16x8(key_ok ? ld16(p.k + base + 16 * ks) : zero16());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)kr[e] * c);
+      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 16 * ks) : zero16());
+    }
+  }
+  if (n > 0) {
+    // step 0 (and, with three slots, step 1) landed; older than the key-row loads
+    wait_vmem();
     __syncthreads();
   }
 
