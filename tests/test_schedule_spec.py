@@ -160,3 +160,24 @@ def test_bq_fwd_schedule_unchunked_when_no_sequence_exceeds_a_share():
     assert S.bq_key_chunks(lengths, h, mq, rows, nprog) == [(b, 0, n) for b, n in enumerate(lengths)]
     tiles, _, _ = S.fwd_schedule(lengths, h, S.MODE_BROADCAST_Q, mq, rows, nprog, dynamic=True)
     assert tiles == S.sorted_cost_tiles(lengths, h, rows, lambda b: mq)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bq_cut_sequence_chunks_within_workspace_bound(seed):
+    # The library sizes the forward's partial-result slots (chunks of sequences cut into
+    # two or more) as min(2 P / (H ceil(Mq / 256)), 2 T / 256) + 1.  A cut sequence is
+    # longer than the chunk, which is at least max(256, H ceil(Mq/256) T / P) keys.
+    rng = np.random.default_rng(500 + seed)
+    for _ in range(50):
+        n = int(rng.integers(1, 80))
+        lengths = (rng.integers(0, 6000, size=n) * (rng.random(n) < 0.9)).tolist()
+        if rng.random() < 0.3:
+            lengths[int(rng.integers(0, n))] = int(rng.integers(20000, 60000))
+        h, mq, p = int(rng.integers(1, 9)), int(rng.integers(1, 1200)), int(rng.integers(1, 600))
+        ch = S.bq_key_chunks(lengths, h, mq, 256, p)
+        per_seq = {}
+        for c in ch:
+            per_seq[c[0]] = per_seq.get(c[0], 0) + 1
+        slots = sum(k for k in per_seq.values() if k > 1)
+        bound = min(2 * p // (h * _cdiv(mq, 256)), 2 * sum(lengths) // 256) + 1
+        assert slots <= bound
