@@ -164,9 +164,13 @@ void bq_key_chunks(const std::vector<int32_t>& lengths, int64_t H, int64_t Mq, i
   }
 }
 
-// Split backward: the most key chunks any lengths with these (B, T) give (chunks are at
-// least kBqChunkMinSteps * kKeyStep keys).
-int64_t bq_chunk_cap(int64_t B, int64_t T) { return B + T / (kBqChunkMinSteps * kKeyStep) + 1; }
+// Split backward: the most key chunks any lengths give.  A sequence that is not cut is
+// one chunk; the chunks of cut sequences number fewer than 2 T / keys, with keys at
+// least kBqChunkMinSteps * kKeyStep and at least H * ceil(Mq / kDqRows) * T / programs.
+int64_t bq_chunk_cap(int64_t B, int64_t H, int64_t Mq, int64_t T, int programs) {
+  return B + std::min<int64_t>(2 * (int64_t)programs / std::max<int64_t>(1, H * cdiv(Mq, kDqRows)),
+                               2 * T / (kBqChunkMinSteps * kKeyStep)) + 1;
+}
 
 // Forward: the most partial-result slots (chunks of sequences cut into two or more):
 // a cut sequence has L > keys >= max(256, H * ceil(Mq / rows) * T / P), so its
@@ -271,8 +275,8 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     // dQ kernel schedule (kDqRows-row tiles of the shared queries against one key chunk
     // each), the key-chunk table int32 [3, NC], the row terms [B, H, Mq, 8] + sentinel,
     // and the chunks' dQ slabs [NC, Mq, H, D] fp32 (NC <= B + T / minimum chunk)
-    L.chunk_cap = bq_chunk_cap(B, T);
     L.programs2_cap = max_programs(o, kDqWgPerCu);
+    L.chunk_cap = bq_chunk_cap(B, H, Mq, T, L.programs2_cap);
     L.seg2_cap = L.programs2_cap + 1;
     L.seg2 = at;
     at += align_up(L.seg2_cap * sizeof(int32_t));
