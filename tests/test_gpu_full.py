@@ -81,3 +81,30 @@ def test_full_size_broadcast_q(dq_path):
     o_ref, lse_ref = G.oracle_fwd(p)
     G.check_fwd(o, lse, o_ref, lse_ref, "workload 2 full")
     G.check_bwd(grads, G.oracle_bwd(p), "workload 2 full")
+
+
+@pytest.mark.parametrize("self_bwd", ["auto", "recompute"])
+def test_tensors_beyond_2_31_elements(self_bwd):
+    # 4200 sequences of 512 tokens, H = 8, D = 128: every [T, H, D] tensor holds 2.2e9
+    # elements, so the last sequences start past element 2^31 of q, k, v, o, dO, dQ, dK,
+    # dV (64-bit offsets everywhere); checked on the first, the last and seeded picks.
+    lengths = [512] * 4200
+    print(f"[case] 4200 x 512 tokens, H=8, D=128, self_bwd={self_bwd}", flush=True)
+    p = W.make_problem(lengths, 8, 128, W.MODE_SELF, seed=91, device="cuda")
+    assert p["total_tokens"] * 8 * 128 > 2 ** 31
+    opts = B.bench_opts(p["mode"], _shape(p), p["offsets_host"], self_bwd=self_bwd)
+    o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts)
+    dq, dk, dv = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"],
+                       p["scale"], opts)
+    torch.cuda.synchronize()
+    off = p["offsets_host"].astype(np.int64)
+    rng = np.random.default_rng(91)
+    picks = sorted({0, 4199, 4198, 2097} | {int(x) for x in rng.integers(0, 4200, size=2)})
+    for b in picks:
+        s, e = int(off[b]), int(off[b + 1])
+        sub = lambda t: G.f64(t[s:e])
+        q, k, v, do = sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"])
+        o_ref, lse_ref = oracle.attention_forward(q, k, v, [0, e - s], p["mode"], p["scale"])
+        G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"beyond 2^31 seq {b}")
+        refs = oracle.attention_backward(q, k, v, do, [0, e - s], p["mode"], p["scale"])
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"beyond 2^31 seq {b}")
