@@ -79,7 +79,8 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // Direct global -> LDS copy (global_load_lds_dwordx4): every lane fetches 16 bytes at
 // sbase + voff (sbase in scalar registers, voff a per-lane byte offset); the wave's 64
 // results land contiguously at lds_base + 16 * lane.  sbase and lds_base must be the
-// same for the whole wave (lds_base goes to M0).  Completion is tracked by vmcnt:
+// same for the whole wave (lds_base goes to M0, which the asm takes as an input operand
+// so that the compiler sets it and knows it is in use).  Completion is tracked by vmcnt:
 // wait_vmem() then a barrier before any wave reads the data.  The instruction is
 // issued from inline assembly on purpose: the compiler cannot tell which LDS bytes the
 // copy writes, and when it sees the copy it waits for it (vmcnt(0)) before the next LDS
@@ -89,8 +90,12 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // see only make its own vmcnt waits more conservative, never less.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, JFA_LDS char* lds_base) {
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+  // The leading s_nop 4 provides the wait states the hardware needs between a VALU write
+  // of an SGPR (the v_readfirstlane that makes sbase uniform, or M0's source) and a
+  // memory instruction reading it.  The compiler inserts such waits for instructions it
+  // knows but cannot see inside this asm; without them the copy may read the SGPR's old
+  // value as its base address.
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
