@@ -1,8 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is generated at full size on the GPU and run through jfa_fwd / jfa_bwd
-with the options bench.py uses by default (static schedule; the stored-dS
-self-attention backward at head_dim 128, the recompute one at 64; both broadcast-Q dQ
+with the options bench.py uses by default (tiles from the run-time counter; the stored-dS
+self-attention backward at head_dim 128, the recompute one at 64; the three broadcast-Q dQ
 paths), and workload 3 also with the recompute backward.
 The oracle then checks sampled sequences one by one -- the longest, the shortest, the
 median and a few seeded picks -- since in self and block-diagonal attention every

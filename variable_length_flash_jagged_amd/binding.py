@@ -140,11 +140,13 @@ def ds_budget_mib(shape, offsets_host):
     return max(1, -(-ds_bytes(shape, offsets_host) // (1 << 20)))
 
 
-def bench_opts(mode, shape, offsets_host, sched=0, dq_path=0, self_bwd="auto"):
-    """Options the benchmark runs with: the given schedule and broadcast-Q dQ path and,
-    for self attention, the backward path: "stored" grants the dS workspace (stored-dS
-    backward), "recompute" does not, "auto" takes the stored-dS backward at head_dim 128
-    (measured faster there) and the recompute backward at 64."""
+def bench_opts(mode, shape, offsets_host, sched=1, dq_path=2, self_bwd="auto"):
+    """Options the benchmark runs with: the given schedule (default: tiles taken from the
+    run-time counter, measured faster than the static deal) and broadcast-Q dQ path
+    (default 2, the fastest) and, for self attention, the backward path: "stored" grants
+    the dS workspace (stored-dS backward), "recompute" does not, "auto" takes the
+    stored-dS backward at head_dim 128 (measured faster there) and the recompute
+    backward at 64."""
     if self_bwd not in ("auto", "stored", "recompute"):
         raise ValueError(f"self_bwd must be auto, stored or recompute, got {self_bwd!r}")
     stored = self_bwd == "stored" or (self_bwd == "auto" and shape.head_dim == 128)
