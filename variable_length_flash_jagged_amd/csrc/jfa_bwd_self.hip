@@ -793,6 +793,261 @@ __global__ void __launch_bounds__(NW * 64)
             [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
+// ------------------------------------------- dK, dV: 16 keys per wave (head_dim 128)
+//
+// The products of dkdv_tile (recompute path) on v_mfma_f32_16x16x32_bf16 with 16 keys
+// per wave and eight waves per 128-key tile: a wave's K, V operands, dK, dV accumulators
+// and scores fit in 256 registers, so two waves share each SIMD and one wave's waits on
+// LDS data and matrix results are covered by the other's work.  Operand layouts
+// (16x16x32): A lane l <-> (row l%16, k 8*(l/16)..+7), B lane l <-> (column l%16, the
+// same k), C lane l <-> (column l%16, rows 4*(l/16)..+3).  S' = Q (cK)^T + row term and
+// dP' = dO V^T + row term come out with lane = key column and, for lane group g = l/16,
+// queries 4g..4g+3 of each 16-query block; dV^T += dO^T P and dK^T += Q^T dS contract
+// over each 32-query step in the order (4g..4g+3, 16+4g..16+4g+3), so the packed P and
+// dS registers are their B operands as they stand, and the A operands dO^T, Q^T are two
+// transposed reads of four rows each.
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Not used yet: parity-clean, but measured slower than dkdv_kernel on the production
+// workload's recompute pass (9.40 against 8.75 ms).  Its two waves per SIMD reach the
+// same phase of a step at the same time (the per-step barrier aligns them), so their
+// matrix and vector work does not overlap; pairing them one phase apart, as the
+// forward does, is the step that remains.
+constexpr bool kUseKv16 = false;
+constexpr int kKv16Waves = 8;
+
+template <int D>
+struct Kv16Cfg {
+  static constexpr int NW = kKv16Waves;
+  static constexpr int BN = NW * 16;    // keys per tile
+  static constexpr int QB = kBwdRows;   // queries per step
+  static constexpr int NQ16 = QB / 16;  // 16-query blocks of S', dP'
+  static constexpr int NK32 = QB / 32;  // 32-query k-steps of dV^T, dK^T
+  static constexpr int NKS = D / 32;    // 32-wide k-steps over the head dim
+  static constexpr int NDB = D / 16;    // 16-wide head-dim blocks of dK^T, dV^T
+  static constexpr int RB = 2 * D;
+  static constexpr int QBUF = QB * RB;
+  static constexpr int ABUF = QB * 16;
+  static constexpr int NS = 3;
+  static constexpr int OFF_Q = 0, OFF_DO = OFF_Q + NS * QBUF, OFF_AUG = OFF_DO + NS * QBUF;
+  static constexpr int SMEM = OFF_AUG + NS * ABUF;
+  static_assert(BN == kBwdKeys && QB == 64, "tiles of the backward schedule, one 64-lane row-term copy");
+};
+
+template <int D>
+struct Kv16Lane {
+  using Copy = TileCopy<Kv16Cfg<D>::RB, Kv16Cfg<D>::QB, kKv16Waves>;
+  Copy copy;
+  bf16x8 sel_s, sel_dp;  // B operands picking the row term's k-slots 0,1 (S') and 4,5 (dP')
+  __device__ __forceinline__ void init_sel(int lane) {
+    const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
+    const bool lo = lane < 16;
+    sel_s = bf16x8{lo ? one : zero, lo ? one : zero, zero, zero, zero, zero, zero, zero};
+    sel_dp = bf16x8{zero, zero, zero, zero, lo ? one : zero, lo ? one : zero, zero, zero};
+  }
+};
+
+// Head-dim columns of row m of block db of the transposed products: four runs of four,
+// run t = m / 4 at column kv16_col(db, t) -- 16-byte chunks c0 and c0 + 2 of the tile row
+// (c0 = 0, 1, 4, 5, 8, 9, 12, 13 over the blocks), both 8-byte halves of each.  With the
+// tiles' row swizzle this keeps the transposed reads of a 32-lane pass on 64 distinct
+// banks (sixteen consecutive columns would put two rows on each bank).
+__device__ __forceinline__ int kv16_col(int db, int t) {
+  const int c0 = (db & 1) | ((db >> 1) << 2);
+  return 8 * (c0 + 2 * (t & 1)) + 4 * (t >> 1);
+}
+
+// A operand [16 head-dim rows of block db x 32 queries] of the transposed product from a
+// row-major query tile: lane group g takes queries q0+4g..+3 and q0+16+4g..+3; lane i of
+// the group is row i, head-dim column kv16_col(db, i / 4) + i % 4.
+template <int RB>
+__device__ __forceinline__ bf16x8 tr16_operand(const JFA_LDS char* tile, int q0, int db, int lane) {
+  const int g = lane >> 4, s16 = lane & 15;
+  const int r = q0 + 4 * g + (s16 >> 2);
+  const int col = kv16_col(db, s16 & 3);
+  const int w8 = (col & 7) * 2;
+  return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8), lds_tr4(tile, swz_off<RB>(r + 16, col >> 3) + w8));
+}
+
+template <int D>
+__device__ __forceinline__ void kv16_step(const JFA_LDS char* qt, const JFA_LDS char* dot, const JFA_LDS char* augt,
+                                          const Kv16Lane<D>& ln, const bf16x8 (&kf)[Kv16Cfg<D>::NKS],
+                                          const bf16x8 (&vf)[Kv16Cfg<D>::NKS], f32x4 (&dk)[Kv16Cfg<D>::NDB],
+                                          f32x4 (&dv)[Kv16Cfg<D>::NDB], int lane) {
+  using C = Kv16Cfg<D>;
+  const int r16 = lane & 15, g = lane >> 4;
+  f32x4 s[C::NQ16], dp[C::NQ16];
+#pragma unroll
+  for (int qb = 0; qb < C::NQ16; ++qb) {
+    const int row = qb * 16 + r16;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // the row's 16-byte term sits in k-slots 0..7 (lane group 0); the other groups read
+    // it too (no branch inside the step) and mask it to zero
+    const u32x4 a16 = lds_ld16(augt, row * 16);
+    const uint32_t keep = g == 0 ? 0xFFFFFFFFu : 0u;
+    const bf16x8 aug = as_bf16x8(u32x4{a16.x & keep, a16.y & keep, a16.z & keep, a16.w & keep});
+    s[qb] = mfma16(aug, ln.sel_s, z);
+    dp[qb] = mfma16(aug, ln.sel_dp, z);
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const int off = swz_off<C::RB>(row, 4 * ks + g);
+      s[qb] = mfma16(as_bf16x8(lds_ld16(qt, off)), kf[ks], s[qb]);
+      dp[qb] = mfma16(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp[qb]);
+    }
+  }
+  // P = 2^S' (S' is the base-2 exponent: K pre-scaled, -lse log2 e in the row term) and
+  // dS = P (dP - Di) (-Di in the row term), packed as the B operands of the next products
+  bf16x8 pb[C::NK32], dsb[C::NK32];
+#pragma unroll
+  for (int kk = 0; kk < C::NK32; ++kk) {
+    float pv[8], dv8[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = fast_exp2(s[2 * kk][i]);
+      pv[4 + i] = fast_exp2(s[2 * kk + 1][i]);
+      dv8[i] = pv[i] * dp[2 * kk][i];
+      dv8[4 + i] = pv[4 + i] * dp[2 * kk + 1][i];
+    }
+    pb[kk] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+    dsb[kk] = pack8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
+  }
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int kk = 0; kk < C::NK32; ++kk) {
+      dv[db] = mfma16(tr16_operand<C::RB>(dot, 32 * kk, db, lane), pb[kk], dv[db]);
+      dk[db] = mfma16(tr16_operand<C::RB>(qt, 32 * kk, db, lane), dsb[kk], dk[db]);
+    }
+  // Issue order: LDS reads run ahead of the MFMAs that consume them -- the first eight up
+  // front, then one after each of the S', dP' MFMAs until that product's reads are out;
+  // the transposed reads of the dV, dK products (two per MFMA) start four MFMAs before
+  // the first of them, which keeps at most 15 LDS operations in flight.
+  constexpr int N1 = 2 * C::NQ16 * (C::NKS + 1);              // S', dP' MFMAs
+  constexpr int N2 = 2 * C::NDB * C::NK32;                    // dV, dK MFMAs
+  constexpr int R1 = C::NQ16 * (2 * C::NKS + 1);              // their LDS reads
+  constexpr int AHEAD = 8, LEAD2 = 4;
+  static_assert(R1 > AHEAD && R1 - AHEAD <= N1 - LEAD2, "read placement");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int k = 0; k < N1 + N2; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k < R1 - AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    else if (k >= N1 - LEAD2 && k < N1 - LEAD2 + N2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
+// Copies of one query step: Q, dO rows (all waves; rows past rows_valid repeat the last
+// valid row) and the row terms (wave 0; rows past rows_valid take the sentinel term).
+template <int D>
+__device__ __forceinline__ void kv16_issue(const Kv16Lane<D>& ln, const uint16_t* qb, const uint16_t* dob,
+                                           const uint16_t* aug, int64_t rs, int64_t aug_row0, int64_t sentinel,
+                                           int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
+                                           JFA_LDS char* augbuf, int wave, int lane) {
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rows_valid, qbuf, wave, lane);
+  ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rows_valid, dobuf, wave, lane);
+  if (wave == 0) {
+    const int64_t r = lane < rows_valid ? aug_row0 + row0 + lane : sentinel;
+    dma16(uniform_ptr(aug), (uint32_t)(r * 16), augbuf);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv16_tile(const BwdParams& p, Tile tile, char* smem_raw, const Kv16Lane<D>& ln,
+                                            int tid) {
+  using C = Kv16Cfg<D>;
+  JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int b = tile.b, h = tile.hb >> 24, j = tile.hb & 0xFFFFFF;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const int64_t s0 = p.offsets[b];
+  const int L = (int)(p.offsets[b + 1] - s0);
+  const int key0 = j * C::BN;
+  const int my_key = wave * 16 + r16;
+  const bool key_ok = my_key < L - key0;
+  const float c = p.scale_log2;
+  // query rows: the sequence's own tokens, or (broadcast-Q) the shared q rows with this
+  // sequence's dO and row terms
+  const bool bq = p.bq != 0;
+  const int Lq = bq ? p.num_q : L;
+  const uint16_t* qb = p.q + (bq ? 0 : s0 * rs) + (int64_t)h * D;
+  const uint16_t* dob = p.dout + (bq ? (int64_t)b * p.num_q : s0) * rs + (int64_t)h * D;
+  const int64_t aug_row0 = bq ? ((int64_t)b * p.num_heads + h) * p.num_q : (int64_t)h * p.total_tokens + s0;
+  const int64_t sentinel = bq ? (int64_t)p.num_seqs * p.num_heads * p.num_q : (int64_t)p.num_heads * p.total_tokens;
+  const int n = (Lq + C::QB - 1) / C::QB;
+  auto issue = [&](int it, int slot) {
+    const int row0 = it * C::QB;
+    kv16_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, Lq - row0),
+                  smem + C::OFF_Q + slot * C::QBUF, smem + C::OFF_DO + slot * C::QBUF,
+                  smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
+  };
+  constexpr int COPIES = 2 * Kv16Lane<D>::Copy::J;
+  f32x4 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dk[db][i] = dv[db][i] = 0.f;
+  // the ring's first copies go out before the key rows are loaded (one round trip)
+  if (n > 0) {
+    issue(0, 0);
+    if (n > 1) issue(1, 1);
+  }
+  // this wave's 16 keys as B operands (lane: key r16, head-dim k-group g), K pre-scaled
+  // by c = scale log2 e; rows past the end are zero (their dK, dV are not stored)
+  bf16x8 kf[C::NKS], vf[C::NKS];
+  {
+    const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 kr = as_bf16x8(key_ok ? ld16(p.k + base + 32 * ks) : zero16());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)kr[e] * c);
+      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 32 * ks) : zero16());
+    }
+  }
+  if (n > 0) {
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int it = 0, cur = 0; it < n; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
+    if (it + 2 < n) issue(it + 2, cur == 0 ? C::NS - 1 : cur - 1);
+    kv16_step<D>(smem + C::OFF_Q + cur * C::QBUF, smem + C::OFF_DO + cur * C::QBUF, smem + C::OFF_AUG + cur * C::ABUF,
+                 ln, kf, vf, dk, dv, lane);
+    if (it + 2 < n) wait_vmem_n<COPIES>();
+    else wait_vmem();
+    __syncthreads();
+  }
+  if (key_ok) {
+    // C layout: lane = key; rows 4g..4g+3 of block db are the four consecutive head-dim
+    // columns kv16_col(db, g) .. +3
+    const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = kv16_col(db, g);
+      st8(p.dk + row + d, pack4(dk[db][0] * p.scale, dk[db][1] * p.scale, dk[db][2] * p.scale, dk[db][3] * p.scale));
+      st8(p.dv + row + d, pack4(dv[db][0], dv[db][1], dv[db][2], dv[db][3]));
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kKv16Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    dkdv16_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[Kv16Cfg<D>::SMEM];
+  __shared__ int next_tile;
+  Kv16Lane<D> ln;
+  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
+  ln.init_sel(threadIdx.x & 63);
+  // broadcast-Q: head-pinned groups of programs_per_head programs
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : (int)gridDim.x, &next_tile,
+            [&](Tile t) { dkdv16_tile<D>(p, t, smem, ln, threadIdx.x); });
+}
+
 // --------------------------------------------------------- stored-dS path: row terms
 
 // Row terms for the dK/dV kernel when no dQ kernel runs before it: D/8 lanes per (token,
@@ -1046,6 +1301,7 @@ hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s)
   } else {
     if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true, false>), grid, block, 0, s, p);
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<128, false, true>), grid, block, 0, s, p);
+    else if (kUseKv16) hipLaunchKernelGGL((dkdv16_kernel<128>), grid, dim3(kKv16Waves * 64), 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<128, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
