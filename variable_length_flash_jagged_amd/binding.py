@@ -140,10 +140,10 @@ def ds_budget_mib(shape, offsets_host):
     return max(1, -(-ds_bytes(shape, offsets_host) // (1 << 20)))
 
 
-def bench_opts(mode, shape, offsets_host, sched=1, dq_path=2, self_bwd="auto"):
-    """Options the benchmark runs with: the given schedule (default: tiles taken from the
-    run-time counter, measured faster than the static deal) and broadcast-Q dQ path
-    (default 2, the fastest) and, for self attention, the backward path: "stored" grants
+def bench_opts(mode, shape, offsets_host, sched=0, dq_path=2, self_bwd="auto"):
+    """Options the benchmark runs with: the given schedule (default: the static deal) and
+    broadcast-Q dQ path (default 2, the fastest) and, for self attention, the backward
+    path: "stored" grants
     the dS workspace (stored-dS backward), "recompute" does not, "auto" takes the
     stored-dS backward at head_dim 128 (measured faster there) and the recompute
     backward at 64."""
