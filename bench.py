@@ -36,8 +36,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--sched", type=int, default=0,
-                    help="0 static host schedule (default), 1 the same order with tiles taken from a run-time counter")
+    ap.add_argument("--sched", type=int, default=1,
+                    help="0 static host schedule, 1 (default) the same tiles with one run-time counter per XCD")
     ap.add_argument("--dq-path", type=int, default=2,
                     help="broadcast-Q backward: 0 fused kernel + fp32 atomics, 1 fused kernel + per-program slabs, "
                          "2 dQ and dK/dV kernels + key-chunk slabs")

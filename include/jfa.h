@@ -108,8 +108,11 @@ typedef struct jfa_shape {
 /* Tuning options; pass NULL for the defaults (all zero). */
 typedef struct jfa_opts {
   int32_t sched;        /* 0: static host schedule (sorted zigzag / head-pinned round robin /
-                           contiguous ranges); 1: same order, tiles taken at run time from an
-                           atomic counter (block-diagonal mode is always static) */
+                           contiguous ranges); 1: same order, tiles taken at run time from
+                           atomic counters: one per XCD (8 groups of consecutive programs,
+                           each serving the tiles the static deal gives them) when the
+                           program count is a multiple of 8, else one; one per head in the
+                           broadcast-Q dK/dV kernel (block-diagonal mode is always static) */
   int32_t dq_path;      /* broadcast-Q backward only. 0: one fused kernel, dQ by fp32
                            atomics into one [Mq,H,D] accumulator; 1: the fused kernel with
                            per-program fp32 partial slabs [P,Mq,D] reduced by a second kernel
@@ -286,8 +289,8 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
  * Tiles are (b, h, blk) triples: forward tiles are tile_rows query rows, backward
  * tiles tile_rows key rows, block-diagonal tiles one 64-token block.  Static
  * schedules list tiles program by program with one segment per program
- * (seg_ptr[P+1]); dynamic schedules list the global order with one segment per
- * counter group.  tiles (3*cap int32) and seg_ptr (seg_cap int32) may be NULL to
+ * (seg_ptr[P+1]); dynamic schedules list each counter group's tiles in sorted order,
+ * one segment per group.  tiles (3*cap int32) and seg_ptr (seg_cap int32) may be NULL to
  * query the counts only; JFA_ERR_CAPACITY if an array is too small. */
 int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,
                  const jfa_opts* opts, int32_t* tiles, int64_t cap, int32_t* seg_ptr,

@@ -33,9 +33,14 @@ Readings where the pages leave the rule open:
   head's dQ only.
 * Broadcast-Q forward keeps the tiles of empty sequences (they must still write
   O = 0 and lse = -inf); self and block-diagonal modes have no tile for them.
-* Dynamic mode keeps the same global order; program p starts with tile p of its group
-  and then takes tiles from a per-group atomic counter.  Its output here is that
-  global order with one segment per counter group.
+* Dynamic mode keeps the sorted order; program p starts with tile p of its group
+  and then takes tiles from a per-group atomic counter.  The pages want neighbouring
+  tiles to meet in one L2; a single counter would scatter one sequence's tiles over
+  all L2s (each XCD has its own), so forward and self-attention backward schedules
+  keep one counter per XCD: when P is a multiple of 8 the programs form 8 groups of
+  P / 8 consecutive ids (one XCD each) and group g serves, in sorted order, the tiles
+  the zigzag deal gives its programs; otherwise one group serves all tiles.  The
+  output here is the tile list with one segment per counter group.
 * Broadcast-Q forward key chunks: with a few hundred tiles (one per sequence, head and
   query block), zigzag dealing cannot help when the tiles of the longest sequence
   alone take longer than the average program's share, so such a sequence's keys are
@@ -76,16 +81,33 @@ def sorted_cost_tiles(lengths, num_heads, rows, rows_of):
     return sorted(tiles, key=lambda t: (-int(lengths[t[0]]), t[0], t[1], t[2]))
 
 
-def _deal_zigzag(order, num_programs):
+XCDS = 8
+
+
+def counter_groups(num_programs):
+    """Counter groups of a dynamic forward or self-attention backward schedule."""
+    return XCDS if num_programs >= XCDS and num_programs % XCDS == 0 else 1
+
+
+def _deal_zigzag(order, num_programs, dynamic=False):
     n_tiles = len(order)
     p_used = min(num_programs, n_tiles)
     if p_used == 0:
-        return [], [0], 0
+        return [], ([0, 0] if dynamic else [0]), 0
     per_prog = [[] for _ in range(p_used)]
     for n, t in enumerate(order):
         per_prog[zigzag_program(n, p_used)].append(t)
+    if dynamic:
+        # one segment per group of p_used / G consecutive programs, in sorted order
+        g = counter_groups(p_used)
+        gsize = p_used // g
+        rank = {t: n for n, t in enumerate(order)}
+        segs = [sorted((t for lst in per_prog[k * gsize:(k + 1) * gsize] for t in lst), key=rank.__getitem__)
+                for k in range(g)]
+    else:
+        segs = per_prog
     tiles, ptr = [], [0]
-    for lst in per_prog:
+    for lst in segs:
         tiles.extend(lst)
         ptr.append(len(tiles))
     return tiles, ptr, p_used
@@ -111,7 +133,8 @@ def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=Fa
     """Forward schedule for MODE_SELF / MODE_BROADCAST_Q.
 
     Returns (tiles, segment_ptr, programs).  Static: tiles in program-major order and
-    one segment per program.  Dynamic: the sorted global order and one segment.  In
+    one segment per program.  Dynamic: one segment per counter group (counter_groups),
+    each holding in sorted order the tiles the static deal gives its programs.  In
     broadcast-Q mode a tile's first entry is the index of its key chunk in
     bq_key_chunks(...) (the sequence index when no sequence is cut)."""
     if mode == MODE_SELF:
@@ -121,9 +144,7 @@ def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=Fa
         order = sorted_cost_tiles(keys, num_heads, rows, lambda c: int(num_q))
     else:
         raise ValueError("fwd_schedule covers the self and broadcast-Q modes")
-    if dynamic:
-        return order, [0, len(order)], min(num_programs, len(order))
-    return _deal_zigzag(order, num_programs)
+    return _deal_zigzag(order, num_programs, dynamic)
 
 
 def bwd_schedule(lengths, num_heads, mode, rows, num_programs, dynamic=False):
@@ -132,9 +153,7 @@ def bwd_schedule(lengths, num_heads, mode, rows, num_programs, dynamic=False):
     broadcast-Q dynamic form has one segment per head."""
     if mode == MODE_SELF:
         order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(lengths[b]))
-        if dynamic:
-            return order, [0, len(order)], min(num_programs, len(order))
-        return _deal_zigzag(order, num_programs)
+        return _deal_zigzag(order, num_programs, dynamic)
     if mode != MODE_BROADCAST_Q:
         raise ValueError("bwd_schedule covers the self and broadcast-Q modes")
     per_head = [[(b, h, j) for b in range(len(lengths)) for j in range(_cdiv(int(lengths[b]), rows))]

@@ -1,7 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is generated at full size on the GPU and run through jfa_fwd / jfa_bwd
-with the options bench.py uses by default (static schedule; the stored-dS
+with the options bench.py uses by default (per-XCD run-time tile counters; the stored-dS
 self-attention backward at head_dim 128, the recompute one at 64; the three broadcast-Q dQ
 paths), and workload 3 also with the recompute backward.
 The oracle then checks sampled sequences one by one -- the longest, the shortest, the

@@ -63,11 +63,37 @@ def test_fwd_covers_every_tile_once_and_balances(seed, mode):
     cost = {t: lengths[t[0]] for t in tiles}
     loads = [sum(cost[t] for t in tiles[ptr[i]:ptr[i + 1]]) for i in range(p)]
     assert max(loads) - min(loads) <= max(lengths)
-    # dynamic mode: the same tiles in global sorted order
+    # dynamic mode (13 programs: one counter group): the same tiles in global sorted order
     dt, dptr, dp = S.fwd_schedule(lengths, h, mode, mq, rows, nprog, dynamic=True)
     assert sorted(dt) == sorted(tiles) and dptr == [0, len(dt)] and dp == p
     keys = [(-lengths[t[0]], t) for t in dt]
     assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("nprog", [16, 24, 40, 7])
+def test_dynamic_counter_groups_hold_one_xcds_static_tiles(seed, nprog):
+    # Dynamic schedules keep one counter per XCD when the program count is a multiple
+    # of 8: group g (programs g P/8 .. (g+1) P/8 - 1) serves exactly the tiles the
+    # static zigzag deal gives those programs, in sorted order.
+    rng = np.random.default_rng(700 + seed)
+    lengths = _random_lengths(rng, 40)
+    h, rows = 2, 64
+    tiles, ptr, p = S.bwd_schedule(lengths, h, S.MODE_SELF, rows, nprog)
+    dt, dptr, dp = S.bwd_schedule(lengths, h, S.MODE_SELF, rows, nprog, dynamic=True)
+    assert dp == p
+    g = 8 if p % 8 == 0 else 1
+    assert len(dptr) == g + 1 and sorted(dt) == sorted(tiles)
+    order = S.sorted_cost_tiles(lengths, h, rows, lambda b: lengths[b])
+    rank = {t: n for n, t in enumerate(order)}
+    gs = p // g
+    for k in range(g):
+        seg = dt[dptr[k]:dptr[k + 1]]
+        static = [t for q in range(k * gs, (k + 1) * gs) for t in tiles[ptr[q]:ptr[q + 1]]]
+        assert sorted(seg) == sorted(static)
+        assert [rank[t] for t in seg] == sorted(rank[t] for t in seg)
+        # the group's first tiles are those its programs start with under the static deal
+        assert seg[:gs] == [tiles[ptr[q]] for q in range(k * gs, (k + 1) * gs)][:len(seg)]
 
 
 @pytest.mark.parametrize("seed", range(5))

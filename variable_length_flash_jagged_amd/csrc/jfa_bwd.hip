@@ -31,6 +31,7 @@
 //    and a second kernel sums the slabs of each head.
 #include "jfa_device.h"
 #include "jfa_internal.h"
+#include "jfa_sched.h"
 
 namespace jfa {
 namespace {
@@ -311,8 +312,8 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
   __shared__ int next_tile;
   const int tid = threadIdx.x;
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
-  // Counter groups: one per head in broadcast-Q mode (head-pinned), one otherwise.
-  const int gsize = (MODE == kBroadcastQ) ? p.programs_per_head : p.num_programs;
+  // Counter groups: one per head in broadcast-Q mode (head-pinned), one per XCD otherwise.
+  const int gsize = (MODE == kBroadcastQ) ? p.programs_per_head : p.num_programs / dynamic_groups(p.num_programs);
   const int grp = prog / gsize, rank = prog % gsize;
   int idx, end, base = 0;
   if (!p.dynamic) {

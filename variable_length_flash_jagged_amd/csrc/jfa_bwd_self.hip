@@ -48,6 +48,7 @@
 
 #include "jfa_device.h"
 #include "jfa_internal.h"
+#include "jfa_sched.h"
 
 namespace jfa {
 namespace {
@@ -732,7 +733,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, Tile tile, char* s
 
 // Persistent tile loop shared by the kernels: static per-program lists, or (dynamic)
 // groups of gsize consecutive programs, group g taking tiles seg_ptr[g] .. seg_ptr[g+1]
-// first one each, then from its atomic counter counters[g].
+// first one each, then from its atomic counter counters[g].  xcd_gsize: the group size
+// of a forward-rule schedule (one group per XCD, or one of all programs).
+__device__ __forceinline__ int xcd_gsize() { return (int)gridDim.x / dynamic_groups((int)gridDim.x); }
+
 template <class F>
 __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles, const int32_t* seg_ptr,
                                           int32_t* counters, int gsize, int* next_tile, F&& body) {
@@ -771,7 +775,7 @@ __global__ void __launch_bounds__(kDqWaves * 64)
   ln.row.init(threadIdx.x & 63);
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, (int)gridDim.x, &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile,
             [&](Tile t) { dq_tile<D, SPARSE>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
@@ -789,7 +793,7 @@ __global__ void __launch_bounds__(NW * 64)
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   // broadcast-Q: head-pinned groups of programs_per_head programs
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : (int)gridDim.x, &next_tile,
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile,
             [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
@@ -1044,7 +1048,7 @@ __global__ void __launch_bounds__(kKv16Waves * 64) __attribute__((amdgpu_waves_p
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   ln.init_sel(threadIdx.x & 63);
   // broadcast-Q: head-pinned groups of programs_per_head programs
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : (int)gridDim.x, &next_tile,
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile,
             [&](Tile t) { dkdv16_tile<D>(p, t, smem, ln, threadIdx.x); });
 }
 
@@ -1265,7 +1269,7 @@ __global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   ln.init(threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, (int)gridDim.x, &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile,
             [&](Tile t) { dq_ds_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 

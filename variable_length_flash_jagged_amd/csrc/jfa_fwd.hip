@@ -37,6 +37,7 @@
 //    Cluster Launch Control").
 #include "jfa_device.h"
 #include "jfa_internal.h"
+#include "jfa_sched.h"
 
 namespace jfa {
 namespace {
@@ -378,20 +379,23 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
   ln.krow.init(tid & 63);
   ln.vtr.init(tid & 63);
   ln.copy.init((uint32_t)(p.num_kv_heads * D * 2), tid >> 6, tid & 63);  // k, v row stride
-  int idx, end;
+  // dynamic: counter group grp (one XCD's programs) takes its own tile segment
+  const int gsize = gridDim.x / dynamic_groups(gridDim.x), grp = prog / gsize;
+  int idx, end, base = 0;
   if (!p.dynamic) {
     idx = p.seg_ptr[prog];
     end = p.seg_ptr[prog + 1];
   } else {
-    idx = prog;
-    end = p.seg_ptr[1];
+    base = p.seg_ptr[grp];
+    end = p.seg_ptr[grp + 1];
+    idx = base + prog % gsize;
   }
   while (idx < end) {
     fwd_tile<D, MODE>(p, p.tiles[idx], smem, ln, tid);
     if (!p.dynamic) {
       ++idx;
     } else {
-      if (tid == 0) next_tile = p.num_programs + atomicAdd(p.counters, 1);
+      if (tid == 0) next_tile = base + gsize + atomicAdd(p.counters + grp, 1);
       __syncthreads();
       idx = next_tile;
       __syncthreads();

@@ -33,22 +33,26 @@ void sorted_tiles(const std::vector<int32_t>& lengths, int num_heads, int rows,
 }
 
 // Zigzag dealing: sorted position n -> program pos (even pass) or P-1-pos (odd pass).
-void deal_zigzag(const std::vector<HostTile>& order, int max_programs, Schedule& out) {
+// Static: one segment per program.  Dynamic: one segment per counter group, the
+// group's programs' tiles in sorted order.
+void deal_zigzag(const std::vector<HostTile>& order, int max_programs, bool dynamic, Schedule& out) {
   const int64_t n = (int64_t)order.size();
   const int p = (int)std::min<int64_t>(max_programs, n);
+  const int g = dynamic ? dynamic_groups(p) : p;
   out.programs = p;
-  out.groups = 0;
-  out.seg_ptr.assign(p + 1, 0);
+  out.groups = dynamic ? g : 0;
+  out.seg_ptr.assign(g + 1, 0);
   out.tiles.resize(n);
   if (p == 0) return;
-  auto prog_of = [p](int64_t i) {
+  const int gsize = p / g;
+  auto seg_of = [p, gsize](int64_t i) {
     const int64_t r = i / p, pos = i % p;
-    return (int)((r & 1) ? p - 1 - pos : pos);
+    return (int)((r & 1) ? p - 1 - pos : pos) / gsize;
   };
-  for (int64_t i = 0; i < n; ++i) out.seg_ptr[prog_of(i) + 1]++;
-  for (int i = 0; i < p; ++i) out.seg_ptr[i + 1] += out.seg_ptr[i];
+  for (int64_t i = 0; i < n; ++i) out.seg_ptr[seg_of(i) + 1]++;
+  for (int i = 0; i < g; ++i) out.seg_ptr[i + 1] += out.seg_ptr[i];
   std::vector<int32_t> fill(out.seg_ptr.begin(), out.seg_ptr.end() - 1);
-  for (int64_t i = 0; i < n; ++i) out.tiles[fill[prog_of(i)]++] = order[i];
+  for (int64_t i = 0; i < n; ++i) out.tiles[fill[seg_of(i)]++] = order[i];
 }
 
 }  // namespace
@@ -61,14 +65,7 @@ void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
   std::vector<HostTile> order;
   sorted_tiles(lengths, num_heads, rows, rows_of, order);
   out.tile_rows = rows;
-  if (dynamic) {
-    out.programs = (int)std::min<int64_t>(max_programs, (int64_t)order.size());
-    out.groups = 1;
-    out.seg_ptr = {0, (int32_t)order.size()};
-    out.tiles = std::move(order);
-    return;
-  }
-  deal_zigzag(order, max_programs, out);
+  deal_zigzag(order, max_programs, dynamic, out);
 }
 
 void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
@@ -77,14 +74,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
   if (mode == kSelfMode) {
     std::vector<HostTile> order;
     sorted_tiles(lengths, num_heads, rows, lengths, order);
-    if (dynamic) {
-      out.programs = (int)std::min<int64_t>(max_programs, (int64_t)order.size());
-      out.groups = 1;
-      out.seg_ptr = {0, (int32_t)order.size()};
-      out.tiles = std::move(order);
-      return;
-    }
-    deal_zigzag(order, max_programs, out);
+    deal_zigzag(order, max_programs, dynamic, out);
     return;
   }
   // Broadcast-Q: head-pinned round robin.

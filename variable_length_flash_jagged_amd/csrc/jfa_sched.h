@@ -11,7 +11,11 @@
 //  * only valid (non-empty) tiles are listed, except broadcast-Q forward tiles of an
 //    empty sequence, which still write O = 0 and lse = -inf;
 //  * dynamic mode keeps the same order and lets programs take tiles from an atomic
-//    counter (one per group);
+//    counter (one per group).  Forward and self-attention backward tiles form one
+//    group per XCD when the program count is a multiple of kXcds: group g is the
+//    programs g*P/kXcds .. (g+1)*P/kXcds - 1 (one XCD, see xcd_program_id) and holds,
+//    in sorted order, the tiles the zigzag deal gives those programs, so neighbouring
+//    tiles of one sequence still meet in one L2; otherwise one group of all tiles;
 //  * block-diagonal tiles (one 64-token block of one head, head fastest) get balanced
 //    contiguous ranges from divmod.
 #pragma once
@@ -21,6 +25,11 @@
 #include <vector>
 
 namespace jfa {
+
+constexpr int kXcds = 8;
+
+// Counter groups of a dynamic forward or self-attention backward schedule of P programs.
+constexpr int dynamic_groups(int programs) { return programs >= kXcds && programs % kXcds == 0 ? kXcds : 1; }
 
 struct HostTile {
   int32_t b, h, blk;
