@@ -30,6 +30,18 @@ def test_self_dynamic_schedule():
     G.run_case(RAGGED + [511, 2], 2, 128, opts=B.make_opts(sched=1), seed=4, label="self dynamic")
 
 
+@pytest.mark.parametrize("nprog", [16, 24])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_dynamic_per_xcd_counter_groups(nprog, head_dim):
+    # nprog a multiple of 8: eight counter groups (one per XCD) of nprog / 8 programs,
+    # each serving the tiles the static deal gives its programs, several per program
+    lengths = RAGGED + [700, 33, 1, 400]
+    G.run_case(lengths, 2, head_dim, opts=B.make_opts(sched=1, num_programs=nprog), seed=61,
+               label=f"self xcd groups P{nprog} D{head_dim}")
+    G.run_case(lengths, 2, head_dim, opts=_ds_opts(lengths, 2, head_dim, sched=1, num_programs=nprog), seed=62,
+               label=f"stored dS xcd groups P{nprog} D{head_dim}")
+
+
 def test_self_few_programs():
     # many tiles per persistent workgroup
     G.run_case(RAGGED, 2, 128, opts=B.make_opts(num_programs=3), seed=5, label="self 3 programs")
