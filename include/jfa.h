@@ -285,6 +285,25 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
                          void* workspace, size_t workspace_bytes,
                          const jfa_opts* opts, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels and results as jfa_fwd without the workspace: the workspace is a
+ * file-scope device array of JFA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (its address is looked up once per device, on
+ * the first call there).  The call allocates no device or pinned host memory (no
+ * hipMalloc, hipHostMalloc or hipFree; the host-side schedule is built in ordinary
+ * heap memory and goes up by a pageable-memory copy, which the runtime has taken when
+ * the call returns) and does not use the kernel timing hook.  Shapes whose jfa_fwd
+ * workspace (jfa_workspace_size, pass JFA_PASS_FWD) exceeds the array return
+ * JFA_ERR_TOO_LARGE before any device work.  Every call on one GPU shares that GPU's
+ * array and each call overwrites it (counters included), so calls that overlap on one
+ * GPU (other streams, other host threads) race: serialise them. */
+#define JFA_NOALLOC_SCRATCH_BYTES (4u << 20)
+int jfa_fwd_noalloc(const jfa_shape* shape, int mode, float scale,
+                    const void* q, const void* k, const void* v,
+                    const int32_t* offsets_dev, const int32_t* offsets_host,
+                    void* o, float* lse, const jfa_opts* opts, void* stream);
+
 /* Host-only view of the tile schedule the calls above would run (no device needed).
  * Tiles are (b, h, blk) triples: forward tiles are tile_rows query rows, backward
  * tiles tile_rows key rows, block-diagonal tiles one 64-token block.  Static

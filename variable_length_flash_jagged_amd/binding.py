@@ -66,6 +66,8 @@ def lib():
         L.jfa_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.c_int, op, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_fwd.restype = ctypes.c_int
         L.jfa_fwd.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, op, vp]
+        L.jfa_fwd_noalloc.restype = ctypes.c_int
+        L.jfa_fwd_noalloc.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, op, vp]
         L.jfa_bwd.restype = ctypes.c_int
         L.jfa_bwd.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               ctypes.c_size_t, op, vp]
@@ -255,6 +257,36 @@ def fwd(q, k, v, offsets, offsets_host=None, mode=MODE_SELF, scale=None, opts=No
     _check(lib().jfa_fwd(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
                          host.ctypes.data if host is not None else None, _ptr(o), _ptr(lse), _ptr(workspace),
                          workspace.numel(), ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_fwd")
+    return o, lse
+
+
+def fwd_noalloc(q, k, v, offsets, offsets_host=None, mode=MODE_SELF, scale=None, opts=None, o=None, lse=None,
+                stream=None):
+    """Forward through jfa_fwd_noalloc (no workspace argument: the library's device
+    scratch array).  Returns (o, lse); o and lse are allocated here when not given."""
+    import torch
+    nb, h, d, t, mq, hkv = _sizes(q, k, v, offsets, mode)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, x, torch.bfloat16)
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t, mq, hkv if hkv != h else 0)
+    if mode == MODE_BROADCAST_Q:
+        o_shape, lse_shape = (nb, mq, h, d), (nb, h, mq)
+    else:
+        o_shape, lse_shape = (t, h, d), (h, t)
+    if o is None:
+        o = torch.empty(o_shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    _check_tensor("o", o, torch.bfloat16, o_shape)
+    _check_tensor("lse", lse, torch.float32, lse_shape)
+    host = None
+    if offsets_host is not None:
+        host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_fwd_noalloc(ctypes.byref(shape), mode, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                 host.ctypes.data if host is not None else None, _ptr(o), _ptr(lse),
+                                 ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_fwd_noalloc")
     return o, lse
 
 

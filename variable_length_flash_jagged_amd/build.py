@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
 
 SOURCES = ["jfa_api.cpp", "jfa_sched.cpp", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_bwd_self.hip", "jfa_bd.hip",
-           "jfa_sparse.hip", "jfa_mxfp8.hip"]
+           "jfa_sparse.hip", "jfa_mxfp8.hip", "jfa_noalloc.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code (the host pass warns that it
 # does not know the feature; that warning is harmless).

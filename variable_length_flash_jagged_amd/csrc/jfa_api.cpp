@@ -22,6 +22,8 @@
 
 using namespace jfa;
 
+static_assert(JFA_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "scratch size in the header");
+
 namespace {
 
 thread_local std::string g_detail;
@@ -378,6 +380,17 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   e = hipEventRecord(s.ev, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   s.pending = true;
+  return JFA_OK;
+}
+
+// Allocation-free variant of upload(): a plain copy from the caller's (pageable) host
+// bytes.  The runtime stages pageable memory itself and returns once it has taken the
+// bytes, so `src` may be reused as soon as this returns.  No pinned staging buffer is
+// allocated.
+int upload_pageable(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  if (bytes == 0) return JFA_OK;
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "uploading the schedule");
   return JFA_OK;
 }
 
@@ -1055,11 +1068,14 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
   return JFA_OK;
 }
 
-// jfa_fwd, and jfa_fwd_rotary with rope non-null (block-diagonal mode only).
+// jfa_fwd, jfa_fwd_rotary with rope non-null (block-diagonal mode only), and
+// jfa_fwd_noalloc (noalloc: the workspace is this device's file-scope scratch array,
+// the schedule goes up by a pageable copy, and the timing hook is not used, so that
+// nothing is allocated).
 static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
                      const float* rope, int32_t rope_positions, const int32_t* offsets_dev,
                      const int32_t* offsets_host, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                     const jfa_opts* opts, void* stream_) {
+                     const jfa_opts* opts, void* stream_, bool noalloc = false) {
   g_detail.clear();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
@@ -1068,28 +1084,39 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     return fail(JFA_ERR_BAD_MODE, "the fused rotary embedding is built for the block-diagonal mode only");
   Opts op;
   if ((rc = check_opts(opts, op))) return rc;
-  if (!q || !k || !v || !o || !lse || !offsets_dev || !workspace)
+  Layout L;
+  layout_for(shape, mode, JFA_PASS_FWD, op, L);
+  if (noalloc && L.total > kNoAllocScratchBytes)
+    return fail(JFA_ERR_TOO_LARGE, "jfa_fwd_noalloc: this shape needs %zu bytes of scratch, more than its %zu",
+                L.total, kNoAllocScratchBytes);
+  if (!q || !k || !v || !o || !lse || !offsets_dev || (!noalloc && !workspace))
     return fail(JFA_ERR_NULL_POINTER, "q, k, v, o, lse, offsets_dev and workspace must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(JFA_ERR_MISALIGNED, "q, k, v, o must be 16-byte aligned and lse 4-byte aligned");
-  if (!aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!noalloc && !aligned(workspace, kAlign)) return fail(JFA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
-  Layout L;
-  layout_for(shape, mode, JFA_PASS_FWD, op, L);
-  if (workspace_bytes < L.total)
+  if (!noalloc && workspace_bytes < L.total)
     return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
   std::vector<int32_t> lengths;
   if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
   if (rope && (rc = check_rope(rope, rope_positions, lengths))) return rc;
+  if (noalloc) {
+    hipError_t e = noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "looking up the device scratch array");
+  }
   char* ws = (char*)workspace;
   const int H = shape->num_heads, D = shape->head_dim;
+  auto put = [&](const void* src, size_t bytes, void* dst) {
+    return noalloc ? upload_pageable(src, bytes, dst, stream) : upload(src, bytes, dst, stream);
+  };
+  auto launch = [&](int kernel, auto fn) { return noalloc ? fn() : timed_launch(kernel, stream, fn); };
 
   if (mode == JFA_MODE_BLOCK_DIAG) {
     std::vector<int32_t> prefix(shape->num_seqs + 1, 0);
     for (int b = 0; b < shape->num_seqs; ++b) prefix[b + 1] = prefix[b] + (int32_t)cdiv(lengths[b], kBlock);
     const int64_t ntiles = (int64_t)prefix.back() * H;
     if (ntiles == 0) return JFA_OK;
-    if ((rc = upload(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix, stream))) return rc;
+    if ((rc = put(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix))) return rc;
     BdParams p{};
     p.q = (const uint16_t*)q;
     p.k = (const uint16_t*)k;
@@ -1107,7 +1134,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     p.scale = scale;
     p.scale_log2 = scale * kLog2eHost;
     p.rope = rope;
-    return launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_bd_fwd(p, D, stream); }),
+    return launch_status(launch(JFA_KERNEL_FWD, [&] { return launch_bd_fwd(p, D, stream); }),
                          "block-diagonal forward launch");
   }
 
@@ -1146,7 +1173,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
   std::vector<char> buf;
   serialise(sc, L, buf, nullptr, nullptr, table.empty() ? nullptr : &table);
-  if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
+  if ((rc = put(buf.data(), buf.size(), ws))) return rc;
   FwdParams p{};
   if (mode == JFA_MODE_BROADCAST_Q) {
     p.chunks = (const int32_t*)(ws + L.chunks);
@@ -1171,7 +1198,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   p.total_tokens = shape->total_tokens;
   p.dynamic = op.sched;
   p.scale_log2 = scale * kLog2eHost;
-  if ((rc = launch_status(timed_launch(JFA_PASS_FWD, stream, [&] { return launch_fwd(p, mode, D, stream); }),
+  if ((rc = launch_status(launch(JFA_KERNEL_FWD, [&] { return launch_fwd(p, mode, D, stream); }),
                           "forward launch")))
     return rc;
   if (ncut == 0) return JFA_OK;
@@ -1183,6 +1210,13 @@ int jfa_fwd(const jfa_shape* shape, int mode, float scale, const void* q, const 
             size_t workspace_bytes, const jfa_opts* opts, void* stream) {
   return fwd_entry(shape, mode, scale, q, k, v, nullptr, 0, offsets_dev, offsets_host, o, lse, workspace,
                    workspace_bytes, opts, stream);
+}
+
+int jfa_fwd_noalloc(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,
+                    const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse,
+                    const jfa_opts* opts, void* stream) {
+  return fwd_entry(shape, mode, scale, q, k, v, nullptr, 0, offsets_dev, offsets_host, o, lse, nullptr, 0, opts,
+                   stream, true);
 }
 
 int jfa_fwd_rotary(const jfa_shape* shape, int mode, float scale, const void* q, const void* k, const void* v,

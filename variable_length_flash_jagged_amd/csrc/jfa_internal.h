@@ -257,6 +257,12 @@ struct MxParams {
   float scale_log2;
 };
 
+// Allocation-free forward (jfa_fwd_noalloc): bytes of the file-scope device scratch
+// array that stands in for the workspace, and the calling device's address of it
+// (looked up with hipGetSymbolAddress on the first call on each device).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Launchers (defined next to their kernels).  head_dim selects the instantiation.
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
 // Broadcast-Q forward: merge the chunk partials of the `cuts` cut sequences into o, lse.
