@@ -36,6 +36,14 @@ Readings where the pages are silent:
 
 All inputs are promoted to float64 before any arithmetic; bf16 inputs therefore
 enter with their exact values.
+
+The backward takes the forward's output O as one of its inputs (bittide page, section
+4: Di = rowsum(dO * O) is formed from the O the forward wrote).  By default the oracle
+uses its own exact O, which gives the analytic gradient; with ``o_given`` it forms Di
+from the O passed in (for instance the bf16 O of the library's forward), which is the
+same backward formula evaluated on the inputs the library's backward receives.  The
+two differ only through Di: dV is unchanged, and dQ, dK move by the first-order terms
+of dS = P * (dP - Di) in Di.
 """
 
 import numpy as np
@@ -72,13 +80,16 @@ def sequence_forward(q, k, v, scale):
     return o, lse, p
 
 
-def sequence_backward(q, k, v, do, scale):
+def sequence_backward(q, k, v, do, scale, o_given=None):
     """Gradient of sum(O * dO) for one head of one sequence, P recomputed from
-    (q, k, v) in fp64.  Returns (dq [Lq, D], dk [Lk, D], dv [Lk, D])."""
+    (q, k, v) in fp64.  Returns (dq [Lq, D], dk [Lk, D], dv [Lk, D]).  o_given [Lq, D]:
+    the forward output Di is formed from (default: the exact O)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     if k.shape[0] == 0:
         return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     o, _, p = sequence_forward(q, k, v, scale)
+    if o_given is not None:
+        o = _f64(o_given)
     dv = p.T @ do
     dp = do @ v.T
     di = (do * o).sum(axis=1)
@@ -139,11 +150,13 @@ def attention_forward(q, k, v, offsets, mode=MODE_SELF, scale=None, block=64):
     return o, lse
 
 
-def attention_backward(q, k, v, do, offsets, mode=MODE_SELF, scale=None, block=64):
+def attention_backward(q, k, v, do, offsets, mode=MODE_SELF, scale=None, block=64, o_given=None):
     """Backward over the whole jagged batch; returns (dq, dk, dv) with the shapes of
     (q, k, v).  In MODE_BROADCAST_Q dq sums the per-sequence contributions and do is
-    [B, Mq, H, D]."""
+    [B, Mq, H, D].  o_given (the layout of the forward's o): the forward output Di is
+    formed from (default: the exact O)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    og = None if o_given is None else _f64(o_given)
     t, h, d = k.shape
     if q.shape[1] != h:
         raise ValueError("the backward needs one query head per key/value head")
@@ -157,7 +170,8 @@ def attention_backward(q, k, v, do, offsets, mode=MODE_SELF, scale=None, block=6
         for b in range(len(off) - 1):
             s, e = off[b], off[b + 1]
             for hh in range(h):
-                g_q, g_k, g_v = sequence_backward(q[:, hh], k[s:e, hh], v[s:e, hh], do[b, :, hh], scale)
+                g_q, g_k, g_v = sequence_backward(q[:, hh], k[s:e, hh], v[s:e, hh], do[b, :, hh], scale,
+                                                  None if og is None else og[b, :, hh])
                 dq[:, hh] += g_q
                 dk[s:e, hh] = g_k
                 dv[s:e, hh] = g_v
@@ -169,7 +183,8 @@ def attention_backward(q, k, v, do, offsets, mode=MODE_SELF, scale=None, block=6
         if e == s:
             continue
         for hh in range(h):
-            g_q, g_k, g_v = sequence_backward(q[s:e, hh], k[s:e, hh], v[s:e, hh], do[s:e, hh], scale)
+            g_q, g_k, g_v = sequence_backward(q[s:e, hh], k[s:e, hh], v[s:e, hh], do[s:e, hh], scale,
+                                              None if og is None else og[s:e, hh])
             dq[s:e, hh] = g_q
             dk[s:e, hh] = g_k
             dv[s:e, hh] = g_v

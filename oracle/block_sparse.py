@@ -127,10 +127,13 @@ def block_sparse_forward(q, k, v, offsets, selection, scale=None, q_block=Q_BLOC
     return o, lse
 
 
-def block_sparse_backward(q, k, v, do, offsets, selection, scale=None, q_block=Q_BLOCK, k_block=K_BLOCK):
+def block_sparse_backward(q, k, v, do, offsets, selection, scale=None, q_block=Q_BLOCK, k_block=K_BLOCK,
+                          o_given=None):
     """Gradient of sum(O * dO) of ``block_sparse_forward`` for a fixed selection.
-    Returns (dq, dk, dv), each [T, H, D]."""
+    Returns (dq, dk, dv), each [T, H, D].  o_given [T, H, D]: the forward output Di is
+    formed from (default: the exact O; see attention.py)."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    og = None if o_given is None else np.asarray(o_given, dtype=np.float64)
     t, h, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
         raise ValueError("the block-sparse backward takes q, k, v, do all [T, H, D] (no grouped heads)")
@@ -145,7 +148,8 @@ def block_sparse_backward(q, k, v, do, offsets, selection, scale=None, q_block=Q
                 r1 = min(r0 + q_block, e)
                 keys = np.concatenate([np.arange(s + j * k_block, min(s + (j + 1) * k_block, e))
                                        for j in selection[b][hh][i]]).astype(np.int64)
-                g_q, g_k, g_v = sequence_backward(q[r0:r1, hh], k[keys, hh], v[keys, hh], do[r0:r1, hh], scale)
+                g_q, g_k, g_v = sequence_backward(q[r0:r1, hh], k[keys, hh], v[keys, hh], do[r0:r1, hh], scale,
+                                                  None if og is None else og[r0:r1, hh])
                 dq[r0:r1, hh] = g_q
                 dk[keys, hh] += g_k
                 dv[keys, hh] += g_v

@@ -67,8 +67,9 @@ def rotary_block_forward(q, k, v, offsets, table, scale=None, block=64):
                              scale, block)
 
 
-def rotary_block_backward(q, k, v, do, offsets, table, scale=None, block=64):
-    """Gradients of sum(O * dO) with respect to q, k (un-rotated) and v."""
+def rotary_block_backward(q, k, v, do, offsets, table, scale=None, block=64, o_given=None):
+    """Gradients of sum(O * dO) with respect to q, k (un-rotated) and v.  o_given: the
+    forward output Di is formed from (default: the exact O; see attention.py)."""
     gq, gk, gv = attention_backward(rotate(q, offsets, table), rotate(k, offsets, table), v, do, offsets,
-                                    MODE_BLOCK_DIAG, scale, block)
+                                    MODE_BLOCK_DIAG, scale, block, o_given)
     return rotate(gq, offsets, table, inverse=True), rotate(gk, offsets, table, inverse=True), gv

@@ -261,6 +261,58 @@ def test_di_identity():
     np.testing.assert_allclose((do * o).sum(axis=1), (p * dp).sum(axis=1), rtol=1e-12, atol=1e-13)
 
 
+def test_backward_on_a_given_forward_output():
+    """o_given (the forward output the backward receives) enters only through
+    Di = rowsum(dO * O): with O' = O + E and delta = rowsum(dO * E), dV is unchanged and
+    dS = P (dP - Di) moves by -P delta, so dQ moves by -scale delta (P K) and dK by
+    -scale (P * delta)^T Q.  Checked against torch autograd of the exact gradient and an
+    independent softmax (scipy), for self and broadcast-Q batches."""
+    from scipy.special import softmax
+    lengths, h, d, scale = [3, 1, 6], 2, 4, 0.45
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    t = int(off[-1])
+    q, k, v, do = _rand(t, h, d), _rand(t, h, d), _rand(t, h, d), _rand(t, h, d)
+    o, _ = oracle.attention_forward(q, k, v, off, 0, scale)
+    e = 0.01 * _rand(t, h, d)
+    g0 = oracle.attention_backward(q, k, v, do, off, 0, scale)
+    g1 = oracle.attention_backward(q, k, v, do, off, 0, scale, o_given=o + e)
+    ge = oracle.attention_backward(q, k, v, do, off, 0, scale, o_given=o)
+    for a, b in zip(g0, ge):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(g1[2], g0[2])
+    for b in range(len(lengths)):
+        s0, s1 = off[b], off[b + 1]
+        for hh in range(h):
+            qq, kk = q[s0:s1, hh], k[s0:s1, hh]
+            pt = torch.tensor(qq, requires_grad=True)
+            kt = torch.tensor(kk, requires_grad=True)
+            ot = torch.softmax(scale * pt @ kt.T, dim=-1) @ torch.tensor(v[s0:s1, hh])
+            (ot * torch.tensor(do[s0:s1, hh])).sum().backward()
+            P = softmax(scale * qq @ kk.T, axis=1)
+            delta = (do[s0:s1, hh] * e[s0:s1, hh]).sum(axis=1)
+            np.testing.assert_allclose(g1[0][s0:s1, hh], pt.grad.numpy() - scale * delta[:, None] * (P @ kk),
+                                       rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(g1[1][s0:s1, hh], kt.grad.numpy() - scale * (P * delta[:, None]).T @ qq,
+                                       rtol=1e-10, atol=1e-12)
+    # broadcast-Q: o [B, Mq, H, D]; dq sums the sequences' shifted contributions
+    mq = 3
+    qb = _rand(mq, h, d)
+    dob = _rand(len(lengths), mq, h, d)
+    ob, _ = oracle.attention_forward(qb, k, v, off, 1, scale)
+    eb = 0.01 * _rand(*ob.shape)
+    b0 = oracle.attention_backward(qb, k, v, dob, off, 1, scale)
+    b1 = oracle.attention_backward(qb, k, v, dob, off, 1, scale, o_given=ob + eb)
+    np.testing.assert_array_equal(b1[2], b0[2])
+    shift = np.zeros_like(qb)
+    for b in range(len(lengths)):
+        s0, s1 = off[b], off[b + 1]
+        for hh in range(h):
+            P = softmax(scale * qb[:, hh] @ k[s0:s1, hh].T, axis=1)
+            delta = (dob[b, :, hh] * eb[b, :, hh]).sum(axis=1)
+            shift[:, hh] -= scale * delta[:, None] * (P @ k[s0:s1, hh])
+    np.testing.assert_allclose(b1[0], b0[0] + shift, rtol=1e-10, atol=1e-12)
+
+
 def test_identical_keys_give_zero_dq():
     k = np.tile(_rand(1, 4), (6, 1))
     dq, _, _ = A.sequence_backward(_rand(3, 4), k, _rand(6, 4), _rand(3, 4), 0.9)
@@ -345,8 +397,10 @@ def test_broadcast_q_empty_sequence():
 # -------------------------------------------------------------- planted mistakes
 
 def _mutant_backward(kind):
-    def seq_bwd(q, k, v, do, scale):
+    def seq_bwd(q, k, v, do, scale, o_given=None):
         o, _, p = A.sequence_forward(q, k, v, scale)
+        if o_given is not None:
+            o = o_given
         dv = p.T @ do
         dp = do @ v.T
         di = (do * o).sum(axis=1)
