@@ -186,9 +186,13 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
     import numpy as np
     import oracle
     from variable_length_flash_jagged_amd import metrics as M
+    # The oracle's matrix products run in the BLAS thread pool; its size comes from the
+    # environment (OMP_NUM_THREADS / OPENBLAS_NUM_THREADS, which a GPU host may set to
+    # the process's share of its cores) and is recorded with the machine's core count.
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in blas] + [1])
     except Exception:  # pragma: no cover
         threads = 1
     done, flops, spent, b = 0, 0, 0.0, 0
@@ -237,6 +241,8 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
         "value": round(flops / spent / 1e12, 6),
         "unit": "TFLOPS",
         "cores": int(threads),
+        "os_cpu_count": os.cpu_count(),
+        "thread_env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")},
         "kind": "oracle",
         "sample": f"first {done} of {len(lengths)} sequences of the same batch (sum L = {int(sum(lengths[:done]))}), "
                   f"one fp64 {'block-sparse ' if sparse_ratio else 'rotary ' if rotary else 'MXFP8 ' if mxfp8 else ''}"

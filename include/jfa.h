@@ -260,6 +260,14 @@ int jfa_bwd_rotary(const jfa_shape* shape, int mode, float scale,
                    void* workspace, size_t workspace_bytes,
                    const jfa_opts* opts, void* stream);
 
+/* The cos / sin table jfa_fwd_rotary and jfa_bwd_rotary take, built on the device:
+ * table[(p * D/2 + i) * 2 + {0, 1}] = cos, sin of p * base^(-2i/D) for p < positions,
+ * i < D/2 (RoFormer's frequencies, usually base = 10000), formed in double precision
+ * and rounded once to fp32.  table: caller-allocated fp32 device array of
+ * positions * head_dim entries, 16-byte aligned; head_dim in {64, 128}; base > 1.
+ * Asynchronous on stream like the other calls. */
+int jfa_rope_table(float* table, int32_t positions, int32_t head_dim, float base, void* stream);
+
 /* Block-sparse top-k self attention, backward: the gradient of sum(O * dout) for the
  * forward of jfa_fwd_block_sparse with its selection held fixed (the pooling and top-k
  * only choose which keys take part and carry no gradient): per (sequence, head, query
@@ -342,6 +350,22 @@ enum jfa_kernel {
  * library on the calling thread's current device and released when forgotten. */
 int jfa_kernel_timing(int enable);
 int jfa_kernel_times(int kernel, int64_t* launches, double* total_ms, int reset);
+
+/* Debug hook: tile-visit counts, for checking that a schedule (static or run-time)
+ * computes every tile exactly once.  counts: caller-allocated device int32 array of
+ * 3 * stride entries that the caller zeroes; NULL turns counting off (the default).
+ * While set, the tile kernels of every jfa_fwd / jfa_bwd / jfa_fwd_noalloc /
+ * jfa_fwd_block_sparse / jfa_bwd_block_sparse / jfa_fwd_mxfp8 call (and the rotary
+ * variants) add 1 to counts[kernel * stride + i] each time they take tile i of their
+ * tile list, kernel = JFA_KERNEL_FWD (the forward kernel), JFA_KERNEL_BWD (the dK/dV
+ * kernel, or the fused broadcast-Q / block-diagonal backward kernel) or
+ * JFA_KERNEL_BWD_DQ (the dQ kernel); block-diagonal tiles are numbered (block, head)
+ * in schedule order.  A call whose list is longer than stride fails with
+ * JFA_ERR_CAPACITY before any device work.  jfa_debug_tile_list_size returns the
+ * length of kernel's tile list in the last such call (0 if it launched no such
+ * kernel).  Process-wide setting, one atomic add per tile; not for concurrent use. */
+int jfa_debug_tile_visits(int32_t* counts, int64_t stride);
+int jfa_debug_tile_list_size(int kernel, int64_t* tiles);
 
 /* Static message for a status code. */
 const char* jfa_error_string(int code);

@@ -179,17 +179,19 @@ def bwd_schedule(lengths, num_heads, mode, rows, num_programs, dynamic=False):
     return tiles, ptr, p_h * num_heads
 
 
-def blockdiag_schedule(lengths, num_heads, num_programs, block=64):
+def blockdiag_schedule(lengths, num_heads, num_programs, block=64, min_tiles=1):
     """Block-diagonal schedule: tiles (b, h, j) for every block j < ceil(L_b / block),
     enumerated with the head fastest, so consecutive tiles cover one contiguous slab
     of the packed buffer.  Program p receives the contiguous range
-    [p*q + min(p, r), (p+1)*q + min(p+1, r)) with (q, r) = divmod(N, P)."""
+    [p*q + min(p, r), (p+1)*q + min(p+1, r)) with (q, r) = divmod(N, P) and
+    P = min(num_programs, ceil(N / min_tiles)) (min_tiles > 1 when a program is a group
+    of workers that should each get a tile, as a workgroup of several waves)."""
     tiles = [(b, h, j)
              for b in range(len(lengths))
              for j in range(_cdiv(int(lengths[b]), block))
              for h in range(num_heads)]
     n_tiles = len(tiles)
-    p_used = min(num_programs, n_tiles)
+    p_used = min(num_programs, _cdiv(n_tiles, min_tiles))
     if p_used == 0:
         return [], [0], 0
     q, r = divmod(n_tiles, p_used)

@@ -76,7 +76,7 @@ def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, la
     p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=bwd, num_kv_heads=num_kv_heads)
     g = G.to_gpu(p)
     o, lse, sel = B.fwd_block_sparse(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], ratio, g["scale"],
-                                     opts)
+                                     opts, *G.nan_outputs_fwd(g))
     torch.cuda.synchronize()
     gpu_sel, used = _split_selection(sel, p["lengths"], heads, ratio)
     assert used == B.block_sparse_entries(B.make_shape(len(lengths), heads, head_dim, p["total_tokens"], 0,
@@ -87,11 +87,13 @@ def _run(lengths, heads, head_dim, ratio, seed, num_kv_heads=None, opts=None, la
     G.check_fwd(o, lse, o_ref, lse_ref, label)
     if bwd:
         grads = B.bwd_block_sparse(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], ratio,
-                                   sel, g["scale"], opts)
+                                   sel, g["scale"], opts, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
         torch.cuda.synchronize()
         refs = S.block_sparse_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
                                        p["offsets_host"], gpu_sel, p["scale"])
-        G.check_bwd(grads, refs, label + " bwd")
+        refs_o = S.block_sparse_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
+                                         p["offsets_host"], gpu_sel, p["scale"], o_given=G.f64(o))
+        G.check_bwd(grads, refs, label + " bwd", p, refs_o)
         return p, g, o, lse, sel, grads
     return p, g, o, lse
 
@@ -179,9 +181,10 @@ def test_block_sparse_backward_full_production_workload_sampled():
     print("[case] block sparse backward full-size workload 7", flush=True)
     p = W.make_workload(7, seed=0, device="cuda")
     ratio = W.WORKLOADS[7]["sparse_ratio"]
-    o, lse, sel = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], ratio, p["scale"])
+    o, lse, sel = B.fwd_block_sparse(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], ratio, p["scale"],
+                                     None, *G.nan_outputs_fwd(p))
     dq, dk, dv = B.bwd_block_sparse(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], ratio,
-                                    sel, p["scale"])
+                                    sel, p["scale"], None, G.nan_like(p["q"]), G.nan_like(p["k"]), G.nan_like(p["v"]))
     torch.cuda.synchronize()
     gpu_sel, _ = _split_selection(sel, p["lengths"], p["num_heads"], ratio)
     off = p["offsets_host"].astype(np.int64)
@@ -191,7 +194,10 @@ def test_block_sparse_backward_full_production_workload_sampled():
         sub = lambda t: G.f64(t[s:e])
         refs = S.block_sparse_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s],
                                        [gpu_sel[b]], p["scale"])
-        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 7 bwd seq {b} (L={e - s})")
+        refs_o = S.block_sparse_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s],
+                                         [gpu_sel[b]], p["scale"], o_given=sub(o))
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 7 bwd seq {b} (L={e - s})",
+                    {"offsets_host": [0, e - s], "mode": p["mode"]}, refs_o)
 
 
 def test_block_sparse_largest_sequence():

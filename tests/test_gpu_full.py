@@ -45,11 +45,13 @@ def _run(workload, opts=None, bench=False, self_bwd="auto"):
     print(f"[case] full-size workload {workload} opts=({opts.sched if opts else 0}, "
           f"{opts.dq_path if opts else 0}, {opts.num_programs if opts else 0}, "
           f"{opts.ds_budget_mib if opts else 0})", flush=True)
-    o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts)
+    # outputs pre-filled with NaN: a row no tile writes fails the finiteness checks
+    o, lse = B.fwd(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], p["mode"], p["scale"], opts,
+                   *G.nan_outputs_fwd(p))
     grads = None
     if p["do"] is not None:
         grads = B.bwd(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], p["mode"],
-                      p["scale"], opts)
+                      p["scale"], opts, G.nan_like(p["q"]), G.nan_like(p["k"]), G.nan_like(p["v"]))
     torch.cuda.synchronize()
     return p, o, lse, grads
 
@@ -72,7 +74,9 @@ def test_full_size_sampled_sequences(workload, samples, self_bwd):
             continue
         dq, dk, dv = grads
         refs = oracle.attention_backward(q, k, v, do, sub_off, mode, p["scale"])
-        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload {workload} seq {b} (L={e - s})")
+        refs_o = oracle.attention_backward(q, k, v, do, sub_off, mode, p["scale"], o_given=G.f64(o[s:e]))
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload {workload} seq {b} (L={e - s})",
+                    {"offsets_host": sub_off, "mode": mode}, refs_o)
 
 
 @pytest.mark.parametrize("dq_path", [0, 1, 2])
@@ -80,7 +84,7 @@ def test_full_size_broadcast_q(dq_path):
     p, o, lse, grads = _run(2, B.make_opts(dq_path=dq_path))
     o_ref, lse_ref = G.oracle_fwd(p)
     G.check_fwd(o, lse, o_ref, lse_ref, "workload 2 full")
-    G.check_bwd(grads, G.oracle_bwd(p), "workload 2 full")
+    G.check_bwd(grads, G.oracle_bwd(p), "workload 2 full", p, G.oracle_bwd(p, o))
 
 
 @pytest.mark.parametrize("self_bwd", ["auto", "recompute"])
@@ -107,4 +111,6 @@ def test_tensors_beyond_2_31_elements(self_bwd):
         o_ref, lse_ref = oracle.attention_forward(q, k, v, [0, e - s], p["mode"], p["scale"])
         G.check_fwd(o[s:e], lse[:, s:e], o_ref, lse_ref, f"beyond 2^31 seq {b}")
         refs = oracle.attention_backward(q, k, v, do, [0, e - s], p["mode"], p["scale"])
-        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"beyond 2^31 seq {b}")
+        refs_o = oracle.attention_backward(q, k, v, do, [0, e - s], p["mode"], p["scale"], o_given=G.f64(o[s:e]))
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"beyond 2^31 seq {b}",
+                    {"offsets_host": [0, e - s], "mode": p["mode"]}, refs_o)

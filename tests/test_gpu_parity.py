@@ -104,8 +104,8 @@ def test_self_stored_ds_and_recompute_paths_on_one_forward():
     assert torch.equal(a[2], b[2])
     assert G.rel_l2(G.f64(b[1]), G.f64(a[1])) < 1e-3
     refs = G.oracle_bwd(p)
-    ea = G.check_bwd(a, refs, "recompute path")
-    eb = G.check_bwd(b, refs, "stored-dS path")
+    ea = G.check_bwd(a, refs, "recompute path", p, G.oracle_bwd(p, o))
+    eb = G.check_bwd(b, refs, "stored-dS path", p, G.oracle_bwd(p, o))
     print(f"rel-L2 vs oracle: recompute {ea}, stored dS {eb}", flush=True)
 
 
@@ -215,7 +215,7 @@ def test_bwd_from_oracle_forward():
     lse = torch.from_numpy(lse_ref).float().cuda()
     grads = G.gpu_bwd(g, o, lse)
     torch.cuda.synchronize()
-    G.check_bwd(grads, G.oracle_bwd(p), "bwd from oracle fwd")
+    G.check_bwd(grads, G.oracle_bwd(p), "bwd from oracle fwd", p, G.oracle_bwd(p, o))
 
 
 def test_outputs_leave_guard_canaries_untouched():

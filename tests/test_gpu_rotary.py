@@ -1,8 +1,10 @@
 """GPU parity of the block-diagonal attention with the fused rotary embedding
 (jfa_fwd_rotary / jfa_bwd_rotary) against the fp64 oracle (oracle/rotary.py).
 
-The library takes its cos/sin table from binding.rope_table (fp32); the oracle builds
-its own in fp64 from the definition, so the table's rounding is inside the tolerance.
+The library builds its cos/sin table on the device (jfa_rope_table, fp32); the oracle
+builds its own in fp64 from the definition, so the table's rounding is inside the
+tolerance, and the device table equals the oracle's rounded to fp32 within one unit in
+the last place.
 A table of zero angles must reproduce the plain block-diagonal kernels bit for bit.
 
 Tolerance of lse.  The rotated q and k enter the bf16 matrix product rounded to bf16
@@ -60,7 +62,8 @@ def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", 
     g = G.to_gpu(p)
     rows = table_rows or max(1, max(lengths))
     rope = B.rope_table(rows, head_dim, device="cuda")
-    o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"])
+    o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"], None,
+                          *G.nan_outputs_fwd(g))
     torch.cuda.synchronize()
     tab = R.rope_table(rows, head_dim)
     o_ref, lse_ref = R.rotary_block_forward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), p["offsets_host"], tab,
@@ -69,11 +72,13 @@ def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", 
     grads = None
     if bwd:
         grads = B.bwd_rotary(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], rope,
-                             g["scale"])
+                             g["scale"], None, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
         torch.cuda.synchronize()
         refs = R.rotary_block_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
                                        p["offsets_host"], tab, p["scale"])
-        G.check_bwd(grads, refs, label + " bwd")
+        refs_o = R.rotary_block_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
+                                         p["offsets_host"], tab, p["scale"], o_given=G.f64(o))
+        G.check_bwd(grads, refs, label + " bwd", p, refs_o)
     return p, g, o, lse, grads
 
 
@@ -97,10 +102,11 @@ def test_rotary_zero_angles_equal_plain_block_attention_bit_exactly():
         g = G.to_gpu(p)
         rope = torch.zeros((700, d // 2, 2), dtype=torch.float32, device="cuda")
         rope[..., 0] = 1.0
-        o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"])
+        o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"], None,
+                          *G.nan_outputs_fwd(g))
         o_p, lse_p = G.gpu_fwd(g)
         grads = B.bwd_rotary(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], rope,
-                             g["scale"])
+                             g["scale"], None, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
         plain = G.gpu_bwd(g, o_p, lse_p)
         torch.cuda.synchronize()
         assert torch.equal(o, o_p) and torch.equal(lse, lse_p)
@@ -116,9 +122,10 @@ def test_rotary_full_workload_sampled():
     lengths = p["lengths"]
     rows = int(max(lengths))
     rope = B.rope_table(rows, p["head_dim"], device="cuda")
-    o, lse = B.fwd_rotary(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], rope, p["scale"])
+    o, lse = B.fwd_rotary(p["q"], p["k"], p["v"], p["offsets"], p["offsets_host"], rope, p["scale"], None,
+                          *G.nan_outputs_fwd(p))
     dq, dk, dv = B.bwd_rotary(p["q"], p["k"], p["v"], o, p["do"], lse, p["offsets"], p["offsets_host"], rope,
-                              p["scale"])
+                              p["scale"], None, G.nan_like(p["q"]), G.nan_like(p["k"]), G.nan_like(p["v"]))
     torch.cuda.synchronize()
     tab = R.rope_table(rows, p["head_dim"])
     off = p["offsets_host"].astype(np.int64)
@@ -131,4 +138,20 @@ def test_rotary_full_workload_sampled():
                    f"workload 8 seq {b} (L={e - s})")
         refs = R.rotary_block_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s], tab,
                                        p["scale"])
-        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 8 seq {b} (L={e - s})")
+        refs_o = R.rotary_block_backward(sub(p["q"]), sub(p["k"]), sub(p["v"]), sub(p["do"]), [0, e - s], tab,
+                                         p["scale"], o_given=sub(o))
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 8 seq {b} (L={e - s})",
+                    {"offsets_host": [0, e - s], "mode": p["mode"]}, refs_o)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_library_rope_table_equals_oracle_table_rounded(head_dim):
+    rows = 4100
+    got = B.rope_table(rows, head_dim, device="cuda").cpu().numpy()
+    want = R.rope_table(rows, head_dim)
+    assert got.shape == want.shape and got.dtype == np.float32
+    # at most one fp32 unit in the last place from the fp64 values, and exactly the
+    # rounded value almost everywhere
+    ulp = np.spacing(np.abs(want).astype(np.float32))
+    assert np.all(np.abs(got.astype(np.float64) - want) <= ulp)
+    assert np.mean(got == want.astype(np.float32)) > 0.999

@@ -11,7 +11,9 @@ import os
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libjfa.so")
+# JFA_LIBRARY names another build of the same library (e.g. the host-sanitizer build the
+# CPU tests make); by default the in-tree libjfa.so.
+LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(PKG, "libjfa.so")
 
 MODE_SELF = 0
 MODE_BROADCAST_Q = 1
@@ -75,6 +77,10 @@ def lib():
         L.jfa_kernel_timing.argtypes = [ctypes.c_int]
         L.jfa_kernel_times.restype = ctypes.c_int
         L.jfa_kernel_times.argtypes = [ctypes.c_int, i64p, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        L.jfa_debug_tile_visits.restype = ctypes.c_int
+        L.jfa_debug_tile_visits.argtypes = [vp, i64]
+        L.jfa_debug_tile_list_size.restype = ctypes.c_int
+        L.jfa_debug_tile_list_size.argtypes = [ctypes.c_int, i64p]
         L.jfa_block_sparse_entries.restype = ctypes.c_int
         L.jfa_block_sparse_entries.argtypes = [sp, vp, f32, i64p]
         L.jfa_fwd_block_sparse.restype = ctypes.c_int
@@ -91,6 +97,8 @@ def lib():
         L.jfa_bwd_rotary.restype = ctypes.c_int
         L.jfa_bwd_rotary.argtypes = [sp, ctypes.c_int, f32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
                                      vp, vp, vp, ctypes.c_size_t, op, vp]
+        L.jfa_rope_table.restype = ctypes.c_int
+        L.jfa_rope_table.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, f32, vp]
         L.jfa_mxfp8_v_tokens.restype = ctypes.c_int
         L.jfa_mxfp8_v_tokens.argtypes = [sp, vp, i64p]
         L.jfa_mxfp8_quantize_qk.restype = ctypes.c_int
@@ -185,6 +193,20 @@ def kernel_times(kernel, reset=False):
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
     _check(lib().jfa_kernel_times(kernel, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0), "jfa_kernel_times")
     return int(n.value), float(ms.value)
+
+
+def debug_tile_visits(counts, stride):
+    """Count tile visits into the zeroed device int32 tensor `counts` (3 * stride
+    entries; None turns counting off): see jfa_debug_tile_visits."""
+    _check(lib().jfa_debug_tile_visits(_ptr(counts) if counts is not None else None, int(stride)),
+           "jfa_debug_tile_visits")
+
+
+def debug_tile_list_size(kernel):
+    """Tile-list length of `kernel` (KERNEL_FWD / KERNEL_BWD / KERNEL_BWD_DQ) in the last call."""
+    n = ctypes.c_int64(0)
+    _check(lib().jfa_debug_tile_list_size(kernel, ctypes.byref(n)), "jfa_debug_tile_list_size")
+    return int(n.value)
 
 
 def _ptr(t):
@@ -394,15 +416,14 @@ def bwd_block_sparse(q, k, v, o, do, lse, offsets, offsets_host, ratio, selectio
     return dq, dk, dv
 
 
-def rope_table(max_positions, head_dim, base=10000.0, device=None):
-    """The cos / sin table jfa_fwd_rotary takes: [max_positions, D/2, 2] fp32 with
-    (cos, sin) of p * base^(-2i/D), formed in float64 and rounded once."""
+def rope_table(max_positions, head_dim, base=10000.0, device="cuda", stream=None):
+    """The cos / sin table jfa_fwd_rotary takes, built by the library (jfa_rope_table):
+    [max_positions, D/2, 2] fp32 on the device."""
     import torch
-    i = np.arange(head_dim // 2, dtype=np.float64)
-    ang = np.arange(max_positions, dtype=np.float64)[:, None] * np.power(float(base), -2.0 * i / head_dim)[None, :]
-    tab = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
-    t = torch.from_numpy(np.ascontiguousarray(tab))
-    return t.to(device) if device is not None else t
+    t = torch.empty((int(max_positions), head_dim // 2, 2), dtype=torch.float32, device=device)
+    _check(lib().jfa_rope_table(_ptr(t), int(max_positions), int(head_dim), float(base), _stream(stream)),
+           "jfa_rope_table")
+    return t
 
 
 def fwd_rotary(q, k, v, offsets, offsets_host, rope, scale=None, opts=None, o=None, lse=None, workspace=None,

@@ -112,6 +112,14 @@ int max_programs(const Opts& o, int wg_per_cu) {
   return o.num_programs > 0 ? o.num_programs : device_cus() * wg_per_cu;
 }
 
+// Resident workgroups per CU of the main (dK/dV or fused) backward kernel: the
+// self-attention dK/dV kernel, which broadcast-Q dq_path 2 also runs, or the fused
+// broadcast-Q kernel.  jfa_bwd and jfa_schedule both size the schedule with it.
+int bwd_wg_per_cu(int mode, int dq_path, int head_dim) {
+  return mode == JFA_MODE_SELF || (mode == JFA_MODE_BROADCAST_Q && dq_path == 2) ? dkdv_wg_per_cu(head_dim)
+                                                                                 : kBqWgPerCu;
+}
+
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct Layout {
   size_t counters = 0, seg = 0, tiles = 0, seg2 = 0, tiles2 = 0, ds_base = 0, stats = 0, ds = 0, prefix = 0, acc = 0,
@@ -516,6 +524,37 @@ int check_mx_shape(const jfa_shape* shape) {
   return JFA_OK;
 }
 
+// Debug tile-visit counting (see jfa_debug_tile_visits in jfa.h).  Regions of the
+// caller's count array per kernel role (forward, dK/dV or fused backward, dQ) and the
+// tile-list lengths of the last call.
+constexpr int kVisitRoles = 3;
+struct VisitDebug {
+  std::mutex mu;
+  int32_t* counts = nullptr;
+  int64_t stride = 0;
+  int64_t last[kVisitRoles] = {0, 0, 0};
+} g_visits;
+
+void visits_begin() {
+  std::lock_guard<std::mutex> lock(g_visits.mu);
+  for (int64_t& n : g_visits.last) n = 0;
+}
+
+// Records that `kernel` walks a list of n tiles in this call and returns its count
+// region (null when counting is off); a list longer than the region fails the call
+// before any device work.
+int visit_region(int kernel, int64_t n, int32_t** out) {
+  std::lock_guard<std::mutex> lock(g_visits.mu);
+  *out = nullptr;
+  g_visits.last[kernel] = n;
+  if (!g_visits.counts) return JFA_OK;
+  if (n > g_visits.stride)
+    return fail(JFA_ERR_CAPACITY, "tile-visit counts: %lld tiles > stride %lld", (long long)n,
+                (long long)g_visits.stride);
+  *out = g_visits.counts + kernel * g_visits.stride;
+  return JFA_OK;
+}
+
 int launch_status(hipError_t e, const char* what) {
   return e == hipSuccess ? JFA_OK : hip_fail(e, what);
 }
@@ -601,6 +640,25 @@ int jfa_kernel_times(int pass, int64_t* launches, double* total_ms, int reset) {
   return JFA_OK;
 }
 
+int jfa_debug_tile_visits(int32_t* counts, int64_t stride) {
+  g_detail.clear();
+  if (counts && stride < 1) return fail(JFA_ERR_BAD_OPTION, "stride must be >= 1");
+  if (counts && !aligned(counts, 4)) return fail(JFA_ERR_MISALIGNED, "counts must be 4-byte aligned");
+  std::lock_guard<std::mutex> lock(g_visits.mu);
+  g_visits.counts = counts;
+  g_visits.stride = counts ? stride : 0;
+  return JFA_OK;
+}
+
+int jfa_debug_tile_list_size(int kernel, int64_t* tiles) {
+  g_detail.clear();
+  if (kernel < 0 || kernel >= kVisitRoles) return fail(JFA_ERR_BAD_MODE, "kernel must be 0, 1 or 2");
+  if (!tiles) return fail(JFA_ERR_NULL_POINTER, "tiles is NULL");
+  std::lock_guard<std::mutex> lock(g_visits.mu);
+  *tiles = g_visits.last[kernel];
+  return JFA_OK;
+}
+
 const char* jfa_last_error_detail(void) { return g_detail.c_str(); }
 
 const char* jfa_error_string(int code) {
@@ -669,6 +727,7 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
                          int32_t* selection, int64_t selection_entries, void* workspace, size_t workspace_bytes,
                          const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, JFA_MODE_SELF);
   if (rc) return rc;
@@ -698,6 +757,8 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kFwdRows, max_programs(op, kFwdWgPerCu), op.sched == 1, sc);
   if (sc.tiles.empty()) return JFA_OK;
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  int32_t* visits = nullptr;
+  if ((rc = visit_region(JFA_KERNEL_FWD, (int64_t)sc.tiles.size(), &visits))) return rc;
   if (P.qt_prefix.back() > L.sp_nqt_cap || P.kb_prefix.back() > L.sp_nkb_cap)
     return fail(JFA_ERR_WORKSPACE, "internal: block capacity");
   std::vector<char> buf;
@@ -761,6 +822,7 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   p.sel = selection;
   p.sel_base = ps.sel_base;
   p.sel_k = ps.sel_k;
+  p.visits = visits;
   return launch_status(timed_launch(JFA_KERNEL_FWD, stream, [&] { return launch_fwd(p, kSelfSparse, D, stream); }),
                        "block-sparse forward launch");
 }
@@ -787,6 +849,7 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
                          int64_t selection_entries, void* dq, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, JFA_MODE_SELF);
   if (rc) return rc;
@@ -822,6 +885,9 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   if ((int64_t)sc.tiles.size() > S.kv_tile_cap || (int64_t)sc.seg_ptr.size() > S.kv_seg_cap ||
       (int64_t)sq.tiles.size() > L.tile2_cap || (int64_t)sq.seg_ptr.size() > L.seg2_cap)
     return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  int32_t *visits = nullptr, *dq_visits = nullptr;
+  if ((rc = visit_region(JFA_KERNEL_BWD, (int64_t)sc.tiles.size(), &visits))) return rc;
+  if ((rc = visit_region(JFA_KERNEL_BWD_DQ, (int64_t)sq.tiles.size(), &dq_visits))) return rc;
   char* ws = (char*)workspace;
   {
     // [counters (zero) .. dQ schedule]
@@ -878,6 +944,8 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
   p.sel_k = mp.sel_k;
   p.sp_bits = bits;
   p.sp_bits_base = mp.bits_base;
+  p.visits = visits;
+  p.dq_visits = dq_visits;
   p.num_seqs = B;
   p.num_heads = H;
   p.num_programs = sc.programs;
@@ -890,6 +958,17 @@ int jfa_bwd_block_sparse(const jfa_shape* shape, float scale, float ratio, const
     return rc;
   return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
                        "block-sparse dK/dV launch");
+}
+
+int jfa_rope_table(float* table, int32_t positions, int32_t head_dim, float base, void* stream) {
+  g_detail.clear();
+  if (!table) return fail(JFA_ERR_NULL_POINTER, "table is NULL");
+  if (!aligned(table, 16)) return fail(JFA_ERR_MISALIGNED, "table must be 16-byte aligned");
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_BAD_HEAD_DIM, "head_dim %d not in {64, 128}", head_dim);
+  if (positions < 0) return fail(JFA_ERR_BAD_SHAPE, "positions < 0");
+  if (!(base > 1.f) || !std::isfinite(base)) return fail(JFA_ERR_BAD_OPTION, "base must be finite and > 1");
+  return launch_status(launch_rope_table(table, positions, head_dim, (double)base, (hipStream_t)stream),
+                       "rotary table launch");
 }
 
 int jfa_mxfp8_v_tokens(const jfa_shape* shape, const int32_t* offsets_host, int64_t* tokens) {
@@ -971,6 +1050,7 @@ int jfa_fwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const 
                   int64_t v_tokens, const int32_t* offsets_dev, const int32_t* offsets_host, void* o, float* lse,
                   void* workspace, size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_mx_shape(shape);
   if (rc) return rc;
@@ -998,6 +1078,8 @@ int jfa_fwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const 
   if (sc.tiles.empty()) return JFA_OK;
   if ((int64_t)sc.tiles.size() > L.tile_cap || (int64_t)sc.seg_ptr.size() > L.seg_cap)
     return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  int32_t* visits = nullptr;
+  if ((rc = visit_region(JFA_KERNEL_FWD, (int64_t)sc.tiles.size(), &visits))) return rc;
   std::vector<char> buf;
   serialise(sc, L, buf, nullptr, &vb);
   char* ws = (char*)workspace;
@@ -1020,6 +1102,7 @@ int jfa_fwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const 
   p.num_programs = sc.programs;
   p.total_tokens = shape->total_tokens;
   p.scale_log2 = scale * kLog2eHost;
+  p.visits = visits;
   return launch_status(timed_launch(JFA_KERNEL_FWD, stream, [&] { return launch_mx_fwd(p, D, stream); }),
                        "MXFP8 forward launch");
 }
@@ -1039,7 +1122,7 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
   Schedule sc;
   const bool dyn = o.sched == 1;
   if (mode == JFA_MODE_BLOCK_DIAG)
-    schedule_blockdiag(lengths, shape->num_heads, kBlock, max_programs(o, kBdWgPerCu), sc);
+    schedule_blockdiag(lengths, shape->num_heads, kBlock, max_programs(o, kBdWgPerCu), kBdWaves, sc);
   else if (pass == JFA_PASS_FWD && mode == JFA_MODE_BROADCAST_Q) {
     KeyChunks kc;
     bq_key_chunks(lengths, shape->num_heads, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), true, kc);
@@ -1048,7 +1131,7 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
     schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
   else
     schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys,
-                 max_programs(o, mode == JFA_MODE_SELF ? dkdv_wg_per_cu(shape->head_dim) : kBqWgPerCu), dyn, sc);
+                 max_programs(o, bwd_wg_per_cu(mode, o.dq_path, shape->head_dim)), dyn, sc);
   if (n_tiles) *n_tiles = (int64_t)sc.tiles.size();
   if (n_segs) *n_segs = (int32_t)sc.seg_ptr.size();
   if (n_programs) *n_programs = sc.programs;
@@ -1077,6 +1160,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
                      const int32_t* offsets_host, void* o, float* lse, void* workspace, size_t workspace_bytes,
                      const jfa_opts* opts, void* stream_, bool noalloc = false) {
   g_detail.clear();
+  visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
   if (rc) return rc;
@@ -1116,8 +1200,11 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     for (int b = 0; b < shape->num_seqs; ++b) prefix[b + 1] = prefix[b] + (int32_t)cdiv(lengths[b], kBlock);
     const int64_t ntiles = (int64_t)prefix.back() * H;
     if (ntiles == 0) return JFA_OK;
+    int32_t* visits = nullptr;
+    if ((rc = visit_region(JFA_KERNEL_FWD, ntiles, &visits))) return rc;
     if ((rc = put(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix))) return rc;
     BdParams p{};
+    p.visits = visits;
     p.q = (const uint16_t*)q;
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
@@ -1171,10 +1258,13 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   }
   if (sc.tiles.empty()) return JFA_OK;
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+  int32_t* visits = nullptr;
+  if ((rc = visit_region(JFA_KERNEL_FWD, (int64_t)sc.tiles.size(), &visits))) return rc;
   std::vector<char> buf;
   serialise(sc, L, buf, nullptr, nullptr, table.empty() ? nullptr : &table);
   if ((rc = put(buf.data(), buf.size(), ws))) return rc;
   FwdParams p{};
+  p.visits = visits;
   if (mode == JFA_MODE_BROADCAST_Q) {
     p.chunks = (const int32_t*)(ws + L.chunks);
     p.num_chunks = nc;
@@ -1237,6 +1327,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
                      const int32_t* offsets_dev, const int32_t* offsets_host, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
   if (rc) return rc;
@@ -1270,8 +1361,11 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     for (int b = 0; b < shape->num_seqs; ++b) prefix[b + 1] = prefix[b] + (int32_t)cdiv(lengths[b], kBlock);
     const int64_t ntiles = (int64_t)prefix.back() * H;
     if (ntiles == 0) return JFA_OK;
+    int32_t* visits = nullptr;
+    if ((rc = visit_region(JFA_KERNEL_BWD, ntiles, &visits))) return rc;
     if ((rc = upload(prefix.data(), prefix.size() * sizeof(int32_t), ws + L.prefix, stream))) return rc;
     BdParams p{};
+    p.visits = visits;
     p.q = (const uint16_t*)q;
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
@@ -1298,11 +1392,10 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
 
   const bool bq_split = mode == JFA_MODE_BROADCAST_Q && op.dq_path == 2;
   Schedule sc;
-  schedule_bwd(lengths, H, mode, kBwdKeys,
-               max_programs(op, mode == JFA_MODE_SELF || bq_split ? dkdv_wg_per_cu(D) : kBqWgPerCu), op.sched == 1,
-               sc);
+  schedule_bwd(lengths, H, mode, kBwdKeys, max_programs(op, bwd_wg_per_cu(mode, op.dq_path, D)), op.sched == 1, sc);
   if ((int64_t)sc.tiles.size() > L.tile_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
   BwdParams p{};
+  if ((rc = visit_region(JFA_KERNEL_BWD, (int64_t)sc.tiles.size(), &p.visits))) return rc;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -1334,6 +1427,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
       schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDsRows, max_programs(op, kDsWgPerCu), op.sched == 1, sq);
       if ((int64_t)sq.tiles.size() > L.tile2_cap || sq.programs > L.programs2_cap)
         return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+      if ((rc = visit_region(JFA_KERNEL_BWD_DQ, (int64_t)sq.tiles.size(), &p.dq_visits))) return rc;
       std::vector<char> buf;
       serialise(sc, L, buf, &sq, &ds_base);
       if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
@@ -1358,6 +1452,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     Schedule sq;
     schedule_fwd(lengths, H, JFA_MODE_SELF, 0, kDqRows, max_programs(op, kDqWgPerCu), op.sched == 1, sq);
     if ((int64_t)sq.tiles.size() > L.tile2_cap) return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+    if ((rc = visit_region(JFA_KERNEL_BWD_DQ, (int64_t)sq.tiles.size(), &p.dq_visits))) return rc;
     std::vector<char> buf;
     serialise(sc, L, buf, &sq);
     if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;
@@ -1391,6 +1486,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     schedule_fwd(kc.len, H, JFA_MODE_BROADCAST_Q, (int)Mq, kDqRows, p2, op.sched == 1, sq);
     if ((int64_t)sq.tiles.size() > L.tile2_cap || sq.programs > L.programs2_cap)
       return fail(JFA_ERR_WORKSPACE, "internal: tile capacity");
+    if ((rc = visit_region(JFA_KERNEL_BWD_DQ, (int64_t)sq.tiles.size(), &p.dq_visits))) return rc;
     std::vector<char> buf;
     serialise(sc, L, buf, &sq, nullptr, &chunks);
     if ((rc = upload(buf.data(), buf.size(), ws, stream))) return rc;

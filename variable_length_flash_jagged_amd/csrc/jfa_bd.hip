@@ -574,7 +574,10 @@ __global__ void __launch_bounds__(BdCfg<D>::NW * 64)
   const int64_t P = gridDim.x, q = p.num_tiles / P, r = p.num_tiles % P;
   const int64_t start = prog * q + min((int64_t)prog, r), end = start + q + (prog < r ? 1 : 0);
   JFA_LDS char* vt = (JFA_LDS char*)smem + wave * C::TBUF;
-  for (int64_t g = start + wave; g < end; g += C::NW) bd_fwd_tile<D, ROPE>(p, locate(p, g), vt, lane);
+  for (int64_t g = start + wave; g < end; g += C::NW) {
+    if (lane == 0) count_visit(p.visits, g);
+    bd_fwd_tile<D, ROPE>(p, locate(p, g), vt, lane);
+  }
 }
 
 template <int D, bool ROPE>
@@ -605,14 +608,17 @@ __global__ void __launch_bounds__(BdCfg<D>::NW * 64)
         tn = locate(p, gn);
         bd_bwd_load<D>(p, tn, nx, lane);
       }
+      if (lane == 0) count_visit(p.visits, g);
       bd_bwd_tile<D, ROPE, true>(p, t, lw, (float*)w, lane, &cur);
       if (gn >= end) break;
       g = gn;
       t = tn;
     }
   } else {
-    for (int64_t g = start + wave; g < end; g += C::NW)
+    for (int64_t g = start + wave; g < end; g += C::NW) {
+      if (lane == 0) count_visit(p.visits, g);
       bd_bwd_tile<D, ROPE>(p, locate(p, g), (JFA_LDS char*)w, (float*)w, lane);
+    }
   }
 }
 
@@ -621,7 +627,32 @@ int bd_programs(const BdParams& p, int nw) {
   return (int)(need < p.num_programs ? need : p.num_programs);
 }
 
+// cos / sin table of the fused rotary embedding: entry (pos, i) = (cos, sin) of
+// pos * base^(-2i/D), i < D/2, formed in double precision and rounded once to fp32.
+// One thread per (pos, i).
+__global__ void rope_table_kernel(float* table, int positions, int head_dim, double base) {
+  const int half = head_dim / 2;
+  const int64_t n = (int64_t)positions * half;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(t % half);
+    const double pos = (double)(t / half);
+    const double ang = pos * pow(base, -2.0 * i / head_dim);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    *reinterpret_cast<float2*>(table + 2 * t) = make_float2((float)cs, (float)sn);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(float* table, int positions, int head_dim, double base, hipStream_t s) {
+  const int64_t n = (int64_t)positions * (head_dim / 2);
+  if (n <= 0) return hipSuccess;
+  const int64_t g = (n + 255) / 256;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)(g < 8192 ? g : 8192)), dim3(256), 0, s, table, positions,
+                     head_dim, base);
+  return hipGetLastError();
+}
 
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s) {
   if (p.num_tiles <= 0) return hipSuccess;

@@ -325,6 +325,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64)
     idx = base + rank;
   }
   while (idx < end) {
+    if (tid == 0) count_visit(p.visits, idx);
     bwd_tile<D, MODE>(p, p.tiles[idx], prog, smem, tid);
     if (!p.dynamic) {
       ++idx;

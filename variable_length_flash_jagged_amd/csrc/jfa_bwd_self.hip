@@ -739,7 +739,7 @@ __device__ __forceinline__ int xcd_gsize() { return (int)gridDim.x / dynamic_gro
 
 template <class F>
 __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles, const int32_t* seg_ptr,
-                                          int32_t* counters, int gsize, int* next_tile, F&& body) {
+                                          int32_t* counters, int gsize, int* next_tile, int32_t* visits, F&& body) {
   const int tid = threadIdx.x;
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
   const int grp = prog / gsize;
@@ -753,6 +753,7 @@ __device__ __forceinline__ void tile_loop(const BwdParams& p, const Tile* tiles,
     idx = base + prog % gsize;
   }
   while (idx < end) {
+    if (tid == 0) count_visit(visits, idx);
     body(tiles[idx]);
     if (!p.dynamic) {
       ++idx;
@@ -775,7 +776,7 @@ __global__ void __launch_bounds__(kDqWaves * 64)
   ln.row.init(threadIdx.x & 63);
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile, p.dq_visits,
             [&](Tile t) { dq_tile<D, SPARSE>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
@@ -793,7 +794,7 @@ __global__ void __launch_bounds__(NW * 64)
   ln.init_pick(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   // broadcast-Q: head-pinned groups of programs_per_head programs
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile,
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile, p.visits,
             [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
@@ -1048,7 +1049,7 @@ __global__ void __launch_bounds__(kKv16Waves * 64) __attribute__((amdgpu_waves_p
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   ln.init_sel(threadIdx.x & 63);
   // broadcast-Q: head-pinned groups of programs_per_head programs
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile,
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile, p.visits,
             [&](Tile t) { dkdv16_tile<D>(p, t, smem, ln, threadIdx.x); });
 }
 
@@ -1269,7 +1270,7 @@ __global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per
   ln.ktr.init(threadIdx.x & 63);
   ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
   ln.init(threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile,
+  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile, p.dq_visits,
             [&](Tile t) { dq_ds_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 

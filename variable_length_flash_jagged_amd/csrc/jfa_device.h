@@ -291,6 +291,12 @@ __device__ __forceinline__ bf16x8 tr_operand(const JFA_LDS char* tile, int row0,
   return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8), lds_tr4(tile, swz_off<RB>(r + 8, col >> 3) + w8));
 }
 
+// Debug tile-visit count (visits null: off): one atomic add per taken tile, issued by a
+// single lane.
+__device__ __forceinline__ void count_visit(int32_t* visits, int64_t idx) {
+  if (visits) atomicAdd(visits + idx, 1);
+}
+
 // Workgroups are dealt to the 8 XCDs round robin by workgroup id; number the programs
 // so that consecutive program ids share an XCD (and its L2).
 __device__ __forceinline__ int xcd_program_id(int wg, int num_wg) {

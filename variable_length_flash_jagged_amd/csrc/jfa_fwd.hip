@@ -391,6 +391,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     idx = base + prog % gsize;
   }
   while (idx < end) {
+    if (tid == 0) count_visit(p.visits, idx);
     fwd_tile<D, MODE>(p, p.tiles[idx], smem, ln, tid);
     if (!p.dynamic) {
       ++idx;

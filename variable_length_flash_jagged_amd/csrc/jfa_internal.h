@@ -109,6 +109,7 @@ struct FwdParams {
   int32_t num_chunks;
   float* part_o;
   float* part_lse;
+  int32_t* visits;  // debug (null: off): visits[i] += 1 each time tile i of the list is taken
 };
 
 // Block means of a bf16 [T, heads, D] tensor: out[h][blk][d] (fp32) over consecutive
@@ -196,6 +197,8 @@ struct BwdParams {
   int32_t programs_per_head;  // broadcast-Q head-pinned groups
   float scale;
   float scale_log2;
+  int32_t* visits;     // debug (null: off): visit counts of the dK/dV (or fused) kernel's tiles
+  int32_t* dq_visits;  // debug (null: off): visit counts of the dQ kernel's tiles
 };
 
 // Block-diagonal forward / backward.
@@ -221,6 +224,7 @@ struct BdParams {
   // fused rotary embedding (null: none): cos, sin of p theta_i at rope[(p D/2 + i) 2 + {0, 1}],
   // p = position inside the sequence, i < D/2; q, k pairs (i, i + D/2) are rotated
   const float* rope;
+  int32_t* visits;  // debug (null: off): visits[g] += 1 for every (block, head) tile g computed
 };
 
 // MXFP8 quantisation: Q / K rows (rows = T * heads, blocks along the head dimension),
@@ -255,6 +259,7 @@ struct MxParams {
   int32_t num_heads, num_programs;
   int64_t total_tokens;
   float scale_log2;
+  int32_t* visits;  // debug (null: off): visits[i] += 1 each time tile i of the list is taken
 };
 
 // Allocation-free forward (jfa_fwd_noalloc): bytes of the file-scope device scratch
@@ -278,6 +283,8 @@ hipError_t launch_bwd_self_prep(const BwdParams& p, int head_dim, hipStream_t s)
 hipError_t launch_bwd_self_dq_ds(const BwdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_fwd(const BdParams& p, int head_dim, hipStream_t s);
 hipError_t launch_bd_bwd(const BdParams& p, int head_dim, hipStream_t s);
+// Rotary table [positions][head_dim/2][2] fp32: cos, sin of pos * base^(-2i/D).
+hipError_t launch_rope_table(float* table, int positions, int head_dim, double base, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 // Block-sparse variant, stage 1.
 hipError_t launch_pool(const PoolParams& p, int head_dim, hipStream_t s);

@@ -369,8 +369,10 @@ __global__ void __launch_bounds__(mx_waves(D) * 64)
     __attribute__((amdgpu_waves_per_eu(2, 2))) mx_fwd_kernel(MxParams p) {
   __shared__ __attribute__((aligned(16))) char smem[MxCfg<D>::SMEM];
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
-  for (int idx = p.seg_ptr[prog]; idx < p.seg_ptr[prog + 1]; ++idx)
+  for (int idx = p.seg_ptr[prog]; idx < p.seg_ptr[prog + 1]; ++idx) {
+    if (threadIdx.x == 0) count_visit(p.visits, idx);
     mx_tile<D>(p, p.tiles[idx], (JFA_LDS char*)smem, threadIdx.x);
+  }
 }
 
 hipError_t grid_launch(void (*k)(MxQuantParams), const MxQuantParams& p, int64_t threads, hipStream_t s) {

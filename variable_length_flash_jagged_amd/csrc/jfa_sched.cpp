@@ -117,7 +117,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
 }
 
 void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int block,
-                        int max_programs, Schedule& out) {
+                        int max_programs, int min_tiles, Schedule& out) {
   out.tile_rows = block;
   out.groups = 0;
   out.tiles.clear();
@@ -125,7 +125,7 @@ void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int 
     for (int32_t j = 0; j < (int32_t)cdiv(lengths[b], block); ++j)
       for (int h = 0; h < num_heads; ++h) out.tiles.push_back({b, h, j});
   const int64_t n = (int64_t)out.tiles.size();
-  const int p = (int)std::min<int64_t>(max_programs, n);
+  const int p = (int)std::min<int64_t>(max_programs, cdiv(n, std::max(1, min_tiles)));
   out.programs = p;
   out.seg_ptr.assign(p + 1, 0);
   if (p == 0) return;

@@ -48,7 +48,9 @@ void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
                   int rows, int max_programs, bool dynamic, Schedule& out);
 void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
                   int max_programs, bool dynamic, Schedule& out);
+// Programs: min(max_programs, ceil(tiles / min_tiles)) (the block-diagonal kernels'
+// workgroups hold min_tiles = kBdWaves waves, one tile each at a time).
 void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int block,
-                        int max_programs, Schedule& out);
+                        int max_programs, int min_tiles, Schedule& out);
 
 }  // namespace jfa
