@@ -44,6 +44,7 @@
 // to zero through the row-term MFMA: every row term carries -1 in one extra k-slot,
 // which those waves' B operand scales by 1e30.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "jfa_device.h"
@@ -798,259 +799,381 @@ __global__ void __launch_bounds__(NW * 64)
             [&](Tile t) { dkdv_tile<D, STORE, SPARSE, NW, NS>(p, t, smem, ln, threadIdx.x); });
 }
 
-// ------------------------------------------- dK, dV: 16 keys per wave (head_dim 128)
+// ------------------------------- dK, dV: two waves per SIMD (self attention, head_dim 128)
 //
-// The products of dkdv_tile (recompute path) on v_mfma_f32_16x16x32_bf16 with 16 keys
-// per wave and eight waves per 128-key tile: a wave's K, V operands, dK, dV accumulators
-// and scores fit in 256 registers, so two waves share each SIMD and one wave's waits on
-// LDS data and matrix results are covered by the other's work.  Operand layouts
-// (16x16x32): A lane l <-> (row l%16, k 8*(l/16)..+7), B lane l <-> (column l%16, the
-// same k), C lane l <-> (column l%16, rows 4*(l/16)..+3).  S' = Q (cK)^T + row term and
-// dP' = dO V^T + row term come out with lane = key column and, for lane group g = l/16,
-// queries 4g..4g+3 of each 16-query block; dV^T += dO^T P and dK^T += Q^T dS contract
-// over each 32-query step in the order (4g..4g+3, 16+4g..16+4g+3), so the packed P and
-// dS registers are their B operands as they stand, and the A operands dO^T, Q^T are two
-// transposed reads of four rows each.
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Not used yet: parity-clean, but measured slower than dkdv_kernel on the production
-// workload's recompute pass (9.40 against 8.75 ms).  Its two waves per SIMD reach the
-// same phase of a step at the same time (the per-step barrier aligns them), so their
-// matrix and vector work does not overlap; pairing them one phase apart, as the
-// forward does, is the step that remains.
-constexpr bool kUseKv16 = false;
-constexpr int kKv16Waves = 8;
-
+// The products of dkdv_tile with two waves on every SIMD, so that one wave's waits on
+// LDS data and matrix results are covered by the other's work.  A workgroup is 8 waves
+// on one 128-key tile; waves w and w + 4 (one SIMD) own the same 32 keys, 32 (w & 3)
+// .. + 31, and split every 64-row query step: wave group g = w / 4 takes rows
+// 32 g .. 32 g + 31.  Each wave keeps fp32 dK^T, dV^T partials of its keys over its
+// rows; at the end of the tile group 1 hands its partials to group 0 through LDS and
+// group 0 stores the sums.  One wave's registers then hold only those partials, the
+// scores and a few operands (no K, V rows): the K tile (pre-scaled by c = scale log2 e
+// and rounded to bf16, as dkdv_tile does in registers) and the V tile stay in LDS for
+// the whole tile and are read as the B operands of S' and dP'.  Q, dO and the row
+// terms stream through a two-slot ring (copies one step ahead).  Per 32-row sub-step a
+// wave runs one stream of 34 MFMAs
+//   S' row term, S' k-steps | dP' row term, dP' k-steps | dV^T (u, db) | dK^T (u, db)
+// with the LDS operands of each read AHEAD positions early, P = 2^S' formed during
+// the dP' k-steps and dS = P dP' during the dV products (as KvStream).
 template <int D>
-struct Kv16Cfg {
-  static constexpr int NW = kKv16Waves;
-  static constexpr int BN = NW * 16;    // keys per tile
-  static constexpr int QB = kBwdRows;   // queries per step
-  static constexpr int NQ16 = QB / 16;  // 16-query blocks of S', dP'
-  static constexpr int NK32 = QB / 32;  // 32-query k-steps of dV^T, dK^T
-  static constexpr int NKS = D / 32;    // 32-wide k-steps over the head dim
-  static constexpr int NDB = D / 16;    // 16-wide head-dim blocks of dK^T, dV^T
+struct Kv2Cfg {
+  static constexpr int NW = 8;
+  static constexpr int BN = 128;       // keys per tile (the backward schedule's kBwdKeys)
+  static constexpr int QB = kBwdRows;  // query rows per step
+  static constexpr int NKS = D / 16;
+  static constexpr int NDB = D / 32;
   static constexpr int RB = 2 * D;
+  static constexpr int KBUF = BN * RB;  // K or V tile
   static constexpr int QBUF = QB * RB;
   static constexpr int ABUF = QB * 16;
-  static constexpr int NS = 3;
-  static constexpr int OFF_Q = 0, OFF_DO = OFF_Q + NS * QBUF, OFF_AUG = OFF_DO + NS * QBUF;
-  static constexpr int SMEM = OFF_AUG + NS * ABUF;
+  // LDS: the two ring slots [Q | dO | row terms] first, so that every ring address is a
+  // per-lane register plus an immediate below 64 KB; then the K and V tiles.
+  static constexpr int SLOT = 2 * QBUF + ABUF;
+  static constexpr int OFF_DO = QBUF, OFF_AUG = 2 * QBUF;
+  static constexpr int OFF_K = 2 * SLOT, OFF_V = OFF_K + KBUF;
+  static constexpr int SMEM = OFF_V + KBUF;
+  // end of tile: group 1's partials, [dK | dV][key block][db][chunk][lane][4 floats]
+  static constexpr int RED_ONE = 4 * NDB * 4 * 64 * 16;
   static_assert(BN == kBwdKeys && QB == 64, "tiles of the backward schedule, one 64-lane row-term copy");
+  static_assert(2 * RED_ONE <= SMEM, "reduction buffer inside the tile's LDS");
+  static_assert(SLOT + OFF_DO + 16 * RB + 256 <= 65536, "ring immediates (the largest: slot 1, dO, rows 16..) below 64 KB");
 };
 
+// Per-lane LDS byte offsets of one wave (its query rows 32 g .., its keys 32 kw ..
+// folded in) and copy offsets.
 template <int D>
-struct Kv16Lane {
-  using Copy = TileCopy<Kv16Cfg<D>::RB, Kv16Cfg<D>::QB, kKv16Waves>;
-  Copy copy;
-  bf16x8 sel_s, sel_dp;  // B operands picking the row term's k-slots 0,1 (S') and 4,5 (dP')
-  __device__ __forceinline__ void init_sel(int lane) {
-    const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
-    const bool lo = lane < 16;
-    sel_s = bf16x8{lo ? one : zero, lo ? one : zero, zero, zero, zero, zero, zero, zero};
-    sel_dp = bf16x8{zero, zero, zero, zero, lo ? one : zero, lo ? one : zero, zero, zero};
-  }
-};
-
-// Head-dim columns of row m of block db of the transposed products: four runs of four,
-// run t = m / 4 at column kv16_col(db, t) -- 16-byte chunks c0 and c0 + 2 of the tile row
-// (c0 = 0, 1, 4, 5, 8, 9, 12, 13 over the blocks), both 8-byte halves of each.  With the
-// tiles' row swizzle this keeps the transposed reads of a 32-lane pass on 64 distinct
-// banks (sixteen consecutive columns would put two rows on each bank).
-__device__ __forceinline__ int kv16_col(int db, int t) {
-  const int c0 = (db & 1) | ((db >> 1) << 2);
-  return 8 * (c0 + 2 * (t & 1)) + 4 * (t >> 1);
-}
-
-// A operand [16 head-dim rows of block db x 32 queries] of the transposed product from a
-// row-major query tile: lane group g takes queries q0+4g..+3 and q0+16+4g..+3; lane i of
-// the group is row i, head-dim column kv16_col(db, i / 4) + i % 4.
-template <int RB>
-__device__ __forceinline__ bf16x8 tr16_operand(const JFA_LDS char* tile, int q0, int db, int lane) {
-  const int g = lane >> 4, s16 = lane & 15;
-  const int r = q0 + 4 * g + (s16 >> 2);
-  const int col = kv16_col(db, s16 & 3);
-  const int w8 = (col & 7) * 2;
-  return join_tr(lds_tr4(tile, swz_off<RB>(r, col >> 3) + w8), lds_tr4(tile, swz_off<RB>(r + 16, col >> 3) + w8));
-}
-
-template <int D>
-__device__ __forceinline__ void kv16_step(const JFA_LDS char* qt, const JFA_LDS char* dot, const JFA_LDS char* augt,
-                                          const Kv16Lane<D>& ln, const bf16x8 (&kf)[Kv16Cfg<D>::NKS],
-                                          const bf16x8 (&vf)[Kv16Cfg<D>::NKS], f32x4 (&dk)[Kv16Cfg<D>::NDB],
-                                          f32x4 (&dv)[Kv16Cfg<D>::NDB], int lane) {
-  using C = Kv16Cfg<D>;
-  const int r16 = lane & 15, g = lane >> 4;
-  f32x4 s[C::NQ16], dp[C::NQ16];
-#pragma unroll
-  for (int qb = 0; qb < C::NQ16; ++qb) {
-    const int row = qb * 16 + r16;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    // the row's 16-byte term sits in k-slots 0..7 (lane group 0); the other groups read
-    // it too (no branch inside the step) and mask it to zero
-    const u32x4 a16 = lds_ld16(augt, row * 16);
-    const uint32_t keep = g == 0 ? 0xFFFFFFFFu : 0u;
-    const bf16x8 aug = as_bf16x8(u32x4{a16.x & keep, a16.y & keep, a16.z & keep, a16.w & keep});
-    s[qb] = mfma16(aug, ln.sel_s, z);
-    dp[qb] = mfma16(aug, ln.sel_dp, z);
+struct Kv2Lane {
+  using C = Kv2Cfg<D>;
+  int qoff[C::NKS];        // row operand ks of the wave's 32 query rows (add a slot base, + OFF_DO for dO)
+  int koff[C::NKS];        // row operand ks of the wave's 32 keys in the K tile (+ KBUF for V)
+  int troff[C::NDB][2];    // transposed operand (db, half) of query rows 32 g .. (+ 16 u rows)
+  int aoff;                // the row term of query row 32 g + l32
+  TileCopy<C::RB, C::QB, 8> copy;   // a step's Q or dO rows
+  TileCopy<C::RB, C::BN, 8> kcopy;  // the tile's K or V rows
+  bf16x8 pick_s, pick_dp;
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride_bytes) {
+    const int g = wave >> 2, kw = wave & 3;
+    RowOperands<C::RB, C::NKS> row;
+    TrOperands<C::RB, C::NDB> tr;
+    row.init(lane);
+    tr.init(lane);
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      const int off = swz_off<C::RB>(row, 4 * ks + g);
-      s[qb] = mfma16(as_bf16x8(lds_ld16(qt, off)), kf[ks], s[qb]);
-      dp[qb] = mfma16(as_bf16x8(lds_ld16(dot, off)), vf[ks], dp[qb]);
+      qoff[ks] = 32 * g * C::RB + row.off[ks];
+      koff[ks] = C::OFF_K + 32 * kw * C::RB + row.off[ks];
+    }
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) troff[db][hi] = 32 * g * C::RB + tr.off[db][hi];
+    aoff = C::OFF_AUG + (32 * g + (lane & 31)) * 16;
+    copy.init(row_stride_bytes, wave, lane);
+    kcopy.init(row_stride_bytes, wave, lane);
+    const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
+    const bool lo = lane < 32;
+    pick_s = bf16x8{lo ? one : zero, lo ? one : zero, zero, zero, zero, zero, zero, zero};
+    pick_dp = bf16x8{zero, zero, zero, zero, lo ? one : zero, lo ? one : zero, zero, zero};
+  }
+};
+
+// One 32-row sub-step of one wave, from ring slot SL, as a single MFMA stream
+// (positions 0 .. N-1).
+template <int D, bool STORE, int AHEAD, int SL>
+struct Kv2Stream {
+  using C = Kv2Cfg<D>;
+  static constexpr int NKS = C::NKS, NDB = C::NDB;
+  static constexpr int S0 = 0, DP0 = NKS + 1, DV0 = 2 * NKS + 2, DK0 = DV0 + 2 * NDB, N = DK0 + 2 * NDB;
+  static constexpr int NBUF = AHEAD + 1;
+  static constexpr int P_PER = 16 / NKS;          // P values per dP' k-step
+  static constexpr int DS_SL = 2 * NDB - 2;       // dS slices: dV positions 2 .. 2 NDB - 1
+  static constexpr int DS_PER = (16 + DS_SL - 1) / DS_SL;
+  static constexpr int ST0 = DK0 + 1, ST1 = DK0 + 3;  // dS store positions (STORE)
+  static constexpr int BASE = SL * C::SLOT;
+
+  const JFA_LDS char* lds;
+  const Kv2Lane<D>& ln;
+  f32x16 (&dk)[NDB];
+  f32x16 (&dv)[NDB];
+  char* sblk;            // STORE: this step's dS block (wave-uniform)
+  uint32_t soff;         // STORE: this lane's store offset
+  const int qq;          // STORE: query block of the 64-row step (the wave group)
+  bf16x8 a[NBUF], b[NBUF];
+  bf16x8 term;
+  f32x16 s, dp;
+  float pr[16], dsr[16];
+  bf16x8 pf[2], dsf[2];
+
+  __device__ __forceinline__ Kv2Stream(const JFA_LDS char* lds_, const Kv2Lane<D>& ln_, f32x16 (&dk_)[NDB],
+                                       f32x16 (&dv_)[NDB], char* sblk_, uint32_t soff_, int qq_)
+      : lds(lds_), ln(ln_), dk(dk_), dv(dv_), sblk(sblk_), soff(soff_), qq(qq_) {}
+
+  __device__ __forceinline__ bf16x8 rd(int reg_off, int imm) const { return as_bf16x8(lds_ld16(lds + imm, reg_off)); }
+  __device__ __forceinline__ bf16x8 rd_tr(int db, int imm) const {
+    return join_tr(lds_tr4(lds + imm, ln.troff[db][0]), lds_tr4(lds + imm, ln.troff[db][1]));
+  }
+
+  template <int K>
+  __device__ __forceinline__ void read() {
+    constexpr int i = K % NBUF;
+    if constexpr (K == S0) {
+      a[i] = rd(ln.aoff, BASE);
+    } else if constexpr (K < DP0) {
+      a[i] = rd(ln.qoff[K - 1], BASE);
+      b[i] = rd(ln.koff[K - 1], 0);
+    } else if constexpr (K == DP0) {
+    } else if constexpr (K < DV0) {
+      a[i] = rd(ln.qoff[K - DP0 - 1], BASE + C::OFF_DO);
+      b[i] = rd(ln.koff[K - DP0 - 1], C::KBUF);
+    } else if constexpr (K < DK0) {
+      constexpr int u = (K - DV0) / NDB, db = (K - DV0) % NDB;
+      a[i] = rd_tr(db, BASE + C::OFF_DO + 16 * u * C::RB);
+    } else {
+      constexpr int u = (K - DK0) / NDB, db = (K - DK0) % NDB;
+      a[i] = rd_tr(db, BASE + 16 * u * C::RB);
     }
   }
-  // P = 2^S' (S' is the base-2 exponent: K pre-scaled, -lse log2 e in the row term) and
-  // dS = P (dP - Di) (-Di in the row term), packed as the B operands of the next products
-  bf16x8 pb[C::NK32], dsb[C::NK32];
-#pragma unroll
-  for (int kk = 0; kk < C::NK32; ++kk) {
-    float pv[8], dv8[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = fast_exp2(s[2 * kk][i]);
-      pv[4 + i] = fast_exp2(s[2 * kk + 1][i]);
-      dv8[i] = pv[i] * dp[2 * kk][i];
-      dv8[4 + i] = pv[4 + i] * dp[2 * kk + 1][i];
-    }
-    pb[kk] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-    dsb[kk] = pack8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
+  template <int K>
+  static constexpr int reads() {
+    return K == S0 ? 1 : (K < DP0 ? 2 : (K == DP0 ? 0 : 2));
   }
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int kk = 0; kk < C::NK32; ++kk) {
-      dv[db] = mfma16(tr16_operand<C::RB>(dot, 32 * kk, db, lane), pb[kk], dv[db]);
-      dk[db] = mfma16(tr16_operand<C::RB>(qt, 32 * kk, db, lane), dsb[kk], dk[db]);
+
+  template <int K>
+  __device__ __forceinline__ void mfma() {
+    constexpr int i = K % NBUF;
+    if constexpr (K == S0) {
+      term = a[i];
+      s = mfma32(term, ln.pick_s, f32x16{});
+    } else if constexpr (K < DP0) {
+      s = mfma32(a[i], b[i], s);
+    } else if constexpr (K == DP0) {
+      dp = mfma32(term, ln.pick_dp, f32x16{});
+    } else if constexpr (K < DV0) {
+      dp = mfma32(a[i], b[i], dp);
+    } else if constexpr (K < DK0) {
+      constexpr int u = (K - DV0) / NDB, db = (K - DV0) % NDB;
+      dv[db] = mfma32(a[i], pf[u], dv[db]);
+    } else {
+      constexpr int u = (K - DK0) / NDB, db = (K - DK0) % NDB;
+      dk[db] = mfma32(a[i], dsf[u], dk[db]);
     }
-  // Issue order: LDS reads run ahead of the MFMAs that consume them -- the first eight up
-  // front, then one after each of the S', dP' MFMAs until that product's reads are out;
-  // the transposed reads of the dV, dK products (two per MFMA) start four MFMAs before
-  // the first of them, which keeps at most 15 LDS operations in flight.
-  constexpr int N1 = 2 * C::NQ16 * (C::NKS + 1);              // S', dP' MFMAs
-  constexpr int N2 = 2 * C::NDB * C::NK32;                    // dV, dK MFMAs
-  constexpr int R1 = C::NQ16 * (2 * C::NKS + 1);              // their LDS reads
-  constexpr int AHEAD = 8, LEAD2 = 4;
-  static_assert(R1 > AHEAD && R1 - AHEAD <= N1 - LEAD2, "read placement");
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+  }
+
+  template <int K>
+  __device__ __forceinline__ void valu() {
+    if constexpr (K >= DP0 + 1 && K < DV0) {
+      constexpr int j = K - DP0 - 1;
 #pragma unroll
-  for (int k = 0; k < N1 + N2; ++k) {
+      for (int e = 0; e < P_PER; ++e) pr[j * P_PER + e] = fast_exp2(s[j * P_PER + e]);
+      if constexpr ((j + 1) * P_PER == 8) pf[0] = pack8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+      if constexpr ((j + 1) * P_PER == 16)
+        pf[1] = pack8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+    } else if constexpr (K >= DV0 + 2 && K < DK0) {
+      constexpr int j = K - DV0 - 2;
+#pragma unroll
+      for (int e = 0; e < DS_PER; ++e) {
+        const int x = j * DS_PER + e;
+        if (x < 16) dsr[x] = pr[x] * dp[x];
+      }
+      if constexpr ((j + 1) * DS_PER >= 8 && j * DS_PER < 8)
+        dsf[0] = pack8(dsr[0], dsr[1], dsr[2], dsr[3], dsr[4], dsr[5], dsr[6], dsr[7]);
+      if constexpr (j == DS_SL - 1) dsf[1] = pack8(dsr[8], dsr[9], dsr[10], dsr[11], dsr[12], dsr[13], dsr[14], dsr[15]);
+    }
+  }
+  template <int K>
+  static constexpr int valus() {
+    if (K >= DP0 + 1 && K < DV0) return 2 * P_PER + ((K - DP0) * P_PER % 8 == 0 ? 4 : 0);
+    if (K >= DV0 + 2 && K < DK0) return DS_PER + 2;
+    return 0;
+  }
+
+  template <int K>
+  __device__ __forceinline__ void store() {
+    if constexpr (STORE && (K == ST0 || K == ST1)) store_ds_unit(sblk, soff, qq, K == ST0 ? 0 : 1, dsf[K == ST0 ? 0 : 1]);
+  }
+
+  template <int K>
+  __device__ __forceinline__ void order() {
+    if constexpr (K == 0) {
+      constexpr int r0 = reads<0>() + (AHEAD > 1 ? reads<1>() : 0) + (AHEAD > 2 ? reads<2>() : 0) +
+                         (AHEAD > 3 ? reads<3>() : 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, r0, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (k < R1 - AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    else if (k >= N1 - LEAD2 && k < N1 - LEAD2 + N2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if constexpr (valus<K>() > 0) __builtin_amdgcn_sched_group_barrier(0x002, valus<K>(), 0);
+    if constexpr (K + AHEAD < N && reads<K + AHEAD>() > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, reads<K + AHEAD>(), 0);
+    if constexpr (STORE && (K == ST0 || K == ST1)) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
   }
-}
 
-// Copies of one query step: Q, dO rows (all waves; rows past rows_valid repeat the last
-// valid row) and the row terms (wave 0; rows past rows_valid take the sentinel term).
-template <int D>
-__device__ __forceinline__ void kv16_issue(const Kv16Lane<D>& ln, const uint16_t* qb, const uint16_t* dob,
-                                           const uint16_t* aug, int64_t rs, int64_t aug_row0, int64_t sentinel,
-                                           int row0, int rows_valid, JFA_LDS char* qbuf, JFA_LDS char* dobuf,
-                                           JFA_LDS char* augbuf, int wave, int lane) {
-  const uint32_t rsb = (uint32_t)(rs * 2);
-  ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rows_valid, qbuf, wave, lane);
-  ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rows_valid, dobuf, wave, lane);
-  if (wave == 0) {
-    const int64_t r = lane < rows_valid ? aug_row0 + row0 + lane : sentinel;
-    dma16(uniform_ptr(aug), (uint32_t)(r * 16), augbuf);
+  template <int K>
+  __device__ __forceinline__ void step() {
+    mfma<K>();
+    valu<K>();
+    if constexpr (K + AHEAD < N) read<K + AHEAD>();
+    store<K>();
   }
-}
+  __device__ __forceinline__ void go() {
+    static_assert(AHEAD >= 1 && AHEAD <= 4, "read-ahead window");
+    prologue(std::make_integer_sequence<int, AHEAD>{});
+    body(std::make_integer_sequence<int, N>{});
+    orders(std::make_integer_sequence<int, N>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int... K>
+  __device__ __forceinline__ void prologue(std::integer_sequence<int, K...>) { (read<K>(), ...); }
+  template <int... K>
+  __device__ __forceinline__ void body(std::integer_sequence<int, K...>) { (step<K>(), ...); }
+  template <int... K>
+  __device__ __forceinline__ void orders(std::integer_sequence<int, K...>) { (order<K>(), ...); }
+};
 
-template <int D>
-__device__ __forceinline__ void dkdv16_tile(const BwdParams& p, Tile tile, char* smem_raw, const Kv16Lane<D>& ln,
-                                            int tid) {
-  using C = Kv16Cfg<D>;
+// MFMA positions an LDS operand is read ahead of its use (the recompute variant, with
+// no dS stores to keep, runs out of registers at 3).
+template <bool STORE>
+constexpr int kv2_ahead() { return STORE ? 3 : 2; }
+
+template <int D, bool STORE>
+__device__ __forceinline__ void dkdv2_tile(const BwdParams& p, Tile tile, char* smem_raw, const Kv2Lane<D>& ln,
+                                           int tid) {
+  using C = Kv2Cfg<D>;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, kw = wave & 3;
+  const int l32 = lane & 31, half = lane >> 5;
   const int b = tile.b, h = tile.hb >> 24, j = tile.hb & 0xFFFFFF;
   const int64_t rs = (int64_t)p.num_heads * D;
+  const uint32_t rsb = (uint32_t)(rs * 2);
   const int64_t s0 = p.offsets[b];
   const int L = (int)(p.offsets[b + 1] - s0);
   const int key0 = j * C::BN;
-  const int my_key = wave * 16 + r16;
-  const bool key_ok = my_key < L - key0;
+  const int keys = min(C::BN, L - key0);
+  const int my_key = 32 * kw + l32;
   const float c = p.scale_log2;
-  // query rows: the sequence's own tokens, or (broadcast-Q) the shared q rows with this
-  // sequence's dO and row terms
-  const bool bq = p.bq != 0;
-  const int Lq = bq ? p.num_q : L;
-  const uint16_t* qb = p.q + (bq ? 0 : s0 * rs) + (int64_t)h * D;
-  const uint16_t* dob = p.dout + (bq ? (int64_t)b * p.num_q : s0) * rs + (int64_t)h * D;
-  const int64_t aug_row0 = bq ? ((int64_t)b * p.num_heads + h) * p.num_q : (int64_t)h * p.total_tokens + s0;
-  const int64_t sentinel = bq ? (int64_t)p.num_seqs * p.num_heads * p.num_q : (int64_t)p.num_heads * p.total_tokens;
-  const int n = (Lq + C::QB - 1) / C::QB;
+  const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
+  const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
+  const int64_t aug_row0 = (int64_t)h * p.total_tokens + s0;
+  const int64_t sentinel = (int64_t)p.num_heads * p.total_tokens;
+  const int n = (L + C::QB - 1) / C::QB;
+  JFA_LDS char* kt = smem + C::OFF_K;
+
   auto issue = [&](int it, int slot) {
-    const int row0 = it * C::QB;
-    kv16_issue<D>(ln, qb, dob, p.row_aug, rs, aug_row0, sentinel, row0, min(C::QB, Lq - row0),
-                  smem + C::OFF_Q + slot * C::QBUF, smem + C::OFF_DO + slot * C::QBUF,
-                  smem + C::OFF_AUG + slot * C::ABUF, wave, lane);
+    JFA_LDS char* base = smem + slot * C::SLOT;
+    const int row0 = it * C::QB, rv = min(C::QB, L - row0);
+    ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rv, base, wave, lane);
+    ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rv, base + C::OFF_DO, wave, lane);
+    if (wave == 0) {
+      const int64_t r = lane < rv ? aug_row0 + row0 + lane : sentinel;
+      dma16(uniform_ptr(p.row_aug), (uint32_t)(r * 16), base + C::OFF_AUG);
+    }
   };
-  constexpr int COPIES = 2 * Kv16Lane<D>::Copy::J;
-  f32x4 dk[C::NDB], dv[C::NDB];
+  // K, V rows of the tile (rows past the sequence repeat its last row: their dK, dV are
+  // not stored and their stored dS is masked by the dQ kernel) and the first step
+  ln.kcopy.issue_rows(p.k + (s0 + key0) * rs + (int64_t)h * D, rsb, keys, kt, wave, lane);
+  ln.kcopy.issue_rows(p.v + (s0 + key0) * rs + (int64_t)h * D, rsb, keys, smem + C::OFF_V, wave, lane);
+  issue(0, 0);
+  wait_vmem();
+  __syncthreads();
+  {
+    // K *= c, rounded to bf16 (elementwise, so the swizzle does not matter)
+    constexpr int PASSES = C::KBUF / (C::NW * 64 * 16);
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int off = ((ps * C::NW + wave) * 64 + lane) * 16;
+      const bf16x8 x = as_bf16x8(lds_ld16(kt, off));
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (bf16)((float)x[e] * c);
+      lds_st16(kt, off, __builtin_bit_cast(u32x4, y));
+    }
+  }
+  __syncthreads();
+
+  f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dk[db][i] = dv[db][i] = 0.f;
-  // the ring's first copies go out before the key rows are loaded (one round trip)
-  if (n > 0) {
-    issue(0, 0);
-    if (n > 1) issue(1, 1);
+    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+  char* ds_row = nullptr;
+  uint32_t ds_off = 0;
+  if constexpr (STORE) {
+    const int64_t nj = (L + C::BN - 1) / C::BN;
+    ds_row = (char*)uniform_ptr(p.ds + (p.ds_base[b] + ((int64_t)h * nj + j) * n) * kDsBlockBytes);
+    ds_off = ds_store_offset(kw, lane);
   }
-  // this wave's 16 keys as B operands (lane: key r16, head-dim k-group g), K pre-scaled
-  // by c = scale log2 e; rows past the end are zero (their dK, dV are not stored)
-  bf16x8 kf[C::NKS], vf[C::NKS];
-  {
-    const int64_t base = (s0 + key0 + my_key) * rs + (int64_t)h * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      const bf16x8 kr = as_bf16x8(key_ok ? ld16(p.k + base + 32 * ks) : zero16());
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)kr[e] * c);
-      vf[ks] = as_bf16x8(key_ok ? ld16(p.v + base + 32 * ks) : zero16());
-    }
-  }
-  if (n > 0) {
-    wait_vmem();
-    __syncthreads();
-  }
-  for (int it = 0, cur = 0; it < n; ++it, cur = (cur == C::NS - 1 ? 0 : cur + 1)) {
-    if (it + 2 < n) issue(it + 2, cur == 0 ? C::NS - 1 : cur - 1);
-    kv16_step<D>(smem + C::OFF_Q + cur * C::QBUF, smem + C::OFF_DO + cur * C::QBUF, smem + C::OFF_AUG + cur * C::ABUF,
-                 ln, kf, vf, dk, dv, lane);
-    if (it + 2 < n) wait_vmem_n<COPIES>();
+  // One step from ring slot SL (compile time, so that every LDS address is a lane
+  // register plus an immediate): the next step's copies go to the other slot first.
+  auto one_step = [&](auto slot_tag, int it) {
+    constexpr int SL = decltype(slot_tag)::value;
+    if (it + 1 < n) issue(it + 1, SL ^ 1);
+    Kv2Stream<D, STORE, kv2_ahead<STORE>(), SL>(smem, ln, dk, dv, ds_row + (int64_t)it * kDsBlockBytes, ds_off, g).go();
+    // the next step's copies were issued before this step's two dS stores; loads and
+    // stores complete in issue order, so waiting for all but those two is enough
+    if (STORE) wait_vmem_n<2>();
     else wait_vmem();
     __syncthreads();
+  };
+  for (int it = 0; it < n; it += 2) {
+    one_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n) one_step(std::integral_constant<int, 1>{}, it + 1);
   }
-  if (key_ok) {
-    // C layout: lane = key; rows 4g..4g+3 of block db are the four consecutive head-dim
-    // columns kv16_col(db, g) .. +3
-    const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D;
+
+  // Group 1 hands its partials to group 0 through LDS (the ring and tiles are free now).
+  {
+    JFA_LDS char* red = smem;
+    const int unit = (kw * C::NDB) * 4 * 1024 + lane * 16;
+    if (g == 1) {
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int d = kv16_col(db, g);
-      st8(p.dk + row + d, pack4(dk[db][0] * p.scale, dk[db][1] * p.scale, dk[db][2] * p.scale, dk[db][3] * p.scale));
-      st8(p.dv + row + d, pack4(dv[db][0], dv[db][1], dv[db][2], dv[db][3]));
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int off = unit + (db * 4 + q4) * 1024;
+          lds_st16(red, off, __builtin_bit_cast(u32x4, float4{dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2],
+                                                                dk[db][4 * q4 + 3]}));
+          lds_st16(red, C::RED_ONE + off,
+                   __builtin_bit_cast(u32x4, float4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2],
+                                                   dv[db][4 * q4 + 3]}));
+        }
     }
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int off = unit + (db * 4 + q4) * 1024;
+          const float4 x = __builtin_bit_cast(float4, lds_ld16(red, off));
+          const float4 y = __builtin_bit_cast(float4, lds_ld16(red, C::RED_ONE + off));
+          dk[db][4 * q4] += x.x; dk[db][4 * q4 + 1] += x.y; dk[db][4 * q4 + 2] += x.z; dk[db][4 * q4 + 3] += x.w;
+          dv[db][4 * q4] += y.x; dv[db][4 * q4 + 1] += y.y; dv[db][4 * q4 + 2] += y.z; dv[db][4 * q4 + 3] += y.w;
+        }
+      if (my_key < keys) {
+        const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D + 4 * half;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = 32 * db + 8 * g4;
+            st8(p.dk + row + d, pack4(dk[db][4 * g4] * p.scale, dk[db][4 * g4 + 1] * p.scale,
+                                      dk[db][4 * g4 + 2] * p.scale, dk[db][4 * g4 + 3] * p.scale));
+            st8(p.dv + row + d, pack4(dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]));
+          }
+      }
+    }
+    __syncthreads();  // the next tile's copies overwrite the buffer
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(kKv16Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-    dkdv16_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[Kv16Cfg<D>::SMEM];
+template <int D, bool STORE>
+__global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    dkdv2_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[Kv2Cfg<D>::SMEM];
   __shared__ int next_tile;
-  Kv16Lane<D> ln;
-  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  ln.init_sel(threadIdx.x & 63);
-  // broadcast-Q: head-pinned groups of programs_per_head programs
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, p.bq ? p.programs_per_head : xcd_gsize(), &next_tile, p.visits,
-            [&](Tile t) { dkdv16_tile<D>(p, t, smem, ln, threadIdx.x); });
+  Kv2Lane<D> ln;
+  ln.init(threadIdx.x >> 6, threadIdx.x & 63, (uint32_t)(p.num_heads * D * 2));
+  tile_loop(p, p.tiles, p.seg_ptr, p.counters, xcd_gsize(), &next_tile, p.visits,
+            [&](Tile t) { dkdv2_tile<D, STORE>(p, t, smem, ln, threadIdx.x); });
 }
 
 // --------------------------------------------------------- stored-dS path: row terms
@@ -1304,9 +1427,10 @@ hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s)
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<64, false, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<64, false, false>), grid, block, 0, s, p);
   } else {
-    if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true, false>), grid, block, 0, s, p);
+    if (p.ds && p.dkdv_variant == 1) hipLaunchKernelGGL((dkdv2_kernel<128, true>), grid, dim3(512), 0, s, p);
+    else if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true, false>), grid, block, 0, s, p);
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<128, false, true>), grid, block, 0, s, p);
-    else if (kUseKv16) hipLaunchKernelGGL((dkdv16_kernel<128>), grid, dim3(kKv16Waves * 64), 0, s, p);
+    else if (p.dkdv_variant == 1 && !p.bq) hipLaunchKernelGGL((dkdv2_kernel<128, false>), grid, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<128, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
