@@ -849,7 +849,7 @@ struct Kv2Lane {
   int koff[C::NKS];        // row operand ks of the wave's 32 keys in the K tile (+ KBUF for V)
   int troff[C::NDB][2];    // transposed operand (db, half) of query rows 32 g .. (+ 16 u rows)
   int aoff;                // the row term of query row 32 g + l32
-  TileCopy<C::RB, C::QB, 8> copy;   // a step's Q or dO rows
+  TileCopy<C::RB, C::QB, 4> copy;   // a step's Q or dO rows (copied by the four waves of group 0)
   TileCopy<C::RB, C::BN, 8> kcopy;  // the tile's K or V rows
   bf16x8 pick_s, pick_dp;
   __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride_bytes) {
@@ -868,7 +868,7 @@ struct Kv2Lane {
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) troff[db][hi] = 32 * g * C::RB + tr.off[db][hi];
     aoff = C::OFF_AUG + (32 * g + (lane & 31)) * 16;
-    copy.init(row_stride_bytes, wave, lane);
+    copy.init(row_stride_bytes, wave & 3, lane);
     kcopy.init(row_stride_bytes, wave, lane);
     const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
     const bool lo = lane < 32;
@@ -1033,147 +1033,232 @@ struct Kv2Stream {
 template <bool STORE>
 constexpr int kv2_ahead() { return STORE ? 3 : 2; }
 
-template <int D, bool STORE>
-__device__ __forceinline__ void dkdv2_tile(const BwdParams& p, Tile tile, char* smem_raw, const Kv2Lane<D>& ln,
-                                           int tid) {
+// Geometry of one dK/dV tile.
+struct Kv2Tile {
+  int h, j, L, key0, keys, n;
+  int64_t s0, b;
+};
+
+template <int D>
+__device__ __forceinline__ Kv2Tile kv2_tile_of(const BwdParams& p, Tile t) {
   using C = Kv2Cfg<D>;
-  JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = wave >> 2, kw = wave & 3;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int b = tile.b, h = tile.hb >> 24, j = tile.hb & 0xFFFFFF;
+  Kv2Tile x;
+  x.b = t.b;
+  x.h = t.hb >> 24;
+  x.j = t.hb & 0xFFFFFF;
+  x.s0 = p.offsets[t.b];
+  x.L = (int)(p.offsets[t.b + 1] - x.s0);
+  x.key0 = x.j * C::BN;
+  x.keys = min(C::BN, x.L - x.key0);
+  x.n = (x.L + C::QB - 1) / C::QB;
+  return x;
+}
+
+// Copies of query step `it` of tile x into ring slot `slot`: Q and dO rows (the four
+// waves of group 0; rows past the sequence repeat its last row) and the row terms
+// (wave 0; rows past the sequence take the sentinel term, P = dS = 0).
+template <int D>
+__device__ __forceinline__ void kv2_issue_step(const BwdParams& p, const Kv2Lane<D>& ln, const Kv2Tile& x, int it,
+                                               int slot, JFA_LDS char* smem, int wave, int lane) {
+  using C = Kv2Cfg<D>;
+  if (wave >= 4) return;
   const int64_t rs = (int64_t)p.num_heads * D;
   const uint32_t rsb = (uint32_t)(rs * 2);
-  const int64_t s0 = p.offsets[b];
-  const int L = (int)(p.offsets[b + 1] - s0);
-  const int key0 = j * C::BN;
-  const int keys = min(C::BN, L - key0);
-  const int my_key = 32 * kw + l32;
-  const float c = p.scale_log2;
-  const uint16_t* qb = p.q + s0 * rs + (int64_t)h * D;
-  const uint16_t* dob = p.dout + s0 * rs + (int64_t)h * D;
-  const int64_t aug_row0 = (int64_t)h * p.total_tokens + s0;
-  const int64_t sentinel = (int64_t)p.num_heads * p.total_tokens;
-  const int n = (L + C::QB - 1) / C::QB;
-  JFA_LDS char* kt = smem + C::OFF_K;
-
-  auto issue = [&](int it, int slot) {
-    JFA_LDS char* base = smem + slot * C::SLOT;
-    const int row0 = it * C::QB, rv = min(C::QB, L - row0);
-    ln.copy.issue_rows(qb + (int64_t)row0 * rs, rsb, rv, base, wave, lane);
-    ln.copy.issue_rows(dob + (int64_t)row0 * rs, rsb, rv, base + C::OFF_DO, wave, lane);
-    if (wave == 0) {
-      const int64_t r = lane < rv ? aug_row0 + row0 + lane : sentinel;
-      dma16(uniform_ptr(p.row_aug), (uint32_t)(r * 16), base + C::OFF_AUG);
-    }
-  };
-  // K, V rows of the tile (rows past the sequence repeat its last row: their dK, dV are
-  // not stored and their stored dS is masked by the dQ kernel) and the first step
-  ln.kcopy.issue_rows(p.k + (s0 + key0) * rs + (int64_t)h * D, rsb, keys, kt, wave, lane);
-  ln.kcopy.issue_rows(p.v + (s0 + key0) * rs + (int64_t)h * D, rsb, keys, smem + C::OFF_V, wave, lane);
-  issue(0, 0);
-  wait_vmem();
-  __syncthreads();
-  {
-    // K *= c, rounded to bf16 (elementwise, so the swizzle does not matter)
-    constexpr int PASSES = C::KBUF / (C::NW * 64 * 16);
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int off = ((ps * C::NW + wave) * 64 + lane) * 16;
-      const bf16x8 x = as_bf16x8(lds_ld16(kt, off));
-      bf16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (bf16)((float)x[e] * c);
-      lds_st16(kt, off, __builtin_bit_cast(u32x4, y));
-    }
-  }
-  __syncthreads();
-
-  f32x16 dk[C::NDB], dv[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
-  char* ds_row = nullptr;
-  uint32_t ds_off = 0;
-  if constexpr (STORE) {
-    const int64_t nj = (L + C::BN - 1) / C::BN;
-    ds_row = (char*)uniform_ptr(p.ds + (p.ds_base[b] + ((int64_t)h * nj + j) * n) * kDsBlockBytes);
-    ds_off = ds_store_offset(kw, lane);
-  }
-  // One step from ring slot SL (compile time, so that every LDS address is a lane
-  // register plus an immediate): the next step's copies go to the other slot first.
-  auto one_step = [&](auto slot_tag, int it) {
-    constexpr int SL = decltype(slot_tag)::value;
-    if (it + 1 < n) issue(it + 1, SL ^ 1);
-    Kv2Stream<D, STORE, kv2_ahead<STORE>(), SL>(smem, ln, dk, dv, ds_row + (int64_t)it * kDsBlockBytes, ds_off, g).go();
-    // the next step's copies were issued before this step's two dS stores; loads and
-    // stores complete in issue order, so waiting for all but those two is enough
-    if (STORE) wait_vmem_n<2>();
-    else wait_vmem();
-    __syncthreads();
-  };
-  for (int it = 0; it < n; it += 2) {
-    one_step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n) one_step(std::integral_constant<int, 1>{}, it + 1);
-  }
-
-  // Group 1 hands its partials to group 0 through LDS (the ring and tiles are free now).
-  {
-    JFA_LDS char* red = smem;
-    const int unit = (kw * C::NDB) * 4 * 1024 + lane * 16;
-    if (g == 1) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int off = unit + (db * 4 + q4) * 1024;
-          lds_st16(red, off, __builtin_bit_cast(u32x4, float4{dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2],
-                                                                dk[db][4 * q4 + 3]}));
-          lds_st16(red, C::RED_ONE + off,
-                   __builtin_bit_cast(u32x4, float4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2],
-                                                   dv[db][4 * q4 + 3]}));
-        }
-    }
-    __syncthreads();
-    if (g == 0) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int off = unit + (db * 4 + q4) * 1024;
-          const float4 x = __builtin_bit_cast(float4, lds_ld16(red, off));
-          const float4 y = __builtin_bit_cast(float4, lds_ld16(red, C::RED_ONE + off));
-          dk[db][4 * q4] += x.x; dk[db][4 * q4 + 1] += x.y; dk[db][4 * q4 + 2] += x.z; dk[db][4 * q4 + 3] += x.w;
-          dv[db][4 * q4] += y.x; dv[db][4 * q4 + 1] += y.y; dv[db][4 * q4 + 2] += y.z; dv[db][4 * q4 + 3] += y.w;
-        }
-      if (my_key < keys) {
-        const int64_t row = (s0 + key0 + my_key) * rs + (int64_t)h * D + 4 * half;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d = 32 * db + 8 * g4;
-            st8(p.dk + row + d, pack4(dk[db][4 * g4] * p.scale, dk[db][4 * g4 + 1] * p.scale,
-                                      dk[db][4 * g4 + 2] * p.scale, dk[db][4 * g4 + 3] * p.scale));
-            st8(p.dv + row + d, pack4(dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]));
-          }
-      }
-    }
-    __syncthreads();  // the next tile's copies overwrite the buffer
+  JFA_LDS char* base = smem + slot * C::SLOT;
+  const int row0 = it * C::QB, rv = min(C::QB, x.L - row0);
+  const int64_t first = (x.s0 + row0) * rs + (int64_t)x.h * D;
+  ln.copy.issue_rows(p.q + first, rsb, rv, base, wave, lane);
+  ln.copy.issue_rows(p.dout + first, rsb, rv, base + C::OFF_DO, wave, lane);
+  if (wave == 0) {
+    const int64_t r = lane < rv ? (int64_t)x.h * p.total_tokens + x.s0 + row0 + lane
+                                : (int64_t)p.num_heads * p.total_tokens;
+    dma16(uniform_ptr(p.row_aug), (uint32_t)(r * 16), base + C::OFF_AUG);
   }
 }
 
+// K, V rows of tile x (all eight waves; rows past the sequence repeat its last row:
+// their dK, dV are not stored and their stored dS is masked by the dQ kernel).
+template <int D>
+__device__ __forceinline__ void kv2_issue_kv(const BwdParams& p, const Kv2Lane<D>& ln, const Kv2Tile& x,
+                                             JFA_LDS char* smem, int wave, int lane) {
+  using C = Kv2Cfg<D>;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  const int64_t first = (x.s0 + x.key0) * rs + (int64_t)x.h * D;
+  ln.kcopy.issue_rows(p.k + first, rsb, x.keys, smem + C::OFF_K, wave, lane);
+  ln.kcopy.issue_rows(p.v + first, rsb, x.keys, smem + C::OFF_V, wave, lane);
+}
+
+// s_waitcnt vmcnt(N) for N < 64 (the counter's high bits sit at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Persistent loop over the dK/dV tiles.  The next tile is reserved one tile ahead, so
+// that its K, V rows and first query step are copied while the current tile sums its
+// two groups' partials (which then use only ring slot 0; every tile starts its steps
+// in slot 1).
 template <int D, bool STORE>
 __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     dkdv2_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[Kv2Cfg<D>::SMEM];
+  using C = Kv2Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
   __shared__ int next_tile;
+  JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, kw = wave & 3;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const float c = p.scale_log2;
   Kv2Lane<D> ln;
-  ln.init(threadIdx.x >> 6, threadIdx.x & 63, (uint32_t)(p.num_heads * D * 2));
-  tile_loop(p, p.tiles, p.seg_ptr, p.counters, xcd_gsize(), &next_tile, p.visits,
-            [&](Tile t) { dkdv2_tile<D, STORE>(p, t, smem, ln, threadIdx.x); });
+  ln.init(wave, lane, (uint32_t)(rs * 2));
+
+  const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  const int gsize = xcd_gsize(), grp = prog / gsize;
+  int idx, end, base = 0;
+  if (!p.dynamic) {
+    idx = p.seg_ptr[prog];
+    end = p.seg_ptr[prog + 1];
+  } else {
+    base = p.seg_ptr[grp];
+    end = p.seg_ptr[grp + 1];
+    idx = base + prog % gsize;
+  }
+  if (idx >= end) return;
+  Kv2Tile x = kv2_tile_of<D>(p, p.tiles[idx]);
+  kv2_issue_kv<D>(p, ln, x, smem, wave, lane);
+  kv2_issue_step<D>(p, ln, x, 0, 1, smem, wave, lane);
+  // store instructions this wave issued for the previous tile's dK, dV, after this
+  // tile's copies (wave-uniform)
+  int stores = 0;
+  while (true) {
+    // reserve the next tile
+    int nxt = idx + 1;
+    if (p.dynamic) {
+      if (tid == 0) next_tile = base + gsize + atomicAdd(p.counters + grp, 1);
+      __syncthreads();
+      nxt = next_tile;
+    }
+    if (tid == 0) count_visit(p.visits, idx);
+    // this tile's K, V and first step have landed (group 0's dK, dV stores of the
+    // previous tile, issued after them, may still be in flight)
+    if (stores) wait_vmem_upto<4 * C::NDB>();
+    else wait_vmem();
+    __syncthreads();
+    {
+      // K *= c, rounded to bf16 (elementwise, so the swizzle does not matter)
+      constexpr int PASSES = C::KBUF / (C::NW * 64 * 16);
+      JFA_LDS char* kt = smem + C::OFF_K;
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int off = ((ps * C::NW + wave) * 64 + lane) * 16;
+        const bf16x8 xv = as_bf16x8(lds_ld16(kt, off));
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)((float)xv[e] * c);
+        lds_st16(kt, off, __builtin_bit_cast(u32x4, y));
+      }
+    }
+    __syncthreads();
+
+    f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
+    char* ds_row = nullptr;
+    uint32_t ds_off = 0;
+    if constexpr (STORE) {
+      const int64_t nj = (x.L + C::BN - 1) / C::BN;
+      ds_row = (char*)uniform_ptr(p.ds + (p.ds_base[x.b] + ((int64_t)x.h * nj + x.j) * x.n) * kDsBlockBytes);
+      ds_off = ds_store_offset(kw, lane);
+    }
+    // Step it reads slot (it + 1) & 1 (compile time, so that every LDS address is a lane
+    // register plus an immediate); the next step's copies go to the other slot first.
+    auto one_step = [&](auto slot_tag, int it) {
+      constexpr int SL = decltype(slot_tag)::value;
+      if (it + 1 < x.n) kv2_issue_step<D>(p, ln, x, it + 1, SL ^ 1, smem, wave, lane);
+      Kv2Stream<D, STORE, kv2_ahead<STORE>(), SL>(smem, ln, dk, dv, ds_row + (int64_t)it * kDsBlockBytes, ds_off, g)
+          .go();
+      // group 0's next-step copies were issued before this step's two dS stores; loads
+      // and stores complete in issue order, so waiting for all but those two suffices
+      if (STORE) wait_vmem_n<2>();
+      else wait_vmem();
+      __syncthreads();
+    };
+    for (int it = 0; it < x.n; it += 2) {
+      one_step(std::integral_constant<int, 1>{}, it);
+      if (it + 1 < x.n) one_step(std::integral_constant<int, 0>{}, it + 1);
+    }
+
+    // Prefetch the next tile (K, V tiles and ring slot 1 are free now).
+    const bool more = nxt < end;
+    Kv2Tile y = x;
+    if (more) {
+      y = kv2_tile_of<D>(p, p.tiles[nxt]);
+      kv2_issue_kv<D>(p, ln, y, smem, wave, lane);
+      kv2_issue_step<D>(p, ln, y, 0, 1, smem, wave, lane);
+    }
+    // The groups swap partials through ring slot 0, a quarter at a time: group 1 hands
+    // its dK partials to group 0 (parts 0, 1: head-dim blocks 0-1, 2-3) and group 0 its
+    // dV partials to group 1 (parts 2, 3); then group 0 stores dK and group 1 dV.
+    {
+      JFA_LDS char* red = smem;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int giver = r < 2 ? 1 : 0;
+        f32x16(&acc)[C::NDB] = r < 2 ? dk : dv;
+        if (g == giver) {
+#pragma unroll
+          for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x16& a = acc[2 * (r & 1) + dl];
+              lds_st16(red, ((kw * 2 + dl) * 4 + q4) * 1024 + lane * 16,
+                       __builtin_bit_cast(u32x4, float4{a[4 * q4], a[4 * q4 + 1], a[4 * q4 + 2], a[4 * q4 + 3]}));
+            }
+        }
+        __syncthreads();
+        if (g != giver) {
+#pragma unroll
+          for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              f32x16& a = acc[2 * (r & 1) + dl];
+              const float4 v4 = __builtin_bit_cast(float4, lds_ld16(red, ((kw * 2 + dl) * 4 + q4) * 1024 + lane * 16));
+              a[4 * q4] += v4.x;
+              a[4 * q4 + 1] += v4.y;
+              a[4 * q4 + 2] += v4.z;
+              a[4 * q4 + 3] += v4.w;
+            }
+        }
+        __syncthreads();
+      }
+    }
+    const int my_key = 32 * kw + l32;
+    // wave-uniform: the store block runs when the wave's first key exists (lane l32 = 0)
+    stores = 32 * kw < x.keys ? 4 * C::NDB : 0;
+    if (stores) {
+      if (my_key < x.keys) {
+        const int64_t row = (x.s0 + x.key0 + my_key) * rs + (int64_t)x.h * D + 4 * half;
+        uint16_t* dst = (g == 0 ? p.dk : p.dv) + row;
+        const f32x16(&a)[C::NDB] = g == 0 ? dk : dv;
+        const float sc = g == 0 ? p.scale : 1.0f;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            st8(dst + 32 * db + 8 * g4,
+                pack4(a[db][4 * g4] * sc, a[db][4 * g4 + 1] * sc, a[db][4 * g4 + 2] * sc, a[db][4 * g4 + 3] * sc));
+      }
+    }
+    if (!more) break;
+    idx = nxt;
+    x = y;
+  }
 }
 
 // --------------------------------------------------------- stored-dS path: row terms
