@@ -11,7 +11,12 @@ result must equal the dense forward bit for bit.
 
 The backward (jfa_bwd_block_sparse) is checked against the oracle's backward for the
 same (GPU) selection; at ratio 1 it walks every query and key step in the dense
-recompute backward's order and must equal jfa_bwd (no dS budget) bit for bit."""
+recompute backward's order.  Its dQ then equals jfa_bwd's (no dS budget) bit for bit,
+and so do dK, dV at head_dim 64, where both run the same one-wave-per-32-keys kernel.
+At head_dim 128 the dense dK/dV kernel splits every 64-row query step over two wave
+groups and adds the groups' fp32 partials at the tile end, while the block-sparse one
+(64-key tiles) sums all rows in one wave: the two sum the same products in another
+order and agree to within one bf16 rounding."""
 
 import numpy as np
 import pytest
@@ -156,13 +161,22 @@ def test_block_sparse_backward_dynamic_schedule_and_few_programs():
     _run(LENGTHS, 2, 64, 0.3, seed=53, opts=B.make_opts(num_programs=3), label="3 programs", bwd=True)
 
 
-def test_block_sparse_backward_ratio_one_equals_dense_backward_bit_exactly():
+def test_block_sparse_backward_ratio_one_equals_dense_backward():
     for d in (64, 128):
         p, g, o, lse, sel, grads = _run(LENGTHS, 2, d, 1.0, seed=54, label=f"ratio 1 D{d}", bwd=True)
         dense = G.gpu_bwd(g, o, lse)
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv"), grads, dense):
-            assert torch.equal(a, b), name
+            if name == "dq" or d == 64:
+                assert torch.equal(a, b), f"D{d} {name}"
+                continue
+            # same products summed in another order, each side rounded once to bf16:
+            # one bf16 step (2^-7 relative) apart, plus cancellation near zero
+            a64, b64 = G.f64(a), G.f64(b)
+            amax = float(np.abs(b64).max())
+            bound = 2.0 ** -7 * np.maximum(np.abs(a64), np.abs(b64)) + 2.0 ** -12 * amax
+            bad = np.abs(a64 - b64) > bound
+            assert not bad.any(), f"D{d} {name}: {int(bad.sum())} elements beyond one rounding step"
 
 
 def test_block_sparse_backward_long_sequences():

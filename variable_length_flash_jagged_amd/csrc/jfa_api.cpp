@@ -7,7 +7,6 @@
 // on the host before launch with no device synchronisation (bittide page, section 5).
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
-#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -1417,10 +1416,6 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   p.dynamic = op.sched;
   p.scale = scale;
   p.scale_log2 = scale * kLog2eHost;
-  {
-    const char* ev = getenv("JFA_DKDV_VARIANT");
-    p.dkdv_variant = ev ? atoi(ev) : 1;
-  }
 
   if (mode == JFA_MODE_SELF) {
     if (sc.tiles.empty()) return JFA_OK;

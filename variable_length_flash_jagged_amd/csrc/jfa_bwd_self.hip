@@ -1089,13 +1089,6 @@ __device__ __forceinline__ void kv2_issue_kv(const BwdParams& p, const Kv2Lane<D
   ln.kcopy.issue_rows(p.v + first, rsb, x.keys, smem + C::OFF_V, wave, lane);
 }
 
-// s_waitcnt vmcnt(N) for N < 64 (the counter's high bits sit at [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmem_upto() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // Persistent loop over the dK/dV tiles.  The next tile is reserved one tile ahead, so
 // that its K, V rows and first query step are copied while the current tile sums its
 // two groups' partials (which then use only ring slot 0; every tile starts its steps
@@ -1512,10 +1505,11 @@ hipError_t launch_bwd_self_dkdv(const BwdParams& p, int head_dim, hipStream_t s)
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<64, false, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<64, false, false>), grid, block, 0, s, p);
   } else {
-    if (p.ds && p.dkdv_variant == 1) hipLaunchKernelGGL((dkdv2_kernel<128, true>), grid, dim3(512), 0, s, p);
-    else if (p.ds) hipLaunchKernelGGL((dkdv_kernel<128, true, false>), grid, block, 0, s, p);
+    // self attention: two waves per SIMD (dkdv2_kernel); broadcast-Q keys and
+    // block-sparse 128-key tiles: one (dkdv_kernel)
+    if (p.ds) hipLaunchKernelGGL((dkdv2_kernel<128, true>), grid, dim3(Kv2Cfg<128>::NW * 64), 0, s, p);
     else if (p.sel) hipLaunchKernelGGL((dkdv_kernel<128, false, true>), grid, block, 0, s, p);
-    else if (p.dkdv_variant == 1 && !p.bq) hipLaunchKernelGGL((dkdv2_kernel<128, false>), grid, dim3(512), 0, s, p);
+    else if (!p.bq) hipLaunchKernelGGL((dkdv2_kernel<128, false>), grid, dim3(Kv2Cfg<128>::NW * 64), 0, s, p);
     else hipLaunchKernelGGL((dkdv_kernel<128, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();

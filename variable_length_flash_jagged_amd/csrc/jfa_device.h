@@ -107,6 +107,13 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// s_waitcnt vmcnt(N) for N < 64 (the counter's high bits sit at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier between the phases of a two-group (ping-pong) kernel.  The LDS
 // reads of a phase are consumed inside it; the lgkmcnt(0) makes sure none is still in
 // flight when another wave's copy reuses its ring slot.  Copies are ordered explicitly

@@ -78,7 +78,8 @@ struct FwdLane {
 template <int D>
 struct FwdWave {
   using C = FwdCfg<D>;
-  bf16x8 qf[C::NKS];     // Q rows (B operands)
+  bf16x8 (&qf)[C::NKS];  // Q rows (B operands), owned by the tile loop
+  __device__ __forceinline__ explicit FwdWave(bf16x8 (&q)[C::NKS]) : qf(q) {}
   f32x16 o[C::NDB];      // O^T accumulators
   f32x16 s[C::NKB];      // scores of the current key tile, then its probabilities
   bf16x8 pf[C::NT16];    // probabilities as B operands of the PV product
@@ -206,43 +207,113 @@ __device__ __forceinline__ void softmax_phase(FwdWave<D>& w, int keys_valid, int
   }
 }
 
+// Geometry of one forward tile (wave-uniform except `row`).
 template <int D, int MODE>
-__device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS char* smem, const FwdLane<D>& ln,
-                                         int tid) {
+struct FwdGeo {
   using C = FwdCfg<D>;
+  static constexpr bool SELF = MODE != kBroadcastQ;  // self attention (dense or block sparse)
+  int b, h, blk, kst, slot, L, Lq, row, n;
+  int64_t s0;
+  const int32_t* list;
+  const uint16_t *kp, *vp;
+  __device__ __forceinline__ void init(const FwdParams& p, Tile tile, int wave, int l32) {
+    h = tile.hb >> 24;
+    blk = tile.hb & 0xFFFFFF;
+    const int hkv = h / (p.num_heads / p.num_kv_heads);  // key/value head of query head h
+    // Broadcast-Q: the tile covers one key chunk (keys kst .. kst + L - 1 of sequence b);
+    // slot >= 0 marks a chunk of a cut sequence, whose partial O and lse go to the slot.
+    b = tile.b;
+    kst = 0;
+    slot = -1;
+    if constexpr (!SELF) {
+      const int ch = tile.b, nc = p.num_chunks;
+      b = p.chunks[ch];
+      kst = p.chunks[nc + ch];
+      slot = p.chunks[3 * nc + ch];
+    }
+    s0 = p.offsets[b];
+    L = SELF ? (int)(p.offsets[b + 1] - s0) : p.chunks[2 * p.num_chunks + tile.b];  // keys visited
+    Lq = SELF ? L : p.num_q;
+    row = blk * C::BM + wave * 32 + l32;
+    // Key tiles visited: all ceil(L/BN) of the sequence, or (block sparse) the tile's
+    // ascending list of kept key tiles.  Only a sequence's last key tile can be partial,
+    // and in an ascending list it comes last, so the masking rule is unchanged.
+    n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
+    list = nullptr;
+    if constexpr (MODE == kSelfSparse) {
+      n = L > 0 ? p.sel_k[b] : 0;
+      list = p.sel + p.sel_base[b] + ((int64_t)h * ((L + C::BM - 1) / C::BM) + blk) * n;
+    }
+    const int64_t rkv = (int64_t)p.num_kv_heads * D;
+    kp = p.k + (s0 + kst) * rkv + (int64_t)hkv * D;
+    vp = p.v + (s0 + kst) * rkv + (int64_t)hkv * D;
+  }
+  __device__ __forceinline__ int tile_of(int i) const { return MODE == kSelfSparse ? list[i] : i; }
+  __device__ __forceinline__ int rows_of(int j) const { return min(C::BN, L - j * C::BN); }
+  // Stage i (K(i), V(i-1)) into the ring slot at byte offset off.  Stage 0 has no V tile and stage n no K
+  // tile; those halves repeat a neighbouring tile instead, so every stage is the same
+  // number of copies and the counted waits stay exact.
+  __device__ __forceinline__ void issue(const FwdParams& p, const FwdLane<D>& ln, int i, int off, JFA_LDS char* smem,
+                                        int wave, int lane) const {
+    const int64_t rkv = (int64_t)p.num_kv_heads * D;
+    const uint32_t rkvb = (uint32_t)(rkv * 2);
+    JFA_LDS char* slot_p = smem + off;
+    const int kt = tile_of(min(i, n - 1)), vt = tile_of(max(i - 1, 0));
+    ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rkv, rkvb, rows_of(kt), slot_p, wave, lane);
+    ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rkv, rkvb, rows_of(vt), slot_p + C::TILE, wave, lane);
+  }
+  // This lane's Q row as B operands (rows past the tile's queries are zero).
+  __device__ __forceinline__ void load_q(const FwdParams& p, bf16x8 (&qf)[C::NKS], int half) const {
+    const int64_t qrow = SELF ? s0 + row : (int64_t)row;
+    const uint16_t* qp = p.q + qrow * ((int64_t)p.num_heads * D) + (int64_t)h * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = as_bf16x8(row < Lq ? ld16(qp + ks * 16) : zero16());
+  }
+};
+
+// Key steps (K/V tiles) of a forward tile: n of its geometry, without building it.
+template <int D, int MODE>
+__device__ __forceinline__ int key_steps(const FwdParams& p, Tile tile) {
+  if constexpr (MODE == kBroadcastQ) {
+    const int L = p.chunks[2 * p.num_chunks + tile.b];
+    return (L + kFwdKeys - 1) / kFwdKeys;
+  } else {
+    const int L = (int)(p.offsets[tile.b + 1] - p.offsets[tile.b]);
+    if constexpr (MODE == kSelfSparse) return L > 0 ? p.sel_k[tile.b] : 0;
+    return (L + kFwdKeys - 1) / kFwdKeys;
+  }
+}
+
+// Vector-memory instructions the epilogue of a tile issues in one wave (O row pieces
+// and the lse), when any of the wave's query rows exists.
+template <int D>
+constexpr int fwd_epilogue_stores() { return 4 * (D / 32) + 1; }
+
+// One forward tile.  Stage i of the tile lives in ring slot (sb + i) % NS.  qf holds
+// the tile's Q rows when pre (the previous tile loaded them and copied stages 0, 1).
+// has_next: the next tile nx (with keys) starts loading after this tile's last softmax
+// phase -- its Q rows into qf (dead after this tile's last S product) and its stages 0,
+// 1 into the two slots after this tile's last stage (their stages n - 2, n - 1 are no
+// longer read).  Returns the number of epilogue stores this wave issued.
+template <int D, int MODE>
+__device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_next, Tile nx, bool pre, int sb,
+                                        int prev_stores, bf16x8 (&qf)[FwdCfg<D>::NKS], JFA_LDS char* smem,
+                                        const FwdLane<D>& ln, int tid) {
+  using C = FwdCfg<D>;
+  constexpr bool SELF = FwdGeo<D, MODE>::SELF;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control flow
   const int g = wave >> 2;  // 0: group A, 1: group B (same SIMD as wave - 4)
-  const int l32 = lane & 31, half = lane >> 5;
-  const int h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
+  const int half = lane >> 5;
   const int H = p.num_heads;
   const int64_t rs = (int64_t)H * D;                   // q, o row stride
-  const int64_t rkv = (int64_t)p.num_kv_heads * D;     // k, v row stride
-  const uint32_t rkvb = (uint32_t)(rkv * 2);
-  const int hkv = h / (H / p.num_kv_heads);            // key/value head of query head h
-  constexpr bool SELF = MODE != kBroadcastQ;           // self attention (dense or block sparse)
-  // Broadcast-Q: the tile covers one key chunk (keys kst .. kst + L - 1 of sequence b);
-  // slot >= 0 marks a chunk of a cut sequence, whose partial O and lse go to the slot.
-  int b = tile.b, kst = 0, slot = -1;
-  if constexpr (!SELF) {
-    const int ch = tile.b, nc = p.num_chunks;
-    b = p.chunks[ch];
-    kst = p.chunks[nc + ch];
-    slot = p.chunks[3 * nc + ch];
-  }
-  const int64_t s0 = p.offsets[b];
-  const int L = SELF ? (int)(p.offsets[b + 1] - s0) : p.chunks[2 * p.num_chunks + tile.b];  // keys visited
-  const int Lq = SELF ? L : p.num_q;
-  const int row = blk * C::BM + wave * 32 + l32;
   const float c = p.scale_log2;
+  FwdGeo<D, MODE> t;
+  t.init(p, tile, wave, lane & 31);
+  const int n = t.n, row = t.row, Lq = t.Lq;
 
-  FwdWave<D> w;
-  {
-    const int64_t qrow = SELF ? s0 + row : (int64_t)row;
-    const uint16_t* qp = p.q + qrow * rs + (int64_t)h * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) w.qf[ks] = as_bf16x8(row < Lq ? ld16(qp + ks * 16) : zero16());
-  }
+  FwdWave<D> w(qf);
+  if (!pre) t.load_q(p, qf, half);
   w.m = -INFINITY;
   w.l = 0.f;
 #pragma unroll
@@ -250,32 +321,24 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
 #pragma unroll
     for (int i = 0; i < 16; ++i) w.o[db][i] = 0.f;
 
-  // Key tiles visited: all ceil(L/BN) of the sequence, or (block sparse) the tile's
-  // ascending list of kept key tiles.  Only a sequence's last key tile can be partial,
-  // and in an ascending list it comes last, so the masking rule below is unchanged.
-  int n = (L + C::BN - 1) / C::BN;  // key tiles; stages 0..n, phases 0..2n+1
-  const int32_t* list = nullptr;
-  if constexpr (MODE == kSelfSparse) {
-    n = L > 0 ? p.sel_k[b] : 0;
-    list = p.sel + p.sel_base[b] + ((int64_t)h * ((L + C::BM - 1) / C::BM) + blk) * n;
-  }
-  auto tile_of = [&](int i) { return MODE == kSelfSparse ? list[i] : i; };
   if (n > 0) {
-    const uint16_t* kp = p.k + (s0 + kst) * rkv + (int64_t)hkv * D;
-    const uint16_t* vp = p.v + (s0 + kst) * rkv + (int64_t)hkv * D;
-    auto rows_of = [&](int j) { return min(C::BN, L - j * C::BN); };
-    // Stage i into slot i % NS.  Stage 0 has no V tile and stage n no K tile; those
-    // halves repeat a neighbouring tile instead, so every stage is the same number of
-    // copies and the counted waits below stay exact.
-    auto issue = [&](int i) {
-      JFA_LDS char* slot = smem + (i % C::NS) * C::STAGE;
-      const int kt = tile_of(min(i, n - 1)), vt = tile_of(max(i - 1, 0));
-      ln.copy.issue_rows(kp + (int64_t)kt * C::BN * rkv, rkvb, rows_of(kt), slot, wave, lane);
-      ln.copy.issue_rows(vp + (int64_t)vt * C::BN * rkv, rkvb, rows_of(vt), slot + C::TILE, wave, lane);
-    };
-    issue(0);
-    wait_vmem();  // Q and stage 0
-    issue(1);
+    // Ring slots as byte offsets advanced one stage at a time (a scalar per use; a
+    // modulo of the stage number would be folded into every lane's LDS address).
+    constexpr int LAST = (C::NS - 1) * C::STAGE;
+    auto adv = [](int off) { return off == LAST ? 0 : off + C::STAGE; };
+    int mat_off = sb * C::STAGE;        // stage of the current matrix phase
+    int iss_off = adv(adv(mat_off));    // slot of the next stage to copy (stage 2 first)
+    auto issue = [&](int i, int off) { t.issue(p, ln, i, off, smem, wave, lane); };
+    if (pre) {
+      // Q and stage 0 landed (stage 1 and the previous tile's epilogue stores, issued
+      // after them, may not have)
+      if (prev_stores) wait_vmem_upto<C::DMA_PER_STAGE + fwd_epilogue_stores<D>()>();
+      else wait_vmem_n<C::DMA_PER_STAGE>();
+    } else {
+      issue(0, mat_off);
+      wait_vmem();  // Q and stage 0
+      issue(1, adv(mat_off));
+    }
     phase_barrier();
 
     // Phase ph (0 .. 2n+1): group A runs matrix phase i in phase 2i and vector phase i
@@ -283,49 +346,62 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
     // barriers: group B idles through phase 0, group A through phase 2n+1.
     int ph = 0;
     auto end_phase = [&]() {
-      if (ph & 1) {
-        // stage ph/2 + 1 is read from the next phase on; stage ph/2 + 2 may still be
-        // in flight
+      if ((ph & 1) && ph < 2 * n + 1) {
+        // stage ph/2 + 1 is read from the next phase on; stage ph/2 + 2 may still be in
+        // flight (after the last phase nothing of this tile is waited for: the next
+        // tile's loads stay in flight through the epilogue)
         if ((ph >> 1) + 2 <= n) wait_vmem_n<C::DMA_PER_STAGE>();
         else wait_vmem();
       }
       phase_barrier();
       ++ph;
-      if (!(ph & 1) && (ph >> 1) + 2 <= n) issue((ph >> 1) + 2);
+      if (!(ph & 1) && (ph >> 1) + 2 <= n) {
+        issue((ph >> 1) + 2, iss_off);
+        iss_off = adv(iss_off);
+      }
     };
-    if (2 <= n) issue(2);
+    if (2 <= n) {
+      issue(2, iss_off);
+      iss_off = adv(iss_off);
+    }
     if (g) end_phase();
     // matrix phase 0: S(0) only.  Matrix phases run at raised wave priority: when both
     // waves of a SIMD have an instruction ready, the one feeding the matrix core goes
     // first (measured: 1.7 % faster than equal priorities; raising the vector phase
     // instead changes nothing).
     __builtin_amdgcn_s_setprio(2);
-    mma_s<D>(smem, ln, w);
+    mma_s<D>(smem + mat_off, ln, w);
     pin_matrix_phase<D>(w);
     __builtin_amdgcn_s_setprio(0);
     end_phase();
-    int slot_off = 0;  // ring offset of stage i - 1
     for (int i = 1; i < n; ++i) {
       softmax_phase<D>(w, C::BN, half, c);  // tiles before the last are full
       pin_vector_phase<D>(w);
       end_phase();
-      slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
-      const JFA_LDS char* slot = smem + slot_off;
+      mat_off = adv(mat_off);
+      const JFA_LDS char* slot_p = smem + mat_off;
       __builtin_amdgcn_s_setprio(2);
-      mma_pv<D>(slot + C::TILE, ln, w);
-      mma_s<D>(slot, ln, w);
+      mma_pv<D>(slot_p + C::TILE, ln, w);
+      mma_s<D>(slot_p, ln, w);
       order_matrix_phase<D>();
       pin_matrix_phase<D>(w);
       __builtin_amdgcn_s_setprio(0);
       end_phase();
     }
-    softmax_phase<D>(w, rows_of(tile_of(n - 1)), half, c);
+    softmax_phase<D>(w, t.rows_of(t.tile_of(n - 1)), half, c);
     pin_vector_phase<D>(w);
     end_phase();
+    if (has_next) {
+      FwdGeo<D, MODE> t2;
+      t2.init(p, nx, wave, lane & 31);
+      t2.load_q(p, qf, half);
+      // every stage 2 .. n has been issued: iss_off is the slot of stage n + 1
+      t2.issue(p, ln, 0, iss_off, smem, wave, lane);
+      t2.issue(p, ln, 1, adv(iss_off), smem, wave, lane);
+    }
     // matrix phase n: O += V(n-1) P(n-1) only
-    slot_off = slot_off == (C::NS - 1) * C::STAGE ? 0 : slot_off + C::STAGE;
     __builtin_amdgcn_s_setprio(2);
-    mma_pv<D>(smem + slot_off + C::TILE, ln, w);
+    mma_pv<D>(smem + adv(mat_off) + C::TILE, ln, w);
     pin_matrix_phase<D>(w);
     __builtin_amdgcn_s_setprio(0);
     end_phase();
@@ -333,12 +409,14 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
   }
 
   // Epilogue: O / l in bf16, lse = ln 2 * (m*c + log2 l); empty rows give 0 and -inf.
+  // (wave-uniform store count: the stores run when the wave's first row exists)
+  const int stores = (row - (lane & 31)) < Lq ? fwd_epilogue_stores<D>() : 0;
   const float lt = half_sum(w.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
-  if (!SELF && slot >= 0 && row < Lq) {
+  if (!SELF && t.slot >= 0 && row < Lq) {
     // chunk of a cut sequence: fp32 O / l and lse of this chunk, merged afterwards
-    float* po = p.part_o + (((int64_t)slot * p.num_q + row) * H + h) * D + 4 * half;
+    float* po = p.part_o + (((int64_t)t.slot * p.num_q + row) * H + t.h) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -347,10 +425,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
         *reinterpret_cast<float4*>(po + 32 * db + 8 * g4) =
             make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
       }
-    if (half == 0) p.part_lse[((int64_t)slot * H + h) * p.num_q + row] = lse;
+    if (half == 0) p.part_lse[((int64_t)t.slot * H + t.h) * p.num_q + row] = lse;
   } else if (row < Lq) {
-    const int64_t orow = SELF ? s0 + row : (int64_t)b * p.num_q + row;
-    uint16_t* op = p.o + orow * rs + (int64_t)h * D + 4 * half;
+    const int64_t orow = SELF ? t.s0 + row : (int64_t)t.b * p.num_q + row;
+    uint16_t* op = p.o + orow * rs + (int64_t)t.h * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -360,10 +438,11 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, Tile tile, JFA_LDS 
             pack4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv));
       }
     if (half == 0) {
-      const int64_t li = SELF ? (int64_t)h * p.total_tokens + s0 + row : ((int64_t)b * H + h) * p.num_q + row;
+      const int64_t li = SELF ? (int64_t)t.h * p.total_tokens + t.s0 + row : ((int64_t)t.b * H + t.h) * p.num_q + row;
       p.lse[li] = lse;
     }
   }
+  return stores;
 }
 
 template <int D, int MODE>
@@ -390,17 +469,34 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     end = p.seg_ptr[grp + 1];
     idx = base + prog % gsize;
   }
-  while (idx < end) {
-    if (tid == 0) count_visit(p.visits, idx);
-    fwd_tile<D, MODE>(p, p.tiles[idx], smem, ln, tid);
-    if (!p.dynamic) {
-      ++idx;
-    } else {
+  if (idx >= end) return;
+  // The next tile is reserved one tile ahead, so that its Q rows and first two stages
+  // load during the current tile's last phases.
+  bf16x8 qf[C::NKS];
+  bool pre = false;
+  int sb = 0, stores = 0;
+  Tile cur = p.tiles[idx];
+  int cur_n = key_steps<D, MODE>(p, cur);
+  while (true) {
+    int nxt = idx + 1;
+    if (p.dynamic) {
       if (tid == 0) next_tile = base + gsize + atomicAdd(p.counters + grp, 1);
       __syncthreads();
-      idx = next_tile;
-      __syncthreads();
+      nxt = next_tile;
     }
+    if (tid == 0) count_visit(p.visits, idx);
+    const bool more = nxt < end;
+    const Tile nt = more ? p.tiles[nxt] : cur;
+    const int nt_n = more ? key_steps<D, MODE>(p, nt) : 0;
+    const bool ahead = more && cur_n > 0 && nt_n > 0;
+    stores = fwd_tile<D, MODE>(p, cur, ahead, nt, pre, sb, stores, qf, smem, ln, tid);
+    if (!more) break;
+    if (cur_n > 0) sb = (sb + cur_n + 1) % C::NS;
+    pre = ahead;
+    idx = nxt;
+    cur = nt;
+    cur_n = nt_n;
+    if (p.dynamic) __syncthreads();  // every wave has read next_tile before it is rewritten
   }
 }
 

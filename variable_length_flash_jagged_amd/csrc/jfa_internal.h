@@ -197,7 +197,6 @@ struct BwdParams {
   int32_t programs_per_head;  // broadcast-Q head-pinned groups
   float scale;
   float scale_log2;
-  int32_t dkdv_variant;  // self attention, head_dim 128: 0 one wave per SIMD (dkdv_kernel), 1 two (dkdv2_kernel)
   int32_t* visits;     // debug (null: off): visit counts of the dK/dV (or fused) kernel's tiles
   int32_t* dq_visits;  // debug (null: off): visit counts of the dQ kernel's tiles
 };
