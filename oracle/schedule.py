@@ -52,6 +52,14 @@ Readings where the pages leave the rule open:
   ceil(L_b / key_step) / P).  Chunks are listed in sequence order; an empty sequence
   keeps one chunk of zero keys.  When no sequence is longer than one chunk the
   schedule is exactly the unchunked one.
+* Self-attention forward key chunks: the same imbalance arises in self attention when
+  a batch holds a few long sequences (their tiles are few and each walks all the
+  sequence's keys), so the same rule applies with each sequence's own query tiles:
+  share = ceil(H * sum_b ceil(L_b / rows) * ceil(L_b / key_step) / P), and a chunk of
+  at least 8 key steps (each cut costs a merge pass that a shorter chunk does not
+  repay; the pages give no number, this one is ours).  Empty sequences have no chunk.  When some sequence is cut, tiles are (chunk, h, blk) with
+  blk < ceil(L_b / rows) for the chunk's sequence b, sorted by the chunk's keys;
+  otherwise the schedule is exactly the unchunked one.
 
 Every function returns plain Python lists so that a reader can compare them by eye.
 """
@@ -129,6 +137,21 @@ def bq_key_chunks(lengths, num_heads, num_q, rows, num_programs, key_step=64, mi
     return chunks
 
 
+def self_key_chunks(lengths, num_heads, rows, num_programs, key_step=64, min_steps=8):
+    """Key chunks of the self-attention forward tiles: a list of (b, first_key, keys)
+    in sequence order, empty sequences skipped (see the module docstring)."""
+    steps = sum(_cdiv(int(n), rows) * _cdiv(int(n), key_step) for n in lengths)
+    share = _cdiv(num_heads * steps, max(1, num_programs))
+    keys = key_step * max(min_steps, share)
+    return [(b, k0, min(keys, int(n) - k0)) for b, n in enumerate(lengths) for k0 in range(0, int(n), keys)]
+
+
+def self_chunks_cut(lengths, num_heads, rows, num_programs):
+    """True when the self-attention forward cuts some sequence into key chunks."""
+    chunks = self_key_chunks(lengths, num_heads, rows, num_programs)
+    return len(chunks) != sum(1 for n in lengths if int(n) > 0)
+
+
 def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=False):
     """Forward schedule for MODE_SELF / MODE_BROADCAST_Q.
 
@@ -136,8 +159,12 @@ def fwd_schedule(lengths, num_heads, mode, num_q, rows, num_programs, dynamic=Fa
     one segment per program.  Dynamic: one segment per counter group (counter_groups),
     each holding in sorted order the tiles the static deal gives its programs.  In
     broadcast-Q mode a tile's first entry is the index of its key chunk in
-    bq_key_chunks(...) (the sequence index when no sequence is cut)."""
-    if mode == MODE_SELF:
+    bq_key_chunks(...) (the sequence index when no sequence is cut); in self mode it
+    is the index in self_key_chunks(...) when some sequence is cut."""
+    if mode == MODE_SELF and self_chunks_cut(lengths, num_heads, rows, num_programs):
+        chunks = self_key_chunks(lengths, num_heads, rows, num_programs)
+        order = sorted_cost_tiles([c[2] for c in chunks], num_heads, rows, lambda c: int(lengths[chunks[c][0]]))
+    elif mode == MODE_SELF:
         order = sorted_cost_tiles(lengths, num_heads, rows, lambda b: int(lengths[b]))
     elif mode == MODE_BROADCAST_Q:
         keys = [c[2] for c in bq_key_chunks(lengths, num_heads, num_q, rows, num_programs)]

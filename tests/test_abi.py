@@ -125,7 +125,8 @@ def test_block_sparse_argument_errors():
     with pytest.raises(B.JfaError) as e:
         B.workspace_size(shape, 2, B.PASS_FWD_SPARSE)  # self mode only
     assert e.value.code == -4
-    assert B.workspace_size(shape, 0, B.PASS_FWD_SPARSE) > B.workspace_size(shape, 0, B.PASS_FWD)
+    # the sparse forward's workspace holds at least the block means of q and k
+    assert B.workspace_size(shape, 0, B.PASS_FWD_SPARSE) >= 2 * (300 // 64 + 2) * 2 * 64 * 4
 
 
 def test_bad_options_and_pass():
@@ -351,6 +352,27 @@ def test_broadcast_q_forward_key_chunks_match_spec(sched):
     want = spec.fwd_schedule(lengths, 4, 1, 256, rows, 256, dynamic=bool(sched))
     got_t, got_s = _to_lists(tiles, seg)
     assert got_t == [tuple(t) for t in want[0]] and got_s == list(want[1]) and progs == want[2]
+
+
+@pytest.mark.parametrize("sched", [0, 1])
+@pytest.mark.parametrize("heads", [1, 3])
+def test_self_forward_key_chunks_match_spec(sched, heads):
+    # few long sequences and many programs: the self-attention forward cuts keys
+    lengths = [128, 4096, 512, 2048, 0]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), heads, 64, int(off[-1]))
+    tiles, seg, progs, rows = B.schedule(shape, 0, 0, off, B.make_opts(sched=sched, num_programs=256))
+    assert spec.self_chunks_cut(lengths, heads, rows, 256)
+    want = spec.fwd_schedule(lengths, heads, 0, 0, rows, 256, dynamic=bool(sched))
+    got_t, got_s = _to_lists(tiles, seg)
+    assert got_t == [tuple(t) for t in want[0]] and got_s == list(want[1]) and progs == want[2]
+
+
+def test_self_forward_workspace_holds_key_chunk_partials():
+    # 2 * 256 rows * P row-heads of fp32 partial O (D floats) and lse
+    s = B.make_shape(4, 1, 64, 6784)
+    ws = B.workspace_size(s, 0, 0, B.make_opts(num_programs=256))
+    assert ws >= 2 * 256 * 256 * (64 + 1) * 4
 
 
 @no_gpu_only

@@ -207,3 +207,83 @@ def test_bq_cut_sequence_chunks_within_workspace_bound(seed):
         slots = sum(k for k in per_seq.values() if k > 1)
         bound = min(2 * p // (h * _cdiv(mq, 256)), 2 * sum(lengths) // 256) + 1
         assert slots <= bound
+
+
+def test_self_key_chunks_hand_example():
+    # one head, 256-row query tiles, 256 programs: key steps 16*64 + 1*2 + 8*32 = 1282,
+    # share = ceil(1282 / 256) = 6 steps < 8, so chunks are 512 keys
+    lengths = [4096, 128, 0, 2048]
+    ch = S.self_key_chunks(lengths, 1, 256, 256)
+    assert ch == [(0, k, 512) for k in range(0, 4096, 512)] + [(1, 0, 128)] + [(3, k, 512) for k in range(0, 2048, 512)]
+    assert S.self_chunks_cut(lengths, 1, 256, 256)
+    assert not S.self_chunks_cut([300, 65, 1], 2, 256, 256)  # 300 keys: under one 512-key chunk
+    tiles, ptr, p = S.fwd_schedule(lengths, 1, S.MODE_SELF, 0, 256, 256)
+    # tiles (chunk, 0, blk): 8 chunks x 16 blocks + 1 + 4 chunks x 8 blocks
+    assert len(tiles) == 8 * 16 + 1 + 4 * 8 and p == 161
+    assert all(blk < -(-lengths[ch[c][0]] // 256) for c, _, blk in tiles)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_self_key_chunks_cover_every_key_and_query_once(seed):
+    rng = np.random.default_rng(900 + seed)
+    lengths = (rng.integers(0, 5000, size=12) * (rng.random(12) < 0.8)).tolist()
+    h, rows, nprog = int(rng.integers(1, 5)), 256, int(rng.integers(16, 600))
+    ch = S.self_key_chunks(lengths, h, rows, nprog)
+    steps = sum(_cdiv(n, rows) * _cdiv(n, 64) for n in lengths)
+    keys = 64 * max(8, _cdiv(h * steps, nprog))
+    assert [c[0] for c in ch] == sorted(c[0] for c in ch)
+    for b, n in enumerate(lengths):
+        mine = [c for c in ch if c[0] == b]
+        assert [c[1] for c in mine] == list(range(0, n, keys))
+        assert sum(c[2] for c in mine) == n and all(0 < c[2] <= keys for c in mine)
+    tiles, _, _ = S.fwd_schedule(lengths, h, S.MODE_SELF, 0, rows, nprog)
+    if S.self_chunks_cut(lengths, h, rows, nprog):
+        # every (chunk, head, query block of the chunk's sequence) once, so each (query
+        # row, key) pair of every sequence is covered exactly once
+        assert sorted(tiles) == sorted((c, hh, i) for c in range(len(ch)) for hh in range(h)
+                                       for i in range(_cdiv(lengths[ch[c][0]], rows)))
+    else:
+        assert sorted(tiles) == sorted((b, hh, i) for b, n in enumerate(lengths) for hh in range(h)
+                                       for i in range(_cdiv(n, rows)))
+
+
+def test_self_schedule_unchunked_for_a_large_batch():
+    # many sequences: the fair share exceeds every sequence's key steps
+    rng = np.random.default_rng(5)
+    lengths = np.clip(np.rint(np.exp(rng.normal(np.log(600.0), 1.0, size=1152))), 1, 4000).astype(int).tolist()
+    assert not S.self_chunks_cut(lengths, 4, 256, 256)
+    assert S.fwd_schedule(lengths, 4, S.MODE_SELF, 0, 256, 256)[0] == _deal_plain(lengths, 4, 256, 256)
+
+
+def _deal_plain(lengths, h, rows, nprog):
+    order = S.sorted_cost_tiles(lengths, h, rows, lambda b: int(lengths[b]))
+    per = [[] for _ in range(min(nprog, len(order)))]
+    for n, t in enumerate(order):
+        per[S.zigzag_program(n, len(per))].append(t)
+    return [t for lst in per for t in lst]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_self_cut_chunks_within_workspace_bound(seed):
+    # The library holds the partial rows of cut sequences in 2 * rows * P row-heads, the
+    # chunks in B + 2 T / 256 + 1 entries and their tiles in H (T / rows + B + 1) + 2 P +
+    # H (B + 2 T / 256 + 1).
+    rng = np.random.default_rng(600 + seed)
+    rows = 256
+    for _ in range(60):
+        n = int(rng.integers(1, 40))
+        lengths = (rng.integers(0, 3000, size=n) * (rng.random(n) < 0.9)).tolist()
+        if rng.random() < 0.5:
+            lengths[int(rng.integers(0, n))] = int(rng.integers(5000, 40000))
+        h, p = int(rng.integers(1, 9)), int(rng.integers(1, 600))
+        ch = S.self_key_chunks(lengths, h, rows, p)
+        per_seq = {}
+        for c in ch:
+            per_seq[c[0]] = per_seq.get(c[0], 0) + 1
+        part = sum(k * lengths[b] for b, k in per_seq.items() if k > 1) * h
+        assert part < 2 * rows * p
+        t = sum(lengths)
+        chunk_cap = n + 2 * t // 256 + 1
+        assert len(ch) <= chunk_cap
+        tiles, _, _ = S.fwd_schedule(lengths, h, S.MODE_SELF, 0, rows, p)
+        assert len(tiles) <= h * (t // rows + n + 1) + 2 * p + h * chunk_cap

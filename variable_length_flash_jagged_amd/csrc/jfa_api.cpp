@@ -133,6 +133,9 @@ struct Layout {
   // forward: partial-result slots of cut sequences (O [S,Mq,H,D], lse [S,H,Mq], fp32)
   size_t chunks = 0, part_o = 0, part_lse = 0;
   int64_t chunk_cap = 0, fwd_slot_cap = 0;
+  // self-attention forward key chunks: partial rows x heads the buffers hold (0: the
+  // layout has no room for them and the forward never cuts)
+  int64_t self_part_cap = 0;
   int programs_cap = 0, programs2_cap = 0;
 };
 
@@ -174,6 +177,79 @@ void bq_key_chunks(const std::vector<int32_t>& lengths, int64_t H, int64_t Mq, i
   }
 }
 
+// Self-attention key chunks (forward): the broadcast-Q rule with each sequence's own
+// query tiles, share = ceil(H * sum_b ceil(L_b / rows) * ceil(L_b / kKeyStep) /
+// programs), and chunks of at least kSelfChunkMinSteps steps (a cut costs a merge
+// launch, which a shorter chunk does not repay).  Only a batch of few long sequences is
+// cut (a cut needs L_b > keys, and keys >= H sum_b L_b^2 / (rows P)); empty sequences
+// have no chunk.
+constexpr int kSelfChunkMinSteps = 8;
+void self_key_chunks(const std::vector<int32_t>& lengths, int64_t H, int rows, int programs, KeyChunks& out) {
+  int64_t steps = 0;
+  for (int32_t len : lengths) steps += cdiv(len, rows) * cdiv(len, kKeyStep);
+  const int64_t share = cdiv(H * steps, std::max(1, programs));
+  out.keys = kKeyStep * std::max<int64_t>(kSelfChunkMinSteps, share);
+  out.b.clear();
+  out.k0.clear();
+  out.len.clear();
+  for (int b = 0; b < (int)lengths.size(); ++b)
+    for (int64_t k0 = 0; k0 < lengths[b]; k0 += out.keys) {
+      out.b.push_back(b);
+      out.k0.push_back((int32_t)k0);
+      out.len.push_back((int32_t)std::min<int64_t>(out.keys, lengths[b] - k0));
+    }
+}
+
+// Partial rows x heads of cut self-attention sequences: a cut sequence has L_b > keys,
+// so its n_b = ceil(L_b / keys) < 2 L_b / keys chunks of L_b rows each, and with keys >=
+// H sum L^2 / (rows P) the sum over cut sequences of n_b L_b H stays below 2 rows P.
+int64_t self_part_cap(int programs) { return 2 * (int64_t)kFwdRows * programs; }
+
+// Self-attention forward key chunks of one call: when some sequence is cut, the chunk
+// table [b | first key | keys | first part row (-1: uncut)] of nc chunks, then the cut
+// table [b | first part row | chunks | row prefix (ncut + 1)] of launch_self_combine,
+// and the schedule of (chunk, h, blk) tiles.  Returns false (and touches nothing) when
+// no sequence is cut: the plain schedule applies.
+struct SelfSplit {
+  std::vector<int32_t> table;
+  int nc = 0, ncut = 0;
+  int64_t cut_rows = 0;   // query rows of the cut sequences (the merge's rows)
+  int64_t part_rows = 0;  // partial rows (per head) the chunks write
+};
+
+bool self_split_plan(const std::vector<int32_t>& lengths, int H, int P, bool dynamic, Schedule& sc, SelfSplit& out) {
+  KeyChunks kc;
+  self_key_chunks(lengths, H, kFwdRows, P, kc);
+  const int nc = (int)kc.b.size();
+  if (nc == 0 || nc == (int)std::count_if(lengths.begin(), lengths.end(), [](int32_t l) { return l > 0; }))
+    return false;
+  std::vector<int32_t> r0(nc, -1), cb, cf, cn, pre{0};
+  int64_t part = 0;
+  for (int c = 0; c < nc;) {
+    int e = c + 1;
+    while (e < nc && kc.b[e] == kc.b[c]) ++e;
+    if (e - c > 1) {
+      const int64_t len = lengths[kc.b[c]];
+      cb.push_back(kc.b[c]);
+      cf.push_back((int32_t)part);
+      cn.push_back(e - c);
+      pre.push_back(pre.back() + (int32_t)len);
+      for (int i = c; i < e; ++i, part += len) r0[i] = (int32_t)part;
+    }
+    c = e;
+  }
+  out.nc = nc;
+  out.ncut = (int)cb.size();
+  out.cut_rows = pre.back();
+  out.part_rows = part;
+  out.table = kc.b;
+  for (const auto* v : {&kc.k0, &kc.len, &r0, &cb, &cf, &cn, &pre}) out.table.insert(out.table.end(), v->begin(), v->end());
+  std::vector<int32_t> rows_of(nc);
+  for (int c = 0; c < nc; ++c) rows_of[c] = lengths[kc.b[c]];
+  schedule_fwd_chunks(kc.len, rows_of, H, kFwdRows, P, dynamic, sc);
+  return true;
+}
+
 // Split backward: the most key chunks any lengths give.  A sequence that is not cut is
 // one chunk; the chunks of cut sequences number fewer than 2 T / keys, with keys at
 // least kBqChunkMinSteps * kKeyStep and at least H * ceil(Mq / kDqRows) * T / programs.
@@ -190,7 +266,9 @@ int64_t bq_fwd_slot_cap(int64_t H, int64_t Mq, int64_t T, int programs) {
                            2 * T / (kBqChunkMinSteps * kKeyStep)) + 1;
 }
 
-void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L) {
+// key_split: room for the self-attention forward's key chunks (jfa_fwd_noalloc, whose
+// scratch array is small, runs without).
+void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L, bool key_split = true) {
   const int64_t B = s->num_seqs, H = s->num_heads, D = s->head_dim, T = s->total_tokens;
   const int64_t Mq = s->num_q;
   size_t at = 0;
@@ -219,6 +297,13 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
       L.tile_cap = H * L.chunk_cap * cdiv(Mq, kFwdRows);
     } else {
       L.tile_cap = H * (T / kFwdRows + B + 1);
+      if (pass == JFA_PASS_FWD && mode == JFA_MODE_SELF && key_split) {
+        // chunks: every sequence plus fewer than 2 T / 256 extra; tiles of cut sequences:
+        // n_b ceil(L_b / rows) H < (n_b L_b H) / rows + n_b H, summed < 2 P + H extra
+        L.self_part_cap = self_part_cap(L.programs_cap);
+        L.chunk_cap = B + 2 * T / (kBqChunkMinSteps * kKeyStep) + 1;
+        L.tile_cap += 2 * (int64_t)L.programs_cap + H * L.chunk_cap;
+      }
     }
   } else {
     L.tile_cap = H * (T / kBwdKeys + B + 1);
@@ -236,6 +321,14 @@ void layout_for(const jfa_shape* s, int mode, int pass, const Opts& o, Layout& L
     at += align_up((T / kMxVPad + B + 1) * sizeof(int32_t));
     L.total = at;
     return;
+  }
+  if (L.self_part_cap > 0) {
+    L.chunks = at;  // [sequence | first key | keys | first part row] per chunk, then the cut table
+    at += align_up((4 * L.chunk_cap + 4 * B + 1) * sizeof(int32_t));
+    L.part_o = at;
+    at += align_up((size_t)(L.self_part_cap * D) * sizeof(float));
+    L.part_lse = at;
+    at += align_up((size_t)L.self_part_cap * sizeof(float));
   }
   if (pass == JFA_PASS_FWD && mode == JFA_MODE_BROADCAST_Q) {
     L.chunks = at;  // [sequence | first key | keys | slot] per chunk, then (b, first slot, slots) per cut sequence
@@ -1127,8 +1220,12 @@ int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offs
     KeyChunks kc;
     bq_key_chunks(lengths, shape->num_heads, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), true, kc);
     schedule_fwd(kc.len, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
-  } else if (pass == JFA_PASS_FWD)
-    schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, max_programs(o, kFwdWgPerCu), dyn, sc);
+  } else if (pass == JFA_PASS_FWD) {
+    SelfSplit split;
+    const int P = max_programs(o, kFwdWgPerCu);
+    if (!(mode == JFA_MODE_SELF && self_split_plan(lengths, shape->num_heads, P, dyn, sc, split)))
+      schedule_fwd(lengths, shape->num_heads, mode, shape->num_q, kFwdRows, P, dyn, sc);
+  }
   else
     schedule_bwd(lengths, shape->num_heads, mode, kBwdKeys,
                  max_programs(o, bwd_wg_per_cu(mode, o.dq_path, shape->head_dim)), dyn, sc);
@@ -1169,7 +1266,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   Opts op;
   if ((rc = check_opts(opts, op))) return rc;
   Layout L;
-  layout_for(shape, mode, JFA_PASS_FWD, op, L);
+  layout_for(shape, mode, JFA_PASS_FWD, op, L, /*key_split=*/!noalloc);
   if (noalloc && L.total > kNoAllocScratchBytes)
     return fail(JFA_ERR_TOO_LARGE, "jfa_fwd_noalloc: this shape needs %zu bytes of scratch, more than its %zu",
                 L.total, kNoAllocScratchBytes);
@@ -1227,9 +1324,20 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
 
   Schedule sc;
   const int P = max_programs(op, kFwdWgPerCu);
-  std::vector<int32_t> table;  // broadcast-Q: key chunks and cut sequences
+  std::vector<int32_t> table;  // key chunks and cut sequences
   int nc = 0, ncut = 0;
-  if (mode == JFA_MODE_BROADCAST_Q) {
+  int kmode = mode;           // kernel mode (kSelfChunks when self-attention keys are cut)
+  int64_t merge_rows = 0;     // self-attention: query rows of the cut sequences
+  SelfSplit split;
+  if (mode == JFA_MODE_SELF && L.self_part_cap > 0 && self_split_plan(lengths, H, P, op.sched == 1, sc, split)) {
+    if (split.nc > L.chunk_cap || split.part_rows * H > L.self_part_cap)
+      return fail(JFA_ERR_WORKSPACE, "internal: key chunk capacity");
+    kmode = kSelfChunks;
+    nc = split.nc;
+    ncut = split.ncut;
+    merge_rows = split.cut_rows;
+    table.swap(split.table);
+  } else if (mode == JFA_MODE_BROADCAST_Q) {
     KeyChunks kc;
     bq_key_chunks(lengths, H, shape->num_q, kFwdRows, P, true, kc);
     nc = (int)kc.b.size();
@@ -1265,7 +1373,7 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   if ((rc = put(buf.data(), buf.size(), ws))) return rc;
   FwdParams p{};
   p.visits = visits;
-  if (mode == JFA_MODE_BROADCAST_Q) {
+  if (!table.empty()) {
     p.chunks = (const int32_t*)(ws + L.chunks);
     p.num_chunks = nc;
     p.part_o = (float*)(ws + L.part_o);
@@ -1288,10 +1396,12 @@ static int fwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
   p.total_tokens = shape->total_tokens;
   p.dynamic = op.sched;
   p.scale_log2 = scale * kLog2eHost;
-  if ((rc = launch_status(launch(JFA_KERNEL_FWD, [&] { return launch_fwd(p, mode, D, stream); }),
+  if ((rc = launch_status(launch(JFA_KERNEL_FWD, [&] { return launch_fwd(p, kmode, D, stream); }),
                           "forward launch")))
     return rc;
   if (ncut == 0) return JFA_OK;
+  if (kmode == kSelfChunks)
+    return launch_status(launch_self_combine(p, ncut, merge_rows, D, stream), "forward chunk merge");
   return launch_status(launch_bq_combine(p, ncut, D, stream), "forward chunk merge");
 }
 

@@ -211,7 +211,8 @@ __device__ __forceinline__ void softmax_phase(FwdWave<D>& w, int keys_valid, int
 template <int D, int MODE>
 struct FwdGeo {
   using C = FwdCfg<D>;
-  static constexpr bool SELF = MODE != kBroadcastQ;  // self attention (dense or block sparse)
+  static constexpr bool SELF = MODE != kBroadcastQ;  // queries are the sequence's own rows
+  static constexpr bool CHUNKED = MODE == kBroadcastQ || MODE == kSelfChunks;  // tiles of key chunks
   int b, h, blk, kst, slot, L, Lq, row, n;
   int64_t s0;
   const int32_t* list;
@@ -220,20 +221,22 @@ struct FwdGeo {
     h = tile.hb >> 24;
     blk = tile.hb & 0xFFFFFF;
     const int hkv = h / (p.num_heads / p.num_kv_heads);  // key/value head of query head h
-    // Broadcast-Q: the tile covers one key chunk (keys kst .. kst + L - 1 of sequence b);
-    // slot >= 0 marks a chunk of a cut sequence, whose partial O and lse go to the slot.
+    // Key chunks (broadcast-Q, and self attention of few long sequences): the tile covers
+    // keys kst .. kst + L - 1 of sequence b; slot >= 0 marks a chunk of a cut sequence,
+    // whose partial O and lse go to the partial buffers.
     b = tile.b;
     kst = 0;
     slot = -1;
-    if constexpr (!SELF) {
+    if constexpr (CHUNKED) {
       const int ch = tile.b, nc = p.num_chunks;
       b = p.chunks[ch];
       kst = p.chunks[nc + ch];
       slot = p.chunks[3 * nc + ch];
     }
     s0 = p.offsets[b];
-    L = SELF ? (int)(p.offsets[b + 1] - s0) : p.chunks[2 * p.num_chunks + tile.b];  // keys visited
-    Lq = SELF ? L : p.num_q;
+    const int Lseq = (int)(p.offsets[b + 1] - s0);
+    L = CHUNKED ? p.chunks[2 * p.num_chunks + tile.b] : Lseq;  // keys visited
+    Lq = SELF ? Lseq : p.num_q;
     row = blk * C::BM + wave * 32 + l32;
     // Key tiles visited: all ceil(L/BN) of the sequence, or (block sparse) the tile's
     // ascending list of kept key tiles.  Only a sequence's last key tile can be partial,
@@ -274,7 +277,7 @@ struct FwdGeo {
 // Key steps (K/V tiles) of a forward tile: n of its geometry, without building it.
 template <int D, int MODE>
 __device__ __forceinline__ int key_steps(const FwdParams& p, Tile tile) {
-  if constexpr (MODE == kBroadcastQ) {
+  if constexpr (MODE == kBroadcastQ || MODE == kSelfChunks) {
     const int L = p.chunks[2 * p.num_chunks + tile.b];
     return (L + kFwdKeys - 1) / kFwdKeys;
   } else {
@@ -414,9 +417,12 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
   const float lt = half_sum(w.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
-  if (!SELF && t.slot >= 0 && row < Lq) {
+  constexpr bool CHUNKED = FwdGeo<D, MODE>::CHUNKED;
+  if (CHUNKED && t.slot >= 0 && row < Lq) {
     // chunk of a cut sequence: fp32 O / l and lse of this chunk, merged afterwards
-    float* po = p.part_o + (((int64_t)t.slot * p.num_q + row) * H + t.h) * D + 4 * half;
+    // (broadcast-Q: slot s of [S, Mq, H] rows; self: part row t.slot + row of [R, H])
+    const int64_t prow = SELF ? (int64_t)t.slot + row : (int64_t)t.slot * p.num_q + row;
+    float* po = p.part_o + (prow * H + t.h) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -425,7 +431,10 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
         *reinterpret_cast<float4*>(po + 32 * db + 8 * g4) =
             make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
       }
-    if (half == 0) p.part_lse[((int64_t)t.slot * H + t.h) * p.num_q + row] = lse;
+    if (half == 0) {
+      if constexpr (SELF) p.part_lse[prow * H + t.h] = lse;
+      else p.part_lse[((int64_t)t.slot * H + t.h) * p.num_q + row] = lse;
+    }
   } else if (row < Lq) {
     const int64_t orow = SELF ? t.s0 + row : (int64_t)t.b * p.num_q + row;
     uint16_t* op = p.o + orow * rs + (int64_t)t.h * D + 4 * half;
@@ -542,6 +551,54 @@ __global__ void bq_combine_kernel(FwdParams p, int cuts, int D) {
   }
 }
 
+// Merge of the chunk partials of cut self-attention sequences (same weights as
+// bq_combine_kernel).  Cut i (sequence b_i, n_i chunks of part rows f_i + c L_b ..,
+// c < n_i) owns rows prefix[i] .. prefix[i + 1] - 1 of the merge's row space; one thread
+// per 8 head-dim columns of a (row, head).  The table follows the 4 nc chunk entries:
+// b[ncut] | first part row[ncut] | chunks[ncut] | row prefix[ncut + 1].
+__global__ void self_combine_kernel(FwdParams p, int cuts, int D) {
+  const int nc = p.num_chunks, H = p.num_heads, nd8 = D / 8;
+  const int* cb = p.chunks + 4 * nc;
+  const int* cf = cb + cuts;
+  const int* cn = cf + cuts;
+  const int* pre = cn + cuts;
+  const int64_t total = (int64_t)pre[cuts] * H * nd8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int d8 = (int)(i % nd8);
+    const int h = (int)((i / nd8) % H);
+    const int r = (int)(i / ((int64_t)nd8 * H));
+    int lo = 0, hi = cuts - 1;  // the cut whose row range holds r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = cb[lo], n = cn[lo];
+    const int row = r - pre[lo];
+    const int64_t s0 = p.offsets[b];
+    const int64_t len = p.offsets[b + 1] - s0;
+    const int64_t first = cf[lo] + row;  // part row of chunk 0; chunk c is c * len further
+    float m = -INFINITY;
+    for (int c = 0; c < n; ++c) m = fmaxf(m, p.part_lse[(first + c * len) * H + h]);
+    float sum = 0.f;
+    for (int c = 0; c < n; ++c) sum += expf(p.part_lse[(first + c * len) * H + h] - m);
+    const float lse = m + logf(sum);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c) {
+      const int64_t pr = first + c * len;
+      const float wgt = expf(p.part_lse[pr * H + h] - lse);
+      const float* src = p.part_o + (pr * H + h) * D + 8 * d8;
+      const float4 a = reinterpret_cast<const float4*>(src)[0];
+      const float4 e = reinterpret_cast<const float4*>(src)[1];
+      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
+      acc[4] += wgt * e.x; acc[5] += wgt * e.y; acc[6] += wgt * e.z; acc[7] += wgt * e.w;
+    }
+    st16(p.o + ((s0 + row) * H + h) * D + 8 * d8,
+         __builtin_bit_cast(u32x4, pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7])));
+    if (d8 == 0) p.lse[(int64_t)h * p.total_tokens + s0 + row] = lse;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bq_combine(const FwdParams& p, int cuts, int head_dim, hipStream_t s) {
@@ -552,10 +609,19 @@ hipError_t launch_bq_combine(const FwdParams& p, int cuts, int head_dim, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_self_combine(const FwdParams& p, int cuts, int64_t rows, int head_dim, hipStream_t s) {
+  const int64_t total = rows * p.num_heads * (head_dim / 8);
+  if (cuts <= 0 || total <= 0) return hipSuccess;
+  const int64_t g = (total + 255) / 256;
+  hipLaunchKernelGGL(self_combine_kernel, dim3((unsigned)(g < 4096 ? g : 4096)), dim3(256), 0, s, p, cuts, head_dim);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
   if (mode == kSelf) return head_dim == 64 ? launch<64, kSelf>(p, s) : launch<128, kSelf>(p, s);
   if (mode == kSelfSparse) return head_dim == 64 ? launch<64, kSelfSparse>(p, s) : launch<128, kSelfSparse>(p, s);
+  if (mode == kSelfChunks) return head_dim == 64 ? launch<64, kSelfChunks>(p, s) : launch<128, kSelfChunks>(p, s);
   return head_dim == 64 ? launch<64, kBroadcastQ>(p, s) : launch<128, kBroadcastQ>(p, s);
 }
 

@@ -7,7 +7,7 @@
 
 namespace jfa {
 
-enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2, kSelfSparse = 3 };
+enum : int { kSelf = 0, kBroadcastQ = 1, kBlockDiag = 2, kSelfSparse = 3, kSelfChunks = 4 };
 
 // Tile geometry.  A forward tile is kFwdRows query rows of one (sequence, head); its
 // key/value loop streams kFwdKeys keys at a time.  A backward tile is kBwdKeys key
@@ -105,6 +105,10 @@ struct FwdParams {
   // of part_o [S, Mq, H, D] / part_lse [S, H, Mq] (fp32: O normalised by the chunk's own
   // row sum, and the chunk's natural-log lse); then follow, per cut sequence i,
   // chunks[4 nc + 3 i + 0..2] = (b, first slot, slots), merged by launch_bq_combine.
+  // Self-attention key chunks (kSelfChunks): the same [4, nc] table, with chunks[3 nc +
+  // c] = -1 or the first part row r0 of the chunk: query row r of the tile's sequence
+  // writes part row r0 + r of part_o [R, H, D] / part_lse [R, H]; then follows the cut
+  // table of launch_self_combine.
   const int32_t* chunks;
   int32_t num_chunks;
   float* part_o;
@@ -272,6 +276,8 @@ hipError_t noalloc_scratch(void** out);
 hipError_t launch_fwd(const FwdParams& p, int mode, int head_dim, hipStream_t s);
 // Broadcast-Q forward: merge the chunk partials of the `cuts` cut sequences into o, lse.
 hipError_t launch_bq_combine(const FwdParams& p, int cuts, int head_dim, hipStream_t s);
+// Merge of cut self-attention sequences: `cuts` cuts covering `rows` query rows in all.
+hipError_t launch_self_combine(const FwdParams& p, int cuts, int64_t rows, int head_dim, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int mode, int head_dim, hipStream_t s);
 // Self-attention backward: dQ kernel (query tiles; also writes the per-row stats the
 // dK/dV kernel reads, so it runs first) and dK/dV kernel (key tiles).

@@ -68,6 +68,14 @@ void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
   deal_zigzag(order, max_programs, dynamic, out);
 }
 
+void schedule_fwd_chunks(const std::vector<int32_t>& cost, const std::vector<int32_t>& rows_of, int num_heads,
+                         int rows, int max_programs, bool dynamic, Schedule& out) {
+  std::vector<HostTile> order;
+  sorted_tiles(cost, num_heads, rows, rows_of, order);
+  out.tile_rows = rows;
+  deal_zigzag(order, max_programs, dynamic, out);
+}
+
 void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
                   int max_programs, bool dynamic, Schedule& out) {
   out.tile_rows = rows;

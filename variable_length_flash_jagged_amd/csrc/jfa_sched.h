@@ -46,6 +46,10 @@ struct Schedule {
 // lengths: L_b for b < B (validated by the caller).
 void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int num_q,
                   int rows, int max_programs, bool dynamic, Schedule& out);
+// Self-attention key chunks: chunk c (a tile "sequence" of cost[c] keys) has
+// ceil(rows_of[c] / rows) query tiles per head (its sequence's rows); same sort and deal.
+void schedule_fwd_chunks(const std::vector<int32_t>& cost, const std::vector<int32_t>& rows_of, int num_heads,
+                         int rows, int max_programs, bool dynamic, Schedule& out);
 void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
                   int max_programs, bool dynamic, Schedule& out);
 // Programs: min(max_programs, ceil(tiles / min_tiles)) (the block-diagonal kernels'
