@@ -23,6 +23,7 @@ import pytest
 import torch
 
 from oracle import block_sparse as S
+from oracle import schedule as spec
 from tests import gpu_helpers as G
 from variable_length_flash_jagged_amd import binding as B
 from variable_length_flash_jagged_amd import workloads as W
@@ -116,7 +117,10 @@ def test_block_sparse_grouped_query_and_dynamic_schedule():
 
 def test_block_sparse_ratio_one_equals_dense_forward_bit_exactly():
     p, g, o, lse = _run(LENGTHS, 2, 128, 1.0, seed=44, label="ratio 1")
-    o_d, lse_d = G.gpu_fwd(g)
+    # the dense forward with 16 programs, whose share leaves every sequence whole (with
+    # more programs it would cut the longest sequences' keys into chunks)
+    assert not spec.self_chunks_cut(LENGTHS, 2, 256, 16)
+    o_d, lse_d = G.gpu_fwd(g, B.make_opts(num_programs=16))
     torch.cuda.synchronize()
     assert torch.equal(o, o_d)
     assert torch.equal(lse, lse_d)

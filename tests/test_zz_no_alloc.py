@@ -1,13 +1,17 @@
 """The allocation-free forward jfa_fwd_noalloc (workspace in the library's device
 scratch array) against jfa_fwd (caller's workspace) through the C ABI: two calls in a
-row, the second on a smaller input, each bit-identical to jfa_fwd on the same inputs
-(same kernels, same schedule) and within the common tolerances of the fp64 oracle.
+row, the second on a smaller input, each within the common tolerances of the fp64
+oracle and bit-identical to jfa_fwd on the same inputs (same kernels, same schedule)
+-- except where jfa_fwd cuts a self-attention sequence's keys into chunks (few long
+sequences, oracle/schedule.py's self_chunks_cut), which jfa_fwd_noalloc never does:
+then the two sum the same keys in another grouping and O agrees to one bf16 step.
 The size limit is checked on the host before any device work."""
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import schedule as spec
 from tests import gpu_helpers as G
 from variable_length_flash_jagged_amd import binding as B
 from variable_length_flash_jagged_amd import workloads as W
@@ -26,8 +30,17 @@ def _one_call(lengths, heads, head_dim, mode, seed, opts, num_q=0):
     o, lse = B.fwd_noalloc(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], mode, g["scale"], opts,
                            _nan_like(o_sh, torch.bfloat16), _nan_like(l_sh, torch.float32))
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), "O differs from jfa_fwd"
-    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), "lse differs from jfa_fwd"
+    nprog = opts.num_programs if opts is not None and opts.num_programs > 0 else \
+        torch.cuda.get_device_properties(0).multi_processor_count
+    if mode == W.MODE_SELF and spec.self_chunks_cut(lengths, heads, 256, nprog):
+        d = (o.float() - o_ref.float()).abs()
+        assert float(d.max()) <= 2.0 ** -7 * float(o_ref.float().abs().max()), "O differs from jfa_fwd"
+        fin = torch.isfinite(lse_ref)
+        assert torch.equal(fin, torch.isfinite(lse))
+        assert float((lse[fin] - lse_ref[fin]).abs().max()) <= 1e-5 * max(1.0, float(lse_ref[fin].abs().max()))
+    else:
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), "O differs from jfa_fwd"
+        assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), "lse differs from jfa_fwd"
     o64, l64 = G.oracle_fwd(p)
     G.check_fwd(o, lse, o64, l64, "noalloc")
 
@@ -37,8 +50,10 @@ def _one_call(lengths, heads, head_dim, mode, seed, opts, num_q=0):
 def test_noalloc_forward_matches_jfa_fwd_twice_smaller_second(sched):
     opts = B.make_opts(sched=sched, num_programs=24)
     big = [1, 5, 63, 64, 65, 127, 128, 129, 200, 257, 700, 33, 0, 1024]
+    assert spec.self_chunks_cut(big, 2, 256, 24)  # jfa_fwd cuts the 1024-token sequence
     _one_call(big, 2, 128, W.MODE_SELF, 71, opts)
     _one_call([3, 300, 17], 2, 128, W.MODE_SELF, 72, opts)
+    _one_call(big, 2, 128, W.MODE_SELF, 71, B.make_opts(sched=sched, num_programs=8))  # no cut: bit-identical
 
 
 @pytest.mark.gpu

@@ -387,47 +387,32 @@ __global__ void dq_reduce_kernel(const float* part, uint16_t* dq, int num_q, int
 }
 
 // Chunk slabs [nc, E] (E = Mq * H * D, a multiple of 8), every one written in full by the
-// dQ kernel, are summed in two deterministic levels: group g of kReduceGroups sums its
-// contiguous range of slabs (in order) into its first slab, in place (each thread owns
-// one 4-float column of its group); then dq[e] = bf16(scale * sum of the group sums in
-// group order).
+// dQ kernel, are summed in a fixed order (run-to-run deterministic) by one thread per
+// 4-float column: group g of kReduceGroups sums its contiguous range of slabs in order,
+// then dq[e] = bf16(scale * sum of the group sums in group order).  The loads of a group
+// do not wait on its sum, so many are in flight per thread.
 constexpr int kReduceGroups = 16;
 
 __device__ __forceinline__ int64_t group_first(int g, int groups, int nc) { return (int64_t)g * nc / groups; }
 
-__global__ void dq_chunk_sum_kernel(float* slabs, int nc, int groups, int64_t slab_elems) {
+__global__ void dq_chunk_reduce_kernel(const float* __restrict__ slabs, uint16_t* __restrict__ dq, int nc,
+                                       int groups, int64_t slab_elems, float scale) {
   const int64_t n4 = slab_elems / 4;
-  const int g = blockIdx.y;
-  const int64_t first = group_first(g, groups, nc), last = group_first(g + 1, groups, nc);
-  if (last - first < 2) return;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    float4* col = reinterpret_cast<float4*>(slabs) + i;
-    float4 acc = col[first * n4];
-    for (int64_t c = first + 1; c < last; ++c) {
-      const float4 a = col[c * n4];
-      acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-    }
-    col[first * n4] = acc;
-  }
-}
-
-__global__ void dq_chunk_final_kernel(const float* slabs, uint16_t* dq, int nc, int groups, int64_t slab_elems,
-                                      float scale) {
-  const int64_t n8 = slab_elems / 8;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float4* col = reinterpret_cast<const float4*>(slabs) + i;
+    float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int g = 0; g < groups; ++g) {
-      const int64_t first = group_first(g, groups, nc);
-      if (group_first(g + 1, groups, nc) == first) continue;
-      const float* src = slabs + first * slab_elems + 8 * i;
-      const float4 a = reinterpret_cast<const float4*>(src)[0];
-      const float4 c = reinterpret_cast<const float4*>(src)[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += c.x; acc[5] += c.y; acc[6] += c.z; acc[7] += c.w;
+      const int64_t first = group_first(g, groups, nc), last = group_first(g + 1, groups, nc);
+      if (last == first) continue;
+      float4 acc = col[first * n4];
+#pragma unroll 8
+      for (int64_t c = first + 1; c < last; ++c) {
+        const float4 a = col[c * n4];
+        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+      }
+      tot.x += acc.x; tot.y += acc.y; tot.z += acc.z; tot.w += acc.w;
     }
-    const bf16x8 r = pack8(acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale, acc[4] * scale,
-                           acc[5] * scale, acc[6] * scale, acc[7] * scale);
-    st16(dq + 8 * i, __builtin_bit_cast(u32x4, r));
+    st8(dq + 4 * i, pack4(tot.x * scale, tot.y * scale, tot.z * scale, tot.w * scale));
   }
 }
 
@@ -469,16 +454,8 @@ hipError_t launch_dq_seq_reduce(float* slabs, uint16_t* dq, int num_slabs, int64
                                 hipStream_t s) {
   if (slab_elems <= 0) return hipSuccess;
   const int groups = num_slabs < kReduceGroups ? num_slabs : kReduceGroups;
-  if (num_slabs >= 2 * groups && groups > 0) {
-    hipLaunchKernelGGL(dq_chunk_sum_kernel, dim3(grid_for(slab_elems / 4, 256), groups), dim3(256), 0, s, slabs,
-                       num_slabs, groups, slab_elems);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // fewer than two slabs per group: no first level, every slab is its own group
-  const int g2 = (num_slabs >= 2 * groups && groups > 0) ? groups : num_slabs;
-  hipLaunchKernelGGL(dq_chunk_final_kernel, dim3(grid_for(slab_elems / 8, 64)), dim3(64), 0, s, slabs, dq,
-                     num_slabs, g2, slab_elems, scale);
+  hipLaunchKernelGGL(dq_chunk_reduce_kernel, dim3(grid_for(slab_elems / 4, 128)), dim3(128), 0, s, slabs, dq,
+                     num_slabs, groups, slab_elems, scale);
   return hipGetLastError();
 }
 

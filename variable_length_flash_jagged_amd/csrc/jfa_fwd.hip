@@ -515,11 +515,43 @@ hipError_t launch(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One pass over the chunk partials of one (row, head) and 8 head-dim columns: with
+// m the running maximum of the chunks' lse, s = sum_c exp(lse_c - m) and acc = sum_c
+// exp(lse_c - m) O_c (each sum rescaled when m grows), so that O = acc / s and
+// lse = m + ln s at the end; a chunk's loads do not wait on the previous chunk's sums.
+struct LseMerge {
+  float m = -INFINITY, s = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void add(float l, const float* o8) {
+    const float4 a = reinterpret_cast<const float4*>(o8)[0];
+    const float4 e = reinterpret_cast<const float4*>(o8)[1];
+    if (!(l > -INFINITY)) return;  // a chunk with no keys for this row adds nothing
+    if (l > m) {
+      const float r = expf(m - l);  // 0 on the first chunk (m = -inf)
+      s *= r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= r;
+      m = l;
+    }
+    const float w = expf(l - m);
+    s += w;
+    acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+    acc[4] += w * e.x; acc[5] += w * e.y; acc[6] += w * e.z; acc[7] += w * e.w;
+  }
+  // O (bf16, 8 columns) and, where lse_out is non-null, the row's lse
+  __device__ __forceinline__ void store(uint16_t* o, float* lse_out) const {
+    const float inv = s > 0.f ? 1.0f / s : 0.f;
+    st16(o, __builtin_bit_cast(u32x4, pack8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv, acc[4] * inv,
+                                            acc[5] * inv, acc[6] * inv, acc[7] * inv)));
+    if (lse_out) *lse_out = s > 0.f ? m + logf(s) : -INFINITY;
+  }
+};
+
 // Merge of the chunk partials of cut broadcast-Q sequences: for cut sequence i with
 // slots f .. f + n - 1 and each (query row, head), lse = log sum_c exp(lse_c) and
 // O = sum_c exp(lse_c - lse) O_c (each O_c normalised by its own row sum, so the
-// weights are the chunks' shares of the full row sum).  One thread per 8 head-dim
-// columns of a (cut sequence, row, head).
+// weights are the chunks' shares of the full row sum), in one pass (LseMerge).  One
+// thread per 8 head-dim columns of a (cut sequence, row, head).
 __global__ void bq_combine_kernel(FwdParams p, int cuts, int D) {
   const int nc = p.num_chunks, H = p.num_heads, Mq = p.num_q, nd8 = D / 8;
   const int64_t total = (int64_t)cuts * Mq * H * nd8;
@@ -530,24 +562,12 @@ __global__ void bq_combine_kernel(FwdParams p, int cuts, int D) {
     const int cut = (int)(i / ((int64_t)nd8 * H * Mq));
     const int* t = p.chunks + 4 * nc + 3 * cut;
     const int b = t[0], first = t[1], n = t[2];
-    float m = -INFINITY;
-    for (int c = 0; c < n; ++c) m = fmaxf(m, p.part_lse[((int64_t)(first + c) * H + h) * Mq + row]);
-    float sum = 0.f;
-    for (int c = 0; c < n; ++c) sum += expf(p.part_lse[((int64_t)(first + c) * H + h) * Mq + row] - m);
-    const float lse = m + logf(sum);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < n; ++c) {
-      const float wgt = expf(p.part_lse[((int64_t)(first + c) * H + h) * Mq + row] - lse);
-      const float* src = p.part_o + (((int64_t)(first + c) * Mq + row) * H + h) * D + 8 * d8;
-      const float4 a = reinterpret_cast<const float4*>(src)[0];
-      const float4 e = reinterpret_cast<const float4*>(src)[1];
-      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-      acc[4] += wgt * e.x; acc[5] += wgt * e.y; acc[6] += wgt * e.z; acc[7] += wgt * e.w;
-    }
+    LseMerge mg;
+    for (int c = 0; c < n; ++c)
+      mg.add(p.part_lse[((int64_t)(first + c) * H + h) * Mq + row],
+             p.part_o + (((int64_t)(first + c) * Mq + row) * H + h) * D + 8 * d8);
     const int64_t orow = (int64_t)b * Mq + row;
-    st16(p.o + (orow * H + h) * D + 8 * d8,
-         __builtin_bit_cast(u32x4, pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7])));
-    if (d8 == 0) p.lse[((int64_t)b * H + h) * Mq + row] = lse;
+    mg.store(p.o + (orow * H + h) * D + 8 * d8, d8 == 0 ? p.lse + ((int64_t)b * H + h) * Mq + row : nullptr);
   }
 }
 
@@ -578,24 +598,12 @@ __global__ void self_combine_kernel(FwdParams p, int cuts, int D) {
     const int64_t s0 = p.offsets[b];
     const int64_t len = p.offsets[b + 1] - s0;
     const int64_t first = cf[lo] + row;  // part row of chunk 0; chunk c is c * len further
-    float m = -INFINITY;
-    for (int c = 0; c < n; ++c) m = fmaxf(m, p.part_lse[(first + c * len) * H + h]);
-    float sum = 0.f;
-    for (int c = 0; c < n; ++c) sum += expf(p.part_lse[(first + c * len) * H + h] - m);
-    const float lse = m + logf(sum);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    LseMerge mg;
     for (int c = 0; c < n; ++c) {
       const int64_t pr = first + c * len;
-      const float wgt = expf(p.part_lse[pr * H + h] - lse);
-      const float* src = p.part_o + (pr * H + h) * D + 8 * d8;
-      const float4 a = reinterpret_cast<const float4*>(src)[0];
-      const float4 e = reinterpret_cast<const float4*>(src)[1];
-      acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-      acc[4] += wgt * e.x; acc[5] += wgt * e.y; acc[6] += wgt * e.z; acc[7] += wgt * e.w;
+      mg.add(p.part_lse[pr * H + h], p.part_o + (pr * H + h) * D + 8 * d8);
     }
-    st16(p.o + ((s0 + row) * H + h) * D + 8 * d8,
-         __builtin_bit_cast(u32x4, pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7])));
-    if (d8 == 0) p.lse[(int64_t)h * p.total_tokens + s0 + row] = lse;
+    mg.store(p.o + ((s0 + row) * H + h) * D + 8 * d8, d8 == 0 ? p.lse + (int64_t)h * p.total_tokens + s0 + row : nullptr);
   }
 }
 
