@@ -220,8 +220,10 @@ def cpu_baseline(p_cpu_fn, lengths, mode, num_heads, head_dim, num_q, target_s, 
             qv, qx = MX.quantise_qk(q)
             kv, kx = MX.quantise_qk(k)
             vv, vx = MX.quantise_v(v, off)
-            MX.mxfp8_forward(MX.dequantise_qk(qv, qx), MX.dequantise_qk(kv, kx), MX.dequantise_v(vv, vx, off), off,
-                             1.0 / np.sqrt(head_dim))
+            qd, kd, vd = MX.dequantise_qk(qv, qx), MX.dequantise_qk(kv, kx), MX.dequantise_v(vv, vx, off)
+            o_mx, _ = MX.mxfp8_forward(qd, kd, vd, off, 1.0 / np.sqrt(head_dim))
+            if not fwd_only:
+                MX.mxfp8_backward(qd, kd, vd, do, off, 1.0 / np.sqrt(head_dim), o_given=o_mx)
         elif rotary:
             from oracle import rotary as R
             tab = R.rope_table(max(1, int(max(lengths[b:e]))), head_dim)
@@ -296,6 +298,8 @@ def main():
                           device="cuda")
     if fwd_only:
         ws_b = None
+    elif mxfp8:
+        ws_b = B.alloc_workspace(shape, mode, B.PASS_BWD_MXFP8, opts, "cuda")
     elif ratio:
         ws_b = torch.empty(B.bwd_block_sparse_workspace_size(shape, p["offsets_host"], opts), dtype=torch.uint8,
                            device="cuda")
@@ -337,6 +341,9 @@ def main():
             B.bwd_block_sparse(q, k, v, o, do, lse, off, off_h, ratio, sel, scale, opts, dq, dk, dv, ws_b)
         elif rotary:
             B.bwd_rotary(q, k, v, o, do, lse, off, off_h, rope, scale, opts, dq, dk, dv, ws_b)
+        elif mxfp8 and not fwd_only:
+            B.bwd_mxfp8(mx["q8"], mx["qs"], mx["k8"], mx["ks"], mx["v8"], mx["vs"], mx["tp"], o, do, lse, off, off_h,
+                        scale, opts, dq, dk, dv, ws_b)
         elif not fwd_only:
             B.bwd(q, k, v, o, do, lse, off, off_h, mode, scale, opts, dq, dk, dv, ws_b)
         if i is not None:
@@ -379,7 +386,7 @@ def main():
     bwd_ms = sum(ev["f1"][i].elapsed_time(ev["b1"][i]) for i in range(args.steps)) / args.steps
     kt = {name: B.kernel_times(kid) for name, kid in
           (("fwd", B.KERNEL_FWD), ("bwd", B.KERNEL_BWD), ("bwd_dq", B.KERNEL_BWD_DQ), ("bwd_prep", B.KERNEL_BWD_PREP),
-           ("select", B.KERNEL_SPARSE_SELECT))}
+           ("select", B.KERNEL_SPARSE_SELECT), ("mx_decode", B.KERNEL_MX_QUANT))}
     B.kernel_timing(False)
 
     ff = M.fwd_flops(lengths, mode, h, d, mq)
@@ -561,7 +568,11 @@ def main():
         "mxfp8": None if not mxfp8 else {
             "v_tokens": int(mx["tp"]), "quantise_ms": round(mx["quant_ms"], 4),
             "quantise_launches": int(mx["quant_launches"]), "bf16_fwd_ms": round(plain[0], 4),
-            "speedup_vs_bf16_fwd": round(plain[0] / fwd_ms, 3)},
+            "speedup_vs_bf16_fwd": round(plain[0] / fwd_ms, 3),
+            # the backward decodes its MXFP8 inputs to bf16 (3 launches a step) before the
+            # bf16 backward kernels
+            "bwd_decode_ms": None if fwd_only else round(kt["mx_decode"][1] / max(1, args.steps), 4),
+            "bwd_decode_launches_per_step": None if fwd_only else kt["mx_decode"][0] // max(1, args.steps)},
         "cache_flush_mib_between_steps": FLUSH_MIB if w["name"] in FLUSH_WORKLOADS else 0,
         "padding": None if mode != W.MODE_SELF else {
             # the work a padded batch would do (every sequence padded to the longest)

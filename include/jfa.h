@@ -69,7 +69,8 @@ enum jfa_pass {
   JFA_PASS_FWD = 0,
   JFA_PASS_BWD = 1,
   JFA_PASS_FWD_SPARSE = 2, /* jfa_fwd_block_sparse (self mode only) */
-  JFA_PASS_FWD_MXFP8 = 3   /* jfa_fwd_mxfp8 and jfa_mxfp8_quantize_v (self mode only) */
+  JFA_PASS_FWD_MXFP8 = 3,  /* jfa_fwd_mxfp8 and jfa_mxfp8_quantize_v (self mode only) */
+  JFA_PASS_BWD_MXFP8 = 4   /* jfa_bwd_mxfp8 (self mode only) */
 };
 
 enum jfa_status {
@@ -227,6 +228,27 @@ int jfa_fwd_mxfp8(const jfa_shape* shape, float scale,
                   const uint8_t* v8t, const uint8_t* v_scales, int64_t v_tokens,
                   const int32_t* offsets_dev, const int32_t* offsets_host,
                   void* o, float* lse,
+                  void* workspace, size_t workspace_bytes,
+                  const jfa_opts* opts, void* stream);
+
+/* Backward of the MXFP8 self-attention forward (same section of the aixai.ru page, which
+ * reports the MXFP8 backward at parity with bf16 on dense shapes without saying which of
+ * its products run in FP8).  The MXFP8 inputs (the layouts above) are decoded once into
+ * bf16 -- exact: an E4M3 value times 2^X keeps its four significant bits in bf16 for
+ * X >= -117 -- and the self-attention backward (jfa_bwd's kernels, P and dS in bf16)
+ * runs on them.  o and lse: jfa_fwd_mxfp8's outputs; dout [T, H, D] bf16.  dq, dk, dv
+ * [T, H, D] bf16: the gradient of attention with respect to the decoded q, k, v (the
+ * quantisation itself passes gradients straight through).  opts as jfa_bwd (stored-dS
+ * path when ds_budget_mib holds dS).  workspace: jfa_workspace_size(shape,
+ * JFA_MODE_SELF, JFA_PASS_BWD_MXFP8, opts) bytes (the three decoded tensors plus
+ * jfa_bwd's workspace).  Argument errors as jfa_bwd and jfa_fwd_mxfp8, reported before
+ * any device work. */
+int jfa_bwd_mxfp8(const jfa_shape* shape, float scale,
+                  const uint8_t* q8, const uint8_t* q_scales, const uint8_t* k8, const uint8_t* k_scales,
+                  const uint8_t* v8t, const uint8_t* v_scales, int64_t v_tokens,
+                  const void* o, const void* dout, const float* lse,
+                  const int32_t* offsets_dev, const int32_t* offsets_host,
+                  void* dq, void* dk, void* dv,
                   void* workspace, size_t workspace_bytes,
                   const jfa_opts* opts, void* stream);
 

@@ -23,7 +23,7 @@ bits, bias 7, 3 mantissa bits, largest finite 448, no infinities).  Readings:
 
 import numpy as np
 
-from .attention import MODE_SELF, attention_forward
+from .attention import MODE_SELF, attention_backward, attention_forward
 from .offsets import validate_offsets
 
 E4M3_MAX = 448.0
@@ -122,6 +122,16 @@ def dequantise_v(vals, xs, offsets):
 def mxfp8_forward(q, k, v, offsets, scale=None):
     """Self attention of the dequantised inputs (fp64, exact P).  Returns (o, lse)."""
     return attention_forward(q, k, v, offsets, MODE_SELF, scale)
+
+
+def mxfp8_backward(q, k, v, do, offsets, scale=None, o_given=None):
+    """Gradient (dq, dk, dv) of self attention with respect to the dequantised inputs
+    (fp64).  Reading: the pages report an MXFP8 backward without saying which of its
+    products run in FP8; this one decodes the inputs and differentiates attention at the
+    decoded point, P and dS unquantised, and lets gradients pass the quantisation
+    straight through.  o_given: the forward output Di is formed from (the MXFP8
+    forward's O, whose P was quantised; default: the exact O)."""
+    return attention_backward(q, k, v, do, offsets, MODE_SELF, scale, o_given=o_given)
 
 
 def p_quantisation_bound(q, k, v, offsets, scale=None):

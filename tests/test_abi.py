@@ -135,7 +135,7 @@ def test_bad_options_and_pass():
         B.workspace_size(shape, 0, 0, B.make_opts(sched=3))
     assert e.value.code == -8
     with pytest.raises(B.JfaError) as e:
-        B.workspace_size(shape, 0, 4)
+        B.workspace_size(shape, 0, 5)   # passes 0 .. 4
     assert e.value.code == -4
 
 
@@ -352,6 +352,27 @@ def test_broadcast_q_forward_key_chunks_match_spec(sched):
     want = spec.fwd_schedule(lengths, 4, 1, 256, rows, 256, dynamic=bool(sched))
     got_t, got_s = _to_lists(tiles, seg)
     assert got_t == [tuple(t) for t in want[0]] and got_s == list(want[1]) and progs == want[2]
+
+
+@no_gpu_only
+def test_mxfp8_backward_argument_errors_before_device_work():
+    lengths = [300, 0, 64, 65, 1]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = B.make_shape(len(lengths), 2, 128, int(off[-1]))
+    t = int(off[-1])
+    ws = B.workspace_size(shape, 0, B.PASS_BWD_MXFP8)
+    # the three decoded tensors plus the self-attention backward's workspace
+    assert ws >= 3 * t * 2 * 128 * 2 + B.workspace_size(shape, 0, B.PASS_BWD)
+    with pytest.raises(B.JfaError) as e:
+        B.workspace_size(shape, 2, B.PASS_BWD_MXFP8)   # self mode only
+    assert e.value.code == -4
+    lib = B.lib()
+    p = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every check fails first
+    args = lambda tokens, ws_bytes, dq=p: (ctypes.byref(shape), 0.1, p, p, p, p, p, p, tokens, p, p, p, p,
+                                           off.ctypes.data, dq, p, p, p, ws_bytes, None, None)
+    assert lib.jfa_bwd_mxfp8(*args(575, 1 << 40)) == -2 and b"v_tokens" in lib.jfa_last_error_detail()
+    assert lib.jfa_bwd_mxfp8(*args(576, 16)) == -7                    # workspace too small
+    assert lib.jfa_bwd_mxfp8(*args(576, 1 << 40, None)) == -1         # dq is NULL
 
 
 @pytest.mark.parametrize("sched", [0, 1])

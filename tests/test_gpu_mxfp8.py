@@ -1,5 +1,5 @@
-"""GPU parity of the MXFP8 variant (jfa_mxfp8_quantize_qk / _v, jfa_fwd_mxfp8) against
-the fp64 oracle (oracle/mxfp8.py).
+"""GPU parity of the MXFP8 variant (jfa_mxfp8_quantize_qk / _v, jfa_fwd_mxfp8,
+jfa_bwd_mxfp8) against the fp64 oracle (oracle/mxfp8.py).
 
 Quantisation is integer work once the block maximum is known: the GPU's E8M0 bytes and
 the values of its E4M3 bytes must equal the oracle's exactly (zero's sign aside).  The
@@ -7,7 +7,9 @@ forward is checked against fp64 attention of the dequantised GPU codes: lse with
 1e-3 (S and the softmax statistics are exact functions of the quantised inputs up to
 fp32 rounding), O within the common 2e-2 plus the oracle's bound on what quantising P
 per 32 keys can change (the kernel quantises the running P of each key step, which the
-bound covers)."""
+bound covers).  The backward is checked against the oracle's gradient at the decoded
+inputs (decoded from the GPU's own codes) with Di formed from the MXFP8 forward's O,
+to the common gradient tolerances (whole batch and every sequence and head)."""
 
 import numpy as np
 import pytest
@@ -151,3 +153,42 @@ def test_mxfp8_full_workload_sampled():
         err = np.abs(G.f64(o[s:e]) - o_ref).max(axis=2)
         assert float((err - G.O_TOL - bound).max()) <= 0, f"workload 9 seq {b} (L={n})"
         assert float(np.abs(G.f64(lse[:, s:e]) - lse_ref).max()) <= G.LSE_TOL, f"workload 9 seq {b} lse"
+
+
+def _decoded(q8, qs, k8, ks, v8, vs, lengths, offsets_host):
+    """fp64 q, k, v decoded from the GPU's codes (the oracle's decoder)."""
+    qd = M.dequantise_qk(M.e4m3_decode(q8.cpu().numpy()), qs.cpu().numpy().astype(np.int64) - 127)
+    kd = M.dequantise_qk(M.e4m3_decode(k8.cpu().numpy()), ks.cpu().numpy().astype(np.int64) - 127)
+    vvals, vxs = _gpu_v_to_tokens(v8, vs, lengths)
+    return qd, kd, M.dequantise_v(vvals, vxs, offsets_host)
+
+
+def _run_bwd(lengths, heads, head_dim, seed, opts=None, label=""):
+    print(f"[case] mxfp8 backward {label} lengths={list(lengths)[:12]} H={heads} D={head_dim} seed={seed}",
+          flush=True)
+    p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=True)
+    g = G.to_gpu(p)
+    q8, qs = B.mxfp8_quantize_qk(g["q"])
+    k8, ks = B.mxfp8_quantize_qk(g["k"])
+    v8, vs, tp = B.mxfp8_quantize_v(g["v"], g["offsets"], g["offsets_host"])
+    o, lse = B.fwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, g["offsets"], g["offsets_host"], g["scale"])
+    grads = B.bwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, o, g["do"], lse, g["offsets"], g["offsets_host"], g["scale"],
+                        opts, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
+    torch.cuda.synchronize()
+    qd, kd, vd = _decoded(q8, qs, k8, ks, v8, vs, p["lengths"], p["offsets_host"])
+    refs = M.mxfp8_backward(qd, kd, vd, G.f64(p["do"]), p["offsets_host"], p["scale"], o_given=G.f64(o))
+    errs = G.check_bwd(grads, refs, label, p, refs)
+    print(f"{label}: rel-L2 dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_mxfp8_backward(head_dim):
+    _run_bwd(LENGTHS, 2, head_dim, seed=74, label=f"D{head_dim}")
+
+
+def test_mxfp8_backward_stored_ds_path_and_production_lengths():
+    lengths = W.workload_lengths(3, 0, 24).tolist()
+    shape = B.make_shape(len(lengths), 2, 128, int(sum(lengths)))
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    opts = B.make_opts(sched=1, ds_budget_mib=B.ds_budget_mib(shape, off))
+    _run_bwd(lengths, 2, 128, seed=75, opts=opts, label="stored dS, production lengths, 24 sequences")

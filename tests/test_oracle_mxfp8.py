@@ -110,3 +110,34 @@ def test_p_quantisation_bound_holds_for_quantised_p():
             assert (err <= bound[s:e, h] + 1e-12).all()
             changed = changed or bool((err > 0).any())
     assert changed                                      # quantising P does change O
+
+
+def test_mxfp8_backward_matches_finite_differences_at_the_decoded_point():
+    """Brute force: central differences of L = sum(O * dO) with respect to single
+    elements of the dequantised q, k, v of two sequences."""
+    lengths = [5, 3]
+    off = oracle.offsets_from_lengths(lengths)
+    rng = np.random.default_rng(11)
+    raw = [rng.standard_normal((8, 1, 32)) for _ in range(3)]
+    qv, qx = M.quantise_qk(raw[0])
+    kv, kx = M.quantise_qk(raw[1])
+    vv, vx = M.quantise_v(raw[2], off)
+    q, k = M.dequantise_qk(qv, qx), M.dequantise_qk(kv, kx)
+    v = M.dequantise_v(vv, vx, off)
+    do = rng.standard_normal((8, 1, 32))
+    grads = M.mxfp8_backward(q, k, v, do, off, 0.2)
+    eps = 1e-6
+
+    def loss(qq, kk, vv_):
+        o, _ = M.mxfp8_forward(qq, kk, vv_, off, 0.2)
+        return float((o * do).sum())
+
+    for which in range(3):
+        for (t, d) in ((0, 0), (4, 17), (6, 31)):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][t, 0, d] += eps
+            up = loss(*args)
+            args[which][t, 0, d] -= 2 * eps
+            down = loss(*args)
+            fd = (up - down) / (2 * eps)
+            assert abs(fd - grads[which][t, 0, d]) <= 1e-6 * max(1.0, abs(fd)), (which, t, d)

@@ -22,6 +22,7 @@ PASS_FWD = 0
 PASS_BWD = 1
 PASS_FWD_SPARSE = 2
 PASS_FWD_MXFP8 = 3
+PASS_BWD_MXFP8 = 4
 KERNEL_FWD = 0
 KERNEL_BWD = 1
 KERNEL_BWD_DQ = 2
@@ -107,6 +108,9 @@ def lib():
         L.jfa_mxfp8_quantize_v.argtypes = [sp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.jfa_fwd_mxfp8.restype = ctypes.c_int
         L.jfa_fwd_mxfp8.argtypes = [sp, f32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, op, vp]
+        L.jfa_bwd_mxfp8.restype = ctypes.c_int
+        L.jfa_bwd_mxfp8.argtypes = [sp, f32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, ctypes.c_size_t, op, vp]
         L.jfa_ds_bytes.restype = ctypes.c_int
         L.jfa_ds_bytes.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_size_t)]
         L.jfa_schedule.restype = ctypes.c_int
@@ -549,3 +553,38 @@ def fwd_mxfp8(q8, q_scales, k8, k_scales, v8t, v_scales, v_tokens, offsets, offs
                                _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts else None,
                                _stream(stream)), "jfa_fwd_mxfp8")
     return o, lse
+
+
+def bwd_mxfp8(q8, q_scales, k8, k_scales, v8t, v_scales, v_tokens, o, do, lse, offsets, offsets_host, scale=None,
+              opts=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of the MXFP8 self-attention forward: gradients (dq, dk, dv bf16 [T, H, D])
+    with respect to the decoded inputs."""
+    import torch
+    t, h, d = q8.shape
+    nb = len(offsets_host) - 1
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    for name, x in (("q8", q8), ("q_scales", q_scales), ("k8", k8), ("k_scales", k_scales), ("v8t", v8t),
+                    ("v_scales", v_scales)):
+        _check_tensor(name, x, torch.uint8)
+    if k8.shape != q8.shape or q_scales.shape != (t, h, d // 32) or k_scales.shape != (t, h, d // 32):
+        raise ValueError("q8, k8 [T, H, D] and their scales [T, H, D/32]")
+    if v8t.shape != (h, d, v_tokens) or v_scales.shape != (h, d, v_tokens // 32):
+        raise ValueError("v8t [H, D, Tp] and v_scales [H, D, Tp/32]")
+    for name, x in (("o", o), ("do", do)):
+        _check_tensor(name, x, torch.bfloat16, (t, h, d))
+    _check_tensor("lse", lse, torch.float32, (h, t))
+    _check_tensor("offsets", offsets, torch.int32, (nb + 1,))
+    shape = make_shape(nb, h, d, t)
+    dq = torch.empty((t, h, d), dtype=torch.bfloat16, device=q8.device) if dq is None else dq
+    dk = torch.empty((t, h, d), dtype=torch.bfloat16, device=q8.device) if dk is None else dk
+    dv = torch.empty((t, h, d), dtype=torch.bfloat16, device=q8.device) if dv is None else dv
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, x, torch.bfloat16, (t, h, d))
+    if workspace is None:
+        workspace = alloc_workspace(shape, MODE_SELF, PASS_BWD_MXFP8, opts, q8.device)
+    host = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    _check(lib().jfa_bwd_mxfp8(ctypes.byref(shape), scale, _ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales),
+                               _ptr(v8t), _ptr(v_scales), v_tokens, _ptr(o), _ptr(do), _ptr(lse), _ptr(offsets),
+                               host.ctypes.data, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                               ctypes.byref(opts) if opts else None, _stream(stream)), "jfa_bwd_mxfp8")
+    return dq, dk, dv

@@ -609,6 +609,33 @@ std::vector<int64_t> mx_vbase(const std::vector<int32_t>& lengths) {
   return vb;
 }
 
+// Workspace of jfa_bwd_mxfp8: the decoded q, k, v (bf16 [T, H, D] each), the V layout
+// tables (padded start of each sequence, sequence of each padded 64-key group), then the
+// self-attention backward's own workspace.
+struct MxBwdLayout {
+  size_t q = 0, k = 0, v = 0, vbase = 0, groups = 0, bwd = 0, total = 0;
+};
+
+void mx_bwd_layout(const jfa_shape* s, const Opts& o, MxBwdLayout& M) {
+  const int64_t B = s->num_seqs, T = s->total_tokens, H = s->num_heads, D = s->head_dim;
+  const size_t tensor = align_up((size_t)(T * H * D) * 2);
+  size_t at = 0;
+  M.q = at;
+  at += tensor;
+  M.k = at;
+  at += tensor;
+  M.v = at;
+  at += tensor;
+  M.vbase = at;
+  at += align_up((B + 1) * sizeof(int64_t));
+  M.groups = at;  // sum_b ceil(L_b / 64) <= T / 64 + B padded groups
+  at += align_up((T / kMxVPad + B + 1) * sizeof(int32_t));
+  Layout L;
+  layout_for(s, JFA_MODE_SELF, JFA_PASS_BWD, o, L);
+  M.bwd = at;
+  M.total = at + L.total;
+}
+
 int check_mx_shape(const jfa_shape* shape) {
   int rc = check_shape(shape, JFA_MODE_SELF);
   if (rc) return rc;
@@ -776,13 +803,22 @@ int jfa_workspace_size(const jfa_shape* shape, int mode, int pass, const jfa_opt
   g_detail.clear();
   int rc = check_shape(shape, mode);
   if (rc) return rc;
-  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_FWD_SPARSE && pass != JFA_PASS_FWD_MXFP8)
+  if (pass != JFA_PASS_FWD && pass != JFA_PASS_BWD && pass != JFA_PASS_FWD_SPARSE && pass != JFA_PASS_FWD_MXFP8 &&
+      pass != JFA_PASS_BWD_MXFP8)
     return fail(JFA_ERR_BAD_MODE, "pass must be a jfa_pass");
-  if ((pass == JFA_PASS_FWD_SPARSE || pass == JFA_PASS_FWD_MXFP8) && mode != JFA_MODE_SELF)
-    return fail(JFA_ERR_BAD_MODE, "the block-sparse and MXFP8 forwards are self mode only");
+  if ((pass == JFA_PASS_FWD_SPARSE || pass == JFA_PASS_FWD_MXFP8 || pass == JFA_PASS_BWD_MXFP8) &&
+      mode != JFA_MODE_SELF)
+    return fail(JFA_ERR_BAD_MODE, "the block-sparse and MXFP8 variants are self mode only");
   if (!bytes) return fail(JFA_ERR_NULL_POINTER, "bytes is NULL");
   Opts o;
   if ((rc = check_opts(opts, o))) return rc;
+  if (pass == JFA_PASS_BWD_MXFP8) {
+    if ((rc = check_mx_shape(shape))) return rc;
+    MxBwdLayout M;
+    mx_bwd_layout(shape, o, M);
+    *bytes = M.total;
+    return JFA_OK;
+  }
   Layout L;
   layout_for(shape, mode, pass, o, L);
   *bytes = L.total;
@@ -1664,6 +1700,74 @@ int jfa_bwd_rotary(const jfa_shape* shape, int mode, float scale, const void* q,
   }
   return bwd_entry(shape, mode, scale, q, k, v, o, dout, lse, rope_cos_sin, rope_positions, offsets_dev,
                    offsets_host, dq, dk, dv, workspace, workspace_bytes, opts, stream);
+}
+
+int jfa_bwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const uint8_t* q_scales,
+                  const uint8_t* k8, const uint8_t* k_scales, const uint8_t* v8t, const uint8_t* v_scales,
+                  int64_t v_tokens, const void* o, const void* dout, const float* lse, const int32_t* offsets_dev,
+                  const int32_t* offsets_host, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
+  g_detail.clear();
+  hipStream_t stream = (hipStream_t)stream_;
+  int rc = check_mx_shape(shape);
+  if (rc) return rc;
+  Opts op;
+  if ((rc = check_opts(opts, op))) return rc;
+  if (!q8 || !q_scales || !k8 || !k_scales || !v8t || !v_scales || !o || !dout || !lse || !offsets_dev || !dq || !dk ||
+      !dv || !workspace)
+    return fail(JFA_ERR_NULL_POINTER, "codes, scales, o, dout, lse, offsets_dev, dq, dk, dv and workspace must be "
+                                      "non-NULL");
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8t, 16) || !aligned(workspace, kAlign))
+    return fail(JFA_ERR_MISALIGNED, "codes 16-byte aligned, workspace 256-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(JFA_ERR_BAD_SHAPE, "scale must be positive and finite");
+  MxBwdLayout M;
+  mx_bwd_layout(shape, op, M);
+  if (workspace_bytes < M.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, M.total);
+  std::vector<int32_t> lengths;
+  if ((rc = intake_offsets(shape, offsets_dev, offsets_host, stream, lengths))) return rc;
+  const std::vector<int64_t> vb = mx_vbase(lengths);
+  if (v_tokens != vb.back())
+    return fail(JFA_ERR_BAD_SHAPE, "v_tokens %lld differs from jfa_mxfp8_v_tokens() = %lld", (long long)v_tokens,
+                (long long)vb.back());
+  char* ws = (char*)workspace;
+  const int H = shape->num_heads, D = shape->head_dim;
+  MxDequantParams p{};
+  p.num_heads = H;
+  p.head_dim = D;
+  p.rows = shape->total_tokens * H;
+  p.scales = q_scales;
+  p.codes = q8;
+  p.out = (uint16_t*)(ws + M.q);
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_MX_QUANT, stream, [&] { return launch_mx_dequant_qk(p, stream); }),
+                          "MXFP8 decode launch")))
+    return rc;
+  p.scales = k_scales;
+  p.codes = k8;
+  p.out = (uint16_t*)(ws + M.k);
+  if ((rc = launch_status(timed_launch(JFA_KERNEL_MX_QUANT, stream, [&] { return launch_mx_dequant_qk(p, stream); }),
+                          "MXFP8 decode launch")))
+    return rc;
+  if (vb.back() > 0) {
+    std::vector<char> buf(M.groups - M.vbase + (size_t)(vb.back() / kMxVPad) * sizeof(int32_t), 0);
+    memcpy(buf.data(), vb.data(), vb.size() * sizeof(int64_t));
+    int32_t* gs = reinterpret_cast<int32_t*>(buf.data() + (M.groups - M.vbase));
+    for (size_t b = 0; b < lengths.size(); ++b)
+      for (int64_t g = vb[b] / kMxVPad; g < vb[b + 1] / kMxVPad; ++g) gs[g] = (int32_t)b;
+    if ((rc = upload(buf.data(), buf.size(), ws + M.vbase, stream))) return rc;
+    p.codes = v8t;
+    p.scales = v_scales;
+    p.out = (uint16_t*)(ws + M.v);
+    p.offsets = offsets_dev;
+    p.vbase = (const int64_t*)(ws + M.vbase);
+    p.group_seq = (const int32_t*)(ws + M.groups);
+    p.tp = vb.back();
+    if ((rc = launch_status(timed_launch(JFA_KERNEL_MX_QUANT, stream, [&] { return launch_mx_dequant_v(p, stream); }),
+                            "MXFP8 V decode launch")))
+      return rc;
+  }
+  return bwd_entry(shape, JFA_MODE_SELF, scale, ws + M.q, ws + M.k, ws + M.v, o, dout, lse, nullptr, 0, offsets_dev,
+                   offsets_host, dq, dk, dv, ws + M.bwd, workspace_bytes - M.bwd, opts, stream);
 }
 
 }  // extern "C"

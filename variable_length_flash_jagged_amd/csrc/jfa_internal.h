@@ -245,6 +245,19 @@ struct MxQuantParams {
   int64_t tp;              // V: padded total (multiple of kMxVPad)
 };
 
+// MXFP8 decoding (the backward's inputs): codes + E8M0 exponents -> bf16.
+struct MxDequantParams {
+  const uint8_t* codes;      // Q/K: [T, H, D]; V: [H][D][tp]
+  const uint8_t* scales;     // Q/K: [T, H, D/32]; V: [H][D][tp/32]
+  uint16_t* out;             // bf16 [T, H, D]
+  int64_t rows;              // Q/K: T * H
+  int32_t num_heads, head_dim;
+  const int32_t* offsets;    // V: [B+1]
+  const int64_t* vbase;      // V: [B+1] padded start of each sequence
+  const int32_t* group_seq;  // V: [tp / kMxVPad] sequence of each padded 64-key group
+  int64_t tp;                // V: padded total
+};
+
 // MXFP8 forward (self attention; one key/value head per query head).
 struct MxParams {
   const uint8_t* q8;
@@ -299,6 +312,8 @@ hipError_t launch_mark(const MarkParams& p, hipStream_t s);
 hipError_t launch_mx_quant_qk(const MxQuantParams& p, hipStream_t s);
 hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s);
 hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s);
+hipError_t launch_mx_dequant_qk(const MxDequantParams& p, hipStream_t s);
+hipError_t launch_mx_dequant_v(const MxDequantParams& p, hipStream_t s);
 // dst[i] = bf16(scale * src[i]), i < n (n multiple of 8).
 hipError_t launch_cast_scale(const float* src, uint16_t* dst, int64_t n, float scale, hipStream_t s);
 // Broadcast-Q partial slabs [P, Mq, D] (programs h*ph .. h*ph+ph-1 hold head h) ->

@@ -130,6 +130,74 @@ __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
   }
 }
 
+// ---------------------------------------------------------------- decoding
+
+// The four E4M3 bytes of a word (OCP E4M3FN, the encoding the quantisers write) times
+// 2^x.  Exact, and exact again in bf16, for x >= -117: the at most four significant bits
+// stay in the normal range.
+__device__ __forceinline__ void mx_decode4(uint32_t word, int x, float* v) {
+  v[0] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)word, 0), x);
+  v[1] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)word, 1), x);
+  v[2] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)word, 2), x);
+  v[3] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)word, 3), x);
+}
+
+// Q or K codes [T, H, D] + exponents [T, H, D/32] -> bf16 [T, H, D]: one thread per 16
+// codes (half of one 32-element block).
+__global__ void __launch_bounds__(256) dequant_qk_kernel(MxDequantParams p) {
+  const int64_t n16 = p.rows * (p.head_dim / 16);
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < n16; g += (int64_t)gridDim.x * 256) {
+    const u32x4 c = ld16(p.codes + 16 * g);
+    const int x = (int)p.scales[g >> 1] - 127;
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx_decode4(c[w], x, v + 4 * w);
+    uint16_t* dst = p.out + 16 * g;
+    st16(dst, __builtin_bit_cast(u32x4, pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7])));
+    st16(dst + 8, __builtin_bit_cast(u32x4, pack8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15])));
+  }
+}
+
+// V codes [H][D][Tp] (transposed per head, sequences padded to 64 keys) + exponents
+// [H][D][Tp/32] -> bf16 [T, H, D].  One workgroup per (padded 64-key group, head): four
+// lanes read one dimension's 64 codes (64 contiguous bytes), decode them and write them
+// into an LDS tile [64 keys][D]; then every lane copies 16-byte row pieces of the tile's
+// valid keys to their token rows.
+template <int D>
+__global__ void __launch_bounds__(256) dequant_v_kernel(MxDequantParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kMxVPad * D];
+  const int H = p.num_heads, t = threadIdx.x;
+  const int64_t groups = p.tp / kMxVPad;
+  for (int64_t gh = blockIdx.x; gh < groups * H; gh += gridDim.x) {
+    const int64_t grp = gh / H;
+    const int h = (int)(gh - grp * H);
+    const int b = p.group_seq[grp];
+    const int64_t s0 = p.offsets[b];
+    const int64_t j0 = grp * kMxVPad - p.vbase[b];  // first key of the group in its sequence
+    const int valid = (int)min<int64_t>(kMxVPad, p.offsets[b + 1] - s0 - j0);
+    __syncthreads();  // the previous group's readers are done with the tile
+#pragma unroll
+    for (int r = 0; r < (4 * D) / 256; ++r) {
+      const int ch = t + 256 * r;
+      const int d = ch >> 2, c = ch & 3;  // 16 keys 16 c .. of dimension d
+      const int64_t row = (int64_t)h * D + d;
+      const u32x4 w = ld16(p.codes + row * p.tp + grp * kMxVPad + 16 * c);
+      const int x = (int)p.scales[row * (p.tp / 32) + 2 * grp + (c >> 1)] - 127;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mx_decode4(w[q], x, v + 4 * q);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[(16 * c + i) * D + d] = __builtin_bit_cast(uint16_t, (bf16)v[i]);
+    }
+    __syncthreads();
+    constexpr int CPR = D / 8;  // 16-byte pieces per key row
+    for (int q = t; q < valid * CPR; q += 256) {
+      const int j = q / CPR, c8 = q % CPR;
+      st16(p.out + ((s0 + j0 + j) * H + h) * D + 8 * c8, *reinterpret_cast<const u32x4*>(&tile[j * D + 8 * c8]));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- forward
 
 template <int D>
@@ -390,6 +458,23 @@ hipError_t launch_mx_quant_qk(const MxQuantParams& p, hipStream_t s) {
 
 hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s) {
   return grid_launch(quant_v_kernel, p, (p.tp / kMxVPad) * p.num_heads * 2 * p.head_dim, s);
+}
+
+hipError_t launch_mx_dequant_qk(const MxDequantParams& p, hipStream_t s) {
+  const int64_t threads = p.rows * (p.head_dim / 16);
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_qk_kernel, dim3((unsigned)std::min<int64_t>((threads + 255) / 256, 16384)), dim3(256), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequant_v(const MxDequantParams& p, hipStream_t s) {
+  const int64_t work = (p.tp / kMxVPad) * p.num_heads;
+  if (work <= 0) return hipSuccess;
+  const dim3 grid((unsigned)std::min<int64_t>(work, 16384));
+  if (p.head_dim == 64) hipLaunchKernelGGL(dequant_v_kernel<64>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(dequant_v_kernel<128>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s) {

@@ -50,8 +50,7 @@ WORKLOADS = {
     7: dict(name="production_jagged_sparse", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0,
             sparse_ratio=0.5),
     8: dict(name="block_diag_rotary", mode=MODE_BLOCK_DIAG, num_heads=4, head_dim=64, num_q=0, rotary=True),
-    9: dict(name="production_jagged_mxfp8", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0, fwd_only=True,
-            mxfp8=True),
+    9: dict(name="production_jagged_mxfp8", mode=MODE_SELF, num_heads=4, head_dim=128, num_q=0, mxfp8=True),
 }
 
 
