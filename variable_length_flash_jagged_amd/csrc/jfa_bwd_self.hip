@@ -179,12 +179,7 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
     // Row term for the dK/dV kernel: -lse log2 e and -Di as bf16 high + low parts
     // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2), and the
     // constant -1 the block-sparse key mask multiplies.
-    const float x = -lse * kLog2e, y = -di;
-    const bf16 xh = (bf16)x, yh = (bf16)y;
-    const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
-    const bf16 z = (bf16)0.0f;
-    const bf16x8 t = {xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
-    st16(p.row_aug + lrow * 8, __builtin_bit_cast(u32x4, t));
+    st16(p.row_aug + lrow * 8, __builtin_bit_cast(u32x4, row_term(lse, di)));
   }
 
   f32x16 dq[C::NDB];
@@ -1282,12 +1277,7 @@ __global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
     for (int m = LPR / 2; m > 0; m >>= 1) di += __shfl_xor(di, m, LPR);
     if (sub == 0) {
       const int64_t t = r / H, h = r - t * H;
-      const float x = -p.lse[h * T + t] * kLog2e, y = -di;
-      const bf16 xh = (bf16)x, yh = (bf16)y;
-      const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
-      const bf16 z = (bf16)0.0f;
-      const bf16x8 v = {xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
-      st16(p.row_aug + (h * T + t) * 8, __builtin_bit_cast(u32x4, v));
+      st16(p.row_aug + (h * T + t) * 8, __builtin_bit_cast(u32x4, row_term(p.lse[h * T + t], di)));
     }
   }
 }

@@ -129,6 +129,19 @@ __device__ __forceinline__ void phase_barrier() {
 // writes them, so that no pass sinks their computation into the next phase (which
 // would put one wave's vector and matrix work back into the same phase).
 __device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+
+// Row term of one query row for the dK/dV kernels' extra MFMA k-step: -lse log2 e and
+// -Di as bf16 high + low parts, and the constant -1 the block-sparse key mask multiplies.
+// One definition for every kernel that writes it (no multiply-add contraction, so the
+// low parts are the same rounding of the same fp32 values everywhere).
+__device__ __forceinline__ bf16x8 row_term(float lse, float di) {
+#pragma clang fp contract(off)
+  const float x = -lse * kLog2e, y = -di;
+  const bf16 xh = (bf16)x, yh = (bf16)y;
+  const bf16 xl = (bf16)(x - (float)xh), yl = (bf16)(y - (float)yh);
+  const bf16 z = (bf16)0.0f;
+  return bf16x8{xh, xl, (bf16)(-1.0f), z, yh, yl, z, z};
+}
 __device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
