@@ -387,32 +387,47 @@ __global__ void dq_reduce_kernel(const float* part, uint16_t* dq, int num_q, int
 }
 
 // Chunk slabs [nc, E] (E = Mq * H * D, a multiple of 8), every one written in full by the
-// dQ kernel, are summed in a fixed order (run-to-run deterministic) by one thread per
-// 4-float column: group g of kReduceGroups sums its contiguous range of slabs in order,
-// then dq[e] = bf16(scale * sum of the group sums in group order).  The loads of a group
-// do not wait on its sum, so many are in flight per thread.
+// dQ kernel, are summed in a fixed order (run-to-run deterministic): group g of
+// kReduceGroups sums its contiguous range of slabs in order, then dq[e] = bf16(scale *
+// sum of the group sums in group order).  One workgroup per 16 four-float columns: its
+// 256 lanes are (group, column), each summing one group of one column; the group sums
+// meet in LDS and 16 lanes add them up.
 constexpr int kReduceGroups = 16;
 
 __device__ __forceinline__ int64_t group_first(int g, int groups, int nc) { return (int64_t)g * nc / groups; }
 
-__global__ void dq_chunk_reduce_kernel(const float* __restrict__ slabs, uint16_t* __restrict__ dq, int nc,
-                                       int groups, int64_t slab_elems, float scale) {
+__global__ void __launch_bounds__(256) dq_chunk_reduce_kernel(const float* __restrict__ slabs,
+                                                              uint16_t* __restrict__ dq, int nc, int groups,
+                                                              int64_t slab_elems, float scale) {
+  __shared__ float4 part[kReduceGroups][16];
   const int64_t n4 = slab_elems / 4;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    const float4* col = reinterpret_cast<const float4*>(slabs) + i;
-    float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = 0; g < groups; ++g) {
+  const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const float4* col = reinterpret_cast<const float4*>(slabs);
+  for (int64_t c0 = (int64_t)blockIdx.x * 16; c0 < n4; c0 += (int64_t)gridDim.x * 16) {
+    const int64_t i = c0 + c;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g < groups && i < n4) {
       const int64_t first = group_first(g, groups, nc), last = group_first(g + 1, groups, nc);
-      if (last == first) continue;
-      float4 acc = col[first * n4];
-#pragma unroll 8
-      for (int64_t c = first + 1; c < last; ++c) {
-        const float4 a = col[c * n4];
-        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+      if (last > first) {
+        acc = col[first * n4 + i];
+        for (int64_t k = first + 1; k < last; ++k) {
+          const float4 a = col[k * n4 + i];
+          acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+        }
       }
-      tot.x += acc.x; tot.y += acc.y; tot.z += acc.z; tot.w += acc.w;
     }
-    st8(dq + 4 * i, pack4(tot.x * scale, tot.y * scale, tot.z * scale, tot.w * scale));
+    part[g][c] = acc;
+    __syncthreads();
+    if (g == 0 && i < n4) {
+      float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int gg = 0; gg < groups; ++gg) {
+        if (group_first(gg + 1, groups, nc) == group_first(gg, groups, nc)) continue;
+        const float4 a = part[gg][c];
+        tot.x += a.x; tot.y += a.y; tot.z += a.z; tot.w += a.w;
+      }
+      st8(dq + 4 * i, pack4(tot.x * scale, tot.y * scale, tot.z * scale, tot.w * scale));
+    }
+    __syncthreads();
   }
 }
 
@@ -454,7 +469,7 @@ hipError_t launch_dq_seq_reduce(float* slabs, uint16_t* dq, int num_slabs, int64
                                 hipStream_t s) {
   if (slab_elems <= 0) return hipSuccess;
   const int groups = num_slabs < kReduceGroups ? num_slabs : kReduceGroups;
-  hipLaunchKernelGGL(dq_chunk_reduce_kernel, dim3(grid_for(slab_elems / 4, 128)), dim3(128), 0, s, slabs, dq,
+  hipLaunchKernelGGL(dq_chunk_reduce_kernel, dim3(grid_for(slab_elems / 4, 16)), dim3(256), 0, s, slabs, dq,
                      num_slabs, groups, slab_elems, scale);
   return hipGetLastError();
 }
