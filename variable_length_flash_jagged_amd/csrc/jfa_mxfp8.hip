@@ -93,40 +93,65 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(MxQuantParams p) {
   }
 }
 
-// V [T, H, D] bf16 -> codes [H][D][Tp] (keys of sequence b at vbase[b] .. + 64 ceil(L/64),
-// zero past L) and exponents + 127 [H][D][Tp/32].  2 D threads take one (64-key group,
-// head): thread (half, d) quantises keys 32 half .. + 31 of the group in dimension d, so
-// a wave's loads cover 64 neighbouring dimensions of one key row; the group's sequence
-// comes from the host-built map group_seq.
+// V [T, H, D] bf16 -> codes [H][D][tp] (transposed per head) + exponents
+// [H][D][tp/32]: one workgroup per (padded 64-key group, 256 / D heads).  The group's
+// key rows of those heads (adjacent in a token row) are loaded 16 bytes per lane into an
+// LDS tile [head][64 keys][D]; then lane (head, d) reads its dimension's 64 values down
+// the tile, forms the two 32-key blocks' exponents and writes its 64 code bytes (one
+// contiguous run of the transposed layout) and its two exponent bytes.  Keys past the
+// sequence's end are zero.
+template <int D>
 __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
-  const int H = p.num_heads, D = p.head_dim;
-  const int per = 2 * D, slots = 256 / per;
-  const int sub = threadIdx.x / per, t = threadIdx.x % per;
-  const int d = t % D, hf = t / D;
-  const int64_t ngroups = p.tp / kMxVPad;
-  for (int64_t gh = (int64_t)blockIdx.x * slots + sub; gh < ngroups * H; gh += (int64_t)gridDim.x * slots) {
-    const int64_t grp = gh / H;
-    const int h = (int)(gh - grp * H);
+  constexpr int HPW = 256 / D;  // heads per workgroup
+  constexpr int CPR = D / 8;    // 16-byte pieces per key row of one head
+  __shared__ __attribute__((aligned(16))) uint16_t tile[HPW * kMxVPad * D];
+  const int H = p.num_heads, t = threadIdx.x;
+  const int hgroups = (H + HPW - 1) / HPW;
+  const int64_t groups = p.tp / kMxVPad;
+  for (int64_t gh = blockIdx.x; gh < groups * hgroups; gh += gridDim.x) {
+    const int64_t grp = gh / hgroups;
+    const int h0 = (int)(gh - grp * hgroups) * HPW;
     const int b = p.group_seq[grp];
     const int64_t s0 = p.offsets[b];
-    const int L = (int)(p.offsets[b + 1] - s0);
-    const int64_t key0 = grp * kMxVPad + 32 * hf;  // padded token index of the block
-    const int j0 = (int)(key0 - p.vbase[b]);       // its first key inside the sequence
-    float v[32];
-    float amax = 0.f;
+    const int64_t j0 = grp * kMxVPad - p.vbase[b];
+    const int valid = (int)min<int64_t>(kMxVPad, p.offsets[b + 1] - s0 - j0);
+    __syncthreads();  // the previous group's readers are done with the tile
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int j = j0 + u;
-      v[u] = j < L ? __uint_as_float((uint32_t)p.x[((s0 + j) * H + h) * D + d] << 16) : 0.f;
-      amax = fmaxf(amax, fabsf(v[u]));
+    for (int r = 0; r < (HPW * kMxVPad * CPR) / 256; ++r) {
+      const int q = t + 256 * r;
+      const int j = q / (HPW * CPR), rem = q % (HPW * CPR);
+      const int hh = rem / CPR, c8 = rem % CPR;
+      u32x4 w = zero16();
+      if (j < valid && h0 + hh < H) w = ld16(p.x + ((s0 + j0 + j) * H + h0 + hh) * D + 8 * c8);
+      *reinterpret_cast<u32x4*>(&tile[(hh * kMxVPad + j) * D + 8 * c8]) = w;
     }
-    const int x = mx_exponent(amax);
-    uint32_t q[8];
-    quantise32(v, x, q);
-    u32x4* dst = reinterpret_cast<u32x4*>(p.codes + ((int64_t)h * D + d) * p.tp + key0);
-    dst[0] = u32x4{q[0], q[1], q[2], q[3]};
-    dst[1] = u32x4{q[4], q[5], q[6], q[7]};
-    p.scales[((int64_t)h * D + d) * (p.tp / 32) + key0 / 32] = (uint8_t)(x + 127);
+    __syncthreads();
+    const int hh = t / D, d = t % D;
+    if (h0 + hh < H) {
+      const int64_t row = (int64_t)(h0 + hh) * D + d;
+      uint32_t q[16];
+      int xs[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float v[32];
+        float amax = 0.f;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          v[u] = __uint_as_float((uint32_t)tile[(hh * kMxVPad + 32 * half + u) * D + d] << 16);
+          amax = fmaxf(amax, fabsf(v[u]));
+        }
+        xs[half] = mx_exponent(amax);
+        uint32_t qq[8];
+        quantise32(v, xs[half], qq);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) q[8 * half + w] = qq[w];
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(p.codes + row * p.tp + grp * kMxVPad);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = u32x4{q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]};
+      *reinterpret_cast<uint16_t*>(p.scales + row * (p.tp / 32) + 2 * grp) =
+          (uint16_t)((xs[0] + 127) | ((xs[1] + 127) << 8));
+    }
   }
 }
 
@@ -457,7 +482,13 @@ hipError_t launch_mx_quant_qk(const MxQuantParams& p, hipStream_t s) {
 }
 
 hipError_t launch_mx_quant_v(const MxQuantParams& p, hipStream_t s) {
-  return grid_launch(quant_v_kernel, p, (p.tp / kMxVPad) * p.num_heads * 2 * p.head_dim, s);
+  const int hpw = 256 / p.head_dim;
+  const int64_t work = (p.tp / kMxVPad) * ((p.num_heads + hpw - 1) / hpw);
+  if (work <= 0) return hipSuccess;
+  const dim3 grid((unsigned)std::min<int64_t>(work, 16384));
+  if (p.head_dim == 64) hipLaunchKernelGGL(quant_v_kernel<64>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(quant_v_kernel<128>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_dequant_qk(const MxDequantParams& p, hipStream_t s) {
