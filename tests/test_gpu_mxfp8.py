@@ -192,3 +192,36 @@ def test_mxfp8_backward_stored_ds_path_and_production_lengths():
     off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     opts = B.make_opts(sched=1, ds_budget_mib=B.ds_budget_mib(shape, off))
     _run_bwd(lengths, 2, 128, seed=75, opts=opts, label="stored dS, production lengths, 24 sequences")
+
+
+def test_mxfp8_backward_full_workload_sampled():
+    """Workload 9's backward at full size in the launch configuration bench.py times
+    (run-time schedule, stored-dS path); sampled sequences against the oracle's gradient
+    at the decoded inputs (each sequence's gradient depends on that sequence only)."""
+    print("[case] mxfp8 backward full-size workload 9", flush=True)
+    p = W.make_workload(9, seed=0, device="cuda")
+    shape = B.make_shape(p["num_seqs"], p["num_heads"], p["head_dim"], p["total_tokens"])
+    opts = B.bench_opts(W.MODE_SELF, shape, p["offsets_host"])
+    q8, qs = B.mxfp8_quantize_qk(p["q"])
+    k8, ks = B.mxfp8_quantize_qk(p["k"])
+    v8, vs, tp = B.mxfp8_quantize_v(p["v"], p["offsets"], p["offsets_host"])
+    o, lse = B.fwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, p["offsets"], p["offsets_host"], p["scale"], opts)
+    dq, dk, dv = B.bwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, o, p["do"], lse, p["offsets"], p["offsets_host"],
+                             p["scale"], opts, G.nan_like(p["q"]), G.nan_like(p["k"]), G.nan_like(p["v"]))
+    torch.cuda.synchronize()
+    off = p["offsets_host"].astype(np.int64)
+    order = np.argsort(p["lengths"], kind="stable")
+    vb = _vbase(p["lengths"])
+    d = p["head_dim"]
+    for b in sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]), 29, 900}):
+        s, e = int(off[b]), int(off[b + 1])
+        n = e - s
+        qd = M.dequantise_qk(M.e4m3_decode(q8[s:e].cpu().numpy()), qs[s:e].cpu().numpy().astype(np.int64) - 127)
+        kd = M.dequantise_qk(M.e4m3_decode(k8[s:e].cpu().numpy()), ks[s:e].cpu().numpy().astype(np.int64) - 127)
+        vcodes = v8[:, :, vb[b]:vb[b] + n].cpu().numpy()
+        vx = vs[:, :, vb[b] // 32:vb[b] // 32 + -(-n // 32)].cpu().numpy().astype(np.float64) - 127
+        vd = (M.e4m3_decode(vcodes) * np.exp2(np.repeat(vx, 32, axis=2)[:, :, :n])).transpose(2, 0, 1)
+        refs = M.mxfp8_backward(qd, kd, vd, G.f64(p["do"][s:e]), [0, n], p["scale"], o_given=G.f64(o[s:e]))
+        G.check_bwd((dq[s:e], dk[s:e], dv[s:e]), refs, f"workload 9 bwd seq {b} (L={n})",
+                    {"offsets_host": [0, n], "mode": W.MODE_SELF}, refs)
+    assert d == 128
