@@ -19,8 +19,9 @@
 //  * Ping-pong between the two waves of each SIMD.  Waves w and w+4 of a workgroup are
 //    placed on the same SIMD; waves 0-3 (group A, rows 0-127) and 4-7 (group B, rows
 //    128-255) run the same sequence of phases one phase apart: a matrix phase
-//    (O += V(i-1) P(i-1), then S(i) = K(i) Q^T) and a vector phase (row max, lazy
-//    rescale, P(i) = 2^(S(i) c - m c), row sums).  Workgroup barriers between phases
+//    (O += V(i-1) P(i-1) and S(i) = K(i) Q^T, their MFMAs alternating) and a vector
+//    phase (row max, lazy rescale, P(i) = 2^(S(i) c - m c), row sums).  Workgroup
+//    barriers between phases
 //    keep the offset, so on every SIMD one wave feeds the matrix core while the other
 //    keeps the vector unit busy (the producer / consumer overlap of matrix and softmax
 //    work the TLX page describes for its forward pipeline, section 3.2, Fig. 1, mapped
@@ -86,25 +87,6 @@ struct FwdWave {
   float m, l;            // running max (raw score units) and sum
 };
 
-// Issue order of the matrix phase: the operands of the first kAhead MFMAs, then every
-// MFMA followed by the LDS reads of the operand kAhead MFMAs later (2 transposed reads
-// per V^T operand, 1 row read per K operand), so that each read has several MFMAs'
-// time to land and only a few operands occupy registers.
-template <int D>
-__device__ __forceinline__ void order_matrix_phase() {
-  using C = FwdCfg<D>;
-  constexpr int kAhead = 4;
-  constexpr int NPV = C::NT16 * C::NDB, NSK = C::NKS * C::NKB;
-  static_assert(NPV >= kAhead, "prefetch window inside the PV product");
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-  for (int k = 0; k < NPV + NSK; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (k + kAhead < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    else if (k + kAhead < NPV + NSK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
 template <int D>
 __device__ __forceinline__ void pin_vector_phase(FwdWave<D>& w) {
 #pragma unroll
@@ -146,6 +128,47 @@ __device__ __forceinline__ void mma_s(const JFA_LDS char* kbuf, const FwdLane<D>
   for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) w.s[kb] = mfma32(ln.krow.read(kbuf, kb * 32, ks), w.qf[ks], w.s[kb]);
+}
+
+// Steady-state matrix phase: O^T += V^T P^T (previous tile) and S^T = K Q^T (this tile)
+// with their MFMAs alternating, so that the LDS reads behind them (two transposed reads
+// per PV operand, one row read per K operand) arrive at an even 1.5 per MFMA instead of
+// two per MFMA through the first half of the phase.
+template <int D>
+__device__ __forceinline__ void mma_pv_s(const JFA_LDS char* kbuf, const JFA_LDS char* vbuf, const FwdLane<D>& ln,
+                                         FwdWave<D>& w) {
+  using C = FwdCfg<D>;
+  constexpr int NPV = C::NT16 * C::NDB, NSK = C::NKS * C::NKB;
+  static_assert(NPV == NSK, "PV and S products alternate one for one");
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w.s[kb][i] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) {
+    const int t = k / C::NDB, db = k % C::NDB;
+    w.o[db] = mfma32(ln.vtr.read(vbuf, 16 * t, db), w.pf[t], w.o[db]);
+    const int ks = k / C::NKB, kb = k % C::NKB;
+    w.s[kb] = mfma32(ln.krow.read(kbuf, kb * 32, ks), w.qf[ks], w.s[kb]);
+  }
+}
+
+// Issue order of mma_pv_s: operands of the first kAhead MFMAs, then each MFMA followed
+// by the reads of the operand kAhead MFMAs later (even positions PV: two reads; odd: S).
+template <int D>
+__device__ __forceinline__ void order_mixed_phase() {
+  using C = FwdCfg<D>;
+  constexpr int kAhead = 4;
+  constexpr int N = 2 * C::NT16 * C::NDB;
+  __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAhead / 2, 0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k + kAhead < N) {
+      if ((k + kAhead) % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
 }
 
 // Vector phase for one key tile: mask (tail tile only), row max, lazy rescale,
@@ -384,9 +407,8 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
       mat_off = adv(mat_off);
       const JFA_LDS char* slot_p = smem + mat_off;
       __builtin_amdgcn_s_setprio(2);
-      mma_pv<D>(slot_p + C::TILE, ln, w);
-      mma_s<D>(slot_p, ln, w);
-      order_matrix_phase<D>();
+      mma_pv_s<D>(slot_p, slot_p + C::TILE, ln, w);
+      order_mixed_phase<D>();
       pin_matrix_phase<D>(w);
       __builtin_amdgcn_s_setprio(0);
       end_phase();
