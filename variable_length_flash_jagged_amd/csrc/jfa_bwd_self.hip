@@ -1268,8 +1268,8 @@ __global__ void __launch_bounds__(256) prep_kernel(BwdParams p) {
     st16(p.row_aug + H * T * 8, __builtin_bit_cast(u32x4, t));
   }
   for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; r < rows; r += (int64_t)gridDim.x * RPB) {
-    const bf16x8 o8 = as_bf16x8(ld16(p.o + r * D + 8 * sub));
-    const bf16x8 d8 = as_bf16x8(ld16(p.dout + r * D + 8 * sub));
+    const bf16x8 o8 = as_bf16x8(ld16_nt(p.o + r * D + 8 * sub));
+    const bf16x8 d8 = as_bf16x8(ld16_nt(p.dout + r * D + 8 * sub));
     float di = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) di = fmaf((float)d8[e], (float)o8[e], di);
@@ -1354,6 +1354,7 @@ __device__ __forceinline__ bf16x8 mask_keys(const bf16x8& b, int t, int half, in
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// One 64-key step (MASK: the tail step of a sequence, keys past keys_valid zeroed).
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_ds_step(const JFA_LDS char* kbuf, const JFA_LDS char* slice, const DsLane<D>& ln,
                                            f32x16 (&acc)[DsCfg<D>::NDB], int half, int keys_valid, int cb) {
@@ -1398,7 +1399,7 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int o = w2 * 4096 + cb * 2048 + c * 1024;
-          dma16(src, (uint32_t)(o + lane * 16), dst + o);
+          dma16_nt(src, (uint32_t)(o + lane * 16), dst + o);  // dS is read once
         }
     }
   };
@@ -1423,18 +1424,21 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
     wait_vmem();
   }
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
+  // Full steps in the loop, the tail step (if any) after it: one instruction path per
+  // loop body, so the accumulators stay in the same registers from step to step (a
+  // full / tail branch inside the body made the compiler copy all 64 accumulator
+  // registers out and back at every step).
+  auto step = [&](int kb, auto mask) {
     if (kb + 2 < nkb) issue(kb + 2);
     const JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
-    const int kv = L - kb * C::BK;
-    if (live) {
-      if (kv >= C::BK) dq_ds_step<D, false>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, C::BK, cb);
-      else dq_ds_step<D, true>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, kv, cb);
-    }
+    if (live) dq_ds_step<D, decltype(mask)::value>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, L - kb * C::BK, cb);
     if (kb + 2 < nkb) wait_one_behind();
     else wait_vmem();
     __syncthreads();
-  }
+  };
+  const int nfull = L / C::BK;
+  for (int kb = 0; kb < nfull; ++kb) step(kb, std::false_type{});
+  if (nfull < nkb) step(nfull, std::true_type{});
 
   // dQ^T C layout: register i <-> head-dim element 32db + 8(i/4) + 4 half + i%4, lane
   // l32 <-> query row 64 pair + 32 cb + l32 of the tile.
