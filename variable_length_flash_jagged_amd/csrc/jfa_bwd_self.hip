@@ -1028,21 +1028,31 @@ struct Kv2Stream {
 template <bool STORE>
 constexpr int kv2_ahead() { return STORE ? 3 : 2; }
 
+// Row stores of one gradient per thread (a 128-key tile of 16-byte chunks over the
+// eight waves) and per tile (dK, then dV), at the end of a dK/dV tile.
+template <int D>
+constexpr int kv2_store_passes() { return Kv2Cfg<D>::BN * Kv2Cfg<D>::RB / 16 / (Kv2Cfg<D>::NW * 64); }
+template <int D>
+constexpr int kv2_stores() { return 2 * kv2_store_passes<D>(); }
+
 // Geometry of one dK/dV tile.
 struct Kv2Tile {
   int h, j, L, key0, keys, n;
   int64_t s0, b;
 };
 
+// Tile idx (wave-uniform) of the list, through scalar loads: at the end of a tile a
+// vector load would wait for the last step's dS stores.
 template <int D>
-__device__ __forceinline__ Kv2Tile kv2_tile_of(const BwdParams& p, Tile t) {
+__device__ __forceinline__ Kv2Tile kv2_tile_at(const BwdParams& p, int idx) {
   using C = Kv2Cfg<D>;
+  const Tile t = ld_uniform(p.tiles, __builtin_amdgcn_readfirstlane(idx));
   Kv2Tile x;
   x.b = t.b;
   x.h = t.hb >> 24;
   x.j = t.hb & 0xFFFFFF;
-  x.s0 = p.offsets[t.b];
-  x.L = (int)(p.offsets[t.b + 1] - x.s0);
+  x.s0 = ld_uniform(p.offsets, t.b);
+  x.L = ld_uniform(p.offsets, t.b + 1) - (int)x.s0;
   x.key0 = x.j * C::BN;
   x.keys = min(C::BN, x.L - x.key0);
   x.n = (x.L + C::QB - 1) / C::QB;
@@ -1116,11 +1126,11 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
     idx = base + prog % gsize;
   }
   if (idx >= end) return;
-  Kv2Tile x = kv2_tile_of<D>(p, p.tiles[idx]);
+  Kv2Tile x = kv2_tile_at<D>(p, idx);
   kv2_issue_kv<D>(p, ln, x, smem, wave, lane);
   kv2_issue_step<D>(p, ln, x, 0, 1, smem, wave, lane);
-  // store instructions this wave issued for the previous tile's dK, dV, after this
-  // tile's copies (wave-uniform)
+  // set once a tile's dK, dV row stores were issued (kv2_stores() per wave, after the
+  // next tile's copies)
   int stores = 0;
   while (true) {
     // reserve the next tile
@@ -1131,9 +1141,9 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
       nxt = next_tile;
     }
     if (tid == 0) count_visit(p.visits, idx);
-    // this tile's K, V and first step have landed (group 0's dK, dV stores of the
-    // previous tile, issued after them, may still be in flight)
-    if (stores) wait_vmem_upto<4 * C::NDB>();
+    // this tile's K, V and first step have landed (the previous tile's dK, dV row
+    // stores, issued after them, may still be in flight)
+    if (stores) wait_vmem_upto<kv2_stores<D>()>();
     else wait_vmem();
     __syncthreads();
     {
@@ -1186,13 +1196,13 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
     const bool more = nxt < end;
     Kv2Tile y = x;
     if (more) {
-      y = kv2_tile_of<D>(p, p.tiles[nxt]);
+      y = kv2_tile_at<D>(p, nxt);
       kv2_issue_kv<D>(p, ln, y, smem, wave, lane);
       kv2_issue_step<D>(p, ln, y, 0, 1, smem, wave, lane);
     }
     // The groups swap partials through ring slot 0, a quarter at a time: group 1 hands
     // its dK partials to group 0 (parts 0, 1: head-dim blocks 0-1, 2-3) and group 0 its
-    // dV partials to group 1 (parts 2, 3); then group 0 stores dK and group 1 dV.
+    // dV partials to group 1 (parts 2, 3); group 0 then holds the tile's dK, group 1 dV.
     {
       JFA_LDS char* red = smem;
 #pragma unroll
@@ -1226,23 +1236,47 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
         __syncthreads();
       }
     }
-    const int my_key = 32 * kw + l32;
-    // wave-uniform: the store block runs when the wave's first key exists (lane l32 = 0)
-    stores = 32 * kw < x.keys ? 4 * C::NDB : 0;
-    if (stores) {
-      if (my_key < x.keys) {
-        const int64_t row = (x.s0 + x.key0 + my_key) * rs + (int64_t)x.h * D + 4 * half;
-        uint16_t* dst = (g == 0 ? p.dk : p.dv) + row;
-        const f32x16(&a)[C::NDB] = g == 0 ? dk : dv;
-        const float sc = g == 0 ? p.scale : 1.0f;
+    // Stores: group 0's dK (times scale), then group 1's dV, go as bf16 rows through ring
+    // slot 0 ([key][D], rows RB + 8 bytes apart, so that the 32 keys of one write land in
+    // distinct banks), and all eight waves write whole rows with 16-byte stores (16 lanes
+    // per 256-byte row) instead of every lane writing 8-byte pieces of its own key's row.
+    // Rows past the tile's keys repeat its last row (same address, same value), so every
+    // wave issues kv2_stores() stores.
+    {
+      constexpr int PITCH = C::RB + 8;
+      static_assert(C::BN * PITCH <= C::SLOT, "staging rows inside ring slot 0");
+      JFA_LDS char* stg = smem;
+      // lane-dependent offsets from an opaque copy of the thread id, computed here: hoisted
+      // out of the tile loop they would stay live through the steps and spill
+      int tl = tid;
+      asm volatile("" : "+v"(tl));
+      const int wbase = (32 * ((tl >> 6) & 3) + (tl & 31)) * PITCH + 8 * ((tl >> 5) & 1);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+      for (int r = 0; r < 2; ++r) {
+        if (g == r) {
+          const f32x16(&a)[C::NDB] = r == 0 ? dk : dv;
+          const float sc = r == 0 ? p.scale : 1.0f;
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            st8(dst + 32 * db + 8 * g4,
-                pack4(a[db][4 * g4] * sc, a[db][4 * g4 + 1] * sc, a[db][4 * g4 + 2] * sc, a[db][4 * g4 + 3] * sc));
+          for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              lds_st8(stg + 64 * db + 16 * g4, wbase,
+                      pack4(a[db][4 * g4] * sc, a[db][4 * g4 + 1] * sc, a[db][4 * g4 + 2] * sc, a[db][4 * g4 + 3] * sc));
+        }
+        __syncthreads();
+        uint16_t* dst = (r == 0 ? p.dk : p.dv) + (x.s0 + x.key0) * rs + (int64_t)x.h * D;
+#pragma unroll
+        for (int k = 0; k < kv2_store_passes<D>(); ++k) {
+          const int q = tl + C::NW * 64 * k;
+          const int row = min(q / (C::RB / 16), x.keys - 1), cc = q % (C::RB / 16);
+          const int ro = row * PITCH + 16 * cc;
+          const u32x2 lo = lds_ld8(stg, ro), hi = lds_ld8(stg, ro + 8);
+          st16(dst + (int64_t)row * rs + 8 * cc, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+        __syncthreads();
       }
     }
+    stores = 1;
     if (!more) break;
     idx = nxt;
     x = y;

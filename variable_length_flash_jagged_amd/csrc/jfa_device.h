@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace jfa {
 
 typedef __bf16 bf16;
@@ -70,6 +72,22 @@ __device__ __forceinline__ void lds_st16(JFA_LDS char* base, int byte_off, const
 }
 __device__ __forceinline__ void lds_st8(JFA_LDS char* base, int byte_off, const u32x2& v) {
   *reinterpret_cast<JFA_LDS u32x2*>(base + byte_off) = v;
+}
+__device__ __forceinline__ u32x2 lds_ld8(const JFA_LDS char* base, int byte_off) {
+  return *reinterpret_cast<const JFA_LDS u32x2*>(base + byte_off);
+}
+
+// Element i (wave-uniform) of a read-only array through the scalar cache: a load from
+// the constant address space, so that it becomes a scalar load, whose completion is
+// counted by lgkmcnt and does not wait for the wave's outstanding vector-memory
+// operations (a vector load's vmcnt wait would).  The array must not be written while
+// the kernel runs.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* a, int64_t i) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "one or two dwords");
+  using W = typename std::conditional<sizeof(T) == 4, uint32_t, uint64_t>::type;
+  const W w = ((const __attribute__((address_space(4))) W*)a)[i];
+  return __builtin_bit_cast(T, w);
 }
 
 // A pointer the whole wave agrees on, moved to scalar registers.
