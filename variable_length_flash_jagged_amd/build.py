@@ -40,8 +40,10 @@ HIP_FLAGS = [
 # compiler would otherwise put every MFMA result in accumulation registers and copy
 # the scores out for the vector work (and the accumulators back and forth) on every
 # step; the VGPR form keeps scores in VGPRs and uses the accumulation registers only
-# for values that do not fit.
-EXTRA_FLAGS = {"jfa_bwd_self.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# for values that do not fit.  The atomic optimizer is off there: its rewrite of the
+# single-lane tile reservation reads the result at once (a vmcnt(0) wait that also waits
+# for every copy in flight), where the kernels consume it a whole tile later.
+EXTRA_FLAGS = {"jfa_bwd_self.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _hipcc():

@@ -1402,28 +1402,97 @@ __device__ __forceinline__ void dq_ds_step(const JFA_LDS char* kbuf, const JFA_L
   }
 }
 
+// Geometry of one dQ tile as one wave sees it (all wave-uniform), from scalar loads of
+// the tile list and the sequence tables.
 template <int D>
-__device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LDS char* smem, const DsLane<D>& ln,
-                                           int tid) {
+struct DsGeo {
   using C = DsCfg<D>;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int b = tile.b, h = tile.hb >> 24, blk = tile.hb & 0xFFFFFF;
-  const int64_t rs = (int64_t)p.num_heads * D;
-  const int64_t s0 = p.offsets[b];
-  const int L = (int)(p.offsets[b + 1] - s0);
-  const int nq = (L + kBwdRows - 1) / kBwdRows, nj = (L + kBwdKeys - 1) / kBwdKeys;
-  const int pair = wave >> 1, cb = wave & 1;
-  const int it = blk * (C::BM / kBwdRows) + pair;  // this wave's stored block column
-  const bool live = it < nq;                       // wave-uniform: rows past the end only
-  const int nkb = (L + C::BK - 1) / C::BK;
-  const uint16_t* kp = p.k + s0 * rs + (int64_t)h * D;
-  const uint32_t rsb = (uint32_t)(rs * 2);
-  // block (j, it) of this (b, h) is at ds_col + j * nq blocks
-  const char* ds_col = p.ds + (p.ds_base[b] + (int64_t)h * nj * nq + it) * kDsBlockBytes;
+  // (no padding bytes: a copy of a struct with padding kept those bytes in memory)
+  int64_t s0;
+  const uint16_t* kp;     // K rows of the sequence, head h
+  const char* ds_col;     // block (j, it) of this (b, h) is at ds_col + j * nq blocks
+  int L, nq, nkb, h, blk;
+  int live;               // this wave's stored block column has rows (rows past the end only)
+  __device__ __forceinline__ void init(const BwdParams& p, int idx, int wave) {
+    const Tile t = ld_uniform(p.dq_tiles, __builtin_amdgcn_readfirstlane(idx));
+    const int b = t.b;
+    h = t.hb >> 24;
+    blk = t.hb & 0xFFFFFF;
+    s0 = ld_uniform(p.offsets, b);
+    L = ld_uniform(p.offsets, b + 1) - (int)s0;
+    nq = (L + kBwdRows - 1) / kBwdRows;
+    const int nj = (L + kBwdKeys - 1) / kBwdKeys;
+    const int it = blk * (C::BM / kBwdRows) + (wave >> 1);  // this wave's stored block column
+    live = it < nq ? 1 : 0;
+    nkb = (L + C::BK - 1) / C::BK;
+    const int64_t rs = (int64_t)p.num_heads * D;
+    kp = p.k + s0 * rs + (int64_t)h * D;
+    ds_col = p.ds + (ld_uniform(p.ds_base, b) + (int64_t)h * nj * nq + it) * kDsBlockBytes;
+  }
+  // vector-memory instructions one wave issues for one step
+  __device__ __forceinline__ int step_copies() const { return C::Copy::J + (live ? C::SLICE_COPIES : 0); }
+};
 
-  auto issue = [&](int kb) {
-    JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
+// s_waitcnt vmcnt(m) for the largest even m <= n (n < 16): at most n of the wave's
+// vector-memory instructions stay outstanding (fewer is never wrong).
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  if (n >= 14) wait_vmem_n<14>();
+  else if (n >= 12) wait_vmem_n<12>();
+  else if (n >= 10) wait_vmem_n<10>();
+  else if (n >= 8) wait_vmem_n<8>();
+  else if (n >= 6) wait_vmem_n<6>();
+  else if (n >= 4) wait_vmem_n<4>();
+  else if (n >= 2) wait_vmem_n<2>();
+  else wait_vmem();
+}
+
+// Persistent loop of the dQ-from-dS kernel.  The next tile is reserved one tile ahead
+// (static list or run-time counter) and its first two steps are copied during the
+// current tile's last two steps, into the ring slots that follow (the ring runs on
+// across tiles), so a tile start waits for no memory round trip.  The tile's dQ rows go
+// out through LDS (two halves of 128 rows, each in the ring slot the last step freed)
+// as whole 16-byte row pieces, instead of each lane writing 8-byte pieces of its own
+// row.  Waits count exactly the wave's vector-memory instructions issued after the step
+// that must have landed (copies of later steps, the previous tile's dQ stores).
+template <int D>
+__global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    dq_ds_kernel(BwdParams p) {
+  using C = DsCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::SMEM];
+  __shared__ int next_tile;
+  JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int pair = wave >> 1, cb = wave & 1;
+  const int64_t rs = (int64_t)p.num_heads * D;
+  const uint32_t rsb = (uint32_t)(rs * 2);
+  DsLane<D> ln;
+  ln.ktr.init(lane);
+  ln.copy.init(rsb, wave, lane);
+  ln.init(lane);
+
+  const int prog = xcd_program_id(blockIdx.x, gridDim.x);
+  const int gsize = xcd_gsize(), grp = prog / gsize;
+  int idx, end, base = 0;
+  if (!p.dynamic) {
+    idx = p.dq_seg_ptr[prog];
+    end = p.dq_seg_ptr[prog + 1];
+  } else {
+    base = p.dq_seg_ptr[grp];
+    end = p.dq_seg_ptr[grp + 1];
+    idx = base + prog % gsize;
+  }
+  if (idx >= end) return;
+
+  constexpr int LAST = (C::NS - 1) * C::STAGE;
+  auto adv = [](int off) { return off == LAST ? 0 : off + C::STAGE; };
+  // Step kb of a tile (its K rows kp, L keys, dS column ds_col of nq blocks, live:
+  // this wave copies dS) into the ring slot at byte offset off.  (Fields passed by value:
+  // a reference chosen at run time between two tiles' geometries would put them in
+  // scratch memory.)
+  auto issue = [&](const uint16_t* kp, int L, int live, const char* ds_col, int nq, int kb, int off) {
+    JFA_LDS char* st = smem + off;
     ln.copy.issue_rows(kp + (int64_t)kb * C::BK * rs, rsb, min(C::BK, L - kb * C::BK), st, wave, lane);
     if (live) {
       const void* src = uniform_ptr(ds_col + ((int64_t)(kb >> 1) * nq * kDsBlockBytes + (kb & 1) * C::SLICE));
@@ -1437,70 +1506,131 @@ __device__ __forceinline__ void dq_ds_tile(const BwdParams& p, Tile tile, JFA_LD
         }
     }
   };
-  // Wait until at most the copies of one more step are outstanding (vector-memory
-  // returns are in order, so the older step has landed).
-  auto wait_one_behind = [&]() {
-    if (live) wait_vmem_n<C::Copy::J + C::SLICE_COPIES>();
-    else wait_vmem_n<C::Copy::J>();
-  };
 
-  f32x16 acc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-
-  issue(0);
-  if (nkb > 1) {
-    issue(1);
-    wait_one_behind();
-  } else {
-    wait_vmem();
+  // Steps are numbered in one sequence across tiles: the current tile's steps 0 .. nkb - 1,
+  // then the next tile's.  Position kb + 2 is copied at the start of step kb (ring slot
+  // of position q: q mod NS); the next tile's steps from 2 on are copied by its own loop.
+  DsGeo<D> cur;
+  cur.init(p, idx, wave);
+  if (p.dynamic && tid == 0) next_tile = base + gsize + atomicAdd(p.counters + kDqCounter + grp, 1);
+  int cur_off = 0, iss_off = 0;
+  int issued = 0;      // positions copied so far (relative to the current tile's step 0)
+  int last_copies = 0; // the wave's copy instructions of position issued - 1
+  int stores_at = -1;  // the previous tile's dQ stores were issued after position stores_at
+  int stores = 0;      // ... and their number
+  issue(cur.kp, cur.L, cur.live, cur.ds_col, cur.nq, 0, iss_off);
+  iss_off = adv(iss_off);
+  issued = 1;
+  last_copies = cur.step_copies();
+  if (cur.nkb > 1) {
+    issue(cur.kp, cur.L, cur.live, cur.ds_col, cur.nq, 1, iss_off);
+    iss_off = adv(iss_off);
+    issued = 2;
   }
+  wait_vmem_le(issued == 2 ? last_copies : 0);  // position 0 has landed
   __syncthreads();
-  // Full steps in the loop, the tail step (if any) after it: one instruction path per
-  // loop body, so the accumulators stay in the same registers from step to step (a
-  // full / tail branch inside the body made the compiler copy all 64 accumulator
-  // registers out and back at every step).
-  auto step = [&](int kb, auto mask) {
-    if (kb + 2 < nkb) issue(kb + 2);
-    const JFA_LDS char* st = smem + (kb % C::NS) * C::STAGE;
-    if (live) dq_ds_step<D, decltype(mask)::value>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, L - kb * C::BK, cb);
-    if (kb + 2 < nkb) wait_one_behind();
-    else wait_vmem();
-    __syncthreads();
-  };
-  const int nfull = L / C::BK;
-  for (int kb = 0; kb < nfull; ++kb) step(kb, std::false_type{});
-  if (nfull < nkb) step(nfull, std::true_type{});
 
-  // dQ^T C layout: register i <-> head-dim element 32db + 8(i/4) + 4 half + i%4, lane
-  // l32 <-> query row 64 pair + 32 cb + l32 of the tile.
-  {
-    const int row = blk * C::BM + pair * 64 + cb * 32 + l32;
-    if (row < L) {
-      uint16_t* qp = p.dq + (s0 + row) * rs + (int64_t)h * D + 4 * half;
+  while (true) {
+    if (tid == 0) count_visit(p.dq_visits, idx);
+    const int nidx = p.dynamic ? next_tile : idx + 1;  // written before the barrier above
+    const bool more = nidx < end;
+    DsGeo<D> nx = cur;
+    if (more) nx.init(p, nidx, wave);
+    // reserve the tile after the next one now (every wave has read next_tile); its
+    // number goes to next_tile before the tile's last barrier, so that the atomic's round
+    // trip overlaps the whole tile
+    // (the raw counter value, set and read under the same condition: no copy of it at
+    // the branch join, which would wait for the atomic right away)
+    const bool reserve = more && p.dynamic && tid == 0;
+    int ticket;
+    if (reserve) ticket = atomicAdd(p.counters + kDqCounter + grp, 1);
+    const int limit = cur.nkb + (more ? min(2, nx.nkb) : 0);  // positions this tile's loop copies
+
+    f32x16 acc[C::NDB];
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          st8(qp + 32 * db + 8 * g4, pack4(acc[db][4 * g4] * p.scale, acc[db][4 * g4 + 1] * p.scale,
-                                          acc[db][4 * g4 + 2] * p.scale, acc[db][4 * g4 + 3] * p.scale));
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+    // Full steps in the loop, the tail step (if any) after it: one instruction path per
+    // loop body, so the accumulators stay in the same registers from step to step (a
+    // full / tail branch inside the body made the compiler copy all 64 accumulator
+    // registers out and back at every step).
+    auto step = [&](int kb, auto mask) {
+      // copy positions up to kb + 2 (two at a tile's first step when its predecessor
+      // could copy only one)
+      for (int rep = 0; rep < 2 && issued <= kb + 2 && issued < limit; ++rep) {
+        const bool in_cur = issued < cur.nkb;
+        issue(in_cur ? cur.kp : nx.kp, in_cur ? cur.L : nx.L, in_cur ? cur.live : nx.live,
+              in_cur ? cur.ds_col : nx.ds_col, in_cur ? cur.nq : nx.nq, in_cur ? issued : issued - cur.nkb, iss_off);
+        last_copies = in_cur ? cur.step_copies() : nx.step_copies();
+        iss_off = adv(iss_off);
+        ++issued;
+      }
+      const JFA_LDS char* st = smem + cur_off;
+      if (cur.live)
+        dq_ds_step<D, decltype(mask)::value>(st, st + C::KBUF + pair * C::SLICE, ln, acc, half, cur.L - kb * C::BK,
+                                             cb);
+      // position kb + 1 must have landed; issued after it: position kb + 2's copies (if
+      // copied yet) and the previous tile's dQ stores (if issued after it)
+      wait_vmem_le((issued - 1 == kb + 2 ? last_copies : 0) + (kb + 1 <= stores_at ? stores : 0));
+      __syncthreads();
+      cur_off = adv(cur_off);
+    };
+    const int nfull = cur.L / C::BK;
+    for (int kb = 0; kb < nfull; ++kb) step(kb, std::false_type{});
+    if (nfull < cur.nkb) step(nfull, std::true_type{});
+
+    // dQ rows through the slot the last step used (the slot before cur_off): half r =
+    // tile rows 128 r .. 128 r + 127 (waves 4 r .. 4 r + 3) as bf16 [row][D], rows RB + 8
+    // bytes apart so that the 32 rows of one write land in distinct banks.  Rows past
+    // the sequence repeat the half's last row (same address, same value).
+    stores = 0;
+    {
+      constexpr int PITCH = C::RB + 8, HALF_ROWS = C::BM / 2;
+      static_assert(HALF_ROWS * PITCH <= C::STAGE, "staging rows inside one ring slot");
+      constexpr int PASSES = HALF_ROWS * (C::RB / 16) / (C::NW * 64);
+      JFA_LDS char* stg = smem + (cur_off == 0 ? LAST : cur_off - C::STAGE);
+      int tl = tid;
+      asm volatile("" : "+v"(tl));  // computed here, not hoisted and kept live through the steps
+      const int wrow = (tl >> 6 >> 1 & 1) * 64 + (tl >> 6 & 1) * 32 + (tl & 31);  // row within the half
+      const int wbase = wrow * PITCH + 8 * ((tl >> 5) & 1);
+      const int row0 = cur.blk * C::BM;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int valid = min(HALF_ROWS, cur.L - row0 - HALF_ROWS * r);  // rows of this half
+        if (valid <= 0) break;                                         // workgroup-uniform
+        if ((wave >> 2) == r) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              lds_st8(stg + 64 * db + 16 * g4, wbase,
+                      pack4(acc[db][4 * g4] * p.scale, acc[db][4 * g4 + 1] * p.scale, acc[db][4 * g4 + 2] * p.scale,
+                            acc[db][4 * g4 + 3] * p.scale));
+        }
+        __syncthreads();
+        uint16_t* dst = p.dq + (cur.s0 + row0 + HALF_ROWS * r) * rs + (int64_t)cur.h * D;
+#pragma unroll
+        for (int k = 0; k < PASSES; ++k) {
+          const int q = tl + C::NW * 64 * k;
+          const int row = min(q / (C::RB / 16), valid - 1), cc = q % (C::RB / 16);
+          const int ro = row * PITCH + 16 * cc;
+          const u32x2 lo = lds_ld8(stg, ro), hi = lds_ld8(stg, ro + 8);
+          st16(dst + (int64_t)row * rs + 8 * cc, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+        stores += PASSES;
+        if (r == 0 && reserve) next_tile = base + gsize + ticket;
+        __syncthreads();
+      }
     }
+    if (!more) break;
+    // renumber from the next tile's step 0 (landed: awaited at the last step)
+    issued -= cur.nkb;
+    stores_at = issued - 1;
+    idx = nidx;
+    cur = nx;
   }
-}
-
-template <int D>
-__global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-    dq_ds_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[DsCfg<D>::SMEM];
-  __shared__ int next_tile;
-  DsLane<D> ln;
-  ln.ktr.init(threadIdx.x & 63);
-  ln.copy.init((uint32_t)(p.num_heads * D * 2), threadIdx.x >> 6, threadIdx.x & 63);
-  ln.init(threadIdx.x & 63);
-  tile_loop(p, p.dq_tiles, p.dq_seg_ptr, p.counters + kDqCounter, xcd_gsize(), &next_tile, p.dq_visits,
-            [&](Tile t) { dq_ds_tile<D>(p, t, (JFA_LDS char*)smem, ln, threadIdx.x); });
 }
 
 }  // namespace
