@@ -142,6 +142,24 @@ __device__ __forceinline__ void wait_vmem_upto() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(n) for a run-time n (0 .. 31; larger counts wait for 31, which is
+// never wrong: fewer outstanding instructions than allowed).
+__device__ __forceinline__ void wait_vmem_at_most(int n) {
+  switch (n < 0 ? 0 : (n > 31 ? 31 : n)) {
+#define JFA_WAIT_CASE(k) \
+  case k:                \
+    wait_vmem_upto<k>(); \
+    break;
+    JFA_WAIT_CASE(0) JFA_WAIT_CASE(1) JFA_WAIT_CASE(2) JFA_WAIT_CASE(3) JFA_WAIT_CASE(4) JFA_WAIT_CASE(5)
+    JFA_WAIT_CASE(6) JFA_WAIT_CASE(7) JFA_WAIT_CASE(8) JFA_WAIT_CASE(9) JFA_WAIT_CASE(10) JFA_WAIT_CASE(11)
+    JFA_WAIT_CASE(12) JFA_WAIT_CASE(13) JFA_WAIT_CASE(14) JFA_WAIT_CASE(15) JFA_WAIT_CASE(16) JFA_WAIT_CASE(17)
+    JFA_WAIT_CASE(18) JFA_WAIT_CASE(19) JFA_WAIT_CASE(20) JFA_WAIT_CASE(21) JFA_WAIT_CASE(22) JFA_WAIT_CASE(23)
+    JFA_WAIT_CASE(24) JFA_WAIT_CASE(25) JFA_WAIT_CASE(26) JFA_WAIT_CASE(27) JFA_WAIT_CASE(28) JFA_WAIT_CASE(29)
+    JFA_WAIT_CASE(30) default: wait_vmem_upto<31>();
+#undef JFA_WAIT_CASE
+  }
+}
+
 // Workgroup barrier between the phases of a two-group (ping-pong) kernel.  The LDS
 // reads of a phase are consumed inside it; the lgkmcnt(0) makes sure none is still in
 // flight when another wave's copy reuses its ring slot.  Copies are ordered explicitly

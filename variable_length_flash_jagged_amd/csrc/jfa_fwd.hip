@@ -310,10 +310,9 @@ __device__ __forceinline__ int key_steps(const FwdParams& p, Tile tile) {
   }
 }
 
-// Vector-memory instructions the epilogue of a tile issues in one wave (O row pieces
-// and the lse), when any of the wave's query rows exists.
+// LDS of the epilogue's O staging: half a tile of bf16 rows, RB + 8 bytes apart.
 template <int D>
-constexpr int fwd_epilogue_stores() { return 4 * (D / 32) + 1; }
+constexpr int fwd_staging_bytes() { return (kFwdRows / 2) * (2 * D + 8); }
 
 // One forward tile.  Stage i of the tile lives in ring slot (sb + i) % NS.  qf holds
 // the tile's Q rows when pre (the previous tile loaded them and copied stages 0, 1).
@@ -324,7 +323,7 @@ constexpr int fwd_epilogue_stores() { return 4 * (D / 32) + 1; }
 template <int D, int MODE>
 __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_next, Tile nx, bool pre, int sb,
                                         int prev_stores, bf16x8 (&qf)[FwdCfg<D>::NKS], JFA_LDS char* smem,
-                                        const FwdLane<D>& ln, int tid) {
+                                        JFA_LDS char* stg, const FwdLane<D>& ln, int tid) {
   using C = FwdCfg<D>;
   constexpr bool SELF = FwdGeo<D, MODE>::SELF;
   const int lane = tid & 63;
@@ -358,8 +357,7 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
     if (pre) {
       // Q and stage 0 landed (stage 1 and the previous tile's epilogue stores, issued
       // after them, may not have)
-      if (prev_stores) wait_vmem_upto<C::DMA_PER_STAGE + fwd_epilogue_stores<D>()>();
-      else wait_vmem_n<C::DMA_PER_STAGE>();
+      wait_vmem_at_most(C::DMA_PER_STAGE + prev_stores);
     } else {
       issue(0, mat_off);
       wait_vmem();  // Q and stage 0
@@ -434,43 +432,75 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
   }
 
   // Epilogue: O / l in bf16, lse = ln 2 * (m*c + log2 l); empty rows give 0 and -inf.
-  // (wave-uniform store count: the stores run when the wave's first row exists)
-  const int stores = (row - (lane & 31)) < Lq ? fwd_epilogue_stores<D>() : 0;
+  const bool any_row = (row - (lane & 31)) < Lq;  // wave-uniform: the wave's first row exists
   const float lt = half_sum(w.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const float lse = lt > 0.f ? (w.m * c + fast_log2(lt)) * kLn2 : -INFINITY;
   constexpr bool CHUNKED = FwdGeo<D, MODE>::CHUNKED;
-  if (CHUNKED && t.slot >= 0 && row < Lq) {
+  int stores = 0;  // vector-memory stores this wave issues (counted by the next tile's first wait)
+  if (CHUNKED && t.slot >= 0) {
     // chunk of a cut sequence: fp32 O / l and lse of this chunk, merged afterwards
     // (broadcast-Q: slot s of [S, Mq, H] rows; self: part row t.slot + row of [R, H])
-    const int64_t prow = SELF ? (int64_t)t.slot + row : (int64_t)t.slot * p.num_q + row;
-    float* po = p.part_o + (prow * H + t.h) * D + 4 * half;
+    if (row < Lq) {
+      const int64_t prow = SELF ? (int64_t)t.slot + row : (int64_t)t.slot * p.num_q + row;
+      float* po = p.part_o + (prow * H + t.h) * D + 4 * half;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+      for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x16& x = w.o[db];
-        *reinterpret_cast<float4*>(po + 32 * db + 8 * g4) =
-            make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& x = w.o[db];
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * g4) =
+              make_float4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv);
+        }
+      if (half == 0) {
+        if constexpr (SELF) p.part_lse[prow * H + t.h] = lse;
+        else p.part_lse[((int64_t)t.slot * H + t.h) * p.num_q + row] = lse;
       }
-    if (half == 0) {
-      if constexpr (SELF) p.part_lse[prow * H + t.h] = lse;
-      else p.part_lse[((int64_t)t.slot * H + t.h) * p.num_q + row] = lse;
     }
-  } else if (row < Lq) {
-    const int64_t orow = SELF ? t.s0 + row : (int64_t)t.b * p.num_q + row;
-    uint16_t* op = p.o + orow * rs + (int64_t)t.h * D + 4 * half;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x16& x = w.o[db];
-        st8(op + 32 * db + 8 * g4,
-            pack4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv));
-      }
-    if (half == 0) {
+    stores = any_row ? 4 * C::NDB + 1 : 0;
+  } else {
+    if (row < Lq && half == 0) {
       const int64_t li = SELF ? (int64_t)t.h * p.total_tokens + t.s0 + row : ((int64_t)t.b * H + t.h) * p.num_q + row;
       p.lse[li] = lse;
+    }
+    stores = any_row ? 1 : 0;
+    // O rows through LDS, half a tile at a time (half r = rows 128 r .. 128 r + 127, the
+    // rows of wave group r), as bf16 [row][D] with rows RB + 8 bytes apart (the 32 rows of
+    // one write land in distinct banks); then all eight waves write whole rows with
+    // 16-byte stores instead of each lane writing 8-byte pieces of its own row.  Rows past
+    // the end repeat the half's last row (same address, same value).
+    constexpr int PITCH = C::RB + 8, HR = C::BM / 2, CPR = C::RB / 16;
+    constexpr int PASSES = HR * CPR / (C::NW * 64);
+    int tl = tid;
+    asm volatile("" : "+v"(tl));  // computed here, not hoisted and kept live through the phases
+    const int wbase = (((tl >> 6) & 3) * 32 + (tl & 31)) * PITCH + 8 * ((tl >> 5) & 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int valid = min(HR, Lq - t.blk * C::BM - HR * r);  // workgroup-uniform
+      if (valid <= 0) break;
+      if (g == r) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16& x = w.o[db];
+            lds_st8(stg + 64 * db + 16 * g4, wbase,
+                    pack4(x[4 * g4] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv));
+          }
+      }
+      __syncthreads();
+      const int row0 = t.blk * C::BM + HR * r;
+      uint16_t* ob = p.o + (SELF ? t.s0 + row0 : (int64_t)t.b * p.num_q + row0) * rs + (int64_t)t.h * D;
+#pragma unroll
+      for (int k = 0; k < PASSES; ++k) {
+        const int q = tl + C::NW * 64 * k;
+        const int rr = min(q / CPR, valid - 1), cc = q % CPR;
+        const int ro = rr * PITCH + 16 * cc;
+        const u32x2 lo = lds_ld8(stg, ro), hi = lds_ld8(stg, ro + 8);
+        st16(ob + (int64_t)rr * rs + 8 * cc, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+      stores += PASSES;
+      __syncthreads();
     }
   }
   return stores;
@@ -481,8 +511,10 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     __attribute__((amdgpu_waves_per_eu(kFwdWgPerCu * kFwdWaves / 4, kFwdWgPerCu * kFwdWaves / 4))) fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stg_raw[fwd_staging_bytes<D>()];
   __shared__ int next_tile;
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
+  JFA_LDS char* stg = (JFA_LDS char*)stg_raw;
   const int tid = threadIdx.x;
   const int prog = xcd_program_id(blockIdx.x, gridDim.x);
   FwdLane<D> ln;
@@ -520,7 +552,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64)
     const Tile nt = more ? p.tiles[nxt] : cur;
     const int nt_n = more ? key_steps<D, MODE>(p, nt) : 0;
     const bool ahead = more && cur_n > 0 && nt_n > 0;
-    stores = fwd_tile<D, MODE>(p, cur, ahead, nt, pre, sb, stores, qf, smem, ln, tid);
+    stores = fwd_tile<D, MODE>(p, cur, ahead, nt, pre, sb, stores, qf, smem, stg, ln, tid);
     if (!more) break;
     if (cur_n > 0) sb = (sb + cur_n + 1) % C::NS;
     pre = ahead;
