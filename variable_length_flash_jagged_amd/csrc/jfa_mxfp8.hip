@@ -99,33 +99,48 @@ __global__ void __launch_bounds__(256) quant_qk_kernel(MxQuantParams p) {
 // LDS tile [head][64 keys][D]; then lane (head, d) reads its dimension's 64 values down
 // the tile, forms the two 32-key blocks' exponents and writes its 64 code bytes (one
 // contiguous run of the transposed layout) and its two exponent bytes.  Keys past the
-// sequence's end are zero.
+// sequence's end are zero.  A workgroup loads its next group's rows into registers
+// before quantising the current one.
 template <int D>
 __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
   constexpr int HPW = 256 / D;  // heads per workgroup
   constexpr int CPR = D / 8;    // 16-byte pieces per key row of one head
+  constexpr int LOADS = (HPW * kMxVPad * CPR) / 256;
   __shared__ __attribute__((aligned(16))) uint16_t tile[HPW * kMxVPad * D];
   const int H = p.num_heads, t = threadIdx.x;
   const int hgroups = (H + HPW - 1) / HPW;
-  const int64_t groups = p.tp / kMxVPad;
-  for (int64_t gh = blockIdx.x; gh < groups * hgroups; gh += gridDim.x) {
+  const int64_t groups = p.tp / kMxVPad, work = groups * hgroups;
+  // The next group's rows are loaded into registers while this group is quantised.
+  u32x4 w[LOADS];
+  auto load = [&](int64_t gh) {
     const int64_t grp = gh / hgroups;
     const int h0 = (int)(gh - grp * hgroups) * HPW;
     const int b = p.group_seq[grp];
     const int64_t s0 = p.offsets[b];
     const int64_t j0 = grp * kMxVPad - p.vbase[b];
     const int valid = (int)min<int64_t>(kMxVPad, p.offsets[b + 1] - s0 - j0);
-    __syncthreads();  // the previous group's readers are done with the tile
 #pragma unroll
-    for (int r = 0; r < (HPW * kMxVPad * CPR) / 256; ++r) {
+    for (int r = 0; r < LOADS; ++r) {
       const int q = t + 256 * r;
       const int j = q / (HPW * CPR), rem = q % (HPW * CPR);
       const int hh = rem / CPR, c8 = rem % CPR;
-      u32x4 w = zero16();
-      if (j < valid && h0 + hh < H) w = ld16(p.x + ((s0 + j0 + j) * H + h0 + hh) * D + 8 * c8);
-      *reinterpret_cast<u32x4*>(&tile[(hh * kMxVPad + j) * D + 8 * c8]) = w;
+      w[r] = (j < valid && h0 + hh < H) ? ld16(p.x + ((s0 + j0 + j) * H + h0 + hh) * D + 8 * c8) : zero16();
+    }
+  };
+  if (blockIdx.x < work) load(blockIdx.x);
+  for (int64_t gh = blockIdx.x; gh < work; gh += gridDim.x) {
+    const int64_t grp = gh / hgroups;
+    const int h0 = (int)(gh - grp * hgroups) * HPW;
+    __syncthreads();  // the previous group's readers are done with the tile
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int q = t + 256 * r;
+      const int j = q / (HPW * CPR), rem = q % (HPW * CPR);
+      const int hh = rem / CPR, c8 = rem % CPR;
+      *reinterpret_cast<u32x4*>(&tile[(hh * kMxVPad + j) * D + 8 * c8]) = w[r];
     }
     __syncthreads();
+    if (gh + gridDim.x < work) load(gh + gridDim.x);
     const int hh = t / D, d = t % D;
     if (h0 + hh < H) {
       const int64_t row = (int64_t)(h0 + hh) * D + d;
@@ -144,7 +159,7 @@ __global__ void __launch_bounds__(256) quant_v_kernel(MxQuantParams p) {
         uint32_t qq[8];
         quantise32(v, xs[half], qq);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) q[8 * half + w] = qq[w];
+        for (int k = 0; k < 8; ++k) q[8 * half + k] = qq[k];
       }
       u32x4* dst = reinterpret_cast<u32x4*>(p.codes + row * p.tp + grp * kMxVPad);
 #pragma unroll
