@@ -36,6 +36,8 @@
 //  * Persistent grid: each workgroup walks its host-scheduled tile list, or takes
 //    tiles from an atomic counter in dynamic mode (aixai.ru page, "Tile balancing and
 //    Cluster Launch Control").
+#include <type_traits>
+
 #include "jfa_device.h"
 #include "jfa_internal.h"
 #include "jfa_sched.h"
@@ -388,47 +390,64 @@ __device__ __forceinline__ int fwd_tile(const FwdParams& p, Tile tile, bool has_
       issue(2, iss_off);
       iss_off = adv(iss_off);
     }
-    if (g) end_phase();
-    // matrix phase 0: S(0) only.  Matrix phases run at raised wave priority: when both
-    // waves of a SIMD have an instruction ready, the one feeding the matrix core goes
-    // first (measured: 1.7 % faster than equal priorities; raising the vector phase
-    // instead changes nothing).
-    __builtin_amdgcn_s_setprio(2);
-    mma_s<D>(smem + mat_off, ln, w);
-    pin_matrix_phase<D>(w);
-    __builtin_amdgcn_s_setprio(0);
-    end_phase();
-    for (int i = 1; i < n; ++i) {
-      softmax_phase<D>(w, C::BN, half, c);  // tiles before the last are full
-      pin_vector_phase<D>(w);
+    // A wave whose 32 query rows all lie past the end (the last tile of a sequence) runs
+    // the same phases -- copies, waits, barriers -- without the products and the softmax.
+    auto phases = [&](auto compute_tag) {
+      constexpr bool COMP = decltype(compute_tag)::value;
+      if (g) end_phase();
+      // matrix phase 0: S(0) only.  Matrix phases run at raised wave priority: when both
+      // waves of a SIMD have an instruction ready, the one feeding the matrix core goes
+      // first (measured: 1.7 % faster than equal priorities; raising the vector phase
+      // instead changes nothing).
+      if constexpr (COMP) {
+        __builtin_amdgcn_s_setprio(2);
+        mma_s<D>(smem + mat_off, ln, w);
+        pin_matrix_phase<D>(w);
+        __builtin_amdgcn_s_setprio(0);
+      }
       end_phase();
-      mat_off = adv(mat_off);
-      const JFA_LDS char* slot_p = smem + mat_off;
-      __builtin_amdgcn_s_setprio(2);
-      mma_pv_s<D>(slot_p, slot_p + C::TILE, ln, w);
-      order_mixed_phase<D>();
-      pin_matrix_phase<D>(w);
-      __builtin_amdgcn_s_setprio(0);
+      for (int i = 1; i < n; ++i) {
+        if constexpr (COMP) {
+          softmax_phase<D>(w, C::BN, half, c);  // tiles before the last are full
+          pin_vector_phase<D>(w);
+        }
+        end_phase();
+        mat_off = adv(mat_off);
+        if constexpr (COMP) {
+          const JFA_LDS char* slot_p = smem + mat_off;
+          __builtin_amdgcn_s_setprio(2);
+          mma_pv_s<D>(slot_p, slot_p + C::TILE, ln, w);
+          order_mixed_phase<D>();
+          pin_matrix_phase<D>(w);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_phase();
+      }
+      if constexpr (COMP) {
+        softmax_phase<D>(w, t.rows_of(t.tile_of(n - 1)), half, c);
+        pin_vector_phase<D>(w);
+      }
       end_phase();
-    }
-    softmax_phase<D>(w, t.rows_of(t.tile_of(n - 1)), half, c);
-    pin_vector_phase<D>(w);
-    end_phase();
-    if (has_next) {
-      FwdGeo<D, MODE> t2;
-      t2.init(p, nx, wave, lane & 31);
-      t2.load_q(p, qf, half);
-      // every stage 2 .. n has been issued: iss_off is the slot of stage n + 1
-      t2.issue(p, ln, 0, iss_off, smem, wave, lane);
-      t2.issue(p, ln, 1, adv(iss_off), smem, wave, lane);
-    }
-    // matrix phase n: O += V(n-1) P(n-1) only
-    __builtin_amdgcn_s_setprio(2);
-    mma_pv<D>(smem + adv(mat_off) + C::TILE, ln, w);
-    pin_matrix_phase<D>(w);
-    __builtin_amdgcn_s_setprio(0);
-    end_phase();
-    if (!g) end_phase();
+      if (has_next) {
+        FwdGeo<D, MODE> t2;
+        t2.init(p, nx, wave, lane & 31);
+        t2.load_q(p, qf, half);
+        // every stage 2 .. n has been issued: iss_off is the slot of stage n + 1
+        t2.issue(p, ln, 0, iss_off, smem, wave, lane);
+        t2.issue(p, ln, 1, adv(iss_off), smem, wave, lane);
+      }
+      // matrix phase n: O += V(n-1) P(n-1) only
+      if constexpr (COMP) {
+        __builtin_amdgcn_s_setprio(2);
+        mma_pv<D>(smem + adv(mat_off) + C::TILE, ln, w);
+        pin_matrix_phase<D>(w);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase();
+      if (!g) end_phase();
+    };
+    if ((row - (lane & 31)) < Lq) phases(std::true_type{});
+    else phases(std::false_type{});
   }
 
   // Epilogue: O / l in bf16, lse = ln 2 * (m*c + log2 l); empty rows give 0 and -inf.
