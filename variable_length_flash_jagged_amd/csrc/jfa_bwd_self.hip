@@ -1176,21 +1176,31 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
     }
     // Step it reads slot (it + 1) & 1 (compile time, so that every LDS address is a lane
     // register plus an immediate); the next step's copies go to the other slot first.
-    auto one_step = [&](auto slot_tag, int it) {
+    // A wave whose 32 keys all lie past the end (in a sequence's last key tile) runs the
+    // same copies, waits and barriers without its streams: fewer LDS reads for the other
+    // waves of the step.  (Its dS rows are not stored: the dQ kernel masks keys past the
+    // end.)  Two instances of the step loop, so that no branch sits inside it.
+    auto one_step = [&](auto slot_tag, auto active_tag, int it) {
       constexpr int SL = decltype(slot_tag)::value;
+      constexpr bool ACTIVE = decltype(active_tag)::value;
       if (it + 1 < x.n) kv2_issue_step<D>(p, ln, x, it + 1, SL ^ 1, smem, wave, lane);
-      Kv2Stream<D, STORE, kv2_ahead<STORE>(), SL>(smem, ln, dk, dv, ds_row + (int64_t)it * kDsBlockBytes, ds_off, g)
-          .go();
+      if constexpr (ACTIVE)
+        Kv2Stream<D, STORE, kv2_ahead<STORE>(), SL>(smem, ln, dk, dv, ds_row + (int64_t)it * kDsBlockBytes, ds_off, g)
+            .go();
       // group 0's next-step copies were issued before this step's two dS stores; loads
       // and stores complete in issue order, so waiting for all but those two suffices
-      if (STORE) wait_vmem_n<2>();
+      if (STORE && ACTIVE) wait_vmem_n<2>();
       else wait_vmem();
       __syncthreads();
     };
-    for (int it = 0; it < x.n; it += 2) {
-      one_step(std::integral_constant<int, 1>{}, it);
-      if (it + 1 < x.n) one_step(std::integral_constant<int, 0>{}, it + 1);
-    }
+    auto steps = [&](auto active_tag) {
+      for (int it = 0; it < x.n; it += 2) {
+        one_step(std::integral_constant<int, 1>{}, active_tag, it);
+        if (it + 1 < x.n) one_step(std::integral_constant<int, 0>{}, active_tag, it + 1);
+      }
+    };
+    if (32 * kw < x.keys) steps(std::true_type{});
+    else steps(std::false_type{});
 
     // Prefetch the next tile (K, V tiles and ring slot 1 are free now).
     const bool more = nxt < end;
