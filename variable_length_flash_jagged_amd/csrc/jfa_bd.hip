@@ -292,29 +292,43 @@ __device__ __forceinline__ void bd_fwd_tile(const BdParams& p, const BdTile& t, 
     }
   }
   wait_vmem();
-  // O^T = V^T P^T.
+  // O^T = V^T P^T for both 32-row blocks.
+  f32x16 o[2][C::NDB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        o[qb][db] = mfma32(tr_operand<C::RB>(vt, 16 * tt, 32 * db, lane), pf[qb][tt], o[qb][db]);
+    }
+  // The O rows go out through the wave's V tile (free once the products have read it;
+  // one wave's LDS instructions execute in order, so its reads of V precede these
+  // writes and the writes precede the reads below): bf16 [row][D] with 16-byte chunks
+  // swizzled by row, then whole rows with 16-byte stores (a row's chunks from
+  // consecutive lanes) -- writing each lane's 8-byte pieces of its own row directly
+  // took about half the kernel's time.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = qb * 32 + l32;
     const float inv = 1.0f / l[qb];
-    f32x16 o[C::NDB];
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+      for (int g4 = 0; g4 < 4; ++g4)
+        lds_st8(vt, swz_off<C::RB>(row, 4 * db + g4) + 8 * half,
+                pack4(o[qb][db][4 * g4] * inv, o[qb][db][4 * g4 + 1] * inv, o[qb][db][4 * g4 + 2] * inv,
+                      o[qb][db][4 * g4 + 3] * inv));
+    if (row < n && half == 0) p.lse[(int64_t)t.h * p.total_tokens + t.t0 + row] = (m[qb] * c + fast_log2(l[qb])) * kLn2;
+  }
+  constexpr int CPR = C::RB / 16;  // 16-byte chunks per row
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) o[db] = mfma32(tr_operand<C::RB>(vt, 16 * tt, 32 * db, lane), pf[qb][tt], o[db]);
-    }
-    if (row < n) {
-      uint16_t* op = p.o + base + row * rs + 4 * half;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          st8(op + 32 * db + 8 * g4, pack4(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
-                                          o[db][4 * g4 + 3] * inv));
-      if (half == 0) p.lse[(int64_t)t.h * p.total_tokens + t.t0 + row] = (m[qb] * c + fast_log2(l[qb])) * kLn2;
-    }
+  for (int k = 0; k < kBlock * CPR / 64; ++k) {
+    const int q = lane + 64 * k;
+    const int row = q / CPR, cc = q % CPR;
+    if (row < n) st16(p.o + base + row * rs + 8 * cc, lds_ld16(vt, swz_off<C::RB>(row, cc)));
   }
 }
 
