@@ -54,7 +54,7 @@ def _check_fwd(o, lse, o_ref, lse_ref, q, k, offsets, tab, scale, label):
 LENGTHS = [64, 130, 5, 0, 256, 1, 63, 65, 700]
 
 
-def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", table_rows=None):
+def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", table_rows=None, opts=None):
     print(f"[case] rotary {label} lengths={lengths} H={heads} Hkv={num_kv_heads or heads} D={head_dim} "
           f"seed={seed} bwd={bwd}", flush=True)
     p = W.make_problem(lengths, heads, head_dim, W.MODE_BLOCK_DIAG, seed=seed, device="cpu", with_grad=bwd,
@@ -62,7 +62,7 @@ def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", 
     g = G.to_gpu(p)
     rows = table_rows or max(1, max(lengths))
     rope = B.rope_table(rows, head_dim, device="cuda")
-    o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"], None,
+    o, lse = B.fwd_rotary(g["q"], g["k"], g["v"], g["offsets"], g["offsets_host"], rope, g["scale"], opts,
                           *G.nan_outputs_fwd(g))
     torch.cuda.synchronize()
     tab = R.rope_table(rows, head_dim)
@@ -72,7 +72,7 @@ def _run(lengths, heads, head_dim, seed, num_kv_heads=None, bwd=True, label="", 
     grads = None
     if bwd:
         grads = B.bwd_rotary(g["q"], g["k"], g["v"], o, g["do"], lse, g["offsets"], g["offsets_host"], rope,
-                             g["scale"], None, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
+                             g["scale"], opts, G.nan_like(g["q"]), G.nan_like(g["k"]), G.nan_like(g["v"]))
         torch.cuda.synchronize()
         refs = R.rotary_block_backward(G.f64(p["q"]), G.f64(p["k"]), G.f64(p["v"]), G.f64(p["do"]),
                                        p["offsets_host"], tab, p["scale"])
