@@ -125,6 +125,17 @@ __device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, JFA_L
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
+// Narrow forms of the same copy: each lane fetches 4 bytes (dma4) or 2 bytes (dma2) at
+// sbase + voff; either way the lane's value lands as one dword at lds_base + 4 * lane
+// (2-byte values zero-extended; measured with an in-bounds probe).
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, JFA_LDS char* lds_base) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma2(const void* sbase, uint32_t voff, JFA_LDS char* lds_base) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_nop 4\n\tglobal_load_lds_ushort %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
