@@ -138,7 +138,7 @@ def kernel_source_digest():
 KERNEL_NAMES = {"fwd_kernel": "fwd_kernel<", "dq_kernel": "dq_kernel<", "dkdv_kernel": "dkdv_kernel<",
                 "dkdv2_kernel": "dkdv2_kernel<",
                 "dq_ds_kernel": "dq_ds_kernel<", "prep_kernel": "prep_kernel<", "mark_kernel": "mark_kernel",
-                "mx_fwd_kernel": "mx_fwd_kernel<",
+                "mx_fwd_kernel": "mx_fwd_kernel<", "mx2_fwd_kernel": "mx2_fwd_kernel(",
                 "bwd_kernel": "bwd_kernel<", "bd_fwd_kernel": "bd_fwd_kernel<", "bd_bwd_kernel": "bd_bwd_kernel<"}
 
 
@@ -530,7 +530,8 @@ def main():
     if mode == W.MODE_BLOCK_DIAG and dom == "fwd":
         roof["kernel"] = "bd_fwd_kernel"
     if mxfp8 and dom == "fwd":
-        roof["kernel"] = "mx_fwd_kernel"
+        # head_dim 128 runs the two-group ping-pong kernel
+        roof["kernel"] = "mx2_fwd_kernel" if d == 128 else "mx_fwd_kernel"
     if dom == "bwd" and mode == W.MODE_SELF and d == 128 and not ratio:
         roof["kernel"] = "dkdv2_kernel"  # the two-waves-per-SIMD dK/dV kernel of self attention
     roof["kernel_ms"] = kd["ms"]
