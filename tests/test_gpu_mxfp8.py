@@ -53,14 +53,14 @@ def _same_values(a, b, what):
     assert bad.size == 0, f"{what}: {bad.size} values differ, first at {bad[0]}: {a.ravel()[bad[0]]} vs {b.ravel()[bad[0]]}"
 
 
-def _run(lengths, heads, head_dim, seed, label=""):
+def _run(lengths, heads, head_dim, seed, label="", opts=None):
     print(f"[case] mxfp8 {label} lengths={list(lengths)[:12]} H={heads} D={head_dim} seed={seed}", flush=True)
     p = W.make_problem(lengths, heads, head_dim, seed=seed, device="cpu", with_grad=False)
     g = G.to_gpu(p)
     q8, qs = B.mxfp8_quantize_qk(g["q"])
     k8, ks = B.mxfp8_quantize_qk(g["k"])
     v8, vs, tp = B.mxfp8_quantize_v(g["v"], g["offsets"], g["offsets_host"])
-    o, lse = B.fwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, g["offsets"], g["offsets_host"], g["scale"])
+    o, lse = B.fwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, g["offsets"], g["offsets_host"], g["scale"], opts)
     torch.cuda.synchronize()
     # quantisers: bit-exact against the oracle
     qv_ref, qx_ref = M.quantise_qk(G.f64(p["q"]))
@@ -96,6 +96,26 @@ def _run(lengths, heads, head_dim, seed, label=""):
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_mxfp8_forward(head_dim):
     _run(LENGTHS, 2, head_dim, seed=71, label=f"D{head_dim}")
+
+
+@pytest.mark.parametrize("nprog", [1, 3, 7])
+def test_mxfp8_forward_many_tiles_per_program(nprog):
+    """Few programs, so that each walks many tiles (at head_dim 128 every tile loads the
+    next tile's first stages and Q rows while it finishes): against the oracle, and bit
+    for bit against the default launch (a tile's result does not depend on the program
+    that runs it or on the tile before it).  The MXFP8 forward deals its tiles statically."""
+    lengths = LENGTHS + [1000, 2, 129]
+    p, o, lse = _run(lengths, 3, 128, seed=74, label=f"{nprog} programs",
+                     opts=B.make_opts(num_programs=nprog))
+    g = G.to_gpu(p)
+    q8, qs = B.mxfp8_quantize_qk(g["q"])
+    k8, ks = B.mxfp8_quantize_qk(g["k"])
+    v8, vs, tp = B.mxfp8_quantize_v(g["v"], g["offsets"], g["offsets_host"])
+    o0, l0 = B.fwd_mxfp8(q8, qs, k8, ks, v8, vs, tp, g["offsets"], g["offsets_host"], g["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), "O differs from the default launch"
+    fin = torch.isfinite(l0)
+    assert torch.equal(fin, torch.isfinite(lse)) and torch.equal(lse[fin], l0[fin]), "lse differs"
 
 
 def test_mxfp8_large_and_small_magnitudes():
