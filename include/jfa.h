@@ -340,7 +340,14 @@ int jfa_fwd_noalloc(const jfa_shape* shape, int mode, float scale,
  * schedules list tiles program by program with one segment per program
  * (seg_ptr[P+1]); dynamic schedules list each counter group's tiles in sorted order,
  * one segment per group.  tiles (3*cap int32) and seg_ptr (seg_cap int32) may be NULL to
- * query the counts only; JFA_ERR_CAPACITY if an array is too small. */
+ * query the counts only; JFA_ERR_CAPACITY if an array is too small.
+ *
+ * Diagnostics: with JFA_LOG set to a value other than "0" in the environment (read once
+ * per process), every schedule the library builds, here or inside the calls above,
+ * prints one line on stderr: its tile and program counts, its segments (programs of a
+ * static schedule, counter groups of a dynamic one), the summed tile cost (a tile costs
+ * its sequence's or key chunk's length where tiles differ in cost, 1 where they cost the
+ * same) and the largest segment cost against the mean. */
 int jfa_schedule(const jfa_shape* shape, int mode, int pass, const int32_t* offsets_host,
                  const jfa_opts* opts, int32_t* tiles, int64_t cap, int32_t* seg_ptr,
                  int64_t seg_cap, int64_t* n_tiles, int32_t* n_segs, int32_t* n_programs,

@@ -1,6 +1,9 @@
 // Host tile scheduler; see jfa_sched.h for the rules and their sources.
 #include "jfa_sched.h"
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <algorithm>
 #include <numeric>
 
@@ -55,6 +58,36 @@ void deal_zigzag(const std::vector<HostTile>& order, int max_programs, bool dyna
   for (int64_t i = 0; i < n; ++i) out.tiles[fill[seg_of(i)]++] = order[i];
 }
 
+// JFA_LOG=1 in the environment: one line on stderr per schedule built, with the tile
+// and program counts and how evenly the tile cost falls on the segments (programs of a
+// static schedule, counter groups of a dynamic one).  A tile costs cost_of[b] (its
+// sequence's or chunk's key length), or 1 where cost_of is empty (equal-cost tiles).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("JFA_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+void log_schedule(const char* what, const std::vector<int32_t>& cost_of, const Schedule& s) {
+  if (!log_enabled()) return;
+  const int segs = (int)s.seg_ptr.size() - 1;
+  double total = 0.0, worst = 0.0;
+  for (int i = 0; i < segs; ++i) {
+    double c = 0.0;
+    for (int32_t t = s.seg_ptr[i]; t < s.seg_ptr[i + 1]; ++t) c += cost_of.empty() ? 1.0 : (double)cost_of[s.tiles[t].b];
+    total += c;
+    worst = std::max(worst, c);
+  }
+  const double mean = segs > 0 ? total / segs : 0.0;
+  fprintf(stderr,
+          "jfa schedule %s: tiles %lld, programs %d, %s %d, tile rows %d, cost %.0f, per segment max %.0f mean %.1f "
+          "(max/mean %.3f)\n",
+          what, (long long)s.tiles.size(), s.programs, s.groups > 0 ? "counter groups" : "static segments", segs,
+          s.tile_rows, total, worst, mean, mean > 0.0 ? worst / mean : 0.0);
+}
+
 }  // namespace
 
 void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int num_q,
@@ -66,6 +99,7 @@ void schedule_fwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
   sorted_tiles(lengths, num_heads, rows, rows_of, order);
   out.tile_rows = rows;
   deal_zigzag(order, max_programs, dynamic, out);
+  log_schedule(mode == kBroadcastMode ? "broadcast-Q sorted zigzag" : "self sorted zigzag", lengths, out);
 }
 
 void schedule_fwd_chunks(const std::vector<int32_t>& cost, const std::vector<int32_t>& rows_of, int num_heads,
@@ -74,6 +108,7 @@ void schedule_fwd_chunks(const std::vector<int32_t>& cost, const std::vector<int
   sorted_tiles(cost, num_heads, rows, rows_of, order);
   out.tile_rows = rows;
   deal_zigzag(order, max_programs, dynamic, out);
+  log_schedule("self key chunks sorted zigzag", cost, out);
 }
 
 void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, int rows,
@@ -83,6 +118,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
     std::vector<HostTile> order;
     sorted_tiles(lengths, num_heads, rows, lengths, order);
     deal_zigzag(order, max_programs, dynamic, out);
+    log_schedule("self backward sorted zigzag", lengths, out);
     return;
   }
   // Broadcast-Q: head-pinned round robin.
@@ -94,6 +130,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
     out.programs = 0;
     out.groups = dynamic ? 1 : 0;
     out.seg_ptr = {0};
+    log_schedule("broadcast-Q backward head-pinned", {}, out);
     return;
   }
   const int ph = (int)std::max<int64_t>(1, std::min<int64_t>(max_programs / num_heads, n_head));
@@ -107,6 +144,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
         for (int32_t j = 0; j < (int32_t)cdiv(lengths[b], rows); ++j) out.tiles.push_back({b, h, j});
       out.seg_ptr.push_back((int32_t)out.tiles.size());
     }
+    log_schedule("broadcast-Q backward head-pinned", {}, out);
     return;
   }
   out.groups = 0;
@@ -122,6 +160,7 @@ void schedule_bwd(const std::vector<int32_t>& lengths, int num_heads, int mode, 
       out.seg_ptr.push_back((int32_t)out.tiles.size());
     }
   }
+  log_schedule("broadcast-Q backward head-pinned", {}, out);
 }
 
 void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int block,
@@ -136,9 +175,11 @@ void schedule_blockdiag(const std::vector<int32_t>& lengths, int num_heads, int 
   const int p = (int)std::min<int64_t>(max_programs, cdiv(n, std::max(1, min_tiles)));
   out.programs = p;
   out.seg_ptr.assign(p + 1, 0);
-  if (p == 0) return;
-  const int64_t q = n / p, r = n % p;
-  for (int i = 0; i <= p; ++i) out.seg_ptr[i] = (int32_t)(i * q + std::min<int64_t>(i, r));
+  if (p > 0) {
+    const int64_t q = n / p, r = n % p;
+    for (int i = 0; i <= p; ++i) out.seg_ptr[i] = (int32_t)(i * q + std::min<int64_t>(i, r));
+  }
+  log_schedule("block-diagonal", {}, out);
 }
 
 }  // namespace jfa
