@@ -215,7 +215,11 @@ int jfa_fwd_block_sparse(const jfa_shape* shape, float scale, float ratio,
  *    the dequantised inputs, S and the softmax statistics in fp32, P quantised per 32
  *    keys of a row with the smallest power-of-two scale that keeps the block maximum
  *    at most 448 before the P V product.  D in {64, 128}; one key/value head per query
- *    head (JFA_ERR_BAD_SHAPE otherwise); static schedule of 128-row tiles.
+ *    head (JFA_ERR_BAD_SHAPE otherwise); static schedule of tiles of 256 query rows
+ *    (D = 128) or 128 (D = 64).  At D = 128 the kernel is a two-group ping-pong whose
+ *    per-lane copy offsets are 32-bit; past D * Tp >= 2^32, or with JFA_MX_GENERIC set
+ *    to a value other than "0" in the environment (read at every call; for tests), the
+ *    one-group kernel of D = 64 runs at D = 128 instead, with the same results' bound.
  * workspace (quantize_v and the forward): jfa_workspace_size(shape, JFA_MODE_SELF,
  * JFA_PASS_FWD_MXFP8, opts) bytes.  Other conventions as jfa_fwd. */
 int jfa_mxfp8_v_tokens(const jfa_shape* shape, const int32_t* offsets_host, int64_t* tokens);

@@ -118,6 +118,27 @@ def test_mxfp8_forward_many_tiles_per_program(nprog):
     assert torch.equal(fin, torch.isfinite(lse)) and torch.equal(lse[fin], l0[fin]), "lse differs"
 
 
+@pytest.mark.parametrize("nprog", [0, 3])
+def test_mxfp8_forward_generic_kernel_at_head_dim_128(monkeypatch, nprog):
+    """The one-group kernel that serves head_dim 128 past the ping-pong kernel's 32-bit
+    copy offsets (D * Tp >= 2^32, too large to check against the oracle), forced at a
+    small size: against the oracle, and close to the ping-pong kernel's output."""
+    lengths = LENGTHS + [1000]
+    monkeypatch.setenv("JFA_MX_GENERIC", "1")
+    opts = B.make_opts(num_programs=nprog)
+    p, o, lse = _run(lengths, 2, 128, seed=75, label=f"generic kernel, programs {nprog}", opts=opts)
+    monkeypatch.delenv("JFA_MX_GENERIC")
+    _, o2, l2 = _run(lengths, 2, 128, seed=75, label=f"ping-pong kernel, programs {nprog}", opts=opts)
+    d = float((o.float() - o2.float()).abs().max())
+    fin = torch.isfinite(l2)
+    assert torch.equal(fin, torch.isfinite(lse))
+    dl = float((lse[fin] - l2[fin]).abs().max())
+    print(f"generic vs ping-pong: O max diff {d:.3e}, lse max diff {dl:.3e}")
+    # same arithmetic in another order of the fp32 sums (measured: 9.8e-4, one bf16
+    # step of O, and 1.4e-6)
+    assert d <= 4e-3 and dl <= 1e-4
+
+
 def test_mxfp8_large_and_small_magnitudes():
     """Inputs spread over many binades: exercises the shared exponents and subnormal
     elements of every block."""

@@ -28,6 +28,7 @@
 // waves x 32 query rows, two waves per SIMD;
 // each 64-key step's K tile, V^T tile and their scales are loaded into registers one
 // step ahead and written to XOR-swizzled LDS tiles between two barriers.
+#include <stdlib.h>
 #include <algorithm>
 #include <type_traits>
 
@@ -38,8 +39,6 @@ namespace jfa {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-constexpr bool kMxPingPong = true;  // head_dim 128 through mx2_fwd_kernel
 
 // OCP MX shared exponent of a block whose largest magnitude is amax.
 __device__ __forceinline__ int mx_exponent(float amax) {
@@ -969,10 +968,18 @@ hipError_t launch_mx_dequant_v(const MxDequantParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// JFA_MX_GENERIC set to a value other than "0" (read at every call) sends head_dim 128
+// through mx_fwd_kernel, which otherwise serves only inputs past the ping-pong kernel's
+// 32-bit copy offsets, so that tests can check it at small sizes.
+bool mx_generic_forced() {
+  const char* e = getenv("JFA_MX_GENERIC");
+  return e && *e && *e != '0';
+}
+
 hipError_t launch_mx_fwd(const MxParams& p, int head_dim, hipStream_t s) {
   if (p.num_programs <= 0) return hipSuccess;
   // the ping-pong kernel's per-lane V^T copy offsets are 32-bit: D * Tp < 2^32
-  if (kMxPingPong && head_dim == 128 && (uint64_t)p.tp * 128u < (uint64_t(1) << 32)) {
+  if (head_dim == 128 && (uint64_t)p.tp * 128u < (uint64_t(1) << 32) && !mx_generic_forced()) {
     hipLaunchKernelGGL(mx2_fwd_kernel, dim3(p.num_programs), dim3(Mx2Cfg::NW * 64), 0, s, p);
     return hipGetLastError();
   }
