@@ -462,7 +462,8 @@ def main():
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     # Per attention kernel: average launch time and the algorithmic work of one launch.
     work = {"fwd": (ff, bytes_f)}
-    stored_ds = not ratio and kt["bwd_prep"][0] > 0
+    bwd_path = B.last_bwd_path()
+    stored_ds = not ratio and bwd_path == B.BWD_PATH_STORED_DS
     if ratio:
         # Block-sparse backward: mark kernel (selection in, bitmaps out), dQ kernel over
         # the kept blocks (S, dP, dQ on attended pairs), dK/dV kernel (S, dP, dV, dK on
@@ -485,9 +486,14 @@ def main():
         # recomputes; Q, K, V, O, dO in, dQ out, lse in and the 16-byte row term out per
         # row and head) and a dK/dV kernel (S, dP, dV, dK; Q, K, V, dO in, dK, dV out,
         # the row term in).
+        # With few tiles the row terms come from the row-term kernel and the dQ kernel
+        # runs beside the dK/dV kernel (it then reads lse and writes no row term).
         pairs = M.valid_pairs(lengths, mode)
         t = int(p["total_tokens"])
-        work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + 20 * t * h)
+        side = bwd_path == B.BWD_PATH_RECOMPUTE_SIDE
+        if side:
+            work["bwd_prep"] = (2 * t * h * d, 4 * t * h * d + 20 * t * h)
+        work["bwd_dq"] = (6 * h * d * pairs, 12 * t * h * d + (4 if side else 20) * t * h)
         work["bwd"] = (8 * h * d * pairs, 12 * t * h * d + 16 * t * h)
     elif mode == W.MODE_BROADCAST_Q and not fwd_only and kt["bwd_dq"][0] > 0:
         # Broadcast-Q through the dQ and dK/dV kernels (dq_path 2): a dQ kernel (S, dP,
@@ -557,7 +563,7 @@ def main():
             "passes": "fwd" if fwd_only else "fwd+bwd",
             "total_tokens": int(p["total_tokens"]), "max_len": int(max(lengths)),
             "sched": ["static", "dynamic"][args.sched], "dq_path": args.dq_path, "seed": args.seed,
-            "self_bwd": ("stored_ds" if stored_ds else "recompute") if mode == W.MODE_SELF else None,
+            "self_bwd": B.BWD_PATH_NAMES[bwd_path] if mode == W.MODE_SELF and not fwd_only else None,
             "ds_budget_mib": int(opts.ds_budget_mib),
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

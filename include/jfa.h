@@ -366,7 +366,8 @@ enum jfa_kernel {
                             dq_path 0 or 1 and in block-diagonal mode */
   JFA_KERNEL_BWD_DQ = 2,  /* the dQ kernel of jfa_bwd in self mode (recompute or stored-dS) and
                              in broadcast-Q mode with dq_path 2, and of jfa_bwd_block_sparse */
-  JFA_KERNEL_BWD_PREP = 3,    /* self mode, stored-dS path: the row-term kernel (Di, lse);
+  JFA_KERNEL_BWD_PREP = 3,    /* self mode: the row-term kernel (Di, lse) of the stored-dS
+                                 path and of the side-by-side recompute path;
                                  jfa_bwd_block_sparse: the selection-bitmap (mark) kernel */
   JFA_KERNEL_SPARSE_SELECT = 4, /* jfa_fwd_block_sparse stage 1: the two pooling launches and the
                                   select launch (each recorded as one launch) */
@@ -383,6 +384,21 @@ enum jfa_kernel {
  * library on the calling thread's current device and released when forgotten. */
 int jfa_kernel_timing(int enable);
 int jfa_kernel_times(int kernel, int64_t* launches, double* total_ms, int reset);
+
+/* Which self-attention backward the calling thread's last jfa_bwd (or jfa_bwd_rotary /
+ * jfa_bwd_mxfp8) call enqueued (JFA_BWD_PATH_OTHER for other modes, for a call that
+ * failed before choosing, or before any call). */
+enum jfa_bwd_path {
+  JFA_BWD_PATH_OTHER = 0,
+  JFA_BWD_PATH_RECOMPUTE = 1,       /* dQ kernel (also writing the row terms), then the
+                                       dK/dV kernel, on the caller's stream */
+  JFA_BWD_PATH_RECOMPUTE_SIDE = 2,  /* the two grids together fit the CUs: the row-term
+                                       kernel, then the dQ kernel on a library-owned side
+                                       stream (default priority) beside the dK/dV kernel;
+                                       the caller's stream waits for both */
+  JFA_BWD_PATH_STORED_DS = 3        /* row-term kernel, dK/dV kernel storing dS, dQ = dS K */
+};
+int jfa_last_bwd_path(void);
 
 /* Debug hook: tile-visit counts, for checking that a schedule (static or run-time)
  * computes every tile exactly once.  counts: caller-allocated device int32 array of

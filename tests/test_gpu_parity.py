@@ -47,6 +47,19 @@ def test_self_few_programs():
     G.run_case(RAGGED, 2, 128, opts=B.make_opts(num_programs=3), seed=5, label="self 3 programs")
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_self_recompute_side_by_side_and_sequential(head_dim):
+    """Recompute backward (no dS budget): with few tiles the dQ kernel runs on the
+    library's side stream beside the dK/dV kernel, the row terms from the row-term
+    kernel; with more tiles than CUs the two kernels run one after the other.  Both
+    against the oracle."""
+    G.run_case(RAGGED, 2, head_dim, seed=24, label=f"recompute side by side D{head_dim}")
+    assert B.last_bwd_path() == B.BWD_PATH_RECOMPUTE_SIDE
+    many = [128] * 300 + [5, 0, 77]  # 302 dQ and 302 dK/dV tiles: more than the CUs
+    G.run_case(many, 1, head_dim, seed=25, label=f"recompute sequential D{head_dim}")
+    assert B.last_bwd_path() == B.BWD_PATH_RECOMPUTE
+
+
 def _ds_opts(lengths, heads, head_dim, **kw):
     off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     shape = B.make_shape(len(lengths), heads, head_dim, int(off[-1]))
@@ -54,13 +67,9 @@ def _ds_opts(lengths, heads, head_dim, **kw):
 
 
 def _ran_stored_ds(fn):
-    """Run fn() with kernel timing on; True when the stored-dS row-term kernel ran."""
-    B.kernel_timing(True)
-    try:
-        fn()
-        return B.kernel_times(B.KERNEL_BWD_PREP)[0] > 0
-    finally:
-        B.kernel_timing(False)
+    """Run fn(); True when its last backward call took the stored-dS path."""
+    fn()
+    return B.last_bwd_path() == B.BWD_PATH_STORED_DS
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])

@@ -29,6 +29,12 @@ KERNEL_BWD_DQ = 2
 KERNEL_BWD_PREP = 3
 KERNEL_SPARSE_SELECT = 4
 KERNEL_MX_QUANT = 5
+BWD_PATH_OTHER = 0
+BWD_PATH_RECOMPUTE = 1
+BWD_PATH_RECOMPUTE_SIDE = 2
+BWD_PATH_STORED_DS = 3
+BWD_PATH_NAMES = {BWD_PATH_OTHER: "other", BWD_PATH_RECOMPUTE: "recompute", BWD_PATH_RECOMPUTE_SIDE: "recompute, dQ beside dK/dV",
+                  BWD_PATH_STORED_DS: "stored dS"}
 
 
 class JfaError(RuntimeError):
@@ -197,6 +203,11 @@ def kernel_times(kernel, reset=False):
     n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
     _check(lib().jfa_kernel_times(kernel, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0), "jfa_kernel_times")
     return int(n.value), float(ms.value)
+
+
+def last_bwd_path():
+    """The self-attention backward (BWD_PATH_*) this thread's last jfa_bwd call enqueued."""
+    return int(lib().jfa_last_bwd_path())
 
 
 def debug_tile_visits(counts, stride):

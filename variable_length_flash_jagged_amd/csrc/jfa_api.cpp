@@ -484,6 +484,42 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   return JFA_OK;
 }
 
+thread_local int g_bwd_path = JFA_BWD_PATH_OTHER;  // jfa_last_bwd_path
+
+// Per-device side stream (default priority) on which a latency-bound recompute
+// backward runs its dQ kernel beside the dK/dV kernel, with the events that fork it from
+// the caller's stream and join it back.  The mutex is held while a call enqueues the
+// fork, the dQ launch and the join.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+
+// Locks and returns this device's side stream, creating it on first use.
+int side_stream(SideStream** out, std::unique_lock<std::mutex>& lock) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return hip_fail(e, "hipGetDevice");
+  SideStream& ss = g_side[dev];
+  lock = std::unique_lock<std::mutex>(ss.mu);
+  if (!ss.s) {
+    e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreate (side stream)");
+  }
+  if (!ss.fork) {
+    e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (fork)");
+  }
+  if (!ss.join) {
+    e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (join)");
+  }
+  *out = &ss;
+  return JFA_OK;
+}
+
 // Allocation-free variant of upload(): a plain copy from the caller's (pageable) host
 // bytes.  The runtime stages pageable memory itself and returns once it has taken the
 // bytes, so `src` may be reused as soon as this returns.  No pinned staging buffer is
@@ -724,6 +760,8 @@ hipError_t timed_launch(int pass, hipStream_t s, F fn) {
 extern "C" {
 
 int jfa_version(void) { return JFA_VERSION; }
+
+int jfa_last_bwd_path(void) { return g_bwd_path; }
 
 int jfa_kernel_timing(int enable) {
   g_detail.clear();
@@ -1473,6 +1511,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
                      const int32_t* offsets_dev, const int32_t* offsets_host, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  g_bwd_path = JFA_BWD_PATH_OTHER;
   visits_begin();
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_shape(shape, mode);
@@ -1584,6 +1623,7 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
       p.dq_tiles = (const Tile*)(ws + L.tiles2);
       p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
       p.dq_programs = sq.programs;
+      g_bwd_path = JFA_BWD_PATH_STORED_DS;
       if ((rc = launch_status(
                timed_launch(JFA_KERNEL_BWD_PREP, stream, [&] { return launch_bwd_self_prep(p, D, stream); }),
                "backward row-term launch")))
@@ -1607,11 +1647,43 @@ static int bwd_entry(const jfa_shape* shape, int mode, float scale, const void* 
     p.dq_tiles = (const Tile*)(ws + L.tiles2);
     p.dq_seg_ptr = (const int32_t*)(ws + L.seg2);
     p.dq_programs = sq.programs;
-    if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq(p, D, stream); }),
+    if ((int64_t)sq.programs + sc.programs > device_cus()) {
+      // Each kernel fills the chip: one after the other, the dQ kernel writing the row terms.
+      g_bwd_path = JFA_BWD_PATH_RECOMPUTE;
+      if ((rc = launch_status(
+               timed_launch(JFA_KERNEL_BWD_DQ, stream, [&] { return launch_bwd_self_dq(p, D, stream); }),
+               "backward dQ launch")))
+        return rc;
+      return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                           "backward dK/dV launch");
+    }
+    // Few tiles (the two grids together fit the CUs, so each kernel's time is its longest
+    // tile's): the row-term kernel first, then the dQ kernel on the side stream beside the
+    // dK/dV kernel on the caller's; neither reads what the other writes, and the caller's
+    // stream waits for both.
+    p.rows_ready = 1;
+    g_bwd_path = JFA_BWD_PATH_RECOMPUTE_SIDE;
+    if ((rc = launch_status(
+             timed_launch(JFA_KERNEL_BWD_PREP, stream, [&] { return launch_bwd_self_prep(p, D, stream); }),
+             "backward row-term launch")))
+      return rc;
+    SideStream* ss = nullptr;
+    std::unique_lock<std::mutex> lock;
+    if ((rc = side_stream(&ss, lock))) return rc;
+    hipError_t e = hipEventRecord(ss->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "forking the side stream");
+    if ((rc = launch_status(timed_launch(JFA_KERNEL_BWD_DQ, ss->s, [&] { return launch_bwd_self_dq(p, D, ss->s); }),
                             "backward dQ launch")))
       return rc;
-    return launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
-                         "backward dK/dV launch");
+    e = hipEventRecord(ss->join, ss->s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
+    rc = launch_status(timed_launch(JFA_PASS_BWD, stream, [&] { return launch_bwd_self_dkdv(p, D, stream); }),
+                       "backward dK/dV launch");
+    e = hipStreamWaitEvent(stream, ss->join, 0);
+    if (rc) return rc;
+    if (e != hipSuccess) return hip_fail(e, "joining the side stream");
+    return JFA_OK;
   }
 
   if (bq_split) {
@@ -1708,6 +1780,7 @@ int jfa_bwd_mxfp8(const jfa_shape* shape, float scale, const uint8_t* q8, const 
                   const int32_t* offsets_host, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, const jfa_opts* opts, void* stream_) {
   g_detail.clear();
+  g_bwd_path = JFA_BWD_PATH_OTHER;
   hipStream_t stream = (hipStream_t)stream_;
   int rc = check_mx_shape(shape);
   if (rc) return rc;

@@ -169,13 +169,13 @@ __device__ __forceinline__ void dq_tile(const BwdParams& p, Tile tile, JFA_LDS c
   }
   const float lse = row_ok ? p.lse[lrow] : INFINITY;
   const float lse2 = lse * kLog2e;
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0 && !p.rows_ready) {
     // sentinel row term for query rows past the end of a sequence (P = dS = 0)
     const bf16 z = (bf16)0.0f;
     const bf16x8 t = {(bf16)(-1e30f), z, (bf16)(-1.0f), z, z, z, z, z};
     st16(p.row_aug + aug_rows * 8, __builtin_bit_cast(u32x4, t));
   }
-  if (row_ok && half == 0 && kstart == 0) {
+  if (row_ok && half == 0 && kstart == 0 && !p.rows_ready) {
     // Row term for the dK/dV kernel: -lse log2 e and -Di as bf16 high + low parts
     // (c S - lse log2 e, c = scale log2 e, is the exponent of P in base 2), and the
     // constant -1 the block-sparse key mask multiplies.
@@ -1108,7 +1108,6 @@ __global__ void __launch_bounds__(Kv2Cfg<D>::NW * 64) __attribute__((amdgpu_wave
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 2, kw = wave & 3;
-  const int l32 = lane & 31, half = lane >> 5;
   const int64_t rs = (int64_t)p.num_heads * D;
   const float c = p.scale_log2;
   Kv2Lane<D> ln;
@@ -1473,7 +1472,7 @@ __global__ void __launch_bounds__(kDsWaves * 64) __attribute__((amdgpu_waves_per
   JFA_LDS char* smem = (JFA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, half = lane >> 5;
+  const int half = lane >> 5;
   const int pair = wave >> 1, cb = wave & 1;
   const int64_t rs = (int64_t)p.num_heads * D;
   const uint32_t rsb = (uint32_t)(rs * 2);

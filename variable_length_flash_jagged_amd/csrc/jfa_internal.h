@@ -203,6 +203,7 @@ struct BwdParams {
   float scale_log2;
   int32_t* visits;     // debug (null: off): visit counts of the dK/dV (or fused) kernel's tiles
   int32_t* dq_visits;  // debug (null: off): visit counts of the dQ kernel's tiles
+  int32_t rows_ready;  // self: 1 = the row-term kernel wrote row_aug, the dQ kernel leaves it alone
 };
 
 // Block-diagonal forward / backward.
