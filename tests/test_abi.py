@@ -94,6 +94,8 @@ def test_backward_refuses_grouped_query_heads_before_device_work():
                      fake, fake, fake, fake, 1 << 30, None, None)
     assert rc == -2
     assert b"num_kv_heads" in lib.jfa_last_error_detail()
+    # a call refused before choosing a backward path reports none
+    assert B.last_bwd_path() == B.BWD_PATH_OTHER
 
 
 @pytest.mark.parametrize("lengths", [[0], [1], [300, 0, 65], [4000, 600, 64]])
